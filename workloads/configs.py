@@ -1,0 +1,125 @@
+"""Chunk layouts of the benchmark workloads (pure bookkeeping, no attention math).
+
+A layout describes a packed token stream the way the block-causal problem is
+stated on the MAGI-1 pages (paperlayer summary §2 and Figure 1; paper-notes
+§2 and Figure 1): a video is a sequence of 24-frame chunks, several videos may
+be packed into one stream (paper-notes Figure 15, "varlen block-causal"), and
+the keys of already-denoised chunks may come from a KV cache (paperlayer §2.4.4).
+
+Fields (all offsets are token indices into the packed streams):
+  q_offsets[n_chunks+1]   chunk c owns queries  [q_offsets[c],  q_offsets[c+1])
+  kv_offsets[n_chunks+1]  chunk c owns keys     [kv_offsets[c], kv_offsets[c+1])
+  seq_chunks[n_seqs+1]    video s owns chunks   [seq_chunks[s], seq_chunks[s+1])
+
+Token counts follow the pages' VAE compression (8x spatial, 4x temporal,
+paperlayer §2.1): a 24-frame chunk is 6 latent frames, and with a 2x2 patch a
+latent frame of H/8 x W/8 becomes (H/16)*(W/16) tokens.
+"""
+from __future__ import annotations
+
+import dataclasses
+import math
+from typing import List, Optional, Sequence
+
+import numpy as np
+
+
+@dataclasses.dataclass(frozen=True)
+class Layout:
+    q_offsets: tuple
+    kv_offsets: tuple
+    seq_chunks: tuple
+
+    @property
+    def n_chunks(self) -> int:
+        return len(self.q_offsets) - 1
+
+    @property
+    def n_seqs(self) -> int:
+        return len(self.seq_chunks) - 1
+
+    @property
+    def t_q(self) -> int:
+        return int(self.q_offsets[-1])
+
+    @property
+    def t_k(self) -> int:
+        return int(self.kv_offsets[-1])
+
+
+def layout_from_chunks(videos: Sequence[Sequence[int]]) -> Layout:
+    """Self-attention layout: each video is a list of chunk token counts; the
+    query and key streams are the same packed stream."""
+    offs = [0]
+    seq = [0]
+    for vid in videos:
+        for n in vid:
+            offs.append(offs[-1] + int(n))
+        seq.append(len(offs) - 1)
+    return Layout(tuple(offs), tuple(offs), tuple(seq))
+
+
+def streaming_layout(n_cached: int, n_active: int, chunk_tokens: int) -> Layout:
+    """One video whose first n_cached chunks are clean (keys/values only, read
+    from the KV cache) and whose last n_active chunks are being denoised
+    (queries and keys/values)."""
+    n = n_cached + n_active
+    q = [max(0, c - n_cached) * chunk_tokens for c in range(n + 1)]
+    kv = [c * chunk_tokens for c in range(n + 1)]
+    return Layout(tuple(q), tuple(kv), (0, n))
+
+
+def packed_chunk_draw(seed: int = 8):
+    """The packed-batch draw: 8 videos, each with 1..10 chunks of one size from
+    {256, 1536, 3840, 9360}; seed 8 is the first seed whose total lies within
+    2% of 120k tokens (121,152)."""
+    sizes = np.array([256, 1536, 3840, 9360])
+    rng = np.random.default_rng(seed)
+    n = rng.integers(1, 11, 8)
+    sz = sizes[rng.integers(0, 4, 8)]
+    return [[int(s)] * int(c) for c, s in zip(n, sz)]
+
+
+def tokens_per_chunk(height: int, width: int, frames: int = 24, patch: int = 2) -> int:
+    lat_frames = frames // 4
+    return lat_frames * (height // 8 // patch) * (width // 8 // patch)
+
+
+@dataclasses.dataclass(frozen=True)
+class Config:
+    name: str
+    layout: Layout
+    n_q_heads: int
+    n_kv_heads: int
+    head_dim: int
+    dtype: str            # "bf16" or "fp32"
+    gain_kind: str        # "ones" or "uniform" (U(0.5, 1.5))
+    seed: int
+    eps: float = 1e-6
+
+    @property
+    def scale(self) -> float:
+        return 1.0 / math.sqrt(self.head_dim)
+
+
+def _configs() -> List[Config]:
+    tiny = Config("tiny", layout_from_chunks([[64, 64, 64]]), 2, 1, 64, "fp32", "ones", 1)
+    c256 = tokens_per_chunk(256, 256)                       # 1536
+    v256 = Config("video256x2", layout_from_chunks([[c256] * 4, [c256] * 4]), 24, 8, 128, "bf16", "uniform", 2)
+    stream = Config("streaming", streaming_layout(16, 4, c256), 24, 8, 128, "bf16", "ones", 3)
+    c480 = tokens_per_chunk(480, 832)                       # 9360
+    v480 = Config("video480x832", layout_from_chunks([[c480] * 16]), 48, 8, 128, "bf16", "ones", 4)
+    packed = Config("packed8", layout_from_chunks(packed_chunk_draw(8)), 32, 8, 128, "bf16", "ones", 5)
+    return [tiny, v256, stream, v480, packed]
+
+
+CONFIGS = _configs()
+
+
+def get_config(name_or_index) -> Config:
+    if isinstance(name_or_index, int):
+        return CONFIGS[name_or_index]
+    for c in CONFIGS:
+        if c.name == name_or_index:
+            return c
+    raise KeyError(name_or_index)
