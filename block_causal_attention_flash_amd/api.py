@@ -1,0 +1,194 @@
+"""Argument marshalling for the C ABI (include/magi_attn.h); no computation here."""
+from __future__ import annotations
+
+import ctypes
+from typing import Optional, Sequence, Tuple
+
+import numpy as np
+
+from . import _abi
+
+_DTYPES = {"bf16": _abi.MAGI_DTYPE_BF16, "fp32": _abi.MAGI_DTYPE_FP32}
+
+
+class MagiAttnError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{message} (status {status})")
+        self.status = status
+        self.message = message
+
+
+def _check(lib, status: int):
+    if status != _abi.MAGI_OK:
+        msg = lib.magi_attn_last_error().decode(errors="replace")
+        raise MagiAttnError(status, msg or lib.magi_attn_status_str(status).decode())
+
+
+def _arr(x) -> np.ndarray:
+    return np.ascontiguousarray(np.asarray(x, dtype=np.int32))
+
+
+class _LayoutArgs:
+    """Keeps the host offset arrays alive for the duration of a call."""
+
+    def __init__(self, q_offsets, kv_offsets, seq_chunks, n_q_heads, n_kv_heads, head_dim, dtype):
+        self.q = _arr(q_offsets)
+        self.kv = None if kv_offsets is None else _arr(kv_offsets)
+        n_chunks = len(self.q) - 1
+        self.seq = _arr([0, n_chunks] if seq_chunks is None else seq_chunks)
+        p = lambda a: None if a is None else a.ctypes.data_as(_abi._i32p)  # noqa: E731
+        dt = _DTYPES[dtype] if isinstance(dtype, str) else int(dtype)
+        self.struct = _abi.Layout(len(self.seq) - 1, p(self.seq), n_chunks, p(self.q), p(self.kv),
+                                  int(n_q_heads), int(n_kv_heads), int(head_dim), dt)
+
+    def ptr(self):
+        return ctypes.byref(self.struct)
+
+
+def magi_attn_abi_version() -> int:
+    return _abi.load().magi_attn_abi_version()
+
+
+def magi_attn_plan_stats(q_offsets, kv_offsets=None, seq_chunks=None, n_q_heads=1, n_kv_heads=1, head_dim=128,
+                         dtype="bf16") -> dict:
+    lib = _abi.load()
+    la = _LayoutArgs(q_offsets, kv_offsets, seq_chunks, n_q_heads, n_kv_heads, head_dim, dtype)
+    st = _abi.Stats()
+    _check(lib, lib.magi_attn_plan_stats(la.ptr(), ctypes.byref(st)))
+    return {name: getattr(st, name) for name, _ in _abi.Stats._fields_}
+
+
+def magi_attn_classify_host(q_offsets, kv_offsets=None, seq_chunks=None, bm=128, bn=64, n_q_heads=1, n_kv_heads=1,
+                            head_dim=128, dtype="bf16") -> np.ndarray:
+    lib = _abi.load()
+    la = _LayoutArgs(q_offsets, kv_offsets, seq_chunks, n_q_heads, n_kv_heads, head_dim, dtype)
+    tq = int(la.q[-1])
+    tk = int((la.kv if la.kv is not None else la.q)[-1])
+    n_qt, n_kt = -(-tq // bm), -(-tk // bn)
+    cls = np.zeros((max(n_qt, 0), max(n_kt, 0)), dtype=np.int8)
+    _check(lib, lib.magi_attn_classify_host(la.ptr(), bm, bn, cls.ctypes.data_as(ctypes.POINTER(ctypes.c_int8))))
+    return cls
+
+
+def magi_attn_plan_create(q_offsets, kv_offsets=None, seq_chunks=None, n_q_heads=1, n_kv_heads=1, head_dim=128,
+                          dtype="bf16") -> int:
+    """Returns the opaque plan handle (an integer address)."""
+    lib = _abi.load()
+    la = _LayoutArgs(q_offsets, kv_offsets, seq_chunks, n_q_heads, n_kv_heads, head_dim, dtype)
+    h = ctypes.c_void_p()
+    _check(lib, lib.magi_attn_plan_create(la.ptr(), ctypes.byref(h)))
+    return h.value
+
+
+def magi_attn_plan_destroy(handle: int) -> None:
+    lib = _abi.load()
+    _check(lib, lib.magi_attn_plan_destroy(handle))
+
+
+def _stream_ptr(stream, device):
+    import torch
+    s = torch.cuda.current_stream(device) if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _gain(g, d, device):
+    import torch
+    if g is None:
+        return torch.ones(d, dtype=torch.float32, device=device)
+    g = g.to(device=device, dtype=torch.float32).contiguous()
+    if g.shape != (d,):
+        raise ValueError(f"gain must have shape ({d},)")
+    return g
+
+
+def magi_attn_fwd(handle: int, q, k, v, q_gain=None, k_gain=None, rms_eps: float = 1e-6,
+                  scale: Optional[float] = None, out=None, lse=None, stream=None):
+    """Enqueues the forward on `stream` (default: torch's current stream).
+    q [T_q,H_q,d], k/v [T_k,H_kv,d] on the GPU; returns (out, lse)."""
+    import torch
+    lib = _abi.load()
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if not t.is_cuda or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous GPU tensor")
+    d = q.shape[-1]
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((q.shape[1], q.shape[0]), dtype=torch.float32, device=q.device)
+    qg = _gain(q_gain, d, q.device)
+    kg = _gain(k_gain, d, q.device)
+    sc = (1.0 / d ** 0.5) if scale is None else float(scale)
+    _check(lib, lib.magi_attn_fwd(handle, q.data_ptr(), k.data_ptr(), v.data_ptr(), qg.data_ptr(), kg.data_ptr(),
+                                  float(rms_eps), sc, out.data_ptr(), lse.data_ptr(), _stream_ptr(stream, q.device)))
+    return out, lse
+
+
+def magi_attn_fwd_simple(q, k, v, chunk_offsets: Sequence[int], q_gain=None, k_gain=None, rms_eps: float = 1e-6,
+                         scale: Optional[float] = None, out=None, lse=None, stream=None):
+    """One video of self-attention with q/kv offsets = chunk_offsets."""
+    import torch
+    lib = _abi.load()
+    offs = _arr(chunk_offsets)
+    d = q.shape[-1]
+    dt = {torch.bfloat16: _abi.MAGI_DTYPE_BF16, torch.float32: _abi.MAGI_DTYPE_FP32}[q.dtype]
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((q.shape[1], q.shape[0]), dtype=torch.float32, device=q.device)
+    qg = _gain(q_gain, d, q.device)
+    kg = _gain(k_gain, d, q.device)
+    sc = (1.0 / d ** 0.5) if scale is None else float(scale)
+    _check(lib, lib.magi_attn_fwd_simple(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
+                                         offs.ctypes.data_as(_abi._i32p), len(offs) - 1, q.shape[1], k.shape[1], d, dt,
+                                         qg.data_ptr(), kg.data_ptr(), float(rms_eps), sc,
+                                         _stream_ptr(stream, q.device)))
+    return out, lse
+
+
+class Plan:
+    """Owns a plan handle for one layout; call() runs the forward."""
+
+    def __init__(self, q_offsets, kv_offsets=None, seq_chunks=None, n_q_heads=1, n_kv_heads=1, head_dim=128,
+                 dtype="bf16"):
+        self.layout = dict(q_offsets=list(map(int, q_offsets)),
+                           kv_offsets=None if kv_offsets is None else list(map(int, kv_offsets)),
+                           seq_chunks=None if seq_chunks is None else list(map(int, seq_chunks)),
+                           n_q_heads=n_q_heads, n_kv_heads=n_kv_heads, head_dim=head_dim, dtype=dtype)
+        self.n_q_heads, self.n_kv_heads, self.head_dim, self.dtype = n_q_heads, n_kv_heads, head_dim, dtype
+        self.t_q = int(self.layout["q_offsets"][-1])
+        kv = self.layout["kv_offsets"] or self.layout["q_offsets"]
+        self.t_k = int(kv[-1])
+        self.handle = magi_attn_plan_create(**self.layout)
+
+    @classmethod
+    def from_layout(cls, layout, n_q_heads, n_kv_heads, head_dim, dtype="bf16"):
+        return cls(layout.q_offsets, layout.kv_offsets, layout.seq_chunks, n_q_heads, n_kv_heads, head_dim, dtype)
+
+    def stats(self) -> dict:
+        return magi_attn_plan_stats(**self.layout)
+
+    def __call__(self, q, k, v, q_gain=None, k_gain=None, rms_eps=1e-6, scale=None, out=None, lse=None, stream=None):
+        import torch
+        want = torch.bfloat16 if self.dtype == "bf16" else torch.float32
+        if q.dtype != want or k.dtype != want or v.dtype != want:
+            raise ValueError(f"q, k, v must be {want}")
+        if tuple(q.shape) != (self.t_q, self.n_q_heads, self.head_dim):
+            raise ValueError(f"q must have shape {(self.t_q, self.n_q_heads, self.head_dim)}")
+        if tuple(k.shape) != (self.t_k, self.n_kv_heads, self.head_dim) or k.shape != v.shape:
+            raise ValueError(f"k and v must have shape {(self.t_k, self.n_kv_heads, self.head_dim)}")
+        if out is not None and (out.shape != q.shape or out.dtype != want or not out.is_contiguous()):
+            raise ValueError("out must match q")
+        if lse is not None and (tuple(lse.shape) != (self.n_q_heads, self.t_q) or lse.dtype != torch.float32):
+            raise ValueError("lse must be float32 [H_q, T_q]")
+        return magi_attn_fwd(self.handle, q, k, v, q_gain, k_gain, rms_eps, scale, out, lse, stream)
+
+    def close(self):
+        if self.handle:
+            magi_attn_plan_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass

@@ -1,0 +1,226 @@
+// C ABI of the block-causal attention forward (declared in include/magi_attn.h).
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+#include <new>
+#include <string>
+
+#include "kernels.hpp"
+#include "magi_attn.h"
+#include "plan.hpp"
+
+struct magi_attn_plan {
+  magi::HostPlan host;
+  int device = 0;
+  void* dmem = nullptr;          // one allocation: items | segments | row bounds
+  const int4* d_items = nullptr;
+  const int4* d_segs = nullptr;
+  const int2* d_rows = nullptr;
+};
+
+namespace {
+
+thread_local std::string g_last_error;
+
+magi_status_t fail(magi_status_t s, const std::string& msg) {
+  g_last_error = msg;
+  return s;
+}
+
+magi_status_t hip_fail(hipError_t e, const char* what) {
+  return fail(MAGI_ERR_HIP, std::string(what) + ": " + hipGetErrorString(e));
+}
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+}  // namespace
+
+extern "C" {
+
+int magi_attn_abi_version(void) { return MAGI_ATTN_ABI_VERSION; }
+
+const char* magi_attn_status_str(magi_status_t s) {
+  switch (s) {
+    case MAGI_OK: return "ok";
+    case MAGI_ERR_INVALID_ARG: return "invalid argument";
+    case MAGI_ERR_UNSUPPORTED: return "unsupported";
+    case MAGI_ERR_NO_MEMORY: return "out of memory";
+    case MAGI_ERR_HIP: return "HIP error";
+  }
+  return "unknown status";
+}
+
+const char* magi_attn_last_error(void) { return g_last_error.c_str(); }
+
+magi_status_t magi_attn_classify_host(const magi_attn_layout_t* layout, int32_t bm, int32_t bn, int8_t* cls) {
+  std::string err;
+  magi_status_t s = magi::validate_layout(layout, err);
+  if (s != MAGI_OK) return fail(s, err);
+  if (bm < 1 || bn < 1) return fail(MAGI_ERR_INVALID_ARG, "tile sizes must be positive");
+  if (!cls) return fail(MAGI_ERR_INVALID_ARG, "cls is NULL");
+  std::vector<magi::RowBounds> rows;
+  magi::row_bounds(layout, rows);
+  const int32_t* kv = layout->kv_offsets ? layout->kv_offsets : layout->q_offsets;
+  const int64_t tq = layout->q_offsets[layout->n_chunks], tk = kv[layout->n_chunks];
+  const int64_t n_qt = (tq + bm - 1) / bm, n_kt = (tk + bn - 1) / bn;
+  std::vector<magi::RowBounds> iv;
+  for (int64_t qt = 0; qt < n_qt; ++qt) {
+    magi::tile_intervals(rows, qt * bm, std::min<int64_t>(tq, qt * bm + bm), iv);
+    for (int64_t kt = 0; kt < n_kt; ++kt)
+      cls[qt * n_kt + kt] = int8_t(magi::classify_pair(iv, kt * bn, kt * bn + bn, tk));
+  }
+  return MAGI_OK;
+}
+
+magi_status_t magi_attn_plan_stats(const magi_attn_layout_t* layout, magi_attn_stats_t* stats) {
+  std::string err;
+  magi_status_t s = magi::validate_layout(layout, err);
+  if (s != MAGI_OK) return fail(s, err);
+  if (!stats) return fail(MAGI_ERR_INVALID_ARG, "stats is NULL");
+  magi::HostPlan hp;
+  const magi::Tiling t = magi::choose_tiling(layout->dtype, layout->head_dim, layout->n_q_heads / layout->n_kv_heads);
+  try {
+    s = magi::build_host_plan(layout, t, hp, err);
+  } catch (const std::bad_alloc&) {
+    return fail(MAGI_ERR_NO_MEMORY, "host allocation failed");
+  }
+  if (s != MAGI_OK) return fail(s, err);
+  *stats = hp.stats;
+  return MAGI_OK;
+}
+
+magi_status_t magi_attn_plan_create(const magi_attn_layout_t* layout, magi_attn_plan_t** out_plan) {
+  if (!out_plan) return fail(MAGI_ERR_INVALID_ARG, "plan output pointer is NULL");
+  *out_plan = nullptr;
+  std::string err;
+  magi_status_t s = magi::validate_layout(layout, err);
+  if (s != MAGI_OK) return fail(s, err);
+  magi_attn_plan* p = new (std::nothrow) magi_attn_plan();
+  if (!p) return fail(MAGI_ERR_NO_MEMORY, "host allocation failed");
+  const magi::Tiling t = magi::choose_tiling(layout->dtype, layout->head_dim, layout->n_q_heads / layout->n_kv_heads);
+  try {
+    s = magi::build_host_plan(layout, t, p->host, err);
+  } catch (const std::bad_alloc&) {
+    delete p;
+    return fail(MAGI_ERR_NO_MEMORY, "host allocation failed");
+  }
+  if (s != MAGI_OK) { delete p; return fail(s, err); }
+
+  const auto& H = p->host;
+  const size_t b_items = H.items.size() * sizeof(magi::WorkItem);
+  const size_t b_segs = H.segs.size() * sizeof(magi::Segment);
+  const size_t b_rows = H.rows.size() * sizeof(magi::RowBounds);
+  const size_t o_segs = round_up(b_items, 256), o_rows = o_segs + round_up(b_segs, 256);
+  const size_t total = std::max<size_t>(o_rows + b_rows, 256);
+  hipError_t e = hipGetDevice(&p->device);
+  if (e != hipSuccess) { delete p; return hip_fail(e, "hipGetDevice"); }
+  e = hipMalloc(&p->dmem, total);
+  if (e != hipSuccess) {
+    delete p;
+    return e == hipErrorOutOfMemory ? fail(MAGI_ERR_NO_MEMORY, "hipMalloc of the plan failed") : hip_fail(e, "hipMalloc");
+  }
+  char* base = static_cast<char*>(p->dmem);
+  if (b_items) e = hipMemcpy(base, H.items.data(), b_items, hipMemcpyHostToDevice);
+  if (e == hipSuccess && b_segs) e = hipMemcpy(base + o_segs, H.segs.data(), b_segs, hipMemcpyHostToDevice);
+  if (e == hipSuccess && b_rows) e = hipMemcpy(base + o_rows, H.rows.data(), b_rows, hipMemcpyHostToDevice);
+  if (e != hipSuccess) {
+    (void)hipFree(p->dmem);
+    delete p;
+    return hip_fail(e, "hipMemcpy of the plan");
+  }
+  p->d_items = reinterpret_cast<const int4*>(base);
+  p->d_segs = reinterpret_cast<const int4*>(base + o_segs);
+  p->d_rows = reinterpret_cast<const int2*>(base + o_rows);
+  *out_plan = p;
+  return MAGI_OK;
+}
+
+magi_status_t magi_attn_plan_destroy(magi_attn_plan_t* plan) {
+  if (!plan) return MAGI_OK;
+  magi_status_t s = MAGI_OK;
+  if (plan->dmem) {
+    hipError_t e = hipFree(plan->dmem);
+    if (e != hipSuccess) s = hip_fail(e, "hipFree of the plan");
+  }
+  delete plan;
+  return s;
+}
+
+magi_status_t magi_attn_fwd(const magi_attn_plan_t* plan, const void* q, const void* k, const void* v,
+                            const float* q_gain, const float* k_gain, float rms_eps, float scale, void* out,
+                            float* lse, void* stream) {
+  if (!plan) return fail(MAGI_ERR_INVALID_ARG, "plan is NULL");
+  const auto& H = plan->host;
+  if (H.items.empty()) return MAGI_OK;                     // no query token: nothing to do
+  if (!q || !k || !v || !out || !lse || !q_gain || !k_gain)
+    return fail(MAGI_ERR_INVALID_ARG, "NULL tensor pointer");
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16))
+    return fail(MAGI_ERR_INVALID_ARG, "q, k, v and out must be 16-byte aligned");
+  if (!aligned(lse, 4) || !aligned(q_gain, 16) || !aligned(k_gain, 16))
+    return fail(MAGI_ERR_INVALID_ARG, "lse must be 4-byte and the gains 16-byte aligned");
+  if (!(rms_eps >= 0.0f) || !std::isfinite(rms_eps)) return fail(MAGI_ERR_INVALID_ARG, "rms_eps must be finite and >= 0");
+  if (!(scale > 0.0f) || !std::isfinite(scale)) return fail(MAGI_ERR_INVALID_ARG, "scale must be finite and > 0");
+
+  magi::FwdParams prm{};
+  prm.q = q;
+  prm.k = k;
+  prm.v = v;
+  prm.out = out;
+  prm.lse = lse;
+  prm.q_gain = q_gain;
+  prm.k_gain = k_gain;
+  prm.items = plan->d_items;
+  prm.segs = plan->d_segs;
+  prm.rows = plan->d_rows;
+  prm.eps = rms_eps;
+  prm.scale = scale;
+  prm.tq = int(H.tq);
+  prm.tk = int(H.tk);
+  prm.hq = H.hq;
+  prm.hk = H.hk;
+  prm.tile_q = H.tiling.tile_q;
+  prm.heads_per_item = H.tiling.heads_per_item;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const int n = int(H.items.size());
+  hipError_t e;
+  if (H.dtype == MAGI_DTYPE_BF16) e = magi::launch_fwd_bf16_d128(prm, n, st);
+  else e = magi::launch_fwd_fp32(prm, H.d, n, st);
+  if (e != hipSuccess) return hip_fail(e, "kernel launch");
+  return MAGI_OK;
+}
+
+magi_status_t magi_attn_fwd_simple(const void* q, const void* k, const void* v, void* out, float* lse,
+                                   const int32_t* chunk_offsets, int32_t n_chunks, int32_t n_q_heads,
+                                   int32_t n_kv_heads, int32_t head_dim, int32_t dtype, const float* q_gain,
+                                   const float* k_gain, float rms_eps, float scale, void* stream) {
+  if (!chunk_offsets) return fail(MAGI_ERR_INVALID_ARG, "chunk_offsets is NULL");
+  const int32_t seq[2] = {0, n_chunks};
+  magi_attn_layout_t L{};
+  L.n_seqs = 1;
+  L.seq_chunks = seq;
+  L.n_chunks = n_chunks;
+  L.q_offsets = chunk_offsets;
+  L.kv_offsets = chunk_offsets;
+  L.n_q_heads = n_q_heads;
+  L.n_kv_heads = n_kv_heads;
+  L.head_dim = head_dim;
+  L.dtype = dtype;
+  magi_attn_plan_t* plan = nullptr;
+  magi_status_t s = magi_attn_plan_create(&L, &plan);
+  if (s != MAGI_OK) return s;
+  s = magi_attn_fwd(plan, q, k, v, q_gain, k_gain, rms_eps, scale, out, lse, stream);
+  if (s == MAGI_OK) {
+    hipError_t e = hipStreamSynchronize(static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) s = hip_fail(e, "hipStreamSynchronize");
+  }
+  const std::string keep = g_last_error;
+  magi_status_t d = magi_attn_plan_destroy(plan);
+  if (s != MAGI_OK) { g_last_error = keep; return s; }
+  return d;
+}
+
+}  // extern "C"

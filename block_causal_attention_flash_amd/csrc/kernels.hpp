@@ -1,0 +1,29 @@
+// Kernel launch interface shared by the C ABI and the HIP kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <cstdint>
+
+namespace magi {
+
+struct FwdParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* out;
+  float* lse;
+  const float* q_gain;
+  const float* k_gain;
+  const int4* items;     // WorkItem[n_items]
+  const int4* segs;      // Segment[]
+  const int2* rows;      // RowBounds[tq]
+  float eps;
+  float scale;           // softmax temperature on <q_hat, k_hat>
+  int tq, tk, hq, hk;
+  int tile_q, heads_per_item;
+};
+
+hipError_t launch_fwd_bf16_d128(const FwdParams& p, int n_items, hipStream_t stream);
+hipError_t launch_fwd_fp32(const FwdParams& p, int head_dim, int n_items, hipStream_t stream);
+
+}  // namespace magi

@@ -1,0 +1,248 @@
+// Host-side planning: validation, tile classification, work list.
+//
+// The mask is the MAGI-1 block-causal rule (paperlayer summary §2 / Figure 1,
+// paper-notes §2 / Figure 1): a query of chunk c in video s attends to the
+// keys [kv_offsets[first chunk of s], kv_offsets[c + 1]), i.e. its own chunk
+// in full and every earlier chunk of the same video; nothing of other videos
+// (paper-notes Figure 15, varlen block-causal). Every query token therefore
+// has one contiguous key interval [lo, hi), and a (query tile, key tile) pair
+// is "full" when every row's interval covers the key tile, "empty" when no
+// row's interval touches it, and "boundary" otherwise. Empty pairs are never
+// launched; only boundary pairs pay for the per-element mask.
+//
+// Work order: the pages' dispatch solver sorts chunks by descending area and
+// hands each to the least-loaded bucket (paperlayer §B.1). The same
+// longest-first rule orders the workgroups of one GPU, with one bucket per
+// XCD: workgroup i runs on XCD i % 8, so items that stream the same KV head
+// are placed on the same XCD and share its L2.
+#include "plan.hpp"
+
+#include <algorithm>
+#include <cstring>
+#include <numeric>
+
+namespace magi {
+
+namespace {
+
+bool supported(int dtype, int d) {
+  if (dtype == MAGI_DTYPE_BF16) return d == 128;
+  if (dtype == MAGI_DTYPE_FP32) return d == 64 || d == 128;
+  return false;
+}
+
+}  // namespace
+
+magi_status_t validate_layout(const magi_attn_layout_t* L, std::string& err) {
+  if (!L) { err = "layout is NULL"; return MAGI_ERR_INVALID_ARG; }
+  if (L->n_chunks < 1) { err = "n_chunks must be >= 1"; return MAGI_ERR_INVALID_ARG; }
+  if (L->n_seqs < 1) { err = "n_seqs must be >= 1"; return MAGI_ERR_INVALID_ARG; }
+  if (!L->seq_chunks || !L->q_offsets) { err = "seq_chunks and q_offsets must not be NULL"; return MAGI_ERR_INVALID_ARG; }
+  const int32_t* kv = L->kv_offsets ? L->kv_offsets : L->q_offsets;
+  if (L->seq_chunks[0] != 0 || L->seq_chunks[L->n_seqs] != L->n_chunks) {
+    err = "seq_chunks must start at 0 and end at n_chunks"; return MAGI_ERR_INVALID_ARG;
+  }
+  for (int s = 0; s < L->n_seqs; ++s)
+    if (L->seq_chunks[s + 1] <= L->seq_chunks[s]) { err = "seq_chunks must be strictly increasing"; return MAGI_ERR_INVALID_ARG; }
+  if (L->q_offsets[0] != 0 || kv[0] != 0) { err = "q_offsets and kv_offsets must start at 0"; return MAGI_ERR_INVALID_ARG; }
+  for (int c = 0; c < L->n_chunks; ++c) {
+    if (L->q_offsets[c + 1] < L->q_offsets[c]) { err = "q_offsets must be non-decreasing"; return MAGI_ERR_INVALID_ARG; }
+    if (kv[c + 1] < kv[c]) { err = "kv_offsets must be non-decreasing"; return MAGI_ERR_INVALID_ARG; }
+  }
+  for (int s = 0; s < L->n_seqs; ++s) {
+    const int32_t lo = kv[L->seq_chunks[s]];
+    for (int c = L->seq_chunks[s]; c < L->seq_chunks[s + 1]; ++c)
+      if (L->q_offsets[c + 1] > L->q_offsets[c] && kv[c + 1] <= lo) {
+        err = "chunk " + std::to_string(c) + " owns queries but sees no key"; return MAGI_ERR_INVALID_ARG;
+      }
+  }
+  if (L->n_q_heads < 1 || L->n_kv_heads < 1 || L->n_q_heads % L->n_kv_heads != 0) {
+    err = "n_q_heads must be a positive multiple of n_kv_heads"; return MAGI_ERR_INVALID_ARG;
+  }
+  if (L->n_q_heads >= 65536) { err = "n_q_heads too large"; return MAGI_ERR_UNSUPPORTED; }
+  if (L->dtype != MAGI_DTYPE_BF16 && L->dtype != MAGI_DTYPE_FP32) { err = "unknown dtype"; return MAGI_ERR_INVALID_ARG; }
+  if (L->head_dim < 1) { err = "head_dim must be positive"; return MAGI_ERR_INVALID_ARG; }
+  if (!supported(L->dtype, L->head_dim)) {
+    err = "unsupported head_dim " + std::to_string(L->head_dim) + " for this dtype (bf16: 128; fp32: 64, 128)";
+    return MAGI_ERR_UNSUPPORTED;
+  }
+  const int64_t esize = L->dtype == MAGI_DTYPE_BF16 ? 2 : 4;
+  const int64_t kv_bytes = int64_t(kv[L->n_chunks]) * L->n_kv_heads * L->head_dim * esize;
+  const int64_t q_elems = int64_t(L->q_offsets[L->n_chunks]) * L->n_q_heads;
+  if (kv_bytes >= (int64_t(1) << 32)) { err = "K/V tensors must be smaller than 4 GiB each"; return MAGI_ERR_UNSUPPORTED; }
+  if (q_elems >= (int64_t(1) << 31)) { err = "T_q * n_q_heads must be below 2^31"; return MAGI_ERR_UNSUPPORTED; }
+  return MAGI_OK;
+}
+
+Tiling choose_tiling(int dtype, int head_dim, int group) {
+  (void)head_dim;
+  Tiling t{};
+  if (dtype == MAGI_DTYPE_BF16) {
+    // 256 (token, head) rows per workgroup: 8 waves x 32 rows. As many query
+    // heads of the GQA group as divide it (power of two, <= 8) share one
+    // workgroup, so one K/V tile in LDS serves all of them.
+    int hpw = 1;
+    while (hpw < 8 && group % (hpw * 2) == 0) hpw *= 2;
+    t.heads_per_item = hpw;
+    t.tile_q = 256 / hpw;
+    t.tile_kv = 64;
+  } else {
+    t.heads_per_item = 1;
+    t.tile_q = 64;
+    t.tile_kv = 32;
+  }
+  return t;
+}
+
+void row_bounds(const magi_attn_layout_t* L, std::vector<RowBounds>& rows) {
+  const int32_t* kv = L->kv_offsets ? L->kv_offsets : L->q_offsets;
+  rows.assign(L->q_offsets[L->n_chunks], RowBounds{0, 0});
+  for (int s = 0; s < L->n_seqs; ++s) {
+    const int32_t lo = kv[L->seq_chunks[s]];
+    for (int c = L->seq_chunks[s]; c < L->seq_chunks[s + 1]; ++c)
+      for (int32_t t = L->q_offsets[c]; t < L->q_offsets[c + 1]; ++t) rows[t] = RowBounds{lo, kv[c + 1]};
+  }
+}
+
+void tile_intervals(const std::vector<RowBounds>& rows, int64_t r0, int64_t r1, std::vector<RowBounds>& out) {
+  out.clear();
+  for (int64_t r = r0; r < r1; ++r) {
+    const RowBounds b = rows[r];
+    if (out.empty() || out.back().lo != b.lo || out.back().hi != b.hi) out.push_back(b);
+  }
+}
+
+int classify_pair(const std::vector<RowBounds>& iv, int64_t k0, int64_t k1, int64_t tk) {
+  bool all = true, any = false;
+  for (const RowBounds& b : iv) {
+    const int64_t lo = b.lo, hi = std::min<int64_t>(b.hi, tk);
+    if (!(lo <= k0 && k1 <= hi)) all = false;
+    if (lo < k1 && k0 < hi) any = true;
+  }
+  if (iv.empty()) return 0;
+  return all ? 2 : (any ? 1 : 0);
+}
+
+magi_status_t build_host_plan(const magi_attn_layout_t* L, const Tiling& tiling, HostPlan& P, std::string& err) {
+  (void)err;
+  const int32_t* kv = L->kv_offsets ? L->kv_offsets : L->q_offsets;
+  P.n_chunks = L->n_chunks;
+  P.n_seqs = L->n_seqs;
+  P.hq = L->n_q_heads;
+  P.hk = L->n_kv_heads;
+  P.d = L->head_dim;
+  P.dtype = L->dtype;
+  P.tq = L->q_offsets[L->n_chunks];
+  P.tk = kv[L->n_chunks];
+  P.tiling = tiling;
+  row_bounds(L, P.rows);
+
+  const int bm = tiling.tile_q, bn = tiling.tile_kv;
+  const int64_t n_qt = (P.tq + bm - 1) / bm;
+  const int64_t n_kt = (P.tk + bn - 1) / bn;
+  const int group = P.hq / P.hk;
+  const int hpw = tiling.heads_per_item;
+  const int groups_per_kvh = group / hpw;
+
+  magi_attn_stats_t& S = P.stats;
+  std::memset(&S, 0, sizeof(S));
+  for (const RowBounds& b : P.rows) S.unmasked_pairs += int64_t(b.hi - b.lo);
+
+  P.segs.clear();
+  P.qt_seg.assign(n_qt + 1, 0);
+  std::vector<int64_t> qt_cost(n_qt, 0);
+  std::vector<RowBounds> iv;
+  for (int64_t qt = 0; qt < n_qt; ++qt) {
+    const int64_t r0 = qt * bm, r1 = std::min<int64_t>(P.tq, r0 + bm);
+    tile_intervals(P.rows, r0, r1, iv);
+    int64_t lo = INT64_MAX, hi = 0;
+    for (const RowBounds& b : iv) { lo = std::min<int64_t>(lo, b.lo); hi = std::max<int64_t>(hi, b.hi); }
+    P.qt_seg[qt] = int32_t(P.segs.size());
+    if (hi > lo) {
+      const int64_t kt0 = lo / bn, kt1 = (hi + bn - 1) / bn;
+      int prev = -1;
+      for (int64_t kt = kt0; kt < kt1; ++kt) {
+        const int cls = classify_pair(iv, kt * bn, kt * bn + bn, P.tk);
+        if (cls == 2) ++S.full_pairs;
+        if (cls == 1) ++S.boundary_pairs;
+        if (cls != 0) {
+          const int masked = cls == 1 ? 1 : 0;
+          if (prev == masked && P.segs.back().kt_end == kt) {
+            P.segs.back().kt_end = int32_t(kt + 1);
+          } else {
+            P.segs.push_back(Segment{int32_t(kt), int32_t(kt + 1), masked, 0});
+          }
+          qt_cost[qt] += 1;
+          S.executed_pairs += (r1 - r0) * int64_t(bn);
+          prev = masked;
+        } else {
+          prev = -1;
+        }
+      }
+    }
+  }
+  P.qt_seg[n_qt] = int32_t(P.segs.size());
+  S.empty_pairs = n_qt * n_kt - S.full_pairs - S.boundary_pairs;
+
+  // Work items: (query tile, KV head, group of hpw query heads).
+  struct Cand { int64_t cost; int32_t qt, kvh, hg; };
+  std::vector<Cand> cands;
+  cands.reserve(size_t(n_qt) * P.hk * groups_per_kvh);
+  for (int kvh = 0; kvh < P.hk; ++kvh)
+    for (int64_t qt = 0; qt < n_qt; ++qt) {
+      if (P.qt_seg[qt + 1] == P.qt_seg[qt]) continue;
+      for (int hg = 0; hg < groups_per_kvh; ++hg) cands.push_back(Cand{qt_cost[qt], int32_t(qt), kvh, hg});
+    }
+  // Longest first; among equals, consecutive query tiles and head groups of
+  // one KV head stay adjacent so concurrently running workgroups read the
+  // same key tiles.
+  std::stable_sort(cands.begin(), cands.end(), [](const Cand& a, const Cand& b) {
+    if (a.cost != b.cost) return a.cost > b.cost;
+    if (a.kvh != b.kvh) return a.kvh < b.kvh;
+    if (a.qt != b.qt) return a.qt < b.qt;
+    return a.hg < b.hg;
+  });
+  std::vector<std::vector<WorkItem>> queues(kNumXcd);
+  std::vector<int64_t> load(kNumXcd, 0);
+  auto make_item = [&](const Cand& c) {
+    const int h0 = c.kvh * group + c.hg * hpw;
+    return WorkItem{int32_t(c.qt * bm), (c.kvh << 16) | h0, P.qt_seg[c.qt], P.qt_seg[c.qt + 1]};
+  };
+  if (P.hk % kNumXcd == 0 || kNumXcd % P.hk == 0) {
+    // Each KV head owns a fixed set of XCDs (or each XCD owns a fixed set of
+    // KV heads); longest-first to the least-loaded XCD of that set.
+    const int per_head = P.hk >= kNumXcd ? 1 : kNumXcd / P.hk;
+    for (const Cand& c : cands) {
+      int best = -1;
+      for (int j = 0; j < per_head; ++j) {
+        const int x = (P.hk >= kNumXcd) ? (c.kvh % kNumXcd) : (c.kvh * per_head + j);
+        if (best < 0 || load[x] < load[best]) best = x;
+      }
+      queues[best].push_back(make_item(c));
+      load[best] += c.cost;
+    }
+  } else {
+    for (const Cand& c : cands) {
+      const int best = int(std::min_element(load.begin(), load.end()) - load.begin());
+      queues[best].push_back(make_item(c));
+      load[best] += c.cost;
+    }
+  }
+  size_t maxlen = 0;
+  for (auto& q : queues) maxlen = std::max(maxlen, q.size());
+  P.items.clear();
+  P.items.reserve(maxlen * kNumXcd);
+  for (size_t j = 0; j < maxlen; ++j)
+    for (int x = 0; x < kNumXcd; ++x)
+      P.items.push_back(j < queues[x].size() ? queues[x][j] : WorkItem{0, 0, 0, 0});
+  // Drop trailing padding.
+  while (!P.items.empty() && P.items.back().seg_begin == P.items.back().seg_end) P.items.pop_back();
+
+  S.tile_q = bm;
+  S.tile_kv = bn;
+  S.heads_per_item = hpw;
+  S.n_items = int32_t(P.items.size());
+  return MAGI_OK;
+}
+
+}  // namespace magi

@@ -1,0 +1,77 @@
+// Host-side planning for the block-causal attention forward: layout
+// validation, tile classification and the GPU work list.
+#pragma once
+
+#include <cstdint>
+#include <string>
+#include <vector>
+
+#include "magi_attn.h"
+
+namespace magi {
+
+// One workgroup's work: query tokens [t0, t0 + tile_q) of `heads_per_item`
+// consecutive query heads starting at h0, all of KV head kvh, over the key
+// tiles listed in segments [seg_begin, seg_end).
+struct WorkItem {
+  int32_t t0;
+  int32_t heads;       // (kvh << 16) | h0
+  int32_t seg_begin;
+  int32_t seg_end;     // == seg_begin: padding item, the workgroup exits at once
+};
+
+// A run of consecutive key tiles of one class for one query tile.
+struct Segment {
+  int32_t kt_begin;
+  int32_t kt_end;
+  int32_t masked;      // 1: boundary tiles (row-dependent key bounds); 0: full
+  int32_t pad;
+};
+
+// Key bounds of one query token: it attends keys [lo, hi).
+struct RowBounds {
+  int32_t lo;
+  int32_t hi;
+};
+
+struct Tiling {
+  int tile_q;          // query tokens per workgroup
+  int tile_kv;         // keys per key tile
+  int heads_per_item;  // query heads per workgroup
+};
+
+struct HostPlan {
+  int n_chunks = 0, n_seqs = 0;
+  int hq = 0, hk = 0, d = 0, dtype = 0;
+  int64_t tq = 0, tk = 0;
+  Tiling tiling{};
+  std::vector<RowBounds> rows;       // [tq]
+  std::vector<Segment> segs;         // all query tiles' segments, concatenated
+  std::vector<int32_t> qt_seg;       // [n_qt + 1] segment range per query tile
+  std::vector<WorkItem> items;       // launch order (XCD-interleaved, padded)
+  magi_attn_stats_t stats{};
+};
+
+// Returns MAGI_OK or an error with a message in `err`.
+magi_status_t validate_layout(const magi_attn_layout_t* layout, std::string& err);
+
+// Tiling used by the kernels for a dtype / head_dim / GQA group size.
+Tiling choose_tiling(int dtype, int head_dim, int group);
+
+// Builds the full host plan (the layout must already be valid).
+magi_status_t build_host_plan(const magi_attn_layout_t* layout, const Tiling& tiling, HostPlan& plan,
+                              std::string& err);
+
+// Per-query-token key bounds [lo, hi) (layout must be valid).
+void row_bounds(const magi_attn_layout_t* layout, std::vector<RowBounds>& rows);
+
+// Class of the pair (query tile rows [r0, r1), key tile [k0, k1)) given the
+// distinct key intervals of those rows: 2 full, 1 boundary, 0 empty.
+int classify_pair(const std::vector<RowBounds>& intervals, int64_t k0, int64_t k1, int64_t tk);
+
+// Distinct consecutive key intervals of query rows [r0, r1).
+void tile_intervals(const std::vector<RowBounds>& rows, int64_t r0, int64_t r1, std::vector<RowBounds>& out);
+
+constexpr int kNumXcd = 8;
+
+}  // namespace magi

@@ -1,0 +1,174 @@
+/*
+ * magi_attn.h -- C ABI of an MI355X (gfx950) block-causal attention forward.
+ *
+ * The operation (MAGI-1 pages): the self-attention of a chunk-wise
+ * autoregressive video diffusion transformer over packed video-chunk tokens.
+ *   - paperlayer summary §2 and Figure 1; paper-notes §2 and its Figure 1:
+ *     attention is bidirectional among the tokens of one chunk and causal
+ *     across chunks (a chunk sees itself and all earlier chunks of its video);
+ *   - paper-notes Figure 15 ("varlen block-causal"): several videos packed in
+ *     one token stream never attend to each other;
+ *   - paperlayer §2.2.2, paper-notes §3.2.2 (architecture list and the DiT block
+ *     pseudocode): queries and keys are normalised per head right before the
+ *     attention ("QK-Norm"), and query heads share key/value heads (GQA);
+ *   - paperlayer §2.4.4: keys/values of clean chunks come from a KV cache, so
+ *     the key stream may be longer than the query stream.
+ *
+ * Per query token i of chunk c (video s) and query head h, with KV head
+ * g = h / (n_q_heads / n_kv_heads):
+ *   q_hat = q * q_gain / sqrt(mean_d(q^2) + eps),  k_hat likewise with k_gain,
+ *   s_ij  = scale * <q_hat_ih, k_hat_jg> for keys j in
+ *           [kv_offsets[seq_chunks[s]], kv_offsets[c + 1]),
+ *   out_ih = sum_j softmax_j(s_ij) v_jg,   lse_hi = ln sum_j exp(s_ij).
+ *
+ * Conventions shared by every entry point:
+ *   - Every function returns a magi_status_t; nothing aborts or throws across
+ *     the ABI. magi_attn_last_error() returns a per-thread detail message.
+ *   - Device tensors are caller-owned, contiguous, 16-byte aligned:
+ *       q, out : [T_q][n_q_heads][head_dim]    (T_q = q_offsets[n_chunks])
+ *       k, v   : [T_k][n_kv_heads][head_dim]   (T_k = kv_offsets[n_chunks])
+ *       lse    : [n_q_heads][T_q] float32 (natural log)
+ *       q_gain, k_gain : [head_dim] float32
+ *     q, k, v and out share the element type of the layout (bf16 or fp32).
+ *     out and lse must not alias any input. The library keeps no tensor
+ *     pointer after a call returns.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ */
+#ifndef MAGI_ATTN_H
+#define MAGI_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#if defined(__GNUC__)
+#define MAGI_API __attribute__((visibility("default")))
+#else
+#define MAGI_API
+#endif
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MAGI_ATTN_ABI_VERSION 1
+
+typedef enum magi_status {
+  MAGI_OK = 0,
+  MAGI_ERR_INVALID_ARG = 1,   /* bad layout, NULL or misaligned pointer, bad size */
+  MAGI_ERR_UNSUPPORTED = 2,   /* valid request this build does not implement      */
+  MAGI_ERR_NO_MEMORY = 3,     /* host or device allocation failed                 */
+  MAGI_ERR_HIP = 4            /* a HIP runtime call or kernel launch failed       */
+} magi_status_t;
+
+typedef enum magi_dtype {
+  MAGI_DTYPE_BF16 = 0,
+  MAGI_DTYPE_FP32 = 1
+} magi_dtype_t;
+
+/*
+ * Chunk layout of the packed query and key streams (host arrays, read during
+ * the call only):
+ *   seq_chunks[n_seqs+1]  : video s owns chunks [seq_chunks[s], seq_chunks[s+1]);
+ *                           seq_chunks[0] == 0, seq_chunks[n_seqs] == n_chunks,
+ *                           strictly increasing (no empty video).
+ *   q_offsets[n_chunks+1] : chunk c owns queries [q_offsets[c], q_offsets[c+1]);
+ *                           non-decreasing from 0 (a chunk may own no queries,
+ *                           as the clean chunks of a KV cache do).
+ *   kv_offsets[n_chunks+1]: chunk c owns keys/values [kv_offsets[c], kv_offsets[c+1]);
+ *                           non-decreasing from 0; NULL means kv_offsets == q_offsets.
+ * A chunk that owns queries must see at least one key.
+ * head_dim: 128 for bf16; 64 or 128 for fp32. n_q_heads % n_kv_heads == 0.
+ */
+typedef struct magi_attn_layout {
+  int32_t n_seqs;
+  const int32_t* seq_chunks;
+  int32_t n_chunks;
+  const int32_t* q_offsets;
+  const int32_t* kv_offsets;
+  int32_t n_q_heads;
+  int32_t n_kv_heads;
+  int32_t head_dim;
+  int32_t dtype;              /* magi_dtype_t */
+} magi_attn_layout_t;
+
+typedef struct magi_attn_plan magi_attn_plan_t;   /* opaque */
+
+/*
+ * Validates a layout, classifies every (query tile, key tile) pair as full,
+ * boundary or empty, orders the non-empty work for the GPU and uploads the
+ * work list to device memory of the current HIP device (one allocation, owned
+ * by the plan). Host arrays are copied; the caller may free them afterwards.
+ * A plan is immutable after creation and may be used by concurrent calls on
+ * several streams of the device it was created on.
+ * Errors: MAGI_ERR_INVALID_ARG (layout rules above), MAGI_ERR_UNSUPPORTED
+ * (head_dim/dtype combination), MAGI_ERR_NO_MEMORY, MAGI_ERR_HIP. On error
+ * *plan is set to NULL. Validation runs before any HIP call.
+ */
+MAGI_API magi_status_t magi_attn_plan_create(const magi_attn_layout_t* layout, magi_attn_plan_t** plan);
+
+/* Frees the plan and its device memory (synchronous with respect to the host;
+ * the caller must not destroy a plan that queued work still uses). NULL is OK. */
+MAGI_API magi_status_t magi_attn_plan_destroy(magi_attn_plan_t* plan);
+
+/*
+ * Enqueues the forward pass on `stream`: out and lse as defined at the top.
+ * rms_eps >= 0 is added to mean(x^2) inside the square root; scale > 0 is the
+ * softmax temperature applied to <q_hat, k_hat> (1/sqrt(head_dim) usually).
+ * Allocates nothing and never synchronises, so it can be captured in a HIP
+ * graph. Errors: MAGI_ERR_INVALID_ARG (NULL/misaligned pointer, bad eps or
+ * scale), MAGI_ERR_HIP (launch failure). Device faults surface at the
+ * caller's next synchronisation.
+ */
+MAGI_API magi_status_t magi_attn_fwd(const magi_attn_plan_t* plan,
+                            const void* q, const void* k, const void* v,
+                            const float* q_gain, const float* k_gain,
+                            float rms_eps, float scale,
+                            void* out, float* lse, void* stream);
+
+/*
+ * One-shot form for a single video of self-attention (q and kv offsets both
+ * = chunk_offsets[n_chunks+1], host array): builds a plan, enqueues the
+ * forward on `stream`, waits for the stream, and destroys the plan. Not
+ * capturable (it allocates and synchronises). Same errors as above.
+ */
+MAGI_API magi_status_t magi_attn_fwd_simple(const void* q, const void* k, const void* v,
+                                   void* out, float* lse,
+                                   const int32_t* chunk_offsets, int32_t n_chunks,
+                                   int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim,
+                                   int32_t dtype, const float* q_gain, const float* k_gain,
+                                   float rms_eps, float scale, void* stream);
+
+/*
+ * Host-only tile classifier (no HIP call): for query tiles of `bm` tokens and
+ * key tiles of `bn` tokens, writes cls[qt * n_kt + kt] = 2 (every pair allowed),
+ * 1 (some allowed, some not) or 0 (none allowed), n_qt = ceil(T_q/bm),
+ * n_kt = ceil(T_k/bn); keys at or beyond T_k count as not allowed. `cls`
+ * must hold n_qt * n_kt bytes. Same layout validation as plan creation.
+ */
+MAGI_API magi_status_t magi_attn_classify_host(const magi_attn_layout_t* layout, int32_t bm, int32_t bn,
+                                      int8_t* cls);
+
+/* Host-only summary of what a plan for `layout` would launch. */
+typedef struct magi_attn_stats {
+  int64_t unmasked_pairs;     /* allowed (query, key) pairs per query head          */
+  int64_t full_pairs;         /* (query tile, key tile) pairs classified full        */
+  int64_t boundary_pairs;     /* ... boundary (masked on the GPU)                    */
+  int64_t empty_pairs;        /* ... empty (never launched)                          */
+  int64_t executed_pairs;     /* (query, key) pairs per query head the kernel computes */
+  int32_t tile_q;             /* query tokens per workgroup                          */
+  int32_t tile_kv;            /* keys per key tile                                   */
+  int32_t heads_per_item;     /* query heads per workgroup                           */
+  int32_t n_items;            /* workgroups launched (including XCD padding)         */
+} magi_attn_stats_t;
+
+MAGI_API magi_status_t magi_attn_plan_stats(const magi_attn_layout_t* layout, magi_attn_stats_t* stats);
+
+MAGI_API const char* magi_attn_status_str(magi_status_t status);
+MAGI_API const char* magi_attn_last_error(void);
+MAGI_API int magi_attn_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MAGI_ATTN_H */
