@@ -1,0 +1,190 @@
+"""Benchmark of the block-causal attention forward on one MI355X.
+
+python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+
+A step is one forward call (query/key RMSNorm, masked softmax attention, LSE)
+over the whole workload, inputs resident in HBM. The plan (tile
+classification and work order) is built once per layout before timing; its
+host time is reported as plan_create_ms. Prints one JSON line.
+
+Useful FLOPs follow the MAGI-1 pages' accounting (paperlayer §B.2.1: the two
+matrix products over the mask area): 4 * head_dim * n_q_heads * (allowed
+query-key pairs per head).
+"""
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "block-causal attn fwd useful TFLOP/s and % bf16 MFMA peak, 1×MI355X"
+PEAK_BF16_TFLOPS = 2500.0          # MI355X dense bf16 MFMA, published
+KERNEL_SRC = os.path.join(ROOT, "block_causal_attention_flash_amd", "csrc", "fwd_bf16.hip")
+
+
+def useful_pairs(layout) -> int:
+    """Allowed (query, key) pairs per head, from the offsets: every query of
+    chunk c sees keys from its video's first key to the end of chunk c."""
+    total = 0
+    for s in range(layout.n_seqs):
+        c0, c1 = layout.seq_chunks[s], layout.seq_chunks[s + 1]
+        lo = layout.kv_offsets[c0]
+        for c in range(c0, c1):
+            total += (layout.q_offsets[c + 1] - layout.q_offsets[c]) * (layout.kv_offsets[c + 1] - lo)
+    return total
+
+
+def kernel_hash() -> str:
+    with open(KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def stored_traffic(workload: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, or
+    None when it is missing or was taken on a different kernel source."""
+    path = os.path.join(ROOT, "profiles", f"fwd_bf16_{workload}_traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        doc = json.load(f)
+    if doc.get("kernel_sha256_16") != kernel_hash():
+        return None
+    return doc.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(cfg, inp, budget_s: float = 20.0):
+    """Times the fp64 oracle on a bounded sample of query rows (all heads) and
+    converts it to useful TFLOP/s on those rows."""
+    import numpy as np
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = 1
+    lay = cfg.layout
+    d, hq = cfg.head_dim, cfg.n_q_heads
+    rng = np.random.default_rng(0)
+    # row blocks of 32 consecutive tokens from randomly chosen chunks
+    flops = 0.0
+    spent = 0.0
+    rows_done = 0
+    t_start = time.perf_counter()
+    qc = [(lay.q_offsets[c], lay.q_offsets[c + 1]) for c in range(lay.n_chunks) if lay.q_offsets[c + 1] > lay.q_offsets[c]]
+    while spent < budget_s and rows_done < lay.t_q:
+        a, b = qc[int(rng.integers(0, len(qc)))]
+        r0 = int(rng.integers(a, max(a + 1, b - 32)))
+        rows = np.arange(r0, min(b, r0 + 32))
+        t0 = time.perf_counter()
+        oracle.attention(inp["q"], inp["k"], inp["v"], inp["q_gain"], inp["k_gain"], cfg.eps, cfg.scale, lay,
+                         rows=rows)
+        spent += time.perf_counter() - t0
+        for r in rows:
+            c = next(i for i in range(lay.n_chunks) if lay.q_offsets[i] <= r < lay.q_offsets[i + 1])
+            s = next(i for i in range(lay.n_seqs) if lay.seq_chunks[i] <= c < lay.seq_chunks[i + 1])
+            flops += 4.0 * d * hq * (lay.kv_offsets[c + 1] - lay.kv_offsets[lay.seq_chunks[s]])
+        rows_done += len(rows)
+        if time.perf_counter() - t_start > 3 * budget_s:
+            break
+    return {"value": flops / spent / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{rows_done} query rows x {hq} heads of {cfg.name} (blocks of 32 rows), "
+                      f"{spent:.1f} s fp64 numpy on the host"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="video480x832")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=20.0)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (the kernel runs on one GPU's "
+              "share; see DESIGN.md for how the path would shard)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from block_causal_attention_flash_amd import Plan
+    from workloads import get_config, make_inputs
+
+    cfg = get_config(args.workload)
+    lay = cfg.layout
+    dev = torch.device("cuda", 0)
+    t0 = time.perf_counter()
+    inp = make_inputs(lay, cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim, cfg.dtype, cfg.gain_kind, cfg.seed)
+    gen_s = time.perf_counter() - t0
+    q, k, v = (inp[n].to(dev) for n in ("q", "k", "v"))
+    qg, kg = inp["q_gain"].to(dev), inp["k_gain"].to(dev)
+    out = torch.empty_like(q)
+    lse = torch.empty((cfg.n_q_heads, lay.t_q), dtype=torch.float32, device=dev)
+    t0 = time.perf_counter()
+    plan = Plan.from_layout(lay, cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim, cfg.dtype)
+    plan_ms = (time.perf_counter() - t0) * 1e3
+    stats = plan.stats()
+    print(f"[bench] {cfg.name}: T_q={lay.t_q} T_k={lay.t_k} heads {cfg.n_q_heads}/{cfg.n_kv_heads} "
+          f"items={stats['n_items']} gen={gen_s:.1f}s plan={plan_ms:.1f}ms", file=sys.stderr, flush=True)
+
+    stream = torch.cuda.current_stream(dev)
+    for _ in range(args.warmup):
+        plan(q, k, v, qg, kg, cfg.eps, cfg.scale, out=out, lse=lse, stream=stream)
+    torch.cuda.synchronize()
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    wall0 = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(args.steps):
+        plan(q, k, v, qg, kg, cfg.eps, cfg.scale, out=out, lse=lse, stream=stream)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - wall0) * 1e3 / args.steps
+    ms = ev0.elapsed_time(ev1) / args.steps
+    print(f"[bench] {args.steps} steps: {ms:.3f} ms/step (events), {wall_ms:.3f} ms/step (host wall)",
+          file=sys.stderr, flush=True)
+
+    pairs = useful_pairs(lay)
+    flops = 4.0 * cfg.head_dim * cfg.n_q_heads * pairs
+    tflops = flops / (ms * 1e-3) / 1e12
+    traffic = stored_traffic(cfg.name)
+    roof = {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+            "frac": round(tflops / PEAK_BF16_TFLOPS, 4), "traffic": traffic}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        print(f"[bench] timing the CPU oracle on a sample (~{args.cpu_budget:.0f} s)", file=sys.stderr, flush=True)
+        cpu = cpu_baseline(cfg, inp, args.cpu_budget)
+
+    rec = {
+        "metric": METRIC,
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": cfg.dtype,
+        "data": "synthetic (seeded N(0,1) Q/K/V, unit QK-norm gains)" if cfg.gain_kind == "ones" else
+                "synthetic (seeded N(0,1) Q/K/V, QK-norm gains U(0.5,1.5))",
+        "config": {"workload": cfg.name, "t_q": lay.t_q, "t_k": lay.t_k, "n_chunks": lay.n_chunks,
+                   "n_videos": lay.n_seqs, "n_q_heads": cfg.n_q_heads, "n_kv_heads": cfg.n_kv_heads,
+                   "head_dim": cfg.head_dim, "useful_flops": flops, "unmasked_pairs_per_head": pairs},
+        "frac_of_peak": round(tflops / PEAK_BF16_TFLOPS, 4),
+        "plan_create_ms": round(plan_ms, 2),
+        "roofline": roof,
+        "cpu_baseline": cpu,
+    }
+    plan.close()
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -5,27 +5,35 @@
 // softmax over its allowed keys of scale * <rms(q) * g_q, rms(k) * g_k>,
 // times V, plus the natural-log log-sum-exp. The forward's cost is the two
 // matrix products over the mask area (paperlayer §B.2.1), so both run on the
-// bf16 matrix cores.
+// bf16 matrix cores (v_mfma_f32_32x32x16_bf16).
 //
-// Workgroup = one work item: 256 (token, head) rows = 8 waves x 32 rows of
-// `heads_per_item` query heads that share one KV head. Per key tile (64 keys):
-//   * the K and V tiles are copied from global memory straight into LDS with
-//     buffer_load ... lds (zero fill past T_k), three stages deep, and serve
-//     all 256 rows: K/V are read from L2 once per workgroup, not per head;
-//   * the K RMS factor r_j = 1/sqrt(mean(k_j^2) + eps) is computed once per
-//     key by the workgroup; g_k is folded into the normalised queries, so the
-//     raw bf16 keys feed the matrix cores and s_ij = r_j * <q'_i, k_j>;
-//   * S^T = K Q'^T on v_mfma_f32_32x32x16_bf16 (lane = query row), softmax in
-//     fp32 registers, P rounded to bf16, O^T += V^T P^T with V read through
-//     ds_read_b64_tr_b16 from the row-major LDS tile.
-// Queries are normalised in the prologue (RMS over head_dim, times g_q * g_k
-// * scale * log2 e) and kept in registers as bf16 MFMA operands.
+// Workgroup = one work item: 256 (token, head) rows of `heads_per_item`
+// query heads that share one KV head; 4 waves, one per SIMD, 64 rows each
+// (two 32-row MFMA blocks). Per 64-key tile:
+//   * K and V tiles are copied from global memory straight into LDS rings
+//     (buffer_load ... lds, zero fill past T_k) two tiles ahead, and serve all
+//     256 rows: K/V leave L2 once per workgroup, not once per query head;
+//   * each staged K tile is RMS-normalised in LDS once, by the workgroup, one
+//     tile ahead of its use (k_hat = k / rms(k), rounded to bf16); g_k is
+//     folded into the normalised queries, so s_ij = <q'_i, k_hat_j>;
+//   * S^T = K Q'^T (lane = query row, 16 keys per lane in registers);
+//   * O^T += V^T P^T with V read through ds_read_b64_tr_b16 from the row-major
+//     V tile.
+// Software pipeline per iteration i: phase 1 issues the 32 MFMAs of S(i);
+// phase 2 issues the 32 MFMAs of P(i-1) V(i-1) while the vector ALUs turn S(i)
+// into P(i) (scale, mask, exp2, round to bf16, row sums). One wave per SIMD
+// keeps the matrix pipe fed from a single instruction stream; a workgroup
+// barrier per tile recycles the LDS rings.
+//
+// Queries are normalised in the prologue (RMS over head_dim, times
+// g_q * g_k * scale * log2 e) and held in registers as bf16 MFMA operands.
 //
 // Softmax. QK-normalisation bounds every logit: |s_ij| <= |q'_i| |k_hat_j|
-// <= |q'_i| sqrt(d). When that bound is at most 40 (log2 units) for all rows
-// of a wave, the wave uses exp2(s) directly (no running maximum, no rescale):
-// softmax is invariant to the shift and 2^+-40 is far inside fp32/bf16 range.
-// Otherwise the wave runs the online softmax with a running row maximum.
+// <= |q'_i| sqrt(d). When that bound is at most 40 (log2 units) for every row
+// of a wave, the wave uses exp2(s) directly, with no running maximum and no
+// rescaling: softmax is invariant to the shift and 2^+-40 lies far inside the
+// fp32/bf16 range. Otherwise the wave keeps a running row maximum and rescales
+// its accumulator only when the maximum has grown by more than 2^8.
 #include "kernels.hpp"
 
 namespace magi {
@@ -35,6 +43,7 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
@@ -42,21 +51,23 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int D = 128;
 constexpr int BN = 64;
-constexpr int NWAVE = 8;
+constexpr int NWAVE = 4;
 constexpr int NTHR = NWAVE * 64;
-constexpr int NSTAGE = 3;
-constexpr int ROW_BYTES = D * 2;                       // 256
-constexpr int TILE_BYTES = BN * ROW_BYTES;             // 16 KiB
-constexpr int UNITS_PER_THREAD = TILE_BYTES / (NTHR * 16);  // 2
+constexpr int LOOKAHEAD = 2;                          // tiles in flight ahead of use
+constexpr int KSTAGES = LOOKAHEAD + 2;                // K(i), K(i+1), K(i+2)..K(i+1+LA)
+constexpr int VSTAGES = LOOKAHEAD + 2;                // V(i-1), V(i)..V(i+LA)
+constexpr int ROW_BYTES = D * 2;                      // 256
+constexpr int TILE_BYTES = BN * ROW_BYTES;            // 16 KiB
+constexpr int UNITS = TILE_BYTES / (NTHR * 16);       // 4 16-byte copies per thread per tensor
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kStaticBound = 40.0f;
+constexpr float kRescaleSlack = 8.0f;
 constexpr float kNegInf = -__builtin_inff();
 
 struct Smem {
-  unsigned char k[NSTAGE][TILE_BYTES];
-  unsigned char v[NSTAGE][TILE_BYTES];
-  float rk[2][BN];
+  unsigned char k[KSTAGES][TILE_BYTES];
+  unsigned char v[VSTAGES][TILE_BYTES];
   float gqk[D];
 };
 
@@ -76,221 +87,347 @@ __device__ __forceinline__ float sumsq8(bf16x8 a, float acc) {
   return acc;
 }
 
-// Walks the key tiles of a work item's segment list, one tile per step.
-struct TileCursor {
-  const int4* segs;
-  int seg, seg_end;
-  int kt, kt_end, masked;
-  __device__ void init(const int4* s, int b, int e) {
-    segs = s; seg = b; seg_end = e;
-    load();
-  }
-  __device__ void load() {
-    if (seg < seg_end) {
-      const int4 g = segs[seg];
-      kt = g.x; kt_end = g.y; masked = g.z;
-    }
-  }
-  __device__ void next() {
-    if (++kt == kt_end) { ++seg; load(); }
-  }
-};
+__device__ __forceinline__ unsigned lds_addr(const void* p) {
+  return unsigned(reinterpret_cast<uintptr_t>(LDS_PTR(const char, p)));
+}
 
-// Copies key tile kt of KV head kvh into LDS stage buffers. LDS images:
+// Raw buffer resource: base, stride 0, num_records = bytes (reads at or past
+// `bytes` return zero), dword3 = 32-bit data format as used for raw buffers.
+__device__ __forceinline__ i32x4 make_rsrc(const void* base, unsigned bytes) {
+  const unsigned long long a = reinterpret_cast<unsigned long long>(base);
+  i32x4 r;
+  r[0] = int(unsigned(a));
+  r[1] = int(unsigned(a >> 32) & 0xffffu);
+  r[2] = int(bytes);
+  r[3] = 0x00020000;
+  return r;
+}
+
+// 16-byte copy global -> LDS: lane i of the wave writes LDS byte m0 + 16 i.
+// Issued through asm so that the compiler does not order later LDS reads of
+// other ring stages behind it; completion is awaited explicitly (vmcnt).
+__device__ __forceinline__ void dma16(i32x4 rsrc, unsigned voff, unsigned lds) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+               :
+               : "s"(lds), "v"(voff), "s"(rsrc)
+               : "memory", "m0");
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  asm volatile("s_waitcnt vmcnt(%0)" : : "n"(N) : "memory");
+}
+
+// All LDS traffic of this wave finished, then the workgroup barrier.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" : : : "memory"); }
+
+// Copies key tile kt of KV head kvh into LDS. Images:
 //   K: row-major [key][128], 16-byte chunk c of key j stored at chunk c ^ (j & 15)
 //   V: row-major [key][128], 64-byte segment g of key j stored at g ^ (j & 3)
 // Each wave instruction writes 1 KiB of LDS (lane i -> +16 i); the lane's
 // global source is chosen so the image comes out swizzled.
-__device__ __forceinline__ void issue_tile(__amdgpu_buffer_rsrc_t rk, __amdgpu_buffer_rsrc_t rv, Smem& sm, int stage,
-                                           int kt, int kvh, int hk, int wave, int lane) {
+__device__ __forceinline__ void issue_k(i32x4 rsrc, unsigned lds_stage, int kt, int kvh, int hk, int wave,
+                                        int lane) {
 #pragma unroll
-  for (int i = 0; i < UNITS_PER_THREAD; ++i) {
-    const int blk = i * NWAVE + wave;                  // 1 KiB block of the image
-    const int u = blk * 64 + lane;                     // 16-byte unit
+  for (int i = 0; i < UNITS; ++i) {
+    const int blk = i * NWAVE + wave;
+    const int u = blk * 64 + lane;
     const int key = u >> 4, pc = u & 15;
     const unsigned row = unsigned((kt * BN + key) * hk + kvh) * ROW_BYTES;
-    const int ck = pc ^ (key & 15);
-    const int cv = ((((pc >> 2) ^ (key & 3)) << 2) | (pc & 3));
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, LDS_PTR(void, sm.k[stage] + blk * 1024), 16, row + ck * 16, 0, 0, 0);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, LDS_PTR(void, sm.v[stage] + blk * 1024), 16, row + cv * 16, 0, 0, 0);
+    dma16(rsrc, row + unsigned((pc ^ (key & 15)) * 16), lds_stage + blk * 1024);
   }
 }
 
-// r_j = 1 / sqrt(mean_d k_j^2 + eps) for the 64 keys of a staged K tile.
-__device__ __forceinline__ void key_rms(Smem& sm, int stage, int rs, float eps) {
+__device__ __forceinline__ void issue_v(i32x4 rsrc, unsigned lds_stage, int kt, int kvh, int hk, int wave,
+                                        int lane) {
+#pragma unroll
+  for (int i = 0; i < UNITS; ++i) {
+    const int blk = i * NWAVE + wave;
+    const int u = blk * 64 + lane;
+    const int key = u >> 4, pc = u & 15;
+    const unsigned row = unsigned((kt * BN + key) * hk + kvh) * ROW_BYTES;
+    const int cv = ((((pc >> 2) ^ (key & 3)) << 2) | (pc & 3));
+    dma16(rsrc, row + unsigned(cv * 16), lds_stage + blk * 1024);
+  }
+}
+
+// Normalises a staged K tile in place: k_hat_j = k_j / sqrt(mean_d k_j^2 + eps),
+// rounded to bf16 (the gain g_k is folded into the queries). Four threads
+// per key, 32 dims each; the swizzled layout is kept.
+__device__ __forceinline__ void key_normalize(unsigned char* kst, float eps) {
   const int tid = threadIdx.x;
-  const int key = tid >> 3, part = tid & 7;
-  const unsigned char* row = sm.k[stage] + key * ROW_BYTES;
-  const bf16x8 a0 = *LDS_PTR(const bf16x8, row + (((2 * part) ^ (key & 15)) * 16));
-  const bf16x8 a1 = *LDS_PTR(const bf16x8, row + (((2 * part + 1) ^ (key & 15)) * 16));
-  float ss = sumsq8(a1, sumsq8(a0, 0.0f));
+  const int key = tid >> 2, part = tid & 3;
+  unsigned char* row = kst + key * ROW_BYTES;
+  bf16x8 x[4];
+  float ss = 0.0f;
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    x[c] = *LDS_PTR(const bf16x8, row + (((4 * part + c) ^ (key & 15)) * 16));
+    ss = sumsq8(x[c], ss);
+  }
   ss += dpp<0xB1>(ss);    // quad_perm [1,0,3,2]
   ss += dpp<0x4E>(ss);    // quad_perm [2,3,0,1]
-  ss += dpp<0x141>(ss);   // row_half_mirror: the other quad of 8 lanes
-  if (part == 0) sm.rk[rs][key] = __builtin_amdgcn_rsqf(ss * (1.0f / D) + eps);
+  const float r = __builtin_amdgcn_rsqf(ss * (1.0f / D) + eps);
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    bf16x8 y;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) y[j] = (__bf16)(float(x[c][j]) * r);
+    *LDS_PTR(bf16x8, row + (((4 * part + c) ^ (key & 15)) * 16)) = y;
+  }
 }
 
 struct WaveState {
-  bf16x8 qf[8];          // B operand of S^T: lane row (l & 31), dims (2ks + (l>>5)) * 8 ..
-  f32x16 o[4];           // O^T accumulator: lane row (l & 31), 4 dim blocks of 32
-  float lsum;            // partial row sum over this lane's half of the keys
-  float m;               // running max (online path), log2 units
-  int lo, hi;            // key bounds of the lane's row
-  bool stat;             // wave-uniform: static-bound softmax
+  bf16x8 qf[2][8];       // B operands of S^T, per row block: lane row (l & 31), dims (2ks + (l>>5)) * 8 ..
+  f32x16 o[2][4];        // O^T accumulators: lane row (l & 31), 4 dim blocks of 32
+  bf16x8 p[2][2][2];     // P of the previous tile, per (row block, key block, k-step)
+  float lsum[2];         // partial row sums over this lane's half of the keys
+  float m[2];            // online path: reference maximum (log2 units)
+  int lo[2], hi[2];      // key bounds of the lane's rows
 };
 
-__device__ __forceinline__ void compute_tile(const Smem& sm, int stage, int rs, int kt, bool masked, WaveState& st,
-                                             int lane) {
+// Phase 1: S^T(tile in stage kst) for both row blocks.
+__device__ __forceinline__ void qk_tile(const unsigned char* kst, const WaveState& st, f32x16 (&s)[2][2], int lane) {
   const int l31 = lane & 31, hi5 = lane >> 5;
-  const unsigned char* kb_base = sm.k[stage];
-  // ---- S^T[key][row] for two 32-key blocks
-  f32x16 s[2];
 #pragma unroll
-  for (int kb = 0; kb < 2; ++kb) {
-    f32x16 acc = {};
-    const unsigned char* row = kb_base + (kb * 32 + l31) * ROW_BYTES;
+  for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
-    for (int ks = 0; ks < 8; ++ks) {
-      const int c = (2 * ks + hi5) ^ (lane & 15);
-      const bf16x8 a = *LDS_PTR(const bf16x8, row + c * 16);
-      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, st.qf[ks], acc, 0, 0, 0);
-    }
-    s[kb] = acc;
-  }
-  // ---- scale by the key RMS factors, mask, exponentiate
-  // lane holds keys kb*32 + (i/4)*8 + hi5*4 + (i%4), i = 0..15
+    for (int kb = 0; kb < 2; ++kb) s[rb][kb] = f32x16{};
 #pragma unroll
-  for (int kb = 0; kb < 2; ++kb) {
+  for (int ks = 0; ks < 8; ++ks) {
+    const int c = (2 * ks + hi5) ^ (lane & 15);
+    bf16x8 a[2];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const f32x4 r = *LDS_PTR(const f32x4, &sm.rk[rs][kb * 32 + u * 8 + hi5 * 4]);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        float x = s[kb][u * 4 + e] * r[e];
-        if (masked) {
-          const int key = kt * BN + kb * 32 + u * 8 + hi5 * 4 + e;
-          x = (key >= st.lo && key < st.hi) ? x : kNegInf;
-        }
-        s[kb][u * 4 + e] = x;
-      }
-    }
-  }
-  if (!st.stat) {
-    float mx = kNegInf;
+    for (int kb = 0; kb < 2; ++kb) a[kb] = *LDS_PTR(const bf16x8, kst + (kb * 32 + l31) * ROW_BYTES + c * 16);
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[kb][i]);
-    mx = fmaxf(mx, xor32(mx));
-    const float m_new = fmaxf(st.m, mx);
-    const float m_use = (m_new == kNegInf) ? 0.0f : m_new;
-    const float alpha = __builtin_amdgcn_exp2f(st.m - m_use);
-    st.m = m_new;
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) s[kb][i] -= m_use;
-    if (__builtin_amdgcn_ballot_w64(alpha != 1.0f)) {
-      st.lsum *= alpha;
-#pragma unroll
-      for (int db = 0; db < 4; ++db) st.o[db] *= alpha;
-    }
+      for (int rb = 0; rb < 2; ++rb)
+        s[rb][kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[kb], st.qf[rb][ks], s[rb][kb], 0, 0, 0);
   }
-  bf16x8 p[2][2];
-#pragma unroll
-  for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-    for (int t = 0; t < 2; ++t)
-#pragma unroll
-      for (int j = 0; j < 8; ++j) p[kb][t][j] = (__bf16)__builtin_amdgcn_exp2f(s[kb][t * 8 + j]);
-  // row sum of the rounded probabilities (what P V actually weights)
-  const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
-#pragma unroll
-  for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-    for (int t = 0; t < 2; ++t)
-#pragma unroll
-      for (int j = 0; j < 8; j += 2) {
-        const bf16x2 pp = {p[kb][t][j], p[kb][t][j + 1]};
-        st.lsum = __builtin_amdgcn_fdot2_f32_bf16(pp, ones, st.lsum, false);
-      }
-  // ---- O^T[dim][row] += V^T P^T
-  // k-step (kb, t) covers keys kb*32 + t*16 + {s*8 + hi5*4 + r}: the P layout.
-  // ds_read_b64_tr_b16: lane 16b+n receives, for r = 0..3, element n%4 of what
-  // lane 16b + 4r + n/4 read; lane 16b+i therefore reads 4 dims of key
-  // (.. + (b>>1)*4 + i/4) at dim (b&1)*16 + (i%4)*4 of the 32-dim block.
-  const unsigned char* vb = sm.v[stage];
+}
+
+// Phase 2 (MFMA part): O^T += V^T P^T for the previous tile.
+// k-step (kb, t) covers keys kb*32 + t*16 + {s*8 + hi5*4 + r}: the P layout.
+// ds_read_b64_tr_b16: lane 16b+n receives, for r = 0..3, element n%4 of what
+// lane 16b + 4r + n/4 read; lane 16b+i therefore reads 4 dims of key
+// (.. + (b>>1)*4 + i/4) at dim (b&1)*16 + (i%4)*4 of the 32-dim block.
+__device__ __forceinline__ void pv_tile(const unsigned char* vst, WaveState& st, int lane) {
   const int b = lane >> 4, n = lane & 15;
   const int key_in = (b >> 1) * 4 + (n >> 2);
   const int dim_in = (b & 1) * 16 + (n & 3) * 4;
 #pragma unroll
-  for (int db = 0; db < 4; ++db) {
+  for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+    for (int t = 0; t < 2; ++t)
 #pragma unroll
-      for (int t = 0; t < 2; ++t) {
+      for (int db = 0; db < 4; ++db) {
         i16x4 h[2];
 #pragma unroll
         for (int sidx = 0; sidx < 2; ++sidx) {
           const int key = kb * 32 + t * 16 + sidx * 8 + key_in;
           const int off = key * ROW_BYTES + ((db ^ (key & 3)) * 64) + dim_in * 2;
-          h[sidx] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(i16x4, vb + off));
+          h[sidx] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(i16x4, vst + off));
         }
         const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(h[0], h[1], 0, 1, 2, 3, 4, 5, 6, 7));
-        st.o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, p[kb][t], st.o[db], 0, 0, 0);
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb)
+          st.o[rb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, st.p[rb][kb][t], st.o[rb][db], 0, 0, 0);
       }
+}
+
+// Phase 2 (vector part): S(i) -> P(i). Lane holds keys kb*32 + u*8 + hi5*4 + e
+// (u, e = 0..3) of its row for each row block.
+template <bool MASKED, bool STATIC>
+__device__ __forceinline__ void softmax_tile(f32x16 (&s)[2][2], int kt, WaveState& st, bf16x8 (&pn)[2][2][2],
+                                             float (&alpha)[2], int lane) {
+  const int hi5 = lane >> 5;
+#pragma unroll
+  for (int rb = 0; rb < 2; ++rb) {
+    if (MASKED) {
+      // key allowed  <=>  (key - lo) < (hi - lo) as unsigned
+      const unsigned base = unsigned(kt * BN + hi5 * 4 - st.lo[rb]);
+      const unsigned len = unsigned(st.hi[rb] - st.lo[rb]);
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const unsigned rel = base + unsigned(kb * 32 + u * 8 + e);
+            s[rb][kb][u * 4 + e] = rel < len ? s[rb][kb][u * 4 + e] : kNegInf;
+          }
+    }
+    alpha[rb] = 1.0f;
+    if (!STATIC) {
+      float mx = kNegInf;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[rb][kb][i]);
+      mx = fmaxf(mx, xor32(mx));
+      // keep the reference maximum unless the tile exceeds it by > 2^8
+      const float m_new = (mx > st.m[rb] + kRescaleSlack) ? mx : st.m[rb];
+      alpha[rb] = (m_new == st.m[rb]) ? 1.0f : __builtin_amdgcn_exp2f(st.m[rb] - m_new);
+      st.m[rb] = m_new;
+      const float m_use = (m_new == kNegInf) ? 0.0f : m_new;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) s[rb][kb][i] -= m_use;
+    }
+    const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+    float ls = 0.0f;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int j = 0; j < 8; j += 2) {
+          const float e0 = __builtin_amdgcn_exp2f(s[rb][kb][t * 8 + j]);
+          const float e1 = __builtin_amdgcn_exp2f(s[rb][kb][t * 8 + j + 1]);
+          const bf16x2 pp = {(__bf16)e0, (__bf16)e1};
+          pn[rb][kb][t][j] = pp[0];
+          pn[rb][kb][t][j + 1] = pp[1];
+          ls = __builtin_amdgcn_fdot2_f32_bf16(pp, ones, ls, false);
+        }
+    st.lsum[rb] = st.lsum[rb] * alpha[rb] + ls;
   }
 }
 
-__global__ void __launch_bounds__(NTHR) __attribute__((amdgpu_waves_per_eu(2, 2)))
-fwd_bf16_d128_kernel(FwdParams prm) {
+template <bool MASKED, bool STATIC>
+__device__ __forceinline__ void iteration(const unsigned char* kst, const unsigned char* vst_prev, int kt,
+                                          WaveState& st, int lane) {
+  f32x16 s[2][2];
+  qk_tile(kst, st, s, lane);
+  pv_tile(vst_prev, st, lane);
+  bf16x8 pn[2][2][2];
+  float alpha[2];
+  softmax_tile<MASKED, STATIC>(s, kt, st, pn, alpha, lane);
+  if (!STATIC) {
+    // P(i-1) V(i-1) was accumulated against the old reference maximum.
+    if (__builtin_amdgcn_ballot_w64(alpha[0] != 1.0f || alpha[1] != 1.0f)) {
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+        for (int db = 0; db < 4; ++db) st.o[rb][db] *= alpha[rb];
+    }
+  }
+#pragma unroll
+  for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int t = 0; t < 2; ++t) st.p[rb][kb][t] = pn[rb][kb][t];
+}
+
+// Per-workgroup constants of the tile loop.
+struct LoopCtx {
+  i32x4 rsk, rsv;           // buffer resources of K and V
+  unsigned k_base, v_base;  // LDS byte addresses of the K and V rings
+  const int* tiles;         // this item's key tile codes
+  int n_tiles, kvh, hk, wave, lane;
+  float eps;
+};
+
+// Top of iteration i: wait for K(i+1) and V(i) (older than the copies issued
+// in iteration i-1), barrier, start the copies of K(i+1+LA) and V(i+LA), and
+// normalise K(i+1) for the next iteration.
+__device__ __forceinline__ void loop_top(Smem& sm, const LoopCtx& c, int i) {
+  if (i > 0) {
+    const int younger = (i + LOOKAHEAD < c.n_tiles ? UNITS : 0) + (i + LOOKAHEAD - 1 < c.n_tiles ? UNITS : 0);
+    if (younger == 2 * UNITS) wait_vmcnt<2 * UNITS>();
+    else if (younger == UNITS) wait_vmcnt<UNITS>();
+    else wait_vmcnt<0>();
+  }
+  lds_barrier();
+  if (i + 1 + LOOKAHEAD < c.n_tiles)
+    issue_k(c.rsk, c.k_base + ((i + 1 + LOOKAHEAD) % KSTAGES) * TILE_BYTES, c.tiles[i + 1 + LOOKAHEAD] >> 1, c.kvh,
+            c.hk, c.wave, c.lane);
+  if (i + LOOKAHEAD < c.n_tiles)
+    issue_v(c.rsv, c.v_base + ((i + LOOKAHEAD) % VSTAGES) * TILE_BYTES, c.tiles[i + LOOKAHEAD] >> 1, c.kvh, c.hk,
+            c.wave, c.lane);
+  if (i + 1 < c.n_tiles) key_normalize(sm.k[(i + 1) % KSTAGES], c.eps);
+}
+
+// Full tiles first (no mask code), then boundary tiles; one loop body each.
+template <bool STATIC>
+__device__ __forceinline__ void run_tiles(Smem& sm, const LoopCtx& c, int n_full, WaveState& st) {
+  for (int i = 0; i < n_full; ++i) {
+    loop_top(sm, c, i);
+    iteration<false, STATIC>(sm.k[i % KSTAGES], sm.v[(i + VSTAGES - 1) % VSTAGES], c.tiles[i] >> 1, st, c.lane);
+  }
+  for (int i = n_full; i < c.n_tiles; ++i) {
+    loop_top(sm, c, i);
+    iteration<true, STATIC>(sm.k[i % KSTAGES], sm.v[(i + VSTAGES - 1) % VSTAGES], c.tiles[i] >> 1, st, c.lane);
+  }
+}
+
+__global__ void __launch_bounds__(NTHR) __attribute__((amdgpu_waves_per_eu(1, 1)))
+fwd_bf16_d128_kernel(FwdParams prm, const int4* __restrict__ items, const int* __restrict__ tiles,
+                     const int2* __restrict__ rows) {
   __shared__ __attribute__((aligned(1024))) Smem sm;
-  const int4 item = prm.items[blockIdx.x];
+  const int4 item = items[2 * blockIdx.x];
   if (item.z == item.w) return;                       // padding item
+  const int n_full = items[2 * blockIdx.x + 1].x;
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
   const int kvh = item.y >> 16, h0 = item.y & 0xffff;
   const int rb_per_head = prm.tile_q >> 5;
-  const int head = h0 + wave / rb_per_head;
-  const int t = item.x + (wave % rb_per_head) * 32 + (lane & 31);
-  const bool valid = t < prm.tq;
+  const int tb = item.z, n_tiles = item.w - item.z;
 
-  // gains product, folded with the temperature and log2 e
+  // ---- K/V tiles 0..LOOKAHEAD in flight before anything else
+  const unsigned kv_bytes = unsigned(prm.tk) * unsigned(prm.hk) * unsigned(ROW_BYTES);
+  const i32x4 rsk = make_rsrc(prm.k, kv_bytes);
+  const i32x4 rsv = make_rsrc(prm.v, kv_bytes);
+  const unsigned k_base = __builtin_amdgcn_readfirstlane(lds_addr(&sm.k[0][0]));
+  const unsigned v_base = __builtin_amdgcn_readfirstlane(lds_addr(&sm.v[0][0]));
+#pragma unroll
+  for (int j = 0; j <= LOOKAHEAD; ++j)
+    if (j < n_tiles) issue_k(rsk, k_base + j * TILE_BYTES, tiles[tb + j] >> 1, kvh, prm.hk, wave, lane);
+#pragma unroll
+  for (int j = 0; j < LOOKAHEAD; ++j)
+    if (j < n_tiles) issue_v(rsv, v_base + j * TILE_BYTES, tiles[tb + j] >> 1, kvh, prm.hk, wave, lane);
+
+  // V stage of tile -1 holds zeros: the first iteration's P(-1) V(-1) adds 0.
+  {
+    unsigned char* vz = sm.v[VSTAGES - 1];
+#pragma unroll
+    for (int i = 0; i < TILE_BYTES / (NTHR * 16); ++i)
+      *LDS_PTR(i32x4, vz + (i * NTHR + tid) * 16) = i32x4{0, 0, 0, 0};
+  }
   if (tid < D) sm.gqk[tid] = prm.q_gain[tid] * prm.k_gain[tid] * (prm.scale * kLog2e);
 
-  const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<void*>(prm.k), (short)0, int(unsigned(prm.tk) * unsigned(prm.hk) * unsigned(ROW_BYTES)), 0x00020000);
-  const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<void*>(prm.v), (short)0, int(unsigned(prm.tk) * unsigned(prm.hk) * unsigned(ROW_BYTES)), 0x00020000);
-
-  // tiles of this item
-  int n_tiles = 0;
-  for (int sg = item.z; sg < item.w; ++sg) { const int4 g = prm.segs[sg]; n_tiles += g.y - g.x; }
-  TileCursor cur_load, cur_comp;
-  cur_load.init(prm.segs, item.z, item.w);
-  cur_comp = cur_load;
-  // prefetch tiles 0 and 1
-  issue_tile(rk, rv, sm, 0, cur_load.kt, kvh, prm.hk, wave, lane);
-  cur_load.next();
-  if (n_tiles > 1) { issue_tile(rk, rv, sm, 1, cur_load.kt, kvh, prm.hk, wave, lane); cur_load.next(); }
+  WaveState st;
+  int tok[2], head[2];
+  bool valid[2];
+#pragma unroll
+  for (int rb = 0; rb < 2; ++rb) {
+    const int blk = wave * 2 + rb;
+    head[rb] = h0 + blk / rb_per_head;
+    tok[rb] = item.x + (blk % rb_per_head) * 32 + (lane & 31);
+    valid[rb] = tok[rb] < prm.tq;
+  }
 
   // ---- query prologue: load, RMS-normalise, fold gains/temperature, to bf16
-  WaveState st;
-  {
-    const __bf16* qrow = reinterpret_cast<const __bf16*>(prm.q) + (size_t(t) * prm.hq + head) * D;
-    bf16x8 qr[8];
+  bf16x8 qr[2][8];
 #pragma unroll
-    for (int ks = 0; ks < 8; ++ks) {
-      if (valid) qr[ks] = *reinterpret_cast<const bf16x8*>(qrow + (2 * ks + (lane >> 5)) * 8);
-      else qr[ks] = bf16x8{};
-    }
+  for (int rb = 0; rb < 2; ++rb) {
+    const __bf16* qrow = reinterpret_cast<const __bf16*>(prm.q) + (size_t(tok[rb]) * prm.hq + head[rb]) * D;
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks)
+      qr[rb][ks] = valid[rb] ? *reinterpret_cast<const bf16x8*>(qrow + (2 * ks + (lane >> 5)) * 8) : bf16x8{};
+  }
+  __syncthreads();                                     // gqk and the zeroed V stage visible
+  float bound_max = 0.0f;
+#pragma unroll
+  for (int rb = 0; rb < 2; ++rb) {
     float ss = 0.0f;
 #pragma unroll
-    for (int ks = 0; ks < 8; ++ks) ss = sumsq8(qr[ks], ss);
+    for (int ks = 0; ks < 8; ++ks) ss = sumsq8(qr[rb][ks], ss);
     ss += xor32(ss);
-    const float rq = __builtin_amdgcn_rsqf(ss * (1.0f / D) + prm.eps);
-    __syncthreads();                                   // gqk visible
+    const float rq = valid[rb] ? __builtin_amdgcn_rsqf(ss * (1.0f / D) + prm.eps) : 0.0f;
     float nq = 0.0f;
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks) {
@@ -298,61 +435,57 @@ fwd_bf16_d128_kernel(FwdParams prm) {
       const f32x4 g0 = *LDS_PTR(const f32x4, &sm.gqk[d0]);
       const f32x4 g1 = *LDS_PTR(const f32x4, &sm.gqk[d0 + 4]);
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const float g = j < 4 ? g0[j] : g1[j - 4];
-        const float x = valid ? float(qr[ks][j]) * rq * g : 0.0f;
-        st.qf[ks][j] = (__bf16)x;
-      }
-      nq = sumsq8(st.qf[ks], nq);
+      for (int j = 0; j < 8; ++j) st.qf[rb][ks][j] = (__bf16)(float(qr[rb][ks][j]) * rq * (j < 4 ? g0[j] : g1[j - 4]));
+      nq = sumsq8(st.qf[rb][ks], nq);
     }
     nq += xor32(nq);
-    const float bound = __builtin_sqrtf(nq) * __builtin_sqrtf(float(D)) * 1.02f;
-    st.stat = __builtin_amdgcn_ballot_w64(!(bound <= kStaticBound)) == 0;
-    const int2 rb = valid ? prm.rows[t] : int2{0, 0};
-    st.lo = rb.x;
-    st.hi = rb.y;
+    bound_max = fmaxf(bound_max, __builtin_sqrtf(nq) * __builtin_sqrtf(float(D)) * 1.02f);
+    const int2 b = valid[rb] ? rows[tok[rb]] : int2{0, 0};
+    st.lo[rb] = b.x;
+    st.hi[rb] = b.y;
 #pragma unroll
-    for (int db = 0; db < 4; ++db) st.o[db] = f32x16{};
-    st.lsum = 0.0f;
-    st.m = kNegInf;
+    for (int db = 0; db < 4; ++db) st.o[rb][db] = f32x16{};
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int t = 0; t < 2; ++t) st.p[rb][kb][t] = bf16x8{};
+    st.lsum[rb] = 0.0f;
+    st.m[rb] = kNegInf;
   }
+  const bool stat = __builtin_amdgcn_ballot_w64(!(bound_max <= kStaticBound)) == 0;
 
-  // tile 0's K factors
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
-  key_rms(sm, 0, 0, prm.eps);
+  // ---- tile 0's keys normalised
+  wait_vmcnt<0>();
+  lds_barrier();
+  key_normalize(sm.k[0], prm.eps);
 
-  for (int i = 0; i < n_tiles; ++i) {
-    // tile i+1 landed (own loads), everyone done with tile i-1, r(i) published
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-    if (i + 2 < n_tiles) {
-      issue_tile(rk, rv, sm, (i + 2) % NSTAGE, cur_load.kt, kvh, prm.hk, wave, lane);
-      cur_load.next();
-    }
-    if (i + 1 < n_tiles) key_rms(sm, (i + 1) % NSTAGE, (i + 1) & 1, prm.eps);
-    compute_tile(sm, i % NSTAGE, i & 1, cur_comp.kt, cur_comp.masked != 0, st, lane);
-    cur_comp.next();
-  }
+  LoopCtx ctx{rsk, rsv, k_base, v_base, tiles + tb, n_tiles, kvh, prm.hk, wave, lane, prm.eps};
+  if (stat) run_tiles<true>(sm, ctx, n_full, st);
+  else run_tiles<false>(sm, ctx, n_full, st);
+  // last tile's P V: its V stage landed before the last barrier
+  pv_tile(sm.v[(n_tiles + VSTAGES - 1) % VSTAGES], st, lane);
 
   // ---- epilogue
-  const float lsum = st.lsum + xor32(st.lsum);
-  if (valid) {
-    const float inv = 1.0f / lsum;
-    __bf16* orow = reinterpret_cast<__bf16*>(prm.out) + (size_t(t) * prm.hq + head) * D;
 #pragma unroll
-    for (int db = 0; db < 4; ++db)
+  for (int rb = 0; rb < 2; ++rb) {
+    const float lsum = st.lsum[rb] + xor32(st.lsum[rb]);
+    if (valid[rb]) {
+      const float inv = 1.0f / lsum;
+      __bf16* orow = reinterpret_cast<__bf16*>(prm.out) + (size_t(tok[rb]) * prm.hq + head[rb]) * D;
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        bf16x4 w;
+      for (int db = 0; db < 4; ++db)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) w[e] = (__bf16)(st.o[db][u * 4 + e] * inv);
-        *reinterpret_cast<bf16x4*>(orow + db * 32 + u * 8 + (lane >> 5) * 4) = w;
+        for (int u = 0; u < 4; ++u) {
+          bf16x4 w;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) w[e] = (__bf16)(st.o[rb][db][u * 4 + e] * inv);
+          *reinterpret_cast<bf16x4*>(orow + db * 32 + u * 8 + (lane >> 5) * 4) = w;
+        }
+      if (lane < 32) {
+        const float l2 = __builtin_amdgcn_logf(lsum);   // log2
+        const float lse = stat ? l2 * kLn2 : (st.m[rb] + l2) * kLn2;
+        prm.lse[size_t(head[rb]) * prm.tq + tok[rb]] = lse;
       }
-    if (lane < 32) {
-      const float l2 = __builtin_amdgcn_logf(lsum);   // log2
-      const float lse = st.stat ? l2 * kLn2 : (st.m + l2) * kLn2;
-      prm.lse[size_t(head) * prm.tq + t] = lse;
     }
   }
 }
@@ -360,7 +493,7 @@ fwd_bf16_d128_kernel(FwdParams prm) {
 }  // namespace
 
 hipError_t launch_fwd_bf16_d128(const FwdParams& p, int n_items, hipStream_t stream) {
-  hipLaunchKernelGGL(fwd_bf16_d128_kernel, dim3(n_items), dim3(NTHR), 0, stream, p);
+  hipLaunchKernelGGL(fwd_bf16_d128_kernel, dim3(n_items), dim3(NTHR), 0, stream, p, p.items, p.tiles, p.rows);
   return hipGetLastError();
 }
 

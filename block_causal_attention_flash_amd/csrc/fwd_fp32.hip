@@ -22,7 +22,7 @@ __global__ void __launch_bounds__(64) fwd_fp32_kernel(FwdParams prm) {
   __shared__ float ks[BN][D];
   __shared__ float vs[BN][D];
   __shared__ float gk[D];
-  const int4 item = prm.items[blockIdx.x];
+  const int4 item = prm.items[2 * blockIdx.x];
   if (item.z == item.w) return;
   const int lane = threadIdx.x;
   const int kvh = item.y >> 16, head = item.y & 0xffff;
@@ -52,9 +52,11 @@ __global__ void __launch_bounds__(64) fwd_fp32_kernel(FwdParams prm) {
   const float* kbase = reinterpret_cast<const float*>(prm.k);
   const float* vbase = reinterpret_cast<const float*>(prm.v);
 
-  for (int sg = item.z; sg < item.w; ++sg) {
-    const int4 seg = prm.segs[sg];
-    for (int kt = seg.x; kt < seg.y; ++kt) {
+  for (int ti = item.z; ti < item.w; ++ti) {
+    const int code = prm.tiles[ti];
+    const int kt = code >> 1;
+    const bool masked = (code & 1) != 0;
+    {
       __syncthreads();
       // stage and normalise the key tile: 2 threads per key
       for (int e = lane; e < BN * D; e += 64) {
@@ -82,7 +84,7 @@ __global__ void __launch_bounds__(64) fwd_fp32_kernel(FwdParams prm) {
         float acc = 0.0f;
         for (int d = 0; d < D; ++d) acc += q[d] * ks[j][d];
         const int key = kt * BN + j;
-        if (seg.z && !(key >= rb.x && key < rb.y)) acc = kNegInf;
+        if (masked && !(key >= rb.x && key < rb.y)) acc = kNegInf;
         s[j] = acc;
         mx = fmaxf(mx, acc);
       }

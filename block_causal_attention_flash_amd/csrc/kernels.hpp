@@ -14,8 +14,8 @@ struct FwdParams {
   float* lse;
   const float* q_gain;
   const float* k_gain;
-  const int4* items;     // WorkItem[n_items]
-  const int4* segs;      // Segment[]
+  const int4* items;     // WorkItem[n_items], two int4 each
+  const int* tiles;      // key tile codes (kt * 2 + masked)
   const int2* rows;      // RowBounds[tq]
   float eps;
   float scale;           // softmax temperature on <q_hat, k_hat>

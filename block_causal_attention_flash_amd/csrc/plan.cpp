@@ -150,6 +150,10 @@ magi_status_t build_host_plan(const magi_attn_layout_t* L, const Tiling& tiling,
 
   P.segs.clear();
   P.qt_seg.assign(n_qt + 1, 0);
+  P.tile_codes.clear();
+  P.qt_tiles.assign(n_qt + 1, 0);
+  P.qt_full.assign(n_qt, 0);
+  std::vector<int32_t> masked_codes;
   std::vector<int64_t> qt_cost(n_qt, 0);
   std::vector<RowBounds> iv;
   for (int64_t qt = 0; qt < n_qt; ++qt) {
@@ -158,6 +162,8 @@ magi_status_t build_host_plan(const magi_attn_layout_t* L, const Tiling& tiling,
     int64_t lo = INT64_MAX, hi = 0;
     for (const RowBounds& b : iv) { lo = std::min<int64_t>(lo, b.lo); hi = std::max<int64_t>(hi, b.hi); }
     P.qt_seg[qt] = int32_t(P.segs.size());
+    P.qt_tiles[qt] = int32_t(P.tile_codes.size());
+    masked_codes.clear();
     if (hi > lo) {
       const int64_t kt0 = lo / bn, kt1 = (hi + bn - 1) / bn;
       int prev = -1;
@@ -173,6 +179,8 @@ magi_status_t build_host_plan(const magi_attn_layout_t* L, const Tiling& tiling,
             P.segs.push_back(Segment{int32_t(kt), int32_t(kt + 1), masked, 0});
           }
           qt_cost[qt] += 1;
+          if (masked) masked_codes.push_back(tile_code(kt, 1));
+          else P.tile_codes.push_back(tile_code(kt, 0));
           S.executed_pairs += (r1 - r0) * int64_t(bn);
           prev = masked;
         } else {
@@ -180,8 +188,11 @@ magi_status_t build_host_plan(const magi_attn_layout_t* L, const Tiling& tiling,
         }
       }
     }
+    P.qt_full[qt] = int32_t(P.tile_codes.size()) - P.qt_tiles[qt];
+    P.tile_codes.insert(P.tile_codes.end(), masked_codes.begin(), masked_codes.end());
   }
   P.qt_seg[n_qt] = int32_t(P.segs.size());
+  P.qt_tiles[n_qt] = int32_t(P.tile_codes.size());
   S.empty_pairs = n_qt * n_kt - S.full_pairs - S.boundary_pairs;
 
   // Work items: (query tile, KV head, group of hpw query heads).
@@ -190,7 +201,7 @@ magi_status_t build_host_plan(const magi_attn_layout_t* L, const Tiling& tiling,
   cands.reserve(size_t(n_qt) * P.hk * groups_per_kvh);
   for (int kvh = 0; kvh < P.hk; ++kvh)
     for (int64_t qt = 0; qt < n_qt; ++qt) {
-      if (P.qt_seg[qt + 1] == P.qt_seg[qt]) continue;
+      if (P.qt_tiles[qt + 1] == P.qt_tiles[qt]) continue;
       for (int hg = 0; hg < groups_per_kvh; ++hg) cands.push_back(Cand{qt_cost[qt], int32_t(qt), kvh, hg});
     }
   // Longest first; among equals, consecutive query tiles and head groups of
@@ -206,7 +217,8 @@ magi_status_t build_host_plan(const magi_attn_layout_t* L, const Tiling& tiling,
   std::vector<int64_t> load(kNumXcd, 0);
   auto make_item = [&](const Cand& c) {
     const int h0 = c.kvh * group + c.hg * hpw;
-    return WorkItem{int32_t(c.qt * bm), (c.kvh << 16) | h0, P.qt_seg[c.qt], P.qt_seg[c.qt + 1]};
+    return WorkItem{int32_t(c.qt * bm), (c.kvh << 16) | h0, P.qt_tiles[c.qt], P.qt_tiles[c.qt + 1], P.qt_full[c.qt],
+                    {0, 0, 0}};
   };
   if (P.hk % kNumXcd == 0 || kNumXcd % P.hk == 0) {
     // Each KV head owns a fixed set of XCDs (or each XCD owns a fixed set of
@@ -234,9 +246,9 @@ magi_status_t build_host_plan(const magi_attn_layout_t* L, const Tiling& tiling,
   P.items.reserve(maxlen * kNumXcd);
   for (size_t j = 0; j < maxlen; ++j)
     for (int x = 0; x < kNumXcd; ++x)
-      P.items.push_back(j < queues[x].size() ? queues[x][j] : WorkItem{0, 0, 0, 0});
+      P.items.push_back(j < queues[x].size() ? queues[x][j] : WorkItem{0, 0, 0, 0, 0, {0, 0, 0}});
   // Drop trailing padding.
-  while (!P.items.empty() && P.items.back().seg_begin == P.items.back().seg_end) P.items.pop_back();
+  while (!P.items.empty() && P.items.back().tile_begin == P.items.back().tile_end) P.items.pop_back();
 
   S.tile_q = bm;
   S.tile_kv = bn;

@@ -12,13 +12,19 @@ namespace magi {
 
 // One workgroup's work: query tokens [t0, t0 + tile_q) of `heads_per_item`
 // consecutive query heads starting at h0, all of KV head kvh, over the key
-// tiles listed in segments [seg_begin, seg_end).
+// tiles whose codes are tile_codes[tile_begin, tile_end); the first n_full of
+// them are full tiles, the rest boundary tiles.
 struct WorkItem {
   int32_t t0;
   int32_t heads;       // (kvh << 16) | h0
-  int32_t seg_begin;
-  int32_t seg_end;     // == seg_begin: padding item, the workgroup exits at once
+  int32_t tile_begin;
+  int32_t tile_end;    // == tile_begin: padding item, the workgroup exits at once
+  int32_t n_full;
+  int32_t pad[3];
 };
+
+// Key tile code: kt * 2 + masked (masked = 1 for boundary tiles).
+inline int32_t tile_code(int64_t kt, int masked) { return int32_t(kt * 2 + masked); }
 
 // A run of consecutive key tiles of one class for one query tile.
 struct Segment {
@@ -48,6 +54,9 @@ struct HostPlan {
   std::vector<RowBounds> rows;       // [tq]
   std::vector<Segment> segs;         // all query tiles' segments, concatenated
   std::vector<int32_t> qt_seg;       // [n_qt + 1] segment range per query tile
+  std::vector<int32_t> tile_codes;   // per query tile: full key tiles ascending, then boundary tiles ascending
+  std::vector<int32_t> qt_tiles;     // [n_qt + 1] range in tile_codes per query tile
+  std::vector<int32_t> qt_full;      // [n_qt] number of full key tiles per query tile
   std::vector<WorkItem> items;       // launch order (XCD-interleaved, padded)
   magi_attn_stats_t stats{};
 };
