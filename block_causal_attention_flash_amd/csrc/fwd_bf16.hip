@@ -8,10 +8,10 @@
 // bf16 matrix cores (v_mfma_f32_32x32x16_bf16).
 //
 // Workgroup = one work item: 256 (token, head) rows of `heads_per_item`
-// query heads that share one KV head; 4 waves, one per SIMD, 64 rows each
-// (two 32-row MFMA blocks). Per 64-key tile:
+// query heads that share one KV head; 8 waves, two per SIMD, 32 rows each
+// (one 32-row MFMA block). Per 32-key tile:
 //   * K and V tiles are copied from global memory straight into LDS rings
-//     (buffer_load ... lds, zero fill past T_k) two tiles ahead, and serve all
+//     (buffer_load ... lds, zero fill past T_k) four tiles ahead, and serve all
 //     256 rows: K/V leave L2 once per workgroup, not once per query head;
 //   * each staged K tile is RMS-normalised in LDS once, by the workgroup, one
 //     tile ahead of its use (k_hat = k / rms(k), rounded to bf16); g_k is
@@ -19,11 +19,11 @@
 //   * S^T = K Q'^T (lane = query row, 16 keys per lane in registers);
 //   * O^T += V^T P^T with V read through ds_read_b64_tr_b16 from the row-major
 //     V tile.
-// Software pipeline per iteration i: phase 1 issues the 32 MFMAs of S(i);
-// phase 2 issues the 32 MFMAs of P(i-1) V(i-1) while the vector ALUs turn S(i)
-// into P(i) (scale, mask, exp2, round to bf16, row sums). One wave per SIMD
-// keeps the matrix pipe fed from a single instruction stream; a workgroup
-// barrier per tile recycles the LDS rings.
+// Software pipeline per iteration i: phase 1 issues the MFMAs of S(i);
+// phase 2 issues the MFMAs of P(i-1) V(i-1) while the vector ALUs turn S(i)
+// into P(i) (mask, exp2, round to bf16, row sums), so each wave's vector work
+// overlaps its own and its SIMD partner's matrix work. A workgroup barrier
+// per tile recycles the LDS rings.
 //
 // Queries are normalised in the prologue (RMS over head_dim, times
 // g_q * g_k * scale * log2 e) and held in registers as bf16 MFMA operands.
@@ -50,15 +50,20 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 #define LDS_PTR(T, p) ((__attribute__((address_space(3))) T*)(p))
 
 constexpr int D = 128;
-constexpr int BN = 64;
-constexpr int NWAVE = 4;
+constexpr int BN = 32;
+constexpr int NWAVE = 8;                              // two waves per SIMD
+constexpr int NRB = 256 / 32 / NWAVE;                 // 32-row MFMA blocks per wave
 constexpr int NTHR = NWAVE * 64;
-constexpr int LOOKAHEAD = 2;                          // tiles in flight ahead of use
+constexpr int LOOKAHEAD = 4;                          // tiles in flight ahead of use
 constexpr int KSTAGES = LOOKAHEAD + 2;                // K(i), K(i+1), K(i+2)..K(i+1+LA)
 constexpr int VSTAGES = LOOKAHEAD + 2;                // V(i-1), V(i)..V(i+LA)
 constexpr int ROW_BYTES = D * 2;                      // 256
-constexpr int TILE_BYTES = BN * ROW_BYTES;            // 16 KiB
-constexpr int UNITS = TILE_BYTES / (NTHR * 16);       // 4 16-byte copies per thread per tensor
+constexpr int TILE_BYTES = BN * ROW_BYTES;            // 8 KiB
+constexpr int UNITS = TILE_BYTES / (NTHR * 16);       // 16-byte copies per thread per tensor
+constexpr int TPK = NTHR / BN;                        // threads per key when normalising K
+constexpr int CPT = 16 / TPK;                         // 16-byte chunks per thread when normalising K
+static_assert(UNITS >= 1 && CPT >= 1 && NRB >= 1, "tile shape");
+constexpr unsigned kNoTile = 0xFFFFFFF0u;             // buffer offset past any K/V tensor: reads zeros
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kStaticBound = 40.0f;
@@ -126,6 +131,7 @@ __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(
 //   V: row-major [key][128], 64-byte segment g of key j stored at g ^ (j & 3)
 // Each wave instruction writes 1 KiB of LDS (lane i -> +16 i); the lane's
 // global source is chosen so the image comes out swizzled.
+// kt < 0: no tile; the copies read past the tensor and write zeros.
 __device__ __forceinline__ void issue_k(i32x4 rsrc, unsigned lds_stage, int kt, int kvh, int hk, int wave,
                                         int lane) {
 #pragma unroll
@@ -134,7 +140,7 @@ __device__ __forceinline__ void issue_k(i32x4 rsrc, unsigned lds_stage, int kt, 
     const int u = blk * 64 + lane;
     const int key = u >> 4, pc = u & 15;
     const unsigned row = unsigned((kt * BN + key) * hk + kvh) * ROW_BYTES;
-    dma16(rsrc, row + unsigned((pc ^ (key & 15)) * 16), lds_stage + blk * 1024);
+    dma16(rsrc, kt < 0 ? kNoTile : row + unsigned((pc ^ (key & 15)) * 16), lds_stage + blk * 1024);
   }
 }
 
@@ -147,68 +153,63 @@ __device__ __forceinline__ void issue_v(i32x4 rsrc, unsigned lds_stage, int kt, 
     const int key = u >> 4, pc = u & 15;
     const unsigned row = unsigned((kt * BN + key) * hk + kvh) * ROW_BYTES;
     const int cv = ((((pc >> 2) ^ (key & 3)) << 2) | (pc & 3));
-    dma16(rsrc, row + unsigned(cv * 16), lds_stage + blk * 1024);
+    dma16(rsrc, kt < 0 ? kNoTile : row + unsigned(cv * 16), lds_stage + blk * 1024);
   }
 }
 
 // Normalises a staged K tile in place: k_hat_j = k_j / sqrt(mean_d k_j^2 + eps),
-// rounded to bf16 (the gain g_k is folded into the queries). Four threads
-// per key, 32 dims each; the swizzled layout is kept.
+// rounded to bf16 (the gain g_k is folded into the queries). TPK threads per
+// key, CPT 16-byte chunks each; the swizzled layout is kept.
 __device__ __forceinline__ void key_normalize(unsigned char* kst, float eps) {
   const int tid = threadIdx.x;
-  const int key = tid >> 2, part = tid & 3;
+  const int key = tid / TPK, part = tid % TPK;
   unsigned char* row = kst + key * ROW_BYTES;
-  bf16x8 x[4];
+  bf16x8 x[CPT];
   float ss = 0.0f;
 #pragma unroll
-  for (int c = 0; c < 4; ++c) {
-    x[c] = *LDS_PTR(const bf16x8, row + (((4 * part + c) ^ (key & 15)) * 16));
+  for (int c = 0; c < CPT; ++c) {
+    x[c] = *LDS_PTR(const bf16x8, row + (((CPT * part + c) ^ (key & 15)) * 16));
     ss = sumsq8(x[c], ss);
   }
-  ss += dpp<0xB1>(ss);    // quad_perm [1,0,3,2]
-  ss += dpp<0x4E>(ss);    // quad_perm [2,3,0,1]
+  ss += dpp<0xB1>(ss);                    // quad_perm [1,0,3,2]
+  ss += dpp<0x4E>(ss);                    // quad_perm [2,3,0,1]
+  if (TPK >= 8) ss += dpp<0x141>(ss);     // row_half_mirror: the other quad of 8 lanes
+  if (TPK >= 16) ss += dpp<0x140>(ss);    // row_mirror: the other half of 16 lanes
   const float r = __builtin_amdgcn_rsqf(ss * (1.0f / D) + eps);
 #pragma unroll
-  for (int c = 0; c < 4; ++c) {
+  for (int c = 0; c < CPT; ++c) {
     bf16x8 y;
 #pragma unroll
     for (int j = 0; j < 8; ++j) y[j] = (__bf16)(float(x[c][j]) * r);
-    *LDS_PTR(bf16x8, row + (((4 * part + c) ^ (key & 15)) * 16)) = y;
+    *LDS_PTR(bf16x8, row + (((CPT * part + c) ^ (key & 15)) * 16)) = y;
   }
 }
 
 struct WaveState {
-  bf16x8 qf[2][8];       // B operands of S^T, per row block: lane row (l & 31), dims (2ks + (l>>5)) * 8 ..
-  f32x16 o[2][4];        // O^T accumulators: lane row (l & 31), 4 dim blocks of 32
-  bf16x8 p[2][2][2];     // P of the previous tile, per (row block, key block, k-step)
-  float lsum[2];         // partial row sums over this lane's half of the keys
-  float m[2];            // online path: reference maximum (log2 units)
-  int lo[2], hi[2];      // key bounds of the lane's rows
+  bf16x8 qf[NRB][8];     // B operands of S^T, per row block: lane row (l & 31), dims (2ks + (l>>5)) * 8 ..
+  f32x16 o[NRB][4];      // O^T accumulators: lane row (l & 31), 4 dim blocks of 32
+  bf16x8 p[NRB][2];      // P of the previous tile, per (row block, 16-key k-step)
+  float lsum[NRB];       // partial row sums over this lane's half of the keys
+  float m[NRB];          // online path: reference maximum (log2 units)
+  int lo[NRB], hi[NRB];  // key bounds of the lane's rows
 };
 
 // Phase 1: S^T(tile in stage kst) for both row blocks.
-__device__ __forceinline__ void qk_tile(const unsigned char* kst, const WaveState& st, f32x16 (&s)[2][2], int lane) {
+__device__ __forceinline__ void qk_tile(const unsigned char* kst, const WaveState& st, f32x16 (&s)[NRB], int lane) {
   const int l31 = lane & 31, hi5 = lane >> 5;
 #pragma unroll
-  for (int rb = 0; rb < 2; ++rb)
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) s[rb][kb] = f32x16{};
+  for (int rb = 0; rb < NRB; ++rb) s[rb] = f32x16{};
 #pragma unroll
   for (int ks = 0; ks < 8; ++ks) {
     const int c = (2 * ks + hi5) ^ (lane & 15);
-    bf16x8 a[2];
+    const bf16x8 a = *LDS_PTR(const bf16x8, kst + l31 * ROW_BYTES + c * 16);
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) a[kb] = *LDS_PTR(const bf16x8, kst + (kb * 32 + l31) * ROW_BYTES + c * 16);
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int rb = 0; rb < 2; ++rb)
-        s[rb][kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[kb], st.qf[rb][ks], s[rb][kb], 0, 0, 0);
+    for (int rb = 0; rb < NRB; ++rb) s[rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, st.qf[rb][ks], s[rb], 0, 0, 0);
   }
 }
 
 // Phase 2 (MFMA part): O^T += V^T P^T for the previous tile.
-// k-step (kb, t) covers keys kb*32 + t*16 + {s*8 + hi5*4 + r}: the P layout.
+// k-step t covers keys t*16 + {s*8 + hi5*4 + r}: the P layout.
 // ds_read_b64_tr_b16: lane 16b+n receives, for r = 0..3, element n%4 of what
 // lane 16b + 4r + n/4 read; lane 16b+i therefore reads 4 dims of key
 // (.. + (b>>1)*4 + i/4) at dim (b&1)*16 + (i%4)*4 of the 32-dim block.
@@ -217,54 +218,48 @@ __device__ __forceinline__ void pv_tile(const unsigned char* vst, WaveState& st,
   const int key_in = (b >> 1) * 4 + (n >> 2);
   const int dim_in = (b & 1) * 16 + (n & 3) * 4;
 #pragma unroll
-  for (int kb = 0; kb < 2; ++kb)
+  for (int t = 0; t < 2; ++t)
 #pragma unroll
-    for (int t = 0; t < 2; ++t)
+    for (int db = 0; db < 4; ++db) {
+      i16x4 h[2];
 #pragma unroll
-      for (int db = 0; db < 4; ++db) {
-        i16x4 h[2];
-#pragma unroll
-        for (int sidx = 0; sidx < 2; ++sidx) {
-          const int key = kb * 32 + t * 16 + sidx * 8 + key_in;
-          const int off = key * ROW_BYTES + ((db ^ (key & 3)) * 64) + dim_in * 2;
-          h[sidx] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(i16x4, vst + off));
-        }
-        const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(h[0], h[1], 0, 1, 2, 3, 4, 5, 6, 7));
-#pragma unroll
-        for (int rb = 0; rb < 2; ++rb)
-          st.o[rb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, st.p[rb][kb][t], st.o[rb][db], 0, 0, 0);
+      for (int sidx = 0; sidx < 2; ++sidx) {
+        const int key = t * 16 + sidx * 8 + key_in;
+        const int off = key * ROW_BYTES + ((db ^ (key & 3)) * 64) + dim_in * 2;
+        h[sidx] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(i16x4, vst + off));
       }
+      const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(h[0], h[1], 0, 1, 2, 3, 4, 5, 6, 7));
+#pragma unroll
+      for (int rb = 0; rb < NRB; ++rb)
+        st.o[rb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, st.p[rb][t], st.o[rb][db], 0, 0, 0);
+    }
 }
 
-// Phase 2 (vector part): S(i) -> P(i). Lane holds keys kb*32 + u*8 + hi5*4 + e
+// Phase 2 (vector part): S(i) -> P(i). Lane holds keys u*8 + hi5*4 + e
 // (u, e = 0..3) of its row for each row block.
 template <bool MASKED, bool STATIC>
-__device__ __forceinline__ void softmax_tile(f32x16 (&s)[2][2], int kt, WaveState& st, bf16x8 (&pn)[2][2][2],
-                                             float (&alpha)[2], int lane) {
+__device__ __forceinline__ void softmax_tile(f32x16 (&s)[NRB], int kt, WaveState& st, bf16x8 (&pn)[NRB][2],
+                                             float (&alpha)[NRB], int lane) {
   const int hi5 = lane >> 5;
 #pragma unroll
-  for (int rb = 0; rb < 2; ++rb) {
+  for (int rb = 0; rb < NRB; ++rb) {
     if (MASKED) {
       // key allowed  <=>  (key - lo) < (hi - lo) as unsigned
       const unsigned base = unsigned(kt * BN + hi5 * 4 - st.lo[rb]);
       const unsigned len = unsigned(st.hi[rb] - st.lo[rb]);
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+      for (int u = 0; u < 4; ++u)
 #pragma unroll
-        for (int u = 0; u < 4; ++u)
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const unsigned rel = base + unsigned(kb * 32 + u * 8 + e);
-            s[rb][kb][u * 4 + e] = rel < len ? s[rb][kb][u * 4 + e] : kNegInf;
-          }
+        for (int e = 0; e < 4; ++e) {
+          const unsigned rel = base + unsigned(u * 8 + e);
+          s[rb][u * 4 + e] = rel < len ? s[rb][u * 4 + e] : kNegInf;
+        }
     }
     alpha[rb] = 1.0f;
     if (!STATIC) {
       float mx = kNegInf;
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[rb][kb][i]);
+      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[rb][i]);
       mx = fmaxf(mx, xor32(mx));
       // keep the reference maximum unless the tile exceeds it by > 2^8
       const float m_new = (mx > st.m[rb] + kRescaleSlack) ? mx : st.m[rb];
@@ -272,53 +267,53 @@ __device__ __forceinline__ void softmax_tile(f32x16 (&s)[2][2], int kt, WaveStat
       st.m[rb] = m_new;
       const float m_use = (m_new == kNegInf) ? 0.0f : m_new;
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) s[rb][kb][i] -= m_use;
+      for (int i = 0; i < 16; ++i) s[rb][i] -= m_use;
     }
     const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
     float ls = 0.0f;
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+    for (int t = 0; t < 2; ++t)
 #pragma unroll
-      for (int t = 0; t < 2; ++t)
-#pragma unroll
-        for (int j = 0; j < 8; j += 2) {
-          const float e0 = __builtin_amdgcn_exp2f(s[rb][kb][t * 8 + j]);
-          const float e1 = __builtin_amdgcn_exp2f(s[rb][kb][t * 8 + j + 1]);
-          const bf16x2 pp = {(__bf16)e0, (__bf16)e1};
-          pn[rb][kb][t][j] = pp[0];
-          pn[rb][kb][t][j + 1] = pp[1];
-          ls = __builtin_amdgcn_fdot2_f32_bf16(pp, ones, ls, false);
-        }
+      for (int j = 0; j < 8; j += 2) {
+        const float e0 = __builtin_amdgcn_exp2f(s[rb][t * 8 + j]);
+        const float e1 = __builtin_amdgcn_exp2f(s[rb][t * 8 + j + 1]);
+        const bf16x2 pp = {(__bf16)e0, (__bf16)e1};
+        pn[rb][t][j] = pp[0];
+        pn[rb][t][j + 1] = pp[1];
+        ls = __builtin_amdgcn_fdot2_f32_bf16(pp, ones, ls, false);
+      }
     st.lsum[rb] = st.lsum[rb] * alpha[rb] + ls;
   }
 }
 
 template <bool MASKED, bool STATIC>
-__device__ __forceinline__ void iteration(const unsigned char* kst, const unsigned char* vst_prev, int kt,
-                                          WaveState& st, int lane) {
-  f32x16 s[2][2];
+__device__ __forceinline__ void iteration(unsigned char* kst_next, const unsigned char* kst,
+                                          const unsigned char* vst_prev, int kt, float eps, WaveState& st, int lane) {
+  // phase 1: S(i) on the matrix cores; K(i+1) normalised on the vector ALUs
+  f32x16 s[NRB];
   qk_tile(kst, st, s, lane);
+  key_normalize(kst_next, eps);
+  // phase 2: P(i-1) V(i-1) on the matrix cores; softmax(i) on the vector ALUs
   pv_tile(vst_prev, st, lane);
-  bf16x8 pn[2][2][2];
-  float alpha[2];
+  bf16x8 pn[NRB][2];
+  float alpha[NRB];
   softmax_tile<MASKED, STATIC>(s, kt, st, pn, alpha, lane);
   if (!STATIC) {
     // P(i-1) V(i-1) was accumulated against the old reference maximum.
-    if (__builtin_amdgcn_ballot_w64(alpha[0] != 1.0f || alpha[1] != 1.0f)) {
+    bool any = false;
 #pragma unroll
-      for (int rb = 0; rb < 2; ++rb)
+    for (int rb = 0; rb < NRB; ++rb) any |= alpha[rb] != 1.0f;
+    if (__builtin_amdgcn_ballot_w64(any)) {
+#pragma unroll
+      for (int rb = 0; rb < NRB; ++rb)
 #pragma unroll
         for (int db = 0; db < 4; ++db) st.o[rb][db] *= alpha[rb];
     }
   }
 #pragma unroll
-  for (int rb = 0; rb < 2; ++rb)
+  for (int rb = 0; rb < NRB; ++rb)
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int t = 0; t < 2; ++t) st.p[rb][kb][t] = pn[rb][kb][t];
+    for (int t = 0; t < 2; ++t) st.p[rb][t] = pn[rb][t];
 }
 
 // Per-workgroup constants of the tile loop.
@@ -330,24 +325,17 @@ struct LoopCtx {
   float eps;
 };
 
-// Top of iteration i: wait for K(i+1) and V(i) (older than the copies issued
-// in iteration i-1), barrier, start the copies of K(i+1+LA) and V(i+LA), and
-// normalise K(i+1) for the next iteration.
+// Top of iteration i: wait for K(i+1) and V(i) (issued LOOKAHEAD iterations
+// earlier; the copies of the LOOKAHEAD-1 iterations since may still fly), barrier, start the copies of K(i+1+LA) and V(i+LA)
+// (zeros past the last tile).
 __device__ __forceinline__ void loop_top(Smem& sm, const LoopCtx& c, int i) {
-  if (i > 0) {
-    const int younger = (i + LOOKAHEAD < c.n_tiles ? UNITS : 0) + (i + LOOKAHEAD - 1 < c.n_tiles ? UNITS : 0);
-    if (younger == 2 * UNITS) wait_vmcnt<2 * UNITS>();
-    else if (younger == UNITS) wait_vmcnt<UNITS>();
-    else wait_vmcnt<0>();
-  }
+  wait_vmcnt<(LOOKAHEAD - 1) * 2 * UNITS>();
   lds_barrier();
-  if (i + 1 + LOOKAHEAD < c.n_tiles)
-    issue_k(c.rsk, c.k_base + ((i + 1 + LOOKAHEAD) % KSTAGES) * TILE_BYTES, c.tiles[i + 1 + LOOKAHEAD] >> 1, c.kvh,
-            c.hk, c.wave, c.lane);
-  if (i + LOOKAHEAD < c.n_tiles)
-    issue_v(c.rsv, c.v_base + ((i + LOOKAHEAD) % VSTAGES) * TILE_BYTES, c.tiles[i + LOOKAHEAD] >> 1, c.kvh, c.hk,
-            c.wave, c.lane);
-  if (i + 1 < c.n_tiles) key_normalize(sm.k[(i + 1) % KSTAGES], c.eps);
+  const int jk = i + 1 + LOOKAHEAD, jv = i + LOOKAHEAD;
+  const int ck = c.tiles[jk < c.n_tiles ? jk : c.n_tiles - 1];
+  const int cv = c.tiles[jv < c.n_tiles ? jv : c.n_tiles - 1];
+  issue_k(c.rsk, c.k_base + (jk % KSTAGES) * TILE_BYTES, jk < c.n_tiles ? ck >> 1 : -1, c.kvh, c.hk, c.wave, c.lane);
+  issue_v(c.rsv, c.v_base + (jv % VSTAGES) * TILE_BYTES, jv < c.n_tiles ? cv >> 1 : -1, c.kvh, c.hk, c.wave, c.lane);
 }
 
 // Full tiles first (no mask code), then boundary tiles; one loop body each.
@@ -355,15 +343,17 @@ template <bool STATIC>
 __device__ __forceinline__ void run_tiles(Smem& sm, const LoopCtx& c, int n_full, WaveState& st) {
   for (int i = 0; i < n_full; ++i) {
     loop_top(sm, c, i);
-    iteration<false, STATIC>(sm.k[i % KSTAGES], sm.v[(i + VSTAGES - 1) % VSTAGES], c.tiles[i] >> 1, st, c.lane);
+    iteration<false, STATIC>(sm.k[(i + 1) % KSTAGES], sm.k[i % KSTAGES], sm.v[(i + VSTAGES - 1) % VSTAGES],
+                             c.tiles[i] >> 1, c.eps, st, c.lane);
   }
   for (int i = n_full; i < c.n_tiles; ++i) {
     loop_top(sm, c, i);
-    iteration<true, STATIC>(sm.k[i % KSTAGES], sm.v[(i + VSTAGES - 1) % VSTAGES], c.tiles[i] >> 1, st, c.lane);
+    iteration<true, STATIC>(sm.k[(i + 1) % KSTAGES], sm.k[i % KSTAGES], sm.v[(i + VSTAGES - 1) % VSTAGES],
+                            c.tiles[i] >> 1, c.eps, st, c.lane);
   }
 }
 
-__global__ void __launch_bounds__(NTHR) __attribute__((amdgpu_waves_per_eu(1, 1)))
+__global__ void __launch_bounds__(NTHR) __attribute__((amdgpu_waves_per_eu(NRB == 1 ? 2 : 1, NRB == 1 ? 2 : 1)))
 fwd_bf16_d128_kernel(FwdParams prm, const int4* __restrict__ items, const int* __restrict__ tiles,
                      const int2* __restrict__ rows) {
   __shared__ __attribute__((aligned(1024))) Smem sm;
@@ -385,10 +375,10 @@ fwd_bf16_d128_kernel(FwdParams prm, const int4* __restrict__ items, const int* _
   const unsigned v_base = __builtin_amdgcn_readfirstlane(lds_addr(&sm.v[0][0]));
 #pragma unroll
   for (int j = 0; j <= LOOKAHEAD; ++j)
-    if (j < n_tiles) issue_k(rsk, k_base + j * TILE_BYTES, tiles[tb + j] >> 1, kvh, prm.hk, wave, lane);
+    issue_k(rsk, k_base + j * TILE_BYTES, j < n_tiles ? tiles[tb + j] >> 1 : -1, kvh, prm.hk, wave, lane);
 #pragma unroll
   for (int j = 0; j < LOOKAHEAD; ++j)
-    if (j < n_tiles) issue_v(rsv, v_base + j * TILE_BYTES, tiles[tb + j] >> 1, kvh, prm.hk, wave, lane);
+    issue_v(rsv, v_base + j * TILE_BYTES, j < n_tiles ? tiles[tb + j] >> 1 : -1, kvh, prm.hk, wave, lane);
 
   // V stage of tile -1 holds zeros: the first iteration's P(-1) V(-1) adds 0.
   {
@@ -400,20 +390,20 @@ fwd_bf16_d128_kernel(FwdParams prm, const int4* __restrict__ items, const int* _
   if (tid < D) sm.gqk[tid] = prm.q_gain[tid] * prm.k_gain[tid] * (prm.scale * kLog2e);
 
   WaveState st;
-  int tok[2], head[2];
-  bool valid[2];
+  int tok[NRB], head[NRB];
+  bool valid[NRB];
 #pragma unroll
-  for (int rb = 0; rb < 2; ++rb) {
-    const int blk = wave * 2 + rb;
+  for (int rb = 0; rb < NRB; ++rb) {
+    const int blk = wave * NRB + rb;
     head[rb] = h0 + blk / rb_per_head;
     tok[rb] = item.x + (blk % rb_per_head) * 32 + (lane & 31);
     valid[rb] = tok[rb] < prm.tq;
   }
 
   // ---- query prologue: load, RMS-normalise, fold gains/temperature, to bf16
-  bf16x8 qr[2][8];
+  bf16x8 qr[NRB][8];
 #pragma unroll
-  for (int rb = 0; rb < 2; ++rb) {
+  for (int rb = 0; rb < NRB; ++rb) {
     const __bf16* qrow = reinterpret_cast<const __bf16*>(prm.q) + (size_t(tok[rb]) * prm.hq + head[rb]) * D;
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks)
@@ -422,7 +412,7 @@ fwd_bf16_d128_kernel(FwdParams prm, const int4* __restrict__ items, const int* _
   __syncthreads();                                     // gqk and the zeroed V stage visible
   float bound_max = 0.0f;
 #pragma unroll
-  for (int rb = 0; rb < 2; ++rb) {
+  for (int rb = 0; rb < NRB; ++rb) {
     float ss = 0.0f;
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks) ss = sumsq8(qr[rb][ks], ss);
@@ -446,9 +436,7 @@ fwd_bf16_d128_kernel(FwdParams prm, const int4* __restrict__ items, const int* _
 #pragma unroll
     for (int db = 0; db < 4; ++db) st.o[rb][db] = f32x16{};
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int t = 0; t < 2; ++t) st.p[rb][kb][t] = bf16x8{};
+    for (int t = 0; t < 2; ++t) st.p[rb][t] = bf16x8{};
     st.lsum[rb] = 0.0f;
     st.m[rb] = kNegInf;
   }
@@ -467,7 +455,7 @@ fwd_bf16_d128_kernel(FwdParams prm, const int4* __restrict__ items, const int* _
 
   // ---- epilogue
 #pragma unroll
-  for (int rb = 0; rb < 2; ++rb) {
+  for (int rb = 0; rb < NRB; ++rb) {
     const float lsum = st.lsum[rb] + xor32(st.lsum[rb]);
     if (valid[rb]) {
       const float inv = 1.0f / lsum;
