@@ -50,20 +50,23 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 #define LDS_PTR(T, p) ((__attribute__((address_space(3))) T*)(p))
 
 constexpr int D = 128;
-constexpr int BN = 32;
+constexpr int BN = 32;                                // keys per tile
 constexpr int NWAVE = 8;                              // two waves per SIMD
 constexpr int NRB = 256 / 32 / NWAVE;                 // 32-row MFMA blocks per wave
 constexpr int NTHR = NWAVE * 64;
-constexpr int LOOKAHEAD = 4;                          // tiles in flight ahead of use
-constexpr int KSTAGES = LOOKAHEAD + 2;                // K(i), K(i+1), K(i+2)..K(i+1+LA)
-constexpr int VSTAGES = LOOKAHEAD + 2;                // V(i-1), V(i)..V(i+LA)
+constexpr int NSTAGE = 8;                             // LDS ring depth (K and V each)
+constexpr int LOOKAHEAD = NSTAGE - 2;                 // copies issued this many tiles ahead
 constexpr int ROW_BYTES = D * 2;                      // 256
 constexpr int TILE_BYTES = BN * ROW_BYTES;            // 8 KiB
 constexpr int UNITS = TILE_BYTES / (NTHR * 16);       // 16-byte copies per thread per tensor
 constexpr int TPK = NTHR / BN;                        // threads per key when normalising K
 constexpr int CPT = 16 / TPK;                         // 16-byte chunks per thread when normalising K
-static_assert(UNITS >= 1 && CPT >= 1 && NRB >= 1, "tile shape");
-constexpr unsigned kNoTile = 0xFFFFFFF0u;             // buffer offset past any K/V tensor: reads zeros
+static_assert(UNITS == 1 && CPT >= 1 && NRB >= 1, "tile shape");
+// Copies in flight that may be younger than the ones a tile needs: the
+// LOOKAHEAD-1 later iterations (K and V each) plus the V copy issued right
+// after the needed K copy.
+constexpr int WAIT_YOUNGER = (LOOKAHEAD - 1) * 2 * UNITS + UNITS;
+constexpr unsigned kNoTile = 0x80000000u;             // scalar offset past any K/V tensor (< 2 GiB): zeros
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kStaticBound = 40.0f;
@@ -71,8 +74,8 @@ constexpr float kRescaleSlack = 8.0f;
 constexpr float kNegInf = -__builtin_inff();
 
 struct Smem {
-  unsigned char k[KSTAGES][TILE_BYTES];
-  unsigned char v[VSTAGES][TILE_BYTES];
+  unsigned char k[NSTAGE][TILE_BYTES];
+  unsigned char v[NSTAGE][TILE_BYTES];
   float gqk[D];
 };
 
@@ -108,13 +111,14 @@ __device__ __forceinline__ i32x4 make_rsrc(const void* base, unsigned bytes) {
   return r;
 }
 
-// 16-byte copy global -> LDS: lane i of the wave writes LDS byte m0 + 16 i.
-// Issued through asm so that the compiler does not order later LDS reads of
-// other ring stages behind it; completion is awaited explicitly (vmcnt).
-__device__ __forceinline__ void dma16(i32x4 rsrc, unsigned voff, unsigned lds) {
-  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+// 16-byte copy global -> LDS at buffer offset voff + soff: lane i of the wave
+// writes LDS byte m0 + 16 i. Issued through asm so that the compiler does not
+// order later LDS reads of other ring stages behind it; completion is awaited
+// explicitly (vmcnt) before the barrier that publishes the stage.
+__device__ __forceinline__ void dma16(i32x4 rsrc, unsigned voff, unsigned soff, unsigned lds) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
                :
-               : "s"(lds), "v"(voff), "s"(rsrc)
+               : "s"(lds), "v"(voff), "s"(rsrc), "s"(soff)
                : "memory", "m0");
 }
 
@@ -126,63 +130,55 @@ __device__ __forceinline__ void wait_vmcnt() {
 // All LDS traffic of this wave finished, then the workgroup barrier.
 __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" : : : "memory"); }
 
-// Copies key tile kt of KV head kvh into LDS. Images:
+// Per-lane constant offsets, computed once. LDS images of a 32-key tile:
 //   K: row-major [key][128], 16-byte chunk c of key j stored at chunk c ^ (j & 15)
 //   V: row-major [key][128], 64-byte segment g of key j stored at g ^ (j & 3)
-// Each wave instruction writes 1 KiB of LDS (lane i -> +16 i); the lane's
-// global source is chosen so the image comes out swizzled.
-// kt < 0: no tile; the copies read past the tensor and write zeros.
-__device__ __forceinline__ void issue_k(i32x4 rsrc, unsigned lds_stage, int kt, int kvh, int hk, int wave,
-                                        int lane) {
-#pragma unroll
-  for (int i = 0; i < UNITS; ++i) {
-    const int blk = i * NWAVE + wave;
-    const int u = blk * 64 + lane;
-    const int key = u >> 4, pc = u & 15;
-    const unsigned row = unsigned((kt * BN + key) * hk + kvh) * ROW_BYTES;
-    dma16(rsrc, kt < 0 ? kNoTile : row + unsigned((pc ^ (key & 15)) * 16), lds_stage + blk * 1024);
-  }
-}
+// Global source of the lane's 16-byte copy unit u = wave*64 + lane (key u/16,
+// physical chunk u%16) within KV head kvh, relative to the tile's first key.
+struct LaneOffsets {
+  unsigned dma_k, dma_v;     // buffer offsets (the tile part goes in the scalar offset)
+  int kq[8];                 // S operand of k-step ks: key (l & 31), chunk 2ks + (l >> 5)
+  int vq[4];                 // P V operand, dim block db: tr-read base of key (b>>1)*4 + n/4
+  int kn;                    // K normalisation: this thread's chunk
+};
 
-__device__ __forceinline__ void issue_v(i32x4 rsrc, unsigned lds_stage, int kt, int kvh, int hk, int wave,
-                                        int lane) {
+__device__ __forceinline__ LaneOffsets lane_offsets(int tid, int hk, int kvh) {
+  LaneOffsets o;
+  const int lane = tid & 63;
+  const int u = tid;                                 // one unit per thread per tensor
+  const int key = u >> 4, pc = u & 15;
+  const unsigned row = unsigned(key * hk + kvh) * ROW_BYTES;
+  o.dma_k = row + unsigned((pc ^ (key & 15)) * 16);
+  o.dma_v = row + unsigned(((((pc >> 2) ^ (key & 3)) << 2) | (pc & 3)) * 16);
+  const int l31 = lane & 31, hi5 = lane >> 5;
 #pragma unroll
-  for (int i = 0; i < UNITS; ++i) {
-    const int blk = i * NWAVE + wave;
-    const int u = blk * 64 + lane;
-    const int key = u >> 4, pc = u & 15;
-    const unsigned row = unsigned((kt * BN + key) * hk + kvh) * ROW_BYTES;
-    const int cv = ((((pc >> 2) ^ (key & 3)) << 2) | (pc & 3));
-    dma16(rsrc, kt < 0 ? kNoTile : row + unsigned(cv * 16), lds_stage + blk * 1024);
-  }
+  for (int ks = 0; ks < 8; ++ks) o.kq[ks] = l31 * ROW_BYTES + (((2 * ks + hi5) ^ (lane & 15)) * 16);
+  const int b = lane >> 4, n = lane & 15;
+  const int key_in = (b >> 1) * 4 + (n >> 2);
+  const int dim_in = (b & 1) * 16 + (n & 3) * 4;
+#pragma unroll
+  for (int db = 0; db < 4; ++db) o.vq[db] = key_in * ROW_BYTES + ((db ^ (key_in & 3)) * 64) + dim_in * 2;
+  const int nkey = tid / TPK, part = tid % TPK;
+  o.kn = nkey * ROW_BYTES + (((CPT * part) ^ (nkey & 15)) * 16);
+  return o;
 }
 
 // Normalises a staged K tile in place: k_hat_j = k_j / sqrt(mean_d k_j^2 + eps),
 // rounded to bf16 (the gain g_k is folded into the queries). TPK threads per
-// key, CPT 16-byte chunks each; the swizzled layout is kept.
-__device__ __forceinline__ void key_normalize(unsigned char* kst, float eps) {
-  const int tid = threadIdx.x;
-  const int key = tid / TPK, part = tid % TPK;
-  unsigned char* row = kst + key * ROW_BYTES;
-  bf16x8 x[CPT];
-  float ss = 0.0f;
-#pragma unroll
-  for (int c = 0; c < CPT; ++c) {
-    x[c] = *LDS_PTR(const bf16x8, row + (((CPT * part + c) ^ (key & 15)) * 16));
-    ss = sumsq8(x[c], ss);
-  }
+// key, one 16-byte chunk each.
+__device__ __forceinline__ void key_normalize(unsigned char* kst, int kn, float eps) {
+  auto* p = LDS_PTR(bf16x8, kst + kn);
+  const bf16x8 x = *p;
+  float ss = sumsq8(x, 0.0f);
   ss += dpp<0xB1>(ss);                    // quad_perm [1,0,3,2]
   ss += dpp<0x4E>(ss);                    // quad_perm [2,3,0,1]
-  if (TPK >= 8) ss += dpp<0x141>(ss);     // row_half_mirror: the other quad of 8 lanes
-  if (TPK >= 16) ss += dpp<0x140>(ss);    // row_mirror: the other half of 16 lanes
+  ss += dpp<0x141>(ss);                   // row_half_mirror: the other quad of 8 lanes
+  ss += dpp<0x140>(ss);                   // row_mirror: the other half of 16 lanes
   const float r = __builtin_amdgcn_rsqf(ss * (1.0f / D) + eps);
+  bf16x8 y;
 #pragma unroll
-  for (int c = 0; c < CPT; ++c) {
-    bf16x8 y;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) y[j] = (__bf16)(float(x[c][j]) * r);
-    *LDS_PTR(bf16x8, row + (((CPT * part + c) ^ (key & 15)) * 16)) = y;
-  }
+  for (int j = 0; j < 8; ++j) y[j] = (__bf16)(float(x[j]) * r);
+  *p = y;
 }
 
 struct WaveState {
@@ -194,15 +190,14 @@ struct WaveState {
   int lo[NRB], hi[NRB];  // key bounds of the lane's rows
 };
 
-// Phase 1: S^T(tile in stage kst) for both row blocks.
-__device__ __forceinline__ void qk_tile(const unsigned char* kst, const WaveState& st, f32x16 (&s)[NRB], int lane) {
-  const int l31 = lane & 31, hi5 = lane >> 5;
+// Phase 1: S^T(tile in stage kst).
+__device__ __forceinline__ void qk_tile(const unsigned char* kst, const LaneOffsets& lo, const WaveState& st,
+                                        f32x16 (&s)[NRB]) {
 #pragma unroll
   for (int rb = 0; rb < NRB; ++rb) s[rb] = f32x16{};
 #pragma unroll
   for (int ks = 0; ks < 8; ++ks) {
-    const int c = (2 * ks + hi5) ^ (lane & 15);
-    const bf16x8 a = *LDS_PTR(const bf16x8, kst + l31 * ROW_BYTES + c * 16);
+    const bf16x8 a = *LDS_PTR(const bf16x8, kst + lo.kq[ks]);
 #pragma unroll
     for (int rb = 0; rb < NRB; ++rb) s[rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, st.qf[rb][ks], s[rb], 0, 0, 0);
   }
@@ -213,21 +208,15 @@ __device__ __forceinline__ void qk_tile(const unsigned char* kst, const WaveStat
 // ds_read_b64_tr_b16: lane 16b+n receives, for r = 0..3, element n%4 of what
 // lane 16b + 4r + n/4 read; lane 16b+i therefore reads 4 dims of key
 // (.. + (b>>1)*4 + i/4) at dim (b&1)*16 + (i%4)*4 of the 32-dim block.
-__device__ __forceinline__ void pv_tile(const unsigned char* vst, WaveState& st, int lane) {
-  const int b = lane >> 4, n = lane & 15;
-  const int key_in = (b >> 1) * 4 + (n >> 2);
-  const int dim_in = (b & 1) * 16 + (n & 3) * 4;
+__device__ __forceinline__ void pv_tile(const unsigned char* vst, const LaneOffsets& lo, WaveState& st) {
 #pragma unroll
   for (int t = 0; t < 2; ++t)
 #pragma unroll
     for (int db = 0; db < 4; ++db) {
       i16x4 h[2];
 #pragma unroll
-      for (int sidx = 0; sidx < 2; ++sidx) {
-        const int key = t * 16 + sidx * 8 + key_in;
-        const int off = key * ROW_BYTES + ((db ^ (key & 3)) * 64) + dim_in * 2;
-        h[sidx] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(i16x4, vst + off));
-      }
+      for (int sidx = 0; sidx < 2; ++sidx)
+        h[sidx] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(i16x4, vst + (t * 16 + sidx * 8) * ROW_BYTES + lo.vq[db]));
       const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(h[0], h[1], 0, 1, 2, 3, 4, 5, 6, 7));
 #pragma unroll
       for (int rb = 0; rb < NRB; ++rb)
@@ -286,18 +275,47 @@ __device__ __forceinline__ void softmax_tile(f32x16 (&s)[NRB], int kt, WaveState
   }
 }
 
+// Per-workgroup constants of the tile loop.
+struct LoopCtx {
+  i32x4 rsk, rsv;             // buffer resources of K and V
+  unsigned k_base, v_base;    // LDS byte addresses of the K and V rings (plus this wave's 1 KiB block)
+  unsigned tile_stride;       // bytes between consecutive key tiles of one KV head: BN * hk * ROW_BYTES
+  const int* tiles;           // this item's key tile codes
+  int n_tiles;
+  float eps;
+};
+
+// Starts the copies of K(j) into stage js and V(jv) into stage jvs (zeros when
+// the index is out of range).
+__device__ __forceinline__ void issue_copies(const LoopCtx& c, const LaneOffsets& lo, int j, int js, int jv, int jvs) {
+  const int ck = c.tiles[j < c.n_tiles ? (j < 0 ? 0 : j) : c.n_tiles - 1];
+  const int cv = c.tiles[jv < c.n_tiles ? (jv < 0 ? 0 : jv) : c.n_tiles - 1];
+  const unsigned sk = (j >= 0 && j < c.n_tiles) ? unsigned(ck >> 1) * c.tile_stride : kNoTile;
+  const unsigned sv = (jv >= 0 && jv < c.n_tiles) ? unsigned(cv >> 1) * c.tile_stride : kNoTile;
+  dma16(c.rsk, lo.dma_k, sk, c.k_base + js * TILE_BYTES);
+  dma16(c.rsv, lo.dma_v, sv, c.v_base + jvs * TILE_BYTES);
+}
+
+// One tile i. The stage of tile j is j % NSTAGE; callers that know i % NSTAGE
+// at compile time pass it as SI so every LDS offset folds into an immediate.
+// Top: wait for K(i+1) (issued LOOKAHEAD iterations ago; the later copies may
+// still fly), barrier (K(i) normalised, K(i+1) landed, stages of tiles i-1 /
+// i-2 free), start K(i+1+LA) and V(i+LA).
+// Phase 1: S(i) on the matrix cores; K(i+1) normalised on the vector ALUs.
+// Phase 2: P(i-1) V(i-1) on the matrix cores; softmax(i) on the vector ALUs.
 template <bool MASKED, bool STATIC>
-__device__ __forceinline__ void iteration(unsigned char* kst_next, const unsigned char* kst,
-                                          const unsigned char* vst_prev, int kt, float eps, WaveState& st, int lane) {
-  // phase 1: S(i) on the matrix cores; K(i+1) normalised on the vector ALUs
+__device__ __forceinline__ void tile_step(Smem& sm, const LoopCtx& c, const LaneOffsets& lo, WaveState& st, int i,
+                                          int si, int lane) {
+  wait_vmcnt<WAIT_YOUNGER>();
+  lds_barrier();
+  issue_copies(c, lo, i + 1 + LOOKAHEAD, (si + 1 + LOOKAHEAD) % NSTAGE, i + LOOKAHEAD, (si + LOOKAHEAD) % NSTAGE);
   f32x16 s[NRB];
-  qk_tile(kst, st, s, lane);
-  key_normalize(kst_next, eps);
-  // phase 2: P(i-1) V(i-1) on the matrix cores; softmax(i) on the vector ALUs
-  pv_tile(vst_prev, st, lane);
+  qk_tile(sm.k[si], lo, st, s);
+  key_normalize(sm.k[(si + 1) % NSTAGE], lo.kn, c.eps);
+  pv_tile(sm.v[(si + NSTAGE - 1) % NSTAGE], lo, st);
   bf16x8 pn[NRB][2];
   float alpha[NRB];
-  softmax_tile<MASKED, STATIC>(s, kt, st, pn, alpha, lane);
+  softmax_tile<MASKED, STATIC>(s, c.tiles[i] >> 1, st, pn, alpha, lane);
   if (!STATIC) {
     // P(i-1) V(i-1) was accumulated against the old reference maximum.
     bool any = false;
@@ -316,41 +334,22 @@ __device__ __forceinline__ void iteration(unsigned char* kst_next, const unsigne
     for (int t = 0; t < 2; ++t) st.p[rb][t] = pn[rb][t];
 }
 
-// Per-workgroup constants of the tile loop.
-struct LoopCtx {
-  i32x4 rsk, rsv;           // buffer resources of K and V
-  unsigned k_base, v_base;  // LDS byte addresses of the K and V rings
-  const int* tiles;         // this item's key tile codes
-  int n_tiles, kvh, hk, wave, lane;
-  float eps;
-};
-
-// Top of iteration i: wait for K(i+1) and V(i) (issued LOOKAHEAD iterations
-// earlier; the copies of the LOOKAHEAD-1 iterations since may still fly), barrier, start the copies of K(i+1+LA) and V(i+LA)
-// (zeros past the last tile).
-__device__ __forceinline__ void loop_top(Smem& sm, const LoopCtx& c, int i) {
-  wait_vmcnt<(LOOKAHEAD - 1) * 2 * UNITS>();
-  lds_barrier();
-  const int jk = i + 1 + LOOKAHEAD, jv = i + LOOKAHEAD;
-  const int ck = c.tiles[jk < c.n_tiles ? jk : c.n_tiles - 1];
-  const int cv = c.tiles[jv < c.n_tiles ? jv : c.n_tiles - 1];
-  issue_k(c.rsk, c.k_base + (jk % KSTAGES) * TILE_BYTES, jk < c.n_tiles ? ck >> 1 : -1, c.kvh, c.hk, c.wave, c.lane);
-  issue_v(c.rsv, c.v_base + (jv % VSTAGES) * TILE_BYTES, jv < c.n_tiles ? cv >> 1 : -1, c.kvh, c.hk, c.wave, c.lane);
+template <bool MASKED, bool STATIC, int U>
+__device__ __forceinline__ void unrolled_steps(Smem& sm, const LoopCtx& c, const LaneOffsets& lo, WaveState& st,
+                                               int i0, int lane) {
+  tile_step<MASKED, STATIC>(sm, c, lo, st, i0 + U, U, lane);
+  if constexpr (U + 1 < NSTAGE) unrolled_steps<MASKED, STATIC, U + 1>(sm, c, lo, st, i0, lane);
 }
 
-// Full tiles first (no mask code), then boundary tiles; one loop body each.
+// Full tiles first (no mask code), then boundary tiles. The full tiles run
+// NSTAGE at a time with compile-time stages; the rest one by one.
 template <bool STATIC>
-__device__ __forceinline__ void run_tiles(Smem& sm, const LoopCtx& c, int n_full, WaveState& st) {
-  for (int i = 0; i < n_full; ++i) {
-    loop_top(sm, c, i);
-    iteration<false, STATIC>(sm.k[(i + 1) % KSTAGES], sm.k[i % KSTAGES], sm.v[(i + VSTAGES - 1) % VSTAGES],
-                             c.tiles[i] >> 1, c.eps, st, c.lane);
-  }
-  for (int i = n_full; i < c.n_tiles; ++i) {
-    loop_top(sm, c, i);
-    iteration<true, STATIC>(sm.k[(i + 1) % KSTAGES], sm.k[i % KSTAGES], sm.v[(i + VSTAGES - 1) % VSTAGES],
-                            c.tiles[i] >> 1, c.eps, st, c.lane);
-  }
+__device__ __forceinline__ void run_tiles(Smem& sm, const LoopCtx& c, const LaneOffsets& lo, int n_full,
+                                          WaveState& st, int lane) {
+  int i = 0;
+  for (; i + NSTAGE <= n_full; i += NSTAGE) unrolled_steps<false, STATIC, 0>(sm, c, lo, st, i, lane);
+  for (; i < n_full; ++i) tile_step<false, STATIC>(sm, c, lo, st, i, i % NSTAGE, lane);
+  for (; i < c.n_tiles; ++i) tile_step<true, STATIC>(sm, c, lo, st, i, i % NSTAGE, lane);
 }
 
 __global__ void __launch_bounds__(NTHR) __attribute__((amdgpu_waves_per_eu(NRB == 1 ? 2 : 1, NRB == 1 ? 2 : 1)))
@@ -367,28 +366,6 @@ fwd_bf16_d128_kernel(FwdParams prm, const int4* __restrict__ items, const int* _
   const int rb_per_head = prm.tile_q >> 5;
   const int tb = item.z, n_tiles = item.w - item.z;
 
-  // ---- K/V tiles 0..LOOKAHEAD in flight before anything else
-  const unsigned kv_bytes = unsigned(prm.tk) * unsigned(prm.hk) * unsigned(ROW_BYTES);
-  const i32x4 rsk = make_rsrc(prm.k, kv_bytes);
-  const i32x4 rsv = make_rsrc(prm.v, kv_bytes);
-  const unsigned k_base = __builtin_amdgcn_readfirstlane(lds_addr(&sm.k[0][0]));
-  const unsigned v_base = __builtin_amdgcn_readfirstlane(lds_addr(&sm.v[0][0]));
-#pragma unroll
-  for (int j = 0; j <= LOOKAHEAD; ++j)
-    issue_k(rsk, k_base + j * TILE_BYTES, j < n_tiles ? tiles[tb + j] >> 1 : -1, kvh, prm.hk, wave, lane);
-#pragma unroll
-  for (int j = 0; j < LOOKAHEAD; ++j)
-    issue_v(rsv, v_base + j * TILE_BYTES, j < n_tiles ? tiles[tb + j] >> 1 : -1, kvh, prm.hk, wave, lane);
-
-  // V stage of tile -1 holds zeros: the first iteration's P(-1) V(-1) adds 0.
-  {
-    unsigned char* vz = sm.v[VSTAGES - 1];
-#pragma unroll
-    for (int i = 0; i < TILE_BYTES / (NTHR * 16); ++i)
-      *LDS_PTR(i32x4, vz + (i * NTHR + tid) * 16) = i32x4{0, 0, 0, 0};
-  }
-  if (tid < D) sm.gqk[tid] = prm.q_gain[tid] * prm.k_gain[tid] * (prm.scale * kLog2e);
-
   WaveState st;
   int tok[NRB], head[NRB];
   bool valid[NRB];
@@ -399,8 +376,7 @@ fwd_bf16_d128_kernel(FwdParams prm, const int4* __restrict__ items, const int* _
     tok[rb] = item.x + (blk % rb_per_head) * 32 + (lane & 31);
     valid[rb] = tok[rb] < prm.tq;
   }
-
-  // ---- query prologue: load, RMS-normalise, fold gains/temperature, to bf16
+  // ---- query loads first (older than every K/V copy)
   bf16x8 qr[NRB][8];
 #pragma unroll
   for (int rb = 0; rb < NRB; ++rb) {
@@ -409,7 +385,28 @@ fwd_bf16_d128_kernel(FwdParams prm, const int4* __restrict__ items, const int* _
     for (int ks = 0; ks < 8; ++ks)
       qr[rb][ks] = valid[rb] ? *reinterpret_cast<const bf16x8*>(qrow + (2 * ks + (lane >> 5)) * 8) : bf16x8{};
   }
-  __syncthreads();                                     // gqk and the zeroed V stage visible
+
+  // ---- K/V copies of iterations -LOOKAHEAD-1 .. -1 (V(-1) is a zero tile)
+  const unsigned kv_bytes = unsigned(prm.tk) * unsigned(prm.hk) * unsigned(ROW_BYTES);
+  const LaneOffsets lo = lane_offsets(tid, prm.hk, kvh);
+  LoopCtx ctx;
+  ctx.rsk = make_rsrc(prm.k, kv_bytes);
+  ctx.rsv = make_rsrc(prm.v, kv_bytes);
+  ctx.k_base = __builtin_amdgcn_readfirstlane(lds_addr(&sm.k[0][0])) + wave * 1024;
+  ctx.v_base = __builtin_amdgcn_readfirstlane(lds_addr(&sm.v[0][0])) + wave * 1024;
+  ctx.tile_stride = unsigned(BN) * unsigned(prm.hk) * unsigned(ROW_BYTES);
+  ctx.tiles = tiles + tb;
+  ctx.n_tiles = n_tiles;
+  ctx.eps = prm.eps;
+#pragma unroll
+  for (int j = -LOOKAHEAD - 1; j < 0; ++j)
+    issue_copies(ctx, lo, j + 1 + LOOKAHEAD, (j + 1 + LOOKAHEAD + NSTAGE) % NSTAGE, j + LOOKAHEAD,
+                 (j + LOOKAHEAD + NSTAGE) % NSTAGE);
+
+  if (tid < D) sm.gqk[tid] = prm.q_gain[tid] * prm.k_gain[tid] * (prm.scale * kLog2e);
+  __syncthreads();                                     // gqk visible
+
+  // ---- query prologue: RMS-normalise, fold gains/temperature, to bf16
   float bound_max = 0.0f;
 #pragma unroll
   for (int rb = 0; rb < NRB; ++rb) {
@@ -442,16 +439,15 @@ fwd_bf16_d128_kernel(FwdParams prm, const int4* __restrict__ items, const int* _
   }
   const bool stat = __builtin_amdgcn_ballot_w64(!(bound_max <= kStaticBound)) == 0;
 
-  // ---- tile 0's keys normalised
-  wait_vmcnt<0>();
+  // ---- K(0) landed (every copy after it may still fly), normalised
+  wait_vmcnt<WAIT_YOUNGER + 1 + 2 * UNITS - 1>();
   lds_barrier();
-  key_normalize(sm.k[0], prm.eps);
+  key_normalize(sm.k[0], lo.kn, prm.eps);
 
-  LoopCtx ctx{rsk, rsv, k_base, v_base, tiles + tb, n_tiles, kvh, prm.hk, wave, lane, prm.eps};
-  if (stat) run_tiles<true>(sm, ctx, n_full, st);
-  else run_tiles<false>(sm, ctx, n_full, st);
+  if (stat) run_tiles<true>(sm, ctx, lo, n_full, st, lane);
+  else run_tiles<false>(sm, ctx, lo, n_full, st, lane);
   // last tile's P V: its V stage landed before the last barrier
-  pv_tile(sm.v[(n_tiles + VSTAGES - 1) % VSTAGES], st, lane);
+  pv_tile(sm.v[(n_tiles + NSTAGE - 1) % NSTAGE], lo, st);
 
   // ---- epilogue
 #pragma unroll
