@@ -96,6 +96,22 @@ def cpu_baseline(cfg, inp, budget_s: float = 20.0):
                       f"{spent:.1f} s fp64 numpy on the host"}
 
 
+def copy_probe(mib: int) -> None:
+    """A plain copy kernel of known size: reads and writes mib MiB per launch.
+    Under rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE its readings give the factor
+    between those counters and true HBM bytes."""
+    import torch
+    n = mib << 20
+    src = torch.empty(n, dtype=torch.uint8, device="cuda")
+    src.fill_(1)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_probe_bytes": n, "launches": 3}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -104,7 +120,12 @@ def main():
     ap.add_argument("--workload", default="video480x832")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=20.0)
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="only run a plain device-to-device copy of this many MiB three times (counter calibration)")
     args = ap.parse_args()
+    if args.copy_probe_mib:
+        copy_probe(args.copy_probe_mib)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (the kernel runs on one GPU's "
               "share; see DESIGN.md for how the path would shard)", file=sys.stderr)
