@@ -5,7 +5,9 @@ Every function has the name of the C entry point it marshals; all of the
 computation runs in the HIP kernels. torch supplies device memory and streams.
 """
 from .api import (MagiAttnError, Plan, magi_attn_abi_version, magi_attn_classify_host, magi_attn_fwd,
-                  magi_attn_fwd_simple, magi_attn_plan_create, magi_attn_plan_destroy, magi_attn_plan_stats)
+                  magi_attn_fwd_simple, magi_attn_plan_create, magi_attn_plan_destroy, magi_attn_plan_stats,
+                  magi_attn_workspace_size)
 
 __all__ = ["MagiAttnError", "Plan", "magi_attn_abi_version", "magi_attn_classify_host", "magi_attn_fwd",
-           "magi_attn_fwd_simple", "magi_attn_plan_create", "magi_attn_plan_destroy", "magi_attn_plan_stats"]
+           "magi_attn_fwd_simple", "magi_attn_plan_create", "magi_attn_plan_destroy", "magi_attn_plan_stats",
+           "magi_attn_workspace_size"]

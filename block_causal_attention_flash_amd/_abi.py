@@ -54,9 +54,11 @@ class Stats(ctypes.Structure):
 SIGNATURES = {
     "magi_attn_plan_create": (ctypes.c_int, [ctypes.POINTER(Layout), ctypes.POINTER(ctypes.c_void_p)]),
     "magi_attn_plan_destroy": (ctypes.c_int, [ctypes.c_void_p]),
+    "magi_attn_workspace_size": (ctypes.c_int, [ctypes.c_void_p, ctypes.POINTER(ctypes.c_size_t)]),
     "magi_attn_fwd": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                                      ctypes.c_void_p, ctypes.c_void_p, ctypes.c_float, ctypes.c_float,
-                                     ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]),
+                                     ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t,
+                                     ctypes.c_void_p]),
     "magi_attn_fwd_simple": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                                             ctypes.c_void_p, _i32p, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
                                             ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p,

@@ -85,6 +85,13 @@ def magi_attn_plan_destroy(handle: int) -> None:
     _check(lib, lib.magi_attn_plan_destroy(handle))
 
 
+def magi_attn_workspace_size(handle: int) -> int:
+    lib = _abi.load()
+    n = ctypes.c_size_t()
+    _check(lib, lib.magi_attn_workspace_size(handle, ctypes.byref(n)))
+    return n.value
+
+
 def _stream_ptr(stream, device):
     import torch
     s = torch.cuda.current_stream(device) if stream is None else stream
@@ -102,9 +109,11 @@ def _gain(g, d, device):
 
 
 def magi_attn_fwd(handle: int, q, k, v, q_gain=None, k_gain=None, rms_eps: float = 1e-6,
-                  scale: Optional[float] = None, out=None, lse=None, stream=None):
+                  scale: Optional[float] = None, out=None, lse=None, workspace=None, stream=None):
     """Enqueues the forward on `stream` (default: torch's current stream).
-    q [T_q,H_q,d], k/v [T_k,H_kv,d] on the GPU; returns (out, lse)."""
+    q [T_q,H_q,d], k/v [T_k,H_kv,d] on the GPU; `workspace` is a device
+    tensor of at least magi_attn_workspace_size(handle) bytes (allocated here
+    when None). Returns (out, lse)."""
     import torch
     lib = _abi.load()
     for name, t in (("q", q), ("k", k), ("v", v)):
@@ -118,8 +127,13 @@ def magi_attn_fwd(handle: int, q, k, v, q_gain=None, k_gain=None, rms_eps: float
     qg = _gain(q_gain, d, q.device)
     kg = _gain(k_gain, d, q.device)
     sc = (1.0 / d ** 0.5) if scale is None else float(scale)
+    need = magi_attn_workspace_size(handle)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    ws_bytes = workspace.numel() * workspace.element_size()
     _check(lib, lib.magi_attn_fwd(handle, q.data_ptr(), k.data_ptr(), v.data_ptr(), qg.data_ptr(), kg.data_ptr(),
-                                  float(rms_eps), sc, out.data_ptr(), lse.data_ptr(), _stream_ptr(stream, q.device)))
+                                  float(rms_eps), sc, out.data_ptr(), lse.data_ptr(), workspace.data_ptr(), ws_bytes,
+                                  _stream_ptr(stream, q.device)))
     return out, lse
 
 
@@ -167,7 +181,11 @@ class Plan:
     def stats(self) -> dict:
         return magi_attn_plan_stats(**self.layout)
 
-    def __call__(self, q, k, v, q_gain=None, k_gain=None, rms_eps=1e-6, scale=None, out=None, lse=None, stream=None):
+    def workspace_size(self) -> int:
+        return magi_attn_workspace_size(self.handle)
+
+    def __call__(self, q, k, v, q_gain=None, k_gain=None, rms_eps=1e-6, scale=None, out=None, lse=None,
+                 workspace=None, stream=None):
         import torch
         want = torch.bfloat16 if self.dtype == "bf16" else torch.float32
         if q.dtype != want or k.dtype != want or v.dtype != want:
@@ -180,7 +198,7 @@ class Plan:
             raise ValueError("out must match q")
         if lse is not None and (tuple(lse.shape) != (self.n_q_heads, self.t_q) or lse.dtype != torch.float32):
             raise ValueError("lse must be float32 [H_q, T_q]")
-        return magi_attn_fwd(self.handle, q, k, v, q_gain, k_gain, rms_eps, scale, out, lse, stream)
+        return magi_attn_fwd(self.handle, q, k, v, q_gain, k_gain, rms_eps, scale, out, lse, workspace, stream)
 
     def close(self):
         if self.handle:

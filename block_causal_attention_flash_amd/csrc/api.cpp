@@ -150,12 +150,24 @@ magi_status_t magi_attn_plan_destroy(magi_attn_plan_t* plan) {
   return s;
 }
 
+magi_status_t magi_attn_workspace_size(const magi_attn_plan_t* plan, size_t* bytes) {
+  if (!plan || !bytes) return fail(MAGI_ERR_INVALID_ARG, "plan or bytes is NULL");
+  const auto& H = plan->host;
+  *bytes = H.dtype == MAGI_DTYPE_BF16 ? magi::workspace_bytes_bf16(H.tk, H.hk, H.d) : 0;
+  return MAGI_OK;
+}
+
 magi_status_t magi_attn_fwd(const magi_attn_plan_t* plan, const void* q, const void* k, const void* v,
                             const float* q_gain, const float* k_gain, float rms_eps, float scale, void* out,
-                            float* lse, void* stream) {
+                            float* lse, void* workspace, size_t workspace_bytes, void* stream) {
   if (!plan) return fail(MAGI_ERR_INVALID_ARG, "plan is NULL");
   const auto& H = plan->host;
   if (H.items.empty()) return MAGI_OK;                     // no query token: nothing to do
+  size_t need = 0;
+  magi_attn_workspace_size(plan, &need);
+  if (workspace_bytes < need) return fail(MAGI_ERR_INVALID_ARG, "workspace smaller than magi_attn_workspace_size()");
+  if (need && (!workspace || !aligned(workspace, 16)))
+    return fail(MAGI_ERR_INVALID_ARG, "workspace must be non-NULL and 16-byte aligned");
   if (!q || !k || !v || !out || !lse || !q_gain || !k_gain)
     return fail(MAGI_ERR_INVALID_ARG, "NULL tensor pointer");
   if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16))
@@ -169,6 +181,7 @@ magi_status_t magi_attn_fwd(const magi_attn_plan_t* plan, const void* q, const v
   prm.q = q;
   prm.k = k;
   prm.v = v;
+  prm.k_hat = workspace;
   prm.out = out;
   prm.lse = lse;
   prm.q_gain = q_gain;
@@ -212,12 +225,22 @@ magi_status_t magi_attn_fwd_simple(const void* q, const void* k, const void* v, 
   magi_attn_plan_t* plan = nullptr;
   magi_status_t s = magi_attn_plan_create(&L, &plan);
   if (s != MAGI_OK) return s;
-  s = magi_attn_fwd(plan, q, k, v, q_gain, k_gain, rms_eps, scale, out, lse, stream);
-  if (s == MAGI_OK) {
-    hipError_t e = hipStreamSynchronize(static_cast<hipStream_t>(stream));
-    if (e != hipSuccess) s = hip_fail(e, "hipStreamSynchronize");
+  size_t ws_bytes = 0;
+  magi_attn_workspace_size(plan, &ws_bytes);
+  void* ws = nullptr;
+  if (ws_bytes) {
+    hipError_t e = hipMalloc(&ws, ws_bytes);
+    if (e != hipSuccess) {
+      magi_attn_plan_destroy(plan);
+      return e == hipErrorOutOfMemory ? fail(MAGI_ERR_NO_MEMORY, "hipMalloc of the workspace failed")
+                                      : hip_fail(e, "hipMalloc");
+    }
   }
+  s = magi_attn_fwd(plan, q, k, v, q_gain, k_gain, rms_eps, scale, out, lse, ws, ws_bytes, stream);
+  hipError_t e = hipStreamSynchronize(static_cast<hipStream_t>(stream));
+  if (s == MAGI_OK && e != hipSuccess) s = hip_fail(e, "hipStreamSynchronize");
   const std::string keep = g_last_error;
+  if (ws) (void)hipFree(ws);
   magi_status_t d = magi_attn_plan_destroy(plan);
   if (s != MAGI_OK) { g_last_error = keep; return s; }
   return d;

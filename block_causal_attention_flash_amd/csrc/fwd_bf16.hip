@@ -13,9 +13,10 @@
 //   * K and V tiles are copied from global memory straight into LDS rings
 //     (buffer_load ... lds, zero fill past T_k) four tiles ahead, and serve all
 //     256 rows: K/V leave L2 once per workgroup, not once per query head;
-//   * each staged K tile is RMS-normalised in LDS once, by the workgroup, one
-//     tile ahead of its use (k_hat = k / rms(k), rounded to bf16); g_k is
-//     folded into the normalised queries, so s_ij = <q'_i, k_hat_j>;
+//   * keys are RMS-normalised once per key by a small pre-pass kernel into a
+//     workspace (k_hat = k / rms(k), rounded to bf16) instead of once per
+//     reading workgroup; g_k is folded into the normalised queries, so
+//     s_ij = <q'_i, k_hat_j>;
 //   * S^T = K Q'^T (lane = query row, 16 keys per lane in registers);
 //   * O^T += V^T P^T with V read through ds_read_b64_tr_b16 from the row-major
 //     V tile.
@@ -59,9 +60,7 @@ constexpr int LOOKAHEAD = NSTAGE - 2;                 // copies issued this many
 constexpr int ROW_BYTES = D * 2;                      // 256
 constexpr int TILE_BYTES = BN * ROW_BYTES;            // 8 KiB
 constexpr int UNITS = TILE_BYTES / (NTHR * 16);       // 16-byte copies per thread per tensor
-constexpr int TPK = NTHR / BN;                        // threads per key when normalising K
-constexpr int CPT = 16 / TPK;                         // 16-byte chunks per thread when normalising K
-static_assert(UNITS == 1 && CPT >= 1 && NRB >= 1, "tile shape");
+static_assert(UNITS == 1 && NRB >= 1, "tile shape");
 // Copies in flight that may be younger than the ones a tile needs: the
 // LOOKAHEAD-1 later iterations (K and V each) plus the V copy issued right
 // after the needed K copy.
@@ -139,7 +138,6 @@ struct LaneOffsets {
   unsigned dma_k, dma_v;     // buffer offsets (the tile part goes in the scalar offset)
   int kq[8];                 // S operand of k-step ks: key (l & 31), chunk 2ks + (l >> 5)
   int vq[4];                 // P V operand, dim block db: tr-read base of key (b>>1)*4 + n/4
-  int kn;                    // K normalisation: this thread's chunk
 };
 
 __device__ __forceinline__ LaneOffsets lane_offsets(int tid, int hk, int kvh) {
@@ -158,27 +156,7 @@ __device__ __forceinline__ LaneOffsets lane_offsets(int tid, int hk, int kvh) {
   const int dim_in = (b & 1) * 16 + (n & 3) * 4;
 #pragma unroll
   for (int db = 0; db < 4; ++db) o.vq[db] = key_in * ROW_BYTES + ((db ^ (key_in & 3)) * 64) + dim_in * 2;
-  const int nkey = tid / TPK, part = tid % TPK;
-  o.kn = nkey * ROW_BYTES + (((CPT * part) ^ (nkey & 15)) * 16);
   return o;
-}
-
-// Normalises a staged K tile in place: k_hat_j = k_j / sqrt(mean_d k_j^2 + eps),
-// rounded to bf16 (the gain g_k is folded into the queries). TPK threads per
-// key, one 16-byte chunk each.
-__device__ __forceinline__ void key_normalize(unsigned char* kst, int kn, float eps) {
-  auto* p = LDS_PTR(bf16x8, kst + kn);
-  const bf16x8 x = *p;
-  float ss = sumsq8(x, 0.0f);
-  ss += dpp<0xB1>(ss);                    // quad_perm [1,0,3,2]
-  ss += dpp<0x4E>(ss);                    // quad_perm [2,3,0,1]
-  ss += dpp<0x141>(ss);                   // row_half_mirror: the other quad of 8 lanes
-  ss += dpp<0x140>(ss);                   // row_mirror: the other half of 16 lanes
-  const float r = __builtin_amdgcn_rsqf(ss * (1.0f / D) + eps);
-  bf16x8 y;
-#pragma unroll
-  for (int j = 0; j < 8; ++j) y[j] = (__bf16)(float(x[j]) * r);
-  *p = y;
 }
 
 struct WaveState {
@@ -282,7 +260,6 @@ struct LoopCtx {
   unsigned tile_stride;       // bytes between consecutive key tiles of one KV head: BN * hk * ROW_BYTES
   const int* tiles;           // this item's key tile codes
   int n_tiles;
-  float eps;
 };
 
 // Starts the copies of K(j) into stage js and V(jv) into stage jvs (zeros when
@@ -299,9 +276,9 @@ __device__ __forceinline__ void issue_copies(const LoopCtx& c, const LaneOffsets
 // One tile i. The stage of tile j is j % NSTAGE; callers that know i % NSTAGE
 // at compile time pass it as SI so every LDS offset folds into an immediate.
 // Top: wait for K(i+1) (issued LOOKAHEAD iterations ago; the later copies may
-// still fly), barrier (K(i) normalised, K(i+1) landed, stages of tiles i-1 /
-// i-2 free), start K(i+1+LA) and V(i+LA).
-// Phase 1: S(i) on the matrix cores; K(i+1) normalised on the vector ALUs.
+// still fly), barrier (K(i) and V(i-1) landed for every wave, stages of tiles
+// i-1 / i-2 free), start K(i+1+LA) and V(i+LA).
+// Phase 1: S(i) on the matrix cores.
 // Phase 2: P(i-1) V(i-1) on the matrix cores; softmax(i) on the vector ALUs.
 template <bool MASKED, bool STATIC>
 __device__ __forceinline__ void tile_step(Smem& sm, const LoopCtx& c, const LaneOffsets& lo, WaveState& st, int i,
@@ -311,7 +288,6 @@ __device__ __forceinline__ void tile_step(Smem& sm, const LoopCtx& c, const Lane
   issue_copies(c, lo, i + 1 + LOOKAHEAD, (si + 1 + LOOKAHEAD) % NSTAGE, i + LOOKAHEAD, (si + LOOKAHEAD) % NSTAGE);
   f32x16 s[NRB];
   qk_tile(sm.k[si], lo, st, s);
-  key_normalize(sm.k[(si + 1) % NSTAGE], lo.kn, c.eps);
   pv_tile(sm.v[(si + NSTAGE - 1) % NSTAGE], lo, st);
   bf16x8 pn[NRB][2];
   float alpha[NRB];
@@ -390,14 +366,13 @@ fwd_bf16_d128_kernel(FwdParams prm, const int4* __restrict__ items, const int* _
   const unsigned kv_bytes = unsigned(prm.tk) * unsigned(prm.hk) * unsigned(ROW_BYTES);
   const LaneOffsets lo = lane_offsets(tid, prm.hk, kvh);
   LoopCtx ctx;
-  ctx.rsk = make_rsrc(prm.k, kv_bytes);
+  ctx.rsk = make_rsrc(prm.k_hat, kv_bytes);
   ctx.rsv = make_rsrc(prm.v, kv_bytes);
   ctx.k_base = __builtin_amdgcn_readfirstlane(lds_addr(&sm.k[0][0])) + wave * 1024;
   ctx.v_base = __builtin_amdgcn_readfirstlane(lds_addr(&sm.v[0][0])) + wave * 1024;
   ctx.tile_stride = unsigned(BN) * unsigned(prm.hk) * unsigned(ROW_BYTES);
   ctx.tiles = tiles + tb;
   ctx.n_tiles = n_tiles;
-  ctx.eps = prm.eps;
 #pragma unroll
   for (int j = -LOOKAHEAD - 1; j < 0; ++j)
     issue_copies(ctx, lo, j + 1 + LOOKAHEAD, (j + 1 + LOOKAHEAD + NSTAGE) % NSTAGE, j + LOOKAHEAD,
@@ -439,11 +414,6 @@ fwd_bf16_d128_kernel(FwdParams prm, const int4* __restrict__ items, const int* _
   }
   const bool stat = __builtin_amdgcn_ballot_w64(!(bound_max <= kStaticBound)) == 0;
 
-  // ---- K(0) landed (every copy after it may still fly), normalised
-  wait_vmcnt<WAIT_YOUNGER + 1 + 2 * UNITS - 1>();
-  lds_barrier();
-  key_normalize(sm.k[0], lo.kn, prm.eps);
-
   if (stat) run_tiles<true>(sm, ctx, lo, n_full, st, lane);
   else run_tiles<false>(sm, ctx, lo, n_full, st, lane);
   // last tile's P V: its V stage landed before the last barrier
@@ -474,9 +444,41 @@ fwd_bf16_d128_kernel(FwdParams prm, const int4* __restrict__ items, const int* _
   }
 }
 
+// RMS-normalises every key once: k_hat = k / sqrt(mean_d k^2 + eps), bf16,
+// same [T_k][H_kv][128] layout. 16 lanes per key row, 16 bytes each; the row
+// sum of squares is reduced with DPP inside each 16-lane row.
+constexpr int KN_THREADS = 256;
+__global__ void __launch_bounds__(KN_THREADS) k_normalize_kernel(const __bf16* __restrict__ k, __bf16* __restrict__ kh,
+                                                                 long long n_rows, float eps) {
+  const long long row = (long long)blockIdx.x * (KN_THREADS / 16) + (threadIdx.x >> 4);
+  if (row >= n_rows) return;                          // whole 16-lane rows exit together
+  const int part = threadIdx.x & 15;
+  const bf16x8 x = *reinterpret_cast<const bf16x8*>(k + row * D + part * 8);
+  float ss = sumsq8(x, 0.0f);
+  ss += dpp<0xB1>(ss);                    // quad_perm [1,0,3,2]
+  ss += dpp<0x4E>(ss);                    // quad_perm [2,3,0,1]
+  ss += dpp<0x141>(ss);                   // row_half_mirror: the other quad of 8 lanes
+  ss += dpp<0x140>(ss);                   // row_mirror: the other half of the 16 lanes
+  const float r = __builtin_amdgcn_rsqf(ss * (1.0f / D) + eps);
+  bf16x8 y;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) y[j] = (__bf16)(float(x[j]) * r);
+  *reinterpret_cast<bf16x8*>(kh + row * D + part * 8) = y;
+}
+
 }  // namespace
 
+size_t workspace_bytes_bf16(long long tk, int hk, int d) { return size_t(tk) * size_t(hk) * size_t(d) * 2; }
+
 hipError_t launch_fwd_bf16_d128(const FwdParams& p, int n_items, hipStream_t stream) {
+  const long long n_rows = (long long)p.tk * p.hk;
+  if (n_rows > 0) {
+    const unsigned blocks = unsigned((n_rows + KN_THREADS / 16 - 1) / (KN_THREADS / 16));
+    hipLaunchKernelGGL(k_normalize_kernel, dim3(blocks), dim3(KN_THREADS), 0, stream,
+                       static_cast<const __bf16*>(p.k), static_cast<__bf16*>(p.k_hat), n_rows, p.eps);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
   hipLaunchKernelGGL(fwd_bf16_d128_kernel, dim3(n_items), dim3(NTHR), 0, stream, p, p.items, p.tiles, p.rows);
   return hipGetLastError();
 }

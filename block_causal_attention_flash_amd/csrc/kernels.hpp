@@ -10,6 +10,7 @@ struct FwdParams {
   const void* q;
   const void* k;
   const void* v;
+  void* k_hat;           // bf16 path: workspace holding RMS-normalised K, [T_k][H_kv][d]
   void* out;
   float* lse;
   const float* q_gain;
@@ -24,6 +25,7 @@ struct FwdParams {
 };
 
 hipError_t launch_fwd_bf16_d128(const FwdParams& p, int n_items, hipStream_t stream);
+size_t workspace_bytes_bf16(long long tk, int hk, int d);
 hipError_t launch_fwd_fp32(const FwdParams& p, int head_dim, int n_items, hipStream_t stream);
 
 }  // namespace magi

@@ -101,7 +101,8 @@ typedef struct magi_attn_plan magi_attn_plan_t;   /* opaque */
  * A plan is immutable after creation and may be used by concurrent calls on
  * several streams of the device it was created on.
  * Errors: MAGI_ERR_INVALID_ARG (layout rules above), MAGI_ERR_UNSUPPORTED
- * (head_dim/dtype combination), MAGI_ERR_NO_MEMORY, MAGI_ERR_HIP. On error
+ * (head_dim/dtype combination; K or V of 2 GiB or more; T_q * n_q_heads of
+ * 2^31 or more), MAGI_ERR_NO_MEMORY, MAGI_ERR_HIP. On error
  * *plan is set to NULL. Validation runs before any HIP call.
  */
 MAGI_API magi_status_t magi_attn_plan_create(const magi_attn_layout_t* layout, magi_attn_plan_t** plan);
@@ -111,25 +112,36 @@ MAGI_API magi_status_t magi_attn_plan_create(const magi_attn_layout_t* layout, m
 MAGI_API magi_status_t magi_attn_plan_destroy(magi_attn_plan_t* plan);
 
 /*
+ * Device workspace bytes that magi_attn_fwd needs for this plan (bf16: one
+ * RMS-normalised copy of K, T_k * n_kv_heads * head_dim * 2 bytes; fp32: 0).
+ */
+MAGI_API magi_status_t magi_attn_workspace_size(const magi_attn_plan_t* plan, size_t* bytes);
+
+/*
  * Enqueues the forward pass on `stream`: out and lse as defined at the top.
  * rms_eps >= 0 is added to mean(x^2) inside the square root; scale > 0 is the
  * softmax temperature applied to <q_hat, k_hat> (1/sqrt(head_dim) usually).
- * Allocates nothing and never synchronises, so it can be captured in a HIP
- * graph. Errors: MAGI_ERR_INVALID_ARG (NULL/misaligned pointer, bad eps or
- * scale), MAGI_ERR_HIP (launch failure). Device faults surface at the
- * caller's next synchronisation.
+ * `workspace` is caller-owned device memory of at least
+ * magi_attn_workspace_size() bytes, 16-byte aligned (may be NULL when that
+ * size is 0); the call overwrites it, so concurrent calls need distinct
+ * workspaces. Allocates nothing and never synchronises, so it can be
+ * captured in a HIP graph. Errors: MAGI_ERR_INVALID_ARG (NULL/misaligned
+ * pointer, workspace too small, bad eps or scale), MAGI_ERR_HIP (launch
+ * failure). Device faults surface at the caller's next synchronisation.
  */
 MAGI_API magi_status_t magi_attn_fwd(const magi_attn_plan_t* plan,
                             const void* q, const void* k, const void* v,
                             const float* q_gain, const float* k_gain,
                             float rms_eps, float scale,
-                            void* out, float* lse, void* stream);
+                            void* out, float* lse,
+                            void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * One-shot form for a single video of self-attention (q and kv offsets both
- * = chunk_offsets[n_chunks+1], host array): builds a plan, enqueues the
- * forward on `stream`, waits for the stream, and destroys the plan. Not
- * capturable (it allocates and synchronises). Same errors as above.
+ * = chunk_offsets[n_chunks+1], host array): builds a plan, allocates the
+ * workspace, enqueues the forward on `stream`, waits for the stream, and
+ * frees both. Not capturable (it allocates and synchronises). Same errors as
+ * above, plus MAGI_ERR_NO_MEMORY.
  */
 MAGI_API magi_status_t magi_attn_fwd_simple(const void* q, const void* k, const void* v,
                                    void* out, float* lse,
