@@ -114,11 +114,18 @@ __device__ __forceinline__ i32x4 make_rsrc(const void* base, unsigned bytes) {
 // writes LDS byte m0 + 16 i. Issued through asm so that the compiler does not
 // order later LDS reads of other ring stages behind it; completion is awaited
 // explicitly (vmcnt) before the barrier that publishes the stage.
+// m0 is saved and restored inside the asm block.
 __device__ __forceinline__ void dma16(i32x4 rsrc, unsigned voff, unsigned soff, unsigned lds) {
-  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
-               :
-               : "s"(lds), "v"(voff), "s"(rsrc), "s"(soff)
-               : "memory", "m0");
+  unsigned saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %1\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dwordx4 %2, %3, %4 offen lds\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "s"(lds), "v"(voff), "s"(rsrc), "s"(soff)
+      : "memory");
 }
 
 template <int N>
@@ -263,7 +270,7 @@ struct LoopCtx {
 };
 
 // Starts the copies of K(j) into stage js and V(jv) into stage jvs (zeros when
-// the index is out of range).
+// the index is out of range). The tile codes come from the item's list.
 __device__ __forceinline__ void issue_copies(const LoopCtx& c, const LaneOffsets& lo, int j, int js, int jv, int jvs) {
   const int ck = c.tiles[j < c.n_tiles ? (j < 0 ? 0 : j) : c.n_tiles - 1];
   const int cv = c.tiles[jv < c.n_tiles ? (jv < 0 ? 0 : jv) : c.n_tiles - 1];
