@@ -181,7 +181,7 @@ magi_status_t magi_attn_fwd(const magi_attn_plan_t* plan, const void* q, const v
   prm.q = q;
   prm.k = k;
   prm.v = v;
-  prm.k_hat = workspace;
+  prm.ws = workspace;
   prm.out = out;
   prm.lse = lse;
   prm.q_gain = q_gain;

@@ -10,16 +10,16 @@
 // Workgroup = one work item: 256 (token, head) rows of `heads_per_item`
 // query heads that share one KV head; 8 waves, two per SIMD, 32 rows each
 // (one 32-row MFMA block). Per 32-key tile:
-//   * K and V tiles are copied from global memory straight into LDS rings
-//     (buffer_load ... lds, zero fill past T_k) four tiles ahead, and serve all
-//     256 rows: K/V leave L2 once per workgroup, not once per query head;
-//   * keys are RMS-normalised once per key by a small pre-pass kernel into a
-//     workspace (k_hat = k / rms(k), rounded to bf16) instead of once per
-//     reading workgroup; g_k is folded into the normalised queries, so
+//   * a pre-pass kernel has RMS-normalised every key once (k_hat = k / rms(k),
+//     bf16) and written K-hat and V^T as per-tile LDS images into a
+//     workspace; g_k is folded into the normalised queries, so
 //     s_ij = <q'_i, k_hat_j>;
+//   * the K-hat and V^T images are copied from global memory straight into
+//     LDS rings (buffer_load ... lds, zero fill past the last tile) six tiles
+//     ahead, and serve all 256 rows: K/V leave L2 once per workgroup, not once
+//     per query head;
 //   * S^T = K Q'^T (lane = query row, 16 keys per lane in registers);
-//   * O^T += V^T P^T with V read through ds_read_b64_tr_b16 from the row-major
-//     V tile.
+//   * O^T += V^T P^T, both operands read with ds_read_b128 / kept in registers.
 // Software pipeline per iteration i: phase 1 issues the MFMAs of S(i);
 // phase 2 issues the MFMAs of P(i-1) V(i-1) while the vector ALUs turn S(i)
 // into P(i) (mask, exp2, round to bf16, row sums), so each wave's vector work
@@ -43,7 +43,6 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
@@ -136,33 +135,31 @@ __device__ __forceinline__ void wait_vmcnt() {
 // All LDS traffic of this wave finished, then the workgroup barrier.
 __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" : : : "memory"); }
 
-// Per-lane constant offsets, computed once. LDS images of a 32-key tile:
-//   K: row-major [key][128], 16-byte chunk c of key j stored at chunk c ^ (j & 15)
-//   V: row-major [key][128], 64-byte segment g of key j stored at g ^ (j & 3)
-// Global source of the lane's 16-byte copy unit u = wave*64 + lane (key u/16,
-// physical chunk u%16) within KV head kvh, relative to the tile's first key.
+// Tile images. The pre-pass writes every (32-key tile, KV head) of K-hat and
+// of V as an 8 KiB block that is copied byte for byte into an LDS ring stage:
+//   K-hat: [key][128 dims], 16-byte chunk c of key j at position c ^ (j & 15);
+//   V^T:   [dim][32 keys], 16-byte chunk c of dim row r at position
+//          c ^ ((r >> 2) & 3); chunk c holds keys 16(c/2) + 4(c%2) + {0..3}
+//          and 16(c/2) + 8 + 4(c%2) + {0..3}, the key order of a lane's P
+//          fragment (see softmax_tile).
+// Both swizzles make every 16-lane phase of a ds_read_b128 hit 16 distinct
+// 16-byte bank groups. Images are stored [tile][KV head], so thread t copies
+// bytes [16t, 16t + 16) of one image.
 struct LaneOffsets {
-  unsigned dma_k, dma_v;     // buffer offsets (the tile part goes in the scalar offset)
+  unsigned dma;              // buffer offset of this thread's copy unit (the tile part goes in the scalar offset)
   int kq[8];                 // S operand of k-step ks: key (l & 31), chunk 2ks + (l >> 5)
-  int vq[4];                 // P V operand, dim block db: tr-read base of key (b>>1)*4 + n/4
+  int vq[2];                 // P V operand of k-step t: dim row (l & 31), chunk 2t + (l >> 5)
 };
 
-__device__ __forceinline__ LaneOffsets lane_offsets(int tid, int hk, int kvh) {
+__device__ __forceinline__ LaneOffsets lane_offsets(int tid, int kvh) {
   LaneOffsets o;
   const int lane = tid & 63;
-  const int u = tid;                                 // one unit per thread per tensor
-  const int key = u >> 4, pc = u & 15;
-  const unsigned row = unsigned(key * hk + kvh) * ROW_BYTES;
-  o.dma_k = row + unsigned((pc ^ (key & 15)) * 16);
-  o.dma_v = row + unsigned(((((pc >> 2) ^ (key & 3)) << 2) | (pc & 3)) * 16);
+  o.dma = unsigned(kvh) * TILE_BYTES + unsigned(tid) * 16;
   const int l31 = lane & 31, hi5 = lane >> 5;
 #pragma unroll
   for (int ks = 0; ks < 8; ++ks) o.kq[ks] = l31 * ROW_BYTES + (((2 * ks + hi5) ^ (lane & 15)) * 16);
-  const int b = lane >> 4, n = lane & 15;
-  const int key_in = (b >> 1) * 4 + (n >> 2);
-  const int dim_in = (b & 1) * 16 + (n & 3) * 4;
 #pragma unroll
-  for (int db = 0; db < 4; ++db) o.vq[db] = key_in * ROW_BYTES + ((db ^ (key_in & 3)) * 64) + dim_in * 2;
+  for (int t = 0; t < 2; ++t) o.vq[t] = l31 * (BN * 2) + (((2 * t + hi5) ^ ((l31 >> 2) & 3)) * 16);
   return o;
 }
 
@@ -188,21 +185,16 @@ __device__ __forceinline__ void qk_tile(const unsigned char* kst, const LaneOffs
   }
 }
 
-// Phase 2 (MFMA part): O^T += V^T P^T for the previous tile.
-// k-step t covers keys t*16 + {s*8 + hi5*4 + r}: the P layout.
-// ds_read_b64_tr_b16: lane 16b+n receives, for r = 0..3, element n%4 of what
-// lane 16b + 4r + n/4 read; lane 16b+i therefore reads 4 dims of key
-// (.. + (b>>1)*4 + i/4) at dim (b&1)*16 + (i%4)*4 of the 32-dim block.
+// Phase 2 (MFMA part): O^T += V^T P^T for the previous tile. The A operand
+// of k-step t, dim block db is one 16-byte chunk of the V^T image: dims
+// db*32 + (l & 31), the 8 keys of logical chunk 2t + (l >> 5), in the order
+// of the lane's P fragment.
 __device__ __forceinline__ void pv_tile(const unsigned char* vst, const LaneOffsets& lo, WaveState& st) {
 #pragma unroll
   for (int t = 0; t < 2; ++t)
 #pragma unroll
     for (int db = 0; db < 4; ++db) {
-      i16x4 h[2];
-#pragma unroll
-      for (int sidx = 0; sidx < 2; ++sidx)
-        h[sidx] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(i16x4, vst + (t * 16 + sidx * 8) * ROW_BYTES + lo.vq[db]));
-      const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(h[0], h[1], 0, 1, 2, 3, 4, 5, 6, 7));
+      const bf16x8 a = *LDS_PTR(const bf16x8, vst + db * (32 * BN * 2) + lo.vq[t]);
 #pragma unroll
       for (int rb = 0; rb < NRB; ++rb)
         st.o[rb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, st.p[rb][t], st.o[rb][db], 0, 0, 0);
@@ -264,7 +256,7 @@ __device__ __forceinline__ void softmax_tile(f32x16 (&s)[NRB], int kt, WaveState
 struct LoopCtx {
   i32x4 rsk, rsv;             // buffer resources of K and V
   unsigned k_base, v_base;    // LDS byte addresses of the K and V rings (plus this wave's 1 KiB block)
-  unsigned tile_stride;       // bytes between consecutive key tiles of one KV head: BN * hk * ROW_BYTES
+  unsigned tile_stride;       // bytes between the images of consecutive key tiles of one KV head: hk * TILE_BYTES
   const int* tiles;           // this item's key tile codes
   int n_tiles;
 };
@@ -276,8 +268,8 @@ __device__ __forceinline__ void issue_copies(const LoopCtx& c, const LaneOffsets
   const int cv = c.tiles[jv < c.n_tiles ? (jv < 0 ? 0 : jv) : c.n_tiles - 1];
   const unsigned sk = (j >= 0 && j < c.n_tiles) ? unsigned(ck >> 1) * c.tile_stride : kNoTile;
   const unsigned sv = (jv >= 0 && jv < c.n_tiles) ? unsigned(cv >> 1) * c.tile_stride : kNoTile;
-  dma16(c.rsk, lo.dma_k, sk, c.k_base + js * TILE_BYTES);
-  dma16(c.rsv, lo.dma_v, sv, c.v_base + jvs * TILE_BYTES);
+  dma16(c.rsk, lo.dma, sk, c.k_base + js * TILE_BYTES);
+  dma16(c.rsv, lo.dma, sv, c.v_base + jvs * TILE_BYTES);
 }
 
 // One tile i. The stage of tile j is j % NSTAGE; callers that know i % NSTAGE
@@ -370,14 +362,15 @@ fwd_bf16_d128_kernel(FwdParams prm, const int4* __restrict__ items, const int* _
   }
 
   // ---- K/V copies of iterations -LOOKAHEAD-1 .. -1 (V(-1) is a zero tile)
-  const unsigned kv_bytes = unsigned(prm.tk) * unsigned(prm.hk) * unsigned(ROW_BYTES);
-  const LaneOffsets lo = lane_offsets(tid, prm.hk, kvh);
+  const unsigned n_kt = unsigned(prm.tk + BN - 1) / BN;
+  const unsigned img_bytes = n_kt * unsigned(prm.hk) * unsigned(TILE_BYTES);
+  const LaneOffsets lo = lane_offsets(tid, kvh);
   LoopCtx ctx;
-  ctx.rsk = make_rsrc(prm.k_hat, kv_bytes);
-  ctx.rsv = make_rsrc(prm.v, kv_bytes);
+  ctx.rsk = make_rsrc(prm.ws, img_bytes);
+  ctx.rsv = make_rsrc(static_cast<const unsigned char*>(prm.ws) + img_bytes, img_bytes);
   ctx.k_base = __builtin_amdgcn_readfirstlane(lds_addr(&sm.k[0][0])) + wave * 1024;
   ctx.v_base = __builtin_amdgcn_readfirstlane(lds_addr(&sm.v[0][0])) + wave * 1024;
-  ctx.tile_stride = unsigned(BN) * unsigned(prm.hk) * unsigned(ROW_BYTES);
+  ctx.tile_stride = unsigned(prm.hk) * unsigned(TILE_BYTES);
   ctx.tiles = tiles + tb;
   ctx.n_tiles = n_tiles;
 #pragma unroll
@@ -451,38 +444,73 @@ fwd_bf16_d128_kernel(FwdParams prm, const int4* __restrict__ items, const int* _
   }
 }
 
-// RMS-normalises every key once: k_hat = k / sqrt(mean_d k^2 + eps), bf16,
-// same [T_k][H_kv][128] layout. 16 lanes per key row, 16 bytes each; the row
-// sum of squares is reduced with DPP inside each 16-lane row.
-constexpr int KN_THREADS = 256;
-__global__ void __launch_bounds__(KN_THREADS) k_normalize_kernel(const __bf16* __restrict__ k, __bf16* __restrict__ kh,
-                                                                 long long n_rows, float eps) {
-  const long long row = (long long)blockIdx.x * (KN_THREADS / 16) + (threadIdx.x >> 4);
-  if (row >= n_rows) return;                          // whole 16-lane rows exit together
-  const int part = threadIdx.x & 15;
-  const bf16x8 x = *reinterpret_cast<const bf16x8*>(k + row * D + part * 8);
-  float ss = sumsq8(x, 0.0f);
-  ss += dpp<0xB1>(ss);                    // quad_perm [1,0,3,2]
-  ss += dpp<0x4E>(ss);                    // quad_perm [2,3,0,1]
-  ss += dpp<0x141>(ss);                   // row_half_mirror: the other quad of 8 lanes
-  ss += dpp<0x140>(ss);                   // row_mirror: the other half of the 16 lanes
-  const float r = __builtin_amdgcn_rsqf(ss * (1.0f / D) + eps);
-  bf16x8 y;
+// Pre-pass: one workgroup per (32-key tile, KV head) writes that tile's two
+// images (layouts above). Keys are RMS-normalised here, once per key:
+// k_hat = k / sqrt(mean_d k^2 + eps) in bf16 (g_k is folded into the
+// queries). Keys past T_k are written as zeros in both images.
+constexpr int PP_THREADS = 256;
+__global__ void __launch_bounds__(PP_THREADS) kv_prepare_kernel(const __bf16* __restrict__ k,
+                                                                const __bf16* __restrict__ v,
+                                                                unsigned char* __restrict__ kimg,
+                                                                unsigned char* __restrict__ vimg, int tk, int hk,
+                                                                float eps) {
+  __shared__ __attribute__((aligned(16))) unsigned char vs[TILE_BYTES];
+  const int kt = blockIdx.x / hk, kvh = blockIdx.x % hk;
+  const size_t img = size_t(blockIdx.x) * TILE_BYTES;
+  const int tid = threadIdx.x;
 #pragma unroll
-  for (int j = 0; j < 8; ++j) y[j] = (__bf16)(float(x[j]) * r);
-  *reinterpret_cast<bf16x8*>(kh + row * D + part * 8) = y;
+  for (int r = 0; r < 2; ++r) {
+    const int u = tid + r * PP_THREADS;        // key u / 16, 16-byte chunk u % 16; 16 lanes per key
+    const int key = u >> 4, c = u & 15;
+    const int tok = kt * BN + key;
+    bf16x8 x = {}, y = {};
+    if (tok < tk) {
+      const size_t src = (size_t(tok) * hk + kvh) * D + c * 8;
+      x = *reinterpret_cast<const bf16x8*>(k + src);
+      y = *reinterpret_cast<const bf16x8*>(v + src);
+    }
+    float ss = sumsq8(x, 0.0f);
+    ss += dpp<0xB1>(ss);                  // quad_perm [1,0,3,2]
+    ss += dpp<0x4E>(ss);                  // quad_perm [2,3,0,1]
+    ss += dpp<0x141>(ss);                 // row_half_mirror: the other quad of 8 lanes
+    ss += dpp<0x140>(ss);                 // row_mirror: the other half of the 16 lanes
+    const float rk = tok < tk ? __builtin_amdgcn_rsqf(ss * (1.0f / D) + eps) : 0.0f;
+    bf16x8 xn;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) xn[j] = (__bf16)(float(x[j]) * rk);
+    *reinterpret_cast<bf16x8*>(kimg + img + key * ROW_BYTES + ((c ^ (key & 15)) * 16)) = xn;
+    *LDS_PTR(bf16x8, vs + key * ROW_BYTES + c * 16) = y;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int r = 0; r < 2; ++r) {
+    const int u = tid + r * PP_THREADS;        // V^T unit: dim row u / 4, physical chunk u % 4
+    const int d = u >> 2, c = (u & 3) ^ ((d >> 2) & 3);
+    bf16x8 w;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int key = 16 * (c >> 1) + 8 * (j >> 2) + 4 * (c & 1) + (j & 3);
+      w[j] = *LDS_PTR(const __bf16, vs + key * ROW_BYTES + d * 2);
+    }
+    *reinterpret_cast<bf16x8*>(vimg + img + u * 16) = w;
+  }
 }
 
 }  // namespace
 
-size_t workspace_bytes_bf16(long long tk, int hk, int d) { return size_t(tk) * size_t(hk) * size_t(d) * 2; }
+size_t workspace_bytes_bf16(long long tk, int hk, int d) {
+  (void)d;
+  const size_t n_kt = size_t((tk + BN - 1) / BN);
+  return 2 * n_kt * size_t(hk) * TILE_BYTES;          // K-hat images, then V^T images
+}
 
 hipError_t launch_fwd_bf16_d128(const FwdParams& p, int n_items, hipStream_t stream) {
-  const long long n_rows = (long long)p.tk * p.hk;
-  if (n_rows > 0) {
-    const unsigned blocks = unsigned((n_rows + KN_THREADS / 16 - 1) / (KN_THREADS / 16));
-    hipLaunchKernelGGL(k_normalize_kernel, dim3(blocks), dim3(KN_THREADS), 0, stream,
-                       static_cast<const __bf16*>(p.k), static_cast<__bf16*>(p.k_hat), n_rows, p.eps);
+  const long long n_kt = (p.tk + BN - 1) / BN;
+  if (n_kt > 0) {
+    unsigned char* kimg = static_cast<unsigned char*>(p.ws);
+    unsigned char* vimg = kimg + size_t(n_kt) * size_t(p.hk) * TILE_BYTES;
+    hipLaunchKernelGGL(kv_prepare_kernel, dim3(unsigned(n_kt * p.hk)), dim3(PP_THREADS), 0, stream,
+                       static_cast<const __bf16*>(p.k), static_cast<const __bf16*>(p.v), kimg, vimg, p.tk, p.hk, p.eps);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

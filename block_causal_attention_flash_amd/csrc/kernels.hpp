@@ -10,7 +10,7 @@ struct FwdParams {
   const void* q;
   const void* k;
   const void* v;
-  void* k_hat;           // bf16 path: workspace holding RMS-normalised K, [T_k][H_kv][d]
+  void* ws;              // bf16 path: workspace of per-tile K-hat and V^T images (fwd_bf16.hip)
   void* out;
   float* lse;
   const float* q_gain;

@@ -67,7 +67,9 @@ magi_status_t validate_layout(const magi_attn_layout_t* L, std::string& err) {
     return MAGI_ERR_UNSUPPORTED;
   }
   const int64_t esize = L->dtype == MAGI_DTYPE_BF16 ? 2 : 4;
-  const int64_t kv_bytes = int64_t(kv[L->n_chunks]) * L->n_kv_heads * L->head_dim * esize;
+  // bf16 keys/values are re-laid out in 32-key tiles: count whole tiles
+  const int64_t tk_pad = L->dtype == MAGI_DTYPE_BF16 ? (int64_t(kv[L->n_chunks]) + 31) / 32 * 32 : kv[L->n_chunks];
+  const int64_t kv_bytes = tk_pad * L->n_kv_heads * L->head_dim * esize;
   const int64_t q_elems = int64_t(L->q_offsets[L->n_chunks]) * L->n_q_heads;
   if (kv_bytes >= (int64_t(1) << 31)) { err = "K/V tensors must be smaller than 2 GiB each"; return MAGI_ERR_UNSUPPORTED; }
   if (q_elems >= (int64_t(1) << 31)) { err = "T_q * n_q_heads must be below 2^31"; return MAGI_ERR_UNSUPPORTED; }
@@ -78,7 +80,7 @@ Tiling choose_tiling(int dtype, int head_dim, int group) {
   (void)head_dim;
   Tiling t{};
   if (dtype == MAGI_DTYPE_BF16) {
-    // 256 (token, head) rows per workgroup: 4 waves x 64 rows. As many query
+    // 256 (token, head) rows per workgroup: 8 waves x 32 rows. As many query
     // heads of the GQA group as divide it (power of two, <= 8) share one
     // workgroup, so one K/V tile in LDS serves all of them.
     int hpw = 1;

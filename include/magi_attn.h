@@ -101,8 +101,9 @@ typedef struct magi_attn_plan magi_attn_plan_t;   /* opaque */
  * A plan is immutable after creation and may be used by concurrent calls on
  * several streams of the device it was created on.
  * Errors: MAGI_ERR_INVALID_ARG (layout rules above), MAGI_ERR_UNSUPPORTED
- * (head_dim/dtype combination; K or V of 2 GiB or more; T_q * n_q_heads of
- * 2^31 or more), MAGI_ERR_NO_MEMORY, MAGI_ERR_HIP. On error
+ * (head_dim/dtype combination; K or V of 2 GiB or more, for bf16 with T_k
+ * rounded up to a multiple of 32; T_q * n_q_heads of 2^31 or more),
+ * MAGI_ERR_NO_MEMORY, MAGI_ERR_HIP. On error
  * *plan is set to NULL. Validation runs before any HIP call.
  */
 MAGI_API magi_status_t magi_attn_plan_create(const magi_attn_layout_t* layout, magi_attn_plan_t** plan);
@@ -112,8 +113,9 @@ MAGI_API magi_status_t magi_attn_plan_create(const magi_attn_layout_t* layout, m
 MAGI_API magi_status_t magi_attn_plan_destroy(magi_attn_plan_t* plan);
 
 /*
- * Device workspace bytes that magi_attn_fwd needs for this plan (bf16: one
- * RMS-normalised copy of K, T_k * n_kv_heads * head_dim * 2 bytes; fp32: 0).
+ * Device workspace bytes that magi_attn_fwd needs for this plan (bf16: the
+ * RMS-normalised keys and the values re-laid out in 32-key tiles,
+ * 2 * ceil(T_k / 32) * 32 * n_kv_heads * head_dim * 2 bytes; fp32: 0).
  */
 MAGI_API magi_status_t magi_attn_workspace_size(const magi_attn_plan_t* plan, size_t* bytes);
 
