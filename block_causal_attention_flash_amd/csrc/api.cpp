@@ -14,9 +14,10 @@
 struct magi_attn_plan {
   magi::HostPlan host;
   int device = 0;
-  void* dmem = nullptr;          // one allocation: items | tile codes | row bounds
+  void* dmem = nullptr;          // one allocation: items | tile codes | tile copy offsets | row bounds
   const int4* d_items = nullptr;
   const int* d_tiles = nullptr;
+  const unsigned* d_soffs = nullptr;
   const int2* d_rows = nullptr;
 };
 
@@ -113,8 +114,10 @@ magi_status_t magi_attn_plan_create(const magi_attn_layout_t* layout, magi_attn_
   const auto& H = p->host;
   const size_t b_items = H.items.size() * sizeof(magi::WorkItem);
   const size_t b_tiles = H.tile_codes.size() * sizeof(int32_t);
+  const size_t b_soffs = H.tile_soff.size() * sizeof(uint32_t);
   const size_t b_rows = H.rows.size() * sizeof(magi::RowBounds);
-  const size_t o_tiles = round_up(b_items, 256), o_rows = o_tiles + round_up(b_tiles, 256);
+  const size_t o_tiles = round_up(b_items, 256), o_soffs = o_tiles + round_up(b_tiles, 256);
+  const size_t o_rows = o_soffs + round_up(b_soffs, 256);
   const size_t total = std::max<size_t>(o_rows + b_rows, 256);
   hipError_t e = hipGetDevice(&p->device);
   if (e != hipSuccess) { delete p; return hip_fail(e, "hipGetDevice"); }
@@ -126,6 +129,7 @@ magi_status_t magi_attn_plan_create(const magi_attn_layout_t* layout, magi_attn_
   char* base = static_cast<char*>(p->dmem);
   if (b_items) e = hipMemcpy(base, H.items.data(), b_items, hipMemcpyHostToDevice);
   if (e == hipSuccess && b_tiles) e = hipMemcpy(base + o_tiles, H.tile_codes.data(), b_tiles, hipMemcpyHostToDevice);
+  if (e == hipSuccess && b_soffs) e = hipMemcpy(base + o_soffs, H.tile_soff.data(), b_soffs, hipMemcpyHostToDevice);
   if (e == hipSuccess && b_rows) e = hipMemcpy(base + o_rows, H.rows.data(), b_rows, hipMemcpyHostToDevice);
   if (e != hipSuccess) {
     (void)hipFree(p->dmem);
@@ -134,6 +138,7 @@ magi_status_t magi_attn_plan_create(const magi_attn_layout_t* layout, magi_attn_
   }
   p->d_items = reinterpret_cast<const int4*>(base);
   p->d_tiles = reinterpret_cast<const int*>(base + o_tiles);
+  p->d_soffs = reinterpret_cast<const unsigned*>(base + o_soffs);
   p->d_rows = reinterpret_cast<const int2*>(base + o_rows);
   *out_plan = p;
   return MAGI_OK;
@@ -188,6 +193,7 @@ magi_status_t magi_attn_fwd(const magi_attn_plan_t* plan, const void* q, const v
   prm.k_gain = k_gain;
   prm.items = plan->d_items;
   prm.tiles = plan->d_tiles;
+  prm.soffs = plan->d_soffs;
   prm.rows = plan->d_rows;
   prm.eps = rms_eps;
   prm.scale = scale;

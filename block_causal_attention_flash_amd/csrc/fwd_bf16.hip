@@ -148,10 +148,12 @@ __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(
 struct LaneOffsets {
   unsigned dma;              // buffer offset of this thread's copy unit (the tile part goes in the scalar offset)
   int kq[8];                 // S operand of k-step ks: key (l & 31), chunk 2ks + (l >> 5)
-  int vq[2];                 // P V operand of k-step t: dim row (l & 31), chunk 2t + (l >> 5)
+  unsigned vq[2];            // P V operand of k-step t: LDS address in V stage 0 of dim row (l & 31),
+                             // chunk 2t + (l >> 5); opaque to the compiler, so that the stage and dim
+                             // block offsets stay immediates (the V ring lies above 64 KiB)
 };
 
-__device__ __forceinline__ LaneOffsets lane_offsets(int tid, int kvh) {
+__device__ __forceinline__ LaneOffsets lane_offsets(int tid, int kvh, unsigned v_ring) {
   LaneOffsets o;
   const int lane = tid & 63;
   o.dma = unsigned(kvh) * TILE_BYTES + unsigned(tid) * 16;
@@ -159,14 +161,17 @@ __device__ __forceinline__ LaneOffsets lane_offsets(int tid, int kvh) {
 #pragma unroll
   for (int ks = 0; ks < 8; ++ks) o.kq[ks] = l31 * ROW_BYTES + (((2 * ks + hi5) ^ (lane & 15)) * 16);
 #pragma unroll
-  for (int t = 0; t < 2; ++t) o.vq[t] = l31 * (BN * 2) + (((2 * t + hi5) ^ ((l31 >> 2) & 3)) * 16);
+  for (int t = 0; t < 2; ++t) {
+    o.vq[t] = v_ring + unsigned(l31 * (BN * 2) + (((2 * t + hi5) ^ ((l31 >> 2) & 3)) * 16));
+    asm("" : "+v"(o.vq[t]));
+  }
   return o;
 }
 
 struct WaveState {
   bf16x8 qf[NRB][8];     // B operands of S^T, per row block: lane row (l & 31), dims (2ks + (l>>5)) * 8 ..
   f32x16 o[NRB][4];      // O^T accumulators: lane row (l & 31), 4 dim blocks of 32
-  bf16x8 p[NRB][2];      // P of the previous tile, per (row block, 16-key k-step)
+  f32x16 s[NRB];         // S^T of the previous tile, softmaxed one step later
   float lsum[NRB];       // partial row sums over this lane's half of the keys
   float m[NRB];          // online path: reference maximum (log2 units)
   int lo[NRB], hi[NRB];  // key bounds of the lane's rows
@@ -189,19 +194,20 @@ __device__ __forceinline__ void qk_tile(const unsigned char* kst, const LaneOffs
 // of k-step t, dim block db is one 16-byte chunk of the V^T image: dims
 // db*32 + (l & 31), the 8 keys of logical chunk 2t + (l >> 5), in the order
 // of the lane's P fragment.
-__device__ __forceinline__ void pv_tile(const unsigned char* vst, const LaneOffsets& lo, WaveState& st) {
+__device__ __forceinline__ void pv_tile(int vstage, const LaneOffsets& lo, const bf16x8 (&p)[NRB][2], WaveState& st) {
+  typedef __attribute__((address_space(3))) const bf16x8 lds_bf16x8;
 #pragma unroll
   for (int t = 0; t < 2; ++t)
 #pragma unroll
     for (int db = 0; db < 4; ++db) {
-      const bf16x8 a = *LDS_PTR(const bf16x8, vst + db * (32 * BN * 2) + lo.vq[t]);
+      const bf16x8 a = *(lds_bf16x8*)(size_t)(lo.vq[t] + unsigned(vstage * TILE_BYTES + db * (32 * BN * 2)));
 #pragma unroll
       for (int rb = 0; rb < NRB; ++rb)
-        st.o[rb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, st.p[rb][t], st.o[rb][db], 0, 0, 0);
+        st.o[rb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, p[rb][t], st.o[rb][db], 0, 0, 0);
     }
 }
 
-// Phase 2 (vector part): S(i) -> P(i). Lane holds keys u*8 + hi5*4 + e
+// Vector part: S -> P for one tile. Lane holds keys u*8 + hi5*4 + e
 // (u, e = 0..3) of its row for each row block.
 template <bool MASKED, bool STATIC>
 __device__ __forceinline__ void softmax_tile(f32x16 (&s)[NRB], int kt, WaveState& st, bf16x8 (&pn)[NRB][2],
@@ -256,43 +262,59 @@ __device__ __forceinline__ void softmax_tile(f32x16 (&s)[NRB], int kt, WaveState
 struct LoopCtx {
   i32x4 rsk, rsv;             // buffer resources of K and V
   unsigned k_base, v_base;    // LDS byte addresses of the K and V rings (plus this wave's 1 KiB block)
-  unsigned tile_stride;       // bytes between the images of consecutive key tiles of one KV head: hk * TILE_BYTES
-  const int* tiles;           // this item's key tile codes
+  const int* tiles;           // this item's key tile codes (for the boundary mask)
+  const unsigned* soffs;      // this item's tile copy offsets; kNoTile in the padding after the list
   int n_tiles;
 };
 
-// Starts the copies of K(j) into stage js and V(jv) into stage jvs (zeros when
-// the index is out of range). The tile codes come from the item's list.
-__device__ __forceinline__ void issue_copies(const LoopCtx& c, const LaneOffsets& lo, int j, int js, int jv, int jvs) {
-  const int ck = c.tiles[j < c.n_tiles ? (j < 0 ? 0 : j) : c.n_tiles - 1];
-  const int cv = c.tiles[jv < c.n_tiles ? (jv < 0 ? 0 : jv) : c.n_tiles - 1];
-  const unsigned sk = (j >= 0 && j < c.n_tiles) ? unsigned(ck >> 1) * c.tile_stride : kNoTile;
-  const unsigned sv = (jv >= 0 && jv < c.n_tiles) ? unsigned(cv >> 1) * c.tile_stride : kNoTile;
+// Starts the copies of the K tile image at scalar offset sk into stage js and
+// of the V image at sv into stage jvs (kNoTile: zeros).
+__device__ __forceinline__ void issue_copies(const LoopCtx& c, const LaneOffsets& lo, unsigned sk, int js, unsigned sv,
+                                             int jvs) {
   dma16(c.rsk, lo.dma, sk, c.k_base + js * TILE_BYTES);
   dma16(c.rsv, lo.dma, sv, c.v_base + jvs * TILE_BYTES);
 }
 
-// One tile i. The stage of tile j is j % NSTAGE; callers that know i % NSTAGE
-// at compile time pass it as SI so every LDS offset folds into an immediate.
+// Issue order of one full, statically bounded step (applied by the machine
+// scheduler to the step's instructions): the K reads run two ahead of the S
+// MFMA chain, four vector instructions of the previous tile's softmax sit
+// between consecutive MFMAs, and the V reads run two ahead of the P V MFMAs.
+__device__ __forceinline__ void order_static_step() {
+  __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);       // DS read: K0, K1
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);     // MFMA: S k-step k
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);     // DS read: K k+2, then V0, V1
+    __builtin_amdgcn_sched_group_barrier(0x402, 4, 0);     // VALU / transcendental: softmax
+  }
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);     // MFMA: P V
+    if (k < 6) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // DS read: V k+2
+  }
+}
+
+// One step i. The stage of tile j is j % NSTAGE; callers that know i % NSTAGE
+// at compile time pass it as si so every LDS offset folds into an immediate.
 // Top: wait for K(i+1) (issued LOOKAHEAD iterations ago; the later copies may
 // still fly), barrier (K(i) and V(i-1) landed for every wave, stages of tiles
-// i-1 / i-2 free), start K(i+1+LA) and V(i+LA).
-// Phase 1: S(i) on the matrix cores.
-// Phase 2: P(i-1) V(i-1) on the matrix cores; softmax(i) on the vector ALUs.
-template <bool MASKED, bool STATIC>
+// i-1 / i-2 free), start K(i+1+LA) and V(i+LA), whose copy offsets are sk and
+// sv. Then, on the matrix cores, S(i) and P(i-1) V(i-1); on the vector ALUs,
+// the softmax of S(i-1) into P(i-1), which overlaps S(i). MASKED_PREV: tile
+// i-1 is a boundary tile.
+template <bool MASKED_PREV, bool STATIC>
 __device__ __forceinline__ void tile_step(Smem& sm, const LoopCtx& c, const LaneOffsets& lo, WaveState& st, int i,
-                                          int si, int lane) {
+                                          int si, unsigned sk, unsigned sv, int lane) {
   wait_vmcnt<WAIT_YOUNGER>();
   lds_barrier();
-  issue_copies(c, lo, i + 1 + LOOKAHEAD, (si + 1 + LOOKAHEAD) % NSTAGE, i + LOOKAHEAD, (si + LOOKAHEAD) % NSTAGE);
-  f32x16 s[NRB];
-  qk_tile(sm.k[si], lo, st, s);
-  pv_tile(sm.v[(si + NSTAGE - 1) % NSTAGE], lo, st);
-  bf16x8 pn[NRB][2];
+  issue_copies(c, lo, sk, (si + 1 + LOOKAHEAD) % NSTAGE, sv, (si + LOOKAHEAD) % NSTAGE);
+  f32x16 s_new[NRB];
+  qk_tile(sm.k[si], lo, st, s_new);
+  bf16x8 p[NRB][2];
   float alpha[NRB];
-  softmax_tile<MASKED, STATIC>(s, c.tiles[i] >> 1, st, pn, alpha, lane);
+  softmax_tile<MASKED_PREV, STATIC>(st.s, MASKED_PREV ? (c.tiles[i - 1] >> 1) : 0, st, p, alpha, lane);
   if (!STATIC) {
-    // P(i-1) V(i-1) was accumulated against the old reference maximum.
+    // O holds the tiles before i-1, accumulated against the old reference maximum.
     bool any = false;
 #pragma unroll
     for (int rb = 0; rb < NRB; ++rb) any |= alpha[rb] != 1.0f;
@@ -303,33 +325,59 @@ __device__ __forceinline__ void tile_step(Smem& sm, const LoopCtx& c, const Lane
         for (int db = 0; db < 4; ++db) st.o[rb][db] *= alpha[rb];
     }
   }
+  pv_tile((si + NSTAGE - 1) % NSTAGE, lo, p, st);
 #pragma unroll
-  for (int rb = 0; rb < NRB; ++rb)
-#pragma unroll
-    for (int t = 0; t < 2; ++t) st.p[rb][t] = pn[rb][t];
+  for (int rb = 0; rb < NRB; ++rb) st.s[rb] = s_new[rb];
+  if (STATIC && !MASKED_PREV) order_static_step();
 }
 
-template <bool MASKED, bool STATIC, int U>
+// so[u] is the copy offset of tile i0 + LOOKAHEAD + u.
+template <bool STATIC, int U>
 __device__ __forceinline__ void unrolled_steps(Smem& sm, const LoopCtx& c, const LaneOffsets& lo, WaveState& st,
-                                               int i0, int lane) {
-  tile_step<MASKED, STATIC>(sm, c, lo, st, i0 + U, U, lane);
-  if constexpr (U + 1 < NSTAGE) unrolled_steps<MASKED, STATIC, U + 1>(sm, c, lo, st, i0, lane);
+                                               int i0, const unsigned (&so)[NSTAGE + 1], int lane) {
+  tile_step<false, STATIC>(sm, c, lo, st, i0 + U, U, so[U + 1], so[U], lane);
+  if constexpr (U + 1 < NSTAGE) unrolled_steps<STATIC, U + 1>(sm, c, lo, st, i0, so, lane);
 }
 
-// Full tiles first (no mask code), then boundary tiles. The full tiles run
-// NSTAGE at a time with compile-time stages; the rest one by one.
+// Full tiles first, then boundary tiles; the softmax of tile i runs in step
+// i + 1, and the last tile's softmax and P V after the loop. Steps whose
+// softmax tile is full run NSTAGE at a time with compile-time stages and
+// their copy offsets loaded once per group; the rest one by one. Copy
+// offsets are read up to LOOKAHEAD + 1 entries past the list, which the
+// list's padding covers.
 template <bool STATIC>
 __device__ __forceinline__ void run_tiles(Smem& sm, const LoopCtx& c, const LaneOffsets& lo, int n_full,
                                           WaveState& st, int lane) {
+  const int n = c.n_tiles;
+  const int n_plain = n_full + 1 < n ? n_full + 1 : n;      // steps i <= n_full: tile i-1 is full
   int i = 0;
-  for (; i + NSTAGE <= n_full; i += NSTAGE) unrolled_steps<false, STATIC, 0>(sm, c, lo, st, i, lane);
-  for (; i < n_full; ++i) tile_step<false, STATIC>(sm, c, lo, st, i, i % NSTAGE, lane);
-  for (; i < c.n_tiles; ++i) tile_step<true, STATIC>(sm, c, lo, st, i, i % NSTAGE, lane);
+  for (; i + NSTAGE <= n_plain; i += NSTAGE) {
+    unsigned so[NSTAGE + 1];
+#pragma unroll
+    for (int u = 0; u <= NSTAGE; ++u) so[u] = c.soffs[i + LOOKAHEAD + u];
+    unrolled_steps<STATIC, 0>(sm, c, lo, st, i, so, lane);
+  }
+  for (; i < n_plain; ++i)
+    tile_step<false, STATIC>(sm, c, lo, st, i, i % NSTAGE, c.soffs[i + 1 + LOOKAHEAD], c.soffs[i + LOOKAHEAD], lane);
+  for (; i < n; ++i)
+    tile_step<true, STATIC>(sm, c, lo, st, i, i % NSTAGE, c.soffs[i + 1 + LOOKAHEAD], c.soffs[i + LOOKAHEAD], lane);
+  // last tile: its V stage landed before the last barrier
+  bf16x8 p[NRB][2];
+  float alpha[NRB];
+  if (n - 1 >= n_full) softmax_tile<true, STATIC>(st.s, c.tiles[n - 1] >> 1, st, p, alpha, lane);
+  else softmax_tile<false, STATIC>(st.s, 0, st, p, alpha, lane);
+  if (!STATIC) {
+#pragma unroll
+    for (int rb = 0; rb < NRB; ++rb)
+#pragma unroll
+      for (int db = 0; db < 4; ++db) st.o[rb][db] *= alpha[rb];
+  }
+  pv_tile((n + NSTAGE - 1) % NSTAGE, lo, p, st);
 }
 
 __global__ void __launch_bounds__(NTHR) __attribute__((amdgpu_waves_per_eu(NRB == 1 ? 2 : 1, NRB == 1 ? 2 : 1)))
 fwd_bf16_d128_kernel(FwdParams prm, const int4* __restrict__ items, const int* __restrict__ tiles,
-                     const int2* __restrict__ rows) {
+                     const unsigned* __restrict__ soffs, const int2* __restrict__ rows) {
   __shared__ __attribute__((aligned(1024))) Smem sm;
   const int4 item = items[2 * blockIdx.x];
   if (item.z == item.w) return;                       // padding item
@@ -364,18 +412,19 @@ fwd_bf16_d128_kernel(FwdParams prm, const int4* __restrict__ items, const int* _
   // ---- K/V copies of iterations -LOOKAHEAD-1 .. -1 (V(-1) is a zero tile)
   const unsigned n_kt = unsigned(prm.tk + BN - 1) / BN;
   const unsigned img_bytes = n_kt * unsigned(prm.hk) * unsigned(TILE_BYTES);
-  const LaneOffsets lo = lane_offsets(tid, kvh);
+  const LaneOffsets lo = lane_offsets(tid, kvh, lds_addr(&sm.v[0][0]));
   LoopCtx ctx;
   ctx.rsk = make_rsrc(prm.ws, img_bytes);
   ctx.rsv = make_rsrc(static_cast<const unsigned char*>(prm.ws) + img_bytes, img_bytes);
   ctx.k_base = __builtin_amdgcn_readfirstlane(lds_addr(&sm.k[0][0])) + wave * 1024;
   ctx.v_base = __builtin_amdgcn_readfirstlane(lds_addr(&sm.v[0][0])) + wave * 1024;
-  ctx.tile_stride = unsigned(prm.hk) * unsigned(TILE_BYTES);
   ctx.tiles = tiles + tb;
+  ctx.soffs = soffs + tb;
   ctx.n_tiles = n_tiles;
 #pragma unroll
   for (int j = -LOOKAHEAD - 1; j < 0; ++j)
-    issue_copies(ctx, lo, j + 1 + LOOKAHEAD, (j + 1 + LOOKAHEAD + NSTAGE) % NSTAGE, j + LOOKAHEAD,
+    issue_copies(ctx, lo, ctx.soffs[j + 1 + LOOKAHEAD], (j + 1 + LOOKAHEAD + NSTAGE) % NSTAGE,
+                 j + LOOKAHEAD >= 0 ? ctx.soffs[j + LOOKAHEAD] : kNoTile,
                  (j + LOOKAHEAD + NSTAGE) % NSTAGE);
 
   if (tid < D) sm.gqk[tid] = prm.q_gain[tid] * prm.k_gain[tid] * (prm.scale * kLog2e);
@@ -408,7 +457,7 @@ fwd_bf16_d128_kernel(FwdParams prm, const int4* __restrict__ items, const int* _
 #pragma unroll
     for (int db = 0; db < 4; ++db) st.o[rb][db] = f32x16{};
 #pragma unroll
-    for (int t = 0; t < 2; ++t) st.p[rb][t] = bf16x8{};
+    for (int e = 0; e < 16; ++e) st.s[rb][e] = kNegInf;        // tile -1: P = 0
     st.lsum[rb] = 0.0f;
     st.m[rb] = kNegInf;
   }
@@ -416,8 +465,6 @@ fwd_bf16_d128_kernel(FwdParams prm, const int4* __restrict__ items, const int* _
 
   if (stat) run_tiles<true>(sm, ctx, lo, n_full, st, lane);
   else run_tiles<false>(sm, ctx, lo, n_full, st, lane);
-  // last tile's P V: its V stage landed before the last barrier
-  pv_tile(sm.v[(n_tiles + NSTAGE - 1) % NSTAGE], lo, st);
 
   // ---- epilogue
 #pragma unroll
@@ -514,7 +561,7 @@ hipError_t launch_fwd_bf16_d128(const FwdParams& p, int n_items, hipStream_t str
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL(fwd_bf16_d128_kernel, dim3(n_items), dim3(NTHR), 0, stream, p, p.items, p.tiles, p.rows);
+  hipLaunchKernelGGL(fwd_bf16_d128_kernel, dim3(n_items), dim3(NTHR), 0, stream, p, p.items, p.tiles, p.soffs, p.rows);
   return hipGetLastError();
 }
 

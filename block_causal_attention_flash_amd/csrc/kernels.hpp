@@ -16,7 +16,8 @@ struct FwdParams {
   const float* q_gain;
   const float* k_gain;
   const int4* items;     // WorkItem[n_items], two int4 each
-  const int* tiles;      // key tile codes (kt * 2 + masked)
+  const int* tiles;      // key tile codes (kt * 2 + masked); lists padded with code -1
+  const unsigned* soffs; // parallel to tiles: byte offset of the tile's image block (bf16 path)
   const int2* rows;      // RowBounds[tq]
   float eps;
   float scale;           // softmax temperature on <q_hat, k_hat>

@@ -154,6 +154,7 @@ magi_status_t build_host_plan(const magi_attn_layout_t* L, const Tiling& tiling,
   P.qt_seg.assign(n_qt + 1, 0);
   P.tile_codes.clear();
   P.qt_tiles.assign(n_qt + 1, 0);
+  P.qt_ntiles.assign(n_qt, 0);
   P.qt_full.assign(n_qt, 0);
   std::vector<int32_t> masked_codes;
   std::vector<int64_t> qt_cost(n_qt, 0);
@@ -192,9 +193,17 @@ magi_status_t build_host_plan(const magi_attn_layout_t* L, const Tiling& tiling,
     }
     P.qt_full[qt] = int32_t(P.tile_codes.size()) - P.qt_tiles[qt];
     P.tile_codes.insert(P.tile_codes.end(), masked_codes.begin(), masked_codes.end());
+    P.qt_ntiles[qt] = int32_t(P.tile_codes.size()) - P.qt_tiles[qt];
+    P.tile_codes.insert(P.tile_codes.end(), kTilePad, -1);
   }
   P.qt_seg[n_qt] = int32_t(P.segs.size());
   P.qt_tiles[n_qt] = int32_t(P.tile_codes.size());
+  // Copy offsets of the bf16 path's per-tile image blocks ([tile][KV head]).
+  const int64_t image_bytes = int64_t(bn) * P.d * 2;
+  P.tile_soff.resize(P.tile_codes.size());
+  for (size_t t = 0; t < P.tile_codes.size(); ++t)
+    P.tile_soff[t] = P.tile_codes[t] < 0 ? kNoTileOffset
+                                         : uint32_t(int64_t(P.tile_codes[t] >> 1) * P.hk * image_bytes);
   S.empty_pairs = n_qt * n_kt - S.full_pairs - S.boundary_pairs;
 
   // Work items: (query tile, KV head, group of hpw query heads).
@@ -203,7 +212,7 @@ magi_status_t build_host_plan(const magi_attn_layout_t* L, const Tiling& tiling,
   cands.reserve(size_t(n_qt) * P.hk * groups_per_kvh);
   for (int kvh = 0; kvh < P.hk; ++kvh)
     for (int64_t qt = 0; qt < n_qt; ++qt) {
-      if (P.qt_tiles[qt + 1] == P.qt_tiles[qt]) continue;
+      if (P.qt_ntiles[qt] == 0) continue;
       for (int hg = 0; hg < groups_per_kvh; ++hg) cands.push_back(Cand{qt_cost[qt], int32_t(qt), kvh, hg});
     }
   // Longest first; among equals, consecutive query tiles and head groups of
@@ -219,7 +228,8 @@ magi_status_t build_host_plan(const magi_attn_layout_t* L, const Tiling& tiling,
   std::vector<int64_t> load(kNumXcd, 0);
   auto make_item = [&](const Cand& c) {
     const int h0 = c.kvh * group + c.hg * hpw;
-    return WorkItem{int32_t(c.qt * bm), (c.kvh << 16) | h0, P.qt_tiles[c.qt], P.qt_tiles[c.qt + 1], P.qt_full[c.qt],
+    return WorkItem{int32_t(c.qt * bm), (c.kvh << 16) | h0, P.qt_tiles[c.qt], P.qt_tiles[c.qt] + P.qt_ntiles[c.qt],
+                    P.qt_full[c.qt],
                     {0, 0, 0}};
   };
   if (P.hk % kNumXcd == 0 || kNumXcd % P.hk == 0) {

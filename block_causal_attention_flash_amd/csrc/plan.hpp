@@ -13,7 +13,9 @@ namespace magi {
 // One workgroup's work: query tokens [t0, t0 + tile_q) of `heads_per_item`
 // consecutive query heads starting at h0, all of KV head kvh, over the key
 // tiles whose codes are tile_codes[tile_begin, tile_end); the first n_full of
-// them are full tiles, the rest boundary tiles.
+// them are full tiles, the rest boundary tiles. Every list is followed by
+// kTilePad padding entries (code -1, copy offset kNoTileOffset), so a kernel
+// may read that far past tile_end.
 struct WorkItem {
   int32_t t0;
   int32_t heads;       // (kvh << 16) | h0
@@ -22,6 +24,9 @@ struct WorkItem {
   int32_t n_full;
   int32_t pad[3];
 };
+
+constexpr int kTilePad = 16;
+constexpr uint32_t kNoTileOffset = 0x80000000u;   // past any tile image buffer (< 2 GiB): reads give zeros
 
 // Key tile code: kt * 2 + masked (masked = 1 for boundary tiles).
 inline int32_t tile_code(int64_t kt, int masked) { return int32_t(kt * 2 + masked); }
@@ -54,8 +59,11 @@ struct HostPlan {
   std::vector<RowBounds> rows;       // [tq]
   std::vector<Segment> segs;         // all query tiles' segments, concatenated
   std::vector<int32_t> qt_seg;       // [n_qt + 1] segment range per query tile
-  std::vector<int32_t> tile_codes;   // per query tile: full key tiles ascending, then boundary tiles ascending
-  std::vector<int32_t> qt_tiles;     // [n_qt + 1] range in tile_codes per query tile
+  std::vector<int32_t> tile_codes;   // per query tile: full key tiles ascending, then boundary tiles ascending, then padding
+  std::vector<uint32_t> tile_soff;   // parallel to tile_codes (bf16): byte offset of the key tile's image block,
+                                     // kt * hk * tile_kv * d * 2; kNoTileOffset for padding
+  std::vector<int32_t> qt_tiles;     // [n_qt + 1] start of each query tile's list in tile_codes
+  std::vector<int32_t> qt_ntiles;    // [n_qt] key tiles per query tile (padding excluded)
   std::vector<int32_t> qt_full;      // [n_qt] number of full key tiles per query tile
   std::vector<WorkItem> items;       // launch order (XCD-interleaved, padded)
   magi_attn_stats_t stats{};
