@@ -59,6 +59,7 @@ constexpr int LOOKAHEAD = NSTAGE - 2;                 // copies issued this many
 constexpr int ROW_BYTES = D * 2;                      // 256
 constexpr int TILE_BYTES = BN * ROW_BYTES;            // 8 KiB
 constexpr int UNITS = TILE_BYTES / (NTHR * 16);       // 16-byte copies per thread per tensor
+constexpr int NPRE = 2;                               // K fragments of the next tile read before the barrier
 static_assert(UNITS == 1 && NRB >= 1, "tile shape");
 // Copies in flight that may be younger than the ones a tile needs: the
 // LOOKAHEAD-1 later iterations (K and V each) plus the V copy issued right
@@ -172,19 +173,20 @@ struct WaveState {
   bf16x8 qf[NRB][8];     // B operands of S^T, per row block: lane row (l & 31), dims (2ks + (l>>5)) * 8 ..
   f32x16 o[NRB][4];      // O^T accumulators: lane row (l & 31), 4 dim blocks of 32
   f32x16 s[NRB];         // S^T of the previous tile, softmaxed one step later
+  bf16x8 kpre[NPRE];     // first K fragments of the current tile, read before the barrier
   float lsum[NRB];       // partial row sums over this lane's half of the keys
   float m[NRB];          // online path: reference maximum (log2 units)
   int lo[NRB], hi[NRB];  // key bounds of the lane's rows
 };
 
-// Phase 1: S^T(tile in stage kst).
+// Phase 1: S^T(tile in stage kst); its first NPRE K fragments are in st.kpre.
 __device__ __forceinline__ void qk_tile(const unsigned char* kst, const LaneOffsets& lo, const WaveState& st,
                                         f32x16 (&s)[NRB]) {
 #pragma unroll
   for (int rb = 0; rb < NRB; ++rb) s[rb] = f32x16{};
 #pragma unroll
   for (int ks = 0; ks < 8; ++ks) {
-    const bf16x8 a = *LDS_PTR(const bf16x8, kst + lo.kq[ks]);
+    const bf16x8 a = ks < NPRE ? st.kpre[ks < NPRE ? ks : 0] : *LDS_PTR(const bf16x8, kst + lo.kq[ks]);
 #pragma unroll
     for (int rb = 0; rb < NRB; ++rb) s[rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, st.qf[rb][ks], s[rb], 0, 0, 0);
   }
@@ -276,22 +278,27 @@ __device__ __forceinline__ void issue_copies(const LoopCtx& c, const LaneOffsets
 }
 
 // Issue order of one full, statically bounded step (applied by the machine
-// scheduler to the step's instructions): the K reads run two ahead of the S
-// MFMA chain, four vector instructions of the previous tile's softmax sit
-// between consecutive MFMAs, and the V reads run two ahead of the P V MFMAs.
+// scheduler to the step's instructions): each of the 16 MFMAs (S of this
+// tile, P V of the previous one) is followed by the next LDS read and two
+// vector instructions of the previous tile's softmax, so the LDS reads stay
+// ahead of the MFMAs and the softmax overlaps them.
 __device__ __forceinline__ void order_static_step() {
-  __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);       // DS read: K0, K1
+  constexpr int reads = 16 - NPRE;
+  if (NPRE < 2) __builtin_amdgcn_sched_group_barrier(0x100, 2 - NPRE, 0);   // DS read
 #pragma unroll
-  for (int k = 0; k < 8; ++k) {
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);     // MFMA: S k-step k
-    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);     // DS read: K k+2, then V0, V1
-    __builtin_amdgcn_sched_group_barrier(0x402, 4, 0);     // VALU / transcendental: softmax
+  for (int k = 0; k < 16; ++k) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                       // MFMA
+    if (k + 2 - NPRE < reads && k < reads) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x402, 2, 0);                       // VALU, transcendental
   }
+  if (NPRE > 0) __builtin_amdgcn_sched_group_barrier(0x100, NPRE, 0);        // next tile's K prefetch
+}
+
+// Reads the first NPRE K fragments of the tile in stage kst into st.kpre;
+// their latency is spent before the next barrier, where the wave waits anyway.
+__device__ __forceinline__ void prefetch_k(const unsigned char* kst, const LaneOffsets& lo, WaveState& st) {
 #pragma unroll
-  for (int k = 0; k < 8; ++k) {
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);     // MFMA: P V
-    if (k < 6) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // DS read: V k+2
-  }
+  for (int ks = 0; ks < NPRE; ++ks) st.kpre[ks] = *LDS_PTR(const bf16x8, kst + lo.kq[ks]);
 }
 
 // One step i. The stage of tile j is j % NSTAGE; callers that know i % NSTAGE
@@ -328,6 +335,8 @@ __device__ __forceinline__ void tile_step(Smem& sm, const LoopCtx& c, const Lane
   pv_tile((si + NSTAGE - 1) % NSTAGE, lo, p, st);
 #pragma unroll
   for (int rb = 0; rb < NRB; ++rb) st.s[rb] = s_new[rb];
+  // K(i+1) was published by this step's barrier
+  prefetch_k(sm.k[(si + 1) % NSTAGE], lo, st);
   if (STATIC && !MASKED_PREV) order_static_step();
 }
 
@@ -428,7 +437,9 @@ fwd_bf16_d128_kernel(FwdParams prm, const int4* __restrict__ items, const int* _
                  (j + LOOKAHEAD + NSTAGE) % NSTAGE);
 
   if (tid < D) sm.gqk[tid] = prm.q_gain[tid] * prm.k_gain[tid] * (prm.scale * kLog2e);
-  __syncthreads();                                     // gqk visible
+  wait_vmcnt<2 * (LOOKAHEAD + 1) * UNITS - 1>();      // K(0), the oldest copy, landed
+  __syncthreads();                                     // gqk and K(0) visible
+  prefetch_k(sm.k[0], lo, st);
 
   // ---- query prologue: RMS-normalise, fold gains/temperature, to bf16
   float bound_max = 0.0f;
