@@ -5,26 +5,27 @@
 // softmax over its allowed keys of scale * <rms(q) * g_q, rms(k) * g_k>,
 // times V, plus the natural-log log-sum-exp. The forward's cost is the two
 // matrix products over the mask area (paperlayer §B.2.1), so both run on the
-// bf16 matrix cores (v_mfma_f32_32x32x16_bf16).
+// bf16 matrix cores (v_mfma_f32_16x16x32_bf16).
 //
-// Workgroup = one work item: 256 (token, head) rows of `heads_per_item`
-// query heads that share one KV head; 8 waves, two per SIMD, 32 rows each
-// (one 32-row MFMA block). Per 32-key tile:
+// Workgroup = one work item: 384 (token, head) rows, i.e. tile_q tokens of
+// `heads_per_item` query heads that share one KV head; 8 waves, two per SIMD,
+// 48 rows each (three 16-row MFMA blocks). Per 32-key tile:
 //   * a pre-pass kernel has RMS-normalised every key once (k_hat = k / rms(k),
 //     bf16) and written K-hat and V^T as per-tile LDS images into a
 //     workspace; g_k is folded into the normalised queries, so
 //     s_ij = <q'_i, k_hat_j>;
 //   * the K-hat and V^T images are copied from global memory straight into
 //     LDS rings (buffer_load ... lds, zero fill past the last tile) six tiles
-//     ahead, and serve all 256 rows: K/V leave L2 once per workgroup, not once
+//     ahead and serve all 384 rows: K/V leave L2 once per workgroup, not once
 //     per query head;
-//   * S^T = K Q'^T (lane = query row, 16 keys per lane in registers);
-//   * O^T += V^T P^T, both operands read with ds_read_b128 / kept in registers.
-// Software pipeline per iteration i: phase 1 issues the MFMAs of S(i);
-// phase 2 issues the MFMAs of P(i-1) V(i-1) while the vector ALUs turn S(i)
-// into P(i) (mask, exp2, round to bf16, row sums), so each wave's vector work
-// overlaps its own and its SIMD partner's matrix work. A workgroup barrier
-// per tile recycles the LDS rings.
+//   * S^T = K Q'^T: every K fragment read from LDS feeds the three row blocks
+//     of the wave (24 MFMAs per tile);
+//   * O^T += V^T P^T: every V^T fragment feeds the three row blocks (24 MFMAs);
+//     P stays in registers.
+// Software pipeline of step i: the MFMAs of S(i) and of P(i-1) V(i-1), with
+// the softmax of S(i-1) into P(i-1) on the vector ALUs between them, and the
+// LDS reads kept ahead of the MFMAs. A workgroup barrier per tile recycles the
+// LDS rings.
 //
 // Queries are normalised in the prologue (RMS over head_dim, times
 // g_q * g_k * scale * log2 e) and held in registers as bf16 MFMA operands.
@@ -35,6 +36,10 @@
 // rescaling: softmax is invariant to the shift and 2^+-40 lies far inside the
 // fp32/bf16 range. Otherwise the wave keeps a running row maximum and rescales
 // its accumulator only when the maximum has grown by more than 2^8.
+//
+// MFMA lane layouts (v_mfma_f32_16x16x32_bf16, lane l, g = l / 16):
+//   A: A[l % 16][8g + j], B: B[8g + j][l % 16] (j = 0..7), D: D[4g + i][l % 16]
+//   (i = 0..3).
 #include "kernels.hpp"
 
 namespace magi {
@@ -44,28 +49,29 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef int i32x4 __attribute__((ext_vector_type(4)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 #define LDS_PTR(T, p) ((__attribute__((address_space(3))) T*)(p))
+typedef __attribute__((address_space(3))) const bf16x8 lds_bf16x8;
 
 constexpr int D = 128;
 constexpr int BN = 32;                                // keys per tile
 constexpr int NWAVE = 8;                              // two waves per SIMD
-constexpr int NRB = 256 / 32 / NWAVE;                 // 32-row MFMA blocks per wave
+constexpr int NRB = 3;                                // 16-row MFMA blocks per wave
+constexpr int ROWS = NWAVE * NRB * 16;                // 384 rows per workgroup
 constexpr int NTHR = NWAVE * 64;
 constexpr int NSTAGE = 8;                             // LDS ring depth (K and V each)
 constexpr int LOOKAHEAD = NSTAGE - 2;                 // copies issued this many tiles ahead
 constexpr int ROW_BYTES = D * 2;                      // 256
 constexpr int TILE_BYTES = BN * ROW_BYTES;            // 8 KiB
-constexpr int UNITS = TILE_BYTES / (NTHR * 16);       // 16-byte copies per thread per tensor
 constexpr int NPRE = 2;                               // K fragments of the next tile read before the barrier
-static_assert(UNITS == 1 && NRB >= 1, "tile shape");
+static_assert(TILE_BYTES == NTHR * 16, "one 16-byte copy per thread per tensor and tile");
+static_assert(ROWS == kBf16RowsPerItem, "rows per work item");
 // Copies in flight that may be younger than the ones a tile needs: the
 // LOOKAHEAD-1 later iterations (K and V each) plus the V copy issued right
 // after the needed K copy.
-constexpr int WAIT_YOUNGER = (LOOKAHEAD - 1) * 2 * UNITS + UNITS;
-constexpr unsigned kNoTile = 0x80000000u;             // scalar offset past any K/V tensor (< 2 GiB): zeros
+constexpr int WAIT_YOUNGER = (LOOKAHEAD - 1) * 2 + 1;
+constexpr unsigned kNoTile = 0x80000000u;             // scalar offset past any tile image buffer (< 2 GiB): zeros
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kStaticBound = 40.0f;
@@ -83,7 +89,17 @@ __device__ __forceinline__ float dpp(float x) {
   return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xF, 0xF, false));
 }
 
-__device__ __forceinline__ float xor32(float x) { return __shfl_xor(x, 32, 64); }
+// Sum / maximum over the four 16-lane groups (lanes l, l^16, l^32, l^48).
+__device__ __forceinline__ float sum_groups(float x) {
+  x += __shfl_xor(x, 16, 64);
+  x += __shfl_xor(x, 32, 64);
+  return x;
+}
+__device__ __forceinline__ float max_groups(float x) {
+  x = fmaxf(x, __shfl_xor(x, 16, 64));
+  x = fmaxf(x, __shfl_xor(x, 32, 64));
+  return x;
+}
 
 __device__ __forceinline__ float sumsq8(bf16x8 a, float acc) {
 #pragma unroll
@@ -110,11 +126,11 @@ __device__ __forceinline__ i32x4 make_rsrc(const void* base, unsigned bytes) {
   return r;
 }
 
-// 16-byte copy global -> LDS at buffer offset voff + soff: lane i of the wave
-// writes LDS byte m0 + 16 i. Issued through asm so that the compiler does not
-// order later LDS reads of other ring stages behind it; completion is awaited
-// explicitly (vmcnt) before the barrier that publishes the stage.
-// m0 is saved and restored inside the asm block.
+// Global -> LDS copy of 16 bytes per lane: lane i reads buffer offset
+// voff + soff (zeros past num_records) and writes LDS byte lds + 16 i. Issued
+// through asm so that the compiler does not order later LDS reads of other
+// ring stages behind it; completion is awaited explicitly (vmcnt) before the
+// barrier that publishes the stage. m0 is saved and restored inside the asm.
 __device__ __forceinline__ void dma16(i32x4 rsrc, unsigned voff, unsigned soff, unsigned lds) {
   unsigned saved;
   asm volatile(
@@ -137,123 +153,130 @@ __device__ __forceinline__ void wait_vmcnt() {
 __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" : : : "memory"); }
 
 // Tile images. The pre-pass writes every (32-key tile, KV head) of K-hat and
-// of V as an 8 KiB block that is copied byte for byte into an LDS ring stage:
-//   K-hat: [key][128 dims], 16-byte chunk c of key j at position c ^ (j & 15);
-//   V^T:   [dim][32 keys], 16-byte chunk c of dim row r at position
-//          c ^ ((r >> 2) & 3); chunk c holds keys 16(c/2) + 4(c%2) + {0..3}
-//          and 16(c/2) + 8 + 4(c%2) + {0..3}, the key order of a lane's P
-//          fragment (see softmax_tile).
-// Both swizzles make every 16-lane phase of a ds_read_b128 hit 16 distinct
-// 16-byte bank groups. Images are stored [tile][KV head], so thread t copies
-// bytes [16t, 16t + 16) of one image.
+// of V as an 8 KiB block that is copied byte for byte into an LDS ring stage.
+// Both are chunk-major, so that a 16-lane phase of a ds_read_b128 reads 256
+// contiguous bytes (no bank conflicts) and every fragment address is a
+// per-lane base plus an instruction immediate:
+//   K-hat: [16 chunks][32 keys][16 bytes]: chunk c of key j (dims 8c..8c+7)
+//          at byte 512 c + 16 j;
+//   V^T:   [4 chunks][128 dims][16 bytes]: chunk c of dim row r holds keys
+//          4c + {0..3} and 16 + 4c + {0..3} (the key order of a lane's P
+//          fragment, see softmax_tile) at byte 2048 c + 16 r.
+// Images are stored [tile][KV head], so thread t copies bytes [16t, 16t + 16)
+// of one image.
 struct LaneOffsets {
-  unsigned dma;              // buffer offset of this thread's copy unit (the tile part goes in the scalar offset)
-  int kq[8];                 // S operand of k-step ks: key (l & 31), chunk 2ks + (l >> 5)
-  unsigned vq[2];            // P V operand of k-step t: LDS address in V stage 0 of dim row (l & 31),
-                             // chunk 2t + (l >> 5); opaque to the compiler, so that the stage and dim
-                             // block offsets stay immediates (the V ring lies above 64 KiB)
+  unsigned dma;      // buffer offset of this thread's copy unit (the tile part goes in the scalar offset)
+  unsigned kq;       // K ring, stage 0: fragment (ks, kb) at kq + 2048 ks + 256 kb
+  unsigned vq;       // V ring, stage 0: fragment db at vq + 256 db
+  // kq and vq are opaque to the compiler, so that stage and fragment offsets
+  // stay instruction immediates wherever the rings lie in LDS.
 };
 
-__device__ __forceinline__ LaneOffsets lane_offsets(int tid, int kvh, unsigned v_ring) {
+__device__ __forceinline__ LaneOffsets lane_offsets(int tid, int kvh, unsigned k_ring, unsigned v_ring) {
   LaneOffsets o;
   const int lane = tid & 63;
   o.dma = unsigned(kvh) * TILE_BYTES + unsigned(tid) * 16;
-  const int l31 = lane & 31, hi5 = lane >> 5;
-#pragma unroll
-  for (int ks = 0; ks < 8; ++ks) o.kq[ks] = l31 * ROW_BYTES + (((2 * ks + hi5) ^ (lane & 15)) * 16);
-#pragma unroll
-  for (int t = 0; t < 2; ++t) {
-    o.vq[t] = v_ring + unsigned(l31 * (BN * 2) + (((2 * t + hi5) ^ ((l31 >> 2) & 3)) * 16));
-    asm("" : "+v"(o.vq[t]));
-  }
+  o.kq = k_ring + unsigned((lane >> 4) * 512 + (lane & 15) * 16);
+  o.vq = v_ring + unsigned((lane >> 4) * 2048 + (lane & 15) * 16);
+  asm("" : "+v"(o.kq));
+  asm("" : "+v"(o.vq));
   return o;
 }
 
 struct WaveState {
-  bf16x8 qf[NRB][8];     // B operands of S^T, per row block: lane row (l & 31), dims (2ks + (l>>5)) * 8 ..
-  f32x16 o[NRB][4];      // O^T accumulators: lane row (l & 31), 4 dim blocks of 32
-  f32x16 s[NRB];         // S^T of the previous tile, softmaxed one step later
+  bf16x8 qf[NRB][4];     // B operands of S^T: row (l & 15) of block rb, dims 32 ks + 8 (l >> 4) ..
+  f32x4 o[NRB][8];       // O^T accumulators: row (l & 15), dims 16 db + 4 (l >> 4) + i
+  bf16x8 p[NRB];         // P of the previous tile (B operands of P V)
   bf16x8 kpre[NPRE];     // first K fragments of the current tile, read before the barrier
-  float lsum[NRB];       // partial row sums over this lane's half of the keys
+  float lsum[NRB];       // partial row sums over this lane's keys
   float m[NRB];          // online path: reference maximum (log2 units)
   int lo[NRB], hi[NRB];  // key bounds of the lane's rows
 };
 
-// Phase 1: S^T(tile in stage kst); its first NPRE K fragments are in st.kpre.
-__device__ __forceinline__ void qk_tile(const unsigned char* kst, const LaneOffsets& lo, const WaveState& st,
-                                        f32x16 (&s)[NRB]) {
+// K fragment f = 2 ks + kb of the tile in K stage kstage: keys 16 kb + (l & 15),
+// dims 32 ks + 8 (l >> 4) ..
+__device__ __forceinline__ bf16x8 k_frag(const LaneOffsets& lo, int kstage, int f) {
+  return *(lds_bf16x8*)(size_t)(lo.kq + unsigned(kstage * TILE_BYTES + (f >> 1) * 2048 + (f & 1) * 256));
+}
+
+// Phase 1: S^T(tile in K stage kstage); its first NPRE K fragments are in st.kpre.
+__device__ __forceinline__ void qk_tile(int kstage, const LaneOffsets& lo, const WaveState& st,
+                                        f32x4 (&s)[NRB][2]) {
 #pragma unroll
-  for (int rb = 0; rb < NRB; ++rb) s[rb] = f32x16{};
+  for (int rb = 0; rb < NRB; ++rb) s[rb][0] = s[rb][1] = f32x4{};
 #pragma unroll
-  for (int ks = 0; ks < 8; ++ks) {
-    const bf16x8 a = ks < NPRE ? st.kpre[ks < NPRE ? ks : 0] : *LDS_PTR(const bf16x8, kst + lo.kq[ks]);
+  for (int f = 0; f < 8; ++f) {
+    const int ks = f >> 1, kb = f & 1;
+    const bf16x8 a = f < NPRE ? st.kpre[f < NPRE ? f : 0] : k_frag(lo, kstage, f);
 #pragma unroll
-    for (int rb = 0; rb < NRB; ++rb) s[rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, st.qf[rb][ks], s[rb], 0, 0, 0);
+    for (int rb = 0; rb < NRB; ++rb)
+      s[rb][kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, st.qf[rb][ks], s[rb][kb], 0, 0, 0);
   }
 }
 
-// Phase 2 (MFMA part): O^T += V^T P^T for the previous tile. The A operand
-// of k-step t, dim block db is one 16-byte chunk of the V^T image: dims
-// db*32 + (l & 31), the 8 keys of logical chunk 2t + (l >> 5), in the order
-// of the lane's P fragment.
-__device__ __forceinline__ void pv_tile(int vstage, const LaneOffsets& lo, const bf16x8 (&p)[NRB][2], WaveState& st) {
-  typedef __attribute__((address_space(3))) const bf16x8 lds_bf16x8;
+// Phase 2 (MFMA part): O^T += V^T P^T for one tile. The A operand of dim
+// block db is one 16-byte chunk of the V^T image: dims 16 db + (l & 15), the
+// 8 keys of chunk (l >> 4), in the order of the lane's P fragment.
+__device__ __forceinline__ void pv_tile(int vstage, const LaneOffsets& lo, const bf16x8 (&p)[NRB], WaveState& st) {
 #pragma unroll
-  for (int t = 0; t < 2; ++t)
+  for (int db = 0; db < 8; ++db) {
+    const bf16x8 a = *(lds_bf16x8*)(size_t)(lo.vq + unsigned(vstage * TILE_BYTES + db * 256));
 #pragma unroll
-    for (int db = 0; db < 4; ++db) {
-      const bf16x8 a = *(lds_bf16x8*)(size_t)(lo.vq[t] + unsigned(vstage * TILE_BYTES + db * (32 * BN * 2)));
-#pragma unroll
-      for (int rb = 0; rb < NRB; ++rb)
-        st.o[rb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, p[rb][t], st.o[rb][db], 0, 0, 0);
-    }
+    for (int rb = 0; rb < NRB; ++rb)
+      st.o[rb][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, p[rb], st.o[rb][db], 0, 0, 0);
+  }
 }
 
-// Vector part: S -> P for one tile. Lane holds keys u*8 + hi5*4 + e
-// (u, e = 0..3) of its row for each row block.
+// Vector part: S -> P for one tile. Lane l holds, for row (l & 15) of each
+// row block, keys 16 kb + 4 g + i (g = l >> 4; kb = 0, 1; i = 0..3); P element
+// j of the B operand is key 16 (j / 4) + 4 g + (j % 4).
 template <bool MASKED, bool STATIC>
-__device__ __forceinline__ void softmax_tile(f32x16 (&s)[NRB], int kt, WaveState& st, bf16x8 (&pn)[NRB][2],
+__device__ __forceinline__ void softmax_tile(f32x4 (&s)[NRB][2], int kt, WaveState& st, bf16x8 (&p)[NRB],
                                              float (&alpha)[NRB], int lane) {
-  const int hi5 = lane >> 5;
+  const int g = lane >> 4;
 #pragma unroll
   for (int rb = 0; rb < NRB; ++rb) {
     if (MASKED) {
       // key allowed  <=>  (key - lo) < (hi - lo) as unsigned
-      const unsigned base = unsigned(kt * BN + hi5 * 4 - st.lo[rb]);
+      const unsigned base = unsigned(kt * BN + g * 4 - st.lo[rb]);
       const unsigned len = unsigned(st.hi[rb] - st.lo[rb]);
 #pragma unroll
-      for (int u = 0; u < 4; ++u)
+      for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const unsigned rel = base + unsigned(u * 8 + e);
-          s[rb][u * 4 + e] = rel < len ? s[rb][u * 4 + e] : kNegInf;
+        for (int i = 0; i < 4; ++i) {
+          const unsigned rel = base + unsigned(kb * 16 + i);
+          s[rb][kb][i] = rel < len ? s[rb][kb][i] : kNegInf;
         }
     }
     alpha[rb] = 1.0f;
     if (!STATIC) {
       float mx = kNegInf;
 #pragma unroll
-      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[rb][i]);
-      mx = fmaxf(mx, xor32(mx));
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) mx = fmaxf(mx, s[rb][kb][i]);
+      mx = max_groups(mx);
       // keep the reference maximum unless the tile exceeds it by > 2^8
       const float m_new = (mx > st.m[rb] + kRescaleSlack) ? mx : st.m[rb];
       alpha[rb] = (m_new == st.m[rb]) ? 1.0f : __builtin_amdgcn_exp2f(st.m[rb] - m_new);
       st.m[rb] = m_new;
       const float m_use = (m_new == kNegInf) ? 0.0f : m_new;
 #pragma unroll
-      for (int i = 0; i < 16; ++i) s[rb][i] -= m_use;
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) s[rb][kb][i] -= m_use;
     }
     const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
     float ls = 0.0f;
 #pragma unroll
-    for (int t = 0; t < 2; ++t)
+    for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int j = 0; j < 8; j += 2) {
-        const float e0 = __builtin_amdgcn_exp2f(s[rb][t * 8 + j]);
-        const float e1 = __builtin_amdgcn_exp2f(s[rb][t * 8 + j + 1]);
+      for (int i = 0; i < 4; i += 2) {
+        const float e0 = __builtin_amdgcn_exp2f(s[rb][kb][i]);
+        const float e1 = __builtin_amdgcn_exp2f(s[rb][kb][i + 1]);
         const bf16x2 pp = {(__bf16)e0, (__bf16)e1};
-        pn[rb][t][j] = pp[0];
-        pn[rb][t][j + 1] = pp[1];
+        p[rb][kb * 4 + i] = pp[0];
+        p[rb][kb * 4 + i + 1] = pp[1];
         ls = __builtin_amdgcn_fdot2_f32_bf16(pp, ones, ls, false);
       }
     st.lsum[rb] = st.lsum[rb] * alpha[rb] + ls;
@@ -262,7 +285,7 @@ __device__ __forceinline__ void softmax_tile(f32x16 (&s)[NRB], int kt, WaveState
 
 // Per-workgroup constants of the tile loop.
 struct LoopCtx {
-  i32x4 rsk, rsv;             // buffer resources of K and V
+  i32x4 rsk, rsv;             // buffer resources of the K-hat and V^T images
   unsigned k_base, v_base;    // LDS byte addresses of the K and V rings (plus this wave's 1 KiB block)
   const int* tiles;           // this item's key tile codes (for the boundary mask)
   const unsigned* soffs;      // this item's tile copy offsets; kNoTile in the padding after the list
@@ -278,27 +301,31 @@ __device__ __forceinline__ void issue_copies(const LoopCtx& c, const LaneOffsets
 }
 
 // Issue order of one full, statically bounded step (applied by the machine
-// scheduler to the step's instructions): each of the 16 MFMAs (S of this
-// tile, P V of the previous one) is followed by the next LDS read and two
-// vector instructions of the previous tile's softmax, so the LDS reads stay
-// ahead of the MFMAs and the softmax overlaps them.
+// scheduler to the step's instructions): each LDS read is followed by the
+// three MFMAs of the row blocks it feeds, with the previous tile's softmax
+// spread between them, so the reads stay ahead of the MFMAs and the vector
+// work overlaps them.
 __device__ __forceinline__ void order_static_step() {
-  constexpr int reads = 16 - NPRE;
-  if (NPRE < 2) __builtin_amdgcn_sched_group_barrier(0x100, 2 - NPRE, 0);   // DS read
+  constexpr int reads = 16 - NPRE;                    // K (8 - NPRE) and V (8)
+  __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // DS read
 #pragma unroll
   for (int k = 0; k < 16; ++k) {
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                       // MFMA
-    if (k + 2 - NPRE < reads && k < reads) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-    __builtin_amdgcn_sched_group_barrier(0x402, 2, 0);                       // VALU, transcendental
+#pragma unroll
+    for (int r = 0; r < NRB; ++r) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
+      __builtin_amdgcn_sched_group_barrier(0x402, 1, 0);   // VALU, transcendental
+    }
+    if (k + 2 < reads) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
   }
-  if (NPRE > 0) __builtin_amdgcn_sched_group_barrier(0x100, NPRE, 0);        // next tile's K prefetch
+  __builtin_amdgcn_sched_group_barrier(0x100, NPRE, 0);    // next tile's K prefetch
 }
 
-// Reads the first NPRE K fragments of the tile in stage kst into st.kpre;
-// their latency is spent before the next barrier, where the wave waits anyway.
-__device__ __forceinline__ void prefetch_k(const unsigned char* kst, const LaneOffsets& lo, WaveState& st) {
+// Reads the first NPRE K fragments of the tile in K stage kstage into
+// st.kpre; their latency is spent before the next barrier, where the wave
+// waits anyway.
+__device__ __forceinline__ void prefetch_k(int kstage, const LaneOffsets& lo, WaveState& st) {
 #pragma unroll
-  for (int ks = 0; ks < NPRE; ++ks) st.kpre[ks] = *LDS_PTR(const bf16x8, kst + lo.kq[ks]);
+  for (int f = 0; f < NPRE; ++f) st.kpre[f] = k_frag(lo, kstage, f);
 }
 
 // One step i. The stage of tile j is j % NSTAGE; callers that know i % NSTAGE
@@ -309,19 +336,19 @@ __device__ __forceinline__ void prefetch_k(const unsigned char* kst, const LaneO
 // sv. Then, on the matrix cores, S(i) and P(i-1) V(i-1); on the vector ALUs,
 // the softmax of S(i-1) into P(i-1), which overlaps S(i). MASKED_PREV: tile
 // i-1 is a boundary tile.
-template <bool MASKED_PREV, bool STATIC>
-__device__ __forceinline__ void tile_step(Smem& sm, const LoopCtx& c, const LaneOffsets& lo, WaveState& st, int i,
-                                          int si, unsigned sk, unsigned sv, int lane) {
+template <bool MASKED, bool STATIC>
+__device__ __forceinline__ void tile_step(const LoopCtx& c, const LaneOffsets& lo, WaveState& st, int i, int si,
+                                          unsigned sk, unsigned sv, int lane) {
   wait_vmcnt<WAIT_YOUNGER>();
   lds_barrier();
   issue_copies(c, lo, sk, (si + 1 + LOOKAHEAD) % NSTAGE, sv, (si + LOOKAHEAD) % NSTAGE);
-  f32x16 s_new[NRB];
-  qk_tile(sm.k[si], lo, st, s_new);
-  bf16x8 p[NRB][2];
+  f32x4 s[NRB][2];
+  qk_tile(si, lo, st, s);
+  pv_tile((si + NSTAGE - 1) % NSTAGE, lo, st.p, st);
+  bf16x8 p[NRB];
   float alpha[NRB];
-  softmax_tile<MASKED_PREV, STATIC>(st.s, MASKED_PREV ? (c.tiles[i - 1] >> 1) : 0, st, p, alpha, lane);
+  softmax_tile<MASKED, STATIC>(s, MASKED ? (c.tiles[i] >> 1) : 0, st, p, alpha, lane);
   if (!STATIC) {
-    // O holds the tiles before i-1, accumulated against the old reference maximum.
     bool any = false;
 #pragma unroll
     for (int rb = 0; rb < NRB; ++rb) any |= alpha[rb] != 1.0f;
@@ -329,23 +356,21 @@ __device__ __forceinline__ void tile_step(Smem& sm, const LoopCtx& c, const Lane
 #pragma unroll
       for (int rb = 0; rb < NRB; ++rb)
 #pragma unroll
-        for (int db = 0; db < 4; ++db) st.o[rb][db] *= alpha[rb];
+        for (int db = 0; db < 8; ++db) st.o[rb][db] *= alpha[rb];
     }
   }
-  pv_tile((si + NSTAGE - 1) % NSTAGE, lo, p, st);
 #pragma unroll
-  for (int rb = 0; rb < NRB; ++rb) st.s[rb] = s_new[rb];
-  // K(i+1) was published by this step's barrier
-  prefetch_k(sm.k[(si + 1) % NSTAGE], lo, st);
-  if (STATIC && !MASKED_PREV) order_static_step();
+  for (int rb = 0; rb < NRB; ++rb) st.p[rb] = p[rb];
+  prefetch_k((si + 1) % NSTAGE, lo, st);
+  if (STATIC && !MASKED) order_static_step();
 }
 
 // so[u] is the copy offset of tile i0 + LOOKAHEAD + u.
 template <bool STATIC, int U>
-__device__ __forceinline__ void unrolled_steps(Smem& sm, const LoopCtx& c, const LaneOffsets& lo, WaveState& st,
-                                               int i0, const unsigned (&so)[NSTAGE + 1], int lane) {
-  tile_step<false, STATIC>(sm, c, lo, st, i0 + U, U, so[U + 1], so[U], lane);
-  if constexpr (U + 1 < NSTAGE) unrolled_steps<STATIC, U + 1>(sm, c, lo, st, i0, so, lane);
+__device__ __forceinline__ void unrolled_steps(const LoopCtx& c, const LaneOffsets& lo, WaveState& st, int i0,
+                                               const unsigned (&so)[NSTAGE + 1], int lane) {
+  tile_step<false, STATIC>(c, lo, st, i0 + U, U, so[U + 1], so[U], lane);
+  if constexpr (U + 1 < NSTAGE) unrolled_steps<STATIC, U + 1>(c, lo, st, i0, so, lane);
 }
 
 // Full tiles first, then boundary tiles; the softmax of tile i runs in step
@@ -355,36 +380,24 @@ __device__ __forceinline__ void unrolled_steps(Smem& sm, const LoopCtx& c, const
 // offsets are read up to LOOKAHEAD + 1 entries past the list, which the
 // list's padding covers.
 template <bool STATIC>
-__device__ __forceinline__ void run_tiles(Smem& sm, const LoopCtx& c, const LaneOffsets& lo, int n_full,
-                                          WaveState& st, int lane) {
+__device__ __forceinline__ void run_tiles(const LoopCtx& c, const LaneOffsets& lo, int n_full, WaveState& st,
+                                          int lane) {
   const int n = c.n_tiles;
-  const int n_plain = n_full + 1 < n ? n_full + 1 : n;      // steps i <= n_full: tile i-1 is full
   int i = 0;
-  for (; i + NSTAGE <= n_plain; i += NSTAGE) {
+  for (; i + NSTAGE <= n_full; i += NSTAGE) {
     unsigned so[NSTAGE + 1];
 #pragma unroll
     for (int u = 0; u <= NSTAGE; ++u) so[u] = c.soffs[i + LOOKAHEAD + u];
-    unrolled_steps<STATIC, 0>(sm, c, lo, st, i, so, lane);
+    unrolled_steps<STATIC, 0>(c, lo, st, i, so, lane);
   }
-  for (; i < n_plain; ++i)
-    tile_step<false, STATIC>(sm, c, lo, st, i, i % NSTAGE, c.soffs[i + 1 + LOOKAHEAD], c.soffs[i + LOOKAHEAD], lane);
+  for (; i < n_full; ++i)
+    tile_step<false, STATIC>(c, lo, st, i, i % NSTAGE, c.soffs[i + 1 + LOOKAHEAD], c.soffs[i + LOOKAHEAD], lane);
   for (; i < n; ++i)
-    tile_step<true, STATIC>(sm, c, lo, st, i, i % NSTAGE, c.soffs[i + 1 + LOOKAHEAD], c.soffs[i + LOOKAHEAD], lane);
-  // last tile: its V stage landed before the last barrier
-  bf16x8 p[NRB][2];
-  float alpha[NRB];
-  if (n - 1 >= n_full) softmax_tile<true, STATIC>(st.s, c.tiles[n - 1] >> 1, st, p, alpha, lane);
-  else softmax_tile<false, STATIC>(st.s, 0, st, p, alpha, lane);
-  if (!STATIC) {
-#pragma unroll
-    for (int rb = 0; rb < NRB; ++rb)
-#pragma unroll
-      for (int db = 0; db < 4; ++db) st.o[rb][db] *= alpha[rb];
-  }
-  pv_tile((n + NSTAGE - 1) % NSTAGE, lo, p, st);
+    tile_step<true, STATIC>(c, lo, st, i, i % NSTAGE, c.soffs[i + 1 + LOOKAHEAD], c.soffs[i + LOOKAHEAD], lane);
+  pv_tile((n + NSTAGE - 1) % NSTAGE, lo, st.p, st);
 }
 
-__global__ void __launch_bounds__(NTHR) __attribute__((amdgpu_waves_per_eu(NRB == 1 ? 2 : 1, NRB == 1 ? 2 : 1)))
+__global__ void __launch_bounds__(NTHR) __attribute__((amdgpu_waves_per_eu(2, 2)))
 fwd_bf16_d128_kernel(FwdParams prm, const int4* __restrict__ items, const int* __restrict__ tiles,
                      const unsigned* __restrict__ soffs, const int2* __restrict__ rows) {
   __shared__ __attribute__((aligned(1024))) Smem sm;
@@ -394,34 +407,35 @@ fwd_bf16_d128_kernel(FwdParams prm, const int4* __restrict__ items, const int* _
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
+  const int g = lane >> 4;
   const int kvh = item.y >> 16, h0 = item.y & 0xffff;
-  const int rb_per_head = prm.tile_q >> 5;
   const int tb = item.z, n_tiles = item.w - item.z;
 
+  // Row r of the item (0..383) is token t0 + r % tile_q of head h0 + r / tile_q.
   WaveState st;
   int tok[NRB], head[NRB];
   bool valid[NRB];
 #pragma unroll
   for (int rb = 0; rb < NRB; ++rb) {
-    const int blk = wave * NRB + rb;
-    head[rb] = h0 + blk / rb_per_head;
-    tok[rb] = item.x + (blk % rb_per_head) * 32 + (lane & 31);
+    const int r = (wave * NRB + rb) * 16 + (lane & 15);
+    head[rb] = h0 + r / prm.tile_q;
+    tok[rb] = item.x + r % prm.tile_q;
     valid[rb] = tok[rb] < prm.tq;
   }
   // ---- query loads first (older than every K/V copy)
-  bf16x8 qr[NRB][8];
+  bf16x8 qr[NRB][4];
 #pragma unroll
   for (int rb = 0; rb < NRB; ++rb) {
     const __bf16* qrow = reinterpret_cast<const __bf16*>(prm.q) + (size_t(tok[rb]) * prm.hq + head[rb]) * D;
 #pragma unroll
-    for (int ks = 0; ks < 8; ++ks)
-      qr[rb][ks] = valid[rb] ? *reinterpret_cast<const bf16x8*>(qrow + (2 * ks + (lane >> 5)) * 8) : bf16x8{};
+    for (int ks = 0; ks < 4; ++ks)
+      qr[rb][ks] = valid[rb] ? *reinterpret_cast<const bf16x8*>(qrow + ks * 32 + g * 8) : bf16x8{};
   }
 
   // ---- K/V copies of iterations -LOOKAHEAD-1 .. -1 (V(-1) is a zero tile)
   const unsigned n_kt = unsigned(prm.tk + BN - 1) / BN;
   const unsigned img_bytes = n_kt * unsigned(prm.hk) * unsigned(TILE_BYTES);
-  const LaneOffsets lo = lane_offsets(tid, kvh, lds_addr(&sm.v[0][0]));
+  const LaneOffsets lo = lane_offsets(tid, kvh, lds_addr(&sm.k[0][0]), lds_addr(&sm.v[0][0]));
   LoopCtx ctx;
   ctx.rsk = make_rsrc(prm.ws, img_bytes);
   ctx.rsv = make_rsrc(static_cast<const unsigned char*>(prm.ws) + img_bytes, img_bytes);
@@ -433,13 +447,12 @@ fwd_bf16_d128_kernel(FwdParams prm, const int4* __restrict__ items, const int* _
 #pragma unroll
   for (int j = -LOOKAHEAD - 1; j < 0; ++j)
     issue_copies(ctx, lo, ctx.soffs[j + 1 + LOOKAHEAD], (j + 1 + LOOKAHEAD + NSTAGE) % NSTAGE,
-                 j + LOOKAHEAD >= 0 ? ctx.soffs[j + LOOKAHEAD] : kNoTile,
-                 (j + LOOKAHEAD + NSTAGE) % NSTAGE);
+                 j + LOOKAHEAD >= 0 ? ctx.soffs[j + LOOKAHEAD] : kNoTile, (j + LOOKAHEAD + NSTAGE) % NSTAGE);
 
   if (tid < D) sm.gqk[tid] = prm.q_gain[tid] * prm.k_gain[tid] * (prm.scale * kLog2e);
-  wait_vmcnt<2 * (LOOKAHEAD + 1) * UNITS - 1>();      // K(0), the oldest copy, landed
+  wait_vmcnt<2 * LOOKAHEAD>();                        // K(0) and V(-1), the oldest copies, landed
   __syncthreads();                                     // gqk and K(0) visible
-  prefetch_k(sm.k[0], lo, st);
+  prefetch_k(0, lo, st);
 
   // ---- query prologue: RMS-normalise, fold gains/temperature, to bf16
   float bound_max = 0.0f;
@@ -447,53 +460,58 @@ fwd_bf16_d128_kernel(FwdParams prm, const int4* __restrict__ items, const int* _
   for (int rb = 0; rb < NRB; ++rb) {
     float ss = 0.0f;
 #pragma unroll
-    for (int ks = 0; ks < 8; ++ks) ss = sumsq8(qr[rb][ks], ss);
-    ss += xor32(ss);
+    for (int ks = 0; ks < 4; ++ks) ss = sumsq8(qr[rb][ks], ss);
+    ss = sum_groups(ss);
     const float rq = valid[rb] ? __builtin_amdgcn_rsqf(ss * (1.0f / D) + prm.eps) : 0.0f;
     float nq = 0.0f;
 #pragma unroll
-    for (int ks = 0; ks < 8; ++ks) {
-      const int d0 = (2 * ks + (lane >> 5)) * 8;
+    for (int ks = 0; ks < 4; ++ks) {
+      const int d0 = ks * 32 + g * 8;
       const f32x4 g0 = *LDS_PTR(const f32x4, &sm.gqk[d0]);
       const f32x4 g1 = *LDS_PTR(const f32x4, &sm.gqk[d0 + 4]);
 #pragma unroll
       for (int j = 0; j < 8; ++j) st.qf[rb][ks][j] = (__bf16)(float(qr[rb][ks][j]) * rq * (j < 4 ? g0[j] : g1[j - 4]));
       nq = sumsq8(st.qf[rb][ks], nq);
     }
-    nq += xor32(nq);
+    nq = sum_groups(nq);
     bound_max = fmaxf(bound_max, __builtin_sqrtf(nq) * __builtin_sqrtf(float(D)) * 1.02f);
     const int2 b = valid[rb] ? rows[tok[rb]] : int2{0, 0};
     st.lo[rb] = b.x;
     st.hi[rb] = b.y;
 #pragma unroll
-    for (int db = 0; db < 4; ++db) st.o[rb][db] = f32x16{};
-#pragma unroll
-    for (int e = 0; e < 16; ++e) st.s[rb][e] = kNegInf;        // tile -1: P = 0
+    for (int db = 0; db < 8; ++db) st.o[rb][db] = f32x4{};
+    st.p[rb] = bf16x8{};                                      // tile -1: P = 0
     st.lsum[rb] = 0.0f;
     st.m[rb] = kNegInf;
   }
   const bool stat = __builtin_amdgcn_ballot_w64(!(bound_max <= kStaticBound)) == 0;
 
-  if (stat) run_tiles<true>(sm, ctx, lo, n_full, st, lane);
-  else run_tiles<false>(sm, ctx, lo, n_full, st, lane);
+  if (stat) run_tiles<true>(ctx, lo, n_full, st, lane);
+  else run_tiles<false>(ctx, lo, n_full, st, lane);
 
-  // ---- epilogue
+  // ---- epilogue: lane l holds dims 16 db + 4 g + i of row (l & 15) per block
+  // (row coordinates recomputed rather than kept live through the loop)
 #pragma unroll
   for (int rb = 0; rb < NRB; ++rb) {
-    const float lsum = st.lsum[rb] + xor32(st.lsum[rb]);
+    const int r = (wave * NRB + rb) * 16 + (lane & 15);
+    head[rb] = h0 + r / prm.tile_q;
+    tok[rb] = item.x + r % prm.tile_q;
+    valid[rb] = tok[rb] < prm.tq;
+  }
+#pragma unroll
+  for (int rb = 0; rb < NRB; ++rb) {
+    const float lsum = sum_groups(st.lsum[rb]);
     if (valid[rb]) {
       const float inv = 1.0f / lsum;
       __bf16* orow = reinterpret_cast<__bf16*>(prm.out) + (size_t(tok[rb]) * prm.hq + head[rb]) * D;
 #pragma unroll
-      for (int db = 0; db < 4; ++db)
+      for (int db = 0; db < 8; ++db) {
+        bf16x4 w;
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          bf16x4 w;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) w[e] = (__bf16)(st.o[rb][db][u * 4 + e] * inv);
-          *reinterpret_cast<bf16x4*>(orow + db * 32 + u * 8 + (lane >> 5) * 4) = w;
-        }
-      if (lane < 32) {
+        for (int i = 0; i < 4; ++i) w[i] = (__bf16)(st.o[rb][db][i] * inv);
+        *reinterpret_cast<bf16x4*>(orow + db * 16 + g * 4) = w;
+      }
+      if (g == 0) {
         const float l2 = __builtin_amdgcn_logf(lsum);   // log2
         const float lse = stat ? l2 * kLn2 : (st.m[rb] + l2) * kLn2;
         prm.lse[size_t(head[rb]) * prm.tq + tok[rb]] = lse;
@@ -536,18 +554,18 @@ __global__ void __launch_bounds__(PP_THREADS) kv_prepare_kernel(const __bf16* __
     bf16x8 xn;
 #pragma unroll
     for (int j = 0; j < 8; ++j) xn[j] = (__bf16)(float(x[j]) * rk);
-    *reinterpret_cast<bf16x8*>(kimg + img + key * ROW_BYTES + ((c ^ (key & 15)) * 16)) = xn;
+    *reinterpret_cast<bf16x8*>(kimg + img + c * 512 + key * 16) = xn;
     *LDS_PTR(bf16x8, vs + key * ROW_BYTES + c * 16) = y;
   }
   __syncthreads();
 #pragma unroll
   for (int r = 0; r < 2; ++r) {
-    const int u = tid + r * PP_THREADS;        // V^T unit: dim row u / 4, physical chunk u % 4
-    const int d = u >> 2, c = (u & 3) ^ ((d >> 2) & 3);
+    const int u = tid + r * PP_THREADS;        // V^T unit: chunk u / 128, dim row u % 128
+    const int c = u >> 7, d = u & 127;
     bf16x8 w;
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      const int key = 16 * (c >> 1) + 8 * (j >> 2) + 4 * (c & 1) + (j & 3);
+      const int key = 16 * (j >> 2) + 4 * c + (j & 3);
       w[j] = *LDS_PTR(const __bf16, vs + key * ROW_BYTES + d * 2);
     }
     *reinterpret_cast<bf16x8*>(vimg + img + u * 16) = w;

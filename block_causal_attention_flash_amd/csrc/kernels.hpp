@@ -6,6 +6,9 @@
 
 namespace magi {
 
+// (token, head) rows of one bf16 work item: tile_q * heads_per_item.
+constexpr int kBf16RowsPerItem = 384;
+
 struct FwdParams {
   const void* q;
   const void* k;

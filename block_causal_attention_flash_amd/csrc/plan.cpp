@@ -17,6 +17,8 @@
 // are placed on the same XCD and share its L2.
 #include "plan.hpp"
 
+#include "kernels.hpp"
+
 #include <algorithm>
 #include <cstring>
 #include <numeric>
@@ -80,13 +82,15 @@ Tiling choose_tiling(int dtype, int head_dim, int group) {
   (void)head_dim;
   Tiling t{};
   if (dtype == MAGI_DTYPE_BF16) {
-    // 256 (token, head) rows per workgroup: 8 waves x 32 rows. As many query
-    // heads of the GQA group as divide it (power of two, <= 8) share one
-    // workgroup, so one K/V tile in LDS serves all of them.
+    // kBf16RowsPerItem (token, head) rows per workgroup: 8 waves x 48 rows.
+    // The largest divisor of the GQA group size that also divides the row
+    // count gives the heads per workgroup (all of them when possible), so
+    // one K/V tile in LDS serves all of them.
     int hpw = 1;
-    while (hpw < 8 && group % (hpw * 2) == 0) hpw *= 2;
+    for (int h = 1; h <= group; ++h)
+      if (group % h == 0 && kBf16RowsPerItem % h == 0) hpw = h;
     t.heads_per_item = hpw;
-    t.tile_q = 256 / hpw;
+    t.tile_q = kBf16RowsPerItem / hpw;
     t.tile_kv = 32;
   } else {
     t.heads_per_item = 1;

@@ -101,12 +101,13 @@ def test_stats_match_mask_areas(built_lib):
 
 
 def test_stats_480p_tile_counts(built_lib):
-    """16 chunks of 9360 tokens with 128-token query tiles and 32-key tiles:
-    only tiles straddling a chunk end need the mask."""
+    """16 chunks of 9360 tokens, 48 query heads on 8 KV heads: one work item
+    covers 64 tokens of all 6 query heads of a KV head (384 rows), with
+    32-key tiles; only tiles straddling a chunk end need the mask."""
     from block_causal_attention_flash_amd import magi_attn_plan_stats
     c = get_config("video480x832")
     st = magi_attn_plan_stats(c.layout.q_offsets, None, None, 48, 8, 128, "bf16")
-    assert st["tile_q"] == 128 and st["tile_kv"] == 32 and st["heads_per_item"] == 2
+    assert st["tile_q"] == 64 and st["tile_kv"] == 32 and st["heads_per_item"] == 6
     assert st["boundary_pairs"] < 0.01 * st["full_pairs"]
     assert st["executed_pairs"] / st["unmasked_pairs"] < 1.01
 
