@@ -217,10 +217,15 @@ __device__ __forceinline__ void qk_tile(int kstage, const LaneOffsets& lo, const
 // Phase 2 (MFMA part): O^T += V^T P^T for one tile. The A operand of dim
 // block db is one 16-byte chunk of the V^T image: dims 16 db + (l & 15), the
 // 8 keys of chunk (l >> 4), in the order of the lane's P fragment.
-__device__ __forceinline__ void pv_tile(int vstage, const LaneOffsets& lo, const bf16x8 (&p)[NRB], WaveState& st) {
+__device__ __forceinline__ bf16x8 v_frag(const LaneOffsets& lo, int vstage, int db) {
+  return *(lds_bf16x8*)(size_t)(lo.vq + unsigned(vstage * TILE_BYTES + db * 256));
+}
+
+__device__ __forceinline__ void pv_tile(int vstage, const LaneOffsets& lo, const bf16x8 (&p)[NRB], WaveState& st,
+                                        const bf16x8* vpre = nullptr) {
 #pragma unroll
   for (int db = 0; db < 8; ++db) {
-    const bf16x8 a = *(lds_bf16x8*)(size_t)(lo.vq + unsigned(vstage * TILE_BYTES + db * 256));
+    const bf16x8 a = (vpre && db < 2) ? vpre[db < 2 ? db : 0] : v_frag(lo, vstage, db);
 #pragma unroll
     for (int rb = 0; rb < NRB; ++rb)
       st.o[rb][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, p[rb], st.o[rb][db], 0, 0, 0);
@@ -342,9 +347,23 @@ __device__ __forceinline__ void tile_step(const LoopCtx& c, const LaneOffsets& l
   wait_vmcnt<WAIT_YOUNGER>();
   lds_barrier();
   issue_copies(c, lo, sk, (si + 1 + LOOKAHEAD) % NSTAGE, sv, (si + LOOKAHEAD) % NSTAGE);
+  const int vst = (si + NSTAGE - 1) % NSTAGE;
   f32x4 s[NRB][2];
   qk_tile(si, lo, st, s);
-  pv_tile((si + NSTAGE - 1) % NSTAGE, lo, st.p, st);
+  bf16x8 vpre[2];
+  vpre[0] = v_frag(lo, vst, 0);
+  vpre[1] = v_frag(lo, vst, 1);
+  if (STATIC && !MASKED) {
+    // region 1: K reads two ahead of the S MFMAs, then the first V reads
+    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+#pragma unroll
+    for (int f = 0; f < 8; ++f) {
+      __builtin_amdgcn_sched_group_barrier(0x008, NRB, 0);
+      if (f < 8 - NPRE) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  pv_tile(vst, lo, st.p, st, vpre);
   bf16x8 p[NRB];
   float alpha[NRB];
   softmax_tile<MASKED, STATIC>(s, MASKED ? (c.tiles[i] >> 1) : 0, st, p, alpha, lane);
@@ -362,7 +381,16 @@ __device__ __forceinline__ void tile_step(const LoopCtx& c, const LaneOffsets& l
 #pragma unroll
   for (int rb = 0; rb < NRB; ++rb) st.p[rb] = p[rb];
   prefetch_k((si + 1) % NSTAGE, lo, st);
-  if (STATIC && !MASKED) order_static_step();
+  if (STATIC && !MASKED) {
+    // region 2: P V MFMAs with the next V read and the softmax of S(i) between them
+#pragma unroll
+    for (int db = 0; db < 8; ++db) {
+      __builtin_amdgcn_sched_group_barrier(0x008, NRB, 0);
+      if (db < 6) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x402, 6, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x100, NPRE, 0);
+  }
 }
 
 // so[u] is the copy offset of tile i0 + LOOKAHEAD + u.
