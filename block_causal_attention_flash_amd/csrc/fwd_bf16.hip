@@ -61,16 +61,19 @@ constexpr int NRB = 3;                                // 16-row MFMA blocks per 
 constexpr int ROWS = NWAVE * NRB * 16;                // 384 rows per workgroup
 constexpr int NTHR = NWAVE * 64;
 constexpr int NSTAGE = 8;                             // LDS ring depth (K and V each)
-constexpr int LOOKAHEAD = NSTAGE - 2;                 // copies issued this many tiles ahead
 constexpr int ROW_BYTES = D * 2;                      // 256
 constexpr int TILE_BYTES = BN * ROW_BYTES;            // 8 KiB
 constexpr int NPRE = 2;                               // K fragments of the next tile read before the barrier
 static_assert(TILE_BYTES == NTHR * 16, "one 16-byte copy per thread per tensor and tile");
 static_assert(ROWS == kBf16RowsPerItem, "rows per work item");
-// Copies in flight that may be younger than the ones a tile needs: the
-// LOOKAHEAD-1 later iterations (K and V each) plus the V copy issued right
-// after the needed K copy.
-constexpr int WAIT_YOUNGER = (LOOKAHEAD - 1) * 2 + 1;
+// The workgroup barrier runs on even steps only. After the barrier of even
+// step i, copies start for K(i+6), V(i+5), K(i+7), V(i+6), in that order, into
+// stages that every wave left before this barrier. Before the barrier of step
+// i, K(i), K(i+1), K(i+2), V(i-1), V(i) must have landed (steps i and i+1 read
+// them; step i+1 reads K(i+2) ahead): everything issued at step i-6 or
+// earlier, plus K(i+2), the first copy issued at step i-4. Up to 7 copies
+// younger than it may still fly.
+constexpr int WAIT_YOUNGER = 7;
 constexpr unsigned kNoTile = 0x80000000u;             // scalar offset past any tile image buffer (< 2 GiB): zeros
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
@@ -335,18 +338,21 @@ __device__ __forceinline__ void prefetch_k(int kstage, const LaneOffsets& lo, Wa
 
 // One step i. The stage of tile j is j % NSTAGE; callers that know i % NSTAGE
 // at compile time pass it as si so every LDS offset folds into an immediate.
-// Top: wait for K(i+1) (issued LOOKAHEAD iterations ago; the later copies may
-// still fly), barrier (K(i) and V(i-1) landed for every wave, stages of tiles
-// i-1 / i-2 free), start K(i+1+LA) and V(i+LA), whose copy offsets are sk and
-// sv. Then, on the matrix cores, S(i) and P(i-1) V(i-1); on the vector ALUs,
-// the softmax of S(i-1) into P(i-1), which overlaps S(i). MASKED_PREV: tile
-// i-1 is a boundary tile.
+// On even steps (sync): wait for the copies listed at WAIT_YOUNGER, barrier,
+// start the next four copies. Then S(i) on the matrix cores (its first K
+// fragments were read at the end of the previous step), P(i-1) V(i-1) with
+// the softmax of S(i) between its MFMAs, and the first K fragments of tile
+// i+1 (published at this or the previous barrier).
+// so4: copy offsets of K(i+6), K(i+7), V(i+5), V(i+6); used on even steps.
 template <bool MASKED, bool STATIC>
 __device__ __forceinline__ void tile_step(const LoopCtx& c, const LaneOffsets& lo, WaveState& st, int i, int si,
-                                          unsigned sk, unsigned sv, int lane) {
-  wait_vmcnt<WAIT_YOUNGER>();
-  lds_barrier();
-  issue_copies(c, lo, sk, (si + 1 + LOOKAHEAD) % NSTAGE, sv, (si + LOOKAHEAD) % NSTAGE);
+                                          bool sync, const unsigned (&so4)[4], int lane) {
+  if (sync) {
+    wait_vmcnt<WAIT_YOUNGER>();
+    lds_barrier();
+    issue_copies(c, lo, so4[0], (si + 6) % NSTAGE, so4[2], (si + 5) % NSTAGE);
+    issue_copies(c, lo, so4[1], (si + 7) % NSTAGE, so4[3], (si + 6) % NSTAGE);
+  }
   const int vst = (si + NSTAGE - 1) % NSTAGE;
   f32x4 s[NRB][2];
   qk_tile(si, lo, st, s);
@@ -393,20 +399,29 @@ __device__ __forceinline__ void tile_step(const LoopCtx& c, const LaneOffsets& l
   }
 }
 
-// so[u] is the copy offset of tile i0 + LOOKAHEAD + u.
+// Copy offsets used by even step i: K(i+6), K(i+7), V(i+5), V(i+6).
+__device__ __forceinline__ void step_offsets(const unsigned* soffs, int i, unsigned (&so4)[4]) {
+  so4[0] = soffs[i + 6];
+  so4[1] = soffs[i + 7];
+  so4[2] = soffs[i + 5];
+  so4[3] = soffs[i + 6];
+}
+
+// so[u] is the copy offset of tile i0 + 5 + u.
 template <bool STATIC, int U>
 __device__ __forceinline__ void unrolled_steps(const LoopCtx& c, const LaneOffsets& lo, WaveState& st, int i0,
                                                const unsigned (&so)[NSTAGE + 1], int lane) {
-  tile_step<false, STATIC>(c, lo, st, i0 + U, U, so[U + 1], so[U], lane);
+  const unsigned so4[4] = {so[U + 1], so[U + 2], so[U], so[U + 1]};
+  tile_step<false, STATIC>(c, lo, st, i0 + U, U, (U & 1) == 0, so4, lane);
   if constexpr (U + 1 < NSTAGE) unrolled_steps<STATIC, U + 1>(c, lo, st, i0, so, lane);
 }
 
-// Full tiles first, then boundary tiles; the softmax of tile i runs in step
-// i + 1, and the last tile's softmax and P V after the loop. Steps whose
-// softmax tile is full run NSTAGE at a time with compile-time stages and
-// their copy offsets loaded once per group; the rest one by one. Copy
-// offsets are read up to LOOKAHEAD + 1 entries past the list, which the
-// list's padding covers.
+// Full tiles first, then boundary tiles. Full tiles run NSTAGE at a time
+// (NSTAGE is even, so groups start on even steps) with compile-time stages and
+// their copy offsets loaded once per group; the rest one by one. Copy offsets
+// are read up to 7 entries past the list, which the list's padding covers.
+// The last tile's P V runs after the loop, behind one more barrier when the
+// last step had none (V(n-1) was then not yet published).
 template <bool STATIC>
 __device__ __forceinline__ void run_tiles(const LoopCtx& c, const LaneOffsets& lo, int n_full, WaveState& st,
                                           int lane) {
@@ -415,13 +430,23 @@ __device__ __forceinline__ void run_tiles(const LoopCtx& c, const LaneOffsets& l
   for (; i + NSTAGE <= n_full; i += NSTAGE) {
     unsigned so[NSTAGE + 1];
 #pragma unroll
-    for (int u = 0; u <= NSTAGE; ++u) so[u] = c.soffs[i + LOOKAHEAD + u];
+    for (int u = 0; u <= NSTAGE; ++u) so[u] = c.soffs[i + 5 + u];
     unrolled_steps<STATIC, 0>(c, lo, st, i, so, lane);
   }
-  for (; i < n_full; ++i)
-    tile_step<false, STATIC>(c, lo, st, i, i % NSTAGE, c.soffs[i + 1 + LOOKAHEAD], c.soffs[i + LOOKAHEAD], lane);
-  for (; i < n; ++i)
-    tile_step<true, STATIC>(c, lo, st, i, i % NSTAGE, c.soffs[i + 1 + LOOKAHEAD], c.soffs[i + LOOKAHEAD], lane);
+  for (; i < n_full; ++i) {
+    unsigned so4[4];
+    step_offsets(c.soffs, i, so4);
+    tile_step<false, STATIC>(c, lo, st, i, i % NSTAGE, (i & 1) == 0, so4, lane);
+  }
+  for (; i < n; ++i) {
+    unsigned so4[4];
+    step_offsets(c.soffs, i, so4);
+    tile_step<true, STATIC>(c, lo, st, i, i % NSTAGE, (i & 1) == 0, so4, lane);
+  }
+  if ((n & 1) == 0) {
+    wait_vmcnt<0>();
+    lds_barrier();
+  }
   pv_tile((n + NSTAGE - 1) % NSTAGE, lo, st.p, st);
 }
 
@@ -460,7 +485,7 @@ fwd_bf16_d128_kernel(FwdParams prm, const int4* __restrict__ items, const int* _
       qr[rb][ks] = valid[rb] ? *reinterpret_cast<const bf16x8*>(qrow + ks * 32 + g * 8) : bf16x8{};
   }
 
-  // ---- K/V copies of iterations -LOOKAHEAD-1 .. -1 (V(-1) is a zero tile)
+  // ---- K/V copies ahead of the first step
   const unsigned n_kt = unsigned(prm.tk + BN - 1) / BN;
   const unsigned img_bytes = n_kt * unsigned(prm.hk) * unsigned(TILE_BYTES);
   const LaneOffsets lo = lane_offsets(tid, kvh, lds_addr(&sm.k[0][0]), lds_addr(&sm.v[0][0]));
@@ -472,13 +497,16 @@ fwd_bf16_d128_kernel(FwdParams prm, const int4* __restrict__ items, const int* _
   ctx.tiles = tiles + tb;
   ctx.soffs = soffs + tb;
   ctx.n_tiles = n_tiles;
+  // the copies of even steps -6, -4, -2 (V(-1) is a zero tile)
 #pragma unroll
-  for (int j = -LOOKAHEAD - 1; j < 0; ++j)
-    issue_copies(ctx, lo, ctx.soffs[j + 1 + LOOKAHEAD], (j + 1 + LOOKAHEAD + NSTAGE) % NSTAGE,
-                 j + LOOKAHEAD >= 0 ? ctx.soffs[j + LOOKAHEAD] : kNoTile, (j + LOOKAHEAD + NSTAGE) % NSTAGE);
+  for (int j = -6; j < 0; j += 2) {
+    issue_copies(ctx, lo, ctx.soffs[j + 6], (j + 6 + NSTAGE) % NSTAGE, j + 5 >= 0 ? ctx.soffs[j + 5] : kNoTile,
+                 (j + 5 + NSTAGE) % NSTAGE);
+    issue_copies(ctx, lo, ctx.soffs[j + 7], (j + 7 + NSTAGE) % NSTAGE, ctx.soffs[j + 6], (j + 6 + NSTAGE) % NSTAGE);
+  }
 
   if (tid < D) sm.gqk[tid] = prm.q_gain[tid] * prm.k_gain[tid] * (prm.scale * kLog2e);
-  wait_vmcnt<2 * LOOKAHEAD>();                        // K(0) and V(-1), the oldest copies, landed
+  wait_vmcnt<11>();                                   // K(0), the oldest of the 12 copies, landed
   __syncthreads();                                     // gqk and K(0) visible
   prefetch_k(0, lo, st);
 
