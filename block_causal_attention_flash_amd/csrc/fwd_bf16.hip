@@ -308,26 +308,6 @@ __device__ __forceinline__ void issue_copies(const LoopCtx& c, const LaneOffsets
   dma16(c.rsv, lo.dma, sv, c.v_base + jvs * TILE_BYTES);
 }
 
-// Issue order of one full, statically bounded step (applied by the machine
-// scheduler to the step's instructions): each LDS read is followed by the
-// three MFMAs of the row blocks it feeds, with the previous tile's softmax
-// spread between them, so the reads stay ahead of the MFMAs and the vector
-// work overlaps them.
-__device__ __forceinline__ void order_static_step() {
-  constexpr int reads = 16 - NPRE;                    // K (8 - NPRE) and V (8)
-  __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // DS read
-#pragma unroll
-  for (int k = 0; k < 16; ++k) {
-#pragma unroll
-    for (int r = 0; r < NRB; ++r) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
-      __builtin_amdgcn_sched_group_barrier(0x402, 1, 0);   // VALU, transcendental
-    }
-    if (k + 2 < reads) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-  }
-  __builtin_amdgcn_sched_group_barrier(0x100, NPRE, 0);    // next tile's K prefetch
-}
-
 // Reads the first NPRE K fragments of the tile in K stage kstage into
 // st.kpre; their latency is spent before the next barrier, where the wave
 // waits anyway.
@@ -393,7 +373,7 @@ __device__ __forceinline__ void tile_step(const LoopCtx& c, const LaneOffsets& l
     for (int db = 0; db < 8; ++db) {
       __builtin_amdgcn_sched_group_barrier(0x008, NRB, 0);
       if (db < 6) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x402, 6, 0);
+      __builtin_amdgcn_sched_group_barrier(0x402, 2 * NRB, 0);
     }
     __builtin_amdgcn_sched_group_barrier(0x100, NPRE, 0);
   }
