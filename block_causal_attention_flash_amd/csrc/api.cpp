@@ -18,6 +18,7 @@ struct magi_attn_plan {
   const int4* d_items = nullptr;
   const int* d_tiles = nullptr;
   const unsigned* d_soffs = nullptr;
+  const int4* d_merges = nullptr;
   const int2* d_rows = nullptr;
 };
 
@@ -116,9 +117,11 @@ magi_status_t magi_attn_plan_create(const magi_attn_layout_t* layout, magi_attn_
   const size_t b_tiles = H.tile_codes.size() * sizeof(int32_t);
   const size_t b_soffs = H.tile_soff.size() * sizeof(uint32_t);
   const size_t b_rows = H.rows.size() * sizeof(magi::RowBounds);
+  const size_t b_merges = H.merges.size() * sizeof(magi::MergeItem);
   const size_t o_tiles = round_up(b_items, 256), o_soffs = o_tiles + round_up(b_tiles, 256);
   const size_t o_rows = o_soffs + round_up(b_soffs, 256);
-  const size_t total = std::max<size_t>(o_rows + b_rows, 256);
+  const size_t o_merges = o_rows + round_up(b_rows, 256);
+  const size_t total = std::max<size_t>(o_merges + b_merges, 256);
   hipError_t e = hipGetDevice(&p->device);
   if (e != hipSuccess) { delete p; return hip_fail(e, "hipGetDevice"); }
   e = hipMalloc(&p->dmem, total);
@@ -131,6 +134,7 @@ magi_status_t magi_attn_plan_create(const magi_attn_layout_t* layout, magi_attn_
   if (e == hipSuccess && b_tiles) e = hipMemcpy(base + o_tiles, H.tile_codes.data(), b_tiles, hipMemcpyHostToDevice);
   if (e == hipSuccess && b_soffs) e = hipMemcpy(base + o_soffs, H.tile_soff.data(), b_soffs, hipMemcpyHostToDevice);
   if (e == hipSuccess && b_rows) e = hipMemcpy(base + o_rows, H.rows.data(), b_rows, hipMemcpyHostToDevice);
+  if (e == hipSuccess && b_merges) e = hipMemcpy(base + o_merges, H.merges.data(), b_merges, hipMemcpyHostToDevice);
   if (e != hipSuccess) {
     (void)hipFree(p->dmem);
     delete p;
@@ -140,6 +144,7 @@ magi_status_t magi_attn_plan_create(const magi_attn_layout_t* layout, magi_attn_
   p->d_tiles = reinterpret_cast<const int*>(base + o_tiles);
   p->d_soffs = reinterpret_cast<const unsigned*>(base + o_soffs);
   p->d_rows = reinterpret_cast<const int2*>(base + o_rows);
+  p->d_merges = reinterpret_cast<const int4*>(base + o_merges);
   *out_plan = p;
   return MAGI_OK;
 }
@@ -158,7 +163,7 @@ magi_status_t magi_attn_plan_destroy(magi_attn_plan_t* plan) {
 magi_status_t magi_attn_workspace_size(const magi_attn_plan_t* plan, size_t* bytes) {
   if (!plan || !bytes) return fail(MAGI_ERR_INVALID_ARG, "plan or bytes is NULL");
   const auto& H = plan->host;
-  *bytes = H.dtype == MAGI_DTYPE_BF16 ? magi::workspace_bytes_bf16(H.tk, H.hk, H.d) : 0;
+  *bytes = H.dtype == MAGI_DTYPE_BF16 ? magi::workspace_bytes_bf16(H.tk, H.hk, H.d, H.n_slots) : 0;
   return MAGI_OK;
 }
 
@@ -195,6 +200,7 @@ magi_status_t magi_attn_fwd(const magi_attn_plan_t* plan, const void* q, const v
   prm.tiles = plan->d_tiles;
   prm.soffs = plan->d_soffs;
   prm.rows = plan->d_rows;
+  prm.merges = plan->d_merges;
   prm.eps = rms_eps;
   prm.scale = scale;
   prm.tq = int(H.tq);
@@ -206,7 +212,7 @@ magi_status_t magi_attn_fwd(const magi_attn_plan_t* plan, const void* q, const v
   hipStream_t st = static_cast<hipStream_t>(stream);
   const int n = int(H.items.size());
   hipError_t e;
-  if (H.dtype == MAGI_DTYPE_BF16) e = magi::launch_fwd_bf16_d128(prm, n, st);
+  if (H.dtype == MAGI_DTYPE_BF16) e = magi::launch_fwd_bf16_d128(prm, n, int(H.merges.size()), H.n_slots, st);
   else e = magi::launch_fwd_fp32(prm, H.d, n, st);
   if (e != hipSuccess) return hip_fail(e, "kernel launch");
   return MAGI_OK;

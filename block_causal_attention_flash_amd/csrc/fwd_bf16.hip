@@ -436,7 +436,9 @@ fwd_bf16_d128_kernel(FwdParams prm, const int4* __restrict__ items, const int* _
   __shared__ __attribute__((aligned(1024))) Smem sm;
   const int4 item = items[2 * blockIdx.x];
   if (item.z == item.w) return;                       // padding item
-  const int n_full = items[2 * blockIdx.x + 1].x;
+  const int2 item2 = reinterpret_cast<const int2*>(items + 2 * blockIdx.x + 1)[0];
+  const int n_full = item2.x;
+  const int slot = item2.y;                            // >= 0: a piece of a split item
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
@@ -534,6 +536,19 @@ fwd_bf16_d128_kernel(FwdParams prm, const int4* __restrict__ items, const int* _
     tok[rb] = item.x + r % prm.tile_q;
     valid[rb] = tok[rb] < prm.tq;
   }
+  if (slot >= 0) {
+    // piece of a split item: unnormalised O, reference maximum (0 on the
+    // static path: exp2(s) itself) and row sum, for the merge kernel
+#pragma unroll
+    for (int rb = 0; rb < NRB; ++rb) {
+      const float lsum = sum_groups(st.lsum[rb]);
+      const size_t r = size_t(slot) * ROWS + size_t((wave * NRB + rb) * 16 + (lane & 15));
+#pragma unroll
+      for (int db = 0; db < 8; ++db) *reinterpret_cast<f32x4*>(prm.part_o + r * D + db * 16 + g * 4) = st.o[rb][db];
+      if (g == 0) *reinterpret_cast<float2*>(prm.part_ml + r * 2) = float2{stat ? 0.0f : st.m[rb], lsum};
+    }
+    return;
+  }
 #pragma unroll
   for (int rb = 0; rb < NRB; ++rb) {
     const float lsum = sum_groups(st.lsum[rb]);
@@ -608,15 +623,64 @@ __global__ void __launch_bounds__(PP_THREADS) kv_prepare_kernel(const __bf16* __
   }
 }
 
-}  // namespace
-
-size_t workspace_bytes_bf16(long long tk, int hk, int d) {
-  (void)d;
-  const size_t n_kt = size_t((tk + BN - 1) / BN);
-  return 2 * n_kt * size_t(hk) * TILE_BYTES;          // K-hat images, then V^T images
+// Merge of a split item's pieces (one workgroup per split item): with the
+// pieces' reference maxima m_s, row sums l_s and unnormalised outputs O_s,
+// M = max m_s, w_s = 2^(m_s - M): out = sum w_s O_s / sum w_s l_s and
+// lse = (M + log2 sum w_s l_s) ln 2. A thread handles 16 dims of one row.
+constexpr int MG_THREADS = 256;
+__global__ void __launch_bounds__(MG_THREADS) merge_kernel(FwdParams prm) {
+  const int4 mi = prm.merges[blockIdx.x];
+  const int h0 = mi.y & 0xffff;
+  for (int u = threadIdx.x; u < ROWS * 8; u += MG_THREADS) {
+    const int r = u >> 3, c = u & 7;
+    const int head = h0 + r / prm.tile_q, tok = mi.x + r % prm.tile_q;
+    if (tok >= prm.tq) continue;
+    float mmax = kNegInf;
+    for (int sp = 0; sp < mi.w; ++sp) mmax = fmaxf(mmax, prm.part_ml[(size_t(mi.z + sp) * ROWS + r) * 2]);
+    float l = 0.0f;
+    f32x4 acc[4] = {};
+    for (int sp = 0; sp < mi.w; ++sp) {
+      const size_t rr = size_t(mi.z + sp) * ROWS + r;
+      const float2 ml = *reinterpret_cast<const float2*>(prm.part_ml + rr * 2);
+      const float w = ml.x == kNegInf ? 0.0f : __builtin_amdgcn_exp2f(ml.x - mmax);
+      l += w * ml.y;
+      const f32x4* po = reinterpret_cast<const f32x4*>(prm.part_o + rr * D + c * 16);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) acc[q] += w * po[q];
+    }
+    const float inv = 1.0f / l;
+    __bf16* orow = reinterpret_cast<__bf16*>(prm.out) + (size_t(tok) * prm.hq + head) * D + c * 16;
+    bf16x8 w0, w1;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      w0[j] = (__bf16)(acc[0][j] * inv);
+      w0[j + 4] = (__bf16)(acc[1][j] * inv);
+      w1[j] = (__bf16)(acc[2][j] * inv);
+      w1[j + 4] = (__bf16)(acc[3][j] * inv);
+    }
+    reinterpret_cast<bf16x8*>(orow)[0] = w0;
+    reinterpret_cast<bf16x8*>(orow)[1] = w1;
+    if (c == 0) prm.lse[size_t(head) * prm.tq + tok] = (mmax + __builtin_amdgcn_logf(l)) * kLn2;
+  }
 }
 
-hipError_t launch_fwd_bf16_d128(const FwdParams& p, int n_items, hipStream_t stream) {
+size_t image_bytes_bf16(long long tk, int hk) {
+  const size_t n_kt = size_t((tk + BN - 1) / BN);
+  return n_kt * size_t(hk) * TILE_BYTES;
+}
+
+}  // namespace
+
+size_t workspace_bytes_bf16(long long tk, int hk, int d, int n_slots) {
+  (void)d;
+  // K-hat images, V^T images, partial O, partial (m, l)
+  return 2 * image_bytes_bf16(tk, hk) + size_t(n_slots) * ROWS * (D + 2) * sizeof(float);
+}
+
+hipError_t launch_fwd_bf16_d128(const FwdParams& prm, int n_items, int n_merges, int n_slots, hipStream_t stream) {
+  FwdParams p = prm;
+  p.part_o = reinterpret_cast<float*>(static_cast<unsigned char*>(p.ws) + 2 * image_bytes_bf16(p.tk, p.hk));
+  p.part_ml = p.part_o + size_t(n_slots) * ROWS * D;
   const long long n_kt = (p.tk + BN - 1) / BN;
   if (n_kt > 0) {
     unsigned char* kimg = static_cast<unsigned char*>(p.ws);
@@ -627,6 +691,9 @@ hipError_t launch_fwd_bf16_d128(const FwdParams& p, int n_items, hipStream_t str
     if (e != hipSuccess) return e;
   }
   hipLaunchKernelGGL(fwd_bf16_d128_kernel, dim3(n_items), dim3(NTHR), 0, stream, p, p.items, p.tiles, p.soffs, p.rows);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || n_merges == 0) return e;
+  hipLaunchKernelGGL(merge_kernel, dim3(n_merges), dim3(MG_THREADS), 0, stream, p);
   return hipGetLastError();
 }
 

@@ -22,14 +22,17 @@ struct FwdParams {
   const int* tiles;      // key tile codes (kt * 2 + masked); lists padded with code -1
   const unsigned* soffs; // parallel to tiles: byte offset of the tile's image block (bf16 path)
   const int2* rows;      // RowBounds[tq]
+  const int4* merges;    // bf16 path: split items (MergeItem)
+  float* part_o;         // bf16 path, set by the launcher: partial O of each slot, [slot][384 rows][d] (workspace)
+  float* part_ml;        // bf16 path, set by the launcher: partial (m, l) of each slot, [slot][384 rows][2]
   float eps;
   float scale;           // softmax temperature on <q_hat, k_hat>
   int tq, tk, hq, hk;
   int tile_q, heads_per_item;
 };
 
-hipError_t launch_fwd_bf16_d128(const FwdParams& p, int n_items, hipStream_t stream);
-size_t workspace_bytes_bf16(long long tk, int hk, int d);
+hipError_t launch_fwd_bf16_d128(const FwdParams& p, int n_items, int n_merges, int n_slots, hipStream_t stream);
+size_t workspace_bytes_bf16(long long tk, int hk, int d, int n_slots);
 hipError_t launch_fwd_fp32(const FwdParams& p, int head_dim, int n_items, hipStream_t stream);
 
 }  // namespace magi

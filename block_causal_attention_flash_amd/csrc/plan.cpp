@@ -210,14 +210,43 @@ magi_status_t build_host_plan(const magi_attn_layout_t* L, const Tiling& tiling,
                                          : uint32_t(int64_t(P.tile_codes[t] >> 1) * P.hk * image_bytes);
   S.empty_pairs = n_qt * n_kt - S.full_pairs - S.boundary_pairs;
 
-  // Work items: (query tile, KV head, group of hpw query heads).
-  struct Cand { int64_t cost; int32_t qt, kvh, hg; };
+  // Work items: (query tile, KV head, group of hpw query heads), cut into
+  // pieces of their tile list when the layout has too few of them.
+  struct Cand { int64_t cost; int32_t qt, kvh, hg, begin, end, slot; };
+  int64_t n_whole = 0, total_cost = 0;
+  for (int64_t qt = 0; qt < n_qt; ++qt)
+    if (P.qt_ntiles[qt] > 0) {
+      n_whole += int64_t(P.hk) * groups_per_kvh;
+      total_cost += qt_cost[qt] * P.hk * groups_per_kvh;
+    }
+  const bool split = P.dtype == MAGI_DTYPE_BF16 && n_whole > 0 && n_whole < kSplitBelowItems;
+  const int64_t piece = std::max<int64_t>(kMinPieceTiles, (total_cost + kSplitTargetItems - 1) / kSplitTargetItems);
   std::vector<Cand> cands;
-  cands.reserve(size_t(n_qt) * P.hk * groups_per_kvh);
+  cands.reserve(size_t(n_whole));
+  P.merges.clear();
+  P.n_slots = 0;
   for (int kvh = 0; kvh < P.hk; ++kvh)
     for (int64_t qt = 0; qt < n_qt; ++qt) {
-      if (P.qt_ntiles[qt] == 0) continue;
-      for (int hg = 0; hg < groups_per_kvh; ++hg) cands.push_back(Cand{qt_cost[qt], int32_t(qt), kvh, hg});
+      const int32_t nt = P.qt_ntiles[qt];
+      if (nt == 0) continue;
+      const int32_t b0 = P.qt_tiles[qt];
+      const int64_t want = (nt + piece - 1) / piece;                        // pieces of about `piece` tiles
+      const int n_pieces =
+          split ? int(std::max<int64_t>(1, std::min<int64_t>({want, int64_t(kMaxPieces), nt / kMinPieceTiles}))) : 1;
+      for (int hg = 0; hg < groups_per_kvh; ++hg) {
+        if (n_pieces == 1) {
+          cands.push_back(Cand{nt, int32_t(qt), kvh, hg, b0, b0 + nt, -1});
+          continue;
+        }
+        const int h0 = kvh * group + hg * hpw;
+        P.merges.push_back(MergeItem{int32_t(qt * bm), (kvh << 16) | h0, P.n_slots, n_pieces});
+        for (int k = 0; k < n_pieces; ++k) {
+          const int32_t pb = b0 + int32_t(int64_t(nt) * k / n_pieces);
+          const int32_t pe = b0 + int32_t(int64_t(nt) * (k + 1) / n_pieces);
+          cands.push_back(Cand{pe - pb, int32_t(qt), kvh, hg, pb, pe, P.n_slots + k});
+        }
+        P.n_slots += n_pieces;
+      }
     }
   // Longest first; among equals, consecutive query tiles and head groups of
   // one KV head stay adjacent so concurrently running workgroups read the
@@ -232,9 +261,10 @@ magi_status_t build_host_plan(const magi_attn_layout_t* L, const Tiling& tiling,
   std::vector<int64_t> load(kNumXcd, 0);
   auto make_item = [&](const Cand& c) {
     const int h0 = c.kvh * group + c.hg * hpw;
-    return WorkItem{int32_t(c.qt * bm), (c.kvh << 16) | h0, P.qt_tiles[c.qt], P.qt_tiles[c.qt] + P.qt_ntiles[c.qt],
-                    P.qt_full[c.qt],
-                    {0, 0, 0}};
+    // full tiles come first in the list: the piece's share of them
+    const int32_t full_end = P.qt_tiles[c.qt] + P.qt_full[c.qt];
+    const int32_t n_full = std::max<int32_t>(0, std::min<int32_t>(c.end, full_end) - c.begin);
+    return WorkItem{int32_t(c.qt * bm), (c.kvh << 16) | h0, c.begin, c.end, n_full, c.slot, {0, 0}};
   };
   if (P.hk % kNumXcd == 0 || kNumXcd % P.hk == 0) {
     // Each KV head owns a fixed set of XCDs (or each XCD owns a fixed set of
@@ -262,7 +292,7 @@ magi_status_t build_host_plan(const magi_attn_layout_t* L, const Tiling& tiling,
   P.items.reserve(maxlen * kNumXcd);
   for (size_t j = 0; j < maxlen; ++j)
     for (int x = 0; x < kNumXcd; ++x)
-      P.items.push_back(j < queues[x].size() ? queues[x][j] : WorkItem{0, 0, 0, 0, 0, {0, 0, 0}});
+      P.items.push_back(j < queues[x].size() ? queues[x][j] : WorkItem{0, 0, 0, 0, 0, -1, {0, 0}});
   // Drop trailing padding.
   while (!P.items.empty() && P.items.back().tile_begin == P.items.back().tile_end) P.items.pop_back();
 

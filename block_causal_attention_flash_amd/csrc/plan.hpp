@@ -22,8 +22,30 @@ struct WorkItem {
   int32_t tile_begin;
   int32_t tile_end;    // == tile_begin: padding item, the workgroup exits at once
   int32_t n_full;
-  int32_t pad[3];
+  int32_t slot;        // -1: writes out / lse; else a piece of a split item: writes partial slot `slot`
+  int32_t pad[2];
 };
+
+// A split item: its rows (as in WorkItem) and the partial slots
+// [slot0, slot0 + n_pieces) that the merge combines into out / lse.
+struct MergeItem {
+  int32_t t0;
+  int32_t heads;
+  int32_t slot0;
+  int32_t n_pieces;
+};
+
+// Split-KV policy (bf16): when a layout has fewer than kSplitBelowItems work
+// items (too few to keep every compute unit busy to the end), items are cut
+// into up to kMaxPieces contiguous ranges of their tile list, about
+// total / kSplitTargetItems tiles each and at least kMinPieceTiles long.
+// (Measured: the 4-chunks-on-16-cached streaming window, 384 items, gains;
+// the two-video 256x256 layout, 768 short items, loses when split.)
+constexpr int kNumCu = 256;
+constexpr int kSplitBelowItems = 2 * kNumCu;
+constexpr int kSplitTargetItems = 4 * kNumCu;
+constexpr int kMaxPieces = 8;
+constexpr int kMinPieceTiles = 64;
 
 constexpr int kTilePad = 16;
 constexpr uint32_t kNoTileOffset = 0x80000000u;   // past any tile image buffer (< 2 GiB): reads give zeros
@@ -66,6 +88,8 @@ struct HostPlan {
   std::vector<int32_t> qt_ntiles;    // [n_qt] key tiles per query tile (padding excluded)
   std::vector<int32_t> qt_full;      // [n_qt] number of full key tiles per query tile
   std::vector<WorkItem> items;       // launch order (XCD-interleaved, padded)
+  std::vector<MergeItem> merges;     // split items
+  int32_t n_slots = 0;               // partial slots (pieces of split items)
   magi_attn_stats_t stats{};
 };
 

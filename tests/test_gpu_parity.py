@@ -108,6 +108,44 @@ def test_fp32_tiny_config():
     compare(*got, *ref, "fp32")
 
 
+# ------------------------------------------------------------------ split key ranges
+
+def split_window_layout():
+    """16 cached chunks of 512 keys, then two query chunks of 96 tokens whose
+    key chunks are 2048 long: the first 128-token query tile holds rows of both
+    (key ranges 10240 and 12288), the second tile has 64 rows past T_q."""
+    kv = [512 * i for i in range(17)] + [8192 + 2048, 8192 + 4096]
+    q = [0] * 17 + [96, 192]
+    return Layout(tuple(q), tuple(kv), (0, 18))
+
+
+def test_bf16_split_key_ranges_merge():
+    """Two work items (one per KV head) are too few for the GPU, so the plan
+    cuts each into pieces of its key-tile list whose partial results a merge
+    kernel combines (the LSE merge identity). The last piece of the first
+    tile holds only keys that the first chunk's rows may not see."""
+    from block_causal_attention_flash_amd import magi_attn_plan_stats
+    lay = split_window_layout()
+    st = magi_attn_plan_stats(lay.q_offsets, lay.kv_offsets, lay.seq_chunks, 6, 2, 128, "bf16")
+    assert st["n_items"] > 2 * 2, st                     # split into pieces
+    for hq, hk in ((6, 2), (8, 1)):
+        rl2, mabs, lerr = full_parity(lay, hq, hk, 128, "bf16", seed=11)
+        log(f"split window {hq}/{hk}: rel_l2={rl2:.3e} max_abs={mabs:.3e} lse_err={lerr:.3e}")
+
+
+def test_bf16_split_online_path():
+    """Pieces on the online-softmax path carry their own reference maxima."""
+    lay = split_window_layout()
+    inp = make_inputs(lay, 6, 2, 128, "bf16", "uniform", 12)
+    inp["q_gain"][0] = 40.0
+    inp["k_gain"][0] = 40.0
+    inp["k"][:, :, 0] = 0.0
+    sc = 1.0 / math.sqrt(128)
+    got_out, got_lse = run_gpu(lay, inp, 6, 2, 128, "bf16", 1e-6, sc)
+    ref_out, ref_lse = oracle.attention(inp["q"], inp["k"], inp["v"], inp["q_gain"], inp["k_gain"], 1e-6, sc, lay)
+    compare(got_out, got_lse, ref_out, ref_lse, "bf16")
+
+
 def test_bf16_online_softmax_path():
     """A gain of 40 on channel 0 of both q and k, with k zero in that channel,
     makes the Cauchy-Schwarz logit bound huge (so every wave runs the
