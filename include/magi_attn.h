@@ -113,9 +113,12 @@ MAGI_API magi_status_t magi_attn_plan_create(const magi_attn_layout_t* layout, m
 MAGI_API magi_status_t magi_attn_plan_destroy(magi_attn_plan_t* plan);
 
 /*
- * Device workspace bytes that magi_attn_fwd needs for this plan (bf16: the
+ * Device workspace bytes that magi_attn_fwd needs for this plan. bf16: the
  * RMS-normalised keys and the values re-laid out in 32-key tiles,
- * 2 * ceil(T_k / 32) * 32 * n_kv_heads * head_dim * 2 bytes; fp32: 0).
+ * 2 * ceil(T_k / 32) * 32 * n_kv_heads * head_dim * 2 bytes, plus, when the
+ * plan splits work items along the key axis (layouts with too few items to
+ * fill the GPU), the pieces' partial results, pieces * 384 * (head_dim + 2)
+ * * 4 bytes. fp32: 0.
  */
 MAGI_API magi_status_t magi_attn_workspace_size(const magi_attn_plan_t* plan, size_t* bytes);
 
