@@ -1,6 +1,6 @@
 """Benchmark of the block-causal attention forward on one MI355X.
 
-python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--kv-range R] [--no-cpu-baseline]
 
 A step is one forward call (query/key RMSNorm, masked softmax attention, LSE)
 over the whole workload, inputs resident in HBM. The plan (tile
@@ -12,6 +12,7 @@ matrix products over the mask area): 4 * head_dim * n_q_heads * (allowed
 query-key pairs per head).
 """
 import argparse
+import dataclasses
 import hashlib
 import json
 import math
@@ -30,13 +31,15 @@ KERNEL_SRC = os.path.join(ROOT, "block_causal_attention_flash_amd", "csrc", "fwd
 
 def useful_pairs(layout) -> int:
     """Allowed (query, key) pairs per head, from the offsets: every query of
-    chunk c sees keys from its video's first key to the end of chunk c."""
+    chunk c sees keys from its video's first key (or, with a KV range R, from
+    chunk c - R + 1 if later) to the end of chunk c."""
+    R = int(getattr(layout, "kv_range", 0))
     total = 0
     for s in range(layout.n_seqs):
         c0, c1 = layout.seq_chunks[s], layout.seq_chunks[s + 1]
-        lo = layout.kv_offsets[c0]
         for c in range(c0, c1):
-            total += (layout.q_offsets[c + 1] - layout.q_offsets[c]) * (layout.kv_offsets[c + 1] - lo)
+            first = max(c0, c - R + 1) if R > 0 else c0
+            total += (layout.q_offsets[c + 1] - layout.q_offsets[c]) * (layout.kv_offsets[c + 1] - layout.kv_offsets[first])
     return total
 
 
@@ -75,6 +78,7 @@ def cpu_baseline(cfg, inp, budget_s: float = 20.0):
     except Exception:  # pragma: no cover
         threads = 1
     lay = cfg.layout
+    R = int(getattr(lay, "kv_range", 0))
     d, hq = cfg.head_dim, cfg.n_q_heads
     rng = np.random.default_rng(0)
     # row blocks of 32 consecutive tokens from randomly chosen chunks
@@ -94,7 +98,8 @@ def cpu_baseline(cfg, inp, budget_s: float = 20.0):
         for r in rows:
             c = next(i for i in range(lay.n_chunks) if lay.q_offsets[i] <= r < lay.q_offsets[i + 1])
             s = next(i for i in range(lay.n_seqs) if lay.seq_chunks[i] <= c < lay.seq_chunks[i + 1])
-            flops += 4.0 * d * hq * (lay.kv_offsets[c + 1] - lay.kv_offsets[lay.seq_chunks[s]])
+            first = max(lay.seq_chunks[s], c - R + 1) if R > 0 else lay.seq_chunks[s]
+            flops += 4.0 * d * hq * (lay.kv_offsets[c + 1] - lay.kv_offsets[first])
         rows_done += len(rows)
         if time.perf_counter() - t_start > 3 * budget_s:
             break
@@ -125,6 +130,8 @@ def main():
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="video480x832")
+    ap.add_argument("--kv-range", type=int, default=0,
+                    help="KV-range window in chunks (0: every earlier chunk of the video is visible)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=20.0)
     ap.add_argument("--copy-probe-mib", type=int, default=0,
@@ -143,6 +150,8 @@ def main():
     from workloads import get_config, make_inputs
 
     cfg = get_config(args.workload)
+    if args.kv_range:
+        cfg = dataclasses.replace(cfg, layout=dataclasses.replace(cfg.layout, kv_range=args.kv_range))
     lay = cfg.layout
     dev = torch.device("cuda", 0)
     t0 = time.perf_counter()
@@ -179,7 +188,7 @@ def main():
     pairs = useful_pairs(lay)
     flops = 4.0 * cfg.head_dim * cfg.n_q_heads * pairs
     tflops = flops / (ms * 1e-3) / 1e12
-    traffic = stored_traffic(cfg.name)
+    traffic = stored_traffic(cfg.name) if not lay.kv_range else None
     roof = {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
             "frac": round(tflops / PEAK_BF16_TFLOPS, 4), "traffic": traffic}
 
@@ -204,7 +213,8 @@ def main():
                 "synthetic (seeded N(0,1) Q/K/V, QK-norm gains U(0.5,1.5))",
         "config": {"workload": cfg.name, "t_q": lay.t_q, "t_k": lay.t_k, "n_chunks": lay.n_chunks,
                    "n_videos": lay.n_seqs, "n_q_heads": cfg.n_q_heads, "n_kv_heads": cfg.n_kv_heads,
-                   "head_dim": cfg.head_dim, "useful_flops": flops, "unmasked_pairs_per_head": pairs},
+                   "head_dim": cfg.head_dim, "kv_range": lay.kv_range, "useful_flops": flops,
+                   "unmasked_pairs_per_head": pairs},
         "frac_of_peak": round(tflops / PEAK_BF16_TFLOPS, 4),
         "plan_create_ms": round(plan_ms, 2),
         "roofline": roof,

@@ -33,6 +33,7 @@ class Layout(ctypes.Structure):
         ("n_kv_heads", ctypes.c_int32),
         ("head_dim", ctypes.c_int32),
         ("dtype", ctypes.c_int32),
+        ("kv_range", ctypes.c_int32),
     ]
 
 

@@ -31,7 +31,7 @@ def _arr(x) -> np.ndarray:
 class _LayoutArgs:
     """Keeps the host offset arrays alive for the duration of a call."""
 
-    def __init__(self, q_offsets, kv_offsets, seq_chunks, n_q_heads, n_kv_heads, head_dim, dtype):
+    def __init__(self, q_offsets, kv_offsets, seq_chunks, n_q_heads, n_kv_heads, head_dim, dtype, kv_range=0):
         self.q = _arr(q_offsets)
         self.kv = None if kv_offsets is None else _arr(kv_offsets)
         n_chunks = len(self.q) - 1
@@ -39,7 +39,7 @@ class _LayoutArgs:
         p = lambda a: None if a is None else a.ctypes.data_as(_abi._i32p)  # noqa: E731
         dt = _DTYPES[dtype] if isinstance(dtype, str) else int(dtype)
         self.struct = _abi.Layout(len(self.seq) - 1, p(self.seq), n_chunks, p(self.q), p(self.kv),
-                                  int(n_q_heads), int(n_kv_heads), int(head_dim), dt)
+                                  int(n_q_heads), int(n_kv_heads), int(head_dim), dt, int(kv_range))
 
     def ptr(self):
         return ctypes.byref(self.struct)
@@ -50,18 +50,18 @@ def magi_attn_abi_version() -> int:
 
 
 def magi_attn_plan_stats(q_offsets, kv_offsets=None, seq_chunks=None, n_q_heads=1, n_kv_heads=1, head_dim=128,
-                         dtype="bf16") -> dict:
+                         dtype="bf16", kv_range=0) -> dict:
     lib = _abi.load()
-    la = _LayoutArgs(q_offsets, kv_offsets, seq_chunks, n_q_heads, n_kv_heads, head_dim, dtype)
+    la = _LayoutArgs(q_offsets, kv_offsets, seq_chunks, n_q_heads, n_kv_heads, head_dim, dtype, kv_range)
     st = _abi.Stats()
     _check(lib, lib.magi_attn_plan_stats(la.ptr(), ctypes.byref(st)))
     return {name: getattr(st, name) for name, _ in _abi.Stats._fields_}
 
 
 def magi_attn_classify_host(q_offsets, kv_offsets=None, seq_chunks=None, bm=128, bn=64, n_q_heads=1, n_kv_heads=1,
-                            head_dim=128, dtype="bf16") -> np.ndarray:
+                            head_dim=128, dtype="bf16", kv_range=0) -> np.ndarray:
     lib = _abi.load()
-    la = _LayoutArgs(q_offsets, kv_offsets, seq_chunks, n_q_heads, n_kv_heads, head_dim, dtype)
+    la = _LayoutArgs(q_offsets, kv_offsets, seq_chunks, n_q_heads, n_kv_heads, head_dim, dtype, kv_range)
     tq = int(la.q[-1])
     tk = int((la.kv if la.kv is not None else la.q)[-1])
     n_qt, n_kt = -(-tq // bm), -(-tk // bn)
@@ -71,10 +71,10 @@ def magi_attn_classify_host(q_offsets, kv_offsets=None, seq_chunks=None, bm=128,
 
 
 def magi_attn_plan_create(q_offsets, kv_offsets=None, seq_chunks=None, n_q_heads=1, n_kv_heads=1, head_dim=128,
-                          dtype="bf16") -> int:
+                          dtype="bf16", kv_range=0) -> int:
     """Returns the opaque plan handle (an integer address)."""
     lib = _abi.load()
-    la = _LayoutArgs(q_offsets, kv_offsets, seq_chunks, n_q_heads, n_kv_heads, head_dim, dtype)
+    la = _LayoutArgs(q_offsets, kv_offsets, seq_chunks, n_q_heads, n_kv_heads, head_dim, dtype, kv_range)
     h = ctypes.c_void_p()
     _check(lib, lib.magi_attn_plan_create(la.ptr(), ctypes.byref(h)))
     return h.value
@@ -163,11 +163,12 @@ class Plan:
     """Owns a plan handle for one layout; call() runs the forward."""
 
     def __init__(self, q_offsets, kv_offsets=None, seq_chunks=None, n_q_heads=1, n_kv_heads=1, head_dim=128,
-                 dtype="bf16"):
+                 dtype="bf16", kv_range=0):
         self.layout = dict(q_offsets=list(map(int, q_offsets)),
                            kv_offsets=None if kv_offsets is None else list(map(int, kv_offsets)),
                            seq_chunks=None if seq_chunks is None else list(map(int, seq_chunks)),
-                           n_q_heads=n_q_heads, n_kv_heads=n_kv_heads, head_dim=head_dim, dtype=dtype)
+                           n_q_heads=n_q_heads, n_kv_heads=n_kv_heads, head_dim=head_dim, dtype=dtype,
+                           kv_range=int(kv_range))
         self.n_q_heads, self.n_kv_heads, self.head_dim, self.dtype = n_q_heads, n_kv_heads, head_dim, dtype
         self.t_q = int(self.layout["q_offsets"][-1])
         kv = self.layout["kv_offsets"] or self.layout["q_offsets"]
@@ -176,7 +177,8 @@ class Plan:
 
     @classmethod
     def from_layout(cls, layout, n_q_heads, n_kv_heads, head_dim, dtype="bf16"):
-        return cls(layout.q_offsets, layout.kv_offsets, layout.seq_chunks, n_q_heads, n_kv_heads, head_dim, dtype)
+        return cls(layout.q_offsets, layout.kv_offsets, layout.seq_chunks, n_q_heads, n_kv_heads, head_dim, dtype,
+                   getattr(layout, "kv_range", 0))
 
     def stats(self) -> dict:
         return magi_attn_plan_stats(**self.layout)

@@ -51,10 +51,10 @@ magi_status_t validate_layout(const magi_attn_layout_t* L, std::string& err) {
     if (L->q_offsets[c + 1] < L->q_offsets[c]) { err = "q_offsets must be non-decreasing"; return MAGI_ERR_INVALID_ARG; }
     if (kv[c + 1] < kv[c]) { err = "kv_offsets must be non-decreasing"; return MAGI_ERR_INVALID_ARG; }
   }
+  if (L->kv_range < 0) { err = "kv_range must be >= 0"; return MAGI_ERR_INVALID_ARG; }
   for (int s = 0; s < L->n_seqs; ++s) {
-    const int32_t lo = kv[L->seq_chunks[s]];
     for (int c = L->seq_chunks[s]; c < L->seq_chunks[s + 1]; ++c)
-      if (L->q_offsets[c + 1] > L->q_offsets[c] && kv[c + 1] <= lo) {
+      if (L->q_offsets[c + 1] > L->q_offsets[c] && kv[c + 1] <= kv[first_visible_chunk(L, s, c)]) {
         err = "chunk " + std::to_string(c) + " owns queries but sees no key"; return MAGI_ERR_INVALID_ARG;
       }
   }
@@ -103,11 +103,11 @@ Tiling choose_tiling(int dtype, int head_dim, int group) {
 void row_bounds(const magi_attn_layout_t* L, std::vector<RowBounds>& rows) {
   const int32_t* kv = L->kv_offsets ? L->kv_offsets : L->q_offsets;
   rows.assign(L->q_offsets[L->n_chunks], RowBounds{0, 0});
-  for (int s = 0; s < L->n_seqs; ++s) {
-    const int32_t lo = kv[L->seq_chunks[s]];
-    for (int c = L->seq_chunks[s]; c < L->seq_chunks[s + 1]; ++c)
+  for (int s = 0; s < L->n_seqs; ++s)
+    for (int c = L->seq_chunks[s]; c < L->seq_chunks[s + 1]; ++c) {
+      const int32_t lo = kv[first_visible_chunk(L, s, c)];
       for (int32_t t = L->q_offsets[c]; t < L->q_offsets[c + 1]; ++t) rows[t] = RowBounds{lo, kv[c + 1]};
-  }
+    }
 }
 
 void tile_intervals(const std::vector<RowBounds>& rows, int64_t r0, int64_t r1, std::vector<RowBounds>& out) {

@@ -93,6 +93,13 @@ struct HostPlan {
   magi_attn_stats_t stats{};
 };
 
+// First chunk whose keys chunk c of video s sees: the video's first chunk, or
+// with a KV range R, the later of that and c - R + 1.
+inline int first_visible_chunk(const magi_attn_layout_t* L, int s, int c) {
+  const int first = L->seq_chunks[s];
+  return L->kv_range > 0 && c - L->kv_range + 1 > first ? c - L->kv_range + 1 : first;
+}
+
 // Returns MAGI_OK or an error with a message in `err`.
 magi_status_t validate_layout(const magi_attn_layout_t* layout, std::string& err);
 

@@ -50,7 +50,7 @@
 extern "C" {
 #endif
 
-#define MAGI_ATTN_ABI_VERSION 1
+#define MAGI_ATTN_ABI_VERSION 2
 
 typedef enum magi_status {
   MAGI_OK = 0,
@@ -76,6 +76,11 @@ typedef enum magi_dtype {
  *                           as the clean chunks of a KV cache do).
  *   kv_offsets[n_chunks+1]: chunk c owns keys/values [kv_offsets[c], kv_offsets[c+1]);
  *                           non-decreasing from 0; NULL means kv_offsets == q_offsets.
+ * kv_range             : 0: a chunk sees every earlier chunk of its video and
+ *                        itself (block-causal); R >= 1: chunk c sees only
+ *                        chunks max(first chunk of its video, c - R + 1) .. c
+ *                        (the pages' "KV range" of streaming inference:
+ *                        paperlayer §2.4.4, paper-notes §3.4.4 and Figure 12).
  * A chunk that owns queries must see at least one key.
  * head_dim: 128 for bf16; 64 or 128 for fp32. n_q_heads % n_kv_heads == 0.
  */
@@ -89,6 +94,7 @@ typedef struct magi_attn_layout {
   int32_t n_kv_heads;
   int32_t head_dim;
   int32_t dtype;              /* magi_dtype_t */
+  int32_t kv_range;           /* 0: block-causal; R >= 1: the last R chunks of the video */
 } magi_attn_layout_t;
 
 typedef struct magi_attn_plan magi_attn_plan_t;   /* opaque */

@@ -82,7 +82,9 @@ def block_causal_mask(layout, rows: Optional[np.ndarray] = None) -> np.ndarray:
     M[i, j] is true when key j lies in the same video as query i and its chunk
     is not later than the query's chunk (paperlayer §2 / Figure 1: bidirectional
     within a chunk, causal across chunks; paper-notes Figure 15: no attention
-    across packed videos).
+    across packed videos). With a KV range R >= 1 (layout.kv_range; paperlayer
+    §2.4.4, paper-notes §3.4.4 and Figure 12) the key's chunk must also be one
+    of the query chunk's R latest: kc > qc - R.
     """
     tq, tk = int(layout.q_offsets[-1]), int(layout.kv_offsets[-1])
     n_chunks = len(layout.q_offsets) - 1
@@ -93,7 +95,11 @@ def block_causal_mask(layout, rows: Optional[np.ndarray] = None) -> np.ndarray:
         qc = qc[np.asarray(rows)]
     same_video = vid[qc][:, None] == vid[kc][None, :]
     not_later = kc[None, :] <= qc[:, None]
-    return same_video & not_later
+    mask = same_video & not_later
+    R = int(getattr(layout, "kv_range", 0))
+    if R > 0:
+        mask &= kc[None, :] > qc[:, None] - R
+    return mask
 
 
 def unmasked_pairs(layout) -> int:
@@ -169,7 +175,8 @@ def attention_loops(q, k, v, q_gain, k_gain, eps: float, scale: float, layout
 
     Independent of numpy's reductions and of the dense-mask construction: a
     key is allowed for a query when both chunks belong to the same video and
-    the key's chunk index is not larger than the query's. Tiny inputs only.
+    the key's chunk index is not larger than the query's (and, with a KV range
+    R, larger than the query's minus R). Tiny inputs only.
     """
     q = _as_f64(q).tolist()
     k = _as_f64(k).tolist()
@@ -202,8 +209,9 @@ def attention_loops(q, k, v, q_gain, k_gain, eps: float, scale: float, layout
     kchunks = [chunk_of(layout.kv_offsets, j) for j in range(tk)]
     for i in range(tq):
         ci = chunk_of(layout.q_offsets, i)
+        R = int(getattr(layout, "kv_range", 0))
         allowed = [j for j in range(tk)
-                   if video_of(kchunks[j]) == video_of(ci) and kchunks[j] <= ci]
+                   if video_of(kchunks[j]) == video_of(ci) and kchunks[j] <= ci and (R == 0 or kchunks[j] > ci - R)]
         for h in range(hq):
             g = h // group
             qi = norm(q[i][h], qg)

@@ -1,0 +1,53 @@
+"""CPU tests of bench.py's host-side accounting: the useful-FLOP pair count it
+reports against the oracle's dense mask, with and without a KV range, and the
+check that its stored HBM-traffic figures belong to the current kernel."""
+import dataclasses
+import json
+import os
+
+import numpy as np
+import pytest
+
+import bench
+import oracle
+from workloads import CONFIGS, Layout, layout_from_chunks, streaming_layout
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def test_useful_pairs_match_golden_mask_areas():
+    with open(os.path.join(ROOT, "tests", "golden", "unmasked_pairs.json")) as f:
+        gold = json.load(f)["pairs_per_head"]
+    for c in CONFIGS:
+        assert bench.useful_pairs(c.layout) == gold[c.name], c.name
+
+
+@pytest.mark.parametrize("R", [0, 1, 2, 3, 5])
+def test_useful_pairs_match_dense_mask_with_window(R):
+    lays = [layout_from_chunks([[7, 5, 9, 3], [4, 4]]), streaming_layout(3, 2, 6),
+            Layout((0, 3, 3, 8, 10), (0, 4, 9, 11, 15), (0, 2, 4))]
+    for lay in lays:
+        lw = dataclasses.replace(lay, kv_range=R)
+        assert bench.useful_pairs(lw) == int(oracle.block_causal_mask(lw).sum())
+
+
+def test_stored_traffic_is_tied_to_the_kernel_source():
+    for name in ("video480x832", "streaming"):
+        path = os.path.join(ROOT, "profiles", f"fwd_bf16_{name}_traffic.json")
+        if not os.path.exists(path):
+            continue
+        with open(path) as f:
+            doc = json.load(f)
+        if doc.get("kernel_sha256_16") == bench.kernel_hash():
+            assert bench.stored_traffic(name) == doc["hbm_bytes_per_launch"]
+        else:
+            assert bench.stored_traffic(name) is None
+    assert bench.stored_traffic("no-such-workload") is None
+
+
+def test_more_than_one_gpu_is_refused(monkeypatch, capsys):
+    monkeypatch.setattr("sys.argv", ["bench.py", "--gpus", "2"])
+    with pytest.raises(SystemExit) as e:
+        bench.main()
+    assert e.value.code == 2
+    assert "one GPU" in capsys.readouterr().err

@@ -230,6 +230,44 @@ def test_config_full_size_sampled_rows(name):
     log(f"config {name}: rows={len(rows)} rel_l2={rl2:.3e} max_abs={mabs:.3e} lse_err={lerr:.3e}")
 
 
+# ------------------------------------------------------------------ KV-range window
+
+@pytest.mark.parametrize("R", [1, 2, 3])
+@pytest.mark.parametrize("hq,hk", [(6, 2), (8, 1)])
+def test_bf16_kv_range_small(R, hq, hk):
+    """A chunk sees only the last R chunks of its video (the pages' KV range);
+    rows whose window starts inside a key tile exercise the lower bound."""
+    base = layout_from_chunks([[130, 70, 96, 150], [190, 40]])
+    lay = Layout(base.q_offsets, base.kv_offsets, base.seq_chunks, R)
+    rl2, mabs, lerr = full_parity(lay, hq, hk, 128, "bf16", seed=20 + R)
+    log(f"kv_range {R} {hq}/{hk}: rel_l2={rl2:.3e} max_abs={mabs:.3e} lse_err={lerr:.3e}")
+
+
+def test_fp32_kv_range_small():
+    base = layout_from_chunks([[30, 17, 41], [25, 9]])
+    lay = Layout(base.q_offsets, base.kv_offsets, base.seq_chunks, 2)
+    full_parity(lay, 4, 2, 64, "fp32", seed=24)
+
+
+def test_kv_range_480x832_sampled_rows():
+    """The 16-chunk 480x832 video with a KV range of 5 chunks."""
+    import dataclasses
+    from block_causal_attention_flash_amd import magi_attn_plan_stats
+    c = get_config("video480x832")
+    lay = dataclasses.replace(c.layout, kv_range=5)
+    inp = make_inputs(lay, c.n_q_heads, c.n_kv_heads, c.head_dim, c.dtype, c.gain_kind, c.seed)
+    st = magi_attn_plan_stats(lay.q_offsets, lay.kv_offsets, lay.seq_chunks, c.n_q_heads, c.n_kv_heads,
+                              c.head_dim, c.dtype, kv_range=5)
+    got_out, got_lse = run_gpu(lay, inp, c.n_q_heads, c.n_kv_heads, c.head_dim, c.dtype, c.eps, c.scale)
+    rows = sample_rows(lay, st["tile_q"], 12, seed=5)
+    rows = rows[np.random.default_rng(2).permutation(len(rows))[:40]]
+    rows.sort()
+    ref_out, ref_lse = oracle.attention(inp["q"], inp["k"], inp["v"], inp["q_gain"], inp["k_gain"], c.eps,
+                                        c.scale, lay, rows=rows)
+    rl2, mabs, lerr = compare(got_out[rows], got_lse[:, rows], ref_out, ref_lse, c.dtype)
+    log(f"kv_range 5 video480x832: rows={len(rows)} rel_l2={rl2:.3e} max_abs={mabs:.3e} lse_err={lerr:.3e}")
+
+
 # ------------------------------------------------------------------ invariants that need no oracle
 
 def _fwd(plan, inp, dev):

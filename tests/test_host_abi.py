@@ -31,7 +31,9 @@ def test_library_exports_every_declared_symbol(built_lib):
 
 def test_abi_version(built_lib):
     from block_causal_attention_flash_amd import magi_attn_abi_version
-    assert magi_attn_abi_version() == 1
+    hdr = open(os.path.join(ROOT, "include", "magi_attn.h")).read()
+    declared = int(re.search(r"#define MAGI_ATTN_ABI_VERSION (\d+)", hdr).group(1))
+    assert magi_attn_abi_version() == declared == 2
 
 
 def brute_classes(layout, bm, bn):
@@ -72,14 +74,38 @@ def random_layout(rng):
 
 @pytest.mark.parametrize("seed", range(40))
 def test_classifier_matches_dense_mask(built_lib, seed):
+    """Tile classes from the library against the oracle's dense mask, for
+    random layouts with and without a KV range."""
     from block_causal_attention_flash_amd import magi_attn_classify_host
     rng = np.random.default_rng(seed)
     lay = random_layout(rng)
     if lay.t_q == 0:
         pytest.skip("no queries")
-    for bm, bn in ((64, 64), (128, 64), (32, 16), (7, 5)):
-        got = magi_attn_classify_host(lay.q_offsets, lay.kv_offsets, lay.seq_chunks, bm=bm, bn=bn)
-        np.testing.assert_array_equal(got, brute_classes(lay, bm, bn))
+    for R in (0, int(rng.integers(1, 4))):
+        lw = Layout(lay.q_offsets, lay.kv_offsets, lay.seq_chunks, R)
+        if R and any(lw.q_offsets[c + 1] > lw.q_offsets[c] and lw.kv_offsets[c + 1] == lw.kv_offsets[max(
+                [s0 for s0 in lw.seq_chunks[:-1] if s0 <= c][-1], c - R + 1)] for c in range(lw.n_chunks)):
+            continue                          # a chunk with queries would see no key: rejected layout
+        for bm, bn in ((64, 64), (128, 64), (32, 16), (7, 5)):
+            got = magi_attn_classify_host(lw.q_offsets, lw.kv_offsets, lw.seq_chunks, bm=bm, bn=bn, kv_range=R)
+            np.testing.assert_array_equal(got, brute_classes(lw, bm, bn))
+
+
+def test_kv_range_stats_and_validation(built_lib):
+    from block_causal_attention_flash_amd import MagiAttnError, magi_attn_plan_stats
+    c = get_config("video480x832")
+    st = magi_attn_plan_stats(c.layout.q_offsets, None, None, 48, 8, 128, "bf16", kv_range=5)
+    assert st["unmasked_pairs"] == 9360 * 9360 * (1 + 2 + 3 + 4 + 5 * 12)
+    assert st["executed_pairs"] / st["unmasked_pairs"] < 1.01
+    full = magi_attn_plan_stats(c.layout.q_offsets, None, None, 48, 8, 128, "bf16", kv_range=16)
+    assert full["unmasked_pairs"] == 9360 * 9360 * sum(range(1, 17))
+    with pytest.raises(MagiAttnError) as e:
+        magi_attn_plan_stats([0, 4, 8], None, None, 1, 1, 128, "bf16", kv_range=-1)
+    assert e.value.status == 1
+    # a chunk whose window holds no key: chunk 2 owns queries but no keys, R = 1
+    with pytest.raises(MagiAttnError) as e:
+        magi_attn_plan_stats([0, 4, 8, 12], [0, 4, 8, 8], None, 1, 1, 128, "bf16", kv_range=1)
+    assert e.value.status == 1
 
 
 def test_stats_match_mask_areas(built_lib):

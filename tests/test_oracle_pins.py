@@ -120,10 +120,14 @@ def check_streaming_prefix(fn=oracle.attention):
 
 
 def allowed_range(layout, i):
-    """[video start, end of own chunk) in key tokens, from the offsets."""
+    """[video start, end of own chunk) in key tokens, from the offsets; with a
+    KV range R the start is that of chunk c - R + 1 when it is later."""
     c = max(cc for cc in range(len(layout.q_offsets) - 1) if layout.q_offsets[cc] <= i < layout.q_offsets[cc + 1])
     s = max(ss for ss in range(len(layout.seq_chunks) - 1) if layout.seq_chunks[ss] <= c)
-    return layout.kv_offsets[layout.seq_chunks[s]], layout.kv_offsets[c + 1]
+    first = layout.seq_chunks[s]
+    if layout.kv_range > 0:
+        first = max(first, c - layout.kv_range + 1)
+    return layout.kv_offsets[first], layout.kv_offsets[c + 1]
 
 
 def check_identical_keys(fn=oracle.attention, layout=None):
@@ -148,6 +152,39 @@ def check_identical_keys(fn=oracle.attention, layout=None):
                 return False
             s = scale * float(np.dot(qh[i, h], kh[g]))
             if abs(lse[h, i] - (s + math.log(hi - lo))) > 1e-12:
+                return False
+    return True
+
+
+def windowed(layout, R):
+    return Layout(layout.q_offsets, layout.kv_offsets, layout.seq_chunks, R)
+
+
+def check_window_wide_is_block_causal(fn=oracle.attention):
+    """A KV range of at least the number of chunks changes nothing."""
+    lay = layout_from_chunks([[5, 7, 3], [4, 6]])
+    inp = small_inputs(lay, 4, 2, 8, seed=15)
+    args = (inp["q"], inp["k"], inp["v"], inp["q_gain"], inp["k_gain"], 1e-6, 0.3)
+    o0, l0 = fn(*args, lay)
+    o1, l1 = fn(*args, windowed(lay, 3))
+    o2, l2 = fn(*args, windowed(lay, 50))
+    return all(np.array_equal(a, b) for a, b in ((o0, o1), (l0, l1), (o0, o2), (l0, l2)))
+
+
+def check_window_slices(R, fn=oracle.attention):
+    """KV range R: the rows of chunk c are full attention (library SDPA) over
+    the keys of chunks max(first, c - R + 1) .. c of their video."""
+    lay = windowed(layout_from_chunks([[5, 7, 3, 6], [4, 6]]), R)
+    inp = small_inputs(lay, 4, 2, 8, seed=16)
+    out, _ = fn(inp["q"], inp["k"], inp["v"], inp["q_gain"], inp["k_gain"], 1e-6, 0.3, lay)
+    for s in range(lay.n_seqs):
+        c0, c1 = lay.seq_chunks[s], lay.seq_chunks[s + 1]
+        for c in range(c0, c1):
+            rows = slice(lay.q_offsets[c], lay.q_offsets[c + 1])
+            keys = slice(lay.kv_offsets[max(c0, c - R + 1)], lay.kv_offsets[c + 1])
+            ref = lib_attention(inp["q"][rows], inp["k"][keys], inp["v"][keys], inp["q_gain"], inp["k_gain"],
+                                1e-6, 0.3)
+            if not np.allclose(out[rows], ref, rtol=1e-12, atol=1e-12):
                 return False
     return True
 
@@ -329,6 +366,56 @@ def test_unmasked_pairs_closed_forms():
         assert gold[name] == oracle.unmasked_pairs(get_config(name).layout)
 
 
+def test_kv_range_wide_is_block_causal():
+    assert check_window_wide_is_block_causal()
+
+
+@pytest.mark.parametrize("R", [1, 2, 3])
+def test_kv_range_is_full_attention_over_the_last_chunks(R):
+    assert check_window_slices(R)
+
+
+def test_kv_range_brute_force_loops():
+    lay = Layout((0, 0, 3, 7, 7, 12, 14), (0, 2, 5, 8, 11, 14, 17), (0, 4, 6), 2)
+    inp = small_inputs(lay, 4, 2, 8, seed=17)
+    args = (inp["q"], inp["k"], inp["v"], inp["q_gain"], inp["k_gain"], 1e-6, 0.3, lay)
+    o1, l1 = oracle.attention(*args)
+    o2, l2 = oracle.attention_loops(*args)
+    assert np.max(np.abs(o1 - o2)) <= 1e-12
+    assert np.max(np.abs(l1 - l2)) <= 1e-12
+
+
+@pytest.mark.parametrize("R", [1, 2, 4])
+def test_kv_range_identical_keys_closed_form(R):
+    lay = Layout((0, 0, 0, 5, 9, 9, 16, 20), (0, 4, 7, 12, 15, 18, 22, 26), (0, 4, 7), R)
+    assert check_identical_keys(layout=lay)
+
+
+def test_kv_range_unmasked_pairs_closed_form():
+    lay = windowed(layout_from_chunks([[3, 4, 5, 6]]), 2)
+    assert oracle.unmasked_pairs(lay) == 3 * 3 + 4 * (3 + 4) + 5 * (4 + 5) + 6 * (5 + 6)
+    # the 16-chunk geometry of the 480x832 video with a KV range of 5, at 90 tokens per chunk
+    assert oracle.unmasked_pairs(windowed(layout_from_chunks([[90] * 16]), 5)) == 90 * 90 * (1 + 2 + 3 + 4 + 5 * 12)
+
+
+def _window_off_by_one(layout, rows=None):
+    """Mutant: a KV range R admits R + 1 chunks."""
+    m = _orig_mask(Layout(layout.q_offsets, layout.kv_offsets, layout.seq_chunks), rows)
+    tq, tk = int(layout.q_offsets[-1]), int(layout.kv_offsets[-1])
+    qc = oracle.token_chunk_ids(layout.q_offsets, tq)
+    kc = oracle.token_chunk_ids(layout.kv_offsets, tk)
+    if rows is not None:
+        qc = qc[np.asarray(rows)]
+    if layout.kv_range > 0:
+        m &= kc[None, :] >= qc[:, None] - layout.kv_range
+    return m
+
+
+def test_planted_window_mistake_is_caught(monkeypatch):
+    monkeypatch.setattr(oracle_mod, "block_causal_mask", _window_off_by_one)
+    assert not check_window_slices(2, oracle_mod.attention)
+
+
 # ----------------------------------------------------------------------------- planted mistakes
 
 def _mutant_mask_no_video(layout, rows=None):
@@ -370,6 +457,7 @@ def test_planted_mistakes_are_caught(monkeypatch, mutant, checks):
 
 
 _orig_rms = oracle_mod.rms_norm
+_orig_mask = oracle_mod.block_causal_mask
 _orig_attention = oracle_mod.attention
 
 

@@ -29,6 +29,7 @@ class Layout:
     q_offsets: tuple
     kv_offsets: tuple
     seq_chunks: tuple
+    kv_range: int = 0      # 0: block-causal; R >= 1: a chunk sees the last R chunks of its video
 
     @property
     def n_chunks(self) -> int:
