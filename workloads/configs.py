@@ -81,6 +81,55 @@ def packed_chunk_draw(seed: int = 8):
     return [[int(s)] * int(c) for c, s in zip(n, sz)]
 
 
+@dataclasses.dataclass(frozen=True)
+class TextLayout:
+    """Text side of the cross-attention: chunk c's queries attend to the text
+    keys [begin[c], end[c]) of one packed text stream of t_text tokens;
+    begin[c] == end[c] means the chunk has no text condition (a clean chunk).
+    Chunk-wise prompts: paperlayer §2.2.3; clean chunks without text:
+    paper-notes §3.2.6."""
+    begin: tuple
+    end: tuple
+    t_text: int
+
+
+def chunk_prompts(prompt_of_chunk: Sequence[Optional[int]], prompt_lengths: Sequence[int]) -> TextLayout:
+    """Prompts packed one after another into the text stream; chunk c uses
+    prompt prompt_of_chunk[c], or no text when that entry is None."""
+    starts = [0]
+    for n in prompt_lengths:
+        starts.append(starts[-1] + int(n))
+    begin = tuple(0 if p is None else starts[p] for p in prompt_of_chunk)
+    end = tuple(0 if p is None else starts[p + 1] for p in prompt_of_chunk)
+    return TextLayout(begin, end, starts[-1])
+
+
+def prompt_draw(layout: Layout, clean_per_video: int, chunks_per_prompt: int, seed: int, lo: int = 64,
+                hi: int = 512) -> TextLayout:
+    """Chunk-wise prompts for a layout: in every video the first
+    `clean_per_video` chunks carry no text, and each following run of
+    `chunks_per_prompt` chunks shares one prompt; chunks without queries (a
+    KV cache) carry none either. Prompt lengths are drawn uniformly from
+    [lo, hi] tokens with default_rng(seed), in prompt order."""
+    prompt_of_chunk: List[Optional[int]] = []
+    n_prompts = 0
+    for s in range(layout.n_seqs):
+        c0, c1 = layout.seq_chunks[s], layout.seq_chunks[s + 1]
+        run = -1
+        for c in range(c0, c1):
+            if c - c0 < clean_per_video or layout.q_offsets[c + 1] == layout.q_offsets[c]:
+                prompt_of_chunk.append(None)
+                continue
+            r = (c - c0 - clean_per_video) // chunks_per_prompt
+            if r != run:
+                run = r
+                n_prompts += 1
+            prompt_of_chunk.append(n_prompts - 1)
+    rng = np.random.default_rng(seed)
+    lengths = rng.integers(lo, hi + 1, n_prompts)
+    return chunk_prompts(prompt_of_chunk, [int(x) for x in lengths])
+
+
 def tokens_per_chunk(height: int, width: int, frames: int = 24, patch: int = 2) -> int:
     lat_frames = frames // 4
     return lat_frames * (height // 8 // patch) * (width // 8 // patch)
@@ -115,6 +164,31 @@ def _configs() -> List[Config]:
 
 
 CONFIGS = _configs()
+
+
+def text_layout(cfg: Config) -> TextLayout:
+    """The cross-attention text of a workload (seed = the workload's + 100):
+      tiny          chunk 0 clean, chunks 1 and 2 with their own prompts of
+                    9..40 tokens (ragged against 32-key tiles);
+      video256x2    per video: chunk 0 clean, one prompt per 2 chunks;
+      streaming     cached chunks without text, the 4 active chunks one
+                    prompt per 2 chunks;
+      video480x832  chunks 0, 1 clean, one prompt per 4 chunks;
+      packed8       per video: chunk 0 clean (one-chunk videos have no text),
+                    one prompt for the rest of the video.
+    Prompt lengths are uniform on [64, 512] tokens (tiny: [9, 40])."""
+    seed = cfg.seed + 100
+    if cfg.name == "tiny":
+        return prompt_draw(cfg.layout, 1, 1, seed, 9, 40)
+    if cfg.name == "video256x2":
+        return prompt_draw(cfg.layout, 1, 2, seed)
+    if cfg.name == "streaming":
+        return prompt_draw(cfg.layout, 0, 2, seed)
+    if cfg.name == "video480x832":
+        return prompt_draw(cfg.layout, 2, 4, seed)
+    if cfg.name == "packed8":
+        return prompt_draw(cfg.layout, 1, 1 << 30, seed)
+    raise KeyError(cfg.name)
 
 
 def get_config(name_or_index) -> Config:
