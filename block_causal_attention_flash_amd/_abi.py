@@ -37,6 +37,35 @@ class Layout(ctypes.Structure):
     ]
 
 
+class Text(ctypes.Structure):
+    _fields_ = [
+        ("t_text", ctypes.c_int32),
+        ("text_begin", _i32p),
+        ("text_end", _i32p),
+    ]
+
+
+class ParallelIO(ctypes.Structure):
+    _fields_ = [
+        ("q", ctypes.c_void_p),
+        ("k", ctypes.c_void_p),
+        ("v", ctypes.c_void_p),
+        ("q_gain", ctypes.c_void_p),
+        ("k_gain", ctypes.c_void_p),
+        ("scale", ctypes.c_float),
+        ("out", ctypes.c_void_p),
+        ("lse", ctypes.c_void_p),
+        ("q_x", ctypes.c_void_p),
+        ("k_x", ctypes.c_void_p),
+        ("v_x", ctypes.c_void_p),
+        ("q_gain_x", ctypes.c_void_p),
+        ("k_gain_x", ctypes.c_void_p),
+        ("scale_x", ctypes.c_float),
+        ("out_x", ctypes.c_void_p),
+        ("lse_x", ctypes.c_void_p),
+    ]
+
+
 class Stats(ctypes.Structure):
     _fields_ = [
         ("unmasked_pairs", ctypes.c_int64),
@@ -54,12 +83,18 @@ class Stats(ctypes.Structure):
 # name -> (restype, argtypes)
 SIGNATURES = {
     "magi_attn_plan_create": (ctypes.c_int, [ctypes.POINTER(Layout), ctypes.POINTER(ctypes.c_void_p)]),
+    "magi_attn_cross_plan_create": (ctypes.c_int, [ctypes.POINTER(Layout), ctypes.POINTER(Text),
+                                                   ctypes.POINTER(ctypes.c_void_p)]),
+    "magi_attn_parallel_plan_create": (ctypes.c_int, [ctypes.POINTER(Layout), ctypes.POINTER(Text),
+                                                      ctypes.POINTER(ctypes.c_void_p)]),
     "magi_attn_plan_destroy": (ctypes.c_int, [ctypes.c_void_p]),
     "magi_attn_workspace_size": (ctypes.c_int, [ctypes.c_void_p, ctypes.POINTER(ctypes.c_size_t)]),
     "magi_attn_fwd": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                                      ctypes.c_void_p, ctypes.c_void_p, ctypes.c_float, ctypes.c_float,
                                      ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t,
                                      ctypes.c_void_p]),
+    "magi_attn_fwd_parallel": (ctypes.c_int, [ctypes.c_void_p, ctypes.POINTER(ParallelIO), ctypes.c_float,
+                                              ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]),
     "magi_attn_fwd_simple": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                                             ctypes.c_void_p, _i32p, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
                                             ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p,
@@ -67,6 +102,10 @@ SIGNATURES = {
     "magi_attn_classify_host": (ctypes.c_int, [ctypes.POINTER(Layout), ctypes.c_int32, ctypes.c_int32,
                                                ctypes.POINTER(ctypes.c_int8)]),
     "magi_attn_plan_stats": (ctypes.c_int, [ctypes.POINTER(Layout), ctypes.POINTER(Stats)]),
+    "magi_attn_cross_classify_host": (ctypes.c_int, [ctypes.POINTER(Layout), ctypes.POINTER(Text), ctypes.c_int32,
+                                                     ctypes.c_int32, ctypes.POINTER(ctypes.c_int8)]),
+    "magi_attn_cross_plan_stats": (ctypes.c_int, [ctypes.POINTER(Layout), ctypes.POINTER(Text), ctypes.c_int32,
+                                                  ctypes.POINTER(Stats)]),
     "magi_attn_status_str": (ctypes.c_char_p, [ctypes.c_int]),
     "magi_attn_last_error": (ctypes.c_char_p, []),
     "magi_attn_abi_version": (ctypes.c_int, []),

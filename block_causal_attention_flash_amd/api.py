@@ -45,6 +45,18 @@ class _LayoutArgs:
         return ctypes.byref(self.struct)
 
 
+class _TextArgs:
+    """Keeps the host text-range arrays alive for the duration of a call."""
+
+    def __init__(self, text_begin, text_end, t_text):
+        self.b = _arr(text_begin)
+        self.e = _arr(text_end)
+        self.struct = _abi.Text(int(t_text), self.b.ctypes.data_as(_abi._i32p), self.e.ctypes.data_as(_abi._i32p))
+
+    def ptr(self):
+        return ctypes.byref(self.struct)
+
+
 def magi_attn_abi_version() -> int:
     return _abi.load().magi_attn_abi_version()
 
@@ -70,6 +82,30 @@ def magi_attn_classify_host(q_offsets, kv_offsets=None, seq_chunks=None, bm=128,
     return cls
 
 
+def magi_attn_cross_classify_host(q_offsets, text_begin, text_end, t_text, bm=128, bn=64, kv_offsets=None,
+                                  seq_chunks=None, n_q_heads=1, n_kv_heads=1, head_dim=128, dtype="bf16",
+                                  kv_range=0) -> np.ndarray:
+    lib = _abi.load()
+    la = _LayoutArgs(q_offsets, kv_offsets, seq_chunks, n_q_heads, n_kv_heads, head_dim, dtype, kv_range)
+    ta = _TextArgs(text_begin, text_end, t_text)
+    n_qt, n_kt = -(-int(la.q[-1]) // bm), -(-int(t_text) // bn)
+    cls = np.zeros((max(n_qt, 0), max(n_kt, 0)), dtype=np.int8)
+    _check(lib, lib.magi_attn_cross_classify_host(la.ptr(), ta.ptr(), bm, bn,
+                                                  cls.ctypes.data_as(ctypes.POINTER(ctypes.c_int8))))
+    return cls
+
+
+def magi_attn_cross_plan_stats(q_offsets, text_begin, text_end, t_text, kv_offsets=None, seq_chunks=None,
+                               n_q_heads=1, n_kv_heads=1, head_dim=128, dtype="bf16", kv_range=0,
+                               with_self=False) -> dict:
+    lib = _abi.load()
+    la = _LayoutArgs(q_offsets, kv_offsets, seq_chunks, n_q_heads, n_kv_heads, head_dim, dtype, kv_range)
+    ta = _TextArgs(text_begin, text_end, t_text)
+    st = _abi.Stats()
+    _check(lib, lib.magi_attn_cross_plan_stats(la.ptr(), ta.ptr(), int(bool(with_self)), ctypes.byref(st)))
+    return {name: getattr(st, name) for name, _ in _abi.Stats._fields_}
+
+
 def magi_attn_plan_create(q_offsets, kv_offsets=None, seq_chunks=None, n_q_heads=1, n_kv_heads=1, head_dim=128,
                           dtype="bf16", kv_range=0) -> int:
     """Returns the opaque plan handle (an integer address)."""
@@ -77,6 +113,26 @@ def magi_attn_plan_create(q_offsets, kv_offsets=None, seq_chunks=None, n_q_heads
     la = _LayoutArgs(q_offsets, kv_offsets, seq_chunks, n_q_heads, n_kv_heads, head_dim, dtype, kv_range)
     h = ctypes.c_void_p()
     _check(lib, lib.magi_attn_plan_create(la.ptr(), ctypes.byref(h)))
+    return h.value
+
+
+def magi_attn_cross_plan_create(q_offsets, text_begin, text_end, t_text, kv_offsets=None, seq_chunks=None,
+                                n_q_heads=1, n_kv_heads=1, head_dim=128, dtype="bf16", kv_range=0) -> int:
+    lib = _abi.load()
+    la = _LayoutArgs(q_offsets, kv_offsets, seq_chunks, n_q_heads, n_kv_heads, head_dim, dtype, kv_range)
+    ta = _TextArgs(text_begin, text_end, t_text)
+    h = ctypes.c_void_p()
+    _check(lib, lib.magi_attn_cross_plan_create(la.ptr(), ta.ptr(), ctypes.byref(h)))
+    return h.value
+
+
+def magi_attn_parallel_plan_create(q_offsets, text_begin, text_end, t_text, kv_offsets=None, seq_chunks=None,
+                                   n_q_heads=1, n_kv_heads=1, head_dim=128, dtype="bf16", kv_range=0) -> int:
+    lib = _abi.load()
+    la = _LayoutArgs(q_offsets, kv_offsets, seq_chunks, n_q_heads, n_kv_heads, head_dim, dtype, kv_range)
+    ta = _TextArgs(text_begin, text_end, t_text)
+    h = ctypes.c_void_p()
+    _check(lib, lib.magi_attn_parallel_plan_create(la.ptr(), ta.ptr(), ctypes.byref(h)))
     return h.value
 
 
@@ -137,6 +193,40 @@ def magi_attn_fwd(handle: int, q, k, v, q_gain=None, k_gain=None, rms_eps: float
     return out, lse
 
 
+def magi_attn_fwd_parallel(handle: int, q, k, v, q_x, k_x, v_x, q_gain=None, k_gain=None, q_gain_x=None,
+                           k_gain_x=None, rms_eps: float = 1e-6, scale: Optional[float] = None,
+                           scale_x: Optional[float] = None, out=None, lse=None, out_x=None, lse_x=None,
+                           workspace=None, stream=None):
+    """Enqueues both attentions of a parallel plan on `stream`: the
+    self-attention of q over k/v and the cross-attention of q_x over the text
+    k_x/v_x. Returns (out, lse, out_x, lse_x)."""
+    import torch
+    lib = _abi.load()
+    for name, t in (("q", q), ("k", k), ("v", v), ("q_x", q_x), ("k_x", k_x), ("v_x", v_x)):
+        if not t.is_cuda or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous GPU tensor")
+    d = q.shape[-1]
+    dev = q.device
+    lse_shape = (q.shape[1], q.shape[0])
+    out = torch.empty_like(q) if out is None else out
+    lse = torch.empty(lse_shape, dtype=torch.float32, device=dev) if lse is None else lse
+    out_x = torch.empty_like(q_x) if out_x is None else out_x
+    lse_x = torch.empty(lse_shape, dtype=torch.float32, device=dev) if lse_x is None else lse_x
+    gains = [_gain(g, d, dev) for g in (q_gain, k_gain, q_gain_x, k_gain_x)]
+    sc = (1.0 / d ** 0.5) if scale is None else float(scale)
+    scx = (1.0 / d ** 0.5) if scale_x is None else float(scale_x)
+    need = magi_attn_workspace_size(handle)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
+    ws_bytes = workspace.numel() * workspace.element_size()
+    io = _abi.ParallelIO(q.data_ptr(), k.data_ptr(), v.data_ptr(), gains[0].data_ptr(), gains[1].data_ptr(), sc,
+                         out.data_ptr(), lse.data_ptr(), q_x.data_ptr(), k_x.data_ptr(), v_x.data_ptr(),
+                         gains[2].data_ptr(), gains[3].data_ptr(), scx, out_x.data_ptr(), lse_x.data_ptr())
+    _check(lib, lib.magi_attn_fwd_parallel(handle, ctypes.byref(io), float(rms_eps), workspace.data_ptr(), ws_bytes,
+                                           _stream_ptr(stream, dev)))
+    return out, lse, out_x, lse_x
+
+
 def magi_attn_fwd_simple(q, k, v, chunk_offsets: Sequence[int], q_gain=None, k_gain=None, rms_eps: float = 1e-6,
                          scale: Optional[float] = None, out=None, lse=None, stream=None):
     """One video of self-attention with q/kv offsets = chunk_offsets."""
@@ -173,7 +263,11 @@ class Plan:
         self.t_q = int(self.layout["q_offsets"][-1])
         kv = self.layout["kv_offsets"] or self.layout["q_offsets"]
         self.t_k = int(kv[-1])
-        self.handle = magi_attn_plan_create(**self.layout)
+        self.handle = None
+        self.handle = self._create()
+
+    def _create(self) -> int:
+        return magi_attn_plan_create(**self.layout)
 
     @classmethod
     def from_layout(cls, layout, n_q_heads, n_kv_heads, head_dim, dtype="bf16"):
@@ -186,20 +280,23 @@ class Plan:
     def workspace_size(self) -> int:
         return magi_attn_workspace_size(self.handle)
 
-    def __call__(self, q, k, v, q_gain=None, k_gain=None, rms_eps=1e-6, scale=None, out=None, lse=None,
-                 workspace=None, stream=None):
+    def _check(self, q, k, v, t_k, out, lse):
         import torch
         want = torch.bfloat16 if self.dtype == "bf16" else torch.float32
         if q.dtype != want or k.dtype != want or v.dtype != want:
             raise ValueError(f"q, k, v must be {want}")
         if tuple(q.shape) != (self.t_q, self.n_q_heads, self.head_dim):
             raise ValueError(f"q must have shape {(self.t_q, self.n_q_heads, self.head_dim)}")
-        if tuple(k.shape) != (self.t_k, self.n_kv_heads, self.head_dim) or k.shape != v.shape:
-            raise ValueError(f"k and v must have shape {(self.t_k, self.n_kv_heads, self.head_dim)}")
+        if tuple(k.shape) != (t_k, self.n_kv_heads, self.head_dim) or k.shape != v.shape:
+            raise ValueError(f"k and v must have shape {(t_k, self.n_kv_heads, self.head_dim)}")
         if out is not None and (out.shape != q.shape or out.dtype != want or not out.is_contiguous()):
             raise ValueError("out must match q")
         if lse is not None and (tuple(lse.shape) != (self.n_q_heads, self.t_q) or lse.dtype != torch.float32):
             raise ValueError("lse must be float32 [H_q, T_q]")
+
+    def __call__(self, q, k, v, q_gain=None, k_gain=None, rms_eps=1e-6, scale=None, out=None, lse=None,
+                 workspace=None, stream=None):
+        self._check(q, k, v, self.t_k, out, lse)
         return magi_attn_fwd(self.handle, q, k, v, q_gain, k_gain, rms_eps, scale, out, lse, workspace, stream)
 
     def close(self):
@@ -212,3 +309,57 @@ class Plan:
             self.close()
         except Exception:
             pass
+
+
+class CrossPlan(Plan):
+    """Plan of the text cross-attention alone: call(q, k_text, v_text, ...)
+    with the cross-attention's gains and temperature."""
+
+    def __init__(self, q_offsets, text_begin, text_end, t_text, kv_offsets=None, seq_chunks=None, n_q_heads=1,
+                 n_kv_heads=1, head_dim=128, dtype="bf16", kv_range=0):
+        self.text = dict(text_begin=list(map(int, text_begin)), text_end=list(map(int, text_end)),
+                         t_text=int(t_text))
+        super().__init__(q_offsets, kv_offsets, seq_chunks, n_q_heads, n_kv_heads, head_dim, dtype, kv_range)
+        self.t_k = self.text["t_text"]
+
+    def _create(self) -> int:
+        return magi_attn_cross_plan_create(**self.layout, **self.text)
+
+    @classmethod
+    def from_layout(cls, layout, text, n_q_heads, n_kv_heads, head_dim, dtype="bf16"):
+        return cls(layout.q_offsets, text.begin, text.end, text.t_text, layout.kv_offsets, layout.seq_chunks,
+                   n_q_heads, n_kv_heads, head_dim, dtype, getattr(layout, "kv_range", 0))
+
+    def stats(self) -> dict:
+        return magi_attn_cross_plan_stats(**self.layout, **self.text)
+
+
+class ParallelPlan(Plan):
+    """Plan of the parallel attention block: the self-attention of a layout
+    and the cross-attention of a text, run as one pass by call()."""
+
+    def __init__(self, q_offsets, text_begin, text_end, t_text, kv_offsets=None, seq_chunks=None, n_q_heads=1,
+                 n_kv_heads=1, head_dim=128, dtype="bf16", kv_range=0):
+        self.text = dict(text_begin=list(map(int, text_begin)), text_end=list(map(int, text_end)),
+                         t_text=int(t_text))
+        super().__init__(q_offsets, kv_offsets, seq_chunks, n_q_heads, n_kv_heads, head_dim, dtype, kv_range)
+
+    def _create(self) -> int:
+        return magi_attn_parallel_plan_create(**self.layout, **self.text)
+
+    @classmethod
+    def from_layout(cls, layout, text, n_q_heads, n_kv_heads, head_dim, dtype="bf16"):
+        return cls(layout.q_offsets, text.begin, text.end, text.t_text, layout.kv_offsets, layout.seq_chunks,
+                   n_q_heads, n_kv_heads, head_dim, dtype, getattr(layout, "kv_range", 0))
+
+    def stats(self) -> dict:
+        return magi_attn_cross_plan_stats(**self.layout, **self.text, with_self=True)
+
+    def __call__(self, q, k, v, k_x, v_x, q_x=None, q_gain=None, k_gain=None, q_gain_x=None, k_gain_x=None,
+                 rms_eps=1e-6, scale=None, scale_x=None, out=None, lse=None, out_x=None, lse_x=None, workspace=None,
+                 stream=None):
+        q_x = q if q_x is None else q_x
+        self._check(q, k, v, self.t_k, out, lse)
+        self._check(q_x, k_x, v_x, self.text["t_text"], out_x, lse_x)
+        return magi_attn_fwd_parallel(self.handle, q, k, v, q_x, k_x, v_x, q_gain, k_gain, q_gain_x, k_gain_x,
+                                      rms_eps, scale, scale_x, out, lse, out_x, lse_x, workspace, stream)

@@ -14,7 +14,7 @@
 struct magi_attn_plan {
   magi::HostPlan host;
   int device = 0;
-  void* dmem = nullptr;          // one allocation: items | tile codes | tile copy offsets | row bounds
+  void* dmem = nullptr;          // one allocation: items | tile codes | tile copy offsets | row bounds | merges
   const int4* d_items = nullptr;
   const int* d_tiles = nullptr;
   const unsigned* d_soffs = nullptr;
@@ -39,54 +39,26 @@ bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p
 
 size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
-}  // namespace
-
-extern "C" {
-
-int magi_attn_abi_version(void) { return MAGI_ATTN_ABI_VERSION; }
-
-const char* magi_attn_status_str(magi_status_t s) {
-  switch (s) {
-    case MAGI_OK: return "ok";
-    case MAGI_ERR_INVALID_ARG: return "invalid argument";
-    case MAGI_ERR_UNSUPPORTED: return "unsupported";
-    case MAGI_ERR_NO_MEMORY: return "out of memory";
-    case MAGI_ERR_HIP: return "HIP error";
-  }
-  return "unknown status";
+magi_status_t validate(int32_t kind, const magi_attn_layout_t* layout, const magi_attn_text_t* text,
+                       std::string& err) {
+  magi_status_t s = magi::validate_layout(layout, err);
+  if (s == MAGI_OK && kind != magi::kPlanSelf) s = magi::validate_text(layout, text, kind, err);
+  return s;
 }
 
-const char* magi_attn_last_error(void) { return g_last_error.c_str(); }
-
-magi_status_t magi_attn_classify_host(const magi_attn_layout_t* layout, int32_t bm, int32_t bn, int8_t* cls) {
-  std::string err;
-  magi_status_t s = magi::validate_layout(layout, err);
-  if (s != MAGI_OK) return fail(s, err);
-  if (bm < 1 || bn < 1) return fail(MAGI_ERR_INVALID_ARG, "tile sizes must be positive");
-  if (!cls) return fail(MAGI_ERR_INVALID_ARG, "cls is NULL");
-  std::vector<magi::RowBounds> rows;
-  magi::row_bounds(layout, rows);
-  const int32_t* kv = layout->kv_offsets ? layout->kv_offsets : layout->q_offsets;
-  const int64_t tq = layout->q_offsets[layout->n_chunks], tk = kv[layout->n_chunks];
-  const int64_t n_qt = (tq + bm - 1) / bm, n_kt = (tk + bn - 1) / bn;
-  std::vector<magi::RowBounds> iv;
-  for (int64_t qt = 0; qt < n_qt; ++qt) {
-    magi::tile_intervals(rows, qt * bm, std::min<int64_t>(tq, qt * bm + bm), iv);
-    for (int64_t kt = 0; kt < n_kt; ++kt)
-      cls[qt * n_kt + kt] = int8_t(magi::classify_pair(iv, kt * bn, kt * bn + bn, tk));
-  }
-  return MAGI_OK;
+magi::Tiling tiling_of(const magi_attn_layout_t* L) {
+  return magi::choose_tiling(L->dtype, L->head_dim, L->n_q_heads / L->n_kv_heads);
 }
 
-magi_status_t magi_attn_plan_stats(const magi_attn_layout_t* layout, magi_attn_stats_t* stats) {
+magi_status_t plan_stats(int32_t kind, const magi_attn_layout_t* layout, const magi_attn_text_t* text,
+                         magi_attn_stats_t* stats) {
   std::string err;
-  magi_status_t s = magi::validate_layout(layout, err);
+  magi_status_t s = validate(kind, layout, text, err);
   if (s != MAGI_OK) return fail(s, err);
   if (!stats) return fail(MAGI_ERR_INVALID_ARG, "stats is NULL");
   magi::HostPlan hp;
-  const magi::Tiling t = magi::choose_tiling(layout->dtype, layout->head_dim, layout->n_q_heads / layout->n_kv_heads);
   try {
-    s = magi::build_host_plan(layout, t, hp, err);
+    s = magi::build_host_plan(kind, layout, text, tiling_of(layout), hp, err);
   } catch (const std::bad_alloc&) {
     return fail(MAGI_ERR_NO_MEMORY, "host allocation failed");
   }
@@ -95,17 +67,29 @@ magi_status_t magi_attn_plan_stats(const magi_attn_layout_t* layout, magi_attn_s
   return MAGI_OK;
 }
 
-magi_status_t magi_attn_plan_create(const magi_attn_layout_t* layout, magi_attn_plan_t** out_plan) {
+// Classes of every (query tile, key tile) pair for per-row key bounds.
+void classify_rows(const std::vector<magi::RowBounds>& rows, int64_t tq, int64_t tk, int32_t bm, int32_t bn,
+                   int8_t* cls) {
+  const int64_t n_qt = (tq + bm - 1) / bm, n_kt = (tk + bn - 1) / bn;
+  std::vector<magi::RowBounds> iv;
+  for (int64_t qt = 0; qt < n_qt; ++qt) {
+    magi::tile_intervals(rows, qt * bm, std::min<int64_t>(tq, qt * bm + bm), iv);
+    for (int64_t kt = 0; kt < n_kt; ++kt)
+      cls[qt * n_kt + kt] = int8_t(magi::classify_pair(iv, kt * bn, kt * bn + bn, tk));
+  }
+}
+
+magi_status_t create_plan(int32_t kind, const magi_attn_layout_t* layout, const magi_attn_text_t* text,
+                          magi_attn_plan_t** out_plan) {
   if (!out_plan) return fail(MAGI_ERR_INVALID_ARG, "plan output pointer is NULL");
   *out_plan = nullptr;
   std::string err;
-  magi_status_t s = magi::validate_layout(layout, err);
+  magi_status_t s = validate(kind, layout, text, err);
   if (s != MAGI_OK) return fail(s, err);
   magi_attn_plan* p = new (std::nothrow) magi_attn_plan();
   if (!p) return fail(MAGI_ERR_NO_MEMORY, "host allocation failed");
-  const magi::Tiling t = magi::choose_tiling(layout->dtype, layout->head_dim, layout->n_q_heads / layout->n_kv_heads);
   try {
-    s = magi::build_host_plan(layout, t, p->host, err);
+    s = magi::build_host_plan(kind, layout, text, tiling_of(layout), p->host, err);
   } catch (const std::bad_alloc&) {
     delete p;
     return fail(MAGI_ERR_NO_MEMORY, "host allocation failed");
@@ -149,6 +133,129 @@ magi_status_t magi_attn_plan_create(const magi_attn_layout_t* layout, magi_attn_
   return MAGI_OK;
 }
 
+// k and v may be NULL when their key stream is empty (tk == 0).
+magi_status_t check_tensors(const void* q, const void* k, const void* v, const float* q_gain, const float* k_gain,
+                            float scale, void* out, float* lse, int64_t tk) {
+  if (!q || !out || !lse || !q_gain || !k_gain || (tk > 0 && (!k || !v)))
+    return fail(MAGI_ERR_INVALID_ARG, "NULL tensor pointer");
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16))
+    return fail(MAGI_ERR_INVALID_ARG, "q, k, v and out must be 16-byte aligned");
+  if (!aligned(lse, 4) || !aligned(q_gain, 16) || !aligned(k_gain, 16))
+    return fail(MAGI_ERR_INVALID_ARG, "lse must be 4-byte and the gains 16-byte aligned");
+  if (!(scale > 0.0f) || !std::isfinite(scale)) return fail(MAGI_ERR_INVALID_ARG, "scale must be finite and > 0");
+  return MAGI_OK;
+}
+
+magi_status_t check_workspace(const magi_attn_plan_t* plan, void* workspace, size_t workspace_bytes) {
+  size_t need = 0;
+  magi_attn_workspace_size(plan, &need);
+  if (workspace_bytes < need) return fail(MAGI_ERR_INVALID_ARG, "workspace smaller than magi_attn_workspace_size()");
+  if (need && (!workspace || !aligned(workspace, 16)))
+    return fail(MAGI_ERR_INVALID_ARG, "workspace must be non-NULL and 16-byte aligned");
+  return MAGI_OK;
+}
+
+// Common launch fields of a plan.
+magi::FwdParams plan_params(const magi_attn_plan_t* plan, float rms_eps, void* workspace) {
+  const auto& H = plan->host;
+  magi::FwdParams prm{};
+  prm.ws = workspace;
+  prm.items = plan->d_items;
+  prm.tiles = plan->d_tiles;
+  prm.soffs = plan->d_soffs;
+  prm.rows = plan->d_rows;
+  prm.merges = plan->d_merges;
+  prm.eps = rms_eps;
+  prm.tq = int(H.tq);
+  prm.tk = int(H.tk);
+  prm.tkx = int(H.tk_x);
+  prm.n_kt_img = int(H.n_kt_img);
+  prm.hq = H.hq;
+  prm.hk = H.hk;
+  prm.tile_q = H.tiling.tile_q;
+  prm.heads_per_item = H.tiling.heads_per_item;
+  return prm;
+}
+
+magi_status_t launch(const magi_attn_plan_t* plan, const magi::FwdParams& prm, void* stream) {
+  const auto& H = plan->host;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const int n = int(H.items.size()), nm = int(H.merges.size());
+  hipError_t e;
+  if (H.dtype == MAGI_DTYPE_BF16) e = magi::launch_fwd_bf16_d128(prm, n, nm, H.n_slots, st);
+  else e = magi::launch_fwd_fp32(prm, H.d, n, nm, st);
+  if (e != hipSuccess) return hip_fail(e, "kernel launch");
+  return MAGI_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int magi_attn_abi_version(void) { return MAGI_ATTN_ABI_VERSION; }
+
+const char* magi_attn_status_str(magi_status_t s) {
+  switch (s) {
+    case MAGI_OK: return "ok";
+    case MAGI_ERR_INVALID_ARG: return "invalid argument";
+    case MAGI_ERR_UNSUPPORTED: return "unsupported";
+    case MAGI_ERR_NO_MEMORY: return "out of memory";
+    case MAGI_ERR_HIP: return "HIP error";
+  }
+  return "unknown status";
+}
+
+const char* magi_attn_last_error(void) { return g_last_error.c_str(); }
+
+magi_status_t magi_attn_classify_host(const magi_attn_layout_t* layout, int32_t bm, int32_t bn, int8_t* cls) {
+  std::string err;
+  magi_status_t s = magi::validate_layout(layout, err);
+  if (s != MAGI_OK) return fail(s, err);
+  if (bm < 1 || bn < 1) return fail(MAGI_ERR_INVALID_ARG, "tile sizes must be positive");
+  if (!cls) return fail(MAGI_ERR_INVALID_ARG, "cls is NULL");
+  std::vector<magi::RowBounds> rows;
+  magi::row_bounds(layout, rows);
+  const int32_t* kv = layout->kv_offsets ? layout->kv_offsets : layout->q_offsets;
+  classify_rows(rows, layout->q_offsets[layout->n_chunks], kv[layout->n_chunks], bm, bn, cls);
+  return MAGI_OK;
+}
+
+magi_status_t magi_attn_cross_classify_host(const magi_attn_layout_t* layout, const magi_attn_text_t* text,
+                                            int32_t bm, int32_t bn, int8_t* cls) {
+  std::string err;
+  magi_status_t s = validate(magi::kPlanCross, layout, text, err);
+  if (s != MAGI_OK) return fail(s, err);
+  if (bm < 1 || bn < 1) return fail(MAGI_ERR_INVALID_ARG, "tile sizes must be positive");
+  if (!cls) return fail(MAGI_ERR_INVALID_ARG, "cls is NULL");
+  std::vector<magi::RowBounds> rows;
+  magi::text_row_bounds(layout, text, rows);
+  classify_rows(rows, layout->q_offsets[layout->n_chunks], text->t_text, bm, bn, cls);
+  return MAGI_OK;
+}
+
+magi_status_t magi_attn_plan_stats(const magi_attn_layout_t* layout, magi_attn_stats_t* stats) {
+  return plan_stats(magi::kPlanSelf, layout, nullptr, stats);
+}
+
+magi_status_t magi_attn_cross_plan_stats(const magi_attn_layout_t* layout, const magi_attn_text_t* text,
+                                         int32_t with_self, magi_attn_stats_t* stats) {
+  return plan_stats(with_self ? magi::kPlanParallel : magi::kPlanCross, layout, text, stats);
+}
+
+magi_status_t magi_attn_plan_create(const magi_attn_layout_t* layout, magi_attn_plan_t** out_plan) {
+  return create_plan(magi::kPlanSelf, layout, nullptr, out_plan);
+}
+
+magi_status_t magi_attn_cross_plan_create(const magi_attn_layout_t* layout, const magi_attn_text_t* text,
+                                          magi_attn_plan_t** out_plan) {
+  return create_plan(magi::kPlanCross, layout, text, out_plan);
+}
+
+magi_status_t magi_attn_parallel_plan_create(const magi_attn_layout_t* layout, const magi_attn_text_t* text,
+                                             magi_attn_plan_t** out_plan) {
+  return create_plan(magi::kPlanParallel, layout, text, out_plan);
+}
+
 magi_status_t magi_attn_plan_destroy(magi_attn_plan_t* plan) {
   if (!plan) return MAGI_OK;
   magi_status_t s = MAGI_OK;
@@ -163,7 +270,7 @@ magi_status_t magi_attn_plan_destroy(magi_attn_plan_t* plan) {
 magi_status_t magi_attn_workspace_size(const magi_attn_plan_t* plan, size_t* bytes) {
   if (!plan || !bytes) return fail(MAGI_ERR_INVALID_ARG, "plan or bytes is NULL");
   const auto& H = plan->host;
-  *bytes = H.dtype == MAGI_DTYPE_BF16 ? magi::workspace_bytes_bf16(H.tk, H.hk, H.d, H.n_slots) : 0;
+  *bytes = H.dtype == MAGI_DTYPE_BF16 ? magi::workspace_bytes_bf16(H.n_kt_img, H.hk, H.n_slots) : 0;
   return MAGI_OK;
 }
 
@@ -172,50 +279,62 @@ magi_status_t magi_attn_fwd(const magi_attn_plan_t* plan, const void* q, const v
                             float* lse, void* workspace, size_t workspace_bytes, void* stream) {
   if (!plan) return fail(MAGI_ERR_INVALID_ARG, "plan is NULL");
   const auto& H = plan->host;
-  if (H.items.empty()) return MAGI_OK;                     // no query token: nothing to do
-  size_t need = 0;
-  magi_attn_workspace_size(plan, &need);
-  if (workspace_bytes < need) return fail(MAGI_ERR_INVALID_ARG, "workspace smaller than magi_attn_workspace_size()");
-  if (need && (!workspace || !aligned(workspace, 16)))
-    return fail(MAGI_ERR_INVALID_ARG, "workspace must be non-NULL and 16-byte aligned");
-  if (!q || !k || !v || !out || !lse || !q_gain || !k_gain)
-    return fail(MAGI_ERR_INVALID_ARG, "NULL tensor pointer");
-  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16))
-    return fail(MAGI_ERR_INVALID_ARG, "q, k, v and out must be 16-byte aligned");
-  if (!aligned(lse, 4) || !aligned(q_gain, 16) || !aligned(k_gain, 16))
-    return fail(MAGI_ERR_INVALID_ARG, "lse must be 4-byte and the gains 16-byte aligned");
+  if (H.kind == magi::kPlanParallel)
+    return fail(MAGI_ERR_INVALID_ARG, "a parallel plan runs with magi_attn_fwd_parallel");
+  if (H.items.empty() && H.merges.empty()) return MAGI_OK;    // no query token: nothing to do
+  magi_status_t s = check_workspace(plan, workspace, workspace_bytes);
+  if (s != MAGI_OK) return s;
+  s = check_tensors(q, k, v, q_gain, k_gain, scale, out, lse, H.tk);
+  if (s != MAGI_OK) return s;
   if (!(rms_eps >= 0.0f) || !std::isfinite(rms_eps)) return fail(MAGI_ERR_INVALID_ARG, "rms_eps must be finite and >= 0");
-  if (!(scale > 0.0f) || !std::isfinite(scale)) return fail(MAGI_ERR_INVALID_ARG, "scale must be finite and > 0");
 
-  magi::FwdParams prm{};
+  magi::FwdParams prm = plan_params(plan, rms_eps, workspace);
   prm.q = q;
   prm.k = k;
   prm.v = v;
-  prm.ws = workspace;
   prm.out = out;
   prm.lse = lse;
   prm.q_gain = q_gain;
   prm.k_gain = k_gain;
-  prm.items = plan->d_items;
-  prm.tiles = plan->d_tiles;
-  prm.soffs = plan->d_soffs;
-  prm.rows = plan->d_rows;
-  prm.merges = plan->d_merges;
-  prm.eps = rms_eps;
   prm.scale = scale;
-  prm.tq = int(H.tq);
-  prm.tk = int(H.tk);
-  prm.hq = H.hq;
-  prm.hk = H.hk;
-  prm.tile_q = H.tiling.tile_q;
-  prm.heads_per_item = H.tiling.heads_per_item;
-  hipStream_t st = static_cast<hipStream_t>(stream);
-  const int n = int(H.items.size());
-  hipError_t e;
-  if (H.dtype == MAGI_DTYPE_BF16) e = magi::launch_fwd_bf16_d128(prm, n, int(H.merges.size()), H.n_slots, st);
-  else e = magi::launch_fwd_fp32(prm, H.d, n, st);
-  if (e != hipSuccess) return hip_fail(e, "kernel launch");
-  return MAGI_OK;
+  return launch(plan, prm, stream);
+}
+
+magi_status_t magi_attn_fwd_parallel(const magi_attn_plan_t* plan, const magi_attn_parallel_io_t* io, float rms_eps,
+                                     void* workspace, size_t workspace_bytes, void* stream) {
+  if (!plan) return fail(MAGI_ERR_INVALID_ARG, "plan is NULL");
+  if (!io) return fail(MAGI_ERR_INVALID_ARG, "io is NULL");
+  const auto& H = plan->host;
+  if (H.kind != magi::kPlanParallel)
+    return fail(MAGI_ERR_INVALID_ARG, "magi_attn_fwd_parallel needs a plan from magi_attn_parallel_plan_create");
+  if (H.items.empty() && H.merges.empty()) return MAGI_OK;    // no query token: nothing to do
+  magi_status_t s = check_workspace(plan, workspace, workspace_bytes);
+  if (s != MAGI_OK) return s;
+  s = check_tensors(io->q, io->k, io->v, io->q_gain, io->k_gain, io->scale, io->out, io->lse, H.tk);
+  if (s != MAGI_OK) return s;
+  s = check_tensors(io->q_x, io->k_x, io->v_x, io->q_gain_x, io->k_gain_x, io->scale_x, io->out_x, io->lse_x,
+                    H.tk_x);
+  if (s != MAGI_OK) return s;
+  if (!(rms_eps >= 0.0f) || !std::isfinite(rms_eps)) return fail(MAGI_ERR_INVALID_ARG, "rms_eps must be finite and >= 0");
+
+  magi::FwdParams prm = plan_params(plan, rms_eps, workspace);
+  prm.q = io->q;
+  prm.k = io->k;
+  prm.v = io->v;
+  prm.out = io->out;
+  prm.lse = io->lse;
+  prm.q_gain = io->q_gain;
+  prm.k_gain = io->k_gain;
+  prm.scale = io->scale;
+  prm.qx = io->q_x;
+  prm.kx = io->k_x;
+  prm.vx = io->v_x;
+  prm.outx = io->out_x;
+  prm.lsex = io->lse_x;
+  prm.q_gain_x = io->q_gain_x;
+  prm.k_gain_x = io->k_gain_x;
+  prm.scale_x = io->scale_x;
+  return launch(plan, prm, stream);
 }
 
 magi_status_t magi_attn_fwd_simple(const void* q, const void* k, const void* v, void* out, float* lse,

@@ -24,8 +24,8 @@
 //     P stays in registers.
 // Software pipeline of step i: the MFMAs of S(i) and of P(i-1) V(i-1), with
 // the softmax of S(i-1) into P(i-1) on the vector ALUs between them, and the
-// LDS reads kept ahead of the MFMAs. A workgroup barrier per tile recycles the
-// LDS rings.
+// LDS reads kept ahead of the MFMAs. A workgroup barrier every second tile
+// recycles the LDS rings.
 //
 // Queries are normalised in the prologue (RMS over head_dim, times
 // g_q * g_k * scale * log2 e) and held in registers as bf16 MFMA operands.
@@ -36,6 +36,13 @@
 // rescaling: softmax is invariant to the shift and 2^+-40 lies far inside the
 // fp32/bf16 range. Otherwise the wave keeps a running row maximum and rescales
 // its accumulator only when the maximum has grown by more than 2^8.
+//
+// The same kernel runs the block's text cross-attention (paperlayer §2.2.2,
+// §2.2.3; paper-notes §3.2.2, §3.2.6): only the key stream and the per-row key
+// bounds differ. A work item of phase 1 (parallel plans) takes the second set
+// of queries, gains, temperature and outputs, and key tiles whose images
+// follow the video keys' in the workspace. A row that sees no key (a chunk
+// without text) gets out = 0 and lse = -inf.
 //
 // MFMA lane layouts (v_mfma_f32_16x16x32_bf16, lane l, g = l / 16):
 //   A: A[l % 16][8g + j], B: B[8g + j][l % 16] (j = 0..7), D: D[4g + i][l % 16]
@@ -436,9 +443,10 @@ fwd_bf16_d128_kernel(FwdParams prm, const int4* __restrict__ items, const int* _
   __shared__ __attribute__((aligned(1024))) Smem sm;
   const int4 item = items[2 * blockIdx.x];
   if (item.z == item.w) return;                       // padding item
-  const int2 item2 = reinterpret_cast<const int2*>(items + 2 * blockIdx.x + 1)[0];
+  const int4 item2 = items[2 * blockIdx.x + 1];
   const int n_full = item2.x;
   const int slot = item2.y;                            // >= 0: a piece of a split item
+  const bool px = item2.z != 0;                        // phase 1: the cross-attention of a parallel plan
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
@@ -461,15 +469,15 @@ fwd_bf16_d128_kernel(FwdParams prm, const int4* __restrict__ items, const int* _
   bf16x8 qr[NRB][4];
 #pragma unroll
   for (int rb = 0; rb < NRB; ++rb) {
-    const __bf16* qrow = reinterpret_cast<const __bf16*>(prm.q) + (size_t(tok[rb]) * prm.hq + head[rb]) * D;
+    const __bf16* qrow =
+        reinterpret_cast<const __bf16*>(px ? prm.qx : prm.q) + (size_t(tok[rb]) * prm.hq + head[rb]) * D;
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks)
       qr[rb][ks] = valid[rb] ? *reinterpret_cast<const bf16x8*>(qrow + ks * 32 + g * 8) : bf16x8{};
   }
 
   // ---- K/V copies ahead of the first step
-  const unsigned n_kt = unsigned(prm.tk + BN - 1) / BN;
-  const unsigned img_bytes = n_kt * unsigned(prm.hk) * unsigned(TILE_BYTES);
+  const unsigned img_bytes = unsigned(prm.n_kt_img) * unsigned(prm.hk) * unsigned(TILE_BYTES);
   const LaneOffsets lo = lane_offsets(tid, kvh, lds_addr(&sm.k[0][0]), lds_addr(&sm.v[0][0]));
   LoopCtx ctx;
   ctx.rsk = make_rsrc(prm.ws, img_bytes);
@@ -487,7 +495,9 @@ fwd_bf16_d128_kernel(FwdParams prm, const int4* __restrict__ items, const int* _
     issue_copies(ctx, lo, ctx.soffs[j + 7], (j + 7 + NSTAGE) % NSTAGE, ctx.soffs[j + 6], (j + 6 + NSTAGE) % NSTAGE);
   }
 
-  if (tid < D) sm.gqk[tid] = prm.q_gain[tid] * prm.k_gain[tid] * (prm.scale * kLog2e);
+  if (tid < D)
+    sm.gqk[tid] = px ? prm.q_gain_x[tid] * prm.k_gain_x[tid] * (prm.scale_x * kLog2e)
+                     : prm.q_gain[tid] * prm.k_gain[tid] * (prm.scale * kLog2e);
   wait_vmcnt<11>();                                   // K(0), the oldest of the 12 copies, landed
   __syncthreads();                                     // gqk and K(0) visible
   prefetch_k(0, lo, st);
@@ -513,7 +523,7 @@ fwd_bf16_d128_kernel(FwdParams prm, const int4* __restrict__ items, const int* _
     }
     nq = sum_groups(nq);
     bound_max = fmaxf(bound_max, __builtin_sqrtf(nq) * __builtin_sqrtf(float(D)) * 1.02f);
-    const int2 b = valid[rb] ? rows[tok[rb]] : int2{0, 0};
+    const int2 b = valid[rb] ? rows[(px ? prm.tq : 0) + tok[rb]] : int2{0, 0};
     st.lo[rb] = b.x;
     st.hi[rb] = b.y;
 #pragma unroll
@@ -549,12 +559,15 @@ fwd_bf16_d128_kernel(FwdParams prm, const int4* __restrict__ items, const int* _
     }
     return;
   }
+  __bf16* const obase = reinterpret_cast<__bf16*>(px ? prm.outx : prm.out);
+  float* const lbase = px ? prm.lsex : prm.lse;
 #pragma unroll
   for (int rb = 0; rb < NRB; ++rb) {
     const float lsum = sum_groups(st.lsum[rb]);
     if (valid[rb]) {
-      const float inv = 1.0f / lsum;
-      __bf16* orow = reinterpret_cast<__bf16*>(prm.out) + (size_t(tok[rb]) * prm.hq + head[rb]) * D;
+      const bool any = lsum > 0.0f;                     // false only for a row that sees no key
+      const float inv = any ? 1.0f / lsum : 0.0f;
+      __bf16* orow = obase + (size_t(tok[rb]) * prm.hq + head[rb]) * D;
 #pragma unroll
       for (int db = 0; db < 8; ++db) {
         bf16x4 w;
@@ -564,8 +577,8 @@ fwd_bf16_d128_kernel(FwdParams prm, const int4* __restrict__ items, const int* _
       }
       if (g == 0) {
         const float l2 = __builtin_amdgcn_logf(lsum);   // log2
-        const float lse = stat ? l2 * kLn2 : (st.m[rb] + l2) * kLn2;
-        prm.lse[size_t(head[rb]) * prm.tq + tok[rb]] = lse;
+        const float lse = !any ? kNegInf : stat ? l2 * kLn2 : (st.m[rb] + l2) * kLn2;
+        lbase[size_t(head[rb]) * prm.tq + tok[rb]] = lse;
       }
     }
   }
@@ -574,15 +587,24 @@ fwd_bf16_d128_kernel(FwdParams prm, const int4* __restrict__ items, const int* _
 // Pre-pass: one workgroup per (32-key tile, KV head) writes that tile's two
 // images (layouts above). Keys are RMS-normalised here, once per key:
 // k_hat = k / sqrt(mean_d k^2 + eps) in bf16 (g_k is folded into the
-// queries). Keys past T_k are written as zeros in both images.
+// queries). Keys past the stream's end are written as zeros in both images.
+// Workgroups [0, n0) cover the first key stream (k, v, tk); a parallel
+// plan's text keys (kx, vx, tkx) follow, so image block b is workgroup b.
 constexpr int PP_THREADS = 256;
-__global__ void __launch_bounds__(PP_THREADS) kv_prepare_kernel(const __bf16* __restrict__ k,
-                                                                const __bf16* __restrict__ v,
+__global__ void __launch_bounds__(PP_THREADS) kv_prepare_kernel(const __bf16* __restrict__ k0,
+                                                                const __bf16* __restrict__ v0,
+                                                                const __bf16* __restrict__ k1,
+                                                                const __bf16* __restrict__ v1,
                                                                 unsigned char* __restrict__ kimg,
-                                                                unsigned char* __restrict__ vimg, int tk, int hk,
-                                                                float eps) {
+                                                                unsigned char* __restrict__ vimg, int tk0, int tk1,
+                                                                int n0, int hk, float eps) {
   __shared__ __attribute__((aligned(16))) unsigned char vs[TILE_BYTES];
-  const int kt = blockIdx.x / hk, kvh = blockIdx.x % hk;
+  const bool second = int(blockIdx.x) >= n0;
+  const int b = second ? int(blockIdx.x) - n0 : int(blockIdx.x);
+  const __bf16* const k = second ? k1 : k0;
+  const __bf16* const v = second ? v1 : v0;
+  const int tk = second ? tk1 : tk0;
+  const int kt = b / hk, kvh = b % hk;
   const size_t img = size_t(blockIdx.x) * TILE_BYTES;
   const int tid = threadIdx.x;
 #pragma unroll
@@ -623,13 +645,18 @@ __global__ void __launch_bounds__(PP_THREADS) kv_prepare_kernel(const __bf16* __
   }
 }
 
-// Merge of a split item's pieces (one workgroup per split item): with the
+// Merge of a split item's pieces (one workgroup per merge entry): with the
 // pieces' reference maxima m_s, row sums l_s and unnormalised outputs O_s,
 // M = max m_s, w_s = 2^(m_s - M): out = sum w_s O_s / sum w_s l_s and
-// lse = (M + log2 sum w_s l_s) ln 2. A thread handles 16 dims of one row.
+// lse = (M + log2 sum w_s l_s) ln 2. A thread handles 16 dims of one row. An
+// entry without pieces (rows that see no key) writes out = 0, lse = -inf, as
+// does a row whose pieces saw no key.
 constexpr int MG_THREADS = 256;
 __global__ void __launch_bounds__(MG_THREADS) merge_kernel(FwdParams prm) {
-  const int4 mi = prm.merges[blockIdx.x];
+  const int4 mi = prm.merges[2 * blockIdx.x];
+  const bool px = prm.merges[2 * blockIdx.x + 1].x != 0;
+  __bf16* const obase = reinterpret_cast<__bf16*>(px ? prm.outx : prm.out);
+  float* const lbase = px ? prm.lsex : prm.lse;
   const int h0 = mi.y & 0xffff;
   for (int u = threadIdx.x; u < ROWS * 8; u += MG_THREADS) {
     const int r = u >> 3, c = u & 7;
@@ -648,8 +675,8 @@ __global__ void __launch_bounds__(MG_THREADS) merge_kernel(FwdParams prm) {
 #pragma unroll
       for (int q = 0; q < 4; ++q) acc[q] += w * po[q];
     }
-    const float inv = 1.0f / l;
-    __bf16* orow = reinterpret_cast<__bf16*>(prm.out) + (size_t(tok) * prm.hq + head) * D + c * 16;
+    const float inv = l > 0.0f ? 1.0f / l : 0.0f;
+    __bf16* orow = obase + (size_t(tok) * prm.hq + head) * D + c * 16;
     bf16x8 w0, w1;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
@@ -660,39 +687,41 @@ __global__ void __launch_bounds__(MG_THREADS) merge_kernel(FwdParams prm) {
     }
     reinterpret_cast<bf16x8*>(orow)[0] = w0;
     reinterpret_cast<bf16x8*>(orow)[1] = w1;
-    if (c == 0) prm.lse[size_t(head) * prm.tq + tok] = (mmax + __builtin_amdgcn_logf(l)) * kLn2;
+    if (c == 0) lbase[size_t(head) * prm.tq + tok] = l > 0.0f ? (mmax + __builtin_amdgcn_logf(l)) * kLn2 : kNegInf;
   }
 }
 
-size_t image_bytes_bf16(long long tk, int hk) {
-  const size_t n_kt = size_t((tk + BN - 1) / BN);
-  return n_kt * size_t(hk) * TILE_BYTES;
-}
+size_t image_bytes_bf16(long long n_kt_img, int hk) { return size_t(n_kt_img) * size_t(hk) * TILE_BYTES; }
 
 }  // namespace
 
-size_t workspace_bytes_bf16(long long tk, int hk, int d, int n_slots) {
-  (void)d;
+size_t workspace_bytes_bf16(long long n_kt_img, int hk, int n_slots) {
   // K-hat images, V^T images, partial O, partial (m, l)
-  return 2 * image_bytes_bf16(tk, hk) + size_t(n_slots) * ROWS * (D + 2) * sizeof(float);
+  return 2 * image_bytes_bf16(n_kt_img, hk) + size_t(n_slots) * ROWS * (D + 2) * sizeof(float);
 }
 
 hipError_t launch_fwd_bf16_d128(const FwdParams& prm, int n_items, int n_merges, int n_slots, hipStream_t stream) {
   FwdParams p = prm;
-  p.part_o = reinterpret_cast<float*>(static_cast<unsigned char*>(p.ws) + 2 * image_bytes_bf16(p.tk, p.hk));
+  const size_t img = image_bytes_bf16(p.n_kt_img, p.hk);
+  p.part_o = reinterpret_cast<float*>(static_cast<unsigned char*>(p.ws) + 2 * img);
   p.part_ml = p.part_o + size_t(n_slots) * ROWS * D;
-  const long long n_kt = (p.tk + BN - 1) / BN;
-  if (n_kt > 0) {
-    unsigned char* kimg = static_cast<unsigned char*>(p.ws);
-    unsigned char* vimg = kimg + size_t(n_kt) * size_t(p.hk) * TILE_BYTES;
-    hipLaunchKernelGGL(kv_prepare_kernel, dim3(unsigned(n_kt * p.hk)), dim3(PP_THREADS), 0, stream,
-                       static_cast<const __bf16*>(p.k), static_cast<const __bf16*>(p.v), kimg, vimg, p.tk, p.hk, p.eps);
+  if (n_items > 0) {
+    if (p.n_kt_img > 0) {
+      unsigned char* kimg = static_cast<unsigned char*>(p.ws);
+      const int n0 = (p.tk + BN - 1) / BN * p.hk;
+      hipLaunchKernelGGL(kv_prepare_kernel, dim3(unsigned(p.n_kt_img) * unsigned(p.hk)), dim3(PP_THREADS), 0, stream,
+                         static_cast<const __bf16*>(p.k), static_cast<const __bf16*>(p.v),
+                         static_cast<const __bf16*>(p.kx), static_cast<const __bf16*>(p.vx), kimg, kimg + img, p.tk,
+                         p.tkx, n0, p.hk, p.eps);
+      const hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return e;
+    }
+    hipLaunchKernelGGL(fwd_bf16_d128_kernel, dim3(n_items), dim3(NTHR), 0, stream, p, p.items, p.tiles, p.soffs,
+                       p.rows);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL(fwd_bf16_d128_kernel, dim3(n_items), dim3(NTHR), 0, stream, p, p.items, p.tiles, p.soffs, p.rows);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess || n_merges == 0) return e;
+  if (n_merges == 0) return hipSuccess;
   hipLaunchKernelGGL(merge_kernel, dim3(n_merges), dim3(MG_THREADS), 0, stream, p);
   return hipGetLastError();
 }

@@ -6,7 +6,9 @@
 // 64 query tokens of one query head, one thread per query row. Key tiles of
 // 32 keys are staged in LDS (shared by the 64 rows), normalised there once,
 // and read back as broadcasts. Online softmax in exp2 units with a per-tile
-// rescale.
+// rescale. Work items of phase 1 (parallel plans) run the text
+// cross-attention with the second set of tensors (paperlayer §2.2.2;
+// paper-notes §3.2.2); rows that see no key get out = 0 and lse = -inf.
 #include "kernels.hpp"
 
 namespace magi {
@@ -24,33 +26,36 @@ __global__ void __launch_bounds__(64) fwd_fp32_kernel(FwdParams prm) {
   __shared__ float gk[D];
   const int4 item = prm.items[2 * blockIdx.x];
   if (item.z == item.w) return;
+  const bool px = prm.items[2 * blockIdx.x + 1].z != 0;   // phase 1: the cross-attention of a parallel plan
   const int lane = threadIdx.x;
   const int kvh = item.y >> 16, head = item.y & 0xffff;
   const int t = item.x + lane;
   const bool valid = t < prm.tq;
-  const float* qg = prm.q_gain;
-  for (int d = lane; d < D; d += 64) gk[d] = prm.k_gain[d];
+  const float* qg = px ? prm.q_gain_x : prm.q_gain;
+  const float* kgain = px ? prm.k_gain_x : prm.k_gain;
+  const int tk = px ? prm.tkx : prm.tk;
+  for (int d = lane; d < D; d += 64) gk[d] = kgain[d];
 
   float q[D];
   float o[D];
   {
-    const float* qrow = reinterpret_cast<const float*>(prm.q) + (size_t(t) * prm.hq + head) * D;
+    const float* qrow = reinterpret_cast<const float*>(px ? prm.qx : prm.q) + (size_t(t) * prm.hq + head) * D;
     float ss = 0.0f;
     for (int d = 0; d < D; ++d) {
       q[d] = valid ? qrow[d] : 0.0f;
       ss += q[d] * q[d];
     }
     const float rq = 1.0f / __builtin_sqrtf(ss / D + prm.eps);
-    const float c = prm.scale * kLog2e;
+    const float c = (px ? prm.scale_x : prm.scale) * kLog2e;
     for (int d = 0; d < D; ++d) {
       q[d] = valid ? q[d] * rq * qg[d] * c : 0.0f;
       o[d] = 0.0f;
     }
   }
-  const int2 rb = valid ? prm.rows[t] : int2{0, 0};
+  const int2 rb = valid ? prm.rows[(px ? prm.tq : 0) + t] : int2{0, 0};
   float m = kNegInf, l = 0.0f;
-  const float* kbase = reinterpret_cast<const float*>(prm.k);
-  const float* vbase = reinterpret_cast<const float*>(prm.v);
+  const float* kbase = reinterpret_cast<const float*>(px ? prm.kx : prm.k);
+  const float* vbase = reinterpret_cast<const float*>(px ? prm.vx : prm.v);
 
   for (int ti = item.z; ti < item.w; ++ti) {
     const int code = prm.tiles[ti];
@@ -62,7 +67,7 @@ __global__ void __launch_bounds__(64) fwd_fp32_kernel(FwdParams prm) {
       for (int e = lane; e < BN * D; e += 64) {
         const int j = e / D, d = e % D;
         const int key = kt * BN + j;
-        const bool in = key < prm.tk;
+        const bool in = key < tk;
         const size_t off = (size_t(key) * prm.hk + kvh) * D + d;
         ks[j][d] = in ? kbase[off] : 0.0f;
         vs[j][d] = in ? vbase[off] : 0.0f;
@@ -102,20 +107,49 @@ __global__ void __launch_bounds__(64) fwd_fp32_kernel(FwdParams prm) {
     }
   }
   if (valid) {
-    float* orow = reinterpret_cast<float*>(prm.out) + (size_t(t) * prm.hq + head) * D;
-    const float inv = 1.0f / l;
+    float* orow = reinterpret_cast<float*>(px ? prm.outx : prm.out) + (size_t(t) * prm.hq + head) * D;
+    const bool any = l > 0.0f;                    // false only for a row that sees no key
+    const float inv = any ? 1.0f / l : 0.0f;
     for (int d = 0; d < D; ++d) orow[d] = o[d] * inv;
-    prm.lse[size_t(head) * prm.tq + t] = (m + __builtin_log2f(l)) * kLn2;
+    (px ? prm.lsex : prm.lse)[size_t(head) * prm.tq + t] = any ? (m + __builtin_log2f(l)) * kLn2 : kNegInf;
+  }
+}
+
+// Rows that see no key at all (merge entries without pieces: query tiles of
+// chunks without text): out = 0, lse = -inf. One wave per entry, one thread
+// per row of the entry's tile_q tokens x heads_per_item heads.
+template <int D>
+__global__ void __launch_bounds__(64) fp32_clear_kernel(FwdParams prm) {
+  const int4 mi = prm.merges[2 * blockIdx.x];
+  const bool px = prm.merges[2 * blockIdx.x + 1].x != 0;
+  float* const obase = reinterpret_cast<float*>(px ? prm.outx : prm.out);
+  float* const lbase = px ? prm.lsex : prm.lse;
+  const int h0 = mi.y & 0xffff;
+  for (int r = threadIdx.x; r < prm.tile_q * prm.heads_per_item; r += 64) {
+    const int head = h0 + r / prm.tile_q, t = mi.x + r % prm.tile_q;
+    if (t >= prm.tq) continue;
+    float* orow = obase + (size_t(t) * prm.hq + head) * D;
+    for (int d = 0; d < D; ++d) orow[d] = 0.0f;
+    lbase[size_t(head) * prm.tq + t] = kNegInf;
   }
 }
 
 }  // namespace
 
-hipError_t launch_fwd_fp32(const FwdParams& p, int head_dim, int n_items, hipStream_t stream) {
+hipError_t launch_fwd_fp32(const FwdParams& p, int head_dim, int n_items, int n_merges, hipStream_t stream) {
+  if (n_items > 0) {
+    if (head_dim == 64)
+      hipLaunchKernelGGL(fwd_fp32_kernel<64>, dim3(n_items), dim3(64), 0, stream, p);
+    else
+      hipLaunchKernelGGL(fwd_fp32_kernel<128>, dim3(n_items), dim3(64), 0, stream, p);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  if (n_merges == 0) return hipSuccess;
   if (head_dim == 64)
-    hipLaunchKernelGGL(fwd_fp32_kernel<64>, dim3(n_items), dim3(64), 0, stream, p);
+    hipLaunchKernelGGL(fp32_clear_kernel<64>, dim3(n_merges), dim3(64), 0, stream, p);
   else
-    hipLaunchKernelGGL(fwd_fp32_kernel<128>, dim3(n_items), dim3(64), 0, stream, p);
+    hipLaunchKernelGGL(fp32_clear_kernel<128>, dim3(n_merges), dim3(64), 0, stream, p);
   return hipGetLastError();
 }
 

@@ -21,18 +21,31 @@ struct FwdParams {
   const int4* items;     // WorkItem[n_items], two int4 each
   const int* tiles;      // key tile codes (kt * 2 + masked); lists padded with code -1
   const unsigned* soffs; // parallel to tiles: byte offset of the tile's image block (bf16 path)
-  const int2* rows;      // RowBounds[tq]
-  const int4* merges;    // bf16 path: split items (MergeItem)
+  const int2* rows;      // RowBounds[n_phases * tq]: phase p's bounds of token t at p * tq + t
+  const int4* merges;    // MergeItem[n_merges], two int4 each: split items and key-less rows
   float* part_o;         // bf16 path, set by the launcher: partial O of each slot, [slot][384 rows][d] (workspace)
   float* part_ml;        // bf16 path, set by the launcher: partial (m, l) of each slot, [slot][384 rows][2]
   float eps;
   float scale;           // softmax temperature on <q_hat, k_hat>
   int tq, tk, hq, hk;
   int tile_q, heads_per_item;
+  // Phase 1 of a parallel plan (work items with phase 1): the text
+  // cross-attention's queries, keys/values [tkx][hk][d], gains, temperature
+  // and outputs. Unused by single-phase plans.
+  const void* qx;
+  const void* kx;
+  const void* vx;
+  void* outx;
+  float* lsex;
+  const float* q_gain_x;
+  const float* k_gain_x;
+  float scale_x;
+  int tkx;
+  int n_kt_img;          // bf16 path: key tiles per KV head in the image arrays (phase 0's keys, then phase 1's)
 };
 
 hipError_t launch_fwd_bf16_d128(const FwdParams& p, int n_items, int n_merges, int n_slots, hipStream_t stream);
-size_t workspace_bytes_bf16(long long tk, int hk, int d, int n_slots);
-hipError_t launch_fwd_fp32(const FwdParams& p, int head_dim, int n_items, hipStream_t stream);
+size_t workspace_bytes_bf16(long long n_kt_img, int hk, int n_slots);
+hipError_t launch_fwd_fp32(const FwdParams& p, int head_dim, int n_items, int n_merges, hipStream_t stream);
 
 }  // namespace magi

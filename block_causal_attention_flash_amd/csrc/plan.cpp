@@ -15,6 +15,12 @@
 // longest-first rule orders the workgroups of one GPU, with one bucket per
 // XCD: workgroup i runs on XCD i % 8, so items that stream the same KV head
 // are placed on the same XCD and share its L2.
+//
+// The text cross-attention (paperlayer §2.2.2, §2.2.3; paper-notes §3.2.2,
+// §3.2.6) is one more rule for the same per-row intervals: the rows of chunk
+// c see the text keys [text_begin[c], text_end[c]). A parallel plan holds
+// both attentions as two phases of one work list, so the short text items
+// are ordered after the long self-attention items and fill the launch's tail.
 #include "plan.hpp"
 
 #include "kernels.hpp"
@@ -78,6 +84,33 @@ magi_status_t validate_layout(const magi_attn_layout_t* L, std::string& err) {
   return MAGI_OK;
 }
 
+magi_status_t validate_text(const magi_attn_layout_t* L, const magi_attn_text_t* T, int32_t kind,
+                            std::string& err) {
+  if (!T) { err = "text is NULL"; return MAGI_ERR_INVALID_ARG; }
+  if (T->t_text < 0) { err = "t_text must be >= 0"; return MAGI_ERR_INVALID_ARG; }
+  if (!T->text_begin || !T->text_end) { err = "text_begin and text_end must not be NULL"; return MAGI_ERR_INVALID_ARG; }
+  for (int c = 0; c < L->n_chunks; ++c) {
+    const int32_t b = T->text_begin[c], e = T->text_end[c];
+    if (b < 0 || e < b || e > T->t_text) {
+      err = "chunk " + std::to_string(c) + ": text range must satisfy 0 <= begin <= end <= t_text";
+      return MAGI_ERR_INVALID_ARG;
+    }
+  }
+  const int64_t esize = L->dtype == MAGI_DTYPE_BF16 ? 2 : 4;
+  const int64_t row_bytes = int64_t(L->n_kv_heads) * L->head_dim * esize;
+  auto padded = [&](int64_t t) { return L->dtype == MAGI_DTYPE_BF16 ? (t + 31) / 32 * 32 : t; };
+  if (padded(T->t_text) * row_bytes >= (int64_t(1) << 31)) {
+    err = "text K/V tensors must be smaller than 2 GiB each"; return MAGI_ERR_UNSUPPORTED;
+  }
+  if (kind == kPlanParallel) {
+    const int32_t* kv = L->kv_offsets ? L->kv_offsets : L->q_offsets;
+    if ((padded(kv[L->n_chunks]) + padded(T->t_text)) * row_bytes >= (int64_t(1) << 31)) {
+      err = "video and text keys together must be smaller than 2 GiB"; return MAGI_ERR_UNSUPPORTED;
+    }
+  }
+  return MAGI_OK;
+}
+
 Tiling choose_tiling(int dtype, int head_dim, int group) {
   (void)head_dim;
   Tiling t{};
@@ -110,6 +143,13 @@ void row_bounds(const magi_attn_layout_t* L, std::vector<RowBounds>& rows) {
     }
 }
 
+void text_row_bounds(const magi_attn_layout_t* L, const magi_attn_text_t* T, std::vector<RowBounds>& rows) {
+  rows.assign(L->q_offsets[L->n_chunks], RowBounds{0, 0});
+  for (int c = 0; c < L->n_chunks; ++c)
+    for (int32_t t = L->q_offsets[c]; t < L->q_offsets[c + 1]; ++t)
+      rows[t] = RowBounds{T->text_begin[c], T->text_end[c]};
+}
+
 void tile_intervals(const std::vector<RowBounds>& rows, int64_t r0, int64_t r1, std::vector<RowBounds>& out) {
   out.clear();
   for (int64_t r = r0; r < r1; ++r) {
@@ -123,15 +163,18 @@ int classify_pair(const std::vector<RowBounds>& iv, int64_t k0, int64_t k1, int6
   for (const RowBounds& b : iv) {
     const int64_t lo = b.lo, hi = std::min<int64_t>(b.hi, tk);
     if (!(lo <= k0 && k1 <= hi)) all = false;
-    if (lo < k1 && k0 < hi) any = true;
+    if (lo < hi && lo < k1 && k0 < hi) any = true;    // an empty interval touches nothing
   }
   if (iv.empty()) return 0;
   return all ? 2 : (any ? 1 : 0);
 }
 
-magi_status_t build_host_plan(const magi_attn_layout_t* L, const Tiling& tiling, HostPlan& P, std::string& err) {
+magi_status_t build_host_plan(int32_t kind, const magi_attn_layout_t* L, const magi_attn_text_t* T,
+                              const Tiling& tiling, HostPlan& P, std::string& err) {
   (void)err;
   const int32_t* kv = L->kv_offsets ? L->kv_offsets : L->q_offsets;
+  P.kind = kind;
+  P.n_phases = kind == kPlanParallel ? 2 : 1;
   P.n_chunks = L->n_chunks;
   P.n_seqs = L->n_seqs;
   P.hq = L->n_q_heads;
@@ -139,120 +182,134 @@ magi_status_t build_host_plan(const magi_attn_layout_t* L, const Tiling& tiling,
   P.d = L->head_dim;
   P.dtype = L->dtype;
   P.tq = L->q_offsets[L->n_chunks];
-  P.tk = kv[L->n_chunks];
+  P.tk = kind == kPlanCross ? T->t_text : kv[L->n_chunks];
+  P.tk_x = kind == kPlanParallel ? T->t_text : 0;
   P.tiling = tiling;
-  row_bounds(L, P.rows);
+
+  // Per-phase key bounds of every query token, phase p at p * tq.
+  std::vector<RowBounds> tmp;
+  if (kind == kPlanCross) text_row_bounds(L, T, P.rows);
+  else row_bounds(L, P.rows);
+  if (kind == kPlanParallel) {
+    text_row_bounds(L, T, tmp);
+    P.rows.insert(P.rows.end(), tmp.begin(), tmp.end());
+  }
 
   const int bm = tiling.tile_q, bn = tiling.tile_kv;
   const int64_t n_qt = (P.tq + bm - 1) / bm;
-  const int64_t n_kt = (P.tk + bn - 1) / bn;
   const int group = P.hq / P.hk;
   const int hpw = tiling.heads_per_item;
   const int groups_per_kvh = group / hpw;
+  const int64_t phase_tk[2] = {P.tk, P.tk_x};
+  const int64_t phase_nkt[2] = {(P.tk + bn - 1) / bn, (P.tk_x + bn - 1) / bn};
+  const int64_t phase_img0[2] = {0, phase_nkt[0]};         // first image tile of each phase's keys
+  P.n_kt_img = phase_nkt[0] + (P.n_phases == 2 ? phase_nkt[1] : 0);
 
   magi_attn_stats_t& S = P.stats;
   std::memset(&S, 0, sizeof(S));
   for (const RowBounds& b : P.rows) S.unmasked_pairs += int64_t(b.hi - b.lo);
 
-  P.segs.clear();
-  P.qt_seg.assign(n_qt + 1, 0);
+  const int64_t n_lists = P.n_phases * n_qt;
   P.tile_codes.clear();
-  P.qt_tiles.assign(n_qt + 1, 0);
-  P.qt_ntiles.assign(n_qt, 0);
-  P.qt_full.assign(n_qt, 0);
+  P.qt_tiles.assign(n_lists + 1, 0);
+  P.qt_ntiles.assign(n_lists, 0);
+  P.qt_full.assign(n_lists, 0);
   std::vector<int32_t> masked_codes;
-  std::vector<int64_t> qt_cost(n_qt, 0);
   std::vector<RowBounds> iv;
-  for (int64_t qt = 0; qt < n_qt; ++qt) {
-    const int64_t r0 = qt * bm, r1 = std::min<int64_t>(P.tq, r0 + bm);
-    tile_intervals(P.rows, r0, r1, iv);
-    int64_t lo = INT64_MAX, hi = 0;
-    for (const RowBounds& b : iv) { lo = std::min<int64_t>(lo, b.lo); hi = std::max<int64_t>(hi, b.hi); }
-    P.qt_seg[qt] = int32_t(P.segs.size());
-    P.qt_tiles[qt] = int32_t(P.tile_codes.size());
-    masked_codes.clear();
-    if (hi > lo) {
-      const int64_t kt0 = lo / bn, kt1 = (hi + bn - 1) / bn;
-      int prev = -1;
-      for (int64_t kt = kt0; kt < kt1; ++kt) {
-        const int cls = classify_pair(iv, kt * bn, kt * bn + bn, P.tk);
-        if (cls == 2) ++S.full_pairs;
-        if (cls == 1) ++S.boundary_pairs;
-        if (cls != 0) {
-          const int masked = cls == 1 ? 1 : 0;
-          if (prev == masked && P.segs.back().kt_end == kt) {
-            P.segs.back().kt_end = int32_t(kt + 1);
-          } else {
-            P.segs.push_back(Segment{int32_t(kt), int32_t(kt + 1), masked, 0});
-          }
-          qt_cost[qt] += 1;
-          if (masked) masked_codes.push_back(tile_code(kt, 1));
+  for (int ph = 0; ph < P.n_phases; ++ph) {
+    const std::vector<RowBounds> rows_ph(P.rows.begin() + ph * P.tq, P.rows.begin() + (ph + 1) * P.tq);
+    const int64_t tk = phase_tk[ph];
+    for (int64_t qt = 0; qt < n_qt; ++qt) {
+      const int64_t li = ph * n_qt + qt;
+      const int64_t r0 = qt * bm, r1 = std::min<int64_t>(P.tq, r0 + bm);
+      tile_intervals(rows_ph, r0, r1, iv);
+      int64_t lo = INT64_MAX, hi = 0;
+      for (const RowBounds& b : iv)
+        if (b.hi > b.lo) { lo = std::min<int64_t>(lo, b.lo); hi = std::max<int64_t>(hi, b.hi); }
+      P.qt_tiles[li] = int32_t(P.tile_codes.size());
+      masked_codes.clear();
+      if (hi > lo) {
+        for (int64_t kt = lo / bn; kt < (hi + bn - 1) / bn; ++kt) {
+          const int cls = classify_pair(iv, kt * bn, kt * bn + bn, tk);
+          if (cls == 2) ++S.full_pairs;
+          if (cls == 1) ++S.boundary_pairs;
+          if (cls == 0) continue;
+          if (cls == 1) masked_codes.push_back(tile_code(kt, 1));
           else P.tile_codes.push_back(tile_code(kt, 0));
           S.executed_pairs += (r1 - r0) * int64_t(bn);
-          prev = masked;
-        } else {
-          prev = -1;
         }
       }
+      P.qt_full[li] = int32_t(P.tile_codes.size()) - P.qt_tiles[li];
+      P.tile_codes.insert(P.tile_codes.end(), masked_codes.begin(), masked_codes.end());
+      P.qt_ntiles[li] = int32_t(P.tile_codes.size()) - P.qt_tiles[li];
+      P.tile_codes.insert(P.tile_codes.end(), kTilePad, -1);
     }
-    P.qt_full[qt] = int32_t(P.tile_codes.size()) - P.qt_tiles[qt];
-    P.tile_codes.insert(P.tile_codes.end(), masked_codes.begin(), masked_codes.end());
-    P.qt_ntiles[qt] = int32_t(P.tile_codes.size()) - P.qt_tiles[qt];
-    P.tile_codes.insert(P.tile_codes.end(), kTilePad, -1);
+    S.empty_pairs += n_qt * phase_nkt[ph];
   }
-  P.qt_seg[n_qt] = int32_t(P.segs.size());
-  P.qt_tiles[n_qt] = int32_t(P.tile_codes.size());
-  // Copy offsets of the bf16 path's per-tile image blocks ([tile][KV head]).
+  P.qt_tiles[n_lists] = int32_t(P.tile_codes.size());
+  S.empty_pairs -= S.full_pairs + S.boundary_pairs;
+  // Copy offsets of the bf16 path's per-tile image blocks ([tile][KV head];
+  // phase 1's tiles follow phase 0's).
   const int64_t image_bytes = int64_t(bn) * P.d * 2;
   P.tile_soff.resize(P.tile_codes.size());
-  for (size_t t = 0; t < P.tile_codes.size(); ++t)
-    P.tile_soff[t] = P.tile_codes[t] < 0 ? kNoTileOffset
-                                         : uint32_t(int64_t(P.tile_codes[t] >> 1) * P.hk * image_bytes);
-  S.empty_pairs = n_qt * n_kt - S.full_pairs - S.boundary_pairs;
+  for (int ph = 0; ph < P.n_phases; ++ph)
+    for (int32_t t = P.qt_tiles[ph * n_qt]; t < P.qt_tiles[(ph + 1) * n_qt]; ++t)
+      P.tile_soff[t] = P.tile_codes[t] < 0
+                           ? kNoTileOffset
+                           : uint32_t((phase_img0[ph] + (P.tile_codes[t] >> 1)) * P.hk * image_bytes);
 
-  // Work items: (query tile, KV head, group of hpw query heads), cut into
-  // pieces of their tile list when the layout has too few of them.
-  struct Cand { int64_t cost; int32_t qt, kvh, hg, begin, end, slot; };
-  int64_t n_whole = 0, total_cost = 0;
-  for (int64_t qt = 0; qt < n_qt; ++qt)
-    if (P.qt_ntiles[qt] > 0) {
-      n_whole += int64_t(P.hk) * groups_per_kvh;
-      total_cost += qt_cost[qt] * P.hk * groups_per_kvh;
-    }
-  const bool split = P.dtype == MAGI_DTYPE_BF16 && n_whole > 0 && n_whole < kSplitBelowItems;
-  const int64_t piece = std::max<int64_t>(kMinPieceTiles, (total_cost + kSplitTargetItems - 1) / kSplitTargetItems);
+  // Work items: (phase, query tile, KV head, group of hpw query heads), cut
+  // into pieces of their tile list when the phase has too few of them (the
+  // decision is per phase: a parallel plan's many short text items do not
+  // fill the GPU for the long self-attention items). Query tiles without any
+  // key in a phase become merge entries without pieces (their rows get
+  // out = 0, lse = -inf).
+  struct Cand { int64_t cost; int32_t ph, qt, kvh, hg, begin, end, slot; };
   std::vector<Cand> cands;
-  cands.reserve(size_t(n_whole));
   P.merges.clear();
   P.n_slots = 0;
-  for (int kvh = 0; kvh < P.hk; ++kvh)
-    for (int64_t qt = 0; qt < n_qt; ++qt) {
-      const int32_t nt = P.qt_ntiles[qt];
-      if (nt == 0) continue;
-      const int32_t b0 = P.qt_tiles[qt];
-      const int64_t want = (nt + piece - 1) / piece;                        // pieces of about `piece` tiles
-      const int n_pieces =
-          split ? int(std::max<int64_t>(1, std::min<int64_t>({want, int64_t(kMaxPieces), nt / kMinPieceTiles}))) : 1;
-      for (int hg = 0; hg < groups_per_kvh; ++hg) {
-        if (n_pieces == 1) {
-          cands.push_back(Cand{nt, int32_t(qt), kvh, hg, b0, b0 + nt, -1});
-          continue;
-        }
-        const int h0 = kvh * group + hg * hpw;
-        P.merges.push_back(MergeItem{int32_t(qt * bm), (kvh << 16) | h0, P.n_slots, n_pieces});
-        for (int k = 0; k < n_pieces; ++k) {
-          const int32_t pb = b0 + int32_t(int64_t(nt) * k / n_pieces);
-          const int32_t pe = b0 + int32_t(int64_t(nt) * (k + 1) / n_pieces);
-          cands.push_back(Cand{pe - pb, int32_t(qt), kvh, hg, pb, pe, P.n_slots + k});
-        }
-        P.n_slots += n_pieces;
+  for (int ph = 0; ph < P.n_phases; ++ph) {
+    int64_t n_whole = 0, total_cost = 0;
+    for (int64_t qt = 0; qt < n_qt; ++qt)
+      if (P.qt_ntiles[ph * n_qt + qt] > 0) {
+        n_whole += int64_t(P.hk) * groups_per_kvh;
+        total_cost += int64_t(P.qt_ntiles[ph * n_qt + qt]) * P.hk * groups_per_kvh;
       }
-    }
+    const bool split = P.dtype == MAGI_DTYPE_BF16 && n_whole > 0 && n_whole < kSplitBelowItems;
+    const int64_t piece =
+        std::max<int64_t>(kMinPieceTiles, (total_cost + kSplitTargetItems - 1) / kSplitTargetItems);
+    for (int kvh = 0; kvh < P.hk; ++kvh)
+      for (int64_t qt = 0; qt < n_qt; ++qt) {
+        const int64_t li = ph * n_qt + qt;
+        const int32_t nt = P.qt_ntiles[li];
+        const int32_t b0 = P.qt_tiles[li];
+        const int64_t want = (nt + piece - 1) / piece;                      // pieces of about `piece` tiles
+        const int n_pieces =
+            nt == 0 ? 0
+            : split ? int(std::max<int64_t>(1, std::min<int64_t>({want, int64_t(kMaxPieces), nt / kMinPieceTiles})))
+                    : 1;
+        for (int hg = 0; hg < groups_per_kvh; ++hg) {
+          if (n_pieces == 1) {
+            cands.push_back(Cand{nt, ph, int32_t(qt), kvh, hg, b0, b0 + nt, -1});
+            continue;
+          }
+          const int h0 = kvh * group + hg * hpw;
+          P.merges.push_back(MergeItem{int32_t(qt * bm), (kvh << 16) | h0, P.n_slots, n_pieces, ph, {0, 0, 0}});
+          for (int k = 0; k < n_pieces; ++k) {
+            const int32_t pb = b0 + int32_t(int64_t(nt) * k / n_pieces);
+            const int32_t pe = b0 + int32_t(int64_t(nt) * (k + 1) / n_pieces);
+            cands.push_back(Cand{pe - pb, ph, int32_t(qt), kvh, hg, pb, pe, P.n_slots + k});
+          }
+          P.n_slots += n_pieces;
+        }
+      }
+  }
   // Longest first; among equals, consecutive query tiles and head groups of
   // one KV head stay adjacent so concurrently running workgroups read the
   // same key tiles.
   std::stable_sort(cands.begin(), cands.end(), [](const Cand& a, const Cand& b) {
     if (a.cost != b.cost) return a.cost > b.cost;
+    if (a.ph != b.ph) return a.ph < b.ph;
     if (a.kvh != b.kvh) return a.kvh < b.kvh;
     if (a.qt != b.qt) return a.qt < b.qt;
     return a.hg < b.hg;
@@ -262,9 +319,10 @@ magi_status_t build_host_plan(const magi_attn_layout_t* L, const Tiling& tiling,
   auto make_item = [&](const Cand& c) {
     const int h0 = c.kvh * group + c.hg * hpw;
     // full tiles come first in the list: the piece's share of them
-    const int32_t full_end = P.qt_tiles[c.qt] + P.qt_full[c.qt];
+    const int64_t li = c.ph * n_qt + c.qt;
+    const int32_t full_end = P.qt_tiles[li] + P.qt_full[li];
     const int32_t n_full = std::max<int32_t>(0, std::min<int32_t>(c.end, full_end) - c.begin);
-    return WorkItem{int32_t(c.qt * bm), (c.kvh << 16) | h0, c.begin, c.end, n_full, c.slot, {0, 0}};
+    return WorkItem{int32_t(c.qt * bm), (c.kvh << 16) | h0, c.begin, c.end, n_full, c.slot, c.ph, 0};
   };
   if (P.hk % kNumXcd == 0 || kNumXcd % P.hk == 0) {
     // Each KV head owns a fixed set of XCDs (or each XCD owns a fixed set of
@@ -292,7 +350,7 @@ magi_status_t build_host_plan(const magi_attn_layout_t* L, const Tiling& tiling,
   P.items.reserve(maxlen * kNumXcd);
   for (size_t j = 0; j < maxlen; ++j)
     for (int x = 0; x < kNumXcd; ++x)
-      P.items.push_back(j < queues[x].size() ? queues[x][j] : WorkItem{0, 0, 0, 0, 0, -1, {0, 0}});
+      P.items.push_back(j < queues[x].size() ? queues[x][j] : WorkItem{0, 0, 0, 0, 0, -1, 0, 0});
   // Drop trailing padding.
   while (!P.items.empty() && P.items.back().tile_begin == P.items.back().tile_end) P.items.pop_back();
 

@@ -10,12 +10,18 @@
 
 namespace magi {
 
+// Kinds of plan. A plan has one or two phases, each an attention of the
+// query stream over one key stream: a self plan has the block-causal
+// self-attention, a cross plan the text cross-attention, and a parallel plan
+// both (phase 0 self, phase 1 cross) in one launch.
+enum PlanKind : int32_t { kPlanSelf = 0, kPlanCross = 1, kPlanParallel = 2 };
+
 // One workgroup's work: query tokens [t0, t0 + tile_q) of `heads_per_item`
 // consecutive query heads starting at h0, all of KV head kvh, over the key
-// tiles whose codes are tile_codes[tile_begin, tile_end); the first n_full of
-// them are full tiles, the rest boundary tiles. Every list is followed by
-// kTilePad padding entries (code -1, copy offset kNoTileOffset), so a kernel
-// may read that far past tile_end.
+// tiles of phase `phase` whose codes are tile_codes[tile_begin, tile_end);
+// the first n_full of them are full tiles, the rest boundary tiles. Every
+// list is followed by kTilePad padding entries (code -1, copy offset
+// kNoTileOffset), so a kernel may read that far past tile_end.
 struct WorkItem {
   int32_t t0;
   int32_t heads;       // (kvh << 16) | h0
@@ -23,16 +29,21 @@ struct WorkItem {
   int32_t tile_end;    // == tile_begin: padding item, the workgroup exits at once
   int32_t n_full;
   int32_t slot;        // -1: writes out / lse; else a piece of a split item: writes partial slot `slot`
-  int32_t pad[2];
+  int32_t phase;       // 0 or 1 (parallel plans: 1 = the cross-attention)
+  int32_t pad;
 };
 
 // A split item: its rows (as in WorkItem) and the partial slots
-// [slot0, slot0 + n_pieces) that the merge combines into out / lse.
+// [slot0, slot0 + n_pieces) that the merge combines into out / lse of its
+// phase. n_pieces == 0: rows that see no key at all (cross-attention rows of
+// chunks without text): out = 0 and lse = -inf.
 struct MergeItem {
   int32_t t0;
   int32_t heads;
   int32_t slot0;
   int32_t n_pieces;
+  int32_t phase;
+  int32_t pad[3];
 };
 
 // Split-KV policy (bf16): when a layout has fewer than kSplitBelowItems work
@@ -53,14 +64,6 @@ constexpr uint32_t kNoTileOffset = 0x80000000u;   // past any tile image buffer 
 // Key tile code: kt * 2 + masked (masked = 1 for boundary tiles).
 inline int32_t tile_code(int64_t kt, int masked) { return int32_t(kt * 2 + masked); }
 
-// A run of consecutive key tiles of one class for one query tile.
-struct Segment {
-  int32_t kt_begin;
-  int32_t kt_end;
-  int32_t masked;      // 1: boundary tiles (row-dependent key bounds); 0: full
-  int32_t pad;
-};
-
 // Key bounds of one query token: it attends keys [lo, hi).
 struct RowBounds {
   int32_t lo;
@@ -74,21 +77,25 @@ struct Tiling {
 };
 
 struct HostPlan {
+  int32_t kind = kPlanSelf;
+  int n_phases = 1;
   int n_chunks = 0, n_seqs = 0;
   int hq = 0, hk = 0, d = 0, dtype = 0;
-  int64_t tq = 0, tk = 0;
+  int64_t tq = 0;
+  int64_t tk = 0;                    // keys of phase 0 (the video keys, or the text of a cross plan)
+  int64_t tk_x = 0;                  // keys of phase 1 (parallel plans: the text)
+  int64_t n_kt_img = 0;              // key tiles per KV head in the bf16 image arrays (phase 0's, then phase 1's)
   Tiling tiling{};
-  std::vector<RowBounds> rows;       // [tq]
-  std::vector<Segment> segs;         // all query tiles' segments, concatenated
-  std::vector<int32_t> qt_seg;       // [n_qt + 1] segment range per query tile
-  std::vector<int32_t> tile_codes;   // per query tile: full key tiles ascending, then boundary tiles ascending, then padding
+  std::vector<RowBounds> rows;       // [n_phases * tq]: phase p's bounds of token t at p * tq + t
+  std::vector<int32_t> tile_codes;   // per (phase, query tile): full key tiles ascending, then boundary tiles
+                                     // ascending, then padding; key tile indices are local to the phase's stream
   std::vector<uint32_t> tile_soff;   // parallel to tile_codes (bf16): byte offset of the key tile's image block,
-                                     // kt * hk * tile_kv * d * 2; kNoTileOffset for padding
-  std::vector<int32_t> qt_tiles;     // [n_qt + 1] start of each query tile's list in tile_codes
-  std::vector<int32_t> qt_ntiles;    // [n_qt] key tiles per query tile (padding excluded)
-  std::vector<int32_t> qt_full;      // [n_qt] number of full key tiles per query tile
+                                     // (phase's first image tile + kt) * hk * tile_kv * d * 2; kNoTileOffset for padding
+  std::vector<int32_t> qt_tiles;     // [n_phases * n_qt + 1] start of each (phase, query tile) list in tile_codes
+  std::vector<int32_t> qt_ntiles;    // [n_phases * n_qt] key tiles per list (padding excluded)
+  std::vector<int32_t> qt_full;      // [n_phases * n_qt] number of full key tiles per list
   std::vector<WorkItem> items;       // launch order (XCD-interleaved, padded)
-  std::vector<MergeItem> merges;     // split items
+  std::vector<MergeItem> merges;     // split items and key-less rows
   int32_t n_slots = 0;               // partial slots (pieces of split items)
   magi_attn_stats_t stats{};
 };
@@ -103,15 +110,24 @@ inline int first_visible_chunk(const magi_attn_layout_t* L, int s, int c) {
 // Returns MAGI_OK or an error with a message in `err`.
 magi_status_t validate_layout(const magi_attn_layout_t* layout, std::string& err);
 
+// Checks the text side of a cross or parallel plan against a valid layout.
+magi_status_t validate_text(const magi_attn_layout_t* layout, const magi_attn_text_t* text, int32_t kind,
+                            std::string& err);
+
 // Tiling used by the kernels for a dtype / head_dim / GQA group size.
 Tiling choose_tiling(int dtype, int head_dim, int group);
 
-// Builds the full host plan (the layout must already be valid).
-magi_status_t build_host_plan(const magi_attn_layout_t* layout, const Tiling& tiling, HostPlan& plan,
-                              std::string& err);
+// Builds the full host plan of a kind (layout and text must already be
+// valid; text is unused for kPlanSelf).
+magi_status_t build_host_plan(int32_t kind, const magi_attn_layout_t* layout, const magi_attn_text_t* text,
+                              const Tiling& tiling, HostPlan& plan, std::string& err);
 
-// Per-query-token key bounds [lo, hi) (layout must be valid).
+// Per-query-token key bounds [lo, hi) of the block-causal self-attention
+// (layout must be valid).
 void row_bounds(const magi_attn_layout_t* layout, std::vector<RowBounds>& rows);
+
+// Per-query-token text bounds [begin[c], end[c]) of the cross-attention.
+void text_row_bounds(const magi_attn_layout_t* layout, const magi_attn_text_t* text, std::vector<RowBounds>& rows);
 
 // Class of the pair (query tile rows [r0, r1), key tile [k0, k1)) given the
 // distinct key intervals of those rows: 2 full, 1 boundary, 0 empty.

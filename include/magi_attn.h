@@ -13,12 +13,16 @@
  *     attention ("QK-Norm"), and query heads share key/value heads (GQA);
  *   - paperlayer §2.4.4: keys/values of clean chunks come from a KV cache, so
  *     the key stream may be longer than the query stream.
+ * Beside it, the same library runs the block's text cross-attention
+ * (paperlayer §2.2.2 and §2.2.3; paper-notes §3.2.2 and §3.2.6), alone or
+ * together with the self-attention in one launch: see magi_attn_text_t.
  *
  * Per query token i of chunk c (video s) and query head h, with KV head
  * g = h / (n_q_heads / n_kv_heads):
  *   q_hat = q * q_gain / sqrt(mean_d(q^2) + eps),  k_hat likewise with k_gain,
  *   s_ij  = scale * <q_hat_ih, k_hat_jg> for keys j in
- *           [kv_offsets[seq_chunks[s]], kv_offsets[c + 1]),
+ *           [kv_offsets[f], kv_offsets[c + 1]), f = seq_chunks[s] (with a KV
+ *           range R >= 1: max(seq_chunks[s], c - R + 1)),
  *   out_ih = sum_j softmax_j(s_ij) v_jg,   lse_hi = ln sum_j exp(s_ij).
  *
  * Conventions shared by every entry point:
@@ -50,7 +54,7 @@
 extern "C" {
 #endif
 
-#define MAGI_ATTN_ABI_VERSION 2
+#define MAGI_ATTN_ABI_VERSION 3
 
 typedef enum magi_status {
   MAGI_OK = 0,
@@ -97,6 +101,31 @@ typedef struct magi_attn_layout {
   int32_t kv_range;           /* 0: block-causal; R >= 1: the last R chunks of the video */
 } magi_attn_layout_t;
 
+/*
+ * Text side of the cross-attention (host arrays, read during the call only).
+ * In every transformer block of MAGI-1 the video tokens also attend to the
+ * text condition, beside the self-attention and from the same query
+ * projection, with QK-Norm and GQA (paperlayer §2.2.2; paper-notes §3.2.2:
+ * architecture list, spec table, block pseudocode). Prompts are given per
+ * chunk (paperlayer §2.2.3) and chunks that are already clean carry no text
+ * (paper-notes §3.2.6). For query token i of chunk c and query head h:
+ *   s_ij   = scale_x * <q_hat_ih, k_hat_jg>  for text keys j in [text_begin[c], text_end[c]),
+ *   out_ih = sum_j softmax_j(s_ij) v_jg,     lse_hi = ln sum_j exp(s_ij),
+ * with q_hat, k_hat RMS-normalised as above (with the cross-attention's own
+ * gains) and the values not normalised. A chunk with text_begin[c] ==
+ * text_end[c] has no text: its rows get out = 0 and lse = -inf.
+ *   t_text           : tokens of the packed text stream, >= 0
+ *   text_begin[n_chunks], text_end[n_chunks] : 0 <= begin <= end <= t_text
+ * Text keys/values are [t_text][n_kv_heads][head_dim] (same heads, head_dim
+ * and dtype as the layout); with t_text == 0 their pointers may be NULL.
+ * Several chunks may share one prompt's range.
+ */
+typedef struct magi_attn_text {
+  int32_t t_text;
+  const int32_t* text_begin;
+  const int32_t* text_end;
+} magi_attn_text_t;
+
 typedef struct magi_attn_plan magi_attn_plan_t;   /* opaque */
 
 /*
@@ -114,14 +143,39 @@ typedef struct magi_attn_plan magi_attn_plan_t;   /* opaque */
  */
 MAGI_API magi_status_t magi_attn_plan_create(const magi_attn_layout_t* layout, magi_attn_plan_t** plan);
 
+/*
+ * Plan of the text cross-attention alone, run with magi_attn_fwd, passing
+ * the text keys/values as k and v and the cross-attention's gains and
+ * temperature. The layout is validated as above (its q_offsets, chunks,
+ * heads, head_dim and dtype are used; its kv_offsets and kv_range are not);
+ * the text must satisfy the rules of magi_attn_text_t. Errors as for
+ * magi_attn_plan_create, with the text's K/V under the same 2 GiB limit.
+ */
+MAGI_API magi_status_t magi_attn_cross_plan_create(const magi_attn_layout_t* layout, const magi_attn_text_t* text,
+                                                   magi_attn_plan_t** plan);
+
+/*
+ * Plan of the parallel attention block's two attentions (paperlayer §2.2.2:
+ * self- and cross-attention side by side from one query projection): the
+ * block-causal self-attention of `layout` and the cross-attention of `text`,
+ * run together by magi_attn_fwd_parallel as one pass (one pre-pass over both
+ * key streams, one main-kernel launch holding both attentions' work items).
+ * Errors as for the two plans above; for bf16 the re-laid-out video and text
+ * keys together must stay under 2 GiB.
+ */
+MAGI_API magi_status_t magi_attn_parallel_plan_create(const magi_attn_layout_t* layout,
+                                                      const magi_attn_text_t* text, magi_attn_plan_t** plan);
+
 /* Frees the plan and its device memory (synchronous with respect to the host;
  * the caller must not destroy a plan that queued work still uses). NULL is OK. */
 MAGI_API magi_status_t magi_attn_plan_destroy(magi_attn_plan_t* plan);
 
 /*
- * Device workspace bytes that magi_attn_fwd needs for this plan. bf16: the
- * RMS-normalised keys and the values re-laid out in 32-key tiles,
- * 2 * ceil(T_k / 32) * 32 * n_kv_heads * head_dim * 2 bytes, plus, when the
+ * Device workspace bytes that magi_attn_fwd (or magi_attn_fwd_parallel)
+ * needs for this plan. bf16: the RMS-normalised keys and the values
+ * re-laid out in 32-key tiles, 2 * n_tiles * 32 * n_kv_heads * head_dim * 2
+ * bytes with n_tiles = ceil(T_k / 32) (parallel plans: plus ceil(t_text / 32)),
+ * plus, when the
  * plan splits work items along the key axis (layouts with too few items to
  * fill the GPU), the pieces' partial results, pieces * 384 * (head_dim + 2)
  * * 4 bytes. fp32: 0.
@@ -129,7 +183,9 @@ MAGI_API magi_status_t magi_attn_plan_destroy(magi_attn_plan_t* plan);
 MAGI_API magi_status_t magi_attn_workspace_size(const magi_attn_plan_t* plan, size_t* bytes);
 
 /*
- * Enqueues the forward pass on `stream`: out and lse as defined at the top.
+ * Enqueues the forward pass of a self or cross plan on `stream`: out and lse
+ * as defined at the top (cross plans: as defined at magi_attn_text_t, with
+ * k, v the text keys/values [t_text][n_kv_heads][head_dim]).
  * rms_eps >= 0 is added to mean(x^2) inside the square root; scale > 0 is the
  * softmax temperature applied to <q_hat, k_hat> (1/sqrt(head_dim) usually).
  * `workspace` is caller-owned device memory of at least
@@ -137,8 +193,9 @@ MAGI_API magi_status_t magi_attn_workspace_size(const magi_attn_plan_t* plan, si
  * size is 0); the call overwrites it, so concurrent calls need distinct
  * workspaces. Allocates nothing and never synchronises, so it can be
  * captured in a HIP graph. Errors: MAGI_ERR_INVALID_ARG (NULL/misaligned
- * pointer, workspace too small, bad eps or scale), MAGI_ERR_HIP (launch
- * failure). Device faults surface at the caller's next synchronisation.
+ * pointer, workspace too small, bad eps or scale, a parallel plan),
+ * MAGI_ERR_HIP (launch failure). Device faults surface at the caller's next
+ * synchronisation.
  */
 MAGI_API magi_status_t magi_attn_fwd(const magi_attn_plan_t* plan,
                             const void* q, const void* k, const void* v,
@@ -146,6 +203,47 @@ MAGI_API magi_status_t magi_attn_fwd(const magi_attn_plan_t* plan,
                             float rms_eps, float scale,
                             void* out, float* lse,
                             void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Tensors of one call of the parallel attention block. The self-attention
+ * takes q, k, v, its gains and scale and writes out, lse, as defined at the
+ * top. The cross-attention takes q_x (the same query projection; the pages
+ * apply RoPE to the self-attention branch only, so q_x may differ from q, or
+ * be the same pointer), the text keys/values k_x, v_x
+ * [t_text][n_kv_heads][head_dim], its own gains and scale_x, and writes
+ * out_x [T_q][n_q_heads][head_dim] and lse_x [n_q_heads][T_q]. Alignment and
+ * ownership as for magi_attn_fwd; no output may alias an input or another
+ * output.
+ */
+typedef struct magi_attn_parallel_io {
+  const void* q;
+  const void* k;
+  const void* v;
+  const float* q_gain;
+  const float* k_gain;
+  float scale;
+  void* out;
+  float* lse;
+  const void* q_x;
+  const void* k_x;
+  const void* v_x;
+  const float* q_gain_x;
+  const float* k_gain_x;
+  float scale_x;
+  void* out_x;
+  float* lse_x;
+} magi_attn_parallel_io_t;
+
+/*
+ * Enqueues both attentions of a parallel plan on `stream` as one pass (the
+ * short cross-attention work items fill the tail of the self-attention
+ * launch). rms_eps applies to both normalisations. Workspace, allocation and
+ * synchronisation rules as for magi_attn_fwd. Errors: those of magi_attn_fwd,
+ * and MAGI_ERR_INVALID_ARG for a plan that is not a parallel plan or a NULL io.
+ */
+MAGI_API magi_status_t magi_attn_fwd_parallel(const magi_attn_plan_t* plan, const magi_attn_parallel_io_t* io,
+                                              float rms_eps, void* workspace, size_t workspace_bytes,
+                                              void* stream);
 
 /*
  * One-shot form for a single video of self-attention (q and kv offsets both
@@ -185,6 +283,17 @@ typedef struct magi_attn_stats {
 } magi_attn_stats_t;
 
 MAGI_API magi_status_t magi_attn_plan_stats(const magi_attn_layout_t* layout, magi_attn_stats_t* stats);
+
+/* Host-only: the tile classes of the cross-attention's text mask (as
+ * magi_attn_classify_host, with n_kt = ceil(t_text / bn)). */
+MAGI_API magi_status_t magi_attn_cross_classify_host(const magi_attn_layout_t* layout,
+                                                     const magi_attn_text_t* text, int32_t bm, int32_t bn,
+                                                     int8_t* cls);
+
+/* Host-only summary of a cross plan (with_self == 0) or a parallel plan
+ * (with_self != 0; pair counts are the sums over both attentions). */
+MAGI_API magi_status_t magi_attn_cross_plan_stats(const magi_attn_layout_t* layout, const magi_attn_text_t* text,
+                                                  int32_t with_self, magi_attn_stats_t* stats);
 
 MAGI_API const char* magi_attn_status_str(magi_status_t status);
 MAGI_API const char* magi_attn_last_error(void);

@@ -10,7 +10,8 @@ import numpy as np
 import pytest
 
 import oracle
-from workloads import CONFIGS, Layout, get_config, layout_from_chunks, streaming_layout
+from workloads import (CONFIGS, Layout, chunk_prompts, get_config, layout_from_chunks, prompt_draw, streaming_layout,
+                       text_layout)
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "magi_attn.h")
@@ -33,11 +34,11 @@ def test_abi_version(built_lib):
     from block_causal_attention_flash_amd import magi_attn_abi_version
     hdr = open(os.path.join(ROOT, "include", "magi_attn.h")).read()
     declared = int(re.search(r"#define MAGI_ATTN_ABI_VERSION (\d+)", hdr).group(1))
-    assert magi_attn_abi_version() == declared == 2
+    assert magi_attn_abi_version() == declared == 3
 
 
-def brute_classes(layout, bm, bn):
-    mask = oracle.block_causal_mask(layout)
+def brute_classes(layout, bm, bn, mask=None):
+    mask = oracle.block_causal_mask(layout) if mask is None else mask
     tq, tk = mask.shape
     n_qt, n_kt = -(-tq // bm), -(-tk // bn)
     padded = np.zeros((n_qt * bm, n_kt * bn), dtype=bool)
@@ -171,3 +172,101 @@ def test_streaming_cached_chunks_need_no_queries(built_lib):
     st = magi_attn_plan_stats(lay.q_offsets, lay.kv_offsets, lay.seq_chunks, 24, 8, 128, "bf16")
     assert st["unmasked_pairs"] == 1536 * 1536 * (17 + 18 + 19 + 20)
     assert st["boundary_pairs"] == 0
+
+
+def random_text(rng, lay):
+    n_prompts = int(rng.integers(0, 4))
+    lens = [int(x) for x in rng.integers(1, 80, n_prompts)]
+    choice = [None if (n_prompts == 0 or rng.random() < 0.3) else int(rng.integers(0, n_prompts))
+              for _ in range(lay.n_chunks)]
+    return chunk_prompts(choice, lens)
+
+
+@pytest.mark.parametrize("seed", range(30))
+def test_cross_classifier_matches_text_mask(built_lib, seed):
+    """Tile classes of the cross-attention against the oracle's dense text
+    mask, for random layouts and chunk-wise prompts (shared prompts, chunks
+    without text, ragged prompt lengths)."""
+    from block_causal_attention_flash_amd import magi_attn_cross_classify_host
+    rng = np.random.default_rng(1000 + seed)
+    lay = random_layout(rng)
+    if lay.t_q == 0:
+        pytest.skip("no queries")
+    text = random_text(rng, lay)
+    mask = oracle.text_mask(lay.q_offsets, text)
+    for bm, bn in ((64, 32), (128, 32), (7, 5)):
+        got = magi_attn_cross_classify_host(lay.q_offsets, text.begin, text.end, text.t_text, bm=bm, bn=bn,
+                                            kv_offsets=lay.kv_offsets, seq_chunks=lay.seq_chunks)
+        if text.t_text == 0:
+            assert got.shape[1] == 0
+            continue
+        np.testing.assert_array_equal(got, brute_classes(lay, bm, bn, mask))
+
+
+@pytest.mark.parametrize("name", [c.name for c in CONFIGS])
+def test_cross_and_parallel_stats(built_lib, name):
+    """Pair counts of the workloads' cross-attention against the oracle's
+    closed form; a parallel plan's counts are the sums of its two attentions
+    and it holds every work item of both."""
+    from block_causal_attention_flash_amd import magi_attn_cross_plan_stats, magi_attn_plan_stats
+    c = get_config(name)
+    lay, text = c.layout, text_layout(c)
+    args = (lay.q_offsets, text.begin, text.end, text.t_text, lay.kv_offsets, lay.seq_chunks, c.n_q_heads,
+            c.n_kv_heads, c.head_dim, c.dtype)
+    x = magi_attn_cross_plan_stats(*args)
+    assert x["unmasked_pairs"] == oracle.text_pairs(lay.q_offsets, text)
+    n_qt = -(-lay.t_q // x["tile_q"])
+    assert x["full_pairs"] + x["boundary_pairs"] + x["empty_pairs"] == n_qt * -(-text.t_text // x["tile_kv"])
+    s = magi_attn_plan_stats(lay.q_offsets, lay.kv_offsets, lay.seq_chunks, c.n_q_heads, c.n_kv_heads, c.head_dim,
+                             c.dtype)
+    p = magi_attn_cross_plan_stats(*args, with_self=True)
+    for k in ("unmasked_pairs", "full_pairs", "boundary_pairs", "empty_pairs", "executed_pairs"):
+        assert p[k] == s[k] + x[k], k
+    assert p["n_items"] >= max(s["n_items"], x["n_items"])
+
+
+TEXT_BAD = [
+    (dict(text_begin=[0, 0], text_end=[0, 5], t_text=4), 1),          # end beyond t_text
+    (dict(text_begin=[3, 0], text_end=[2, 0], t_text=4), 1),          # begin after end
+    (dict(text_begin=[-1, 0], text_end=[0, 0], t_text=4), 1),         # negative begin
+    (dict(text_begin=[0, 0], text_end=[0, 0], t_text=-1), 1),         # negative t_text
+    (dict(text_begin=[0, 0], text_end=[0, 0], t_text=1 << 30), 2),    # text K/V of 2 GiB or more
+]
+
+
+@pytest.mark.parametrize("kw,status", TEXT_BAD)
+def test_invalid_text_is_rejected(built_lib, kw, status):
+    from block_causal_attention_flash_amd import (MagiAttnError, magi_attn_cross_plan_create,
+                                                  magi_attn_cross_plan_stats, magi_attn_parallel_plan_create)
+    args = dict(q_offsets=[0, 4, 8], n_q_heads=2, n_kv_heads=1, head_dim=128, dtype="bf16")
+    args.update(kw)
+    for fn in (magi_attn_cross_plan_stats, magi_attn_cross_plan_create, magi_attn_parallel_plan_create):
+        with pytest.raises(MagiAttnError) as e:
+            fn(**args)
+        assert e.value.status == status and e.value.message
+
+
+def test_parallel_plan_size_limit(built_lib):
+    """Video and text keys together are limited to 2 GiB of tile images
+    (bf16): each alone fits, the two together do not."""
+    from block_causal_attention_flash_amd import MagiAttnError, magi_attn_cross_plan_stats
+    tk = 7 * (1 << 20) // 8                        # 0.875 Mi keys x 8 heads x 256 B = 1.75 GiB
+    args = ([0, 16, tk], [0, 0], [0, tk // 4], tk // 4, None, None, 8, 8, 128, "bf16")
+    magi_attn_cross_plan_stats(*args)                          # the text alone: 0.44 GiB
+    with pytest.raises(MagiAttnError) as e:
+        magi_attn_cross_plan_stats(*args, with_self=True)
+    assert e.value.status == 2
+
+
+def test_prompt_draw_structure():
+    """The workload text recipe: clean chunks carry no text, cache chunks
+    carry none, runs of chunks share one prompt."""
+    lay = layout_from_chunks([[5] * 7, [3] * 2, [4]])
+    t = prompt_draw(lay, 1, 3, seed=0, lo=10, hi=12)
+    ranges = list(zip(t.begin, t.end))
+    assert ranges[0] == (0, 0) and ranges[7] == (0, 0) and ranges[9] == (0, 0)
+    assert ranges[1] == ranges[2] == ranges[3] and ranges[4] == ranges[5] == ranges[6] and ranges[1] != ranges[4]
+    assert all(10 <= e - b <= 12 for b, e in ranges if e > b)
+    assert t.t_text == max(t.end)
+    st = prompt_draw(streaming_layout(3, 2, 4), 0, 1, seed=1)
+    assert all(b == e for b, e in zip(st.begin[:3], st.end[:3]))
