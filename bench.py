@@ -1,9 +1,13 @@
 """Benchmark of the block-causal attention forward on one MI355X.
 
-python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--kv-range R] [--no-cpu-baseline]
+python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--kv-range R]
+                [--attention self|cross|parallel] [--no-cpu-baseline]
 
 A step is one forward call (query/key RMSNorm, masked softmax attention, LSE)
-over the whole workload, inputs resident in HBM. The plan (tile
+over the whole workload, inputs resident in HBM: the block-causal
+self-attention by default; with --attention cross the text cross-attention of
+the workload's chunk-wise prompts; with --attention parallel both in one
+launch (their useful FLOPs summed). The plan (tile
 classification and work order) is built once per layout before timing; its
 host time is reported as plan_create_ms. Prints one JSON line.
 
@@ -25,6 +29,8 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 METRIC = "block-causal attn fwd useful TFLOP/s and % bf16 MFMA peak, 1×MI355X"
+METRIC_CROSS = "text cross-attn fwd useful TFLOP/s and % bf16 MFMA peak, 1×MI355X"
+METRIC_PARALLEL = "parallel block-causal self- + text cross-attn fwd useful TFLOP/s and % bf16 MFMA peak, 1×MI355X"
 PEAK_BF16_TFLOPS = 2500.0          # MI355X dense bf16 MFMA, published
 KERNEL_SRC = os.path.join(ROOT, "block_causal_attention_flash_amd", "csrc", "fwd_bf16.hip")
 
@@ -43,6 +49,13 @@ def useful_pairs(layout) -> int:
     return total
 
 
+def useful_text_pairs(layout, text) -> int:
+    """Allowed (query, text key) pairs per head: chunk c's queries times its
+    prompt's length."""
+    return sum((layout.q_offsets[c + 1] - layout.q_offsets[c]) * (text.end[c] - text.begin[c])
+               for c in range(layout.n_chunks))
+
+
 def kernel_hash() -> str:
     """sha256 (16 hex digits) of the kernel source with comments and blank
     space removed, so that the stored counters go stale on code changes only."""
@@ -54,10 +67,11 @@ def kernel_hash() -> str:
     return hashlib.sha256(src.encode()).hexdigest()[:16]
 
 
-def stored_traffic(workload: str):
+def stored_traffic(workload: str, attention: str = "self"):
     """HBM bytes per launch from the committed rocprofv3 counter summary, or
     None when it is missing or was taken on a different kernel source."""
-    path = os.path.join(ROOT, "profiles", f"fwd_bf16_{workload}_traffic.json")
+    suffix = "" if attention == "self" else f"_{attention}"
+    path = os.path.join(ROOT, "profiles", f"fwd_bf16_{workload}{suffix}_traffic.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
@@ -67,9 +81,18 @@ def stored_traffic(workload: str):
     return doc.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(cfg, inp, budget_s: float = 20.0):
-    """Times the fp64 oracle on a bounded sample of query rows (all heads) and
-    converts it to useful TFLOP/s on those rows."""
+def first_visible(lay, c):
+    """First chunk whose keys chunk c sees (its video's first, or with a KV
+    range R the later of that and c - R + 1)."""
+    R = int(getattr(lay, "kv_range", 0))
+    s = next(i for i in range(lay.n_seqs) if lay.seq_chunks[i] <= c < lay.seq_chunks[i + 1])
+    return max(lay.seq_chunks[s], c - R + 1) if R > 0 else lay.seq_chunks[s]
+
+
+def cpu_baseline(cfg, inp, budget_s: float = 20.0, attention: str = "self", text=None, tx=None):
+    """Times the fp64 oracle(s) of the benchmarked attention on a bounded
+    sample of query rows (all heads) and converts it to useful TFLOP/s on
+    those rows."""
     import numpy as np
     import oracle
     try:
@@ -78,7 +101,6 @@ def cpu_baseline(cfg, inp, budget_s: float = 20.0):
     except Exception:  # pragma: no cover
         threads = 1
     lay = cfg.layout
-    R = int(getattr(lay, "kv_range", 0))
     d, hq = cfg.head_dim, cfg.n_q_heads
     rng = np.random.default_rng(0)
     # row blocks of 32 consecutive tokens from randomly chosen chunks
@@ -86,25 +108,28 @@ def cpu_baseline(cfg, inp, budget_s: float = 20.0):
     spent = 0.0
     rows_done = 0
     t_start = time.perf_counter()
-    qc = [(lay.q_offsets[c], lay.q_offsets[c + 1]) for c in range(lay.n_chunks) if lay.q_offsets[c + 1] > lay.q_offsets[c]]
+    qc = [c for c in range(lay.n_chunks) if lay.q_offsets[c + 1] > lay.q_offsets[c]]
     while spent < budget_s and rows_done < lay.t_q:
-        a, b = qc[int(rng.integers(0, len(qc)))]
+        c = qc[int(rng.integers(0, len(qc)))]
+        a, b = lay.q_offsets[c], lay.q_offsets[c + 1]
         r0 = int(rng.integers(a, max(a + 1, b - 32)))
         rows = np.arange(r0, min(b, r0 + 32))
         t0 = time.perf_counter()
-        oracle.attention(inp["q"], inp["k"], inp["v"], inp["q_gain"], inp["k_gain"], cfg.eps, cfg.scale, lay,
-                         rows=rows)
+        if attention in ("self", "parallel"):
+            oracle.attention(inp["q"], inp["k"], inp["v"], inp["q_gain"], inp["k_gain"], cfg.eps, cfg.scale, lay,
+                             rows=rows)
+            flops += 4.0 * d * hq * len(rows) * (lay.kv_offsets[c + 1] - lay.kv_offsets[first_visible(lay, c)])
+        if attention in ("cross", "parallel"):
+            oracle.cross_attention(inp["q"], tx["k_x"], tx["v_x"], tx["q_gain_x"], tx["k_gain_x"], cfg.eps,
+                                   cfg.scale, lay.q_offsets, text, rows=rows)
+            flops += 4.0 * d * hq * len(rows) * (text.end[c] - text.begin[c])
         spent += time.perf_counter() - t0
-        for r in rows:
-            c = next(i for i in range(lay.n_chunks) if lay.q_offsets[i] <= r < lay.q_offsets[i + 1])
-            s = next(i for i in range(lay.n_seqs) if lay.seq_chunks[i] <= c < lay.seq_chunks[i + 1])
-            first = max(lay.seq_chunks[s], c - R + 1) if R > 0 else lay.seq_chunks[s]
-            flops += 4.0 * d * hq * (lay.kv_offsets[c + 1] - lay.kv_offsets[first])
         rows_done += len(rows)
         if time.perf_counter() - t_start > 3 * budget_s:
             break
+    what = {"self": "", "cross": " (cross-attention)", "parallel": " (self- and cross-attention)"}[attention]
     return {"value": flops / spent / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"{rows_done} query rows x {hq} heads of {cfg.name} (blocks of 32 rows), "
+            "sample": f"{rows_done} query rows x {hq} heads of {cfg.name}{what} (blocks of 32 rows), "
                       f"{spent:.1f} s fp64 numpy on the host"}
 
 
@@ -132,6 +157,9 @@ def main():
     ap.add_argument("--workload", default="video480x832")
     ap.add_argument("--kv-range", type=int, default=0,
                     help="KV-range window in chunks (0: every earlier chunk of the video is visible)")
+    ap.add_argument("--attention", choices=("self", "cross", "parallel"), default="self",
+                    help="self: the block-causal self-attention; cross: the text cross-attention of the workload's "
+                         "chunk-wise prompts; parallel: both in one launch")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=20.0)
     ap.add_argument("--copy-probe-mib", type=int, default=0,
@@ -146,38 +174,58 @@ def main():
         sys.exit(2)
 
     import torch
-    from block_causal_attention_flash_amd import Plan
-    from workloads import get_config, make_inputs
+    from block_causal_attention_flash_amd import CrossPlan, ParallelPlan, Plan
+    from workloads import get_config, make_inputs, make_text_inputs, text_layout
 
     cfg = get_config(args.workload)
     if args.kv_range:
         cfg = dataclasses.replace(cfg, layout=dataclasses.replace(cfg.layout, kv_range=args.kv_range))
     lay = cfg.layout
+    mode = args.attention
+    text = text_layout(cfg) if mode != "self" else None
     dev = torch.device("cuda", 0)
     t0 = time.perf_counter()
     inp = make_inputs(lay, cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim, cfg.dtype, cfg.gain_kind, cfg.seed)
+    tx = (make_text_inputs(text, cfg.n_kv_heads, cfg.head_dim, cfg.dtype, cfg.gain_kind, cfg.seed + 100)
+          if text is not None else None)
     gen_s = time.perf_counter() - t0
-    q, k, v = (inp[n].to(dev) for n in ("q", "k", "v"))
-    qg, kg = inp["q_gain"].to(dev), inp["k_gain"].to(dev)
-    out = torch.empty_like(q)
-    lse = torch.empty((cfg.n_q_heads, lay.t_q), dtype=torch.float32, device=dev)
+    g = lambda t: t.to(dev)  # noqa: E731
+    q = g(inp["q"])
+    lse_shape = (cfg.n_q_heads, lay.t_q)
+    out, lse = torch.empty_like(q), torch.empty(lse_shape, dtype=torch.float32, device=dev)
     t0 = time.perf_counter()
-    plan = Plan.from_layout(lay, cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim, cfg.dtype)
+    if mode == "self":
+        plan = Plan.from_layout(lay, cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim, cfg.dtype)
+        k, v, qg, kg = g(inp["k"]), g(inp["v"]), g(inp["q_gain"]), g(inp["k_gain"])
+        step = lambda: plan(q, k, v, qg, kg, cfg.eps, cfg.scale, out=out, lse=lse, stream=stream)  # noqa: E731
+    elif mode == "cross":
+        plan = CrossPlan.from_layout(lay, text, cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim, cfg.dtype)
+        kx, vx, qgx, kgx = g(tx["k_x"]), g(tx["v_x"]), g(tx["q_gain_x"]), g(tx["k_gain_x"])
+        step = lambda: plan(q, kx, vx, qgx, kgx, cfg.eps, cfg.scale, out=out, lse=lse, stream=stream)  # noqa: E731
+    else:
+        plan = ParallelPlan.from_layout(lay, text, cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim, cfg.dtype)
+        k, v, qg, kg = g(inp["k"]), g(inp["v"]), g(inp["q_gain"]), g(inp["k_gain"])
+        kx, vx, qgx, kgx = g(tx["k_x"]), g(tx["v_x"]), g(tx["q_gain_x"]), g(tx["k_gain_x"])
+        out_x, lse_x = torch.empty_like(q), torch.empty(lse_shape, dtype=torch.float32, device=dev)
+        step = lambda: plan(q, k, v, kx, vx, q_gain=qg, k_gain=kg, q_gain_x=qgx, k_gain_x=kgx,  # noqa: E731
+                            rms_eps=cfg.eps, scale=cfg.scale, scale_x=cfg.scale, out=out, lse=lse, out_x=out_x,
+                            lse_x=lse_x, stream=stream)
     plan_ms = (time.perf_counter() - t0) * 1e3
     stats = plan.stats()
-    print(f"[bench] {cfg.name}: T_q={lay.t_q} T_k={lay.t_k} heads {cfg.n_q_heads}/{cfg.n_kv_heads} "
+    print(f"[bench] {cfg.name} ({mode}): T_q={lay.t_q} T_k={lay.t_k}"
+          f"{'' if text is None else f' T_text={text.t_text}'} heads {cfg.n_q_heads}/{cfg.n_kv_heads} "
           f"items={stats['n_items']} gen={gen_s:.1f}s plan={plan_ms:.1f}ms", file=sys.stderr, flush=True)
 
     stream = torch.cuda.current_stream(dev)
     for _ in range(args.warmup):
-        plan(q, k, v, qg, kg, cfg.eps, cfg.scale, out=out, lse=lse, stream=stream)
+        step()
     torch.cuda.synchronize()
     ev0 = torch.cuda.Event(enable_timing=True)
     ev1 = torch.cuda.Event(enable_timing=True)
     wall0 = time.perf_counter()
     ev0.record(stream)
     for _ in range(args.steps):
-        plan(q, k, v, qg, kg, cfg.eps, cfg.scale, out=out, lse=lse, stream=stream)
+        step()
     ev1.record(stream)
     torch.cuda.synchronize()
     wall_ms = (time.perf_counter() - wall0) * 1e3 / args.steps
@@ -185,20 +233,27 @@ def main():
     print(f"[bench] {args.steps} steps: {ms:.3f} ms/step (events), {wall_ms:.3f} ms/step (host wall)",
           file=sys.stderr, flush=True)
 
-    pairs = useful_pairs(lay)
-    flops = 4.0 * cfg.head_dim * cfg.n_q_heads * pairs
+    pairs = useful_pairs(lay) if mode != "cross" else 0
+    pairs_x = useful_text_pairs(lay, text) if mode != "self" else 0
+    flops = 4.0 * cfg.head_dim * cfg.n_q_heads * (pairs + pairs_x)
     tflops = flops / (ms * 1e-3) / 1e12
-    traffic = stored_traffic(cfg.name) if not lay.kv_range else None
+    traffic = stored_traffic(cfg.name, mode) if not lay.kv_range else None
     roof = {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
             "frac": round(tflops / PEAK_BF16_TFLOPS, 4), "traffic": traffic}
 
     cpu = None
     if not args.no_cpu_baseline:
         print(f"[bench] timing the CPU oracle on a sample (~{args.cpu_budget:.0f} s)", file=sys.stderr, flush=True)
-        cpu = cpu_baseline(cfg, inp, args.cpu_budget)
+        cpu = cpu_baseline(cfg, inp, args.cpu_budget, mode, text, tx)
 
+    config = {"workload": cfg.name, "attention": mode, "t_q": lay.t_q, "t_k": lay.t_k, "n_chunks": lay.n_chunks,
+              "n_videos": lay.n_seqs, "n_q_heads": cfg.n_q_heads, "n_kv_heads": cfg.n_kv_heads,
+              "head_dim": cfg.head_dim, "kv_range": lay.kv_range, "useful_flops": flops,
+              "unmasked_pairs_per_head": pairs}
+    if text is not None:
+        config.update({"t_text": text.t_text, "text_pairs_per_head": pairs_x})
     rec = {
-        "metric": METRIC,
+        "metric": METRIC if mode == "self" else METRIC_CROSS if mode == "cross" else METRIC_PARALLEL,
         "value": round(tflops, 2),
         "unit": "TFLOP/s",
         "n_gpus": 1,
@@ -211,10 +266,7 @@ def main():
         "dtype": cfg.dtype,
         "data": "synthetic (seeded N(0,1) Q/K/V, unit QK-norm gains)" if cfg.gain_kind == "ones" else
                 "synthetic (seeded N(0,1) Q/K/V, QK-norm gains U(0.5,1.5))",
-        "config": {"workload": cfg.name, "t_q": lay.t_q, "t_k": lay.t_k, "n_chunks": lay.n_chunks,
-                   "n_videos": lay.n_seqs, "n_q_heads": cfg.n_q_heads, "n_kv_heads": cfg.n_kv_heads,
-                   "head_dim": cfg.head_dim, "kv_range": lay.kv_range, "useful_flops": flops,
-                   "unmasked_pairs_per_head": pairs},
+        "config": config,
         "frac_of_peak": round(tflops / PEAK_BF16_TFLOPS, 4),
         "plan_create_ms": round(plan_ms, 2),
         "roofline": roof,

@@ -51,3 +51,10 @@ def test_more_than_one_gpu_is_refused(monkeypatch, capsys):
         bench.main()
     assert e.value.code == 2
     assert "one GPU" in capsys.readouterr().err
+
+
+def test_useful_text_pairs_match_oracle():
+    from workloads import text_layout
+    for c in CONFIGS:
+        t = text_layout(c)
+        assert bench.useful_text_pairs(c.layout, t) == oracle.text_pairs(c.layout.q_offsets, t), c.name
