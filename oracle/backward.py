@@ -1,0 +1,89 @@
+"""fp64 CPU oracle of the backward pass of block-causal QK-RMSNorm GQA attention.
+
+TEST INFRASTRUCTURE ONLY. Nothing on the product path may import, call or
+execute this module: only the tests, the smoke check and the benchmark's CPU
+baseline leg use it. It shares no code with the HIP library.
+
+What is differentiated is the forward of oracle.dense (the MAGI-1 pages:
+paperlayer §2 / Figure 1 and §2.2.2, paper-notes §3.2.2 and Figure 15), whose
+training needs the gradients of the attention (paperlayer §4.1 and §B.1:
+MagiAttention's kernel runs the backward from the forward's saved softmax
+statistics). For the upstream gradient dO of out:
+
+  forward    u = x / r,  r = sqrt(mean_d(x^2) + eps),  x_hat = u * g       (q and k)
+             s_ij = scale <q_hat_i, k_hat_j> on allowed pairs,  P = softmax_j(s),  O = P V
+  backward   dP_ij = <dO_i, v_j>
+             dS_ij = P_ij (dP_ij - sum_l P_il dP_il)          (softmax Jacobian)
+             dq_hat_i = scale sum_j dS_ij k_hat_j
+             dk_hat_j = scale sum_i dS_ij q_hat_i              (over every query head of j's group)
+             dv_j     = sum_i P_ij dO_i                        (likewise)
+             dx = (g * dx_hat - u * mean_d(u * g * dx_hat)) / r (RMSNorm, per token and head)
+             dg = sum over tokens and heads of u * dx_hat      (one gain vector per tensor)
+
+Every function below is that chain rule written out without tiling.
+"""
+from __future__ import annotations
+
+from typing import Tuple
+
+import numpy as np
+
+from . import dense
+
+
+def softmax_backward(p: np.ndarray, dp: np.ndarray) -> np.ndarray:
+    """dS = P * (dP - rowsum(P * dP)): the Jacobian of a row softmax applied
+    to dP. Masked entries have P = 0 and get dS = 0."""
+    return p * (dp - np.sum(p * dp, axis=-1, keepdims=True))
+
+
+def rms_norm_backward(u: np.ndarray, r: np.ndarray, gain: np.ndarray, dxh: np.ndarray) -> np.ndarray:
+    """Gradient of x -> x * gain / sqrt(mean(x^2) + eps) with respect to x,
+    given u = x / r and the gradient dxh of the output."""
+    t = gain * dxh
+    return (t - u * np.mean(u * t, axis=-1, keepdims=True)) / r
+
+
+def gain_gradient(u: np.ndarray, dxh: np.ndarray) -> np.ndarray:
+    """Gradient of the shared gain vector: u * dxh summed over tokens and heads."""
+    return np.sum(u * dxh, axis=(0, 1))
+
+
+def attention_backward(q, k, v, q_gain, k_gain, eps: float, scale: float, layout, dout, row_block: int = 256
+                       ) -> Tuple[np.ndarray, np.ndarray, np.ndarray, np.ndarray, np.ndarray]:
+    """Returns dq [T_q,H_q,d], dk, dv [T_k,H_kv,d], dq_gain, dk_gain [d] (fp64)."""
+    q = dense._as_f64(q)
+    k = dense._as_f64(k)
+    v = dense._as_f64(v)
+    do = dense._as_f64(dout)
+    gq = dense._as_f64(q_gain)
+    gk = dense._as_f64(k_gain)
+    tq, hq, d = q.shape
+    hk = k.shape[1]
+    group = hq // hk
+    rq = np.sqrt(np.mean(q * q, axis=-1, keepdims=True) + eps)
+    rk = np.sqrt(np.mean(k * k, axis=-1, keepdims=True) + eps)
+    uq, uk = q / rq, k / rk
+    qh, kh = uq * gq, uk * gk
+    dqh = np.zeros_like(q)
+    dkh = np.zeros_like(k)
+    dv = np.zeros_like(v)
+    for r0 in range(0, tq, row_block):
+        rows = np.arange(r0, min(tq, r0 + row_block))
+        mask = dense.block_causal_mask(layout, rows)
+        live = mask.any(axis=1)
+        for h in range(hq):
+            g = h // group
+            s = scale * (qh[rows, h, :] @ kh[:, g, :].T)
+            s = np.where(mask, s, -np.inf)
+            m = np.max(np.where(live[:, None], s, 0.0), axis=1, keepdims=True)
+            e = np.where(mask, np.exp(s - m), 0.0)
+            p = e / np.maximum(np.sum(e, axis=1, keepdims=True), np.finfo(np.float64).tiny)
+            dp = do[rows, h, :] @ v[:, g, :].T
+            ds = softmax_backward(p, dp)
+            dqh[rows, h, :] = scale * (ds @ kh[:, g, :])
+            dkh[:, g, :] += scale * (ds.T @ qh[rows, h, :])
+            dv[:, g, :] += p.T @ do[rows, h, :]
+    dq = rms_norm_backward(uq, rq, gq, dqh)
+    dk = rms_norm_backward(uk, rk, gk, dkh)
+    return dq, dk, dv, gain_gradient(uq, dqh), gain_gradient(uk, dkh)
