@@ -66,6 +66,11 @@ class ParallelIO(ctypes.Structure):
     ]
 
 
+class BwdIO(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in ("q", "k", "v", "q_gain", "k_gain", "out", "lse", "dout", "dq", "dk",
+                                               "dv", "dq_gain", "dk_gain")]
+
+
 class Stats(ctypes.Structure):
     _fields_ = [
         ("unmasked_pairs", ctypes.c_int64),
@@ -83,6 +88,10 @@ class Stats(ctypes.Structure):
 # name -> (restype, argtypes)
 SIGNATURES = {
     "magi_attn_plan_create": (ctypes.c_int, [ctypes.POINTER(Layout), ctypes.POINTER(ctypes.c_void_p)]),
+    "magi_attn_train_plan_create": (ctypes.c_int, [ctypes.POINTER(Layout), ctypes.POINTER(ctypes.c_void_p)]),
+    "magi_attn_bwd_workspace_size": (ctypes.c_int, [ctypes.c_void_p, ctypes.POINTER(ctypes.c_size_t)]),
+    "magi_attn_bwd": (ctypes.c_int, [ctypes.c_void_p, ctypes.POINTER(BwdIO), ctypes.c_float, ctypes.c_float,
+                                     ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]),
     "magi_attn_cross_plan_create": (ctypes.c_int, [ctypes.POINTER(Layout), ctypes.POINTER(Text),
                                                    ctypes.POINTER(ctypes.c_void_p)]),
     "magi_attn_parallel_plan_create": (ctypes.c_int, [ctypes.POINTER(Layout), ctypes.POINTER(Text),
@@ -102,6 +111,8 @@ SIGNATURES = {
     "magi_attn_classify_host": (ctypes.c_int, [ctypes.POINTER(Layout), ctypes.c_int32, ctypes.c_int32,
                                                ctypes.POINTER(ctypes.c_int8)]),
     "magi_attn_plan_stats": (ctypes.c_int, [ctypes.POINTER(Layout), ctypes.POINTER(Stats)]),
+    "magi_attn_key_classify_host": (ctypes.c_int, [ctypes.POINTER(Layout), ctypes.c_int32, ctypes.c_int32,
+                                                   ctypes.POINTER(ctypes.c_int8)]),
     "magi_attn_cross_classify_host": (ctypes.c_int, [ctypes.POINTER(Layout), ctypes.POINTER(Text), ctypes.c_int32,
                                                      ctypes.c_int32, ctypes.POINTER(ctypes.c_int8)]),
     "magi_attn_cross_plan_stats": (ctypes.c_int, [ctypes.POINTER(Layout), ctypes.POINTER(Text), ctypes.c_int32,

@@ -82,6 +82,17 @@ def magi_attn_classify_host(q_offsets, kv_offsets=None, seq_chunks=None, bm=128,
     return cls
 
 
+def magi_attn_key_classify_host(q_offsets, kv_offsets=None, seq_chunks=None, bk=128, bt=32, n_q_heads=1, n_kv_heads=1,
+                                head_dim=128, dtype="bf16", kv_range=0) -> np.ndarray:
+    lib = _abi.load()
+    la = _LayoutArgs(q_offsets, kv_offsets, seq_chunks, n_q_heads, n_kv_heads, head_dim, dtype, kv_range)
+    tq = int(la.q[-1])
+    tk = int((la.kv if la.kv is not None else la.q)[-1])
+    cls = np.zeros((max(-(-tk // bk), 0), max(-(-tq // bt), 0)), dtype=np.int8)
+    _check(lib, lib.magi_attn_key_classify_host(la.ptr(), bk, bt, cls.ctypes.data_as(ctypes.POINTER(ctypes.c_int8))))
+    return cls
+
+
 def magi_attn_cross_classify_host(q_offsets, text_begin, text_end, t_text, bm=128, bn=64, kv_offsets=None,
                                   seq_chunks=None, n_q_heads=1, n_kv_heads=1, head_dim=128, dtype="bf16",
                                   kv_range=0) -> np.ndarray:
@@ -114,6 +125,53 @@ def magi_attn_plan_create(q_offsets, kv_offsets=None, seq_chunks=None, n_q_heads
     h = ctypes.c_void_p()
     _check(lib, lib.magi_attn_plan_create(la.ptr(), ctypes.byref(h)))
     return h.value
+
+
+def magi_attn_train_plan_create(q_offsets, kv_offsets=None, seq_chunks=None, n_q_heads=1, n_kv_heads=1, head_dim=128,
+                                dtype="bf16", kv_range=0) -> int:
+    lib = _abi.load()
+    la = _LayoutArgs(q_offsets, kv_offsets, seq_chunks, n_q_heads, n_kv_heads, head_dim, dtype, kv_range)
+    h = ctypes.c_void_p()
+    _check(lib, lib.magi_attn_train_plan_create(la.ptr(), ctypes.byref(h)))
+    return h.value
+
+
+def magi_attn_bwd_workspace_size(handle: int) -> int:
+    lib = _abi.load()
+    n = ctypes.c_size_t()
+    _check(lib, lib.magi_attn_bwd_workspace_size(handle, ctypes.byref(n)))
+    return n.value
+
+
+def magi_attn_bwd(handle: int, q, k, v, out, lse, dout, q_gain=None, k_gain=None, rms_eps: float = 1e-6,
+                  scale: Optional[float] = None, dq=None, dk=None, dv=None, dq_gain=None, dk_gain=None,
+                  workspace=None, stream=None):
+    """Enqueues the backward on `stream`: the gradients with respect to q, k,
+    v and both gains for the upstream gradient dout of out. Returns
+    (dq, dk, dv, dq_gain, dk_gain)."""
+    import torch
+    lib = _abi.load()
+    for name, t in (("q", q), ("k", k), ("v", v), ("out", out), ("lse", lse), ("dout", dout)):
+        if not t.is_cuda or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous GPU tensor")
+    d = q.shape[-1]
+    dev = q.device
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    dq_gain = torch.empty(d, dtype=torch.float32, device=dev) if dq_gain is None else dq_gain
+    dk_gain = torch.empty(d, dtype=torch.float32, device=dev) if dk_gain is None else dk_gain
+    qg = _gain(q_gain, d, dev)
+    kg = _gain(k_gain, d, dev)
+    sc = (1.0 / d ** 0.5) if scale is None else float(scale)
+    need = magi_attn_bwd_workspace_size(handle)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
+    ws_bytes = workspace.numel() * workspace.element_size()
+    io = _abi.BwdIO(*(t.data_ptr() for t in (q, k, v, qg, kg, out, lse, dout, dq, dk, dv, dq_gain, dk_gain)))
+    _check(lib, lib.magi_attn_bwd(handle, ctypes.byref(io), float(rms_eps), sc, workspace.data_ptr(), ws_bytes,
+                                  _stream_ptr(stream, dev)))
+    return dq, dk, dv, dq_gain, dk_gain
 
 
 def magi_attn_cross_plan_create(q_offsets, text_begin, text_end, t_text, kv_offsets=None, seq_chunks=None,
@@ -363,3 +421,22 @@ class ParallelPlan(Plan):
         self._check(q_x, k_x, v_x, self.text["t_text"], out_x, lse_x)
         return magi_attn_fwd_parallel(self.handle, q, k, v, q_x, k_x, v_x, q_gain, k_gain, q_gain_x, k_gain_x,
                                       rms_eps, scale, scale_x, out, lse, out_x, lse_x, workspace, stream)
+
+
+class TrainPlan(Plan):
+    """A self-attention plan that also runs the backward: call() is the
+    forward, backward() the gradients from the forward's out and lse."""
+
+    def _create(self) -> int:
+        return magi_attn_train_plan_create(**self.layout)
+
+    def bwd_workspace_size(self) -> int:
+        return magi_attn_bwd_workspace_size(self.handle)
+
+    def backward(self, q, k, v, out, lse, dout, q_gain=None, k_gain=None, rms_eps=1e-6, scale=None, dq=None, dk=None,
+                 dv=None, dq_gain=None, dk_gain=None, workspace=None, stream=None):
+        self._check(q, k, v, self.t_k, out, lse)
+        if dout.shape != q.shape or dout.dtype != q.dtype:
+            raise ValueError("dout must match q")
+        return magi_attn_bwd(self.handle, q, k, v, out, lse, dout, q_gain, k_gain, rms_eps, scale, dq, dk, dv, dq_gain,
+                             dk_gain, workspace, stream)

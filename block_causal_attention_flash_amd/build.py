@@ -9,7 +9,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libmagi_attn.so")
-SOURCES = ["api.cpp", "plan.cpp", "fwd_bf16.hip", "fwd_fp32.hip"]
+SOURCES = ["api.cpp", "plan.cpp", "fwd_bf16.hip", "fwd_fp32.hip", "bwd_bf16.hip", "bwd_fp32.hip"]
 
 # gfx950 only; packed-fp32 VALU forms are disabled on purpose (the compiler
 # still emits scalar fp32); code object v5 for the HIP runtime shipped with torch.

@@ -13,13 +13,21 @@
 
 struct magi_attn_plan {
   magi::HostPlan host;
+  bool train = false;            // has the backward's lists
+  magi::BwdHostPlan bwd;
   int device = 0;
-  void* dmem = nullptr;          // one allocation: items | tile codes | tile copy offsets | row bounds | merges
+  void* dmem = nullptr;          // one allocation of every device list below
   const int4* d_items = nullptr;
   const int* d_tiles = nullptr;
   const unsigned* d_soffs = nullptr;
   const int4* d_merges = nullptr;
   const int2* d_rows = nullptr;
+  const int4* d_dq_items = nullptr;
+  const int* d_dq_tiles = nullptr;
+  const unsigned* d_dq_soffs = nullptr;
+  const int4* d_kv_items = nullptr;
+  const int* d_kv_tiles = nullptr;
+  const int2* d_key_rows = nullptr;
 };
 
 namespace {
@@ -79,17 +87,36 @@ void classify_rows(const std::vector<magi::RowBounds>& rows, int64_t tq, int64_t
   }
 }
 
-magi_status_t create_plan(int32_t kind, const magi_attn_layout_t* layout, const magi_attn_text_t* text,
+// Host arrays copied into the plan's one device allocation, 256-byte aligned.
+struct Upload {
+  std::vector<std::pair<const void*, size_t>> parts;
+  std::vector<size_t> offsets;
+  size_t total = 0;
+  size_t add(const void* p, size_t bytes) {
+    const size_t o = total;
+    parts.emplace_back(p, bytes);
+    offsets.push_back(o);
+    total += round_up(bytes, 256);
+    return o;
+  }
+};
+
+magi_status_t create_plan(int32_t kind, bool train, const magi_attn_layout_t* layout, const magi_attn_text_t* text,
                           magi_attn_plan_t** out_plan) {
   if (!out_plan) return fail(MAGI_ERR_INVALID_ARG, "plan output pointer is NULL");
   *out_plan = nullptr;
   std::string err;
   magi_status_t s = validate(kind, layout, text, err);
   if (s != MAGI_OK) return fail(s, err);
+  if (train && layout->dtype == MAGI_DTYPE_BF16 &&
+      (int64_t(layout->q_offsets[layout->n_chunks]) + 31) / 32 * 32 * layout->n_q_heads * 256 >= (int64_t(1) << 31))
+    return fail(MAGI_ERR_UNSUPPORTED, "training plans need T_q (rounded up to 32) * n_q_heads * 256 below 2 GiB");
   magi_attn_plan* p = new (std::nothrow) magi_attn_plan();
   if (!p) return fail(MAGI_ERR_NO_MEMORY, "host allocation failed");
+  p->train = train;
   try {
     s = magi::build_host_plan(kind, layout, text, tiling_of(layout), p->host, err);
+    if (s == MAGI_OK && train) s = magi::build_bwd_plan(layout, p->bwd, err);
   } catch (const std::bad_alloc&) {
     delete p;
     return fail(MAGI_ERR_NO_MEMORY, "host allocation failed");
@@ -97,38 +124,46 @@ magi_status_t create_plan(int32_t kind, const magi_attn_layout_t* layout, const 
   if (s != MAGI_OK) { delete p; return fail(s, err); }
 
   const auto& H = p->host;
-  const size_t b_items = H.items.size() * sizeof(magi::WorkItem);
-  const size_t b_tiles = H.tile_codes.size() * sizeof(int32_t);
-  const size_t b_soffs = H.tile_soff.size() * sizeof(uint32_t);
-  const size_t b_rows = H.rows.size() * sizeof(magi::RowBounds);
-  const size_t b_merges = H.merges.size() * sizeof(magi::MergeItem);
-  const size_t o_tiles = round_up(b_items, 256), o_soffs = o_tiles + round_up(b_tiles, 256);
-  const size_t o_rows = o_soffs + round_up(b_soffs, 256);
-  const size_t o_merges = o_rows + round_up(b_rows, 256);
-  const size_t total = std::max<size_t>(o_merges + b_merges, 256);
+  const auto& B = p->bwd;
+  auto bytes = [](const auto& v) { return v.size() * sizeof(v[0]); };
+  Upload up;
+  const size_t o_items = up.add(H.items.data(), bytes(H.items));
+  const size_t o_tiles = up.add(H.tile_codes.data(), bytes(H.tile_codes));
+  const size_t o_soffs = up.add(H.tile_soff.data(), bytes(H.tile_soff));
+  const size_t o_rows = up.add(H.rows.data(), bytes(H.rows));
+  const size_t o_merges = up.add(H.merges.data(), bytes(H.merges));
+  const size_t o_dq_items = up.add(B.dq.items.data(), bytes(B.dq.items));
+  const size_t o_dq_tiles = up.add(B.dq.tile_codes.data(), bytes(B.dq.tile_codes));
+  const size_t o_dq_soffs = up.add(B.dq.tile_soff.data(), bytes(B.dq.tile_soff));
+  const size_t o_kv_items = up.add(B.items.data(), bytes(B.items));
+  const size_t o_kv_tiles = up.add(B.kv_tiles.data(), bytes(B.kv_tiles));
+  const size_t o_key_rows = up.add(B.key_rows.data(), bytes(B.key_rows));
   hipError_t e = hipGetDevice(&p->device);
   if (e != hipSuccess) { delete p; return hip_fail(e, "hipGetDevice"); }
-  e = hipMalloc(&p->dmem, total);
+  e = hipMalloc(&p->dmem, std::max<size_t>(up.total, 256));
   if (e != hipSuccess) {
     delete p;
     return e == hipErrorOutOfMemory ? fail(MAGI_ERR_NO_MEMORY, "hipMalloc of the plan failed") : hip_fail(e, "hipMalloc");
   }
   char* base = static_cast<char*>(p->dmem);
-  if (b_items) e = hipMemcpy(base, H.items.data(), b_items, hipMemcpyHostToDevice);
-  if (e == hipSuccess && b_tiles) e = hipMemcpy(base + o_tiles, H.tile_codes.data(), b_tiles, hipMemcpyHostToDevice);
-  if (e == hipSuccess && b_soffs) e = hipMemcpy(base + o_soffs, H.tile_soff.data(), b_soffs, hipMemcpyHostToDevice);
-  if (e == hipSuccess && b_rows) e = hipMemcpy(base + o_rows, H.rows.data(), b_rows, hipMemcpyHostToDevice);
-  if (e == hipSuccess && b_merges) e = hipMemcpy(base + o_merges, H.merges.data(), b_merges, hipMemcpyHostToDevice);
+  for (size_t i = 0; i < up.parts.size() && e == hipSuccess; ++i)
+    if (up.parts[i].second) e = hipMemcpy(base + up.offsets[i], up.parts[i].first, up.parts[i].second, hipMemcpyHostToDevice);
   if (e != hipSuccess) {
     (void)hipFree(p->dmem);
     delete p;
     return hip_fail(e, "hipMemcpy of the plan");
   }
-  p->d_items = reinterpret_cast<const int4*>(base);
+  p->d_items = reinterpret_cast<const int4*>(base + o_items);
   p->d_tiles = reinterpret_cast<const int*>(base + o_tiles);
   p->d_soffs = reinterpret_cast<const unsigned*>(base + o_soffs);
   p->d_rows = reinterpret_cast<const int2*>(base + o_rows);
   p->d_merges = reinterpret_cast<const int4*>(base + o_merges);
+  p->d_dq_items = reinterpret_cast<const int4*>(base + o_dq_items);
+  p->d_dq_tiles = reinterpret_cast<const int*>(base + o_dq_tiles);
+  p->d_dq_soffs = reinterpret_cast<const unsigned*>(base + o_dq_soffs);
+  p->d_kv_items = reinterpret_cast<const int4*>(base + o_kv_items);
+  p->d_kv_tiles = reinterpret_cast<const int*>(base + o_kv_tiles);
+  p->d_key_rows = reinterpret_cast<const int2*>(base + o_key_rows);
   *out_plan = p;
   return MAGI_OK;
 }
@@ -220,6 +255,19 @@ magi_status_t magi_attn_classify_host(const magi_attn_layout_t* layout, int32_t 
   return MAGI_OK;
 }
 
+magi_status_t magi_attn_key_classify_host(const magi_attn_layout_t* layout, int32_t bk, int32_t bt, int8_t* cls) {
+  std::string err;
+  magi_status_t s = magi::validate_layout(layout, err);
+  if (s != MAGI_OK) return fail(s, err);
+  if (bk < 1 || bt < 1) return fail(MAGI_ERR_INVALID_ARG, "tile sizes must be positive");
+  if (!cls) return fail(MAGI_ERR_INVALID_ARG, "cls is NULL");
+  std::vector<magi::RowBounds> keys;
+  magi::key_bounds(layout, keys);
+  const int32_t* kv = layout->kv_offsets ? layout->kv_offsets : layout->q_offsets;
+  classify_rows(keys, kv[layout->n_chunks], layout->q_offsets[layout->n_chunks], bk, bt, cls);
+  return MAGI_OK;
+}
+
 magi_status_t magi_attn_cross_classify_host(const magi_attn_layout_t* layout, const magi_attn_text_t* text,
                                             int32_t bm, int32_t bn, int8_t* cls) {
   std::string err;
@@ -243,17 +291,21 @@ magi_status_t magi_attn_cross_plan_stats(const magi_attn_layout_t* layout, const
 }
 
 magi_status_t magi_attn_plan_create(const magi_attn_layout_t* layout, magi_attn_plan_t** out_plan) {
-  return create_plan(magi::kPlanSelf, layout, nullptr, out_plan);
+  return create_plan(magi::kPlanSelf, false, layout, nullptr, out_plan);
+}
+
+magi_status_t magi_attn_train_plan_create(const magi_attn_layout_t* layout, magi_attn_plan_t** out_plan) {
+  return create_plan(magi::kPlanSelf, true, layout, nullptr, out_plan);
 }
 
 magi_status_t magi_attn_cross_plan_create(const magi_attn_layout_t* layout, const magi_attn_text_t* text,
                                           magi_attn_plan_t** out_plan) {
-  return create_plan(magi::kPlanCross, layout, text, out_plan);
+  return create_plan(magi::kPlanCross, false, layout, text, out_plan);
 }
 
 magi_status_t magi_attn_parallel_plan_create(const magi_attn_layout_t* layout, const magi_attn_text_t* text,
                                              magi_attn_plan_t** out_plan) {
-  return create_plan(magi::kPlanParallel, layout, text, out_plan);
+  return create_plan(magi::kPlanParallel, false, layout, text, out_plan);
 }
 
 magi_status_t magi_attn_plan_destroy(magi_attn_plan_t* plan) {
@@ -335,6 +387,75 @@ magi_status_t magi_attn_fwd_parallel(const magi_attn_plan_t* plan, const magi_at
   prm.k_gain_x = io->k_gain_x;
   prm.scale_x = io->scale_x;
   return launch(plan, prm, stream);
+}
+
+magi_status_t magi_attn_bwd_workspace_size(const magi_attn_plan_t* plan, size_t* bytes) {
+  if (!plan || !bytes) return fail(MAGI_ERR_INVALID_ARG, "plan or bytes is NULL");
+  if (!plan->train) return fail(MAGI_ERR_INVALID_ARG, "not a training plan (magi_attn_train_plan_create)");
+  const auto& H = plan->host;
+  const int nq = int(plan->bwd.dq.items.size()), nk = int(plan->bwd.items.size());
+  *bytes = H.dtype == MAGI_DTYPE_BF16 ? magi::bwd_workspace_layout(H.tq, H.tk, H.hq, H.hk, nq, nk).total
+                                      : magi::bwd_workspace_bytes_fp32(H.tq, H.tk, H.hq, H.hk, H.d, nq, nk);
+  return MAGI_OK;
+}
+
+magi_status_t magi_attn_bwd(const magi_attn_plan_t* plan, const magi_attn_bwd_io_t* io, float rms_eps, float scale,
+                            void* workspace, size_t workspace_bytes, void* stream) {
+  if (!plan) return fail(MAGI_ERR_INVALID_ARG, "plan is NULL");
+  if (!io) return fail(MAGI_ERR_INVALID_ARG, "io is NULL");
+  if (!plan->train) return fail(MAGI_ERR_INVALID_ARG, "magi_attn_bwd needs a plan from magi_attn_train_plan_create");
+  const auto& H = plan->host;
+  size_t need = 0;
+  magi_attn_bwd_workspace_size(plan, &need);
+  if (workspace_bytes < need) return fail(MAGI_ERR_INVALID_ARG, "workspace smaller than magi_attn_bwd_workspace_size()");
+  if (need && (!workspace || !aligned(workspace, 16)))
+    return fail(MAGI_ERR_INVALID_ARG, "workspace must be non-NULL and 16-byte aligned");
+  const void* tens[] = {io->q, io->k, io->v, io->out, io->dout, io->dq, io->dk, io->dv};
+  for (const void* t : tens)
+    if (!t || !aligned(t, 16)) return fail(MAGI_ERR_INVALID_ARG, "q, k, v, out, dout, dq, dk, dv must be non-NULL and 16-byte aligned");
+  if (!io->lse || !aligned(io->lse, 4) || !io->q_gain || !io->k_gain || !aligned(io->q_gain, 16) ||
+      !aligned(io->k_gain, 16) || !io->dq_gain || !io->dk_gain || !aligned(io->dq_gain, 4) || !aligned(io->dk_gain, 4))
+    return fail(MAGI_ERR_INVALID_ARG, "lse, the gains and the gain gradients must be non-NULL and aligned");
+  if (!(rms_eps >= 0.0f) || !std::isfinite(rms_eps)) return fail(MAGI_ERR_INVALID_ARG, "rms_eps must be finite and >= 0");
+  if (!(scale > 0.0f) || !std::isfinite(scale)) return fail(MAGI_ERR_INVALID_ARG, "scale must be finite and > 0");
+  if (H.tq == 0) return MAGI_OK;
+
+  magi::BwdParams b{};
+  b.q = io->q;
+  b.k = io->k;
+  b.v = io->v;
+  b.out = io->out;
+  b.dout = io->dout;
+  b.lse = io->lse;
+  b.q_gain = io->q_gain;
+  b.k_gain = io->k_gain;
+  b.dq = io->dq;
+  b.dk = io->dk;
+  b.dv = io->dv;
+  b.dq_gain = io->dq_gain;
+  b.dk_gain = io->dk_gain;
+  b.ws = workspace;
+  b.eps = rms_eps;
+  b.scale = scale;
+  b.tq = int(H.tq);
+  b.tk = int(H.tk);
+  b.hq = H.hq;
+  b.hk = H.hk;
+  b.tile_q = plan->bwd.dq.tiling.tile_q;
+  b.heads_per_item = plan->bwd.dq.tiling.heads_per_item;
+  b.dq_items = plan->d_dq_items;
+  b.dq_tiles = plan->d_dq_tiles;
+  b.dq_soffs = plan->d_dq_soffs;
+  b.rows = plan->d_rows;
+  b.kv_items = plan->d_kv_items;
+  b.kv_tiles = plan->d_kv_tiles;
+  b.key_rows = plan->d_key_rows;
+  b.n_dq_items = int(plan->bwd.dq.items.size());
+  b.n_kv_items = int(plan->bwd.items.size());
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const hipError_t e = H.dtype == MAGI_DTYPE_BF16 ? magi::launch_bwd_bf16_d128(b, st) : magi::launch_bwd_fp32(b, H.d, st);
+  if (e != hipSuccess) return hip_fail(e, "kernel launch");
+  return MAGI_OK;
 }
 
 magi_status_t magi_attn_fwd_simple(const void* q, const void* k, const void* v, void* out, float* lse,

@@ -1,0 +1,676 @@
+// Backward of the block-causal QK-RMSNorm GQA attention, bf16, head_dim 128, gfx950.
+//
+// Training needs the gradients of the attention of the MAGI-1 pages
+// (paperlayer §2 / Figure 1, §2.2.2; paper-notes §3.2.2 and Figure 15), and
+// the pages' attention kernel runs its backward from the forward's saved
+// softmax statistics (paperlayer §4.1.2, §B.1). With q' = rms(q) g_q g_k
+// scale log2(e) (the forward's folded query), k_hat = rms(k), the natural
+// log-sum-exp lse of each row and the upstream gradient dO:
+//   P_ij  = 2^(<q'_i, k_hat_j> - lse_i log2 e)        (recomputed, no max pass)
+//   dP_ij = <dO_i, v_j>,  D_i = <dO_i, O_i>,  dS_ij = P_ij (dP_ij - D_i)
+//   dq_hat_i = scale g_k * sum_j dS_ij k_hat_j        (dq kernel)
+//   dk_hat_j = scale sum_i dS_ij (rms(q_i) g_q)       (dk/dv kernel, over all query heads of j's group)
+//   dv_j     = sum_i P_ij dO_i                        (dk/dv kernel)
+//   dx = (g dx_hat - u mean_d(u g dx_hat)) / r,  u = x / r   (RMSNorm, in the epilogues)
+//   dg = sum over rows of u dx_hat                    (per-workgroup partials, then one reduction)
+//
+// Kernels, in stream order:
+//   prep_q  per (32-token tile, query head): the tile images of q', of
+//           dO, of dO^T and of (rms(q) g_q)^T, and the row statistics
+//           (lse log2 e, D);
+//   prep_k  per (32-key tile, KV head): the images of k_hat, of V and of
+//           k_hat^T;
+//   dq      query-stationary (the forward's order): 8 waves x 32 rows, per
+//           key tile S^T and dP^T on the matrix cores, dS on the vector ALUs,
+//           then (dq_hat)^T += k_hat^T dS^T;
+//   dkdv    key-stationary: 8 waves x 16 keys of one KV head, per
+//           (32-token tile, query head) S and dP, then dV^T += dO^T P and
+//           dK^T += (q_hat)^T dS;
+//   reduce  the gain gradients from the per-workgroup partials.
+// Tile images follow the forward's two layouts: "row" [16 chunks][32 rows]
+// [16 B] (A operand: lane l reads row l % 16, dims 8 (l / 16) + 32 ks ..)
+// and "transposed" [4 chunks][128 dims][16 B] whose chunk c holds rows
+// 4c + {0..3} and 16 + 4c + {0..3} (the row order of a lane's fragment of a
+// 16x16 result pair). Copies into LDS rings use LDS-direct buffer loads two
+// steps ahead.
+#include "kernels.hpp"
+
+namespace magi {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+#define LDS_PTR(T, p) ((__attribute__((address_space(3))) T*)(p))
+typedef __attribute__((address_space(3))) const bf16x8 lds_bf16x8;
+typedef __attribute__((address_space(3))) const f32x4 lds_f32x4;
+
+constexpr int D = 128;
+constexpr int TT = 32;                       // tokens per image (and per dk/dv step), keys per dq tile
+constexpr int IMG = TT * D * 2;              // 8 KiB
+constexpr int NTHR = 512;
+constexpr int RING = 4;                      // LDS ring stages, copies two steps ahead
+constexpr unsigned kNoTile = 0x80000000u;    // past every image array (< 2 GiB): zeros
+constexpr float kLog2e = 1.4426950408889634f;
+static_assert(IMG == NTHR * 16, "one 16-byte copy per thread per image");
+static_assert(kBwdRowsPerItem == 8 * 32 && kBwdKeysPerItem == 8 * 16, "8 waves per workgroup");
+
+__device__ __forceinline__ unsigned lds_addr(const void* p) {
+  return unsigned(reinterpret_cast<uintptr_t>(LDS_PTR(const char, p)));
+}
+
+__device__ __forceinline__ i32x4 make_rsrc(const void* base, unsigned bytes) {
+  const unsigned long long a = reinterpret_cast<unsigned long long>(base);
+  i32x4 r;
+  r[0] = int(unsigned(a));
+  r[1] = int(unsigned(a >> 32) & 0xffffu);
+  r[2] = int(bytes);
+  r[3] = 0x00020000;
+  return r;
+}
+
+// Global -> LDS copy of 16 bytes per active lane: lane i (of the wave) reads
+// buffer offset voff + soff (zeros past the buffer) and writes LDS byte
+// lds + 16 i, so a workgroup that copies one 8 KiB image passes each wave's
+// own 1 KiB part of the stage as `lds`. m0 is saved and restored inside the
+// asm; completion is awaited with vmcnt.
+__device__ __forceinline__ void dma16(i32x4 rsrc, unsigned voff, unsigned soff, unsigned lds) {
+  unsigned saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %1\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dwordx4 %2, %3, %4 offen lds\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "s"(lds), "v"(voff), "s"(rsrc), "s"(soff)
+      : "memory");
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  asm volatile("s_waitcnt vmcnt(%0)" : : "n"(N) : "memory");
+}
+
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" : : : "memory"); }
+
+// Sums over the four 16-lane groups / over the 16 lanes of a group.
+__device__ __forceinline__ float sum_groups(float x) {
+  x += __shfl_xor(x, 16, 64);
+  x += __shfl_xor(x, 32, 64);
+  return x;
+}
+__device__ __forceinline__ float sum16(float x) {
+  x += __shfl_xor(x, 1, 64);
+  x += __shfl_xor(x, 2, 64);
+  x += __shfl_xor(x, 4, 64);
+  x += __shfl_xor(x, 8, 64);
+  return x;
+}
+__device__ __forceinline__ float sum8(float x) {
+  x += __shfl_xor(x, 1, 64);
+  x += __shfl_xor(x, 2, 64);
+  x += __shfl_xor(x, 4, 64);
+  return x;
+}
+
+__device__ __forceinline__ f32x4 mfma(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// Row j of the transposed layout's chunk c: the 8 rows 16 (jj / 4) + 4c + jj % 4.
+__device__ __forceinline__ int perm_row(int c, int jj) { return 16 * (jj >> 2) + 4 * c + (jj & 3); }
+
+// ------------------------------------------------------------------ pre-passes
+
+// One workgroup per (32-token tile tt, query head h), image b = tt * hq + h;
+// thread t: token row j = t / 8, dims [16 (t % 8), +16).
+constexpr int PREP_THREADS = 256;
+__global__ void __launch_bounds__(PREP_THREADS) bwd_prep_q_kernel(BwdParams p, BwdLayout L) {
+  __shared__ __attribute__((aligned(16))) __bf16 sh_qh[TT][D + 8];
+  __shared__ __attribute__((aligned(16))) __bf16 sh_do[TT][D + 8];
+  unsigned char* ws = static_cast<unsigned char*>(p.ws);
+  const int b = blockIdx.x, tt = b / p.hq, h = b % p.hq;
+  const int t = threadIdx.x, j = t >> 3, part = t & 7;
+  const int tok = tt * TT + j;
+  const bool valid = tok < p.tq;
+  const size_t row = (size_t(tok) * p.hq + h) * D + part * 16;
+  bf16x8 q[2] = {}, dd[2] = {}, oo[2] = {};
+  if (valid) {
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      q[c] = *reinterpret_cast<const bf16x8*>(static_cast<const __bf16*>(p.q) + row + 8 * c);
+      dd[c] = *reinterpret_cast<const bf16x8*>(static_cast<const __bf16*>(p.dout) + row + 8 * c);
+      oo[c] = *reinterpret_cast<const bf16x8*>(static_cast<const __bf16*>(p.out) + row + 8 * c);
+    }
+  }
+  float ss = 0.0f, dsum = 0.0f;
+#pragma unroll
+  for (int c = 0; c < 2; ++c)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      ss += float(q[c][e]) * float(q[c][e]);
+      dsum += float(dd[c][e]) * float(oo[c][e]);
+    }
+  ss = sum8(ss);
+  dsum = sum8(dsum);
+  const float rq = valid ? __builtin_amdgcn_rsqf(ss * (1.0f / D) + p.eps) : 0.0f;
+  const float fold = p.scale * kLog2e;
+#pragma unroll
+  for (int c = 0; c < 2; ++c) {
+    bf16x8 qs, qh;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int d = part * 16 + 8 * c + e;
+      const float u = float(q[c][e]) * rq;
+      qs[e] = (__bf16)(u * p.q_gain[d] * p.k_gain[d] * fold);
+      qh[e] = (__bf16)(u * p.q_gain[d]);
+      sh_qh[j][d] = qh[e];
+      sh_do[j][d] = dd[c][e];
+    }
+    const size_t at = size_t(b) * IMG + 512 * (2 * part + c) + 16 * j;
+    *reinterpret_cast<bf16x8*>(ws + L.qs + at) = qs;
+    *reinterpret_cast<bf16x8*>(ws + L.dos + at) = dd[c];
+  }
+  if (part == 0) {
+    float* rs = reinterpret_cast<float*>(ws + L.rs) + size_t(b) * 64;
+    rs[j] = valid ? p.lse[size_t(h) * p.tq + tok] * kLog2e : 0.0f;
+    rs[32 + j] = valid ? dsum : 0.0f;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int r = 0; r < 2; ++r) {
+    const int u = t + PREP_THREADS * r;          // transposed unit: chunk u / 128, dim u % 128
+    const int c = u >> 7, d = u & 127;
+    bf16x8 wq, wd;
+#pragma unroll
+    for (int jj = 0; jj < 8; ++jj) {
+      wq[jj] = sh_qh[perm_row(c, jj)][d];
+      wd[jj] = sh_do[perm_row(c, jj)][d];
+    }
+    const size_t at = size_t(b) * IMG + 2048 * c + 16 * d;
+    *reinterpret_cast<bf16x8*>(ws + L.qht + at) = wq;
+    *reinterpret_cast<bf16x8*>(ws + L.dot + at) = wd;
+  }
+}
+
+// One workgroup per (32-key tile kt, KV head), image b = kt * hk + kvh.
+__global__ void __launch_bounds__(PREP_THREADS) bwd_prep_k_kernel(BwdParams p, BwdLayout L) {
+  __shared__ __attribute__((aligned(16))) __bf16 sh_k[TT][D + 8];
+  unsigned char* ws = static_cast<unsigned char*>(p.ws);
+  const int b = blockIdx.x, kt = b / p.hk, kvh = b % p.hk;
+  const int t = threadIdx.x, j = t >> 3, part = t & 7;
+  const int key = kt * TT + j;
+  const bool valid = key < p.tk;
+  const size_t row = (size_t(key) * p.hk + kvh) * D + part * 16;
+  bf16x8 k[2] = {}, v[2] = {};
+  if (valid) {
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      k[c] = *reinterpret_cast<const bf16x8*>(static_cast<const __bf16*>(p.k) + row + 8 * c);
+      v[c] = *reinterpret_cast<const bf16x8*>(static_cast<const __bf16*>(p.v) + row + 8 * c);
+    }
+  }
+  float ss = 0.0f;
+#pragma unroll
+  for (int c = 0; c < 2; ++c)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) ss += float(k[c][e]) * float(k[c][e]);
+  ss = sum8(ss);
+  const float rk = valid ? __builtin_amdgcn_rsqf(ss * (1.0f / D) + p.eps) : 0.0f;
+#pragma unroll
+  for (int c = 0; c < 2; ++c) {
+    bf16x8 kh;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      kh[e] = (__bf16)(float(k[c][e]) * rk);
+      sh_k[j][part * 16 + 8 * c + e] = kh[e];
+    }
+    const size_t at = size_t(b) * IMG + 512 * (2 * part + c) + 16 * j;
+    *reinterpret_cast<bf16x8*>(ws + L.kh + at) = kh;
+    *reinterpret_cast<bf16x8*>(ws + L.vr + at) = v[c];
+  }
+  __syncthreads();
+#pragma unroll
+  for (int r = 0; r < 2; ++r) {
+    const int u = t + PREP_THREADS * r;
+    const int c = u >> 7, d = u & 127;
+    bf16x8 w;
+#pragma unroll
+    for (int jj = 0; jj < 8; ++jj) w[jj] = sh_k[perm_row(c, jj)][d];
+    *reinterpret_cast<bf16x8*>(ws + L.kht + size_t(b) * IMG + 2048 * c + 16 * d) = w;
+  }
+}
+
+// Writes the wave-summed gain partial of every lane's 32 dims (16 db + 4 g + i)
+// through LDS and the workgroup's sum to part[0 .. 127].
+__device__ __forceinline__ void store_gain_partial(float (&gp)[8][4], float (*red)[D], float* part, int wave,
+                                                   int lane, int tid) {
+  const int g = lane >> 4;
+#pragma unroll
+  for (int db = 0; db < 8; ++db)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float x = sum16(gp[db][i]);
+      if ((lane & 15) == 0) red[wave][16 * db + 4 * g + i] = x;
+    }
+  __syncthreads();
+  if (tid < D) {
+    float x = 0.0f;
+#pragma unroll
+    for (int w = 0; w < 8; ++w) x += red[w][tid];
+    part[tid] = x;
+  }
+}
+
+// RMSNorm backward of one row held as 32 dims per lane (dims 16 db + 4 g + i,
+// four lanes per row): x the input row, dxh the gradient of x_hat = rms(x) g.
+// Writes dx (bf16) when `store`, and adds u * dxh to gp.
+__device__ __forceinline__ void rms_backward_row(const __bf16* xrow, __bf16* dxrow, const float (&dxh)[8][4],
+                                                 const float* gain, float eps, bool store, float (&gp)[8][4],
+                                                 int g) {
+  bf16x4 xv[8];
+#pragma unroll
+  for (int db = 0; db < 8; ++db)
+    xv[db] = store ? *reinterpret_cast<const bf16x4*>(xrow + 16 * db + 4 * g) : bf16x4{};
+  float ss = 0.0f;
+#pragma unroll
+  for (int db = 0; db < 8; ++db)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) ss += float(xv[db][i]) * float(xv[db][i]);
+  ss = sum_groups(ss);
+  const float r = __builtin_amdgcn_rsqf(ss * (1.0f / D) + eps);
+  float m = 0.0f;
+#pragma unroll
+  for (int db = 0; db < 8; ++db)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) m += float(xv[db][i]) * r * gain[16 * db + 4 * g + i] * dxh[db][i];
+  m = sum_groups(m) * (1.0f / D);
+#pragma unroll
+  for (int db = 0; db < 8; ++db) {
+    bf16x4 w;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float u = float(xv[db][i]) * r;
+      w[i] = (__bf16)((gain[16 * db + 4 * g + i] * dxh[db][i] - u * m) * r);
+      gp[db][i] += store ? u * dxh[db][i] : 0.0f;
+    }
+    if (store) *reinterpret_cast<bf16x4*>(dxrow + 16 * db + 4 * g) = w;
+  }
+}
+
+// ------------------------------------------------------------------ dq
+
+struct DqLds {
+  unsigned char kh[RING][IMG];
+  unsigned char vr[RING][IMG];
+  unsigned char kht[RING][IMG];
+  float gk[D];           // scale * g_k
+  float gq[D];
+  float red[8][D];
+};
+
+__global__ void __launch_bounds__(NTHR) __attribute__((amdgpu_waves_per_eu(2, 2)))
+bwd_dq_kernel(BwdParams p, BwdLayout L, const int4* __restrict__ items, const int* __restrict__ tiles,
+              const unsigned* __restrict__ soffs_all) {
+  __shared__ __attribute__((aligned(1024))) DqLds sm;
+  unsigned char* ws = static_cast<unsigned char*>(p.ws);
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63, g = lane >> 4, r16 = lane & 15;
+  float* part = reinterpret_cast<float*>(ws + L.pgq) + size_t(blockIdx.x) * D;
+  const int4 item = items[2 * blockIdx.x];
+  if (item.z == item.w) {                              // padding item: an empty partial
+    if (tid < D) part[tid] = 0.0f;
+    return;
+  }
+  const int n_full = items[2 * blockIdx.x + 1].x;
+  const int kvh = item.y >> 16, h0 = item.y & 0xffff;
+  const int n = item.w - item.z;
+  // The wave's 32 rows are one (token tile, head) image.
+  const int r0 = wave * 32;
+  const int head = h0 + r0 / p.tile_q;
+  const int tok0 = item.x + r0 % p.tile_q;
+  const int img = (tok0 / TT) * p.hq + head;
+  // A wave whose rows all lie past T_q (the last query tile) has no image:
+  // it computes with zeros (P = 1, dP = 0, dS = 0) and stores nothing.
+  const bool live = tok0 < p.tq;
+
+  bf16x8 qs[2][4], dov[2][4];
+  {
+    const size_t base = size_t(live ? img : 0) * IMG + 512 * g + 16 * r16;
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        qs[rb][ks] = live ? *reinterpret_cast<const bf16x8*>(ws + L.qs + base + 2048 * ks + 256 * rb) : bf16x8{};
+        dov[rb][ks] = live ? *reinterpret_cast<const bf16x8*>(ws + L.dos + base + 2048 * ks + 256 * rb) : bf16x8{};
+      }
+  }
+  float lse2[2], dvv[2];
+  int lo[2], hi[2];
+  {
+    const float* rs = reinterpret_cast<const float*>(ws + L.rs) + size_t(live ? img : 0) * 64;
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb) {
+      lse2[rb] = live ? rs[16 * rb + r16] : 0.0f;
+      dvv[rb] = live ? rs[32 + 16 * rb + r16] : 0.0f;
+      const int tok = tok0 + 16 * rb + r16;
+      const int2 bnd = tok < p.tq ? p.rows[tok] : int2{0, 0};
+      lo[rb] = bnd.x;
+      hi[rb] = bnd.y;
+    }
+  }
+  if (tid < D) {
+    sm.gk[tid] = p.k_gain[tid] * p.scale;
+    sm.gq[tid] = p.q_gain[tid];
+  }
+
+  const unsigned n_kt = unsigned(p.tk + TT - 1) / TT;
+  const unsigned kbytes = n_kt * unsigned(p.hk) * IMG;
+  const i32x4 rkh = make_rsrc(ws + L.kh, kbytes), rvr = make_rsrc(ws + L.vr, kbytes),
+              rkht = make_rsrc(ws + L.kht, kbytes);
+  const unsigned voff = unsigned(kvh) * IMG + unsigned(tid) * 16;
+  const unsigned kh0 = lds_addr(sm.kh[0]), vr0 = lds_addr(sm.vr[0]), kht0 = lds_addr(sm.kht[0]);
+  const unsigned wpart = unsigned(wave) * 1024;  // this wave's part of every image copy
+  const int* codes = tiles + item.z;
+  const unsigned* soffs = soffs_all + item.z;    // padded past the list with kNoTile
+  auto issue = [&](int i) {
+    const unsigned so = __builtin_amdgcn_readfirstlane(soffs[i]);
+    const unsigned st = unsigned(i % RING) * IMG + wpart;
+    dma16(rkh, voff, so, kh0 + st);
+    dma16(rvr, voff, so, vr0 + st);
+    dma16(rkht, voff, so, kht0 + st);
+  };
+  issue(0);
+  issue(1);
+
+  f32x4 acc[2][8];
+#pragma unroll
+  for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+    for (int db = 0; db < 8; ++db) acc[rb][db] = f32x4{};
+  const unsigned rowq = 512 * g + 16 * r16, colq = 2048 * g + 16 * r16;
+  for (int i = 0; i < n; ++i) {
+    wait_vmcnt<3>();                                  // tile i landed; tile i + 1 may still fly
+    lds_barrier();                                    // and every wave left the stage tile i + 2 overwrites
+    issue(i + 2);
+    const unsigned st = unsigned(i % RING) * IMG;
+    f32x4 s[2][2], dp[2][2];
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb) s[rb][0] = s[rb][1] = dp[rb][0] = dp[rb][1] = f32x4{};
+#pragma unroll
+    for (int f = 0; f < 8; ++f) {
+      const int ks = f >> 1, kb = f & 1;
+      const bf16x8 a = *(lds_bf16x8*)(size_t)(kh0 + st + rowq + 2048 * ks + 256 * kb);
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb) s[rb][kb] = mfma(a, qs[rb][ks], s[rb][kb]);
+    }
+#pragma unroll
+    for (int f = 0; f < 8; ++f) {
+      const int ks = f >> 1, kb = f & 1;
+      const bf16x8 a = *(lds_bf16x8*)(size_t)(vr0 + st + rowq + 2048 * ks + 256 * kb);
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb) dp[rb][kb] = mfma(a, dov[rb][ks], dp[rb][kb]);
+    }
+    // lane: row r16 of block rb, keys 16 kb + 4 g + i of the tile
+    const bool masked = i >= n_full;
+    const int kt = masked ? (codes[i] >> 1) : 0;
+    bf16x8 ds[2];
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          float pv = __builtin_amdgcn_exp2f(s[rb][kb][e] - lse2[rb]);
+          if (masked) {
+            const unsigned rel = unsigned(kt * TT + 16 * kb + 4 * g + e - lo[rb]);
+            if (rel >= unsigned(hi[rb] - lo[rb])) pv = 0.0f;
+          }
+          ds[rb][4 * kb + e] = (__bf16)(pv * (dp[rb][kb][e] - dvv[rb]));
+        }
+#pragma unroll
+    for (int db = 0; db < 8; ++db) {
+      const bf16x8 a = *(lds_bf16x8*)(size_t)(kht0 + st + colq + 256 * db);
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb) acc[rb][db] = mfma(a, ds[rb], acc[rb][db]);
+    }
+  }
+  wait_vmcnt<0>();                                    // the padding copies of the last two steps
+
+  // Epilogue: lane holds dims 16 db + 4 g + i of row r16 of block rb.
+  float gp[8][4];
+#pragma unroll
+  for (int db = 0; db < 8; ++db)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) gp[db][e] = 0.0f;
+  __syncthreads();                                    // gains in LDS (and the loop's last reads) done
+#pragma unroll
+  for (int rb = 0; rb < 2; ++rb) {
+    const int tok = tok0 + 16 * rb + r16;
+    const bool valid = tok < p.tq;
+    float dxh[8][4];
+#pragma unroll
+    for (int db = 0; db < 8; ++db)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) dxh[db][e] = sm.gk[16 * db + 4 * g + e] * acc[rb][db][e];
+    const size_t off = (size_t(valid ? tok : 0) * p.hq + head) * D;
+    rms_backward_row(static_cast<const __bf16*>(p.q) + off, static_cast<__bf16*>(p.dq) + off, dxh, sm.gq, p.eps,
+                     valid, gp, g);
+  }
+  store_gain_partial(gp, sm.red, part, wave, lane, tid);
+}
+
+// ------------------------------------------------------------------ dk / dv
+
+struct KvLds {
+  unsigned char qs[RING][IMG];
+  unsigned char dos[RING][IMG];
+  unsigned char dot[RING][IMG];
+  unsigned char qht[RING][IMG];
+  float rs[RING][8][64];  // per stage and wave: lse log2 e [32], D [32] of the step's rows
+  float gk[D];
+  float red[8][D];
+};
+
+__global__ void __launch_bounds__(NTHR) __attribute__((amdgpu_waves_per_eu(2, 2)))
+bwd_dkdv_kernel(BwdParams p, BwdLayout L, const int4* __restrict__ items, const int* __restrict__ tiles) {
+  __shared__ __attribute__((aligned(1024))) KvLds sm;
+  unsigned char* ws = static_cast<unsigned char*>(p.ws);
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63, g = lane >> 4, r16 = lane & 15;
+  float* part = reinterpret_cast<float*>(ws + L.pgk) + size_t(blockIdx.x) * D;
+  const int4 item = items[2 * blockIdx.x];
+  if (item.z == item.w) {
+    if (tid < D) part[tid] = 0.0f;
+    return;
+  }
+  const int n_full = items[2 * blockIdx.x + 1].x;
+  const int kb = item.x, kvh = item.y;
+  const int G = p.hq / p.hk;
+  const int n_entries = item.w - item.z;
+  const int n_steps = n_entries * G;
+  // The wave's 16 keys: kb * 128 + 16 wave + (0..15); the lane's key (B operand column, output row).
+  const int key = kb * kBwdKeysPerItem + 16 * wave + r16;
+  const int kt = (kb * kBwdKeysPerItem + 16 * wave) / TT;
+  const unsigned n_kt = unsigned(p.tk + TT - 1) / TT;
+  bf16x8 ku[4], vv[4];
+  {
+    const bool have = unsigned(kt) < n_kt;
+    const size_t base = (size_t(kt) * p.hk + kvh) * IMG + 512 * g + 16 * (16 * (wave & 1) + r16);
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      ku[ks] = have ? *reinterpret_cast<const bf16x8*>(ws + L.kh + base + 2048 * ks) : bf16x8{};
+      vv[ks] = have ? *reinterpret_cast<const bf16x8*>(ws + L.vr + base + 2048 * ks) : bf16x8{};
+    }
+  }
+  const int2 kbnd = key < p.tk ? p.key_rows[key] : int2{0, 0};
+  if (tid < D) sm.gk[tid] = p.k_gain[tid];
+
+  const unsigned n_tt = unsigned(p.tq + TT - 1) / TT;
+  const unsigned qbytes = n_tt * unsigned(p.hq) * IMG;
+  const i32x4 rqs = make_rsrc(ws + L.qs, qbytes), rdo = make_rsrc(ws + L.dos, qbytes),
+              rdot = make_rsrc(ws + L.dot, qbytes), rqht = make_rsrc(ws + L.qht, qbytes),
+              rrs = make_rsrc(ws + L.rs, n_tt * unsigned(p.hq) * 256u);
+  const unsigned qs0 = lds_addr(sm.qs[0]), do0 = lds_addr(sm.dos[0]), dot0 = lds_addr(sm.dot[0]),
+                 qht0 = lds_addr(sm.qht[0]), rs0 = lds_addr(&sm.rs[0][wave][0]);
+  const int* codes = tiles + item.z;
+  const int hbase = kvh * G;
+  // Step s = (entry s / G, head hbase + s % G); its image (token tile, head).
+  int ie = 0, ih = 0;                                 // entry and head of the next step to issue
+  const unsigned wpart = unsigned(wave) * 1024;  // this wave's part of every image copy
+  auto issue = [&]() {
+    const bool live = ie < n_entries;
+    const unsigned imgi = __builtin_amdgcn_readfirstlane(live ? unsigned((codes[ie] >> 1) * p.hq + hbase + ih) : 0u);
+    const unsigned so = live ? imgi * IMG : kNoTile;
+    const unsigned st = unsigned(((ie * G + ih) % RING)) * IMG + wpart;
+    dma16(rqs, unsigned(tid) * 16, so, qs0 + st);
+    dma16(rdo, unsigned(tid) * 16, so, do0 + st);
+    dma16(rdot, unsigned(tid) * 16, so, dot0 + st);
+    dma16(rqht, unsigned(tid) * 16, so, qht0 + st);
+    if (lane < 16)
+      dma16(rrs, unsigned(lane) * 16, live ? imgi * 256u : kNoTile, rs0 + unsigned((ie * G + ih) % RING) * 8 * 256);
+    if (++ih == G) { ih = 0; ++ie; }
+  };
+  issue();
+  issue();
+
+  f32x4 accv[8], acck[8];
+#pragma unroll
+  for (int db = 0; db < 8; ++db) accv[db] = acck[db] = f32x4{};
+  const unsigned rowq = 512 * g + 16 * r16, colq = 2048 * g + 16 * r16;
+  int ce = 0, ch = 0;                                 // entry and head of the current step
+  for (int s = 0; s < n_steps; ++s) {
+    wait_vmcnt<5>();                                  // step s landed; step s + 1 may still fly
+    lds_barrier();
+    issue();
+    const unsigned st = unsigned(s % RING) * IMG;
+    f32x4 sc[2], dp[2];
+    sc[0] = sc[1] = dp[0] = dp[1] = f32x4{};
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb) {
+        const bf16x8 a = *(lds_bf16x8*)(size_t)(qs0 + st + rowq + 2048 * ks + 256 * rb);
+        sc[rb] = mfma(a, ku[ks], sc[rb]);
+      }
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb) {
+        const bf16x8 a = *(lds_bf16x8*)(size_t)(do0 + st + rowq + 2048 * ks + 256 * rb);
+        dp[rb] = mfma(a, vv[ks], dp[rb]);
+      }
+    // lane: key r16, rows 16 rb + 4 g + e of the step's token tile
+    const unsigned rsa = rs0 + unsigned(s % RING) * 8 * 256;
+    const bool masked = ce >= n_full;
+    const int tt = codes[ce] >> 1;
+    bf16x8 pb, dsb;
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb) {
+      const f32x4 l2 = *(lds_f32x4*)(size_t)(rsa + 4 * (16 * rb + 4 * g));
+      const f32x4 dd = *(lds_f32x4*)(size_t)(rsa + 128 + 4 * (16 * rb + 4 * g));
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        float pv = __builtin_amdgcn_exp2f(sc[rb][e] - l2[e]);
+        if (masked) {
+          const unsigned rel = unsigned(tt * TT + 16 * rb + 4 * g + e - kbnd.x);
+          if (rel >= unsigned(kbnd.y - kbnd.x)) pv = 0.0f;
+        }
+        pb[4 * rb + e] = (__bf16)pv;
+        dsb[4 * rb + e] = (__bf16)(pv * (dp[rb][e] - dd[e]));
+      }
+    }
+#pragma unroll
+    for (int db = 0; db < 8; ++db) {
+      const bf16x8 a = *(lds_bf16x8*)(size_t)(dot0 + st + colq + 256 * db);
+      accv[db] = mfma(a, pb, accv[db]);
+    }
+#pragma unroll
+    for (int db = 0; db < 8; ++db) {
+      const bf16x8 a = *(lds_bf16x8*)(size_t)(qht0 + st + colq + 256 * db);
+      acck[db] = mfma(a, dsb, acck[db]);
+    }
+    if (++ch == G) { ch = 0; ++ce; }
+  }
+  wait_vmcnt<0>();
+
+  // Epilogue: lane holds dims 16 db + 4 g + e of key r16.
+  const bool valid = key < p.tk;
+  const size_t off = (size_t(valid ? key : 0) * p.hk + kvh) * D;
+  if (valid) {
+#pragma unroll
+    for (int db = 0; db < 8; ++db) {
+      bf16x4 w;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) w[e] = (__bf16)accv[db][e];
+      *reinterpret_cast<bf16x4*>(static_cast<__bf16*>(p.dv) + off + 16 * db + 4 * g) = w;
+    }
+  }
+  float gp[8][4], dxh[8][4];
+#pragma unroll
+  for (int db = 0; db < 8; ++db)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      gp[db][e] = 0.0f;
+      dxh[db][e] = p.scale * acck[db][e];
+    }
+  __syncthreads();
+  rms_backward_row(static_cast<const __bf16*>(p.k) + off, static_cast<__bf16*>(p.dk) + off, dxh, sm.gk, p.eps,
+                   valid, gp, g);
+  store_gain_partial(gp, sm.red, part, wave, lane, tid);
+}
+
+// Sums the per-workgroup gain partials in a fixed order.
+__global__ void __launch_bounds__(256) bwd_gain_reduce_kernel(const float* pgq, int nq, const float* pgk, int nk,
+                                                             float* dq_gain, float* dk_gain) {
+  const int t = threadIdx.x, d = t & 127;
+  const float* src = t < D ? pgq : pgk;
+  const int n = t < D ? nq : nk;
+  float x = 0.0f;
+  for (int i = 0; i < n; ++i) x += src[size_t(i) * D + d];
+  (t < D ? dq_gain : dk_gain)[d] = x;
+}
+
+}  // namespace
+
+BwdLayout bwd_workspace_layout(long long tq, long long tk, int hq, int hk, int n_dq_items, int n_kv_items) {
+  auto up = [](size_t x) { return (x + 255) / 256 * 256; };
+  const size_t qimg = size_t((tq + TT - 1) / TT) * size_t(hq) * IMG;
+  const size_t kimg = size_t((tk + TT - 1) / TT) * size_t(hk) * IMG;
+  BwdLayout L{};
+  L.qs = 0;
+  L.dos = L.qs + up(qimg);
+  L.dot = L.dos + up(qimg);
+  L.qht = L.dot + up(qimg);
+  L.rs = L.qht + up(qimg);
+  L.kh = L.rs + up(qimg / IMG * 256);
+  L.vr = L.kh + up(kimg);
+  L.kht = L.vr + up(kimg);
+  L.pgq = L.kht + up(kimg);
+  L.pgk = L.pgq + up(size_t(n_dq_items) * D * sizeof(float));
+  L.total = L.pgk + up(size_t(n_kv_items) * D * sizeof(float));
+  return L;
+}
+
+hipError_t launch_bwd_bf16_d128(const BwdParams& p, hipStream_t stream) {
+  const BwdLayout L = bwd_workspace_layout(p.tq, p.tk, p.hq, p.hk, p.n_dq_items, p.n_kv_items);
+  const unsigned n_tt = unsigned((p.tq + TT - 1) / TT), n_kt = unsigned((p.tk + TT - 1) / TT);
+  hipLaunchKernelGGL(bwd_prep_q_kernel, dim3(n_tt * unsigned(p.hq)), dim3(PREP_THREADS), 0, stream, p, L);
+  hipLaunchKernelGGL(bwd_prep_k_kernel, dim3(n_kt * unsigned(p.hk)), dim3(PREP_THREADS), 0, stream, p, L);
+  if (p.n_dq_items > 0)
+    hipLaunchKernelGGL(bwd_dq_kernel, dim3(p.n_dq_items), dim3(NTHR), 0, stream, p, L, p.dq_items, p.dq_tiles,
+                       p.dq_soffs);
+  if (p.n_kv_items > 0)
+    hipLaunchKernelGGL(bwd_dkdv_kernel, dim3(p.n_kv_items), dim3(NTHR), 0, stream, p, L, p.kv_items, p.kv_tiles);
+  unsigned char* ws = static_cast<unsigned char*>(p.ws);
+  hipLaunchKernelGGL(bwd_gain_reduce_kernel, dim3(1), dim3(256), 0, stream, reinterpret_cast<const float*>(ws + L.pgq),
+                     p.n_dq_items, reinterpret_cast<const float*>(ws + L.pgk), p.n_kv_items, p.dq_gain, p.dk_gain);
+  return hipGetLastError();
+}
+
+}  // namespace magi

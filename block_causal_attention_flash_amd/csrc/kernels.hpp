@@ -8,6 +8,9 @@ namespace magi {
 
 // (token, head) rows of one bf16 work item: tile_q * heads_per_item.
 constexpr int kBf16RowsPerItem = 384;
+// Rows of one bf16 dq work item of the backward, and keys of one dk/dv item.
+constexpr int kBwdRowsPerItem = 256;
+constexpr int kBwdKeysPerItem = 128;
 
 struct FwdParams {
   const void* q;
@@ -43,6 +46,50 @@ struct FwdParams {
   int tkx;
   int n_kt_img;          // bf16 path: key tiles per KV head in the image arrays (phase 0's keys, then phase 1's)
 };
+
+// Backward pass (dq, dk, dv and both gain gradients) of the self-attention.
+// Work lists come from a training plan: query-stationary items for dq (the
+// forward's item layout with `bwd_rows` rows per item) and key-stationary
+// items for dk/dv (a block of keys of one KV head over the token tiles that
+// see it).
+struct BwdParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* out;
+  const void* dout;
+  const float* lse;
+  const float* q_gain;
+  const float* k_gain;
+  void* dq;
+  void* dk;
+  void* dv;
+  float* dq_gain;
+  float* dk_gain;
+  void* ws;               // workspace (layout: bwd_workspace_layout)
+  float eps;
+  float scale;
+  int tq, tk, hq, hk;
+  int tile_q, heads_per_item;        // dq items
+  const int4* dq_items;   // WorkItem[n_dq_items]
+  const int* dq_tiles;    // key tile codes per dq item list
+  const unsigned* dq_soffs;
+  const int2* rows;       // per-token key bounds [tq]
+  const int4* kv_items;   // KeyItem[n_kv_items]
+  const int* kv_tiles;    // token tile codes (tt * 2 + masked) per key block
+  const int2* key_rows;   // per-key token bounds [tk]
+  int n_dq_items, n_kv_items;
+};
+
+// Byte offsets of the backward workspace's parts.
+struct BwdLayout {
+  size_t qs, dos, dot, qht, rs, kh, vr, kht, pgq, pgk, total;
+};
+BwdLayout bwd_workspace_layout(long long tq, long long tk, int hq, int hk, int n_dq_items, int n_kv_items);
+hipError_t launch_bwd_bf16_d128(const BwdParams& p, hipStream_t stream);
+hipError_t launch_bwd_fp32(const BwdParams& p, int head_dim, hipStream_t stream);
+size_t bwd_workspace_bytes_fp32(long long tq, long long tk, int hq, int hk, int head_dim, int n_dq_items,
+                                int n_kv_items);
 
 hipError_t launch_fwd_bf16_d128(const FwdParams& p, int n_items, int n_merges, int n_slots, hipStream_t stream);
 size_t workspace_bytes_bf16(long long n_kt_img, int hk, int n_slots);

@@ -133,6 +133,34 @@ Tiling choose_tiling(int dtype, int head_dim, int group) {
   return t;
 }
 
+Tiling choose_bwd_tiling(int dtype, int head_dim, int group) {
+  Tiling t = choose_tiling(dtype, head_dim, group);
+  if (dtype == MAGI_DTYPE_BF16) {
+    // kBwdRowsPerItem rows per dq workgroup: 8 waves x 32 rows.
+    int hpw = 1;
+    for (int h = 1; h <= group; ++h)
+      if (group % h == 0 && kBwdRowsPerItem % h == 0) hpw = h;
+    t.heads_per_item = hpw;
+    t.tile_q = kBwdRowsPerItem / hpw;
+  }
+  return t;
+}
+
+void key_bounds(const magi_attn_layout_t* L, std::vector<RowBounds>& keys) {
+  // Query chunk c sees key chunk j of its video when j <= c and, with a KV
+  // range R, c <= j + R - 1: the queries of chunks [j, last] for the last such
+  // chunk, one contiguous token range.
+  const int32_t* kv = L->kv_offsets ? L->kv_offsets : L->q_offsets;
+  keys.assign(kv[L->n_chunks], RowBounds{0, 0});
+  for (int s = 0; s < L->n_seqs; ++s)
+    for (int j = L->seq_chunks[s]; j < L->seq_chunks[s + 1]; ++j) {
+      int last = L->seq_chunks[s + 1] - 1;
+      if (L->kv_range > 0 && j + L->kv_range - 1 < last) last = j + L->kv_range - 1;
+      const RowBounds b{L->q_offsets[j], L->q_offsets[last + 1]};
+      for (int32_t t = kv[j]; t < kv[j + 1]; ++t) keys[t] = b;
+    }
+}
+
 void row_bounds(const magi_attn_layout_t* L, std::vector<RowBounds>& rows) {
   const int32_t* kv = L->kv_offsets ? L->kv_offsets : L->q_offsets;
   rows.assign(L->q_offsets[L->n_chunks], RowBounds{0, 0});
@@ -170,7 +198,7 @@ int classify_pair(const std::vector<RowBounds>& iv, int64_t k0, int64_t k1, int6
 }
 
 magi_status_t build_host_plan(int32_t kind, const magi_attn_layout_t* L, const magi_attn_text_t* T,
-                              const Tiling& tiling, HostPlan& P, std::string& err) {
+                              const Tiling& tiling, HostPlan& P, std::string& err, bool allow_split) {
   (void)err;
   const int32_t* kv = L->kv_offsets ? L->kv_offsets : L->q_offsets;
   P.kind = kind;
@@ -275,7 +303,7 @@ magi_status_t build_host_plan(int32_t kind, const magi_attn_layout_t* L, const m
         n_whole += int64_t(P.hk) * groups_per_kvh;
         total_cost += int64_t(P.qt_ntiles[ph * n_qt + qt]) * P.hk * groups_per_kvh;
       }
-    const bool split = P.dtype == MAGI_DTYPE_BF16 && n_whole > 0 && n_whole < kSplitBelowItems;
+    const bool split = allow_split && P.dtype == MAGI_DTYPE_BF16 && n_whole > 0 && n_whole < kSplitBelowItems;
     const int64_t piece =
         std::max<int64_t>(kMinPieceTiles, (total_cost + kSplitTargetItems - 1) / kSplitTargetItems);
     for (int kvh = 0; kvh < P.hk; ++kvh)
@@ -358,6 +386,84 @@ magi_status_t build_host_plan(int32_t kind, const magi_attn_layout_t* L, const m
   S.tile_kv = bn;
   S.heads_per_item = hpw;
   S.n_items = int32_t(P.items.size());
+  return MAGI_OK;
+}
+
+magi_status_t build_bwd_plan(const magi_attn_layout_t* L, BwdHostPlan& B, std::string& err) {
+  const int group = L->n_q_heads / L->n_kv_heads;
+  magi_status_t s = build_host_plan(kPlanSelf, L, nullptr, choose_bwd_tiling(L->dtype, L->head_dim, group), B.dq, err,
+                                    /*allow_split=*/false);
+  if (s != MAGI_OK) return s;
+  const int32_t* kv = L->kv_offsets ? L->kv_offsets : L->q_offsets;
+  const int64_t tq = L->q_offsets[L->n_chunks], tk = kv[L->n_chunks];
+  const int kb_size = L->dtype == MAGI_DTYPE_BF16 ? kBwdKeysPerItem : 64;
+  const int tt_size = B.token_tile;
+  B.key_block = kb_size;
+  key_bounds(L, B.key_rows);
+
+  // Per key block: the token tiles that see any of its keys, full first.
+  const int64_t n_kb = (tk + kb_size - 1) / kb_size;
+  std::vector<int32_t> kb_begin(n_kb), kb_n(n_kb), kb_full(n_kb);
+  std::vector<int32_t> masked_codes;
+  std::vector<RowBounds> iv;
+  B.kv_tiles.clear();
+  for (int64_t kb = 0; kb < n_kb; ++kb) {
+    const int64_t k0 = kb * kb_size, k1 = std::min<int64_t>(tk, k0 + kb_size);
+    tile_intervals(B.key_rows, k0, k1, iv);
+    int64_t lo = INT64_MAX, hi = 0;
+    for (const RowBounds& b : iv)
+      if (b.hi > b.lo) { lo = std::min<int64_t>(lo, b.lo); hi = std::max<int64_t>(hi, b.hi); }
+    kb_begin[kb] = int32_t(B.kv_tiles.size());
+    masked_codes.clear();
+    if (hi > lo)
+      for (int64_t tt = lo / tt_size; tt < (hi + tt_size - 1) / tt_size; ++tt) {
+        const int cls = classify_pair(iv, tt * tt_size, tt * tt_size + tt_size, tq);
+        if (cls == 2) B.kv_tiles.push_back(tile_code(tt, 0));
+        else if (cls == 1) masked_codes.push_back(tile_code(tt, 1));
+      }
+    kb_full[kb] = int32_t(B.kv_tiles.size()) - kb_begin[kb];
+    B.kv_tiles.insert(B.kv_tiles.end(), masked_codes.begin(), masked_codes.end());
+    kb_n[kb] = int32_t(B.kv_tiles.size()) - kb_begin[kb];
+    B.kv_tiles.insert(B.kv_tiles.end(), kTilePad, -1);
+  }
+
+  // Items (key block, KV head), longest first, KV head -> XCD as for the
+  // forward's items.
+  struct Cand { int64_t cost; int32_t kb, kvh; };
+  std::vector<Cand> cands;
+  for (int kvh = 0; kvh < L->n_kv_heads; ++kvh)
+    for (int64_t kb = 0; kb < n_kb; ++kb)
+      if (kb_n[kb] > 0) cands.push_back(Cand{int64_t(kb_n[kb]) * group, int32_t(kb), kvh});
+  std::stable_sort(cands.begin(), cands.end(), [](const Cand& a, const Cand& b) {
+    if (a.cost != b.cost) return a.cost > b.cost;
+    if (a.kvh != b.kvh) return a.kvh < b.kvh;
+    return a.kb < b.kb;
+  });
+  const int hk = L->n_kv_heads;
+  std::vector<std::vector<KeyItem>> queues(kNumXcd);
+  std::vector<int64_t> load(kNumXcd, 0);
+  const bool by_head = hk % kNumXcd == 0 || kNumXcd % hk == 0;
+  const int per_head = hk >= kNumXcd ? 1 : kNumXcd / hk;
+  for (const Cand& c : cands) {
+    int best = -1;
+    if (by_head) {
+      for (int j = 0; j < per_head; ++j) {
+        const int x = hk >= kNumXcd ? c.kvh % kNumXcd : c.kvh * per_head + j;
+        if (best < 0 || load[x] < load[best]) best = x;
+      }
+    } else {
+      best = int(std::min_element(load.begin(), load.end()) - load.begin());
+    }
+    queues[best].push_back(KeyItem{c.kb, c.kvh, kb_begin[c.kb], kb_begin[c.kb] + kb_n[c.kb], kb_full[c.kb], {0, 0, 0}});
+    load[best] += c.cost;
+  }
+  size_t maxlen = 0;
+  for (auto& q : queues) maxlen = std::max(maxlen, q.size());
+  B.items.clear();
+  for (size_t j = 0; j < maxlen; ++j)
+    for (int x = 0; x < kNumXcd; ++x)
+      B.items.push_back(j < queues[x].size() ? queues[x][j] : KeyItem{0, 0, 0, 0, 0, {0, 0, 0}});
+  while (!B.items.empty() && B.items.back().tile_begin == B.items.back().tile_end) B.items.pop_back();
   return MAGI_OK;
 }
 

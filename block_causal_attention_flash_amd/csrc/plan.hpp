@@ -100,6 +100,30 @@ struct HostPlan {
   magi_attn_stats_t stats{};
 };
 
+// The backward's dk/dv work: keys [kb * key_block, (kb + 1) * key_block) of
+// KV head kvh over the token tiles whose codes (tt * 2 + masked) are
+// kv_tiles[tile_begin, tile_end), full tiles first; every query head of the
+// KV head's group is a step of its own. Lists are followed by kTilePad
+// padding codes (-1).
+struct KeyItem {
+  int32_t kb;
+  int32_t kvh;
+  int32_t tile_begin;
+  int32_t tile_end;    // == tile_begin: padding item
+  int32_t n_full;
+  int32_t pad[3];
+};
+
+// Backward work lists of a training plan.
+struct BwdHostPlan {
+  HostPlan dq;                       // query-stationary dq items (never split)
+  int32_t key_block = 0;             // keys per dk/dv item
+  int32_t token_tile = 32;           // tokens per dk/dv step
+  std::vector<RowBounds> key_rows;   // [tk] token bounds [qlo, qhi) of the queries that see each key
+  std::vector<int32_t> kv_tiles;     // per key block: token tile codes, full first, then boundary; padded
+  std::vector<KeyItem> items;        // launch order (XCD-interleaved, padded)
+};
+
 // First chunk whose keys chunk c of video s sees: the video's first chunk, or
 // with a KV range R, the later of that and c - R + 1.
 inline int first_visible_chunk(const magi_attn_layout_t* L, int s, int c) {
@@ -117,10 +141,20 @@ magi_status_t validate_text(const magi_attn_layout_t* layout, const magi_attn_te
 // Tiling used by the kernels for a dtype / head_dim / GQA group size.
 Tiling choose_tiling(int dtype, int head_dim, int group);
 
+// Tiling of the backward's dq items for a dtype / head_dim / GQA group size.
+Tiling choose_bwd_tiling(int dtype, int head_dim, int group);
+
 // Builds the full host plan of a kind (layout and text must already be
-// valid; text is unused for kPlanSelf).
+// valid; text is unused for kPlanSelf). allow_split = false keeps every work
+// item whole (the backward's dq lists).
 magi_status_t build_host_plan(int32_t kind, const magi_attn_layout_t* layout, const magi_attn_text_t* text,
-                              const Tiling& tiling, HostPlan& plan, std::string& err);
+                              const Tiling& tiling, HostPlan& plan, std::string& err, bool allow_split = true);
+
+// Builds the backward's work lists of a self-attention layout (valid).
+magi_status_t build_bwd_plan(const magi_attn_layout_t* layout, BwdHostPlan& plan, std::string& err);
+
+// Per-key token bounds [qlo, qhi): the queries that see each key.
+void key_bounds(const magi_attn_layout_t* layout, std::vector<RowBounds>& keys);
 
 // Per-query-token key bounds [lo, hi) of the block-causal self-attention
 // (layout must be valid).

@@ -13,7 +13,9 @@
  *     attention ("QK-Norm"), and query heads share key/value heads (GQA);
  *   - paperlayer §2.4.4: keys/values of clean chunks come from a KV cache, so
  *     the key stream may be longer than the query stream.
- * Beside it, the same library runs the block's text cross-attention
+ * The backward of the self-attention (dq, dk, dv and the gradients of both
+ * QK-norm gains) runs from the forward's saved log-sum-exp: see
+ * magi_attn_bwd. Beside it, the same library runs the block's text cross-attention
  * (paperlayer §2.2.2 and §2.2.3; paper-notes §3.2.2 and §3.2.6), alone or
  * together with the self-attention in one launch: see magi_attn_text_t.
  *
@@ -54,7 +56,7 @@
 extern "C" {
 #endif
 
-#define MAGI_ATTN_ABI_VERSION 3
+#define MAGI_ATTN_ABI_VERSION 4
 
 typedef enum magi_status {
   MAGI_OK = 0,
@@ -166,6 +168,17 @@ MAGI_API magi_status_t magi_attn_cross_plan_create(const magi_attn_layout_t* lay
 MAGI_API magi_status_t magi_attn_parallel_plan_create(const magi_attn_layout_t* layout,
                                                       const magi_attn_text_t* text, magi_attn_plan_t** plan);
 
+/*
+ * Plan for training: the self-attention plan of magi_attn_plan_create (it
+ * runs the forward with magi_attn_fwd) plus the work lists of the backward
+ * (magi_attn_bwd): query-stationary lists for dq and, for dk/dv, the token
+ * tiles that see each block of keys. Same rules and errors as
+ * magi_attn_plan_create; in addition, for bf16, T_q rounded up to a multiple
+ * of 32 times n_q_heads times 256 bytes must stay under 2 GiB (the
+ * backward's per-row images).
+ */
+MAGI_API magi_status_t magi_attn_train_plan_create(const magi_attn_layout_t* layout, magi_attn_plan_t** plan);
+
 /* Frees the plan and its device memory (synchronous with respect to the host;
  * the caller must not destroy a plan that queued work still uses). NULL is OK. */
 MAGI_API magi_status_t magi_attn_plan_destroy(magi_attn_plan_t* plan);
@@ -245,6 +258,50 @@ MAGI_API magi_status_t magi_attn_fwd_parallel(const magi_attn_plan_t* plan, cons
                                               float rms_eps, void* workspace, size_t workspace_bytes,
                                               void* stream);
 
+/* Device workspace bytes of magi_attn_bwd for a training plan (bf16: the
+ * re-laid-out queries, upstream gradients, keys and values, about
+ * 4 * |q| + 3 * |k| bytes; fp32: the normalised queries, 2 * |q|; plus
+ * per-workgroup gain partials). */
+MAGI_API magi_status_t magi_attn_bwd_workspace_size(const magi_attn_plan_t* plan, size_t* bytes);
+
+/*
+ * Tensors of one backward call. Inputs: q, k, v, q_gain, k_gain as given to
+ * the forward; out and lse that the forward returned for them; dout, the
+ * gradient of the loss with respect to out ([T_q][n_q_heads][head_dim], the
+ * element type of the layout). Outputs (caller-owned, written in full):
+ * dq [T_q][n_q_heads][head_dim], dk and dv [T_k][n_kv_heads][head_dim] (the
+ * element type of the layout), dq_gain and dk_gain [head_dim] float32.
+ */
+typedef struct magi_attn_bwd_io {
+  const void* q;
+  const void* k;
+  const void* v;
+  const float* q_gain;
+  const float* k_gain;
+  const void* out;
+  const float* lse;
+  const void* dout;
+  void* dq;
+  void* dk;
+  void* dv;
+  float* dq_gain;
+  float* dk_gain;
+} magi_attn_bwd_io_t;
+
+/*
+ * Enqueues the backward pass of the self-attention on `stream`: the
+ * gradients of a loss with respect to q, k, v and both gains, given its
+ * gradient dout with respect to out (the chain rule of the forward defined
+ * at the top; the attention's backward from saved softmax statistics,
+ * paperlayer §4.1.2 and §B.1). rms_eps and scale must be the forward's. The
+ * softmax is recomputed from lse, so lse must be the one the forward wrote
+ * for these inputs. Workspace, allocation and synchronisation rules as for
+ * magi_attn_fwd. Errors: MAGI_ERR_INVALID_ARG (not a training plan, NULL or
+ * misaligned pointer, workspace too small, bad eps or scale), MAGI_ERR_HIP.
+ */
+MAGI_API magi_status_t magi_attn_bwd(const magi_attn_plan_t* plan, const magi_attn_bwd_io_t* io, float rms_eps,
+                                     float scale, void* workspace, size_t workspace_bytes, void* stream);
+
 /*
  * One-shot form for a single video of self-attention (q and kv offsets both
  * = chunk_offsets[n_chunks+1], host array): builds a plan, allocates the
@@ -283,6 +340,13 @@ typedef struct magi_attn_stats {
 } magi_attn_stats_t;
 
 MAGI_API magi_status_t magi_attn_plan_stats(const magi_attn_layout_t* layout, magi_attn_stats_t* stats);
+
+/* Host-only: the classes of the backward's (key block, token tile) pairs:
+ * cls[kb * n_tt + tt] for blocks of `bk` keys and tiles of `bt` query
+ * tokens (n_kb = ceil(T_k/bk), n_tt = ceil(T_q/bt)), with the values and
+ * validation of magi_attn_classify_host. */
+MAGI_API magi_status_t magi_attn_key_classify_host(const magi_attn_layout_t* layout, int32_t bk, int32_t bt,
+                                                   int8_t* cls);
 
 /* Host-only: the tile classes of the cross-attention's text mask (as
  * magi_attn_classify_host, with n_kt = ceil(t_text / bn)). */

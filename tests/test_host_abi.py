@@ -34,7 +34,7 @@ def test_abi_version(built_lib):
     from block_causal_attention_flash_amd import magi_attn_abi_version
     hdr = open(os.path.join(ROOT, "include", "magi_attn.h")).read()
     declared = int(re.search(r"#define MAGI_ATTN_ABI_VERSION (\d+)", hdr).group(1))
-    assert magi_attn_abi_version() == declared == 3
+    assert magi_attn_abi_version() == declared == 4
 
 
 def brute_classes(layout, bm, bn, mask=None):
@@ -270,3 +270,23 @@ def test_prompt_draw_structure():
     assert t.t_text == max(t.end)
     st = prompt_draw(streaming_layout(3, 2, 4), 0, 1, seed=1)
     assert all(b == e for b, e in zip(st.begin[:3], st.end[:3]))
+
+
+@pytest.mark.parametrize("seed", range(30))
+def test_key_classifier_matches_transposed_mask(built_lib, seed):
+    """The backward's (key block, token tile) classes against the transpose
+    of the oracle's dense mask, for random layouts with and without a KV
+    range."""
+    from block_causal_attention_flash_amd import magi_attn_key_classify_host
+    rng = np.random.default_rng(2000 + seed)
+    lay = random_layout(rng)
+    if lay.t_q == 0:
+        pytest.skip("no queries")
+    for R in (0, int(rng.integers(1, 4))):
+        lw = Layout(lay.q_offsets, lay.kv_offsets, lay.seq_chunks, R)
+        mask = oracle.block_causal_mask(lw)
+        if (mask.sum(axis=1) == 0).any() and lw.t_q:
+            continue                          # a chunk with queries would see no key: rejected layout
+        for bk, bt in ((128, 32), (64, 32), (7, 5)):
+            got = magi_attn_key_classify_host(lw.q_offsets, lw.kv_offsets, lw.seq_chunks, bk=bk, bt=bt, kv_range=R)
+            np.testing.assert_array_equal(got, brute_classes(lw, bk, bt, mask.T.copy()))
