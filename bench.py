@@ -30,6 +30,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "block-causal attn fwd useful TFLOP/s and % bf16 MFMA peak, 1×MI355X"
 METRIC_CROSS = "text cross-attn fwd useful TFLOP/s and % bf16 MFMA peak, 1×MI355X"
+METRIC_BACKWARD = "block-causal attn bwd useful TFLOP/s (2.5x fwd FLOPs) and % bf16 MFMA peak, 1×MI355X"
 METRIC_PARALLEL = "parallel block-causal self- + text cross-attn fwd useful TFLOP/s and % bf16 MFMA peak, 1×MI355X"
 PEAK_BF16_TFLOPS = 2500.0          # MI355X dense bf16 MFMA, published
 KERNEL_SRC = os.path.join(ROOT, "block_causal_attention_flash_amd", "csrc", "fwd_bf16.hip")
@@ -133,6 +134,68 @@ def cpu_baseline(cfg, inp, budget_s: float = 20.0, attention: str = "self", text
                       f"{spent:.1f} s fp64 numpy on the host"}
 
 
+def bench_backward(args) -> None:
+    """One step = one backward call of the self-attention (the forward's out
+    and lse computed once before timing). Useful FLOPs: 2.5 x the forward's
+    (the five products S, dP, dV, dK, dQ over the mask area)."""
+    import numpy as np
+    import torch
+    from block_causal_attention_flash_amd import TrainPlan
+    from workloads import get_config, make_inputs
+
+    cfg = get_config(args.workload)
+    if args.kv_range:
+        cfg = dataclasses.replace(cfg, layout=dataclasses.replace(cfg.layout, kv_range=args.kv_range))
+    lay = cfg.layout
+    dev = torch.device("cuda", 0)
+    inp = make_inputs(lay, cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim, cfg.dtype, cfg.gain_kind, cfg.seed)
+    g = {n: t.to(dev) for n, t in inp.items()}
+    tdt = g["q"].dtype
+    dout = torch.from_numpy(np.random.default_rng(cfg.seed + 7).standard_normal(
+        (lay.t_q, cfg.n_q_heads, cfg.head_dim), dtype=np.float32)).to(tdt).to(dev)
+    t0 = time.perf_counter()
+    plan = TrainPlan.from_layout(lay, cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim, cfg.dtype)
+    plan_ms = (time.perf_counter() - t0) * 1e3
+    stream = torch.cuda.current_stream(dev)
+    out, lse = plan(g["q"], g["k"], g["v"], g["q_gain"], g["k_gain"], cfg.eps, cfg.scale, stream=stream)
+    ws = torch.empty(max(plan.bwd_workspace_size(), 16), dtype=torch.uint8, device=dev)
+    dq, dk, dv = torch.empty_like(g["q"]), torch.empty_like(g["k"]), torch.empty_like(g["v"])
+    dgq = torch.empty(cfg.head_dim, dtype=torch.float32, device=dev)
+    dgk = torch.empty_like(dgq)
+    step = lambda: plan.backward(g["q"], g["k"], g["v"], out, lse, dout, g["q_gain"], g["k_gain"], cfg.eps,  # noqa
+                                 cfg.scale, dq, dk, dv, dgq, dgk, ws, stream)
+    print(f"[bench] {cfg.name} backward: T_q={lay.t_q} T_k={lay.t_k} workspace={ws.numel() / 2**30:.2f} GiB "
+          f"plan={plan_ms:.1f}ms", file=sys.stderr, flush=True)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record(stream)
+    for _ in range(args.steps):
+        step()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    ms = ev0.elapsed_time(ev1) / args.steps
+    pairs = useful_pairs(lay)
+    flops = 2.5 * 4.0 * cfg.head_dim * cfg.n_q_heads * pairs
+    tflops = flops / (ms * 1e-3) / 1e12
+    roof = {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+            "frac": round(tflops / PEAK_BF16_TFLOPS, 4), "traffic": None}
+    rec = {
+        "metric": METRIC_BACKWARD, "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": cfg.dtype, "data": "synthetic (seeded N(0,1) Q/K/V/dO)",
+        "config": {"workload": cfg.name, "pass": "backward", "t_q": lay.t_q, "t_k": lay.t_k,
+                   "n_chunks": lay.n_chunks, "n_q_heads": cfg.n_q_heads, "n_kv_heads": cfg.n_kv_heads,
+                   "head_dim": cfg.head_dim, "kv_range": lay.kv_range, "useful_flops": flops,
+                   "unmasked_pairs_per_head": pairs},
+        "frac_of_peak": round(tflops / PEAK_BF16_TFLOPS, 4), "plan_create_ms": round(plan_ms, 2),
+        "roofline": roof, "cpu_baseline": None,
+    }
+    plan.close()
+    print(json.dumps(rec), flush=True)
+
+
 def copy_probe(mib: int) -> None:
     """A plain copy kernel of known size: reads and writes mib MiB per launch.
     Under rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE its readings give the factor
@@ -160,6 +223,8 @@ def main():
     ap.add_argument("--attention", choices=("self", "cross", "parallel"), default="self",
                     help="self: the block-causal self-attention; cross: the text cross-attention of the workload's "
                          "chunk-wise prompts; parallel: both in one launch")
+    ap.add_argument("--backward", action="store_true",
+                    help="time the self-attention's backward (magi_attn_bwd) instead of the forward")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=20.0)
     ap.add_argument("--copy-probe-mib", type=int, default=0,
@@ -173,6 +238,8 @@ def main():
               "share; see DESIGN.md for how the path would shard)", file=sys.stderr)
         sys.exit(2)
 
+    if args.backward:
+        return bench_backward(args)
     import torch
     from block_causal_attention_flash_amd import CrossPlan, ParallelPlan, Plan
     from workloads import get_config, make_inputs, make_text_inputs, text_layout

@@ -625,15 +625,32 @@ bwd_dkdv_kernel(BwdParams p, BwdLayout L, const int4* __restrict__ items, const 
   store_gain_partial(gp, sm.red, part, wave, lane, tid);
 }
 
-// Sums the per-workgroup gain partials in a fixed order.
-__global__ void __launch_bounds__(256) bwd_gain_reduce_kernel(const float* pgq, int nq, const float* pgk, int nk,
-                                                             float* dq_gain, float* dk_gain) {
-  const int t = threadIdx.x, d = t & 127;
-  const float* src = t < D ? pgq : pgk;
-  const int n = t < D ? nq : nk;
+// Sums the per-workgroup gain partials in a fixed order, in two levels:
+// workgroup b of REDUCE_SLICES (for dq, then as many for dk) sums the
+// partial rows [n b / S, n (b + 1) / S) into level[b]; the final pass sums
+// the S level rows. Threads: 2 halves x 128 dims.
+constexpr int REDUCE_SLICES = 256;
+__global__ void __launch_bounds__(256) bwd_gain_slices_kernel(const float* pgq, int nq, const float* pgk, int nk,
+                                                             float* level) {
+  const bool kside = blockIdx.x >= REDUCE_SLICES;
+  const int b = kside ? blockIdx.x - REDUCE_SLICES : blockIdx.x;
+  const float* src = kside ? pgk : pgq;
+  const int n = kside ? nk : nq;
+  const int i0 = int(int64_t(n) * b / REDUCE_SLICES), i1 = int(int64_t(n) * (b + 1) / REDUCE_SLICES);
+  __shared__ float half[D];
+  const int t = threadIdx.x, d = t & 127, h = t >> 7;
   float x = 0.0f;
-  for (int i = 0; i < n; ++i) x += src[size_t(i) * D + d];
-  (t < D ? dq_gain : dk_gain)[d] = x;
+  for (int i = i0 + h; i < i1; i += 2) x += src[size_t(i) * D + d];
+  if (h == 1) half[d] = x;
+  __syncthreads();
+  if (h == 0) level[size_t(blockIdx.x) * D + d] = x + half[d];
+}
+
+__global__ void __launch_bounds__(256) bwd_gain_final_kernel(const float* level, float* dq_gain, float* dk_gain) {
+  const int t = threadIdx.x, d = t & 127, side = t >> 7;
+  float x = 0.0f;
+  for (int b = 0; b < REDUCE_SLICES; ++b) x += level[size_t(side * REDUCE_SLICES + b) * D + d];
+  (side ? dk_gain : dq_gain)[d] = x;
 }
 
 }  // namespace
@@ -653,7 +670,8 @@ BwdLayout bwd_workspace_layout(long long tq, long long tk, int hq, int hk, int n
   L.kht = L.vr + up(kimg);
   L.pgq = L.kht + up(kimg);
   L.pgk = L.pgq + up(size_t(n_dq_items) * D * sizeof(float));
-  L.total = L.pgk + up(size_t(n_kv_items) * D * sizeof(float));
+  L.level = L.pgk + up(size_t(n_kv_items) * D * sizeof(float));
+  L.total = L.level + up(size_t(2 * REDUCE_SLICES) * D * sizeof(float));
   return L;
 }
 
@@ -668,8 +686,11 @@ hipError_t launch_bwd_bf16_d128(const BwdParams& p, hipStream_t stream) {
   if (p.n_kv_items > 0)
     hipLaunchKernelGGL(bwd_dkdv_kernel, dim3(p.n_kv_items), dim3(NTHR), 0, stream, p, L, p.kv_items, p.kv_tiles);
   unsigned char* ws = static_cast<unsigned char*>(p.ws);
-  hipLaunchKernelGGL(bwd_gain_reduce_kernel, dim3(1), dim3(256), 0, stream, reinterpret_cast<const float*>(ws + L.pgq),
-                     p.n_dq_items, reinterpret_cast<const float*>(ws + L.pgk), p.n_kv_items, p.dq_gain, p.dk_gain);
+  float* level = reinterpret_cast<float*>(ws + L.level);
+  hipLaunchKernelGGL(bwd_gain_slices_kernel, dim3(2 * REDUCE_SLICES), dim3(256), 0, stream,
+                     reinterpret_cast<const float*>(ws + L.pgq), p.n_dq_items,
+                     reinterpret_cast<const float*>(ws + L.pgk), p.n_kv_items, level);
+  hipLaunchKernelGGL(bwd_gain_final_kernel, dim3(1), dim3(256), 0, stream, level, p.dq_gain, p.dk_gain);
   return hipGetLastError();
 }
 

@@ -87,3 +87,65 @@ def attention_backward(q, k, v, q_gain, k_gain, eps: float, scale: float, layout
     dq = rms_norm_backward(uq, rq, gq, dqh)
     dk = rms_norm_backward(uk, rk, gk, dkh)
     return dq, dk, dv, gain_gradient(uq, dqh), gain_gradient(uk, dkh)
+
+
+def _row_terms(q, k, v, do, gq, gk, eps, scale, layout, rows):
+    """For query rows `rows`: q_hat, u, r of the rows, k_hat of all keys,
+    and per head the full-row P and dS (the chain rule restricted to rows)."""
+    tq, hq, d = q.shape
+    hk = k.shape[1]
+    group = hq // hk
+    rq = np.sqrt(np.mean(q[rows] ** 2, axis=-1, keepdims=True) + eps)
+    uq = q[rows] / rq
+    rk = np.sqrt(np.mean(k * k, axis=-1, keepdims=True) + eps)
+    kh = k / rk * gk
+    mask = dense.block_causal_mask(layout, rows)
+    ps, dss = [], []
+    for h in range(hq):
+        g = h // group
+        s = np.where(mask, scale * ((uq[:, h, :] * gq) @ kh[:, g, :].T), -np.inf)
+        e = np.where(mask, np.exp(s - np.max(s, axis=1, keepdims=True)), 0.0)
+        p = e / np.sum(e, axis=1, keepdims=True)
+        ps.append(p)
+        dss.append(softmax_backward(p, do[rows, h, :] @ v[:, g, :].T))
+    return uq, rq, kh, ps, dss
+
+
+def dq_rows(q, k, v, q_gain, k_gain, eps: float, scale: float, layout, dout, rows) -> np.ndarray:
+    """dq of the query rows `rows` only ([R, H_q, d]): the same chain rule as
+    attention_backward, evaluated for those rows."""
+    q, k, v, do = (dense._as_f64(x) for x in (q, k, v, dout))
+    gq, gk = dense._as_f64(q_gain), dense._as_f64(k_gain)
+    rows = np.asarray(rows, dtype=np.int64)
+    hq = q.shape[1]
+    group = hq // k.shape[1]
+    uq, rq, kh, _, dss = _row_terms(q, k, v, do, gq, gk, eps, scale, layout, rows)
+    dqh = np.stack([scale * (dss[h] @ kh[:, h // group, :]) for h in range(hq)], axis=1)
+    return rms_norm_backward(uq, rq, gq, dqh)
+
+
+def dkv_keys(q, k, v, q_gain, k_gain, eps: float, scale: float, layout, dout, keys
+             ) -> Tuple[np.ndarray, np.ndarray]:
+    """dk and dv of the keys `keys` only ([K, H_kv, d] each), summed over
+    every query row that sees them (each row's softmax over all its keys)."""
+    q, k, v, do = (dense._as_f64(x) for x in (q, k, v, dout))
+    gq, gk = dense._as_f64(q_gain), dense._as_f64(k_gain)
+    keys = np.asarray(keys, dtype=np.int64)
+    hq, hk = q.shape[1], k.shape[1]
+    group = hq // hk
+    tq = q.shape[0]
+    seen = np.zeros(tq, dtype=bool)
+    for r0 in range(0, tq, 1024):
+        seen[r0:r0 + 1024] = dense.block_causal_mask(layout, np.arange(r0, min(tq, r0 + 1024)))[:, keys].any(axis=1)
+    rows = np.nonzero(seen)[0]
+    dkh = np.zeros((len(keys), hk, q.shape[2]))
+    dv = np.zeros_like(dkh)
+    for b0 in range(0, len(rows), 256):
+        rb = rows[b0:b0 + 256]
+        uq, _, _, ps, dss = _row_terms(q, k, v, do, gq, gk, eps, scale, layout, rb)
+        for h in range(hq):
+            g = h // group
+            dkh[:, g, :] += scale * (dss[h][:, keys].T @ (uq[:, h, :] * gq))
+            dv[:, g, :] += ps[h][:, keys].T @ do[rb, h, :]
+    rk = np.sqrt(np.mean(k[keys] ** 2, axis=-1, keepdims=True) + eps)
+    return rms_norm_backward(k[keys] / rk, rk, gk, dkh), dv

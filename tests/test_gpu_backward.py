@@ -128,3 +128,77 @@ def test_backward_needs_a_training_plan():
         magi_attn_bwd(plan.handle, z, zk, zk, z, lse, z)
     assert e.value.status == 1
     plan.close()
+
+
+# ------------------------------------------------------------------ full-size workloads
+
+def _sample_rows(lay, n_random, seed):
+    rng = np.random.default_rng(seed)
+    rows = set()
+    for c in range(lay.n_chunks):
+        a, b = lay.q_offsets[c], lay.q_offsets[c + 1]
+        for r in (a, b - 1):
+            if a <= r < b:
+                rows.add(r)
+    rows.update(int(x) for x in rng.integers(0, lay.t_q, n_random))
+    return np.array(sorted(rows))
+
+
+@pytest.mark.parametrize("name", ["video480x832", "video256x2", "streaming", "packed8"])
+def test_backward_full_size(name):
+    """The workload at full size, in the launch configuration the benchmark
+    times: dq of sampled rows (chunk edges and random rows) against the
+    oracle; dk and dv of sampled keys of a late chunk (seen by few rows) on
+    the smaller workloads; and, over every row and key, properties that hold
+    at any size: sum_j dv_jg = sum over g's query rows of dO (softmax rows
+    sum to one), <q_i, dq_i> ~ 0 (RMSNorm is scale invariant), all finite."""
+    from workloads import get_config
+    from block_causal_attention_flash_amd import TrainPlan
+    c = get_config(name)
+    lay = c.layout
+    log(f"backward {name}: generating inputs")
+    inp = make_inputs(lay, c.n_q_heads, c.n_kv_heads, c.head_dim, c.dtype, c.gain_kind, c.seed)
+    dout = torch.from_numpy(np.random.default_rng(c.seed + 7).standard_normal(
+        (lay.t_q, c.n_q_heads, c.head_dim), dtype=np.float32)).to(torch.bfloat16)
+    g = {n: t.to(DEV) for n, t in inp.items()}
+    plan = TrainPlan.from_layout(lay, c.n_q_heads, c.n_kv_heads, c.head_dim, c.dtype)
+    log(f"backward {name}: GPU forward + backward")
+    out, lse = plan(g["q"], g["k"], g["v"], g["q_gain"], g["k_gain"], c.eps, c.scale)
+    dq, dk, dv, dgq, dgk = plan.backward(g["q"], g["k"], g["v"], out, lse, dout.to(DEV), g["q_gain"], g["k_gain"],
+                                         c.eps, c.scale)
+    torch.cuda.synchronize()
+    plan.close()
+    del out
+    for t in (dq, dk, dv, dgq, dgk):
+        assert bool(torch.isfinite(t).all())
+    # sum of dv over keys, per KV head, against the upstream gradients
+    G = c.n_q_heads // c.n_kv_heads
+    lhs = dv.double().sum(0)
+    rhs = dout.to(DEV).double().reshape(lay.t_q, c.n_kv_heads, G, c.head_dim).sum((0, 2))
+    err = float(torch.linalg.vector_norm(lhs - rhs) / torch.linalg.vector_norm(rhs))
+    log(f"backward {name}: sum dv identity rel {err:.2e}")
+    assert err <= 1e-2
+    # <q, dq> per row, relative to |q| |dq|
+    qd = (g["q"].float() * dq.float()).sum(-1).abs()
+    ratio = float((qd / (torch.linalg.vector_norm(g["q"].float(), dim=-1)
+                         * torch.linalg.vector_norm(dq.float(), dim=-1) + 1e-30)).max())
+    log(f"backward {name}: max |<q, dq>| / (|q| |dq|) {ratio:.2e}")
+    assert ratio <= 2e-2
+    rows = _sample_rows(lay, 8 if name == "video480x832" else 16, seed=c.seed)
+    log(f"backward {name}: dq oracle on {len(rows)} rows")
+    args = (inp["q"], inp["k"], inp["v"], inp["q_gain"], inp["k_gain"], c.eps, c.scale, lay, dout)
+    ref = oracle.dq_rows(*args, rows)
+    e_dq = rel_l2(dq[torch.as_tensor(rows, device=DEV)].double().cpu().numpy(), ref)
+    log(f"backward {name}: dq rows rel_l2 {e_dq:.2e}")
+    assert e_dq <= TOL["bf16"]
+    if name in ("video256x2", "streaming"):
+        last = lay.n_chunks - 1
+        keys = np.random.default_rng(c.seed).integers(lay.kv_offsets[last], lay.kv_offsets[last + 1], 6)
+        keys = np.unique(np.concatenate([keys, [lay.kv_offsets[last], lay.kv_offsets[last + 1] - 1]]))
+        log(f"backward {name}: dk/dv oracle on {len(keys)} keys")
+        rk, rv = oracle.dkv_keys(*args, keys)
+        kk = torch.as_tensor(keys, device=DEV)
+        e_dk = rel_l2(dk[kk].double().cpu().numpy(), rk)
+        e_dv = rel_l2(dv[kk].double().cpu().numpy(), rv)
+        log(f"backward {name}: dk keys rel_l2 {e_dk:.2e} dv keys rel_l2 {e_dv:.2e}")
+        assert e_dk <= TOL["bf16"] and e_dv <= TOL["bf16"]

@@ -148,6 +148,22 @@ def test_unseen_keys_get_no_gradient():
     assert np.max(np.abs(dk[:lay.kv_offsets[1]])) > 0
 
 
+@pytest.mark.parametrize("name", list(LAYOUTS))
+def test_row_and_key_restrictions_match_the_full_backward(name):
+    """dq_rows and dkv_keys (used on samples of full-size layouts) give the
+    full backward's rows and keys."""
+    lay = LAYOUTS[name]
+    inp, dout = case(lay, 6, 2, 8, seed=9)
+    args = (inp["q"], inp["k"], inp["v"], inp["q_gain"], inp["k_gain"], 1e-6, 0.5, lay, dout)
+    dq, dk, dv, _, _ = bwd_mod.attention_backward(*args)
+    rows = np.array([0, 3, lay.t_q - 1])
+    keys = np.array([0, lay.t_k // 2, lay.t_k - 1])
+    assert np.allclose(bwd_mod.dq_rows(*args, rows), dq[rows], rtol=1e-12, atol=1e-13)
+    gk, gv = bwd_mod.dkv_keys(*args, keys)
+    assert np.allclose(gk, dk[keys], rtol=1e-12, atol=1e-13)
+    assert np.allclose(gv, dv[keys], rtol=1e-12, atol=1e-13)
+
+
 # ----------------------------------------------------------------------------- planted mistakes
 
 _orig_softmax_backward = bwd_mod.softmax_backward
