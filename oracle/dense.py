@@ -84,7 +84,10 @@ def block_causal_mask(layout, rows: Optional[np.ndarray] = None) -> np.ndarray:
     within a chunk, causal across chunks; paper-notes Figure 15: no attention
     across packed videos). With a KV range R >= 1 (layout.kv_range; paperlayer
     §2.4.4, paper-notes §3.4.4 and Figure 12) the key's chunk must also be one
-    of the query chunk's R latest: kc > qc - R.
+    of the query chunk's R latest: kc > qc - R. With layout.last_global set, the
+    last video of the stream is a global block (paper-notes Figure 15(g),
+    paperlayer Figure 23: varlen block-causal with a last global block): its
+    queries see every key of the stream.
     """
     tq, tk = int(layout.q_offsets[-1]), int(layout.kv_offsets[-1])
     n_chunks = len(layout.q_offsets) - 1
@@ -99,7 +102,13 @@ def block_causal_mask(layout, rows: Optional[np.ndarray] = None) -> np.ndarray:
     R = int(getattr(layout, "kv_range", 0))
     if R > 0:
         mask &= kc[None, :] > qc[:, None] - R
+    if int(getattr(layout, "last_global", 0)):
+        mask[vid[qc] == n_seqs_of(layout) - 1, :] = True
     return mask
+
+
+def n_seqs_of(layout) -> int:
+    return len(layout.seq_chunks) - 1
 
 
 def unmasked_pairs(layout) -> int:
@@ -176,7 +185,8 @@ def attention_loops(q, k, v, q_gain, k_gain, eps: float, scale: float, layout
     Independent of numpy's reductions and of the dense-mask construction: a
     key is allowed for a query when both chunks belong to the same video and
     the key's chunk index is not larger than the query's (and, with a KV range
-    R, larger than the query's minus R). Tiny inputs only.
+    R, larger than the query's minus R); a query of a last global block sees
+    every key. Tiny inputs only.
     """
     q = _as_f64(q).tolist()
     k = _as_f64(k).tolist()
@@ -210,8 +220,11 @@ def attention_loops(q, k, v, q_gain, k_gain, eps: float, scale: float, layout
     for i in range(tq):
         ci = chunk_of(layout.q_offsets, i)
         R = int(getattr(layout, "kv_range", 0))
-        allowed = [j for j in range(tk)
-                   if video_of(kchunks[j]) == video_of(ci) and kchunks[j] <= ci and (R == 0 or kchunks[j] > ci - R)]
+        if int(getattr(layout, "last_global", 0)) and video_of(ci) == len(layout.seq_chunks) - 2:
+            allowed = list(range(tk))             # a query of the global block sees every key
+        else:
+            allowed = [j for j in range(tk)
+                       if video_of(kchunks[j]) == video_of(ci) and kchunks[j] <= ci and (R == 0 or kchunks[j] > ci - R)]
         for h in range(hq):
             g = h // group
             qi = norm(q[i][h], qg)

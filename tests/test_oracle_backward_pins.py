@@ -36,6 +36,8 @@ def mask_from_offsets(lay):
     m = (vid(qc)[:, None] == vid(kc)[None, :]) & (kc[None, :] <= qc[:, None])
     if lay.kv_range:
         m &= kc[None, :] > qc[:, None] - lay.kv_range
+    if lay.last_global:
+        m[vid(qc) == len(lay.seq_chunks) - 2, :] = True
     return torch.from_numpy(m)
 
 
@@ -71,6 +73,7 @@ LAYOUTS = {
     "packed": layout_from_chunks([[5, 7, 3], [4], [2, 6]]),
     "streaming": streaming_layout(3, 2, 4),
     "window": dataclasses.replace(layout_from_chunks([[3, 4, 2, 5, 3]]), kv_range=2),
+    "last_global": dataclasses.replace(layout_from_chunks([[5, 7, 3], [4, 2], [3, 4]]), last_global=1),
 }
 
 

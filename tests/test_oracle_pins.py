@@ -492,3 +492,53 @@ def _lse_log2_attention(*args, **kw):
     """Mutant: log-sum-exp reported in base 2."""
     o, l = _orig_attention(*args, **kw)
     return o, l / math.log(2.0)
+
+
+# ----------------------------------------------------------------------------- last global block
+
+def global_case():
+    base = layout_from_chunks([[7, 5, 9], [4, 6], [3, 8]])
+    return Layout(base.q_offsets, base.kv_offsets, base.seq_chunks, 0, 1)
+
+
+def check_global_rows(fn=oracle.attention):
+    """The last video's queries (the global block) attend to every key of the
+    stream: full attention over all keys (SDPA); every other row is as
+    without the flag."""
+    lay = global_case()
+    inp = small_inputs(lay, 4, 2, 16, seed=31)
+    out, lse = fn(inp["q"], inp["k"], inp["v"], inp["q_gain"], inp["k_gain"], 1e-6, 0.3, lay)
+    g0 = lay.q_offsets[lay.seq_chunks[-2]]
+    ref = lib_attention(inp["q"][g0:], inp["k"], inp["v"], inp["q_gain"], inp["k_gain"], 1e-6, 0.3)
+    plain = Layout(lay.q_offsets, lay.kv_offsets, lay.seq_chunks)
+    o2, _ = oracle.attention(inp["q"], inp["k"], inp["v"], inp["q_gain"], inp["k_gain"], 1e-6, 0.3, plain)
+    return np.allclose(out[g0:], ref, rtol=1e-12, atol=1e-12) and np.array_equal(out[:g0], o2[:g0])
+
+
+def test_last_global_block_is_full_attention_over_the_stream():
+    assert check_global_rows()
+
+
+def test_last_global_block_brute_force_loops():
+    lay = global_case()
+    inp = small_inputs(lay, 4, 2, 8, seed=32)
+    a = (inp["q"], inp["k"], inp["v"], inp["q_gain"], inp["k_gain"], 1e-6, 0.5, lay)
+    o1, l1 = oracle.attention(*a)
+    o2, l2 = oracle.attention_loops(*a)
+    assert np.allclose(o1, o2, rtol=1e-12, atol=1e-12) and np.allclose(l1, l2, rtol=1e-12, atol=1e-12)
+
+
+def test_last_global_block_mask_area():
+    lay = global_case()
+    plain = Layout(lay.q_offsets, lay.kv_offsets, lay.seq_chunks)
+    g0 = lay.q_offsets[lay.seq_chunks[-2]]
+    own = int(oracle.block_causal_mask(plain)[:g0].sum())
+    assert oracle.unmasked_pairs(lay) == own + (lay.t_q - g0) * lay.t_k
+
+
+def test_planted_global_mistake_is_caught(monkeypatch):
+    """Mutant: the global flag is ignored (the last video stays block-causal)."""
+    monkeypatch.setattr(oracle_mod, "block_causal_mask",
+                        lambda lay, rows=None: _orig_mask(Layout(lay.q_offsets, lay.kv_offsets, lay.seq_chunks,
+                                                                 lay.kv_range), rows))
+    assert not check_global_rows(oracle_mod.attention)

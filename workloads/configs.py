@@ -30,6 +30,7 @@ class Layout:
     kv_offsets: tuple
     seq_chunks: tuple
     kv_range: int = 0      # 0: block-causal; R >= 1: a chunk sees the last R chunks of its video
+    last_global: int = 0   # 1: the last video is a global block whose queries see every key of the stream
 
     @property
     def n_chunks(self) -> int:
