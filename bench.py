@@ -1,7 +1,7 @@
 """Benchmark of the block-causal attention forward on one MI355X.
 
-python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--kv-range R]
-                [--attention self|cross|parallel] [--no-cpu-baseline]
+python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--kv-range R] [--last-global]
+                [--attention self|cross|parallel] [--backward] [--no-cpu-baseline]
 
 A step is one forward call (query/key RMSNorm, masked softmax attention, LSE)
 over the whole workload, inputs resident in HBM: the block-causal
@@ -39,14 +39,18 @@ KERNEL_SRC = os.path.join(ROOT, "block_causal_attention_flash_amd", "csrc", "fwd
 def useful_pairs(layout) -> int:
     """Allowed (query, key) pairs per head, from the offsets: every query of
     chunk c sees keys from its video's first key (or, with a KV range R, from
-    chunk c - R + 1 if later) to the end of chunk c."""
+    chunk c - R + 1 if later) to the end of chunk c; a last global block's
+    queries see all T_k keys."""
     R = int(getattr(layout, "kv_range", 0))
+    G = int(getattr(layout, "last_global", 0))
     total = 0
     for s in range(layout.n_seqs):
         c0, c1 = layout.seq_chunks[s], layout.seq_chunks[s + 1]
         for c in range(c0, c1):
             first = max(c0, c - R + 1) if R > 0 else c0
-            total += (layout.q_offsets[c + 1] - layout.q_offsets[c]) * (layout.kv_offsets[c + 1] - layout.kv_offsets[first])
+            keys = layout.kv_offsets[-1] if (G and s == layout.n_seqs - 1) else \
+                layout.kv_offsets[c + 1] - layout.kv_offsets[first]
+            total += (layout.q_offsets[c + 1] - layout.q_offsets[c]) * keys
     return total
 
 
@@ -119,7 +123,9 @@ def cpu_baseline(cfg, inp, budget_s: float = 20.0, attention: str = "self", text
         if attention in ("self", "parallel"):
             oracle.attention(inp["q"], inp["k"], inp["v"], inp["q_gain"], inp["k_gain"], cfg.eps, cfg.scale, lay,
                              rows=rows)
-            flops += 4.0 * d * hq * len(rows) * (lay.kv_offsets[c + 1] - lay.kv_offsets[first_visible(lay, c)])
+            glob = lay.last_global and c >= lay.seq_chunks[-2]
+            keys = lay.t_k if glob else lay.kv_offsets[c + 1] - lay.kv_offsets[first_visible(lay, c)]
+            flops += 4.0 * d * hq * len(rows) * keys
         if attention in ("cross", "parallel"):
             oracle.cross_attention(inp["q"], tx["k_x"], tx["v_x"], tx["q_gain_x"], tx["k_gain_x"], cfg.eps,
                                    cfg.scale, lay.q_offsets, text, rows=rows)
@@ -144,8 +150,9 @@ def bench_backward(args) -> None:
     from workloads import get_config, make_inputs
 
     cfg = get_config(args.workload)
-    if args.kv_range:
-        cfg = dataclasses.replace(cfg, layout=dataclasses.replace(cfg.layout, kv_range=args.kv_range))
+    if args.kv_range or args.last_global:
+        cfg = dataclasses.replace(cfg, layout=dataclasses.replace(cfg.layout, kv_range=args.kv_range,
+                                                                  last_global=int(args.last_global)))
     lay = cfg.layout
     dev = torch.device("cuda", 0)
     inp = make_inputs(lay, cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim, cfg.dtype, cfg.gain_kind, cfg.seed)
@@ -187,8 +194,8 @@ def bench_backward(args) -> None:
         "vs_baseline": None, "dtype": cfg.dtype, "data": "synthetic (seeded N(0,1) Q/K/V/dO)",
         "config": {"workload": cfg.name, "pass": "backward", "t_q": lay.t_q, "t_k": lay.t_k,
                    "n_chunks": lay.n_chunks, "n_q_heads": cfg.n_q_heads, "n_kv_heads": cfg.n_kv_heads,
-                   "head_dim": cfg.head_dim, "kv_range": lay.kv_range, "useful_flops": flops,
-                   "unmasked_pairs_per_head": pairs},
+                   "head_dim": cfg.head_dim, "kv_range": lay.kv_range, "last_global": lay.last_global,
+                   "useful_flops": flops, "unmasked_pairs_per_head": pairs},
         "frac_of_peak": round(tflops / PEAK_BF16_TFLOPS, 4), "plan_create_ms": round(plan_ms, 2),
         "roofline": roof, "cpu_baseline": None,
     }
@@ -220,6 +227,8 @@ def main():
     ap.add_argument("--workload", default="video480x832")
     ap.add_argument("--kv-range", type=int, default=0,
                     help="KV-range window in chunks (0: every earlier chunk of the video is visible)")
+    ap.add_argument("--last-global", action="store_true",
+                    help="the workload's last video is a global block whose queries see every key of the stream")
     ap.add_argument("--attention", choices=("self", "cross", "parallel"), default="self",
                     help="self: the block-causal self-attention; cross: the text cross-attention of the workload's "
                          "chunk-wise prompts; parallel: both in one launch")
@@ -245,8 +254,9 @@ def main():
     from workloads import get_config, make_inputs, make_text_inputs, text_layout
 
     cfg = get_config(args.workload)
-    if args.kv_range:
-        cfg = dataclasses.replace(cfg, layout=dataclasses.replace(cfg.layout, kv_range=args.kv_range))
+    if args.kv_range or args.last_global:
+        cfg = dataclasses.replace(cfg, layout=dataclasses.replace(cfg.layout, kv_range=args.kv_range,
+                                                                  last_global=int(args.last_global)))
     lay = cfg.layout
     mode = args.attention
     text = text_layout(cfg) if mode != "self" else None
@@ -304,7 +314,7 @@ def main():
     pairs_x = useful_text_pairs(lay, text) if mode != "self" else 0
     flops = 4.0 * cfg.head_dim * cfg.n_q_heads * (pairs + pairs_x)
     tflops = flops / (ms * 1e-3) / 1e12
-    traffic = stored_traffic(cfg.name, mode) if not lay.kv_range else None
+    traffic = stored_traffic(cfg.name, mode) if not (lay.kv_range or lay.last_global) else None
     roof = {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
             "frac": round(tflops / PEAK_BF16_TFLOPS, 4), "traffic": traffic}
 
@@ -315,8 +325,8 @@ def main():
 
     config = {"workload": cfg.name, "attention": mode, "t_q": lay.t_q, "t_k": lay.t_k, "n_chunks": lay.n_chunks,
               "n_videos": lay.n_seqs, "n_q_heads": cfg.n_q_heads, "n_kv_heads": cfg.n_kv_heads,
-              "head_dim": cfg.head_dim, "kv_range": lay.kv_range, "useful_flops": flops,
-              "unmasked_pairs_per_head": pairs}
+              "head_dim": cfg.head_dim, "kv_range": lay.kv_range, "last_global": lay.last_global,
+              "useful_flops": flops, "unmasked_pairs_per_head": pairs}
     if text is not None:
         config.update({"t_text": text.t_text, "text_pairs_per_head": pairs_x})
     rec = {

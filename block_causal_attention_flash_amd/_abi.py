@@ -34,6 +34,7 @@ class Layout(ctypes.Structure):
         ("head_dim", ctypes.c_int32),
         ("dtype", ctypes.c_int32),
         ("kv_range", ctypes.c_int32),
+        ("last_global", ctypes.c_int32),
     ]
 
 

@@ -31,7 +31,7 @@ def _arr(x) -> np.ndarray:
 class _LayoutArgs:
     """Keeps the host offset arrays alive for the duration of a call."""
 
-    def __init__(self, q_offsets, kv_offsets, seq_chunks, n_q_heads, n_kv_heads, head_dim, dtype, kv_range=0):
+    def __init__(self, q_offsets, kv_offsets, seq_chunks, n_q_heads, n_kv_heads, head_dim, dtype, kv_range=0, last_global=0):
         self.q = _arr(q_offsets)
         self.kv = None if kv_offsets is None else _arr(kv_offsets)
         n_chunks = len(self.q) - 1
@@ -39,7 +39,8 @@ class _LayoutArgs:
         p = lambda a: None if a is None else a.ctypes.data_as(_abi._i32p)  # noqa: E731
         dt = _DTYPES[dtype] if isinstance(dtype, str) else int(dtype)
         self.struct = _abi.Layout(len(self.seq) - 1, p(self.seq), n_chunks, p(self.q), p(self.kv),
-                                  int(n_q_heads), int(n_kv_heads), int(head_dim), dt, int(kv_range))
+                                  int(n_q_heads), int(n_kv_heads), int(head_dim), dt, int(kv_range),
+                                  int(last_global))
 
     def ptr(self):
         return ctypes.byref(self.struct)
@@ -62,18 +63,18 @@ def magi_attn_abi_version() -> int:
 
 
 def magi_attn_plan_stats(q_offsets, kv_offsets=None, seq_chunks=None, n_q_heads=1, n_kv_heads=1, head_dim=128,
-                         dtype="bf16", kv_range=0) -> dict:
+                         dtype="bf16", kv_range=0, last_global=0) -> dict:
     lib = _abi.load()
-    la = _LayoutArgs(q_offsets, kv_offsets, seq_chunks, n_q_heads, n_kv_heads, head_dim, dtype, kv_range)
+    la = _LayoutArgs(q_offsets, kv_offsets, seq_chunks, n_q_heads, n_kv_heads, head_dim, dtype, kv_range, last_global)
     st = _abi.Stats()
     _check(lib, lib.magi_attn_plan_stats(la.ptr(), ctypes.byref(st)))
     return {name: getattr(st, name) for name, _ in _abi.Stats._fields_}
 
 
 def magi_attn_classify_host(q_offsets, kv_offsets=None, seq_chunks=None, bm=128, bn=64, n_q_heads=1, n_kv_heads=1,
-                            head_dim=128, dtype="bf16", kv_range=0) -> np.ndarray:
+                            head_dim=128, dtype="bf16", kv_range=0, last_global=0) -> np.ndarray:
     lib = _abi.load()
-    la = _LayoutArgs(q_offsets, kv_offsets, seq_chunks, n_q_heads, n_kv_heads, head_dim, dtype, kv_range)
+    la = _LayoutArgs(q_offsets, kv_offsets, seq_chunks, n_q_heads, n_kv_heads, head_dim, dtype, kv_range, last_global)
     tq = int(la.q[-1])
     tk = int((la.kv if la.kv is not None else la.q)[-1])
     n_qt, n_kt = -(-tq // bm), -(-tk // bn)
@@ -83,9 +84,9 @@ def magi_attn_classify_host(q_offsets, kv_offsets=None, seq_chunks=None, bm=128,
 
 
 def magi_attn_key_classify_host(q_offsets, kv_offsets=None, seq_chunks=None, bk=128, bt=32, n_q_heads=1, n_kv_heads=1,
-                                head_dim=128, dtype="bf16", kv_range=0) -> np.ndarray:
+                                head_dim=128, dtype="bf16", kv_range=0, last_global=0) -> np.ndarray:
     lib = _abi.load()
-    la = _LayoutArgs(q_offsets, kv_offsets, seq_chunks, n_q_heads, n_kv_heads, head_dim, dtype, kv_range)
+    la = _LayoutArgs(q_offsets, kv_offsets, seq_chunks, n_q_heads, n_kv_heads, head_dim, dtype, kv_range, last_global)
     tq = int(la.q[-1])
     tk = int((la.kv if la.kv is not None else la.q)[-1])
     cls = np.zeros((max(-(-tk // bk), 0), max(-(-tq // bt), 0)), dtype=np.int8)
@@ -95,9 +96,9 @@ def magi_attn_key_classify_host(q_offsets, kv_offsets=None, seq_chunks=None, bk=
 
 def magi_attn_cross_classify_host(q_offsets, text_begin, text_end, t_text, bm=128, bn=64, kv_offsets=None,
                                   seq_chunks=None, n_q_heads=1, n_kv_heads=1, head_dim=128, dtype="bf16",
-                                  kv_range=0) -> np.ndarray:
+                                  kv_range=0, last_global=0) -> np.ndarray:
     lib = _abi.load()
-    la = _LayoutArgs(q_offsets, kv_offsets, seq_chunks, n_q_heads, n_kv_heads, head_dim, dtype, kv_range)
+    la = _LayoutArgs(q_offsets, kv_offsets, seq_chunks, n_q_heads, n_kv_heads, head_dim, dtype, kv_range, last_global)
     ta = _TextArgs(text_begin, text_end, t_text)
     n_qt, n_kt = -(-int(la.q[-1]) // bm), -(-int(t_text) // bn)
     cls = np.zeros((max(n_qt, 0), max(n_kt, 0)), dtype=np.int8)
@@ -107,10 +108,10 @@ def magi_attn_cross_classify_host(q_offsets, text_begin, text_end, t_text, bm=12
 
 
 def magi_attn_cross_plan_stats(q_offsets, text_begin, text_end, t_text, kv_offsets=None, seq_chunks=None,
-                               n_q_heads=1, n_kv_heads=1, head_dim=128, dtype="bf16", kv_range=0,
+                               n_q_heads=1, n_kv_heads=1, head_dim=128, dtype="bf16", kv_range=0, last_global=0,
                                with_self=False) -> dict:
     lib = _abi.load()
-    la = _LayoutArgs(q_offsets, kv_offsets, seq_chunks, n_q_heads, n_kv_heads, head_dim, dtype, kv_range)
+    la = _LayoutArgs(q_offsets, kv_offsets, seq_chunks, n_q_heads, n_kv_heads, head_dim, dtype, kv_range, last_global)
     ta = _TextArgs(text_begin, text_end, t_text)
     st = _abi.Stats()
     _check(lib, lib.magi_attn_cross_plan_stats(la.ptr(), ta.ptr(), int(bool(with_self)), ctypes.byref(st)))
@@ -118,19 +119,19 @@ def magi_attn_cross_plan_stats(q_offsets, text_begin, text_end, t_text, kv_offse
 
 
 def magi_attn_plan_create(q_offsets, kv_offsets=None, seq_chunks=None, n_q_heads=1, n_kv_heads=1, head_dim=128,
-                          dtype="bf16", kv_range=0) -> int:
+                          dtype="bf16", kv_range=0, last_global=0) -> int:
     """Returns the opaque plan handle (an integer address)."""
     lib = _abi.load()
-    la = _LayoutArgs(q_offsets, kv_offsets, seq_chunks, n_q_heads, n_kv_heads, head_dim, dtype, kv_range)
+    la = _LayoutArgs(q_offsets, kv_offsets, seq_chunks, n_q_heads, n_kv_heads, head_dim, dtype, kv_range, last_global)
     h = ctypes.c_void_p()
     _check(lib, lib.magi_attn_plan_create(la.ptr(), ctypes.byref(h)))
     return h.value
 
 
 def magi_attn_train_plan_create(q_offsets, kv_offsets=None, seq_chunks=None, n_q_heads=1, n_kv_heads=1, head_dim=128,
-                                dtype="bf16", kv_range=0) -> int:
+                                dtype="bf16", kv_range=0, last_global=0) -> int:
     lib = _abi.load()
-    la = _LayoutArgs(q_offsets, kv_offsets, seq_chunks, n_q_heads, n_kv_heads, head_dim, dtype, kv_range)
+    la = _LayoutArgs(q_offsets, kv_offsets, seq_chunks, n_q_heads, n_kv_heads, head_dim, dtype, kv_range, last_global)
     h = ctypes.c_void_p()
     _check(lib, lib.magi_attn_train_plan_create(la.ptr(), ctypes.byref(h)))
     return h.value
@@ -175,9 +176,9 @@ def magi_attn_bwd(handle: int, q, k, v, out, lse, dout, q_gain=None, k_gain=None
 
 
 def magi_attn_cross_plan_create(q_offsets, text_begin, text_end, t_text, kv_offsets=None, seq_chunks=None,
-                                n_q_heads=1, n_kv_heads=1, head_dim=128, dtype="bf16", kv_range=0) -> int:
+                                n_q_heads=1, n_kv_heads=1, head_dim=128, dtype="bf16", kv_range=0, last_global=0) -> int:
     lib = _abi.load()
-    la = _LayoutArgs(q_offsets, kv_offsets, seq_chunks, n_q_heads, n_kv_heads, head_dim, dtype, kv_range)
+    la = _LayoutArgs(q_offsets, kv_offsets, seq_chunks, n_q_heads, n_kv_heads, head_dim, dtype, kv_range, last_global)
     ta = _TextArgs(text_begin, text_end, t_text)
     h = ctypes.c_void_p()
     _check(lib, lib.magi_attn_cross_plan_create(la.ptr(), ta.ptr(), ctypes.byref(h)))
@@ -185,9 +186,9 @@ def magi_attn_cross_plan_create(q_offsets, text_begin, text_end, t_text, kv_offs
 
 
 def magi_attn_parallel_plan_create(q_offsets, text_begin, text_end, t_text, kv_offsets=None, seq_chunks=None,
-                                   n_q_heads=1, n_kv_heads=1, head_dim=128, dtype="bf16", kv_range=0) -> int:
+                                   n_q_heads=1, n_kv_heads=1, head_dim=128, dtype="bf16", kv_range=0, last_global=0) -> int:
     lib = _abi.load()
-    la = _LayoutArgs(q_offsets, kv_offsets, seq_chunks, n_q_heads, n_kv_heads, head_dim, dtype, kv_range)
+    la = _LayoutArgs(q_offsets, kv_offsets, seq_chunks, n_q_heads, n_kv_heads, head_dim, dtype, kv_range, last_global)
     ta = _TextArgs(text_begin, text_end, t_text)
     h = ctypes.c_void_p()
     _check(lib, lib.magi_attn_parallel_plan_create(la.ptr(), ta.ptr(), ctypes.byref(h)))
@@ -311,12 +312,12 @@ class Plan:
     """Owns a plan handle for one layout; call() runs the forward."""
 
     def __init__(self, q_offsets, kv_offsets=None, seq_chunks=None, n_q_heads=1, n_kv_heads=1, head_dim=128,
-                 dtype="bf16", kv_range=0):
+                 dtype="bf16", kv_range=0, last_global=0):
         self.layout = dict(q_offsets=list(map(int, q_offsets)),
                            kv_offsets=None if kv_offsets is None else list(map(int, kv_offsets)),
                            seq_chunks=None if seq_chunks is None else list(map(int, seq_chunks)),
                            n_q_heads=n_q_heads, n_kv_heads=n_kv_heads, head_dim=head_dim, dtype=dtype,
-                           kv_range=int(kv_range))
+                           kv_range=int(kv_range), last_global=int(last_global))
         self.n_q_heads, self.n_kv_heads, self.head_dim, self.dtype = n_q_heads, n_kv_heads, head_dim, dtype
         self.t_q = int(self.layout["q_offsets"][-1])
         kv = self.layout["kv_offsets"] or self.layout["q_offsets"]
@@ -330,7 +331,7 @@ class Plan:
     @classmethod
     def from_layout(cls, layout, n_q_heads, n_kv_heads, head_dim, dtype="bf16"):
         return cls(layout.q_offsets, layout.kv_offsets, layout.seq_chunks, n_q_heads, n_kv_heads, head_dim, dtype,
-                   getattr(layout, "kv_range", 0))
+                   getattr(layout, "kv_range", 0), getattr(layout, "last_global", 0))
 
     def stats(self) -> dict:
         return magi_attn_plan_stats(**self.layout)
@@ -374,10 +375,10 @@ class CrossPlan(Plan):
     with the cross-attention's gains and temperature."""
 
     def __init__(self, q_offsets, text_begin, text_end, t_text, kv_offsets=None, seq_chunks=None, n_q_heads=1,
-                 n_kv_heads=1, head_dim=128, dtype="bf16", kv_range=0):
+                 n_kv_heads=1, head_dim=128, dtype="bf16", kv_range=0, last_global=0):
         self.text = dict(text_begin=list(map(int, text_begin)), text_end=list(map(int, text_end)),
                          t_text=int(t_text))
-        super().__init__(q_offsets, kv_offsets, seq_chunks, n_q_heads, n_kv_heads, head_dim, dtype, kv_range)
+        super().__init__(q_offsets, kv_offsets, seq_chunks, n_q_heads, n_kv_heads, head_dim, dtype, kv_range, last_global)
         self.t_k = self.text["t_text"]
 
     def _create(self) -> int:
@@ -386,7 +387,8 @@ class CrossPlan(Plan):
     @classmethod
     def from_layout(cls, layout, text, n_q_heads, n_kv_heads, head_dim, dtype="bf16"):
         return cls(layout.q_offsets, text.begin, text.end, text.t_text, layout.kv_offsets, layout.seq_chunks,
-                   n_q_heads, n_kv_heads, head_dim, dtype, getattr(layout, "kv_range", 0))
+                   n_q_heads, n_kv_heads, head_dim, dtype, getattr(layout, "kv_range", 0),
+                   getattr(layout, "last_global", 0))
 
     def stats(self) -> dict:
         return magi_attn_cross_plan_stats(**self.layout, **self.text)
@@ -397,10 +399,10 @@ class ParallelPlan(Plan):
     and the cross-attention of a text, run as one pass by call()."""
 
     def __init__(self, q_offsets, text_begin, text_end, t_text, kv_offsets=None, seq_chunks=None, n_q_heads=1,
-                 n_kv_heads=1, head_dim=128, dtype="bf16", kv_range=0):
+                 n_kv_heads=1, head_dim=128, dtype="bf16", kv_range=0, last_global=0):
         self.text = dict(text_begin=list(map(int, text_begin)), text_end=list(map(int, text_end)),
                          t_text=int(t_text))
-        super().__init__(q_offsets, kv_offsets, seq_chunks, n_q_heads, n_kv_heads, head_dim, dtype, kv_range)
+        super().__init__(q_offsets, kv_offsets, seq_chunks, n_q_heads, n_kv_heads, head_dim, dtype, kv_range, last_global)
 
     def _create(self) -> int:
         return magi_attn_parallel_plan_create(**self.layout, **self.text)
@@ -408,7 +410,8 @@ class ParallelPlan(Plan):
     @classmethod
     def from_layout(cls, layout, text, n_q_heads, n_kv_heads, head_dim, dtype="bf16"):
         return cls(layout.q_offsets, text.begin, text.end, text.t_text, layout.kv_offsets, layout.seq_chunks,
-                   n_q_heads, n_kv_heads, head_dim, dtype, getattr(layout, "kv_range", 0))
+                   n_q_heads, n_kv_heads, head_dim, dtype, getattr(layout, "kv_range", 0),
+                   getattr(layout, "last_global", 0))
 
     def stats(self) -> dict:
         return magi_attn_cross_plan_stats(**self.layout, **self.text, with_self=True)

@@ -27,7 +27,7 @@ struct magi_attn_plan {
   const unsigned* d_dq_soffs = nullptr;
   const int4* d_kv_items = nullptr;
   const int* d_kv_tiles = nullptr;
-  const int2* d_key_rows = nullptr;
+  const int4* d_key_rows = nullptr;
 };
 
 namespace {
@@ -163,7 +163,7 @@ magi_status_t create_plan(int32_t kind, bool train, const magi_attn_layout_t* la
   p->d_dq_soffs = reinterpret_cast<const unsigned*>(base + o_dq_soffs);
   p->d_kv_items = reinterpret_cast<const int4*>(base + o_kv_items);
   p->d_kv_tiles = reinterpret_cast<const int*>(base + o_kv_tiles);
-  p->d_key_rows = reinterpret_cast<const int2*>(base + o_key_rows);
+  p->d_key_rows = reinterpret_cast<const int4*>(base + o_key_rows);
   *out_plan = p;
   return MAGI_OK;
 }
@@ -261,10 +261,17 @@ magi_status_t magi_attn_key_classify_host(const magi_attn_layout_t* layout, int3
   if (s != MAGI_OK) return fail(s, err);
   if (bk < 1 || bt < 1) return fail(MAGI_ERR_INVALID_ARG, "tile sizes must be positive");
   if (!cls) return fail(MAGI_ERR_INVALID_ARG, "cls is NULL");
-  std::vector<magi::RowBounds> keys;
+  std::vector<magi::KeyBounds> keys;
   magi::key_bounds(layout, keys);
   const int32_t* kv = layout->kv_offsets ? layout->kv_offsets : layout->q_offsets;
-  classify_rows(keys, kv[layout->n_chunks], layout->q_offsets[layout->n_chunks], bk, bt, cls);
+  const int64_t tk = kv[layout->n_chunks], tq = layout->q_offsets[layout->n_chunks];
+  const int64_t n_kb = (tk + bk - 1) / bk, n_tt = (tq + bt - 1) / bt;
+  std::vector<magi::KeyBounds> iv;
+  for (int64_t kb = 0; kb < n_kb; ++kb) {
+    iv.assign(keys.begin() + kb * bk, keys.begin() + std::min<int64_t>(tk, kb * bk + bk));
+    for (int64_t tt = 0; tt < n_tt; ++tt)
+      cls[kb * n_tt + tt] = int8_t(magi::classify_key_pair(iv, tt * bt, tt * bt + bt, tq));
+  }
   return MAGI_OK;
 }
 

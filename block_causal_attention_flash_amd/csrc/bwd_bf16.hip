@@ -508,7 +508,7 @@ bwd_dkdv_kernel(BwdParams p, BwdLayout L, const int4* __restrict__ items, const 
       vv[ks] = have ? *reinterpret_cast<const bf16x8*>(ws + L.vr + base + 2048 * ks) : bf16x8{};
     }
   }
-  const int2 kbnd = key < p.tk ? p.key_rows[key] : int2{0, 0};
+  const int4 kbnd = key < p.tk ? p.key_rows[key] : int4{0, 0, 0, 0};   // token ranges that see the key
   if (tid < D) sm.gk[tid] = p.k_gain[tid];
 
   const unsigned n_tt = unsigned(p.tq + TT - 1) / TT;
@@ -578,8 +578,9 @@ bwd_dkdv_kernel(BwdParams p, BwdLayout L, const int4* __restrict__ items, const 
       for (int e = 0; e < 4; ++e) {
         float pv = __builtin_amdgcn_exp2f(sc[rb][e] - l2[e]);
         if (masked) {
-          const unsigned rel = unsigned(tt * TT + 16 * rb + 4 * g + e - kbnd.x);
-          if (rel >= unsigned(kbnd.y - kbnd.x)) pv = 0.0f;
+          const int tok = tt * TT + 16 * rb + 4 * g + e;
+          if (unsigned(tok - kbnd.x) >= unsigned(kbnd.y - kbnd.x) && unsigned(tok - kbnd.z) >= unsigned(kbnd.w - kbnd.z))
+            pv = 0.0f;
         }
         pb[4 * rb + e] = (__bf16)pv;
         dsb[4 * rb + e] = (__bf16)(pv * (dp[rb][e] - dd[e]));

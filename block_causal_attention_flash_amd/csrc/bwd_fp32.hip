@@ -187,7 +187,7 @@ __global__ void __launch_bounds__(64) bwd_dkdv_f32_kernel(BwdParams p, F32Layout
     vv[d] = valid ? v[d] : 0.0f;
     ak[d] = av[d] = 0.0f;
   }
-  const int2 kbnd = valid ? p.key_rows[key] : int2{0, 0};
+  const int4 kbnd = valid ? p.key_rows[key] : int4{0, 0, 0, 0};
   const float* qp = reinterpret_cast<const float*>(ws + L.qp);
   const float* qh = reinterpret_cast<const float*>(ws + L.qh);
   const float* dd = reinterpret_cast<const float*>(ws + L.dd);
@@ -214,7 +214,9 @@ __global__ void __launch_bounds__(64) bwd_dkdv_f32_kernel(BwdParams p, F32Layout
       __syncthreads();
       for (int j = 0; j < BN; ++j) {
         const int tok = tt * BN + j;
-        if (tok >= p.tq || (masked && !(tok >= kbnd.x && tok < kbnd.y))) continue;
+        if (tok >= p.tq ||
+            (masked && !(tok >= kbnd.x && tok < kbnd.y) && !(tok >= kbnd.z && tok < kbnd.w)))
+          continue;
         float s = 0.0f, dp = 0.0f;
         for (int d = 0; d < D; ++d) {
           s += sq[j][d] * ku[d];

@@ -77,7 +77,7 @@ struct BwdParams {
   const int2* rows;       // per-token key bounds [tq]
   const int4* kv_items;   // KeyItem[n_kv_items]
   const int* kv_tiles;    // token tile codes (tt * 2 + masked) per key block
-  const int2* key_rows;   // per-key token bounds [tk]
+  const int4* key_rows;   // per-key token ranges [tk]: own video [x, y), last global block [z, w)
   int n_dq_items, n_kv_items;
 };
 

@@ -58,9 +58,11 @@ magi_status_t validate_layout(const magi_attn_layout_t* L, std::string& err) {
     if (kv[c + 1] < kv[c]) { err = "kv_offsets must be non-decreasing"; return MAGI_ERR_INVALID_ARG; }
   }
   if (L->kv_range < 0) { err = "kv_range must be >= 0"; return MAGI_ERR_INVALID_ARG; }
+  if (L->last_global != 0 && L->last_global != 1) { err = "last_global must be 0 or 1"; return MAGI_ERR_INVALID_ARG; }
   for (int s = 0; s < L->n_seqs; ++s) {
     for (int c = L->seq_chunks[s]; c < L->seq_chunks[s + 1]; ++c)
-      if (L->q_offsets[c + 1] > L->q_offsets[c] && kv[c + 1] <= kv[first_visible_chunk(L, s, c)]) {
+      if (L->q_offsets[c + 1] > L->q_offsets[c] &&
+          (global_video(L, s) ? kv[L->n_chunks] == 0 : kv[c + 1] <= kv[first_visible_chunk(L, s, c)])) {
         err = "chunk " + std::to_string(c) + " owns queries but sees no key"; return MAGI_ERR_INVALID_ARG;
       }
   }
@@ -146,19 +148,40 @@ Tiling choose_bwd_tiling(int dtype, int head_dim, int group) {
   return t;
 }
 
-void key_bounds(const magi_attn_layout_t* L, std::vector<RowBounds>& keys) {
+void key_bounds(const magi_attn_layout_t* L, std::vector<KeyBounds>& keys) {
   // Query chunk c sees key chunk j of its video when j <= c and, with a KV
   // range R, c <= j + R - 1: the queries of chunks [j, last] for the last such
-  // chunk, one contiguous token range.
+  // chunk, one contiguous token range. A last global block's queries (the
+  // stream's last tokens) see every key: a second range for keys of other
+  // videos, the only range for its own keys.
   const int32_t* kv = L->kv_offsets ? L->kv_offsets : L->q_offsets;
-  keys.assign(kv[L->n_chunks], RowBounds{0, 0});
+  const int32_t tq = L->q_offsets[L->n_chunks];
+  const int32_t g0 = L->last_global ? L->q_offsets[L->seq_chunks[L->n_seqs - 1]] : tq;
+  keys.assign(kv[L->n_chunks], KeyBounds{0, 0, 0, 0});
   for (int s = 0; s < L->n_seqs; ++s)
     for (int j = L->seq_chunks[s]; j < L->seq_chunks[s + 1]; ++j) {
       int last = L->seq_chunks[s + 1] - 1;
       if (L->kv_range > 0 && j + L->kv_range - 1 < last) last = j + L->kv_range - 1;
-      const RowBounds b{L->q_offsets[j], L->q_offsets[last + 1]};
+      KeyBounds b{L->q_offsets[j], L->q_offsets[last + 1], g0, tq};
+      if (global_video(L, s)) b = KeyBounds{g0, tq, 0, 0};
       for (int32_t t = kv[j]; t < kv[j + 1]; ++t) keys[t] = b;
     }
+}
+
+int classify_key_pair(const std::vector<KeyBounds>& iv, int64_t t0, int64_t t1, int64_t tq) {
+  if (iv.empty()) return 0;
+  bool all = true, any = false;
+  for (const KeyBounds& b : iv) {
+    const int64_t lo = b.lo, hi = std::min<int64_t>(b.hi, tq), glo = b.glo, ghi = std::min<int64_t>(b.ghi, tq);
+    const bool r1 = lo < hi, r2 = glo < ghi;
+    auto covers = [&](int64_t a0, int64_t a1) { return a0 <= t0 && t1 <= a1; };
+    bool cover = (r1 && covers(lo, hi)) || (r2 && covers(glo, ghi));
+    if (!cover && r1 && r2 && std::max(lo, glo) <= std::min(hi, ghi))      // the two ranges touch: one range
+      cover = covers(std::min(lo, glo), std::max(hi, ghi));
+    if (!cover) all = false;
+    if ((r1 && lo < t1 && t0 < hi) || (r2 && glo < t1 && t0 < ghi)) any = true;
+  }
+  return all ? 2 : (any ? 1 : 0);
 }
 
 void row_bounds(const magi_attn_layout_t* L, std::vector<RowBounds>& rows) {
@@ -166,8 +189,9 @@ void row_bounds(const magi_attn_layout_t* L, std::vector<RowBounds>& rows) {
   rows.assign(L->q_offsets[L->n_chunks], RowBounds{0, 0});
   for (int s = 0; s < L->n_seqs; ++s)
     for (int c = L->seq_chunks[s]; c < L->seq_chunks[s + 1]; ++c) {
-      const int32_t lo = kv[first_visible_chunk(L, s, c)];
-      for (int32_t t = L->q_offsets[c]; t < L->q_offsets[c + 1]; ++t) rows[t] = RowBounds{lo, kv[c + 1]};
+      const RowBounds b = global_video(L, s) ? RowBounds{0, kv[L->n_chunks]}
+                                             : RowBounds{kv[first_visible_chunk(L, s, c)], kv[c + 1]};
+      for (int32_t t = L->q_offsets[c]; t < L->q_offsets[c + 1]; ++t) rows[t] = b;
     }
 }
 
@@ -405,22 +429,32 @@ magi_status_t build_bwd_plan(const magi_attn_layout_t* L, BwdHostPlan& B, std::s
   const int64_t n_kb = (tk + kb_size - 1) / kb_size;
   std::vector<int32_t> kb_begin(n_kb), kb_n(n_kb), kb_full(n_kb);
   std::vector<int32_t> masked_codes;
-  std::vector<RowBounds> iv;
+  std::vector<KeyBounds> iv;
+  std::vector<char> cand;
   B.kv_tiles.clear();
+  const int64_t n_tt = (tq + tt_size - 1) / tt_size;
   for (int64_t kb = 0; kb < n_kb; ++kb) {
     const int64_t k0 = kb * kb_size, k1 = std::min<int64_t>(tk, k0 + kb_size);
-    tile_intervals(B.key_rows, k0, k1, iv);
-    int64_t lo = INT64_MAX, hi = 0;
-    for (const RowBounds& b : iv)
-      if (b.hi > b.lo) { lo = std::min<int64_t>(lo, b.lo); hi = std::max<int64_t>(hi, b.hi); }
+    iv.clear();
+    for (int64_t j = k0; j < k1; ++j) {
+      const KeyBounds& b = B.key_rows[j];
+      if (iv.empty() || iv.back().lo != b.lo || iv.back().hi != b.hi || iv.back().glo != b.glo || iv.back().ghi != b.ghi)
+        iv.push_back(b);
+    }
+    // candidate token tiles: those touching any key's ranges
+    cand.assign(n_tt, 0);
+    for (const KeyBounds& b : iv) {
+      if (b.hi > b.lo) for (int64_t tt = b.lo / tt_size; tt < (b.hi + tt_size - 1) / tt_size; ++tt) cand[tt] = 1;
+      if (b.ghi > b.glo) for (int64_t tt = b.glo / tt_size; tt < (b.ghi + tt_size - 1) / tt_size; ++tt) cand[tt] = 1;
+    }
     kb_begin[kb] = int32_t(B.kv_tiles.size());
     masked_codes.clear();
-    if (hi > lo)
-      for (int64_t tt = lo / tt_size; tt < (hi + tt_size - 1) / tt_size; ++tt) {
-        const int cls = classify_pair(iv, tt * tt_size, tt * tt_size + tt_size, tq);
-        if (cls == 2) B.kv_tiles.push_back(tile_code(tt, 0));
-        else if (cls == 1) masked_codes.push_back(tile_code(tt, 1));
-      }
+    for (int64_t tt = 0; tt < n_tt; ++tt) {
+      if (!cand[tt]) continue;
+      const int cls = classify_key_pair(iv, tt * tt_size, tt * tt_size + tt_size, tq);
+      if (cls == 2) B.kv_tiles.push_back(tile_code(tt, 0));
+      else if (cls == 1) masked_codes.push_back(tile_code(tt, 1));
+    }
     kb_full[kb] = int32_t(B.kv_tiles.size()) - kb_begin[kb];
     B.kv_tiles.insert(B.kv_tiles.end(), masked_codes.begin(), masked_codes.end());
     kb_n[kb] = int32_t(B.kv_tiles.size()) - kb_begin[kb];

@@ -114,18 +114,28 @@ struct KeyItem {
   int32_t pad[3];
 };
 
+// Token ranges of the queries that see one key: its own video's [lo, hi),
+// and [glo, ghi) for the rows of a last global block (empty otherwise).
+struct KeyBounds {
+  int32_t lo, hi, glo, ghi;
+};
+
 // Backward work lists of a training plan.
 struct BwdHostPlan {
   HostPlan dq;                       // query-stationary dq items (never split)
   int32_t key_block = 0;             // keys per dk/dv item
   int32_t token_tile = 32;           // tokens per dk/dv step
-  std::vector<RowBounds> key_rows;   // [tk] token bounds [qlo, qhi) of the queries that see each key
+  std::vector<KeyBounds> key_rows;   // [tk] token ranges of the queries that see each key
   std::vector<int32_t> kv_tiles;     // per key block: token tile codes, full first, then boundary; padded
   std::vector<KeyItem> items;        // launch order (XCD-interleaved, padded)
 };
 
+// Whether video s is a last global block (its queries see every key).
+inline bool global_video(const magi_attn_layout_t* L, int s) { return L->last_global && s == L->n_seqs - 1; }
+
 // First chunk whose keys chunk c of video s sees: the video's first chunk, or
-// with a KV range R, the later of that and c - R + 1.
+// with a KV range R, the later of that and c - R + 1 (a global block: every
+// chunk's keys, see row_bounds).
 inline int first_visible_chunk(const magi_attn_layout_t* L, int s, int c) {
   const int first = L->seq_chunks[s];
   return L->kv_range > 0 && c - L->kv_range + 1 > first ? c - L->kv_range + 1 : first;
@@ -153,8 +163,13 @@ magi_status_t build_host_plan(int32_t kind, const magi_attn_layout_t* layout, co
 // Builds the backward's work lists of a self-attention layout (valid).
 magi_status_t build_bwd_plan(const magi_attn_layout_t* layout, BwdHostPlan& plan, std::string& err);
 
-// Per-key token bounds [qlo, qhi): the queries that see each key.
-void key_bounds(const magi_attn_layout_t* layout, std::vector<RowBounds>& keys);
+// Per-key token ranges: the queries that see each key.
+void key_bounds(const magi_attn_layout_t* layout, std::vector<KeyBounds>& keys);
+
+// Class of the pair (token tile [t0, t1), keys with ranges iv): 2 every
+// (token, key) pair allowed, 1 some, 0 none; tokens at or past tq count as
+// not allowed.
+int classify_key_pair(const std::vector<KeyBounds>& iv, int64_t t0, int64_t t1, int64_t tq);
 
 // Per-query-token key bounds [lo, hi) of the block-causal self-attention
 // (layout must be valid).

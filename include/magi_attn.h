@@ -24,7 +24,8 @@
  *   q_hat = q * q_gain / sqrt(mean_d(q^2) + eps),  k_hat likewise with k_gain,
  *   s_ij  = scale * <q_hat_ih, k_hat_jg> for keys j in
  *           [kv_offsets[f], kv_offsets[c + 1]), f = seq_chunks[s] (with a KV
- *           range R >= 1: max(seq_chunks[s], c - R + 1)),
+ *           range R >= 1: max(seq_chunks[s], c - R + 1)); all of [0, T_k)
+ *           for the queries of a last global block,
  *   out_ih = sum_j softmax_j(s_ij) v_jg,   lse_hi = ln sum_j exp(s_ij).
  *
  * Conventions shared by every entry point:
@@ -56,7 +57,7 @@
 extern "C" {
 #endif
 
-#define MAGI_ATTN_ABI_VERSION 4
+#define MAGI_ATTN_ABI_VERSION 5
 
 typedef enum magi_status {
   MAGI_OK = 0,
@@ -87,6 +88,11 @@ typedef enum magi_dtype {
  *                        chunks max(first chunk of its video, c - R + 1) .. c
  *                        (the pages' "KV range" of streaming inference:
  *                        paperlayer §2.4.4, paper-notes §3.4.4 and Figure 12).
+ * last_global          : 1: the last video is a global block (the pages'
+ *                        "varlen block-causal with a (last) global block":
+ *                        paper-notes Figure 15(g), paperlayer Figure 23):
+ *                        its queries see every key of the stream, [0, T_k);
+ *                        no other video sees its keys. 0: off.
  * A chunk that owns queries must see at least one key.
  * head_dim: 128 for bf16; 64 or 128 for fp32. n_q_heads % n_kv_heads == 0.
  */
@@ -101,6 +107,7 @@ typedef struct magi_attn_layout {
   int32_t head_dim;
   int32_t dtype;              /* magi_dtype_t */
   int32_t kv_range;           /* 0: block-causal; R >= 1: the last R chunks of the video */
+  int32_t last_global;        /* 1: the last video's queries see every key of the stream */
 } magi_attn_layout_t;
 
 /*

@@ -23,11 +23,12 @@ def test_useful_pairs_match_golden_mask_areas():
 
 
 @pytest.mark.parametrize("R", [0, 1, 2, 3, 5])
-def test_useful_pairs_match_dense_mask_with_window(R):
+@pytest.mark.parametrize("last_global", [0, 1])
+def test_useful_pairs_match_dense_mask_with_window(R, last_global):
     lays = [layout_from_chunks([[7, 5, 9, 3], [4, 4]]), streaming_layout(3, 2, 6),
             Layout((0, 3, 3, 8, 10), (0, 4, 9, 11, 15), (0, 2, 4))]
     for lay in lays:
-        lw = dataclasses.replace(lay, kv_range=R)
+        lw = dataclasses.replace(lay, kv_range=R, last_global=last_global)
         assert bench.useful_pairs(lw) == int(oracle.block_causal_mask(lw).sum())
 
 

@@ -76,6 +76,8 @@ SMALL = [
     ("streaming", streaming_layout(5, 3, 96)),
     ("kv_cache_mixed", Layout((0, 0, 0, 77, 150, 150, 260), (0, 64, 130, 200, 333, 400, 470), (0, 4, 6))),
     ("window", dataclasses.replace(layout_from_chunks([[130, 70, 96, 150], [190, 40]]), kv_range=2)),
+    ("last_global", dataclasses.replace(layout_from_chunks([[130, 70], [1, 2, 3], [96, 150], [190, 40]]),
+                                        last_global=1)),
 ]
 
 
@@ -87,7 +89,10 @@ def test_bf16_backward_small(name, lay, hq, hk):
     log("  rel_l2 dq {:.2e} dk {:.2e} dv {:.2e} dgq {:.2e} dgk {:.2e}".format(*errs))
 
 
-@pytest.mark.parametrize("name,lay", SMALL[:4], ids=[s[0] for s in SMALL[:4]])
+FP32_SMALL = SMALL[:4] + SMALL[-1:]
+
+
+@pytest.mark.parametrize("name,lay", FP32_SMALL, ids=[s[0] for s in FP32_SMALL])
 @pytest.mark.parametrize("d", [64, 128])
 def test_fp32_backward_small(name, lay, d):
     log(f"fp32 backward {name} d={d}")

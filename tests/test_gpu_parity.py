@@ -268,6 +268,47 @@ def test_kv_range_480x832_sampled_rows():
     log(f"kv_range 5 video480x832: rows={len(rows)} rel_l2={rl2:.3e} max_abs={mabs:.3e} lse_err={lerr:.3e}")
 
 
+# ------------------------------------------------------------------ last global block
+
+def _global(lay):
+    return Layout(lay.q_offsets, lay.kv_offsets, lay.seq_chunks, lay.kv_range, 1)
+
+
+@pytest.mark.parametrize("hq,hk", [(6, 2), (8, 1)])
+def test_bf16_last_global_small(hq, hk):
+    """Varlen block-causal with a last global block: the last video's rows see
+    every key of the stream (boundary tiles where its rows meet the other
+    videos' rows in one query tile)."""
+    lay = _global(layout_from_chunks([[130, 70], [1, 2, 3], [96, 150], [190, 40]]))
+    rl2, mabs, lerr = full_parity(lay, hq, hk, 128, "bf16", seed=40 + hq)
+    log(f"last global {hq}/{hk}: rel_l2={rl2:.3e} max_abs={mabs:.3e} lse_err={lerr:.3e}")
+
+
+def test_bf16_last_global_with_window_and_cache():
+    lay = Layout((0, 0, 0, 77, 150, 150, 260), (0, 64, 130, 200, 333, 400, 470), (0, 4, 6), 2, 1)
+    full_parity(lay, 6, 2, 128, "bf16", seed=44)
+
+
+def test_fp32_last_global_small():
+    full_parity(_global(layout_from_chunks([[30, 17], [41], [25, 9]])), 4, 2, 64, "fp32", seed=45)
+
+
+def test_last_global_packed8_sampled_rows():
+    """The packed 8-video batch with its last video as the global block."""
+    from block_causal_attention_flash_amd import magi_attn_plan_stats
+    c = get_config("packed8")
+    lay = _global(c.layout)
+    inp = make_inputs(lay, c.n_q_heads, c.n_kv_heads, c.head_dim, c.dtype, c.gain_kind, c.seed)
+    st = magi_attn_plan_stats(lay.q_offsets, lay.kv_offsets, lay.seq_chunks, c.n_q_heads, c.n_kv_heads,
+                              c.head_dim, c.dtype, last_global=1)
+    got_out, got_lse = run_gpu(lay, inp, c.n_q_heads, c.n_kv_heads, c.head_dim, c.dtype, c.eps, c.scale)
+    rows = sample_rows(lay, st["tile_q"], 24, seed=6)
+    ref_out, ref_lse = oracle.attention(inp["q"], inp["k"], inp["v"], inp["q_gain"], inp["k_gain"], c.eps,
+                                        c.scale, lay, rows=rows)
+    rl2, mabs, lerr = compare(got_out[rows], got_lse[:, rows], ref_out, ref_lse, c.dtype)
+    log(f"last global packed8: rows={len(rows)} rel_l2={rl2:.3e} max_abs={mabs:.3e} lse_err={lerr:.3e}")
+
+
 # ------------------------------------------------------------------ invariants that need no oracle
 
 def _fwd(plan, inp, dev):

@@ -34,7 +34,7 @@ def test_abi_version(built_lib):
     from block_causal_attention_flash_amd import magi_attn_abi_version
     hdr = open(os.path.join(ROOT, "include", "magi_attn.h")).read()
     declared = int(re.search(r"#define MAGI_ATTN_ABI_VERSION (\d+)", hdr).group(1))
-    assert magi_attn_abi_version() == declared == 4
+    assert magi_attn_abi_version() == declared == 5
 
 
 def brute_classes(layout, bm, bn, mask=None):
@@ -82,14 +82,15 @@ def test_classifier_matches_dense_mask(built_lib, seed):
     lay = random_layout(rng)
     if lay.t_q == 0:
         pytest.skip("no queries")
-    for R in (0, int(rng.integers(1, 4))):
-        lw = Layout(lay.q_offsets, lay.kv_offsets, lay.seq_chunks, R)
-        if R and any(lw.q_offsets[c + 1] > lw.q_offsets[c] and lw.kv_offsets[c + 1] == lw.kv_offsets[max(
-                [s0 for s0 in lw.seq_chunks[:-1] if s0 <= c][-1], c - R + 1)] for c in range(lw.n_chunks)):
+    for R, lg in ((0, 0), (int(rng.integers(1, 4)), 0), (0, 1), (int(rng.integers(1, 4)), 1)):
+        lw = Layout(lay.q_offsets, lay.kv_offsets, lay.seq_chunks, R, lg)
+        mask = oracle.block_causal_mask(lw)
+        if (mask.sum(axis=1) == 0).any():
             continue                          # a chunk with queries would see no key: rejected layout
         for bm, bn in ((64, 64), (128, 64), (32, 16), (7, 5)):
-            got = magi_attn_classify_host(lw.q_offsets, lw.kv_offsets, lw.seq_chunks, bm=bm, bn=bn, kv_range=R)
-            np.testing.assert_array_equal(got, brute_classes(lw, bm, bn))
+            got = magi_attn_classify_host(lw.q_offsets, lw.kv_offsets, lw.seq_chunks, bm=bm, bn=bn, kv_range=R,
+                                          last_global=lg)
+            np.testing.assert_array_equal(got, brute_classes(lw, bm, bn, mask))
 
 
 def test_kv_range_stats_and_validation(built_lib):
@@ -282,11 +283,28 @@ def test_key_classifier_matches_transposed_mask(built_lib, seed):
     lay = random_layout(rng)
     if lay.t_q == 0:
         pytest.skip("no queries")
-    for R in (0, int(rng.integers(1, 4))):
-        lw = Layout(lay.q_offsets, lay.kv_offsets, lay.seq_chunks, R)
+    for R, lg in ((0, 0), (int(rng.integers(1, 4)), 0), (0, 1), (int(rng.integers(1, 4)), 1)):
+        lw = Layout(lay.q_offsets, lay.kv_offsets, lay.seq_chunks, R, lg)
         mask = oracle.block_causal_mask(lw)
         if (mask.sum(axis=1) == 0).any() and lw.t_q:
             continue                          # a chunk with queries would see no key: rejected layout
         for bk, bt in ((128, 32), (64, 32), (7, 5)):
-            got = magi_attn_key_classify_host(lw.q_offsets, lw.kv_offsets, lw.seq_chunks, bk=bk, bt=bt, kv_range=R)
+            got = magi_attn_key_classify_host(lw.q_offsets, lw.kv_offsets, lw.seq_chunks, bk=bk, bt=bt, kv_range=R,
+                                              last_global=lg)
             np.testing.assert_array_equal(got, brute_classes(lw, bk, bt, mask.T.copy()))
+
+
+def test_last_global_stats(built_lib):
+    """packed8 with its last video as a global block: the mask area in closed
+    form (the other videos' block-causal area plus the global rows times T_k)."""
+    from block_causal_attention_flash_amd import MagiAttnError, magi_attn_plan_stats
+    c = get_config("packed8")
+    lay = c.layout
+    plain = magi_attn_plan_stats(lay.q_offsets, None, lay.seq_chunks, 32, 8, 128, "bf16")
+    st = magi_attn_plan_stats(lay.q_offsets, None, lay.seq_chunks, 32, 8, 128, "bf16", last_global=1)
+    g0 = lay.q_offsets[lay.seq_chunks[-2]]
+    g_own = sum((lay.q_offsets[cc + 1] - lay.q_offsets[cc]) * (lay.q_offsets[cc + 1] - g0)
+                for cc in range(lay.seq_chunks[-2], lay.n_chunks))
+    assert st["unmasked_pairs"] == plain["unmasked_pairs"] - g_own + (lay.t_q - g0) * lay.t_q
+    with pytest.raises(MagiAttnError):
+        magi_attn_plan_stats([0, 4], None, None, 1, 1, 128, "bf16", last_global=2)
