@@ -3,36 +3,39 @@
 // Training needs the gradients of the attention of the MAGI-1 pages
 // (paperlayer §2 / Figure 1, §2.2.2; paper-notes §3.2.2 and Figure 15), and
 // the pages' attention kernel runs its backward from the forward's saved
-// softmax statistics (paperlayer §4.1.2, §B.1). With q' = rms(q) g_q g_k
-// scale log2(e) (the forward's folded query), k_hat = rms(k), the natural
+// softmax statistics (paperlayer §4.1.2, §B.1). With q_hat = rms(q) g_q,
+// k' = rms(k) g_k scale log2(e) (both rounded to bf16 once), the natural
 // log-sum-exp lse of each row and the upstream gradient dO:
-//   P_ij  = 2^(<q'_i, k_hat_j> - lse_i log2 e)        (recomputed, no max pass)
+//   P_ij  = 2^(<q_hat_i, k'_j> - lse_i log2 e)        (recomputed, no max pass)
 //   dP_ij = <dO_i, v_j>,  D_i = <dO_i, O_i>,  dS_ij = P_ij (dP_ij - D_i)
-//   dq_hat_i = scale g_k * sum_j dS_ij k_hat_j        (dq kernel)
-//   dk_hat_j = scale sum_i dS_ij (rms(q_i) g_q)       (dk/dv kernel, over all query heads of j's group)
+//   dq_hat_i = sum_j dS_ij k'_j / log2 e              (dq kernel; = scale sum_j dS_ij k_hat_j)
+//   dk_hat_j = scale sum_i dS_ij q_hat_i              (dk/dv kernel, over all query heads of j's group)
 //   dv_j     = sum_i P_ij dO_i                        (dk/dv kernel)
 //   dx = (g dx_hat - u mean_d(u g dx_hat)) / r,  u = x / r   (RMSNorm, in the epilogues)
 //   dg = sum over rows of u dx_hat                    (per-workgroup partials, then one reduction)
 //
 // Kernels, in stream order:
-//   prep_q  per (32-token tile, query head): the tile images of q', of
-//           dO, of dO^T and of (rms(q) g_q)^T, and the row statistics
-//           (lse log2 e, D);
-//   prep_k  per (32-key tile, KV head): the images of k_hat, of V and of
-//           k_hat^T;
+//   prep_q  per (32-token tile, query head): the tile images of q_hat and of
+//           dO, and the row statistics (lse log2 e, D);
+//   prep_k  per (32-key tile, KV head): the images of k' and of V;
 //   dq      query-stationary (the forward's order): 8 waves x 32 rows, per
 //           key tile S^T and dP^T on the matrix cores, dS on the vector ALUs,
-//           then (dq_hat)^T += k_hat^T dS^T;
+//           then (dq_hat)^T += k'^T dS^T;
 //   dkdv    key-stationary: 8 waves x 16 keys of one KV head, per
 //           (32-token tile, query head) S and dP, then dV^T += dO^T P and
-//           dK^T += (q_hat)^T dS;
+//           dK^T += q_hat^T dS;
 //   reduce  the gain gradients from the per-workgroup partials.
-// Tile images follow the forward's two layouts: "row" [16 chunks][32 rows]
-// [16 B] (A operand: lane l reads row l % 16, dims 8 (l / 16) + 32 ks ..)
-// and "transposed" [4 chunks][128 dims][16 B] whose chunk c holds rows
-// 4c + {0..3} and 16 + 4c + {0..3} (the row order of a lane's fragment of a
-// 16x16 result pair). Copies into LDS rings use LDS-direct buffer loads two
-// steps ahead.
+// Every image has the forward's row layout [16 chunks][32 rows][16 B]
+// (chunk c of row r holds dims 8c..8c+7 at byte 512 c + 16 r). A lane reads
+// an MFMA operand fragment in row order with one ds_read_b128 (row l % 16,
+// dims 32 ks + 8 (l / 16) ..), or transposed with two LDS transpose loads
+// (ds_read_b64_tr_b16: within 16 lanes, lane i's element j comes from the
+// 8-byte address of lane 4j + i / 4, element i % 4) that give lane l dim
+// 16 db + l % 16 of rows 4 (l / 16) + {0..3} and 16 + 4 (l / 16) + {0..3}:
+// the row order of a lane's fragment of a 16x16 result pair. Copies into LDS
+// rings use LDS-direct buffer loads four steps ahead; on even steps a wave
+// waits for its copies of the step pair and the workgroup barrier publishes
+// both stages (and frees the two stages the next pair of copies fills).
 #include "kernels.hpp"
 
 namespace magi {
@@ -46,12 +49,14 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 #define LDS_PTR(T, p) ((__attribute__((address_space(3))) T*)(p))
 typedef __attribute__((address_space(3))) const bf16x8 lds_bf16x8;
 typedef __attribute__((address_space(3))) const f32x4 lds_f32x4;
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
 constexpr int D = 128;
 constexpr int TT = 32;                       // tokens per image (and per dk/dv step), keys per dq tile
 constexpr int IMG = TT * D * 2;              // 8 KiB
 constexpr int NTHR = 512;
-constexpr int RING = 4;                      // LDS ring stages, copies two steps ahead
+constexpr int RING = 8;                      // LDS ring stages: copies four steps ahead, a barrier every second step
 constexpr unsigned kNoTile = 0x80000000u;    // past every image array (< 2 GiB): zeros
 constexpr float kLog2e = 1.4426950408889634f;
 static_assert(IMG == NTHR * 16, "one 16-byte copy per thread per image");
@@ -120,8 +125,22 @@ __device__ __forceinline__ f32x4 mfma(bf16x8 a, bf16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
-// Row j of the transposed layout's chunk c: the 8 rows 16 (jj / 4) + 4c + jj % 4.
-__device__ __forceinline__ int perm_row(int c, int jj) { return 16 * (jj >> 2) + 4 * c + (jj & 3); }
+// Per-lane byte offset of the transposed fragment reads: lane l = 16 g + 4 j + q
+// points at row 4 g + j, dims 4 q .. 4 q + 3 of dim block 0 of a row image.
+__device__ __forceinline__ unsigned tr_lane_offset(int lane) {
+  const int g = lane >> 4, j = (lane >> 2) & 3, q = lane & 3;
+  return unsigned(512 * (q >> 1) + 16 * (4 * g + j) + 8 * (q & 1));
+}
+
+// A operand of 16 dims (block db) x 32 rows, rows in the order of a lane's
+// fragment of a 16x16 result pair, read transposed from a row image at
+// `addr` = image base + tr_lane_offset(lane).
+__device__ __forceinline__ bf16x8 tr_frag(unsigned addr, int db) {
+  const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(size_t)(addr + 1024 * db));
+  const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(size_t)(addr + 1024 * db + 256));
+  const i16x4 w[2] = {lo, hi};
+  return __builtin_bit_cast(bf16x8, w);
+}
 
 // ------------------------------------------------------------------ pre-passes
 
@@ -129,8 +148,6 @@ __device__ __forceinline__ int perm_row(int c, int jj) { return 16 * (jj >> 2) +
 // thread t: token row j = t / 8, dims [16 (t % 8), +16).
 constexpr int PREP_THREADS = 256;
 __global__ void __launch_bounds__(PREP_THREADS) bwd_prep_q_kernel(BwdParams p, BwdLayout L) {
-  __shared__ __attribute__((aligned(16))) __bf16 sh_qh[TT][D + 8];
-  __shared__ __attribute__((aligned(16))) __bf16 sh_do[TT][D + 8];
   unsigned char* ws = static_cast<unsigned char*>(p.ws);
   const int b = blockIdx.x, tt = b / p.hq, h = b % p.hq;
   const int t = threadIdx.x, j = t >> 3, part = t & 7;
@@ -157,21 +174,13 @@ __global__ void __launch_bounds__(PREP_THREADS) bwd_prep_q_kernel(BwdParams p, B
   ss = sum8(ss);
   dsum = sum8(dsum);
   const float rq = valid ? __builtin_amdgcn_rsqf(ss * (1.0f / D) + p.eps) : 0.0f;
-  const float fold = p.scale * kLog2e;
 #pragma unroll
   for (int c = 0; c < 2; ++c) {
-    bf16x8 qs, qh;
+    bf16x8 qh;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int d = part * 16 + 8 * c + e;
-      const float u = float(q[c][e]) * rq;
-      qs[e] = (__bf16)(u * p.q_gain[d] * p.k_gain[d] * fold);
-      qh[e] = (__bf16)(u * p.q_gain[d]);
-      sh_qh[j][d] = qh[e];
-      sh_do[j][d] = dd[c][e];
-    }
+    for (int e = 0; e < 8; ++e) qh[e] = (__bf16)(float(q[c][e]) * rq * p.q_gain[part * 16 + 8 * c + e]);
     const size_t at = size_t(b) * IMG + 512 * (2 * part + c) + 16 * j;
-    *reinterpret_cast<bf16x8*>(ws + L.qs + at) = qs;
+    *reinterpret_cast<bf16x8*>(ws + L.qs + at) = qh;
     *reinterpret_cast<bf16x8*>(ws + L.dos + at) = dd[c];
   }
   if (part == 0) {
@@ -179,26 +188,10 @@ __global__ void __launch_bounds__(PREP_THREADS) bwd_prep_q_kernel(BwdParams p, B
     rs[j] = valid ? p.lse[size_t(h) * p.tq + tok] * kLog2e : 0.0f;
     rs[32 + j] = valid ? dsum : 0.0f;
   }
-  __syncthreads();
-#pragma unroll
-  for (int r = 0; r < 2; ++r) {
-    const int u = t + PREP_THREADS * r;          // transposed unit: chunk u / 128, dim u % 128
-    const int c = u >> 7, d = u & 127;
-    bf16x8 wq, wd;
-#pragma unroll
-    for (int jj = 0; jj < 8; ++jj) {
-      wq[jj] = sh_qh[perm_row(c, jj)][d];
-      wd[jj] = sh_do[perm_row(c, jj)][d];
-    }
-    const size_t at = size_t(b) * IMG + 2048 * c + 16 * d;
-    *reinterpret_cast<bf16x8*>(ws + L.qht + at) = wq;
-    *reinterpret_cast<bf16x8*>(ws + L.dot + at) = wd;
-  }
 }
 
 // One workgroup per (32-key tile kt, KV head), image b = kt * hk + kvh.
 __global__ void __launch_bounds__(PREP_THREADS) bwd_prep_k_kernel(BwdParams p, BwdLayout L) {
-  __shared__ __attribute__((aligned(16))) __bf16 sh_k[TT][D + 8];
   unsigned char* ws = static_cast<unsigned char*>(p.ws);
   const int b = blockIdx.x, kt = b / p.hk, kvh = b % p.hk;
   const int t = threadIdx.x, j = t >> 3, part = t & 7;
@@ -220,27 +213,15 @@ __global__ void __launch_bounds__(PREP_THREADS) bwd_prep_k_kernel(BwdParams p, B
     for (int e = 0; e < 8; ++e) ss += float(k[c][e]) * float(k[c][e]);
   ss = sum8(ss);
   const float rk = valid ? __builtin_amdgcn_rsqf(ss * (1.0f / D) + p.eps) : 0.0f;
+  const float fold = p.scale * kLog2e;
 #pragma unroll
   for (int c = 0; c < 2; ++c) {
-    bf16x8 kh;
+    bf16x8 kf;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      kh[e] = (__bf16)(float(k[c][e]) * rk);
-      sh_k[j][part * 16 + 8 * c + e] = kh[e];
-    }
+    for (int e = 0; e < 8; ++e) kf[e] = (__bf16)(float(k[c][e]) * rk * p.k_gain[part * 16 + 8 * c + e] * fold);
     const size_t at = size_t(b) * IMG + 512 * (2 * part + c) + 16 * j;
-    *reinterpret_cast<bf16x8*>(ws + L.kh + at) = kh;
+    *reinterpret_cast<bf16x8*>(ws + L.kh + at) = kf;
     *reinterpret_cast<bf16x8*>(ws + L.vr + at) = v[c];
-  }
-  __syncthreads();
-#pragma unroll
-  for (int r = 0; r < 2; ++r) {
-    const int u = t + PREP_THREADS * r;
-    const int c = u >> 7, d = u & 127;
-    bf16x8 w;
-#pragma unroll
-    for (int jj = 0; jj < 8; ++jj) w[jj] = sh_k[perm_row(c, jj)][d];
-    *reinterpret_cast<bf16x8*>(ws + L.kht + size_t(b) * IMG + 2048 * c + 16 * d) = w;
   }
 }
 
@@ -306,8 +287,6 @@ __device__ __forceinline__ void rms_backward_row(const __bf16* xrow, __bf16* dxr
 struct DqLds {
   unsigned char kh[RING][IMG];
   unsigned char vr[RING][IMG];
-  unsigned char kht[RING][IMG];
-  float gk[D];           // scale * g_k
   float gq[D];
   float red[8][D];
 };
@@ -363,17 +342,13 @@ bwd_dq_kernel(BwdParams p, BwdLayout L, const int4* __restrict__ items, const in
       hi[rb] = bnd.y;
     }
   }
-  if (tid < D) {
-    sm.gk[tid] = p.k_gain[tid] * p.scale;
-    sm.gq[tid] = p.q_gain[tid];
-  }
+  if (tid < D) sm.gq[tid] = p.q_gain[tid];
 
   const unsigned n_kt = unsigned(p.tk + TT - 1) / TT;
   const unsigned kbytes = n_kt * unsigned(p.hk) * IMG;
-  const i32x4 rkh = make_rsrc(ws + L.kh, kbytes), rvr = make_rsrc(ws + L.vr, kbytes),
-              rkht = make_rsrc(ws + L.kht, kbytes);
+  const i32x4 rkh = make_rsrc(ws + L.kh, kbytes), rvr = make_rsrc(ws + L.vr, kbytes);
   const unsigned voff = unsigned(kvh) * IMG + unsigned(tid) * 16;
-  const unsigned kh0 = lds_addr(sm.kh[0]), vr0 = lds_addr(sm.vr[0]), kht0 = lds_addr(sm.kht[0]);
+  const unsigned kh0 = lds_addr(sm.kh[0]), vr0 = lds_addr(sm.vr[0]);
   const unsigned wpart = unsigned(wave) * 1024;  // this wave's part of every image copy
   const int* codes = tiles + item.z;
   const unsigned* soffs = soffs_all + item.z;    // padded past the list with kNoTile
@@ -382,21 +357,22 @@ bwd_dq_kernel(BwdParams p, BwdLayout L, const int4* __restrict__ items, const in
     const unsigned st = unsigned(i % RING) * IMG + wpart;
     dma16(rkh, voff, so, kh0 + st);
     dma16(rvr, voff, so, vr0 + st);
-    dma16(rkht, voff, so, kht0 + st);
   };
-  issue(0);
-  issue(1);
+  for (int i = 0; i < 4; ++i) issue(i);
 
   f32x4 acc[2][8];
 #pragma unroll
   for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
     for (int db = 0; db < 8; ++db) acc[rb][db] = f32x4{};
-  const unsigned rowq = 512 * g + 16 * r16, colq = 2048 * g + 16 * r16;
+  const unsigned rowq = 512 * g + 16 * r16, trq = tr_lane_offset(lane);
   for (int i = 0; i < n; ++i) {
-    wait_vmcnt<3>();                                  // tile i landed; tile i + 1 may still fly
-    lds_barrier();                                    // and every wave left the stage tile i + 2 overwrites
-    issue(i + 2);
+    if ((i & 1) == 0) {
+      wait_vmcnt<4>();                                // tiles i, i + 1 landed; i + 2, i + 3 may still fly
+      lds_barrier();                                  // and every wave left the stages of tiles i - 4, i - 3
+      issue(i + 4);
+      issue(i + 5);
+    }
     const unsigned st = unsigned(i % RING) * IMG;
     f32x4 s[2][2], dp[2][2];
 #pragma unroll
@@ -434,7 +410,7 @@ bwd_dq_kernel(BwdParams p, BwdLayout L, const int4* __restrict__ items, const in
         }
 #pragma unroll
     for (int db = 0; db < 8; ++db) {
-      const bf16x8 a = *(lds_bf16x8*)(size_t)(kht0 + st + colq + 256 * db);
+      const bf16x8 a = tr_frag(kh0 + st + trq, db);
 #pragma unroll
       for (int rb = 0; rb < 2; ++rb) acc[rb][db] = mfma(a, ds[rb], acc[rb][db]);
     }
@@ -456,7 +432,7 @@ bwd_dq_kernel(BwdParams p, BwdLayout L, const int4* __restrict__ items, const in
 #pragma unroll
     for (int db = 0; db < 8; ++db)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) dxh[db][e] = sm.gk[16 * db + 4 * g + e] * acc[rb][db][e];
+      for (int e = 0; e < 4; ++e) dxh[db][e] = acc[rb][db][e] * (1.0f / kLog2e);
     const size_t off = (size_t(valid ? tok : 0) * p.hq + head) * D;
     rms_backward_row(static_cast<const __bf16*>(p.q) + off, static_cast<__bf16*>(p.dq) + off, dxh, sm.gq, p.eps,
                      valid, gp, g);
@@ -469,8 +445,6 @@ bwd_dq_kernel(BwdParams p, BwdLayout L, const int4* __restrict__ items, const in
 struct KvLds {
   unsigned char qs[RING][IMG];
   unsigned char dos[RING][IMG];
-  unsigned char dot[RING][IMG];
-  unsigned char qht[RING][IMG];
   float rs[RING][8][64];  // per stage and wave: lse log2 e [32], D [32] of the step's rows
   float gk[D];
   float red[8][D];
@@ -514,10 +488,8 @@ bwd_dkdv_kernel(BwdParams p, BwdLayout L, const int4* __restrict__ items, const 
   const unsigned n_tt = unsigned(p.tq + TT - 1) / TT;
   const unsigned qbytes = n_tt * unsigned(p.hq) * IMG;
   const i32x4 rqs = make_rsrc(ws + L.qs, qbytes), rdo = make_rsrc(ws + L.dos, qbytes),
-              rdot = make_rsrc(ws + L.dot, qbytes), rqht = make_rsrc(ws + L.qht, qbytes),
               rrs = make_rsrc(ws + L.rs, n_tt * unsigned(p.hq) * 256u);
-  const unsigned qs0 = lds_addr(sm.qs[0]), do0 = lds_addr(sm.dos[0]), dot0 = lds_addr(sm.dot[0]),
-                 qht0 = lds_addr(sm.qht[0]), rs0 = lds_addr(&sm.rs[0][wave][0]);
+  const unsigned qs0 = lds_addr(sm.qs[0]), do0 = lds_addr(sm.dos[0]), rs0 = lds_addr(&sm.rs[0][wave][0]);
   const int* codes = tiles + item.z;
   const int hbase = kvh * G;
   // Step s = (entry s / G, head hbase + s % G); its image (token tile, head).
@@ -530,24 +502,24 @@ bwd_dkdv_kernel(BwdParams p, BwdLayout L, const int4* __restrict__ items, const 
     const unsigned st = unsigned(((ie * G + ih) % RING)) * IMG + wpart;
     dma16(rqs, unsigned(tid) * 16, so, qs0 + st);
     dma16(rdo, unsigned(tid) * 16, so, do0 + st);
-    dma16(rdot, unsigned(tid) * 16, so, dot0 + st);
-    dma16(rqht, unsigned(tid) * 16, so, qht0 + st);
     if (lane < 16)
       dma16(rrs, unsigned(lane) * 16, live ? imgi * 256u : kNoTile, rs0 + unsigned((ie * G + ih) % RING) * 8 * 256);
     if (++ih == G) { ih = 0; ++ie; }
   };
-  issue();
-  issue();
+  for (int i = 0; i < 4; ++i) issue();
 
   f32x4 accv[8], acck[8];
 #pragma unroll
   for (int db = 0; db < 8; ++db) accv[db] = acck[db] = f32x4{};
-  const unsigned rowq = 512 * g + 16 * r16, colq = 2048 * g + 16 * r16;
+  const unsigned rowq = 512 * g + 16 * r16, trq = tr_lane_offset(lane);
   int ce = 0, ch = 0;                                 // entry and head of the current step
   for (int s = 0; s < n_steps; ++s) {
-    wait_vmcnt<5>();                                  // step s landed; step s + 1 may still fly
-    lds_barrier();
-    issue();
+    if ((s & 1) == 0) {
+      wait_vmcnt<6>();                                // steps s, s + 1 landed; s + 2, s + 3 may still fly
+      lds_barrier();
+      issue();
+      issue();
+    }
     const unsigned st = unsigned(s % RING) * IMG;
     f32x4 sc[2], dp[2];
     sc[0] = sc[1] = dp[0] = dp[1] = f32x4{};
@@ -587,15 +559,9 @@ bwd_dkdv_kernel(BwdParams p, BwdLayout L, const int4* __restrict__ items, const 
       }
     }
 #pragma unroll
-    for (int db = 0; db < 8; ++db) {
-      const bf16x8 a = *(lds_bf16x8*)(size_t)(dot0 + st + colq + 256 * db);
-      accv[db] = mfma(a, pb, accv[db]);
-    }
+    for (int db = 0; db < 8; ++db) accv[db] = mfma(tr_frag(do0 + st + trq, db), pb, accv[db]);
 #pragma unroll
-    for (int db = 0; db < 8; ++db) {
-      const bf16x8 a = *(lds_bf16x8*)(size_t)(qht0 + st + colq + 256 * db);
-      acck[db] = mfma(a, dsb, acck[db]);
-    }
+    for (int db = 0; db < 8; ++db) acck[db] = mfma(tr_frag(qs0 + st + trq, db), dsb, acck[db]);
     if (++ch == G) { ch = 0; ++ce; }
   }
   wait_vmcnt<0>();
@@ -663,13 +629,10 @@ BwdLayout bwd_workspace_layout(long long tq, long long tk, int hq, int hk, int n
   BwdLayout L{};
   L.qs = 0;
   L.dos = L.qs + up(qimg);
-  L.dot = L.dos + up(qimg);
-  L.qht = L.dot + up(qimg);
-  L.rs = L.qht + up(qimg);
+  L.rs = L.dos + up(qimg);
   L.kh = L.rs + up(qimg / IMG * 256);
   L.vr = L.kh + up(kimg);
-  L.kht = L.vr + up(kimg);
-  L.pgq = L.kht + up(kimg);
+  L.pgq = L.vr + up(kimg);
   L.pgk = L.pgq + up(size_t(n_dq_items) * D * sizeof(float));
   L.level = L.pgk + up(size_t(n_kv_items) * D * sizeof(float));
   L.total = L.level + up(size_t(2 * REDUCE_SLICES) * D * sizeof(float));

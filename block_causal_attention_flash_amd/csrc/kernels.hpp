@@ -83,7 +83,7 @@ struct BwdParams {
 
 // Byte offsets of the backward workspace's parts.
 struct BwdLayout {
-  size_t qs, dos, dot, qht, rs, kh, vr, kht, pgq, pgk, level, total;
+  size_t qs, dos, rs, kh, vr, pgq, pgk, level, total;
 };
 BwdLayout bwd_workspace_layout(long long tq, long long tk, int hq, int hk, int n_dq_items, int n_kv_items);
 hipError_t launch_bwd_bf16_d128(const BwdParams& p, hipStream_t stream);

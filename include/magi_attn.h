@@ -266,8 +266,8 @@ MAGI_API magi_status_t magi_attn_fwd_parallel(const magi_attn_plan_t* plan, cons
                                               void* stream);
 
 /* Device workspace bytes of magi_attn_bwd for a training plan (bf16: the
- * re-laid-out queries, upstream gradients, keys and values, about
- * 4 * |q| + 3 * |k| bytes; fp32: the normalised queries, 2 * |q|; plus
+ * re-laid-out normalised queries, upstream gradients, keys and values, about
+ * 2 * |q| + 2 * |k| bytes; fp32: the normalised queries, 2 * |q|; plus
  * per-workgroup gain partials). */
 MAGI_API magi_status_t magi_attn_bwd_workspace_size(const magi_attn_plan_t* plan, size_t* bytes);
 
