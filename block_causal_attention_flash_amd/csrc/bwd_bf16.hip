@@ -21,12 +21,16 @@
 //   dq      query-stationary (the forward's order): 8 waves x 32 rows, per
 //           key tile S^T and dP^T on the matrix cores, dS on the vector ALUs,
 //           then (dq_hat)^T += k'^T dS^T;
-//   dkdv    key-stationary: 8 waves x 16 keys of one KV head, per
+//   dkdv    key-stationary: 8 waves x 32 keys of one KV head, per
 //           (32-token tile, query head) S and dP, then dV^T += dO^T P and
 //           dK^T += q_hat^T dS;
 //   reduce  the gain gradients from the per-workgroup partials.
-// Every image has the forward's row layout [16 chunks][32 rows][16 B]
-// (chunk c of row r holds dims 8c..8c+7 at byte 512 c + 16 r). A lane reads
+// Every image is [16 chunks][32 row slots][16 B]: chunk c of row r (dims
+// 8c..8c+7) sits at byte 512 c + 16 (r XOR 12 (c mod 2)). The XOR keeps each
+// 16-row block of a chunk in its own 256 bytes, so row reads stay contiguous,
+// and puts the odd chunk's rows of a transposed read (rows 4 g .. 4 g + 3 of
+// chunks 2 b and 2 b + 1 for the 16 lanes of group g) on the other banks: a
+// quarter wave covers 32 distinct banks and a half wave 64. A lane reads
 // an MFMA operand fragment in row order with one ds_read_b128 (row l % 16,
 // dims 32 ks + 8 (l / 16) ..), or transposed with two LDS transpose loads
 // (ds_read_b64_tr_b16: within 16 lanes, lane i's element j comes from the
@@ -60,7 +64,7 @@ constexpr int RING = 8;                      // LDS ring stages: copies four ste
 constexpr unsigned kNoTile = 0x80000000u;    // past every image array (< 2 GiB): zeros
 constexpr float kLog2e = 1.4426950408889634f;
 static_assert(IMG == NTHR * 16, "one 16-byte copy per thread per image");
-static_assert(kBwdRowsPerItem == 8 * 32 && kBwdKeysPerItem == 8 * 16, "8 waves per workgroup");
+static_assert(kBwdRowsPerItem == 8 * 32 && kBwdKeysPerItem == 8 * 32, "8 waves per workgroup");
 
 __device__ __forceinline__ unsigned lds_addr(const void* p) {
   return unsigned(reinterpret_cast<uintptr_t>(LDS_PTR(const char, p)));
@@ -125,11 +129,17 @@ __device__ __forceinline__ f32x4 mfma(bf16x8 a, bf16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
+// Byte offset of (chunk c, row r) in an image.
+__device__ __forceinline__ constexpr unsigned img_off(int c, int r) {
+  return unsigned(512 * c + 16 * (r ^ (12 * (c & 1))));
+}
+
 // Per-lane byte offset of the transposed fragment reads: lane l = 16 g + 4 j + q
-// points at row 4 g + j, dims 4 q .. 4 q + 3 of dim block 0 of a row image.
+// points at row 4 g + j, dims 4 q .. 4 q + 3 of dim block 0 of an image (rows
+// 16 .. 31 lie 256 bytes further: the XOR does not touch bit 4 of the row).
 __device__ __forceinline__ unsigned tr_lane_offset(int lane) {
   const int g = lane >> 4, j = (lane >> 2) & 3, q = lane & 3;
-  return unsigned(512 * (q >> 1) + 16 * (4 * g + j) + 8 * (q & 1));
+  return img_off(q >> 1, 4 * g + j) + unsigned(8 * (q & 1));
 }
 
 // A operand of 16 dims (block db) x 32 rows, rows in the order of a lane's
@@ -179,7 +189,7 @@ __global__ void __launch_bounds__(PREP_THREADS) bwd_prep_q_kernel(BwdParams p, B
     bf16x8 qh;
 #pragma unroll
     for (int e = 0; e < 8; ++e) qh[e] = (__bf16)(float(q[c][e]) * rq * p.q_gain[part * 16 + 8 * c + e]);
-    const size_t at = size_t(b) * IMG + 512 * (2 * part + c) + 16 * j;
+    const size_t at = size_t(b) * IMG + img_off(2 * part + c, j);
     *reinterpret_cast<bf16x8*>(ws + L.qs + at) = qh;
     *reinterpret_cast<bf16x8*>(ws + L.dos + at) = dd[c];
   }
@@ -219,7 +229,7 @@ __global__ void __launch_bounds__(PREP_THREADS) bwd_prep_k_kernel(BwdParams p, B
     bf16x8 kf;
 #pragma unroll
     for (int e = 0; e < 8; ++e) kf[e] = (__bf16)(float(k[c][e]) * rk * p.k_gain[part * 16 + 8 * c + e] * fold);
-    const size_t at = size_t(b) * IMG + 512 * (2 * part + c) + 16 * j;
+    const size_t at = size_t(b) * IMG + img_off(2 * part + c, j);
     *reinterpret_cast<bf16x8*>(ws + L.kh + at) = kf;
     *reinterpret_cast<bf16x8*>(ws + L.vr + at) = v[c];
   }
@@ -319,7 +329,7 @@ bwd_dq_kernel(BwdParams p, BwdLayout L, const int4* __restrict__ items, const in
 
   bf16x8 qs[2][4], dov[2][4];
   {
-    const size_t base = size_t(live ? img : 0) * IMG + 512 * g + 16 * r16;
+    const size_t base = size_t(live ? img : 0) * IMG + img_off(g, r16);
 #pragma unroll
     for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
@@ -365,7 +375,7 @@ bwd_dq_kernel(BwdParams p, BwdLayout L, const int4* __restrict__ items, const in
   for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
     for (int db = 0; db < 8; ++db) acc[rb][db] = f32x4{};
-  const unsigned rowq = 512 * g + 16 * r16, trq = tr_lane_offset(lane);
+  const unsigned rowq = img_off(g, r16), trq = tr_lane_offset(lane);  // chunk g + 4 ks has g's parity
   for (int i = 0; i < n; ++i) {
     if ((i & 1) == 0) {
       wait_vmcnt<4>();                                // tiles i, i + 1 landed; i + 2, i + 3 may still fly
@@ -450,6 +460,9 @@ struct KvLds {
   float red[8][D];
 };
 
+// 8 waves x 32 keys: wave w holds keys 32 w + 16 j + (0..15), j = 0, 1, of
+// the item's 256, which are rows 16 j + (0..15) of one 32-key image. Every
+// LDS fragment of a step feeds the MFMAs of both 16-key halves.
 __global__ void __launch_bounds__(NTHR) __attribute__((amdgpu_waves_per_eu(2, 2)))
 bwd_dkdv_kernel(BwdParams p, BwdLayout L, const int4* __restrict__ items, const int* __restrict__ tiles) {
   __shared__ __attribute__((aligned(1024))) KvLds sm;
@@ -468,21 +481,26 @@ bwd_dkdv_kernel(BwdParams p, BwdLayout L, const int4* __restrict__ items, const 
   const int G = p.hq / p.hk;
   const int n_entries = item.w - item.z;
   const int n_steps = n_entries * G;
-  // The wave's 16 keys: kb * 128 + 16 wave + (0..15); the lane's key (B operand column, output row).
-  const int key = kb * kBwdKeysPerItem + 16 * wave + r16;
-  const int kt = (kb * kBwdKeysPerItem + 16 * wave) / TT;
+  // The lane's keys (B operand columns, output rows), one per half.
+  const int kt = kb * (kBwdKeysPerItem / TT) + wave;
+  const int key0 = kt * TT + r16;
   const unsigned n_kt = unsigned(p.tk + TT - 1) / TT;
-  bf16x8 ku[4], vv[4];
+  bf16x8 ku[2][4], vv[2][4];
   {
     const bool have = unsigned(kt) < n_kt;
-    const size_t base = (size_t(kt) * p.hk + kvh) * IMG + 512 * g + 16 * (16 * (wave & 1) + r16);
+    const size_t base = (size_t(have ? kt : 0) * p.hk + kvh) * IMG;
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      ku[ks] = have ? *reinterpret_cast<const bf16x8*>(ws + L.kh + base + 2048 * ks) : bf16x8{};
-      vv[ks] = have ? *reinterpret_cast<const bf16x8*>(ws + L.vr + base + 2048 * ks) : bf16x8{};
-    }
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        const size_t at = base + img_off(g, 16 * j + r16) + 2048 * ks;
+        ku[j][ks] = have ? *reinterpret_cast<const bf16x8*>(ws + L.kh + at) : bf16x8{};
+        vv[j][ks] = have ? *reinterpret_cast<const bf16x8*>(ws + L.vr + at) : bf16x8{};
+      }
   }
-  const int4 kbnd = key < p.tk ? p.key_rows[key] : int4{0, 0, 0, 0};   // token ranges that see the key
+  int4 kbnd[2];                                       // token ranges that see each key
+#pragma unroll
+  for (int j = 0; j < 2; ++j) kbnd[j] = key0 + 16 * j < p.tk ? p.key_rows[key0 + 16 * j] : int4{0, 0, 0, 0};
   if (tid < D) sm.gk[tid] = p.k_gain[tid];
 
   const unsigned n_tt = unsigned(p.tq + TT - 1) / TT;
@@ -508,10 +526,12 @@ bwd_dkdv_kernel(BwdParams p, BwdLayout L, const int4* __restrict__ items, const 
   };
   for (int i = 0; i < 4; ++i) issue();
 
-  f32x4 accv[8], acck[8];
+  f32x4 accv[2][8], acck[2][8];
 #pragma unroll
-  for (int db = 0; db < 8; ++db) accv[db] = acck[db] = f32x4{};
-  const unsigned rowq = 512 * g + 16 * r16, trq = tr_lane_offset(lane);
+  for (int j = 0; j < 2; ++j)
+#pragma unroll
+    for (int db = 0; db < 8; ++db) accv[j][db] = acck[j][db] = f32x4{};
+  const unsigned rowq = img_off(g, r16), trq = tr_lane_offset(lane);  // chunk g + 4 ks has g's parity
   int ce = 0, ch = 0;                                 // entry and head of the current step
   for (int s = 0; s < n_steps; ++s) {
     if ((s & 1) == 0) {
@@ -521,74 +541,106 @@ bwd_dkdv_kernel(BwdParams p, BwdLayout L, const int4* __restrict__ items, const 
       issue();
     }
     const unsigned st = unsigned(s % RING) * IMG;
-    f32x4 sc[2], dp[2];
-    sc[0] = sc[1] = dp[0] = dp[1] = f32x4{};
+    const unsigned rsa = rs0 + unsigned(s % RING) * 8 * 256;
+    const bool masked = ce >= n_full;
+    const int tt = codes[ce] >> 1;
+    // S (lane: key r16 of half j, rows 16 rb + 4 g + e of the step's token tile)
+    f32x4 sc[2][2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) sc[j][0] = sc[j][1] = f32x4{};
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
       for (int rb = 0; rb < 2; ++rb) {
         const bf16x8 a = *(lds_bf16x8*)(size_t)(qs0 + st + rowq + 2048 * ks + 256 * rb);
-        sc[rb] = mfma(a, ku[ks], sc[rb]);
+        sc[0][rb] = mfma(a, ku[0][ks], sc[0][rb]);
+        sc[1][rb] = mfma(a, ku[1][ks], sc[1][rb]);
       }
+    f32x4 pf[2][2];
+    bf16x8 pb[2];
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb) {
+      const f32x4 l2 = *(lds_f32x4*)(size_t)(rsa + 4 * (16 * rb + 4 * g));
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          float pv = __builtin_amdgcn_exp2f(sc[j][rb][e] - l2[e]);
+          if (masked) {
+            const int tok = tt * TT + 16 * rb + 4 * g + e;
+            if (unsigned(tok - kbnd[j].x) >= unsigned(kbnd[j].y - kbnd[j].x) &&
+                unsigned(tok - kbnd[j].z) >= unsigned(kbnd[j].w - kbnd[j].z))
+              pv = 0.0f;
+          }
+          pf[j][rb][e] = pv;
+          pb[j][4 * rb + e] = (__bf16)pv;
+        }
+    }
+#pragma unroll
+    for (int db = 0; db < 8; ++db) {
+      const bf16x8 a = tr_frag(do0 + st + trq, db);
+      accv[0][db] = mfma(a, pb[0], accv[0][db]);
+      accv[1][db] = mfma(a, pb[1], accv[1][db]);
+    }
+    f32x4 dp[2][2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) dp[j][0] = dp[j][1] = f32x4{};
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
       for (int rb = 0; rb < 2; ++rb) {
         const bf16x8 a = *(lds_bf16x8*)(size_t)(do0 + st + rowq + 2048 * ks + 256 * rb);
-        dp[rb] = mfma(a, vv[ks], dp[rb]);
+        dp[0][rb] = mfma(a, vv[0][ks], dp[0][rb]);
+        dp[1][rb] = mfma(a, vv[1][ks], dp[1][rb]);
       }
-    // lane: key r16, rows 16 rb + 4 g + e of the step's token tile
-    const unsigned rsa = rs0 + unsigned(s % RING) * 8 * 256;
-    const bool masked = ce >= n_full;
-    const int tt = codes[ce] >> 1;
-    bf16x8 pb, dsb;
+    bf16x8 dsb[2];
 #pragma unroll
     for (int rb = 0; rb < 2; ++rb) {
-      const f32x4 l2 = *(lds_f32x4*)(size_t)(rsa + 4 * (16 * rb + 4 * g));
       const f32x4 dd = *(lds_f32x4*)(size_t)(rsa + 128 + 4 * (16 * rb + 4 * g));
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        float pv = __builtin_amdgcn_exp2f(sc[rb][e] - l2[e]);
-        if (masked) {
-          const int tok = tt * TT + 16 * rb + 4 * g + e;
-          if (unsigned(tok - kbnd.x) >= unsigned(kbnd.y - kbnd.x) && unsigned(tok - kbnd.z) >= unsigned(kbnd.w - kbnd.z))
-            pv = 0.0f;
-        }
-        pb[4 * rb + e] = (__bf16)pv;
-        dsb[4 * rb + e] = (__bf16)(pv * (dp[rb][e] - dd[e]));
-      }
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) dsb[j][4 * rb + e] = (__bf16)(pf[j][rb][e] * (dp[j][rb][e] - dd[e]));
     }
 #pragma unroll
-    for (int db = 0; db < 8; ++db) accv[db] = mfma(tr_frag(do0 + st + trq, db), pb, accv[db]);
-#pragma unroll
-    for (int db = 0; db < 8; ++db) acck[db] = mfma(tr_frag(qs0 + st + trq, db), dsb, acck[db]);
+    for (int db = 0; db < 8; ++db) {
+      const bf16x8 a = tr_frag(qs0 + st + trq, db);
+      acck[0][db] = mfma(a, dsb[0], acck[0][db]);
+      acck[1][db] = mfma(a, dsb[1], acck[1][db]);
+    }
     if (++ch == G) { ch = 0; ++ce; }
   }
   wait_vmcnt<0>();
 
-  // Epilogue: lane holds dims 16 db + 4 g + e of key r16.
-  const bool valid = key < p.tk;
-  const size_t off = (size_t(valid ? key : 0) * p.hk + kvh) * D;
-  if (valid) {
-#pragma unroll
-    for (int db = 0; db < 8; ++db) {
-      bf16x4 w;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) w[e] = (__bf16)accv[db][e];
-      *reinterpret_cast<bf16x4*>(static_cast<__bf16*>(p.dv) + off + 16 * db + 4 * g) = w;
-    }
-  }
-  float gp[8][4], dxh[8][4];
+  // Epilogue: lane holds dims 16 db + 4 g + e of key key0 + 16 j.
+  float gp[8][4];
 #pragma unroll
   for (int db = 0; db < 8; ++db)
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      gp[db][e] = 0.0f;
-      dxh[db][e] = p.scale * acck[db][e];
-    }
+    for (int e = 0; e < 4; ++e) gp[db][e] = 0.0f;
   __syncthreads();
-  rms_backward_row(static_cast<const __bf16*>(p.k) + off, static_cast<__bf16*>(p.dk) + off, dxh, sm.gk, p.eps,
-                   valid, gp, g);
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int key = key0 + 16 * j;
+    const bool valid = key < p.tk;
+    const size_t off = (size_t(valid ? key : 0) * p.hk + kvh) * D;
+    if (valid) {
+#pragma unroll
+      for (int db = 0; db < 8; ++db) {
+        bf16x4 w;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) w[e] = (__bf16)accv[j][db][e];
+        *reinterpret_cast<bf16x4*>(static_cast<__bf16*>(p.dv) + off + 16 * db + 4 * g) = w;
+      }
+    }
+    float dxh[8][4];
+#pragma unroll
+    for (int db = 0; db < 8; ++db)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) dxh[db][e] = p.scale * acck[j][db][e];
+    rms_backward_row(static_cast<const __bf16*>(p.k) + off, static_cast<__bf16*>(p.dk) + off, dxh, sm.gk, p.eps,
+                     valid, gp, g);
+  }
   store_gain_partial(gp, sm.red, part, wave, lane, tid);
 }
 

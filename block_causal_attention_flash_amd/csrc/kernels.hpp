@@ -10,7 +10,7 @@ namespace magi {
 constexpr int kBf16RowsPerItem = 384;
 // Rows of one bf16 dq work item of the backward, and keys of one dk/dv item.
 constexpr int kBwdRowsPerItem = 256;
-constexpr int kBwdKeysPerItem = 128;
+constexpr int kBwdKeysPerItem = 256;
 
 struct FwdParams {
   const void* q;
