@@ -34,6 +34,7 @@ METRIC_BACKWARD = "block-causal attn bwd useful TFLOP/s (2.5x fwd FLOPs) and % b
 METRIC_PARALLEL = "parallel block-causal self- + text cross-attn fwd useful TFLOP/s and % bf16 MFMA peak, 1×MI355X"
 PEAK_BF16_TFLOPS = 2500.0          # MI355X dense bf16 MFMA, published
 KERNEL_SRC = os.path.join(ROOT, "block_causal_attention_flash_amd", "csrc", "fwd_bf16.hip")
+BWD_KERNEL_SRC = os.path.join(ROOT, "block_causal_attention_flash_amd", "csrc", "bwd_bf16.hip")
 
 
 def useful_pairs(layout) -> int:
@@ -61,10 +62,10 @@ def useful_text_pairs(layout, text) -> int:
                for c in range(layout.n_chunks))
 
 
-def kernel_hash() -> str:
-    """sha256 (16 hex digits) of the kernel source with comments and blank
+def kernel_hash(path: str = KERNEL_SRC) -> str:
+    """sha256 (16 hex digits) of a kernel source with comments and blank
     space removed, so that the stored counters go stale on code changes only."""
-    with open(KERNEL_SRC) as f:
+    with open(path) as f:
         src = f.read()
     src = re.sub(r"/\*.*?\*/", " ", src, flags=re.S)
     src = re.sub(r"//[^\n]*", " ", src)
@@ -84,6 +85,19 @@ def stored_traffic(workload: str, attention: str = "self"):
     if doc.get("kernel_sha256_16") != kernel_hash():
         return None
     return doc.get("hbm_bytes_per_launch")
+
+
+def stored_backward_traffic(workload: str):
+    """HBM bytes per backward call (all of its kernels) from the committed
+    counter summary, or None when missing or taken on a different source."""
+    path = os.path.join(ROOT, "profiles", f"bwd_bf16_{workload}_traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        doc = json.load(f)
+    if doc.get("kernel_sha256_16") != kernel_hash(BWD_KERNEL_SRC):
+        return None
+    return doc.get("hbm_bytes_per_call")
 
 
 def first_visible(lay, c):
@@ -186,8 +200,12 @@ def bench_backward(args) -> None:
     pairs = useful_pairs(lay)
     flops = 2.5 * 4.0 * cfg.head_dim * cfg.n_q_heads * pairs
     tflops = flops / (ms * 1e-3) / 1e12
+    # The roofline of the whole call (pre-passes, dq, dk/dv, reductions):
+    # useful FLOPs over the call's time; traffic is summed over its kernels.
     roof = {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-            "frac": round(tflops / PEAK_BF16_TFLOPS, 4), "traffic": None}
+            "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
+            "traffic": stored_backward_traffic(cfg.name) if cfg.dtype == "bf16" and not (lay.kv_range or lay.last_global)
+            else None}
     rec = {
         "metric": METRIC_BACKWARD, "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak",

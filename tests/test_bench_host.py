@@ -46,6 +46,26 @@ def test_stored_traffic_is_tied_to_the_kernel_source():
     assert bench.stored_traffic("no-such-workload") is None
 
 
+def test_stored_backward_traffic_is_tied_to_the_backward_source(tmp_path, monkeypatch):
+    path = os.path.join(ROOT, "profiles", "bwd_bf16_video480x832_traffic.json")
+    if os.path.exists(path):
+        with open(path) as f:
+            doc = json.load(f)
+        want = doc["hbm_bytes_per_call"] if doc.get("kernel_sha256_16") == bench.kernel_hash(bench.BWD_KERNEL_SRC) else None
+        assert bench.stored_backward_traffic("video480x832") == want
+    # a changed source (comments aside) makes the stored figure stale
+    src = tmp_path / "bwd.hip"
+    with open(bench.BWD_KERNEL_SRC) as f:
+        text = f.read()
+    src.write_text(text + "\n// a comment changes nothing\n")
+    assert bench.kernel_hash(str(src)) == bench.kernel_hash(bench.BWD_KERNEL_SRC)
+    src.write_text(text + "\nint changed;\n")
+    assert bench.kernel_hash(str(src)) != bench.kernel_hash(bench.BWD_KERNEL_SRC)
+    monkeypatch.setattr(bench, "BWD_KERNEL_SRC", str(src))
+    assert bench.stored_backward_traffic("video480x832") is None
+    assert bench.stored_backward_traffic("no-such-workload") is None
+
+
 def test_more_than_one_gpu_is_refused(monkeypatch, capsys):
     monkeypatch.setattr("sys.argv", ["bench.py", "--gpus", "2"])
     with pytest.raises(SystemExit) as e:
