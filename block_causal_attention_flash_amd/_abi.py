@@ -90,6 +90,8 @@ class Stats(ctypes.Structure):
 SIGNATURES = {
     "magi_attn_plan_create": (ctypes.c_int, [ctypes.POINTER(Layout), ctypes.POINTER(ctypes.c_void_p)]),
     "magi_attn_train_plan_create": (ctypes.c_int, [ctypes.POINTER(Layout), ctypes.POINTER(ctypes.c_void_p)]),
+    "magi_attn_cross_train_plan_create": (ctypes.c_int, [ctypes.POINTER(Layout), ctypes.POINTER(Text),
+                                                         ctypes.POINTER(ctypes.c_void_p)]),
     "magi_attn_bwd_workspace_size": (ctypes.c_int, [ctypes.c_void_p, ctypes.POINTER(ctypes.c_size_t)]),
     "magi_attn_bwd": (ctypes.c_int, [ctypes.c_void_p, ctypes.POINTER(BwdIO), ctypes.c_float, ctypes.c_float,
                                      ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]),

@@ -137,6 +137,17 @@ def magi_attn_train_plan_create(q_offsets, kv_offsets=None, seq_chunks=None, n_q
     return h.value
 
 
+def magi_attn_cross_train_plan_create(q_offsets, text_begin, text_end, t_text, kv_offsets=None, seq_chunks=None,
+                                      n_q_heads=1, n_kv_heads=1, head_dim=128, dtype="bf16", kv_range=0,
+                                      last_global=0) -> int:
+    lib = _abi.load()
+    la = _LayoutArgs(q_offsets, kv_offsets, seq_chunks, n_q_heads, n_kv_heads, head_dim, dtype, kv_range, last_global)
+    ta = _TextArgs(text_begin, text_end, t_text)
+    h = ctypes.c_void_p()
+    _check(lib, lib.magi_attn_cross_train_plan_create(la.ptr(), ta.ptr(), ctypes.byref(h)))
+    return h.value
+
+
 def magi_attn_bwd_workspace_size(handle: int) -> int:
     lib = _abi.load()
     n = ctypes.c_size_t()
@@ -426,12 +437,9 @@ class ParallelPlan(Plan):
                                       rms_eps, scale, scale_x, out, lse, out_x, lse_x, workspace, stream)
 
 
-class TrainPlan(Plan):
-    """A self-attention plan that also runs the backward: call() is the
-    forward, backward() the gradients from the forward's out and lse."""
-
-    def _create(self) -> int:
-        return magi_attn_train_plan_create(**self.layout)
+class _Backward:
+    """backward() of a training plan: the gradients from the forward's out
+    and lse (keys of the plan's key stream: the video's, or the text's)."""
 
     def bwd_workspace_size(self) -> int:
         return magi_attn_bwd_workspace_size(self.handle)
@@ -443,3 +451,20 @@ class TrainPlan(Plan):
             raise ValueError("dout must match q")
         return magi_attn_bwd(self.handle, q, k, v, out, lse, dout, q_gain, k_gain, rms_eps, scale, dq, dk, dv, dq_gain,
                              dk_gain, workspace, stream)
+
+
+class TrainPlan(_Backward, Plan):
+    """A self-attention plan that also runs the backward: call() is the
+    forward, backward() the gradients from the forward's out and lse."""
+
+    def _create(self) -> int:
+        return magi_attn_train_plan_create(**self.layout)
+
+
+class CrossTrainPlan(_Backward, CrossPlan):
+    """A cross-attention plan that also runs the backward: call(q, k_text,
+    v_text, ...) is the forward, backward(q, k_text, v_text, out, lse, dout,
+    ...) the gradients, dk and dv over the text tokens."""
+
+    def _create(self) -> int:
+        return magi_attn_cross_train_plan_create(**self.layout, **self.text)

@@ -28,6 +28,8 @@ struct magi_attn_plan {
   const int4* d_kv_items = nullptr;
   const int* d_kv_tiles = nullptr;
   const int4* d_key_rows = nullptr;
+  const int2* d_dq_zero = nullptr;
+  const int2* d_kv_zero = nullptr;
 };
 
 namespace {
@@ -116,7 +118,7 @@ magi_status_t create_plan(int32_t kind, bool train, const magi_attn_layout_t* la
   p->train = train;
   try {
     s = magi::build_host_plan(kind, layout, text, tiling_of(layout), p->host, err);
-    if (s == MAGI_OK && train) s = magi::build_bwd_plan(layout, p->bwd, err);
+    if (s == MAGI_OK && train) s = magi::build_bwd_plan(layout, kind == magi::kPlanCross ? text : nullptr, p->bwd, err);
   } catch (const std::bad_alloc&) {
     delete p;
     return fail(MAGI_ERR_NO_MEMORY, "host allocation failed");
@@ -138,6 +140,8 @@ magi_status_t create_plan(int32_t kind, bool train, const magi_attn_layout_t* la
   const size_t o_kv_items = up.add(B.items.data(), bytes(B.items));
   const size_t o_kv_tiles = up.add(B.kv_tiles.data(), bytes(B.kv_tiles));
   const size_t o_key_rows = up.add(B.key_rows.data(), bytes(B.key_rows));
+  const size_t o_dq_zero = up.add(B.dq_zero.data(), bytes(B.dq_zero));
+  const size_t o_kv_zero = up.add(B.kv_zero.data(), bytes(B.kv_zero));
   hipError_t e = hipGetDevice(&p->device);
   if (e != hipSuccess) { delete p; return hip_fail(e, "hipGetDevice"); }
   e = hipMalloc(&p->dmem, std::max<size_t>(up.total, 256));
@@ -164,6 +168,8 @@ magi_status_t create_plan(int32_t kind, bool train, const magi_attn_layout_t* la
   p->d_kv_items = reinterpret_cast<const int4*>(base + o_kv_items);
   p->d_kv_tiles = reinterpret_cast<const int*>(base + o_kv_tiles);
   p->d_key_rows = reinterpret_cast<const int4*>(base + o_key_rows);
+  p->d_dq_zero = reinterpret_cast<const int2*>(base + o_dq_zero);
+  p->d_kv_zero = reinterpret_cast<const int2*>(base + o_kv_zero);
   *out_plan = p;
   return MAGI_OK;
 }
@@ -305,6 +311,11 @@ magi_status_t magi_attn_train_plan_create(const magi_attn_layout_t* layout, magi
   return create_plan(magi::kPlanSelf, true, layout, nullptr, out_plan);
 }
 
+magi_status_t magi_attn_cross_train_plan_create(const magi_attn_layout_t* layout, const magi_attn_text_t* text,
+                                                magi_attn_plan_t** out_plan) {
+  return create_plan(magi::kPlanCross, true, layout, text, out_plan);
+}
+
 magi_status_t magi_attn_cross_plan_create(const magi_attn_layout_t* layout, const magi_attn_text_t* text,
                                           magi_attn_plan_t** out_plan) {
   return create_plan(magi::kPlanCross, false, layout, text, out_plan);
@@ -410,16 +421,22 @@ magi_status_t magi_attn_bwd(const magi_attn_plan_t* plan, const magi_attn_bwd_io
                             void* workspace, size_t workspace_bytes, void* stream) {
   if (!plan) return fail(MAGI_ERR_INVALID_ARG, "plan is NULL");
   if (!io) return fail(MAGI_ERR_INVALID_ARG, "io is NULL");
-  if (!plan->train) return fail(MAGI_ERR_INVALID_ARG, "magi_attn_bwd needs a plan from magi_attn_train_plan_create");
+  if (!plan->train)
+    return fail(MAGI_ERR_INVALID_ARG,
+                "magi_attn_bwd needs a plan from magi_attn_train_plan_create or magi_attn_cross_train_plan_create");
   const auto& H = plan->host;
   size_t need = 0;
   magi_attn_bwd_workspace_size(plan, &need);
   if (workspace_bytes < need) return fail(MAGI_ERR_INVALID_ARG, "workspace smaller than magi_attn_bwd_workspace_size()");
   if (need && (!workspace || !aligned(workspace, 16)))
     return fail(MAGI_ERR_INVALID_ARG, "workspace must be non-NULL and 16-byte aligned");
-  const void* tens[] = {io->q, io->k, io->v, io->out, io->dout, io->dq, io->dk, io->dv};
+  const void* tens[] = {io->q, io->out, io->dout, io->dq};
   for (const void* t : tens)
-    if (!t || !aligned(t, 16)) return fail(MAGI_ERR_INVALID_ARG, "q, k, v, out, dout, dq, dk, dv must be non-NULL and 16-byte aligned");
+    if (!t || !aligned(t, 16)) return fail(MAGI_ERR_INVALID_ARG, "q, out, dout, dq must be non-NULL and 16-byte aligned");
+  const void* ktens[] = {io->k, io->v, io->dk, io->dv};                 // may be NULL when there are no keys
+  for (const void* t : ktens)
+    if ((H.tk > 0 && !t) || !aligned(t, 16))
+      return fail(MAGI_ERR_INVALID_ARG, "k, v, dk, dv must be non-NULL (unless T_k == 0) and 16-byte aligned");
   if (!io->lse || !aligned(io->lse, 4) || !io->q_gain || !io->k_gain || !aligned(io->q_gain, 16) ||
       !aligned(io->k_gain, 16) || !io->dq_gain || !io->dk_gain || !aligned(io->dq_gain, 4) || !aligned(io->dk_gain, 4))
     return fail(MAGI_ERR_INVALID_ARG, "lse, the gains and the gain gradients must be non-NULL and aligned");
@@ -457,6 +474,11 @@ magi_status_t magi_attn_bwd(const magi_attn_plan_t* plan, const magi_attn_bwd_io
   b.kv_items = plan->d_kv_items;
   b.kv_tiles = plan->d_kv_tiles;
   b.key_rows = plan->d_key_rows;
+  b.dq_zero = plan->d_dq_zero;
+  b.n_dq_zero = int(plan->bwd.dq_zero.size() / 2);
+  b.kv_zero = plan->d_kv_zero;
+  b.n_kv_zero = int(plan->bwd.kv_zero.size() / 2);
+  b.key_block = plan->bwd.key_block;
   b.n_dq_items = int(plan->bwd.dq.items.size());
   b.n_kv_items = int(plan->bwd.items.size());
   hipStream_t st = static_cast<hipStream_t>(stream);

@@ -672,7 +672,34 @@ __global__ void __launch_bounds__(256) bwd_gain_final_kernel(const float* level,
   (side ? dk_gain : dq_gain)[d] = x;
 }
 
+// dq = 0 over the blocks whose rows see no key (no dq item covers them): one
+// workgroup per block of `rows` tokens x `heads` heads, 16-byte stores.
+__global__ void __launch_bounds__(256) bwd_zero_rows_kernel(unsigned char* dq, const int2* __restrict__ blocks,
+                                                           int rows, int heads, int tq, int hq, int row_bytes) {
+  const int2 blk = blocks[blockIdx.x];
+  const int chunks = row_bytes / 16;
+  const int n = rows * heads * chunks;
+  for (int i = threadIdx.x; i < n; i += blockDim.x) {
+    const int c = i % chunks, hh = (i / chunks) % heads, r = i / (chunks * heads);
+    const int tok = blk.x + r;
+    if (tok < tq) *reinterpret_cast<int4*>(dq + (size_t(tok) * hq + blk.y + hh) * row_bytes + 16 * c) = int4{0, 0, 0, 0};
+  }
+}
+
 }  // namespace
+
+hipError_t launch_bwd_zero_rows(const BwdParams& p, int row_bytes, hipStream_t stream) {
+  if (p.n_dq_zero > 0)
+    hipLaunchKernelGGL(bwd_zero_rows_kernel, dim3(p.n_dq_zero), dim3(256), 0, stream, static_cast<unsigned char*>(p.dq),
+                       p.dq_zero, p.tile_q, p.heads_per_item, p.tq, p.hq, row_bytes);
+  if (p.n_kv_zero > 0) {
+    hipLaunchKernelGGL(bwd_zero_rows_kernel, dim3(p.n_kv_zero), dim3(256), 0, stream, static_cast<unsigned char*>(p.dk),
+                       p.kv_zero, p.key_block, p.hk, p.tk, p.hk, row_bytes);
+    hipLaunchKernelGGL(bwd_zero_rows_kernel, dim3(p.n_kv_zero), dim3(256), 0, stream, static_cast<unsigned char*>(p.dv),
+                       p.kv_zero, p.key_block, p.hk, p.tk, p.hk, row_bytes);
+  }
+  return hipGetLastError();
+}
 
 BwdLayout bwd_workspace_layout(long long tq, long long tk, int hq, int hk, int n_dq_items, int n_kv_items) {
   auto up = [](size_t x) { return (x + 255) / 256 * 256; };
@@ -695,7 +722,10 @@ hipError_t launch_bwd_bf16_d128(const BwdParams& p, hipStream_t stream) {
   const BwdLayout L = bwd_workspace_layout(p.tq, p.tk, p.hq, p.hk, p.n_dq_items, p.n_kv_items);
   const unsigned n_tt = unsigned((p.tq + TT - 1) / TT), n_kt = unsigned((p.tk + TT - 1) / TT);
   hipLaunchKernelGGL(bwd_prep_q_kernel, dim3(n_tt * unsigned(p.hq)), dim3(PREP_THREADS), 0, stream, p, L);
-  hipLaunchKernelGGL(bwd_prep_k_kernel, dim3(n_kt * unsigned(p.hk)), dim3(PREP_THREADS), 0, stream, p, L);
+  if (n_kt > 0)
+    hipLaunchKernelGGL(bwd_prep_k_kernel, dim3(n_kt * unsigned(p.hk)), dim3(PREP_THREADS), 0, stream, p, L);
+  const hipError_t ez = launch_bwd_zero_rows(p, D * 2, stream);
+  if (ez != hipSuccess) return ez;
   if (p.n_dq_items > 0)
     hipLaunchKernelGGL(bwd_dq_kernel, dim3(p.n_dq_items), dim3(NTHR), 0, stream, p, L, p.dq_items, p.dq_tiles,
                        p.dq_soffs);

@@ -270,6 +270,8 @@ hipError_t launch(const BwdParams& p, hipStream_t stream) {
   hipLaunchKernelGGL(bwd_prep_f32_kernel<D>, dim3(unsigned((rows + 63) / 64)), dim3(64), 0, stream, p, L);
   if (p.n_dq_items > 0) hipLaunchKernelGGL(bwd_dq_f32_kernel<D>, dim3(p.n_dq_items), dim3(64), 0, stream, p, L);
   if (p.n_kv_items > 0) hipLaunchKernelGGL(bwd_dkdv_f32_kernel<D>, dim3(p.n_kv_items), dim3(64), 0, stream, p, L);
+  const hipError_t ez = launch_bwd_zero_rows(p, D * 4, stream);
+  if (ez != hipSuccess) return ez;
   unsigned char* ws = static_cast<unsigned char*>(p.ws);
   hipLaunchKernelGGL(bwd_gain_reduce_f32_kernel<D>, dim3(1), dim3(256), 0, stream,
                      reinterpret_cast<const float*>(ws + L.pgq), p.n_dq_items,

@@ -78,7 +78,11 @@ struct BwdParams {
   const int4* kv_items;   // KeyItem[n_kv_items]
   const int* kv_tiles;    // token tile codes (tt * 2 + masked) per key block
   const int4* key_rows;   // per-key token ranges [tk]: own video [x, y), last global block [z, w)
-  int n_dq_items, n_kv_items;
+                          // (cross plans: the two runs of rows that see a text key)
+  const int2* dq_zero;    // (t0, first head) of the dq blocks (tile_q tokens x heads_per_item heads) with no key
+  const int2* kv_zero;    // (first key, 0) of the key blocks (key_block keys x all KV heads) no query sees
+  int key_block;
+  int n_dq_items, n_kv_items, n_dq_zero, n_kv_zero;
 };
 
 // Byte offsets of the backward workspace's parts.
@@ -88,6 +92,9 @@ struct BwdLayout {
 BwdLayout bwd_workspace_layout(long long tq, long long tk, int hq, int hk, int n_dq_items, int n_kv_items);
 hipError_t launch_bwd_bf16_d128(const BwdParams& p, hipStream_t stream);
 hipError_t launch_bwd_fp32(const BwdParams& p, int head_dim, hipStream_t stream);
+// Writes zeros where no item writes: dq over the p.dq_zero blocks, dk and dv
+// over the p.kv_zero blocks (rows of row_bytes = head_dim * element size).
+hipError_t launch_bwd_zero_rows(const BwdParams& p, int row_bytes, hipStream_t stream);
 size_t bwd_workspace_bytes_fp32(long long tq, long long tk, int hq, int hk, int head_dim, int n_dq_items,
                                 int n_kv_items);
 

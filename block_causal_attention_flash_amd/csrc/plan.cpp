@@ -168,6 +168,34 @@ void key_bounds(const magi_attn_layout_t* L, std::vector<KeyBounds>& keys) {
     }
 }
 
+magi_status_t text_key_bounds(const magi_attn_layout_t* L, const magi_attn_text_t* T, std::vector<KeyBounds>& keys,
+                              std::string& err) {
+  // Chunks in order: a chunk's rows either extend the key's latest range
+  // (they start where it ends) or open its next one.
+  keys.assign(T->t_text, KeyBounds{0, 0, 0, 0});
+  for (int c = 0; c < L->n_chunks; ++c) {
+    const int32_t r0 = L->q_offsets[c], r1 = L->q_offsets[c + 1];
+    if (r0 == r1) continue;
+    for (int32_t j = T->text_begin[c]; j < T->text_end[c]; ++j) {
+      KeyBounds& b = keys[j];
+      if (b.glo < b.ghi) {
+        if (b.ghi != r0) {
+          err = "text token " + std::to_string(j) +
+                " is seen by more than two separate runs of chunks (the backward supports two)";
+          return MAGI_ERR_UNSUPPORTED;
+        }
+        b.ghi = r1;
+      } else if (b.lo < b.hi) {
+        if (b.hi == r0) b.hi = r1;
+        else b.glo = r0, b.ghi = r1;
+      } else {
+        b.lo = r0, b.hi = r1;
+      }
+    }
+  }
+  return MAGI_OK;
+}
+
 int classify_key_pair(const std::vector<KeyBounds>& iv, int64_t t0, int64_t t1, int64_t tq) {
   if (iv.empty()) return 0;
   bool all = true, any = false;
@@ -413,17 +441,31 @@ magi_status_t build_host_plan(int32_t kind, const magi_attn_layout_t* L, const m
   return MAGI_OK;
 }
 
-magi_status_t build_bwd_plan(const magi_attn_layout_t* L, BwdHostPlan& B, std::string& err) {
+magi_status_t build_bwd_plan(const magi_attn_layout_t* L, const magi_attn_text_t* T, BwdHostPlan& B,
+                             std::string& err) {
   const int group = L->n_q_heads / L->n_kv_heads;
-  magi_status_t s = build_host_plan(kPlanSelf, L, nullptr, choose_bwd_tiling(L->dtype, L->head_dim, group), B.dq, err,
-                                    /*allow_split=*/false);
+  magi_status_t s = build_host_plan(T ? kPlanCross : kPlanSelf, L, T, choose_bwd_tiling(L->dtype, L->head_dim, group),
+                                    B.dq, err, /*allow_split=*/false);
   if (s != MAGI_OK) return s;
+  // Query blocks without any key have no dq item (their merge entries hold no
+  // pieces): their dq is zero.
+  B.dq_zero.clear();
+  for (const MergeItem& m : B.dq.merges)
+    if (m.n_pieces == 0) {
+      B.dq_zero.push_back(m.t0);
+      B.dq_zero.push_back(m.heads & 0xffff);
+    }
   const int32_t* kv = L->kv_offsets ? L->kv_offsets : L->q_offsets;
-  const int64_t tq = L->q_offsets[L->n_chunks], tk = kv[L->n_chunks];
+  const int64_t tq = L->q_offsets[L->n_chunks], tk = T ? T->t_text : kv[L->n_chunks];
   const int kb_size = L->dtype == MAGI_DTYPE_BF16 ? kBwdKeysPerItem : 64;
   const int tt_size = B.token_tile;
   B.key_block = kb_size;
-  key_bounds(L, B.key_rows);
+  if (T) {
+    s = text_key_bounds(L, T, B.key_rows, err);
+    if (s != MAGI_OK) return s;
+  } else {
+    key_bounds(L, B.key_rows);
+  }
 
   // Per key block: the token tiles that see any of its keys, full first.
   const int64_t n_kb = (tk + kb_size - 1) / kb_size;
@@ -460,6 +502,13 @@ magi_status_t build_bwd_plan(const magi_attn_layout_t* L, BwdHostPlan& B, std::s
     kb_n[kb] = int32_t(B.kv_tiles.size()) - kb_begin[kb];
     B.kv_tiles.insert(B.kv_tiles.end(), kTilePad, -1);
   }
+  // Key blocks that no query sees get no item: their dk and dv are zero.
+  B.kv_zero.clear();
+  for (int64_t kb = 0; kb < n_kb; ++kb)
+    if (kb_n[kb] == 0) {
+      B.kv_zero.push_back(int32_t(kb * kb_size));
+      B.kv_zero.push_back(0);
+    }
 
   // Items (key block, KV head), longest first, KV head -> XCD as for the
   // forward's items.

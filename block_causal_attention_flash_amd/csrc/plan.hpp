@@ -128,6 +128,8 @@ struct BwdHostPlan {
   std::vector<KeyBounds> key_rows;   // [tk] token ranges of the queries that see each key
   std::vector<int32_t> kv_tiles;     // per key block: token tile codes, full first, then boundary; padded
   std::vector<KeyItem> items;        // launch order (XCD-interleaved, padded)
+  std::vector<int32_t> dq_zero;      // (t0, first head) of the dq blocks whose rows see no key: dq = 0 there
+  std::vector<int32_t> kv_zero;      // (first key, 0) of the key blocks no query sees: dk = dv = 0 there
 };
 
 // Whether video s is a last global block (its queries see every key).
@@ -161,7 +163,10 @@ magi_status_t build_host_plan(int32_t kind, const magi_attn_layout_t* layout, co
                               const Tiling& tiling, HostPlan& plan, std::string& err, bool allow_split = true);
 
 // Builds the backward's work lists of a self-attention layout (valid).
-magi_status_t build_bwd_plan(const magi_attn_layout_t* layout, BwdHostPlan& plan, std::string& err);
+// Backward lists of a self plan (text == NULL) or of a cross plan (the text
+// keys are the keys).
+magi_status_t build_bwd_plan(const magi_attn_layout_t* layout, const magi_attn_text_t* text, BwdHostPlan& plan,
+                             std::string& err);
 
 // Per-key token ranges: the queries that see each key.
 void key_bounds(const magi_attn_layout_t* layout, std::vector<KeyBounds>& keys);
@@ -169,6 +174,13 @@ void key_bounds(const magi_attn_layout_t* layout, std::vector<KeyBounds>& keys);
 // Class of the pair (token tile [t0, t1), keys with ranges iv): 2 every
 // (token, key) pair allowed, 1 some, 0 none; tokens at or past tq count as
 // not allowed.
+// The token ranges of the queries that see each text key (chunk c's rows see
+// [text_begin[c], text_end[c])): the rows of the chunks whose range holds the
+// key, merged where they touch. MAGI_ERR_UNSUPPORTED when some key is seen by
+// more than two separate runs of rows.
+magi_status_t text_key_bounds(const magi_attn_layout_t* layout, const magi_attn_text_t* text,
+                              std::vector<KeyBounds>& keys, std::string& err);
+
 int classify_key_pair(const std::vector<KeyBounds>& iv, int64_t t0, int64_t t1, int64_t tq);
 
 // Per-query-token key bounds [lo, hi) of the block-causal self-attention

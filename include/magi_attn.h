@@ -57,7 +57,7 @@
 extern "C" {
 #endif
 
-#define MAGI_ATTN_ABI_VERSION 5
+#define MAGI_ATTN_ABI_VERSION 6
 
 typedef enum magi_status {
   MAGI_OK = 0,
@@ -186,6 +186,19 @@ MAGI_API magi_status_t magi_attn_parallel_plan_create(const magi_attn_layout_t* 
  */
 MAGI_API magi_status_t magi_attn_train_plan_create(const magi_attn_layout_t* layout, magi_attn_plan_t** plan);
 
+/*
+ * Plan for training the text cross-attention (magi_attn_text_t): the cross
+ * plan of magi_attn_cross_plan_create (forward with magi_attn_fwd, the text
+ * keys/values as k and v) plus the backward's lists, with the text keys as
+ * the keys (the training of the pages' cross-attention branch, paperlayer
+ * §2.2.2 with §4.1.2). Same rules and errors as magi_attn_cross_plan_create
+ * and magi_attn_train_plan_create; in addition MAGI_ERR_UNSUPPORTED when a
+ * text token is seen by more than two separate runs of query rows (chunks
+ * that share a prompt and are adjacent count as one run).
+ */
+MAGI_API magi_status_t magi_attn_cross_train_plan_create(const magi_attn_layout_t* layout,
+                                                         const magi_attn_text_t* text, magi_attn_plan_t** plan);
+
 /* Frees the plan and its device memory (synchronous with respect to the host;
  * the caller must not destroy a plan that queued work still uses). NULL is OK. */
 MAGI_API magi_status_t magi_attn_plan_destroy(magi_attn_plan_t* plan);
@@ -277,7 +290,11 @@ MAGI_API magi_status_t magi_attn_bwd_workspace_size(const magi_attn_plan_t* plan
  * gradient of the loss with respect to out ([T_q][n_q_heads][head_dim], the
  * element type of the layout). Outputs (caller-owned, written in full):
  * dq [T_q][n_q_heads][head_dim], dk and dv [T_k][n_kv_heads][head_dim] (the
- * element type of the layout), dq_gain and dk_gain [head_dim] float32.
+ * element type of the layout), dq_gain and dk_gain [head_dim] float32. For a
+ * cross training plan, k and v are the text keys/values, dk and dv
+ * [t_text][n_kv_heads][head_dim] their gradients, and the gains the
+ * cross-attention's; with t_text == 0, k, v, dk and dv may be NULL. Rows
+ * that see no key (a chunk without text) get dq = 0.
  */
 typedef struct magi_attn_bwd_io {
   const void* q;
@@ -296,7 +313,7 @@ typedef struct magi_attn_bwd_io {
 } magi_attn_bwd_io_t;
 
 /*
- * Enqueues the backward pass of the self-attention on `stream`: the
+ * Enqueues the backward pass of a training plan's attention on `stream`: the
  * gradients of a loss with respect to q, k, v and both gains, given its
  * gradient dout with respect to out (the chain rule of the forward defined
  * at the top; the attention's backward from saved softmax statistics,

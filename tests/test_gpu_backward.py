@@ -52,7 +52,10 @@ def run(lay, hq, hk, d, dtype, seed, eps=1e-6, scale=None):
     plan = TrainPlan.from_layout(lay, hq, hk, d, dtype)
     g = {n: t.to(DEV) for n, t in inp.items()}
     out, lse = plan(g["q"], g["k"], g["v"], g["q_gain"], g["k_gain"], eps, sc)
-    grads = plan.backward(g["q"], g["k"], g["v"], out, lse, dout.to(DEV), g["q_gain"], g["k_gain"], eps, sc)
+    # Poison the outputs: every element must be written.
+    dq, dk, dv = (torch.full_like(g[n], float("nan")) for n in ("q", "k", "v"))
+    grads = plan.backward(g["q"], g["k"], g["v"], out, lse, dout.to(DEV), g["q_gain"], g["k_gain"], eps, sc,
+                          dq=dq, dk=dk, dv=dv)
     torch.cuda.synchronize()
     got = [t.double().cpu().numpy() for t in grads]
     plan.close()
@@ -78,6 +81,8 @@ SMALL = [
     ("window", dataclasses.replace(layout_from_chunks([[130, 70, 96, 150], [190, 40]]), kv_range=2)),
     ("last_global", dataclasses.replace(layout_from_chunks([[130, 70], [1, 2, 3], [96, 150], [190, 40]]),
                                         last_global=1)),
+    # video 0 is one cached chunk without queries: no row sees its 300 keys (a whole 256-key block among them)
+    ("unseen_video", Layout((0, 0, 140, 230), (0, 300, 400, 530), (0, 1, 3))),
 ]
 
 
@@ -89,7 +94,7 @@ def test_bf16_backward_small(name, lay, hq, hk):
     log("  rel_l2 dq {:.2e} dk {:.2e} dv {:.2e} dgq {:.2e} dgk {:.2e}".format(*errs))
 
 
-FP32_SMALL = SMALL[:4] + SMALL[-1:]
+FP32_SMALL = SMALL[:4] + SMALL[-2:]
 
 
 @pytest.mark.parametrize("name,lay", FP32_SMALL, ids=[s[0] for s in FP32_SMALL])
@@ -98,6 +103,13 @@ def test_fp32_backward_small(name, lay, d):
     log(f"fp32 backward {name} d={d}")
     errs = check(lay, 4, 2, d, "fp32", seed=d)
     log("  rel_l2 dq {:.2e} dk {:.2e} dv {:.2e} dgq {:.2e} dgk {:.2e}".format(*errs))
+
+
+def test_keys_no_row_sees_get_zero_gradients():
+    lay = SMALL[-1][1]
+    got, ref = run(lay, 6, 2, 128, "bf16", seed=4)
+    assert np.all(ref[1][:300] == 0) and np.all(ref[2][:300] == 0)
+    assert np.all(got[1][:300] == 0) and np.all(got[2][:300] == 0)
 
 
 def test_bf16_backward_scale_and_eps():

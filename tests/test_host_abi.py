@@ -34,7 +34,7 @@ def test_abi_version(built_lib):
     from block_causal_attention_flash_amd import magi_attn_abi_version
     hdr = open(os.path.join(ROOT, "include", "magi_attn.h")).read()
     declared = int(re.search(r"#define MAGI_ATTN_ABI_VERSION (\d+)", hdr).group(1))
-    assert magi_attn_abi_version() == declared == 5
+    assert magi_attn_abi_version() == declared == 6
 
 
 def brute_classes(layout, bm, bn, mask=None):
@@ -238,13 +238,28 @@ TEXT_BAD = [
 @pytest.mark.parametrize("kw,status", TEXT_BAD)
 def test_invalid_text_is_rejected(built_lib, kw, status):
     from block_causal_attention_flash_amd import (MagiAttnError, magi_attn_cross_plan_create,
-                                                  magi_attn_cross_plan_stats, magi_attn_parallel_plan_create)
+                                                  magi_attn_cross_plan_stats, magi_attn_cross_train_plan_create,
+                                                  magi_attn_parallel_plan_create)
     args = dict(q_offsets=[0, 4, 8], n_q_heads=2, n_kv_heads=1, head_dim=128, dtype="bf16")
     args.update(kw)
-    for fn in (magi_attn_cross_plan_stats, magi_attn_cross_plan_create, magi_attn_parallel_plan_create):
+    for fn in (magi_attn_cross_plan_stats, magi_attn_cross_plan_create, magi_attn_parallel_plan_create,
+               magi_attn_cross_train_plan_create):
         with pytest.raises(MagiAttnError) as e:
             fn(**args)
         assert e.value.status == status and e.value.message
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+def test_cross_training_plan_limits_a_text_token_to_two_runs_of_rows(built_lib, dtype):
+    """The backward keeps two token ranges per text key. Chunks 0, 2 and 4
+    share one prompt with chunks of other prompts between them: three runs of
+    rows, refused before any HIP call. (Two runs pass this check and go on to
+    allocate the plan, which needs a GPU.)"""
+    from block_causal_attention_flash_amd import MagiAttnError, magi_attn_cross_train_plan_create
+    with pytest.raises(MagiAttnError) as e:
+        magi_attn_cross_train_plan_create([0, 4, 8, 12, 16, 20], [0, 5, 0, 5, 0], [5, 9, 5, 9, 5], 9,
+                                          n_q_heads=2, n_kv_heads=1, head_dim=128, dtype=dtype)
+    assert e.value.status == 2 and "two" in e.value.message
 
 
 def test_parallel_plan_size_limit(built_lib):
