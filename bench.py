@@ -31,6 +31,7 @@ sys.path.insert(0, ROOT)
 METRIC = "block-causal attn fwd useful TFLOP/s and % bf16 MFMA peak, 1×MI355X"
 METRIC_CROSS = "text cross-attn fwd useful TFLOP/s and % bf16 MFMA peak, 1×MI355X"
 METRIC_BACKWARD = "block-causal attn bwd useful TFLOP/s (2.5x fwd FLOPs) and % bf16 MFMA peak, 1×MI355X"
+METRIC_CROSS_BACKWARD = "text cross-attn bwd useful TFLOP/s (2.5x fwd FLOPs) and % bf16 MFMA peak, 1×MI355X"
 METRIC_PARALLEL = "parallel block-causal self- + text cross-attn fwd useful TFLOP/s and % bf16 MFMA peak, 1×MI355X"
 PEAK_BF16_TFLOPS = 2500.0          # MI355X dense bf16 MFMA, published
 KERNEL_SRC = os.path.join(ROOT, "block_causal_attention_flash_amd", "csrc", "fwd_bf16.hip")
@@ -155,27 +156,36 @@ def cpu_baseline(cfg, inp, budget_s: float = 20.0, attention: str = "self", text
 
 
 def bench_backward(args) -> None:
-    """One step = one backward call of the self-attention (the forward's out
-    and lse computed once before timing). Useful FLOPs: 2.5 x the forward's
-    (the five products S, dP, dV, dK, dQ over the mask area)."""
+    """One step = one backward call of the self-attention, or with
+    --attention cross of the text cross-attention (the forward's out and lse
+    computed once before timing). Useful FLOPs: 2.5 x the forward's (the
+    five products S, dP, dV, dK, dQ over the mask area)."""
     import numpy as np
     import torch
-    from block_causal_attention_flash_amd import TrainPlan
-    from workloads import get_config, make_inputs
+    from block_causal_attention_flash_amd import CrossTrainPlan, TrainPlan
+    from workloads import get_config, make_inputs, make_text_inputs, text_layout
 
     cfg = get_config(args.workload)
     if args.kv_range or args.last_global:
         cfg = dataclasses.replace(cfg, layout=dataclasses.replace(cfg.layout, kv_range=args.kv_range,
                                                                   last_global=int(args.last_global)))
     lay = cfg.layout
+    cross = args.attention == "cross"
     dev = torch.device("cuda", 0)
     inp = make_inputs(lay, cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim, cfg.dtype, cfg.gain_kind, cfg.seed)
+    text = text_layout(cfg) if cross else None
+    if cross:       # the text's keys, values and gains take the places of the video's
+        tx = make_text_inputs(text, cfg.n_kv_heads, cfg.head_dim, cfg.dtype, cfg.gain_kind, cfg.seed + 100)
+        inp.update(k=tx["k_x"], v=tx["v_x"], q_gain=tx["q_gain_x"], k_gain=tx["k_gain_x"])
     g = {n: t.to(dev) for n, t in inp.items()}
     tdt = g["q"].dtype
     dout = torch.from_numpy(np.random.default_rng(cfg.seed + 7).standard_normal(
         (lay.t_q, cfg.n_q_heads, cfg.head_dim), dtype=np.float32)).to(tdt).to(dev)
     t0 = time.perf_counter()
-    plan = TrainPlan.from_layout(lay, cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim, cfg.dtype)
+    if cross:
+        plan = CrossTrainPlan.from_layout(lay, text, cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim, cfg.dtype)
+    else:
+        plan = TrainPlan.from_layout(lay, cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim, cfg.dtype)
     plan_ms = (time.perf_counter() - t0) * 1e3
     stream = torch.cuda.current_stream(dev)
     out, lse = plan(g["q"], g["k"], g["v"], g["q_gain"], g["k_gain"], cfg.eps, cfg.scale, stream=stream)
@@ -185,7 +195,8 @@ def bench_backward(args) -> None:
     dgk = torch.empty_like(dgq)
     step = lambda: plan.backward(g["q"], g["k"], g["v"], out, lse, dout, g["q_gain"], g["k_gain"], cfg.eps,  # noqa
                                  cfg.scale, dq, dk, dv, dgq, dgk, ws, stream)
-    print(f"[bench] {cfg.name} backward: T_q={lay.t_q} T_k={lay.t_k} workspace={ws.numel() / 2**30:.2f} GiB "
+    print(f"[bench] {cfg.name} {args.attention} backward: T_q={lay.t_q} "
+          f"T_k={text.t_text if cross else lay.t_k} workspace={ws.numel() / 2**30:.2f} GiB "
           f"plan={plan_ms:.1f}ms", file=sys.stderr, flush=True)
     for _ in range(args.warmup):
         step()
@@ -197,20 +208,21 @@ def bench_backward(args) -> None:
     ev1.record(stream)
     torch.cuda.synchronize()
     ms = ev0.elapsed_time(ev1) / args.steps
-    pairs = useful_pairs(lay)
+    pairs = useful_text_pairs(lay, text) if cross else useful_pairs(lay)
     flops = 2.5 * 4.0 * cfg.head_dim * cfg.n_q_heads * pairs
     tflops = flops / (ms * 1e-3) / 1e12
     # The roofline of the whole call (pre-passes, dq, dk/dv, reductions):
     # useful FLOPs over the call's time; traffic is summed over its kernels.
     roof = {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
             "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
-            "traffic": stored_backward_traffic(cfg.name) if cfg.dtype == "bf16" and not (lay.kv_range or lay.last_global)
-            else None}
+            "traffic": stored_backward_traffic(cfg.name)
+            if cfg.dtype == "bf16" and not (cross or lay.kv_range or lay.last_global) else None}
     rec = {
-        "metric": METRIC_BACKWARD, "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "metric": METRIC_CROSS_BACKWARD if cross else METRIC_BACKWARD, "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": cfg.dtype, "data": "synthetic (seeded N(0,1) Q/K/V/dO)",
-        "config": {"workload": cfg.name, "pass": "backward", "t_q": lay.t_q, "t_k": lay.t_k,
+        "config": {"workload": cfg.name, "pass": "backward", "attention": args.attention, "t_q": lay.t_q,
+                   "t_k": text.t_text if cross else lay.t_k,
                    "n_chunks": lay.n_chunks, "n_q_heads": cfg.n_q_heads, "n_kv_heads": cfg.n_kv_heads,
                    "head_dim": cfg.head_dim, "kv_range": lay.kv_range, "last_global": lay.last_global,
                    "useful_flops": flops, "unmasked_pairs_per_head": pairs},
@@ -251,7 +263,8 @@ def main():
                     help="self: the block-causal self-attention; cross: the text cross-attention of the workload's "
                          "chunk-wise prompts; parallel: both in one launch")
     ap.add_argument("--backward", action="store_true",
-                    help="time the self-attention's backward (magi_attn_bwd) instead of the forward")
+                    help="time the backward (magi_attn_bwd) of the self- or (--attention cross) the "
+                         "cross-attention instead of the forward")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=20.0)
     ap.add_argument("--copy-probe-mib", type=int, default=0,
@@ -266,6 +279,10 @@ def main():
         sys.exit(2)
 
     if args.backward:
+        if args.attention == "parallel":
+            print("--backward takes --attention self or cross (the parallel block's backward is the two "
+                  "backwards, one per training plan)", file=sys.stderr)
+            sys.exit(2)
         return bench_backward(args)
     import torch
     from block_causal_attention_flash_amd import CrossPlan, ParallelPlan, Plan

@@ -30,6 +30,7 @@ struct magi_attn_plan {
   const int4* d_key_rows = nullptr;
   const int2* d_dq_zero = nullptr;
   const int2* d_kv_zero = nullptr;
+  const int4* d_kv_merges = nullptr;
 };
 
 namespace {
@@ -142,6 +143,7 @@ magi_status_t create_plan(int32_t kind, bool train, const magi_attn_layout_t* la
   const size_t o_key_rows = up.add(B.key_rows.data(), bytes(B.key_rows));
   const size_t o_dq_zero = up.add(B.dq_zero.data(), bytes(B.dq_zero));
   const size_t o_kv_zero = up.add(B.kv_zero.data(), bytes(B.kv_zero));
+  const size_t o_kv_merges = up.add(B.kv_merges.data(), bytes(B.kv_merges));
   hipError_t e = hipGetDevice(&p->device);
   if (e != hipSuccess) { delete p; return hip_fail(e, "hipGetDevice"); }
   e = hipMalloc(&p->dmem, std::max<size_t>(up.total, 256));
@@ -170,6 +172,7 @@ magi_status_t create_plan(int32_t kind, bool train, const magi_attn_layout_t* la
   p->d_key_rows = reinterpret_cast<const int4*>(base + o_key_rows);
   p->d_dq_zero = reinterpret_cast<const int2*>(base + o_dq_zero);
   p->d_kv_zero = reinterpret_cast<const int2*>(base + o_kv_zero);
+  p->d_kv_merges = reinterpret_cast<const int4*>(base + o_kv_merges);
   *out_plan = p;
   return MAGI_OK;
 }
@@ -412,7 +415,9 @@ magi_status_t magi_attn_bwd_workspace_size(const magi_attn_plan_t* plan, size_t*
   if (!plan->train) return fail(MAGI_ERR_INVALID_ARG, "not a training plan (magi_attn_train_plan_create)");
   const auto& H = plan->host;
   const int nq = int(plan->bwd.dq.items.size()), nk = int(plan->bwd.items.size());
-  *bytes = H.dtype == MAGI_DTYPE_BF16 ? magi::bwd_workspace_layout(H.tq, H.tk, H.hq, H.hk, nq, nk).total
+  const auto& B = plan->bwd;
+  *bytes = H.dtype == MAGI_DTYPE_BF16
+               ? magi::bwd_workspace_layout(H.tq, H.tk, H.hq, H.hk, nq, nk + int(B.kv_merges.size()), B.n_kv_slots).total
                                       : magi::bwd_workspace_bytes_fp32(H.tq, H.tk, H.hq, H.hk, H.d, nq, nk);
   return MAGI_OK;
 }
@@ -479,6 +484,9 @@ magi_status_t magi_attn_bwd(const magi_attn_plan_t* plan, const magi_attn_bwd_io
   b.kv_zero = plan->d_kv_zero;
   b.n_kv_zero = int(plan->bwd.kv_zero.size() / 2);
   b.key_block = plan->bwd.key_block;
+  b.kv_merges = plan->d_kv_merges;
+  b.n_kv_merges = int(plan->bwd.kv_merges.size());
+  b.n_kv_slots = plan->bwd.n_kv_slots;
   b.n_dq_items = int(plan->bwd.dq.items.size());
   b.n_kv_items = int(plan->bwd.items.size());
   hipStream_t st = static_cast<hipStream_t>(stream);

@@ -612,7 +612,12 @@ bwd_dkdv_kernel(BwdParams p, BwdLayout L, const int4* __restrict__ items, const 
   }
   wait_vmcnt<0>();
 
-  // Epilogue: lane holds dims 16 db + 4 g + e of key key0 + 16 j.
+  // Epilogue: lane holds dims 16 db + 4 g + e of key key0 + 16 j. A piece of
+  // a split list (slot >= 0) writes its fp32 sums of dV and of dK-hat / scale
+  // to the slot ([2][256 keys][128 dims]) and a zero gain partial; the merge
+  // adds the pieces and finishes.
+  const int slot = __builtin_amdgcn_readfirstlane(items[2 * blockIdx.x + 1].y);
+  float* pk = reinterpret_cast<float*>(ws + L.pkv) + size_t(slot < 0 ? 0 : slot) * 2 * kBwdKeysPerItem * D;
   float gp[8][4];
 #pragma unroll
   for (int db = 0; db < 8; ++db)
@@ -621,6 +626,15 @@ bwd_dkdv_kernel(BwdParams p, BwdLayout L, const int4* __restrict__ items, const 
   __syncthreads();
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
+    if (slot >= 0) {
+      const int kl = 32 * wave + 16 * j + r16;
+#pragma unroll
+      for (int db = 0; db < 8; ++db) {
+        *reinterpret_cast<f32x4*>(pk + size_t(kl) * D + 16 * db + 4 * g) = accv[j][db];
+        *reinterpret_cast<f32x4*>(pk + size_t(kBwdKeysPerItem + kl) * D + 16 * db + 4 * g) = acck[j][db];
+      }
+      continue;
+    }
     const int key = key0 + 16 * j;
     const bool valid = key < p.tk;
     const size_t off = (size_t(valid ? key : 0) * p.hk + kvh) * D;
@@ -672,6 +686,93 @@ __global__ void __launch_bounds__(256) bwd_gain_final_kernel(const float* level,
   (side ? dk_gain : dq_gain)[d] = x;
 }
 
+// Finishes a split dk/dv item: sums its pieces' slots in piece order, writes
+// dV, applies the RMSNorm backward to dK-hat = scale * sum and writes dK and
+// the workgroup's gain partial (row n_kv_items + merge index). Thread t
+// handles dims [32 (t % 4), +32) of keys t / 4 + 64 i, i = 0..3.
+constexpr int MERGE_THREADS = 256;
+__global__ void __launch_bounds__(MERGE_THREADS) bwd_kv_merge_kernel(BwdParams p, BwdLayout L,
+                                                                     const int4* __restrict__ merges) {
+  __shared__ float gk[D];
+  __shared__ float red[64][D + 1];
+  unsigned char* ws = static_cast<unsigned char*>(p.ws);
+  const int4 m = merges[blockIdx.x];                  // key block, KV head, first slot, pieces
+  const int t = threadIdx.x, quarter = t & 3, kq = t >> 2;
+  if (t < D) gk[t] = p.k_gain[t];
+  __syncthreads();
+  float gp[32];
+#pragma unroll
+  for (int i = 0; i < 32; ++i) gp[i] = 0.0f;
+  const float* slots = reinterpret_cast<const float*>(ws + L.pkv);
+  for (int pass = 0; pass < kBwdKeysPerItem / 64; ++pass) {
+    const int kl = 64 * pass + kq;
+    const int key = m.x * kBwdKeysPerItem + kl;
+    const bool valid = key < p.tk;
+    float sv[32], sk[32];
+#pragma unroll
+    for (int i = 0; i < 32; ++i) sv[i] = sk[i] = 0.0f;
+    for (int k = 0; k < m.w; ++k) {
+      const float* s = slots + size_t(m.z + k) * 2 * kBwdKeysPerItem * D + size_t(kl) * D + 32 * quarter;
+#pragma unroll
+      for (int c = 0; c < 8; ++c) {
+        const f32x4 a = *reinterpret_cast<const f32x4*>(s + 4 * c);
+        const f32x4 b = *reinterpret_cast<const f32x4*>(s + size_t(kBwdKeysPerItem) * D + 4 * c);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          sv[4 * c + e] += a[e];
+          sk[4 * c + e] += b[e];
+        }
+      }
+    }
+    const size_t off = (size_t(valid ? key : 0) * p.hk + m.y) * D + 32 * quarter;
+    float x[32];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const bf16x8 xv = valid ? *reinterpret_cast<const bf16x8*>(static_cast<const __bf16*>(p.k) + off + 8 * c)
+                              : bf16x8{};
+#pragma unroll
+      for (int e = 0; e < 8; ++e) x[8 * c + e] = float(xv[e]);
+    }
+    float ss = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 32; ++i) ss += x[i] * x[i];
+    ss += __shfl_xor(ss, 1, 64);
+    ss += __shfl_xor(ss, 2, 64);
+    const float r = __builtin_amdgcn_rsqf(ss * (1.0f / D) + p.eps);
+    float mm = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 32; ++i) mm += x[i] * r * gk[32 * quarter + i] * (p.scale * sk[i]);
+    mm += __shfl_xor(mm, 1, 64);
+    mm += __shfl_xor(mm, 2, 64);
+    mm *= 1.0f / D;
+    if (valid) {
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        bf16x8 wv, wk;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int i = 8 * c + e;
+          const float dxh = p.scale * sk[i], u = x[i] * r;
+          wv[e] = (__bf16)sv[i];
+          wk[e] = (__bf16)((gk[32 * quarter + i] * dxh - u * mm) * r);
+          gp[i] += u * dxh;
+        }
+        *reinterpret_cast<bf16x8*>(static_cast<__bf16*>(p.dv) + off + 8 * c) = wv;
+        *reinterpret_cast<bf16x8*>(static_cast<__bf16*>(p.dk) + off + 8 * c) = wk;
+      }
+    }
+  }
+  // gain partial: sum over the 64 keys of each quarter
+#pragma unroll
+  for (int i = 0; i < 32; ++i) red[kq][32 * quarter + i] = gp[i];
+  __syncthreads();
+  if (t < D) {
+    float s = 0.0f;
+    for (int k = 0; k < 64; ++k) s += red[k][t];
+    reinterpret_cast<float*>(ws + L.pgk)[size_t(p.n_kv_items + blockIdx.x) * D + t] = s;
+  }
+}
+
 // dq = 0 over the blocks whose rows see no key (no dq item covers them): one
 // workgroup per block of `rows` tokens x `heads` heads, 16-byte stores.
 __global__ void __launch_bounds__(256) bwd_zero_rows_kernel(unsigned char* dq, const int2* __restrict__ blocks,
@@ -701,7 +802,8 @@ hipError_t launch_bwd_zero_rows(const BwdParams& p, int row_bytes, hipStream_t s
   return hipGetLastError();
 }
 
-BwdLayout bwd_workspace_layout(long long tq, long long tk, int hq, int hk, int n_dq_items, int n_kv_items) {
+BwdLayout bwd_workspace_layout(long long tq, long long tk, int hq, int hk, int n_dq_items, int n_kv_rows,
+                               int n_kv_slots) {
   auto up = [](size_t x) { return (x + 255) / 256 * 256; };
   const size_t qimg = size_t((tq + TT - 1) / TT) * size_t(hq) * IMG;
   const size_t kimg = size_t((tk + TT - 1) / TT) * size_t(hk) * IMG;
@@ -713,13 +815,15 @@ BwdLayout bwd_workspace_layout(long long tq, long long tk, int hq, int hk, int n
   L.vr = L.kh + up(kimg);
   L.pgq = L.vr + up(kimg);
   L.pgk = L.pgq + up(size_t(n_dq_items) * D * sizeof(float));
-  L.level = L.pgk + up(size_t(n_kv_items) * D * sizeof(float));
+  L.pkv = L.pgk + up(size_t(n_kv_rows) * D * sizeof(float));
+  L.level = L.pkv + up(size_t(n_kv_slots) * 2 * kBwdKeysPerItem * D * sizeof(float));
   L.total = L.level + up(size_t(2 * REDUCE_SLICES) * D * sizeof(float));
   return L;
 }
 
 hipError_t launch_bwd_bf16_d128(const BwdParams& p, hipStream_t stream) {
-  const BwdLayout L = bwd_workspace_layout(p.tq, p.tk, p.hq, p.hk, p.n_dq_items, p.n_kv_items);
+  const BwdLayout L =
+      bwd_workspace_layout(p.tq, p.tk, p.hq, p.hk, p.n_dq_items, p.n_kv_items + p.n_kv_merges, p.n_kv_slots);
   const unsigned n_tt = unsigned((p.tq + TT - 1) / TT), n_kt = unsigned((p.tk + TT - 1) / TT);
   hipLaunchKernelGGL(bwd_prep_q_kernel, dim3(n_tt * unsigned(p.hq)), dim3(PREP_THREADS), 0, stream, p, L);
   if (n_kt > 0)
@@ -731,11 +835,13 @@ hipError_t launch_bwd_bf16_d128(const BwdParams& p, hipStream_t stream) {
                        p.dq_soffs);
   if (p.n_kv_items > 0)
     hipLaunchKernelGGL(bwd_dkdv_kernel, dim3(p.n_kv_items), dim3(NTHR), 0, stream, p, L, p.kv_items, p.kv_tiles);
+  if (p.n_kv_merges > 0)
+    hipLaunchKernelGGL(bwd_kv_merge_kernel, dim3(p.n_kv_merges), dim3(MERGE_THREADS), 0, stream, p, L, p.kv_merges);
   unsigned char* ws = static_cast<unsigned char*>(p.ws);
   float* level = reinterpret_cast<float*>(ws + L.level);
   hipLaunchKernelGGL(bwd_gain_slices_kernel, dim3(2 * REDUCE_SLICES), dim3(256), 0, stream,
                      reinterpret_cast<const float*>(ws + L.pgq), p.n_dq_items,
-                     reinterpret_cast<const float*>(ws + L.pgk), p.n_kv_items, level);
+                     reinterpret_cast<const float*>(ws + L.pgk), p.n_kv_items + p.n_kv_merges, level);
   hipLaunchKernelGGL(bwd_gain_final_kernel, dim3(1), dim3(256), 0, stream, level, p.dq_gain, p.dk_gain);
   return hipGetLastError();
 }

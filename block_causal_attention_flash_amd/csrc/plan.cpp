@@ -511,18 +511,44 @@ magi_status_t build_bwd_plan(const magi_attn_layout_t* L, const magi_attn_text_t
     }
 
   // Items (key block, KV head), longest first, KV head -> XCD as for the
-  // forward's items.
-  struct Cand { int64_t cost; int32_t kb, kvh; };
+  // forward's items. With too few of them to fill the GPU (bf16: a short
+  // text stream, a small video), each list is cut into pieces that write
+  // fp32 partial sums to slots, summed in piece order afterwards.
+  const int hk = L->n_kv_heads;
+  struct Cand { int64_t cost; int32_t kb, kvh, begin, end, full, slot; };
   std::vector<Cand> cands;
-  for (int kvh = 0; kvh < L->n_kv_heads; ++kvh)
-    for (int64_t kb = 0; kb < n_kb; ++kb)
-      if (kb_n[kb] > 0) cands.push_back(Cand{int64_t(kb_n[kb]) * group, int32_t(kb), kvh});
+  int64_t n_whole = 0, total = 0;
+  for (int64_t kb = 0; kb < n_kb; ++kb)
+    if (kb_n[kb] > 0) n_whole += hk, total += int64_t(kb_n[kb]) * hk;
+  const bool split = L->dtype == MAGI_DTYPE_BF16 && n_whole > 0 && n_whole < kBwdSplitBelowItems;
+  const int64_t piece =
+      std::max<int64_t>(kBwdMinPieceEntries, (total + kBwdSplitTargetItems - 1) / kBwdSplitTargetItems);
+  B.kv_merges.clear();
+  B.n_kv_slots = 0;
+  for (int kvh = 0; kvh < hk; ++kvh)
+    for (int64_t kb = 0; kb < n_kb; ++kb) {
+      const int32_t n = kb_n[kb], b0 = kb_begin[kb];
+      if (n == 0) continue;
+      const int n_pieces =
+          split ? int(std::max<int64_t>(1, std::min<int64_t>(kBwdMaxPieces, (n + piece - 1) / piece))) : 1;
+      if (n_pieces == 1) {
+        cands.push_back(Cand{int64_t(n) * group, int32_t(kb), kvh, b0, b0 + n, kb_full[kb], -1});
+        continue;
+      }
+      B.kv_merges.push_back(KeyMerge{int32_t(kb), kvh, B.n_kv_slots, n_pieces});
+      for (int k = 0; k < n_pieces; ++k) {
+        const int32_t pb = b0 + int32_t(int64_t(n) * k / n_pieces), pe = b0 + int32_t(int64_t(n) * (k + 1) / n_pieces);
+        const int32_t full = std::max(0, std::min(pe - pb, kb_full[kb] - (pb - b0)));
+        cands.push_back(Cand{int64_t(pe - pb) * group, int32_t(kb), kvh, pb, pe, full, B.n_kv_slots + k});
+      }
+      B.n_kv_slots += n_pieces;
+    }
   std::stable_sort(cands.begin(), cands.end(), [](const Cand& a, const Cand& b) {
     if (a.cost != b.cost) return a.cost > b.cost;
     if (a.kvh != b.kvh) return a.kvh < b.kvh;
-    return a.kb < b.kb;
+    if (a.kb != b.kb) return a.kb < b.kb;
+    return a.begin < b.begin;
   });
-  const int hk = L->n_kv_heads;
   std::vector<std::vector<KeyItem>> queues(kNumXcd);
   std::vector<int64_t> load(kNumXcd, 0);
   const bool by_head = hk % kNumXcd == 0 || kNumXcd % hk == 0;
@@ -537,7 +563,7 @@ magi_status_t build_bwd_plan(const magi_attn_layout_t* L, const magi_attn_text_t
     } else {
       best = int(std::min_element(load.begin(), load.end()) - load.begin());
     }
-    queues[best].push_back(KeyItem{c.kb, c.kvh, kb_begin[c.kb], kb_begin[c.kb] + kb_n[c.kb], kb_full[c.kb], {0, 0, 0}});
+    queues[best].push_back(KeyItem{c.kb, c.kvh, c.begin, c.end, c.full, c.slot, {0, 0}});
     load[best] += c.cost;
   }
   size_t maxlen = 0;
@@ -545,7 +571,7 @@ magi_status_t build_bwd_plan(const magi_attn_layout_t* L, const magi_attn_text_t
   B.items.clear();
   for (size_t j = 0; j < maxlen; ++j)
     for (int x = 0; x < kNumXcd; ++x)
-      B.items.push_back(j < queues[x].size() ? queues[x][j] : KeyItem{0, 0, 0, 0, 0, {0, 0, 0}});
+      B.items.push_back(j < queues[x].size() ? queues[x][j] : KeyItem{0, 0, 0, 0, 0, -1, {0, 0}});
   while (!B.items.empty() && B.items.back().tile_begin == B.items.back().tile_end) B.items.pop_back();
   return MAGI_OK;
 }

@@ -57,6 +57,15 @@ constexpr int kSplitBelowItems = 2 * kNumCu;
 constexpr int kSplitTargetItems = 4 * kNumCu;
 constexpr int kMaxPieces = 8;
 constexpr int kMinPieceTiles = 64;
+// The backward's dk/dv items (bf16) split the same way when there are
+// fewer (key block, KV head) items than CUs (a short text stream): each
+// token-tile list is cut into up to kBwdMaxPieces pieces of at least
+// kBwdMinPieceEntries entries, about total / kBwdSplitTargetItems each.
+// (With 384 items, video 256x2, the split was 9% slower than none.)
+constexpr int kBwdSplitBelowItems = kNumCu;
+constexpr int kBwdSplitTargetItems = 4 * kNumCu;
+constexpr int kBwdMaxPieces = 64;
+constexpr int kBwdMinPieceEntries = 8;
 
 constexpr int kTilePad = 16;
 constexpr uint32_t kNoTileOffset = 0x80000000u;   // past any tile image buffer (< 2 GiB): reads give zeros
@@ -111,7 +120,13 @@ struct KeyItem {
   int32_t tile_begin;
   int32_t tile_end;    // == tile_begin: padding item
   int32_t n_full;
-  int32_t pad[3];
+  int32_t slot;        // -1: the whole list; else a piece, writing partial sums to this slot
+  int32_t pad[2];
+};
+
+// A split (key block, KV head): pieces slot0 .. slot0 + n_pieces - 1.
+struct KeyMerge {
+  int32_t kb, kvh, slot0, n_pieces;
 };
 
 // Token ranges of the queries that see one key: its own video's [lo, hi),
@@ -130,6 +145,8 @@ struct BwdHostPlan {
   std::vector<KeyItem> items;        // launch order (XCD-interleaved, padded)
   std::vector<int32_t> dq_zero;      // (t0, first head) of the dq blocks whose rows see no key: dq = 0 there
   std::vector<int32_t> kv_zero;      // (first key, 0) of the key blocks no query sees: dk = dv = 0 there
+  std::vector<KeyMerge> kv_merges;   // split (key block, KV head) items, summed after the dk/dv kernel
+  int32_t n_kv_slots = 0;            // partial slots of their pieces
 };
 
 // Whether video s is a last global block (its queries see every key).

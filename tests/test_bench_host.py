@@ -74,6 +74,14 @@ def test_more_than_one_gpu_is_refused(monkeypatch, capsys):
     assert "one GPU" in capsys.readouterr().err
 
 
+def test_parallel_backward_is_refused(monkeypatch, capsys):
+    monkeypatch.setattr("sys.argv", ["bench.py", "--backward", "--attention", "parallel"])
+    with pytest.raises(SystemExit) as e:
+        bench.main()
+    assert e.value.code == 2
+    assert "self or cross" in capsys.readouterr().err
+
+
 def test_useful_text_pairs_match_oracle():
     from workloads import text_layout
     for c in CONFIGS:
