@@ -275,7 +275,7 @@ def main():
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (the kernel runs on one GPU's "
-              "share; see DESIGN.md for how the path would shard)", file=sys.stderr)
+              "share of the work)", file=sys.stderr)
         sys.exit(2)
 
     if args.backward:

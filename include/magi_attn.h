@@ -62,7 +62,7 @@ extern "C" {
 typedef enum magi_status {
   MAGI_OK = 0,
   MAGI_ERR_INVALID_ARG = 1,   /* bad layout, NULL or misaligned pointer, bad size */
-  MAGI_ERR_UNSUPPORTED = 2,   /* valid request this build does not implement      */
+  MAGI_ERR_UNSUPPORTED = 2,   /* valid request the library does not implement    */
   MAGI_ERR_NO_MEMORY = 3,     /* host or device allocation failed                 */
   MAGI_ERR_HIP = 4            /* a HIP runtime call or kernel launch failed       */
 } magi_status_t;
