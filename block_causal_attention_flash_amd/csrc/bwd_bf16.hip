@@ -16,7 +16,8 @@
 //
 // Kernels, in stream order:
 //   prep_q  per (32-token tile, query head): the tile images of q_hat and of
-//           dO, and the row statistics (lse log2 e, D);
+//           dO, and the row statistics negated (-lse log2 e, -D: the
+//           starting values of the S and dP accumulators);
 //   prep_k  per (32-key tile, KV head): the images of k' and of V;
 //   dq      query-stationary (the forward's order): 8 waves x 32 rows, per
 //           key tile S^T and dP^T on the matrix cores, dS on the vector ALUs,
@@ -195,8 +196,8 @@ __global__ void __launch_bounds__(PREP_THREADS) bwd_prep_q_kernel(BwdParams p, B
   }
   if (part == 0) {
     float* rs = reinterpret_cast<float*>(ws + L.rs) + size_t(b) * 64;
-    rs[j] = valid ? p.lse[size_t(h) * p.tq + tok] * kLog2e : 0.0f;
-    rs[32 + j] = valid ? dsum : 0.0f;
+    rs[j] = valid ? -p.lse[size_t(h) * p.tq + tok] * kLog2e : 0.0f;
+    rs[32 + j] = valid ? -dsum : 0.0f;
   }
 }
 
@@ -338,14 +339,14 @@ bwd_dq_kernel(BwdParams p, BwdLayout L, const int4* __restrict__ items, const in
         dov[rb][ks] = live ? *reinterpret_cast<const bf16x8*>(ws + L.dos + base + 2048 * ks + 256 * rb) : bf16x8{};
       }
   }
-  float lse2[2], dvv[2];
+  float nl2[2], nd[2];                               // -lse log2 e and -D of the lane's rows
   int lo[2], hi[2];
   {
     const float* rs = reinterpret_cast<const float*>(ws + L.rs) + size_t(live ? img : 0) * 64;
 #pragma unroll
     for (int rb = 0; rb < 2; ++rb) {
-      lse2[rb] = live ? rs[16 * rb + r16] : 0.0f;
-      dvv[rb] = live ? rs[32 + 16 * rb + r16] : 0.0f;
+      nl2[rb] = live ? rs[16 * rb + r16] : 0.0f;
+      nd[rb] = live ? rs[32 + 16 * rb + r16] : 0.0f;
       const int tok = tok0 + 16 * rb + r16;
       const int2 bnd = tok < p.tq ? p.rows[tok] : int2{0, 0};
       lo[rb] = bnd.x;
@@ -384,9 +385,15 @@ bwd_dq_kernel(BwdParams p, BwdLayout L, const int4* __restrict__ items, const in
       issue(i + 5);
     }
     const unsigned st = unsigned(i % RING) * IMG;
+    // The S^T and dP^T chains start from -lse log2 e and -D (the lane's row
+    // is the same for its four elements), so they end as S - lse log2 e and
+    // dP - D.
     f32x4 s[2][2], dp[2][2];
 #pragma unroll
-    for (int rb = 0; rb < 2; ++rb) s[rb][0] = s[rb][1] = dp[rb][0] = dp[rb][1] = f32x4{};
+    for (int rb = 0; rb < 2; ++rb) {
+      s[rb][0] = s[rb][1] = f32x4{nl2[rb], nl2[rb], nl2[rb], nl2[rb]};
+      dp[rb][0] = dp[rb][1] = f32x4{nd[rb], nd[rb], nd[rb], nd[rb]};
+    }
 #pragma unroll
     for (int f = 0; f < 8; ++f) {
       const int ks = f >> 1, kb = f & 1;
@@ -411,12 +418,12 @@ bwd_dq_kernel(BwdParams p, BwdLayout L, const int4* __restrict__ items, const in
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          float pv = __builtin_amdgcn_exp2f(s[rb][kb][e] - lse2[rb]);
+          float pv = __builtin_amdgcn_exp2f(s[rb][kb][e]);
           if (masked) {
             const unsigned rel = unsigned(kt * TT + 16 * kb + 4 * g + e - lo[rb]);
             if (rel >= unsigned(hi[rb] - lo[rb])) pv = 0.0f;
           }
-          ds[rb][4 * kb + e] = (__bf16)(pv * (dp[rb][kb][e] - dvv[rb]));
+          ds[rb][4 * kb + e] = (__bf16)(pv * dp[rb][kb][e]);
         }
 #pragma unroll
     for (int db = 0; db < 8; ++db) {
@@ -455,7 +462,7 @@ bwd_dq_kernel(BwdParams p, BwdLayout L, const int4* __restrict__ items, const in
 struct KvLds {
   unsigned char qs[RING][IMG];
   unsigned char dos[RING][IMG];
-  float rs[RING][8][64];  // per stage and wave: lse log2 e [32], D [32] of the step's rows
+  float rs[RING][8][64];  // per stage and wave: -lse log2 e [32], -D [32] of the step's rows
   float gk[D];
   float red[8][D];
 };
@@ -544,10 +551,11 @@ bwd_dkdv_kernel(BwdParams p, BwdLayout L, const int4* __restrict__ items, const 
     const unsigned rsa = rs0 + unsigned(s % RING) * 8 * 256;
     const bool masked = ce >= n_full;
     const int tt = codes[ce] >> 1;
-    // S (lane: key r16 of half j, rows 16 rb + 4 g + e of the step's token tile)
+    // S (lane: key r16 of half j, rows 16 rb + 4 g + e of the step's token
+    // tile), started from the rows' -lse log2 e so that it ends as S - lse log2 e
     f32x4 sc[2][2];
 #pragma unroll
-    for (int j = 0; j < 2; ++j) sc[j][0] = sc[j][1] = f32x4{};
+    for (int rb = 0; rb < 2; ++rb) sc[0][rb] = sc[1][rb] = *(lds_f32x4*)(size_t)(rsa + 4 * (16 * rb + 4 * g));
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
@@ -560,12 +568,11 @@ bwd_dkdv_kernel(BwdParams p, BwdLayout L, const int4* __restrict__ items, const 
     bf16x8 pb[2];
 #pragma unroll
     for (int rb = 0; rb < 2; ++rb) {
-      const f32x4 l2 = *(lds_f32x4*)(size_t)(rsa + 4 * (16 * rb + 4 * g));
 #pragma unroll
       for (int j = 0; j < 2; ++j)
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          float pv = __builtin_amdgcn_exp2f(sc[j][rb][e] - l2[e]);
+          float pv = __builtin_amdgcn_exp2f(sc[j][rb][e]);
           if (masked) {
             const int tok = tt * TT + 16 * rb + 4 * g + e;
             if (unsigned(tok - kbnd[j].x) >= unsigned(kbnd[j].y - kbnd[j].x) &&
@@ -582,9 +589,9 @@ bwd_dkdv_kernel(BwdParams p, BwdLayout L, const int4* __restrict__ items, const 
       accv[0][db] = mfma(a, pb[0], accv[0][db]);
       accv[1][db] = mfma(a, pb[1], accv[1][db]);
     }
-    f32x4 dp[2][2];
+    f32x4 dp[2][2];                                   // started from -D: ends as dP - D
 #pragma unroll
-    for (int j = 0; j < 2; ++j) dp[j][0] = dp[j][1] = f32x4{};
+    for (int rb = 0; rb < 2; ++rb) dp[0][rb] = dp[1][rb] = *(lds_f32x4*)(size_t)(rsa + 128 + 4 * (16 * rb + 4 * g));
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
@@ -595,13 +602,11 @@ bwd_dkdv_kernel(BwdParams p, BwdLayout L, const int4* __restrict__ items, const 
       }
     bf16x8 dsb[2];
 #pragma unroll
-    for (int rb = 0; rb < 2; ++rb) {
-      const f32x4 dd = *(lds_f32x4*)(size_t)(rsa + 128 + 4 * (16 * rb + 4 * g));
+    for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
       for (int j = 0; j < 2; ++j)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) dsb[j][4 * rb + e] = (__bf16)(pf[j][rb][e] * (dp[j][rb][e] - dd[e]));
-    }
+        for (int e = 0; e < 4; ++e) dsb[j][4 * rb + e] = (__bf16)(pf[j][rb][e] * dp[j][rb][e]);
 #pragma unroll
     for (int db = 0; db < 8; ++db) {
       const bf16x8 a = tr_frag(qs0 + st + trq, db);
