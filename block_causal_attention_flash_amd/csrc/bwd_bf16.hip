@@ -411,20 +411,26 @@ bwd_dq_kernel(BwdParams p, BwdLayout L, const int4* __restrict__ items, const in
     // lane: row r16 of block rb, keys 16 kb + 4 g + i of the tile
     const bool masked = i >= n_full;
     const int kt = masked ? (codes[i] >> 1) : 0;
+    if (masked) {                                     // keys outside the row's range: S = -inf, P = 0
+      asm volatile("" ::: "memory");                  // a branch, not selects on every step
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb) {
+        const unsigned base = unsigned(kt * TT + 4 * g - lo[rb]), len = unsigned(hi[rb] - lo[rb]);
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            s[rb][kb][e] = base + unsigned(16 * kb + e) < len ? s[rb][kb][e] : -__builtin_inff();
+      }
+    }
     bf16x8 ds[2];
 #pragma unroll
     for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          float pv = __builtin_amdgcn_exp2f(s[rb][kb][e]);
-          if (masked) {
-            const unsigned rel = unsigned(kt * TT + 16 * kb + 4 * g + e - lo[rb]);
-            if (rel >= unsigned(hi[rb] - lo[rb])) pv = 0.0f;
-          }
-          ds[rb][4 * kb + e] = (__bf16)(pv * dp[rb][kb][e]);
-        }
+        for (int e = 0; e < 4; ++e)
+          ds[rb][4 * kb + e] = (__bf16)(__builtin_amdgcn_exp2f(s[rb][kb][e]) * dp[rb][kb][e]);
 #pragma unroll
     for (int db = 0; db < 8; ++db) {
       const bf16x8 a = tr_frag(kh0 + st + trq, db);
@@ -564,25 +570,32 @@ bwd_dkdv_kernel(BwdParams p, BwdLayout L, const int4* __restrict__ items, const 
         sc[0][rb] = mfma(a, ku[0][ks], sc[0][rb]);
         sc[1][rb] = mfma(a, ku[1][ks], sc[1][rb]);
       }
+    if (masked) {                                     // rows that do not see the key: S = -inf, P = 0
+      asm volatile("" ::: "memory");                  // a branch, not selects on every step
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int tok = tt * TT + 16 * rb + 4 * g + e;
+            if (unsigned(tok - kbnd[j].x) >= unsigned(kbnd[j].y - kbnd[j].x) &&
+                unsigned(tok - kbnd[j].z) >= unsigned(kbnd[j].w - kbnd[j].z))
+              sc[j][rb][e] = -__builtin_inff();
+          }
+    }
     f32x4 pf[2][2];
     bf16x8 pb[2];
 #pragma unroll
-    for (int rb = 0; rb < 2; ++rb) {
+    for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
       for (int j = 0; j < 2; ++j)
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          float pv = __builtin_amdgcn_exp2f(sc[j][rb][e]);
-          if (masked) {
-            const int tok = tt * TT + 16 * rb + 4 * g + e;
-            if (unsigned(tok - kbnd[j].x) >= unsigned(kbnd[j].y - kbnd[j].x) &&
-                unsigned(tok - kbnd[j].z) >= unsigned(kbnd[j].w - kbnd[j].z))
-              pv = 0.0f;
-          }
+          const float pv = __builtin_amdgcn_exp2f(sc[j][rb][e]);
           pf[j][rb][e] = pv;
           pb[j][4 * rb + e] = (__bf16)pv;
         }
-    }
 #pragma unroll
     for (int db = 0; db < 8; ++db) {
       const bf16x8 a = tr_frag(do0 + st + trq, db);
