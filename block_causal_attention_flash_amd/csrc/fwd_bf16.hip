@@ -31,11 +31,16 @@
 // g_q * g_k * scale * log2 e) and held in registers as bf16 MFMA operands.
 //
 // Softmax. QK-normalisation bounds every logit: |s_ij| <= |q'_i| |k_hat_j|
-// <= |q'_i| sqrt(d). When that bound is at most 40 (log2 units) for every row
-// of a wave, the wave uses exp2(s) directly, with no running maximum and no
+// <= d max_c |g_q,c g_k,c| scale log2 e (the normalised rows have at most
+// norm sqrt(d)). When that bound of the item's gains is at most 40 (log2
+// units), the item uses exp2(s) directly, with no running maximum and no
 // rescaling: softmax is invariant to the shift and 2^+-40 lies far inside the
-// fp32/bf16 range. Otherwise the wave keeps a running row maximum and rescales
-// its accumulator only when the maximum has grown by more than 2^8.
+// fp32/bf16 range. Otherwise it keeps a running row maximum and rescales its
+// accumulator only when the maximum has grown by more than 2^8. The two cases
+// are two instances of the kernel, both launched: each workgroup takes the
+// gains of its phase, and the instance that does not match exits at once.
+// (One kernel holding both loops paid for the online loop's registers with
+// spills in the static one, 2.5% of its time.)
 //
 // The same kernel runs the block's text cross-attention (paperlayer §2.2.2,
 // §2.2.3; paper-notes §3.2.2, §3.2.6): only the key stream and the per-row key
@@ -437,6 +442,7 @@ __device__ __forceinline__ void run_tiles(const LoopCtx& c, const LaneOffsets& l
   pv_tile((n + NSTAGE - 1) % NSTAGE, lo, st.p, st);
 }
 
+template <bool STATIC>
 __global__ void __launch_bounds__(NTHR) __attribute__((amdgpu_waves_per_eu(2, 2)))
 fwd_bf16_d128_kernel(FwdParams prm, const int4* __restrict__ items, const int* __restrict__ tiles,
                      const unsigned* __restrict__ soffs, const int2* __restrict__ rows) {
@@ -451,6 +457,21 @@ fwd_bf16_d128_kernel(FwdParams prm, const int4* __restrict__ items, const int* _
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
   const int g = lane >> 4;
+
+  // ---- static or online softmax, from the gains of the item's phase (every
+  // wave reduces all D of them; the result is uniform over the grid's phase)
+  {
+    const float* gq = px ? prm.q_gain_x : prm.q_gain;
+    const float* gk = px ? prm.k_gain_x : prm.k_gain;
+    float gm = 0.0f;
+#pragma unroll
+    for (int c = lane; c < D; c += 64) gm = fmaxf(gm, __builtin_fabsf(gq[c] * gk[c]));
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) gm = fmaxf(gm, __shfl_xor(gm, o, 64));
+    const float bound = float(D) * gm * __builtin_fabsf((px ? prm.scale_x : prm.scale) * kLog2e) * 1.02f;
+    const bool stat = bound <= kStaticBound;          // false for NaN gains
+    if (stat != STATIC) return;
+  }
   const int kvh = item.y >> 16, h0 = item.y & 0xffff;
   const int tb = item.z, n_tiles = item.w - item.z;
 
@@ -503,7 +524,6 @@ fwd_bf16_d128_kernel(FwdParams prm, const int4* __restrict__ items, const int* _
   prefetch_k(0, lo, st);
 
   // ---- query prologue: RMS-normalise, fold gains/temperature, to bf16
-  float bound_max = 0.0f;
 #pragma unroll
   for (int rb = 0; rb < NRB; ++rb) {
     float ss = 0.0f;
@@ -511,7 +531,6 @@ fwd_bf16_d128_kernel(FwdParams prm, const int4* __restrict__ items, const int* _
     for (int ks = 0; ks < 4; ++ks) ss = sumsq8(qr[rb][ks], ss);
     ss = sum_groups(ss);
     const float rq = valid[rb] ? __builtin_amdgcn_rsqf(ss * (1.0f / D) + prm.eps) : 0.0f;
-    float nq = 0.0f;
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
       const int d0 = ks * 32 + g * 8;
@@ -519,10 +538,7 @@ fwd_bf16_d128_kernel(FwdParams prm, const int4* __restrict__ items, const int* _
       const f32x4 g1 = *LDS_PTR(const f32x4, &sm.gqk[d0 + 4]);
 #pragma unroll
       for (int j = 0; j < 8; ++j) st.qf[rb][ks][j] = (__bf16)(float(qr[rb][ks][j]) * rq * (j < 4 ? g0[j] : g1[j - 4]));
-      nq = sumsq8(st.qf[rb][ks], nq);
     }
-    nq = sum_groups(nq);
-    bound_max = fmaxf(bound_max, __builtin_sqrtf(nq) * __builtin_sqrtf(float(D)) * 1.02f);
     const int2 b = valid[rb] ? rows[(px ? prm.tq : 0) + tok[rb]] : int2{0, 0};
     st.lo[rb] = b.x;
     st.hi[rb] = b.y;
@@ -532,10 +548,7 @@ fwd_bf16_d128_kernel(FwdParams prm, const int4* __restrict__ items, const int* _
     st.lsum[rb] = 0.0f;
     st.m[rb] = kNegInf;
   }
-  const bool stat = __builtin_amdgcn_ballot_w64(!(bound_max <= kStaticBound)) == 0;
-
-  if (stat) run_tiles<true>(ctx, lo, n_full, st, lane);
-  else run_tiles<false>(ctx, lo, n_full, st, lane);
+  run_tiles<STATIC>(ctx, lo, n_full, st, lane);
 
   // ---- epilogue: lane l holds dims 16 db + 4 g + i of row (l & 15) per block
   // (row coordinates recomputed rather than kept live through the loop)
@@ -555,7 +568,7 @@ fwd_bf16_d128_kernel(FwdParams prm, const int4* __restrict__ items, const int* _
       const size_t r = size_t(slot) * ROWS + size_t((wave * NRB + rb) * 16 + (lane & 15));
 #pragma unroll
       for (int db = 0; db < 8; ++db) *reinterpret_cast<f32x4*>(prm.part_o + r * D + db * 16 + g * 4) = st.o[rb][db];
-      if (g == 0) *reinterpret_cast<float2*>(prm.part_ml + r * 2) = float2{stat ? 0.0f : st.m[rb], lsum};
+      if (g == 0) *reinterpret_cast<float2*>(prm.part_ml + r * 2) = float2{STATIC ? 0.0f : st.m[rb], lsum};
     }
     return;
   }
@@ -577,7 +590,7 @@ fwd_bf16_d128_kernel(FwdParams prm, const int4* __restrict__ items, const int* _
       }
       if (g == 0) {
         const float l2 = __builtin_amdgcn_logf(lsum);   // log2
-        const float lse = !any ? kNegInf : stat ? l2 * kLn2 : (st.m[rb] + l2) * kLn2;
+        const float lse = !any ? kNegInf : STATIC ? l2 * kLn2 : (st.m[rb] + l2) * kLn2;
         lbase[size_t(head[rb]) * prm.tq + tok[rb]] = lse;
       }
     }
@@ -716,8 +729,11 @@ hipError_t launch_fwd_bf16_d128(const FwdParams& prm, int n_items, int n_merges,
       const hipError_t e = hipGetLastError();
       if (e != hipSuccess) return e;
     }
-    hipLaunchKernelGGL(fwd_bf16_d128_kernel, dim3(n_items), dim3(NTHR), 0, stream, p, p.items, p.tiles, p.soffs,
-                       p.rows);
+    // Both instances: each workgroup runs in the one that matches its gains.
+    hipLaunchKernelGGL(fwd_bf16_d128_kernel<true>, dim3(n_items), dim3(NTHR), 0, stream, p, p.items, p.tiles,
+                       p.soffs, p.rows);
+    hipLaunchKernelGGL(fwd_bf16_d128_kernel<false>, dim3(n_items), dim3(NTHR), 0, stream, p, p.items, p.tiles,
+                       p.soffs, p.rows);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

@@ -225,6 +225,28 @@ def test_parallel_with_split_self_attention():
     compare(out_x, lse_x, *ref_cross(lay, text, tx, 0.088), "bf16", tol_cross(tx, 0.088))
 
 
+@pytest.mark.parametrize("online", ["cross", "self"])
+def test_parallel_with_one_phase_on_the_online_softmax(online):
+    """One phase's gains make the logit bound of its items large (a gain of 40
+    on channel 0 of q and k, with that channel of k zero so the logits do not
+    change): its workgroups run the online-softmax instance of the kernel,
+    the other phase's the static one, in the same parallel launch."""
+    lay, text = CASES["mixed"]
+    inp, tx = inputs(lay, text, 6, 2, 128, "bf16", seed=13, distinct_qx=True)
+    if online == "cross":
+        tx["q_gain_x"][0] = 40.0
+        tx["k_gain_x"][0] = 40.0
+        tx["k_x"][:, :, 0] = 0.0
+    else:
+        inp["q_gain"][0] = 40.0
+        inp["k_gain"][0] = 40.0
+        inp["k"][:, :, 0] = 0.0
+    out, lse, out_x, lse_x = run_parallel(lay, text, inp, tx, 6, 2, 128, "bf16", 0.088, 0.07)
+    compare(out, lse, *oracle.attention(inp["q"], inp["k"], inp["v"], inp["q_gain"], inp["k_gain"], 1e-6, 0.088,
+                                        lay), "bf16")
+    compare(out_x, lse_x, *ref_cross(lay, text, tx, 0.07), "bf16", tol_cross(tx, 0.07))
+
+
 @pytest.mark.parametrize("dtype,d", [("bf16", 128), ("fp32", 128)])
 def test_cross_without_any_text(dtype, d):
     """No chunk has text: nothing but zero rows, out = 0 and lse = -inf
