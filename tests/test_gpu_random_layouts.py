@@ -1,0 +1,163 @@
+"""Seeded random layouts through the whole path (C ABI): the forward and the
+backward of a training plan against the fp64 oracle, and, for a random text,
+the cross-attention's forward and backward.
+
+Each layout mixes what the fixed cases test one at a time: packed videos of
+one to three chunks, ragged chunk lengths off the tile grids, leading cached
+chunks without queries (a KV cache), a KV-range window, a last global block,
+and several GQA ratios. Tolerances are those of the fixed cases: forward bf16
+max-abs 2e-2, relative L2 5e-3 and LSE 1e-2 (the cross LSE: the per-row bound
+of its own tests); backward relative L2 1e-2 per gradient.
+"""
+import math
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from workloads import Layout, TextLayout, make_inputs, make_text_inputs
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+SEEDS = list(range(30))
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu(built_lib):
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import block_causal_attention_flash_amd  # noqa: F401
+    return built_lib
+
+
+def log(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def random_case(seed):
+    """A layout, a text for it and a head configuration from default_rng(seed)."""
+    rng = np.random.default_rng(1000 + seed)
+    q_off, kv_off, seq = [0], [0], [0]
+    for _ in range(int(rng.integers(1, 4))):
+        n_ch = int(rng.integers(1, 5))
+        n_cached = int(rng.integers(0, n_ch))           # leading chunks without queries
+        for c in range(n_ch):
+            kv_off.append(kv_off[-1] + int(rng.integers(1, 170)))
+            q_off.append(q_off[-1] + (0 if c < n_cached else int(rng.integers(1, 170))))
+        seq.append(seq[-1] + n_ch)
+    lay = Layout(tuple(q_off), tuple(kv_off), tuple(seq), kv_range=int(rng.choice([0, 0, 1, 2, 3])),
+                 last_global=int(rng.integers(0, 2)))
+    # text: per video, leading clean chunks without text, then prompts of
+    # that video, each shared by a run of adjacent chunks (one run of rows
+    # per prompt, as chunk-wise prompts give)
+    lengths = [int(x) for x in rng.integers(1, 90, 2 * (len(seq) - 1))]
+    starts = np.concatenate([[0], np.cumsum(lengths)])
+    begin, end = [], []
+    for v in range(len(seq) - 1):
+        n_clean = int(rng.integers(0, 2))
+        cur = 2 * v
+        for c in range(seq[v], seq[v + 1]):
+            if c - seq[v] < n_clean:
+                begin.append(0)
+                end.append(0)
+                continue
+            if c - seq[v] > n_clean and cur == 2 * v and rng.random() < 0.4:
+                cur += 1
+            begin.append(int(starts[cur]))
+            end.append(int(starts[cur + 1]))
+    text = TextLayout(tuple(begin), tuple(end), int(starts[-1]))
+    hq, hk = [(2, 1), (4, 2), (6, 2), (3, 3), (8, 1)][seed % 5]
+    return lay, text, hq, hk
+
+
+def rel_l2(got, ref):
+    n = np.linalg.norm(ref)
+    return float(np.linalg.norm(got - ref) / n) if n > 0 else float(np.linalg.norm(got))
+
+
+def describe(lay, text, hq, hk):
+    return (f"q_offsets={lay.q_offsets} kv_offsets={lay.kv_offsets} seq_chunks={lay.seq_chunks} "
+            f"kv_range={lay.kv_range} last_global={lay.last_global} text={text.begin}/{text.end}/{text.t_text} "
+            f"heads={hq}/{hk}")
+
+
+@pytest.mark.parametrize("seed", SEEDS)
+def test_random_layout_self_attention(seed):
+    from block_causal_attention_flash_amd import TrainPlan
+    lay, text, hq, hk = random_case(seed)
+    log(f"random self {seed}: {describe(lay, text, hq, hk)}")
+    sc = 1 / math.sqrt(128)
+    inp = make_inputs(lay, hq, hk, 128, "bf16", "uniform", seed)
+    dout = torch.from_numpy(np.random.default_rng(seed + 7).standard_normal((lay.t_q, hq, 128))
+                            .astype(np.float32)).to(torch.bfloat16)
+    g = {n: t.to(DEV) for n, t in inp.items()}
+    plan = TrainPlan.from_layout(lay, hq, hk, 128, "bf16")
+    out, lse = plan(g["q"], g["k"], g["v"], g["q_gain"], g["k_gain"], 1e-6, sc)
+    dq, dk, dv = (torch.full_like(g[n], float("nan")) for n in ("q", "k", "v"))
+    grads = plan.backward(g["q"], g["k"], g["v"], out, lse, dout.to(DEV), g["q_gain"], g["k_gain"], 1e-6, sc,
+                          dq=dq, dk=dk, dv=dv)
+    torch.cuda.synchronize()
+    got_out, got_lse = out.double().cpu().numpy(), lse.double().cpu().numpy()
+    got = [t.double().cpu().numpy() for t in grads]
+    plan.close()
+    ref_out, ref_lse = oracle.attention(inp["q"], inp["k"], inp["v"], inp["q_gain"], inp["k_gain"], 1e-6, sc, lay)
+    d = got_out - ref_out
+    assert np.all(np.isfinite(got_out)) and np.all(np.isfinite(got_lse))
+    assert np.max(np.abs(d)) <= 2e-2 and rel_l2(got_out, ref_out) <= 5e-3
+    assert np.max(np.abs(got_lse - ref_lse)) <= 1e-2
+    ref = oracle.attention_backward(inp["q"], inp["k"], inp["v"], inp["q_gain"], inp["k_gain"], 1e-6, sc, lay,
+                                    dout)
+    errs = [rel_l2(a, b) for a, b in zip(got, ref)]
+    for a in got:
+        assert np.all(np.isfinite(a))
+    assert max(errs) <= 1e-2, dict(zip(("dq", "dk", "dv", "dq_gain", "dk_gain"), errs))
+    unseen = np.all(ref[2] == 0, axis=(1, 2))
+    assert np.all(got[1][unseen] == 0) and np.all(got[2][unseen] == 0)
+
+
+@pytest.mark.parametrize("seed", SEEDS)
+def test_random_layout_cross_attention(seed):
+    from block_causal_attention_flash_amd import CrossTrainPlan
+    lay, text, hq, hk = random_case(seed)
+    log(f"random cross {seed}: {describe(lay, text, hq, hk)}")
+    sc = 0.8 / math.sqrt(128)
+    q = make_inputs(lay, hq, hk, 128, "bf16", "uniform", seed)["q"]
+    tx = make_text_inputs(text, hk, 128, "bf16", "uniform", seed + 1)
+    dout = torch.from_numpy(np.random.default_rng(seed + 9).standard_normal((lay.t_q, hq, 128))
+                            .astype(np.float32)).to(torch.bfloat16)
+    g = {n: t.to(DEV) for n, t in tx.items()}
+    plan = CrossTrainPlan.from_layout(lay, text, hq, hk, 128, "bf16")
+    out, lse = plan(q.to(DEV), g["k_x"], g["v_x"], g["q_gain_x"], g["k_gain_x"], 1e-6, sc)
+    dq = torch.full_like(q.to(DEV), float("nan"))
+    dk, dv = (torch.full_like(g[n], float("nan")) for n in ("k_x", "v_x"))
+    grads = plan.backward(q.to(DEV), g["k_x"], g["v_x"], out, lse, dout.to(DEV), g["q_gain_x"], g["k_gain_x"], 1e-6,
+                          sc, dq=dq, dk=dk, dv=dv)
+    torch.cuda.synchronize()
+    got_out, got_lse = out.double().cpu().numpy(), lse.double().cpu().numpy()
+    got = [t.double().cpu().numpy() for t in grads]
+    plan.close()
+    ref_out, ref_lse = oracle.cross_attention(q, tx["k_x"], tx["v_x"], tx["q_gain_x"], tx["k_gain_x"], 1e-6, sc,
+                                              lay.q_offsets, text)
+    assert np.all(np.isfinite(got_out))
+    assert np.max(np.abs(got_out - ref_out)) <= 2e-2 and rel_l2(got_out, ref_out) <= 5e-3
+    live = np.isfinite(ref_lse)
+    assert np.array_equal(np.isfinite(got_lse), live) and np.all(got_out[~live.T.any(axis=1)] == 0)
+    # the cross LSE bound of its own tests: 2^-7 sqrt(d) |q'| per row, at least 1e-2
+    qf = q.double().numpy()
+    qn = qf / np.sqrt(np.mean(qf ** 2, axis=-1, keepdims=True) + 1e-6) * tx["q_gain_x"].double().numpy()
+    qprime = np.linalg.norm(qn * tx["k_gain_x"].double().numpy(), axis=-1) * sc      # [T_q, H_q]
+    bound = np.maximum(1e-2, 2.0 ** -7 * math.sqrt(128) * qprime.T)
+    assert np.all(np.abs(got_lse[live] - ref_lse[live]) <= bound[live])
+    ref = oracle.cross_attention_backward(q, tx["k_x"], tx["v_x"], tx["q_gain_x"], tx["k_gain_x"], 1e-6, sc,
+                                          lay.q_offsets, text, dout)
+    errs = [rel_l2(a, b) for a, b in zip(got, ref)]
+    for a in got:
+        assert np.all(np.isfinite(a))
+    assert max(errs) <= 1e-2, dict(zip(("dq", "dk", "dv", "dq_gain", "dk_gain"), errs))
+    assert np.all(got[0][np.all(ref[0] == 0, axis=(1, 2))] == 0)
+    unseen = np.all(ref[2] == 0, axis=(1, 2))
+    assert np.all(got[1][unseen] == 0) and np.all(got[2][unseen] == 0)
