@@ -306,22 +306,28 @@ def main():
     lse_shape = (cfg.n_q_heads, lay.t_q)
     out, lse = torch.empty_like(q), torch.empty(lse_shape, dtype=torch.float32, device=dev)
     t0 = time.perf_counter()
+    # The workspace is allocated once, as a training or serving loop would.
     if mode == "self":
         plan = Plan.from_layout(lay, cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim, cfg.dtype)
+        ws = torch.empty(max(plan.workspace_size(), 16), dtype=torch.uint8, device=dev)
         k, v, qg, kg = g(inp["k"]), g(inp["v"]), g(inp["q_gain"]), g(inp["k_gain"])
-        step = lambda: plan(q, k, v, qg, kg, cfg.eps, cfg.scale, out=out, lse=lse, stream=stream)  # noqa: E731
+        step = lambda: plan(q, k, v, qg, kg, cfg.eps, cfg.scale, out=out, lse=lse, workspace=ws,  # noqa: E731
+                            stream=stream)
     elif mode == "cross":
         plan = CrossPlan.from_layout(lay, text, cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim, cfg.dtype)
+        ws = torch.empty(max(plan.workspace_size(), 16), dtype=torch.uint8, device=dev)
         kx, vx, qgx, kgx = g(tx["k_x"]), g(tx["v_x"]), g(tx["q_gain_x"]), g(tx["k_gain_x"])
-        step = lambda: plan(q, kx, vx, qgx, kgx, cfg.eps, cfg.scale, out=out, lse=lse, stream=stream)  # noqa: E731
+        step = lambda: plan(q, kx, vx, qgx, kgx, cfg.eps, cfg.scale, out=out, lse=lse, workspace=ws,  # noqa: E731
+                            stream=stream)
     else:
         plan = ParallelPlan.from_layout(lay, text, cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim, cfg.dtype)
+        ws = torch.empty(max(plan.workspace_size(), 16), dtype=torch.uint8, device=dev)
         k, v, qg, kg = g(inp["k"]), g(inp["v"]), g(inp["q_gain"]), g(inp["k_gain"])
         kx, vx, qgx, kgx = g(tx["k_x"]), g(tx["v_x"]), g(tx["q_gain_x"]), g(tx["k_gain_x"])
         out_x, lse_x = torch.empty_like(q), torch.empty(lse_shape, dtype=torch.float32, device=dev)
         step = lambda: plan(q, k, v, kx, vx, q_gain=qg, k_gain=kg, q_gain_x=qgx, k_gain_x=kgx,  # noqa: E731
                             rms_eps=cfg.eps, scale=cfg.scale, scale_x=cfg.scale, out=out, lse=lse, out_x=out_x,
-                            lse_x=lse_x, stream=stream)
+                            lse_x=lse_x, workspace=ws, stream=stream)
     plan_ms = (time.perf_counter() - t0) * 1e3
     stats = plan.stats()
     print(f"[bench] {cfg.name} ({mode}): T_q={lay.t_q} T_k={lay.t_k}"

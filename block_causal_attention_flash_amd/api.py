@@ -176,9 +176,8 @@ def magi_attn_bwd(handle: int, q, k, v, out, lse, dout, q_gain=None, k_gain=None
     qg = _gain(q_gain, d, dev)
     kg = _gain(k_gain, d, dev)
     sc = (1.0 / d ** 0.5) if scale is None else float(scale)
-    need = magi_attn_bwd_workspace_size(handle)
-    if workspace is None:
-        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
+    if workspace is None:                              # (the library checks a given workspace's size)
+        workspace = torch.empty(max(magi_attn_bwd_workspace_size(handle), 16), dtype=torch.uint8, device=dev)
     ws_bytes = workspace.numel() * workspace.element_size()
     io = _abi.BwdIO(*(t.data_ptr() for t in (q, k, v, qg, kg, out, lse, dout, dq, dk, dv, dq_gain, dk_gain)))
     _check(lib, lib.magi_attn_bwd(handle, ctypes.byref(io), float(rms_eps), sc, workspace.data_ptr(), ws_bytes,
@@ -253,9 +252,8 @@ def magi_attn_fwd(handle: int, q, k, v, q_gain=None, k_gain=None, rms_eps: float
     qg = _gain(q_gain, d, q.device)
     kg = _gain(k_gain, d, q.device)
     sc = (1.0 / d ** 0.5) if scale is None else float(scale)
-    need = magi_attn_workspace_size(handle)
-    if workspace is None:
-        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    if workspace is None:                              # (the library checks a given workspace's size)
+        workspace = torch.empty(max(magi_attn_workspace_size(handle), 16), dtype=torch.uint8, device=q.device)
     ws_bytes = workspace.numel() * workspace.element_size()
     _check(lib, lib.magi_attn_fwd(handle, q.data_ptr(), k.data_ptr(), v.data_ptr(), qg.data_ptr(), kg.data_ptr(),
                                   float(rms_eps), sc, out.data_ptr(), lse.data_ptr(), workspace.data_ptr(), ws_bytes,
@@ -285,9 +283,8 @@ def magi_attn_fwd_parallel(handle: int, q, k, v, q_x, k_x, v_x, q_gain=None, k_g
     gains = [_gain(g, d, dev) for g in (q_gain, k_gain, q_gain_x, k_gain_x)]
     sc = (1.0 / d ** 0.5) if scale is None else float(scale)
     scx = (1.0 / d ** 0.5) if scale_x is None else float(scale_x)
-    need = magi_attn_workspace_size(handle)
-    if workspace is None:
-        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
+    if workspace is None:                              # (the library checks a given workspace's size)
+        workspace = torch.empty(max(magi_attn_workspace_size(handle), 16), dtype=torch.uint8, device=dev)
     ws_bytes = workspace.numel() * workspace.element_size()
     io = _abi.ParallelIO(q.data_ptr(), k.data_ptr(), v.data_ptr(), gains[0].data_ptr(), gains[1].data_ptr(), sc,
                          out.data_ptr(), lse.data_ptr(), q_x.data_ptr(), k_x.data_ptr(), v_x.data_ptr(),
