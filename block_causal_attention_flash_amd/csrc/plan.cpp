@@ -138,10 +138,12 @@ Tiling choose_tiling(int dtype, int head_dim, int group) {
 Tiling choose_bwd_tiling(int dtype, int head_dim, int group) {
   Tiling t = choose_tiling(dtype, head_dim, group);
   if (dtype == MAGI_DTYPE_BF16) {
-    // kBwdRowsPerItem rows per dq workgroup: 8 waves x 32 rows.
+    // kBwdRowsPerItem rows per dq workgroup: 8 waves x 32 rows, each wave's
+    // rows one 32-token image of one head, so the item's token tile must be a
+    // multiple of 32: heads per item divide both the group and 256 / 32.
     int hpw = 1;
     for (int h = 1; h <= group; ++h)
-      if (group % h == 0 && kBwdRowsPerItem % h == 0) hpw = h;
+      if (group % h == 0 && (kBwdRowsPerItem / 32) % h == 0) hpw = h;
     t.heads_per_item = hpw;
     t.tile_q = kBwdRowsPerItem / hpw;
   }
@@ -444,8 +446,12 @@ magi_status_t build_host_plan(int32_t kind, const magi_attn_layout_t* L, const m
 magi_status_t build_bwd_plan(const magi_attn_layout_t* L, const magi_attn_text_t* T, BwdHostPlan& B,
                              std::string& err) {
   const int group = L->n_q_heads / L->n_kv_heads;
-  magi_status_t s = build_host_plan(T ? kPlanCross : kPlanSelf, L, T, choose_bwd_tiling(L->dtype, L->head_dim, group),
-                                    B.dq, err, /*allow_split=*/false);
+  const Tiling tiling = choose_bwd_tiling(L->dtype, L->head_dim, group);
+  if (L->dtype == MAGI_DTYPE_BF16 && tiling.tile_q % 32 != 0) {
+    err = "internal: backward query tile not a multiple of 32 tokens";
+    return MAGI_ERR_UNSUPPORTED;
+  }
+  magi_status_t s = build_host_plan(T ? kPlanCross : kPlanSelf, L, T, tiling, B.dq, err, /*allow_split=*/false);
   if (s != MAGI_OK) return s;
   // Query blocks without any key have no dq item (their merge entries hold no
   // pieces): their dq is zero.

@@ -215,3 +215,34 @@ def test_random_layout_fp32(seed):
             assert np.all(np.isfinite(a))
         assert max(errs) <= 1e-5, dict(zip(("dq", "dk", "dv", "dq_gain", "dk_gain"), errs))
 
+
+@pytest.mark.parametrize("seed,hq,hk", [(3, 24, 2), (5, 32, 2), (7, 24, 1)])
+def test_random_layout_wide_groups(seed, hq, hk):
+    """Query-head groups of 12, 16 and 24 (work items of 32, 24 and 16 tokens
+    of every head of the group): forward and backward against the oracle."""
+    from block_causal_attention_flash_amd import TrainPlan
+    lay, _, _, _ = random_case(seed)
+    log(f"random wide groups {seed} {hq}/{hk}: {lay}")
+    sc = 1 / math.sqrt(128)
+    inp = make_inputs(lay, hq, hk, 128, "bf16", "uniform", seed)
+    dout = torch.from_numpy(np.random.default_rng(seed + 7).standard_normal((lay.t_q, hq, 128))
+                            .astype(np.float32)).to(torch.bfloat16)
+    g = {n: t.to(DEV) for n, t in inp.items()}
+    plan = TrainPlan.from_layout(lay, hq, hk, 128, "bf16")
+    out, lse = plan(g["q"], g["k"], g["v"], g["q_gain"], g["k_gain"], 1e-6, sc)
+    dq, dk, dv = (torch.full_like(g[n], float("nan")) for n in ("q", "k", "v"))
+    grads = plan.backward(g["q"], g["k"], g["v"], out, lse, dout.to(DEV), g["q_gain"], g["k_gain"], 1e-6, sc,
+                          dq=dq, dk=dk, dv=dv)
+    torch.cuda.synchronize()
+    got_out, got_lse = out.double().cpu().numpy(), lse.double().cpu().numpy()
+    got = [t.double().cpu().numpy() for t in grads]
+    plan.close()
+    ref_out, ref_lse = oracle.attention(inp["q"], inp["k"], inp["v"], inp["q_gain"], inp["k_gain"], 1e-6, sc, lay)
+    assert np.max(np.abs(got_out - ref_out)) <= 2e-2 and rel_l2(got_out, ref_out) <= 5e-3
+    assert np.max(np.abs(got_lse - ref_lse)) <= 1e-2
+    ref = oracle.attention_backward(inp["q"], inp["k"], inp["v"], inp["q_gain"], inp["k_gain"], 1e-6, sc, lay,
+                                    dout)
+    errs = [rel_l2(a, b) for a, b in zip(got, ref)]
+    assert all(np.all(np.isfinite(a)) for a in got)
+    assert max(errs) <= 1e-2, dict(zip(("dq", "dk", "dv", "dq_gain", "dk_gain"), errs))
+
