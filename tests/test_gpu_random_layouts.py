@@ -216,10 +216,11 @@ def test_random_layout_fp32(seed):
         assert max(errs) <= 1e-5, dict(zip(("dq", "dk", "dv", "dq_gain", "dk_gain"), errs))
 
 
-@pytest.mark.parametrize("seed,hq,hk", [(3, 24, 2), (5, 32, 2), (7, 24, 1)])
+@pytest.mark.parametrize("seed,hq,hk", [(3, 24, 2), (5, 32, 2), (7, 24, 1), (9, 32, 1), (11, 48, 1)])
 def test_random_layout_wide_groups(seed, hq, hk):
-    """Query-head groups of 12, 16 and 24 (work items of 32, 24 and 16 tokens
-    of every head of the group): forward and backward against the oracle."""
+    """Query-head groups of 12, 16, 24, 32 and 48 (forward work items of 32
+    down to 8 tokens of every head of the group; backward items of at least
+    32 tokens): forward and backward against the oracle."""
     from block_causal_attention_flash_amd import TrainPlan
     lay, _, _, _ = random_case(seed)
     log(f"random wide groups {seed} {hq}/{hk}: {lay}")
