@@ -132,9 +132,13 @@ def test_random_layout_self_attention(seed):
 
 @pytest.mark.parametrize("seed", SEEDS)
 def test_random_layout_cross_attention(seed):
-    from block_causal_attention_flash_amd import CrossTrainPlan
     lay, text, hq, hk = random_case(seed)
     log(f"random cross {seed}: {describe(lay, text, hq, hk)}")
+    check_cross(seed, lay, text, hq, hk)
+
+
+def check_cross(seed, lay, text, hq, hk):
+    from block_causal_attention_flash_amd import CrossTrainPlan
     sc = 0.8 / math.sqrt(128)
     q = make_inputs(lay, hq, hk, 128, "bf16", "uniform", seed)["q"]
     tx = make_text_inputs(text, hk, 128, "bf16", "uniform", seed + 1)
@@ -246,4 +250,12 @@ def test_random_layout_wide_groups(seed, hq, hk):
     errs = [rel_l2(a, b) for a, b in zip(got, ref)]
     assert all(np.all(np.isfinite(a)) for a in got)
     assert max(errs) <= 1e-2, dict(zip(("dq", "dk", "dv", "dq_gain", "dk_gain"), errs))
+
+
+@pytest.mark.parametrize("seed,hq,hk", [(4, 24, 2), (6, 32, 2), (8, 24, 1), (10, 48, 1)])
+def test_random_layout_wide_groups_cross(seed, hq, hk):
+    """The cross-attention's forward and backward with groups of 12 to 48."""
+    lay, text, _, _ = random_case(seed)
+    log(f"random cross wide groups {seed} {hq}/{hk}: {describe(lay, text, hq, hk)}")
+    check_cross(seed, lay, text, hq, hk)
 
