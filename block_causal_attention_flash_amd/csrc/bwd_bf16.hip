@@ -24,8 +24,17 @@
 //           then (dq_hat)^T += k'^T dS^T;
 //   dkdv    key-stationary: 8 waves x 32 keys of one KV head, per
 //           (32-token tile, query head) S and dP, then dV^T += dO^T P and
-//           dK^T += q_hat^T dS;
+//           dK^T += q_hat^T dS; when a plan has fewer key blocks x KV heads
+//           than CUs, each list is cut into pieces that write fp32 sums;
+//   merge   adds a split list's pieces in order and finishes like dkdv;
+//   zero    dq of rows no item covers (they see no key) and dk, dv of key
+//           blocks no row sees;
 //   reduce  the gain gradients from the per-workgroup partials.
+// On boundary tiles a branch that unmasked steps skip sets S to -inf outside
+// each row's (dq) or each key's (dk/dv) allowed range before the
+// exponentials. A cross-attention plan runs the same kernels: its keys are
+// the text's, a row's range is its chunk's text, a text key's rows are the
+// chunks whose prompt holds it.
 // Every image is [16 chunks][32 row slots][16 B]: chunk c of row r (dims
 // 8c..8c+7) sits at byte 512 c + 16 (r XOR 12 (c mod 2)). The XOR keeps each
 // 16-row block of a chunk in its own 256 bytes, so row reads stay contiguous,
