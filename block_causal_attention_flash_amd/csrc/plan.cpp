@@ -21,6 +21,18 @@
 // c see the text keys [text_begin[c], text_end[c]). A parallel plan holds
 // both attentions as two phases of one work list, so the short text items
 // are ordered after the long self-attention items and fill the launch's tail.
+//
+// A KV range R (paperlayer §2.4.4) moves each row's lower bound to chunk
+// c - R + 1; a last global block (paper-notes Figure 15(g)) gives its rows
+// the whole key stream. Both keep one interval per row.
+//
+// A training plan adds the backward's lists: dq items as the forward's (never
+// split), and dk/dv items per (key block, KV head) over the token tiles that
+// see the block. A key is seen by at most two token ranges (its own video's
+// later chunks, and a global block's rows; for the text, at most two runs of
+// chunks sharing its prompt), so a (token tile, key block) pair is classified
+// full, boundary or empty as in the forward. With fewer such items than CUs
+// the lists are cut into pieces whose partial sums a merge adds in order.
 #include "plan.hpp"
 
 #include "kernels.hpp"
