@@ -155,6 +155,57 @@ def cpu_baseline(cfg, inp, budget_s: float = 20.0, attention: str = "self", text
                       f"{spent:.1f} s fp64 numpy on the host"}
 
 
+def cpu_baseline_backward(cfg, inp, dout, budget_s: float = 20.0, text=None):
+    """Times the fp64 backward oracle on a bounded sample: the first n tokens
+    of the workload's first chunk (with text, for the cross-attention) as a
+    one-chunk layout, n doubling from 256 while the oracle takes under a
+    quarter of the budget. Useful FLOPs as the GPU line counts them: 2.5x the
+    forward's over the sample's pairs."""
+    import numpy as np
+    import oracle
+    from workloads import Layout, TextLayout
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = 1
+    lay = cfg.layout
+    d, hq = cfg.head_dim, cfg.n_q_heads
+    if text is None:
+        c = next(c for c in range(lay.n_chunks) if lay.q_offsets[c + 1] > lay.q_offsets[c])
+    else:
+        c = next((c for c in range(lay.n_chunks)
+                  if lay.q_offsets[c + 1] > lay.q_offsets[c] and text.end[c] > text.begin[c]), None)
+        if c is None:
+            return None
+    a, b = lay.q_offsets[c], lay.q_offsets[c + 1]
+    ka = lay.kv_offsets[c]
+    n, spent, flops = 256, 0.0, 0.0
+    while True:
+        n = min(n, b - a, lay.kv_offsets[c + 1] - ka) if text is None else min(n, b - a)
+        sub = Layout((0, n), (0, n), (0, 1))
+        q, g = inp["q"][a:a + n], dout[a:a + n]
+        t0 = time.perf_counter()
+        if text is None:
+            oracle.attention_backward(q, inp["k"][ka:ka + n], inp["v"][ka:ka + n], inp["q_gain"], inp["k_gain"],
+                                      cfg.eps, cfg.scale, sub, g)
+            pairs = n * n
+        else:
+            sub_text = TextLayout((text.begin[c],), (text.end[c],), text.t_text)
+            oracle.cross_attention_backward(q, inp["k"], inp["v"], inp["q_gain"], inp["k_gain"], cfg.eps, cfg.scale,
+                                            sub.q_offsets, sub_text, g)
+            pairs = n * (text.end[c] - text.begin[c])
+        spent = time.perf_counter() - t0
+        flops = 2.5 * 4.0 * d * hq * pairs
+        if spent > budget_s / 4 or n >= b - a or (text is None and n >= lay.kv_offsets[c + 1] - ka):
+            break
+        n *= 2
+    what = "its text" if text is not None else "itself"
+    return {"value": flops / spent / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"backward of the first {n} tokens of chunk {c} of {cfg.name} attending to {what}, "
+                      f"{hq} heads, {spent:.1f} s fp64 numpy on the host"}
+
+
 def bench_backward(args) -> None:
     """One step = one backward call of the self-attention, or with
     --attention cross of the text cross-attention (the forward's out and lse
@@ -230,6 +281,12 @@ def bench_backward(args) -> None:
         "roofline": roof, "cpu_baseline": None,
     }
     plan.close()
+    if not args.no_cpu_baseline:
+        print(f"[bench] timing the CPU backward oracle on a sample (~{args.cpu_budget / 4:.0f} s)", file=sys.stderr,
+              flush=True)
+        dout_cpu = dout.cpu()
+        host = {n: t for n, t in inp.items()}
+        rec["cpu_baseline"] = cpu_baseline_backward(cfg, host, dout_cpu, args.cpu_budget, text)
     print(json.dumps(rec), flush=True)
 
 
