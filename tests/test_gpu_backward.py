@@ -219,3 +219,49 @@ def test_backward_full_size(name):
         e_dv = rel_l2(dv[kk].double().cpu().numpy(), rv)
         log(f"backward {name}: dk keys rel_l2 {e_dk:.2e} dv keys rel_l2 {e_dv:.2e}")
         assert e_dk <= TOL["bf16"] and e_dv <= TOL["bf16"]
+
+
+# ------------------------------------------------------------------ the size limit
+
+def test_kv_stream_at_the_2gib_limit_forward_and_backward():
+    """A KV stream 64 KiB under the 2 GiB limit of the bf16 tile images
+    (1,048,528 keys x 8 KV heads): a cached prefix of 1,048,428 keys without
+    queries, then one chunk of 100 queries with a KV range of 1, so the
+    queries see only the last 100 keys. The GPU plans, prepares and addresses
+    the whole stream (tile offsets near 2^31); the oracle needs only the last
+    chunk, since no query sees the prefix. The prefix's dk and dv must be
+    exactly 0 (key blocks no row sees)."""
+    from block_causal_attention_flash_amd import TrainPlan
+    hq, hk, d, n, prefix = 16, 8, 128, 100, 1_048_428
+    lay = Layout((0, 0, n), (0, prefix, prefix + n), (0, 2), kv_range=1)
+    sub = Layout((0, n), (0, n), (0, 1))
+    small = make_inputs(sub, hq, hk, d, "bf16", "uniform", 21)
+    gen = torch.Generator(device=DEV).manual_seed(21)
+    k = torch.randn(prefix + n, hk, d, generator=gen, device=DEV, dtype=torch.float32).to(torch.bfloat16)
+    v = torch.randn(prefix + n, hk, d, generator=gen, device=DEV, dtype=torch.float32).to(torch.bfloat16)
+    k[prefix:] = small["k"].to(DEV)
+    v[prefix:] = small["v"].to(DEV)
+    q, qg, kg = (small[x].to(DEV) for x in ("q", "q_gain", "k_gain"))
+    dout = torch.from_numpy(np.random.default_rng(22).standard_normal((n, hq, d)).astype(np.float32)).to(
+        torch.bfloat16)
+    sc = 1 / math.sqrt(d)
+    log("2 GiB stream: plan, forward, backward")
+    plan = TrainPlan.from_layout(lay, hq, hk, d, "bf16")
+    out, lse = plan(q, k, v, qg, kg, 1e-6, sc)
+    dk, dv = torch.full_like(k, float("nan")), torch.full_like(v, float("nan"))
+    dq, dk, dv, dgq, dgk = plan.backward(q, k, v, out, lse, dout.to(DEV), qg, kg, 1e-6, sc, dk=dk, dv=dv)
+    torch.cuda.synchronize()
+    plan.close()
+    assert bool((dk[:prefix] == 0).all()) and bool((dv[:prefix] == 0).all())
+    ref_out, ref_lse = oracle.attention(small["q"], small["k"], small["v"], small["q_gain"], small["k_gain"], 1e-6,
+                                        sc, sub)
+    got_out = out.double().cpu().numpy()
+    assert np.max(np.abs(got_out - ref_out)) <= 2e-2 and rel_l2(got_out, ref_out) <= 5e-3
+    assert np.max(np.abs(lse.double().cpu().numpy() - ref_lse)) <= 1e-2
+    ref = oracle.attention_backward(small["q"], small["k"], small["v"], small["q_gain"], small["k_gain"], 1e-6, sc,
+                                    sub, dout)
+    got = [dq.double().cpu().numpy(), dk[prefix:].double().cpu().numpy(), dv[prefix:].double().cpu().numpy(),
+           dgq.double().cpu().numpy(), dgk.double().cpu().numpy()]
+    errs = [rel_l2(a, b) for a, b in zip(got, ref)]
+    log("  rel_l2 dq {:.2e} dk {:.2e} dv {:.2e} dgq {:.2e} dgk {:.2e}".format(*errs))
+    assert max(errs) <= TOL["bf16"]
