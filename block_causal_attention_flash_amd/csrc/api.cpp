@@ -1,4 +1,4 @@
-// C ABI of the block-causal attention forward (declared in include/magi_attn.h).
+// C ABI of the block-causal attention library: plans, forward, backward (declared in include/magi_attn.h).
 #include <hip/hip_runtime.h>
 
 #include <cmath>
