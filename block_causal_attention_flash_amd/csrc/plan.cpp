@@ -38,6 +38,7 @@
 #include "kernels.hpp"
 
 #include <algorithm>
+#include <cmath>
 #include <cstring>
 #include <numeric>
 
@@ -263,6 +264,27 @@ int classify_pair(const std::vector<RowBounds>& iv, int64_t k0, int64_t k1, int6
   return all ? 2 : (any ? 1 : 0);
 }
 
+
+// Tiles per piece for a phase of n_whole items holding total_cost key tiles.
+// Items run one per CU at a time, so cutting every item into p pieces takes
+// ceil(n_whole p / kNumCu) rounds of (mean / p + kPieceOverheadTiles) tiles;
+// p is the smallest count that minimises that time, up to kMaxPieces and
+// with pieces of at least kMinPieceTiles.
+int64_t split_piece_tiles(int64_t n_whole, int64_t total_cost) {
+  const double mean = double(total_cost) / double(n_whole);
+  int best_p = 1;
+  double best = 0.0;
+  for (int p = 1; p <= kMaxPieces && (p == 1 || mean / p >= kMinPieceTiles); ++p) {
+    const double rounds = double((n_whole * p + kNumCu - 1) / kNumCu);
+    const double t = rounds * (mean / p + kPieceOverheadTiles);
+    if (p == 1 || t < best * (1.0 - 1e-9)) {
+      best = t;
+      best_p = p;
+    }
+  }
+  return std::max<int64_t>(1, int64_t(std::ceil(mean / best_p)));
+}
+
 magi_status_t build_host_plan(int32_t kind, const magi_attn_layout_t* L, const magi_attn_text_t* T,
                               const Tiling& tiling, HostPlan& P, std::string& err, bool allow_split) {
   (void)err;
@@ -370,14 +392,13 @@ magi_status_t build_host_plan(int32_t kind, const magi_attn_layout_t* L, const m
         total_cost += int64_t(P.qt_ntiles[ph * n_qt + qt]) * P.hk * groups_per_kvh;
       }
     const bool split = allow_split && P.dtype == MAGI_DTYPE_BF16 && n_whole > 0 && n_whole < kSplitBelowItems;
-    const int64_t piece =
-        std::max<int64_t>(kMinPieceTiles, (total_cost + kSplitTargetItems - 1) / kSplitTargetItems);
+    const int64_t piece = split ? split_piece_tiles(n_whole, total_cost) : int64_t(1) << 40;
     for (int kvh = 0; kvh < P.hk; ++kvh)
       for (int64_t qt = 0; qt < n_qt; ++qt) {
         const int64_t li = ph * n_qt + qt;
         const int32_t nt = P.qt_ntiles[li];
         const int32_t b0 = P.qt_tiles[li];
-        const int64_t want = (nt + piece - 1) / piece;                      // pieces of about `piece` tiles
+        const int64_t want = (nt + piece / 2) / piece;                      // pieces of about `piece` tiles
         const int n_pieces =
             nt == 0 ? 0
             : split ? int(std::max<int64_t>(1, std::min<int64_t>({want, int64_t(kMaxPieces), nt / kMinPieceTiles})))

@@ -48,15 +48,17 @@ struct MergeItem {
 
 // Split-KV policy (bf16): when a layout has fewer than kSplitBelowItems work
 // items (too few to keep every compute unit busy to the end), items are cut
-// into up to kMaxPieces contiguous ranges of their tile list, about
-// total / kSplitTargetItems tiles each and at least kMinPieceTiles long.
+// into up to kMaxPieces contiguous ranges of their tile list, at least
+// kMinPieceTiles long. The piece length is the mean list cut into the count
+// that finishes the phase soonest, counting whole rounds of one item per CU
+// and kPieceOverheadTiles per piece (query load, epilogue, merge).
 // (Measured: the 4-chunks-on-16-cached streaming window, 384 items, gains;
 // the two-video 256x256 layout, 768 short items, loses when split.)
 constexpr int kNumCu = 256;
 constexpr int kSplitBelowItems = 2 * kNumCu;
-constexpr int kSplitTargetItems = 4 * kNumCu;
 constexpr int kMaxPieces = 8;
 constexpr int kMinPieceTiles = 64;
+constexpr double kPieceOverheadTiles = 16.0;
 // The backward's dk/dv items (bf16) split the same way when there are
 // fewer (key block, KV head) items than CUs (a short text stream): each
 // token-tile list is cut into up to kBwdMaxPieces pieces of at least
