@@ -323,3 +323,32 @@ def test_last_global_stats(built_lib):
     assert st["unmasked_pairs"] == plain["unmasked_pairs"] - g_own + (lay.t_q - g0) * lay.t_q
     with pytest.raises(MagiAttnError):
         magi_attn_plan_stats([0, 4], None, None, 1, 1, 128, "bf16", last_global=2)
+
+
+def test_split_piece_count_fills_whole_rounds(built_lib):
+    """Split-KV piece counts (bf16). The streaming window has 384 whole items
+    (128-token query tiles x 8 KV heads x 1 head group), under 2 per compute
+    unit: with one item per CU at a time, 2 pieces per item make 768 pieces in
+    3 full rounds of 256, where 3 pieces would take 4.5 rounds. Layouts with at
+    least 512 items stay whole; a layout of 4 items is cut as finely as the
+    64-tile minimum allows."""
+    from block_causal_attention_flash_amd import magi_attn_plan_stats
+    c = get_config("streaming")
+    lay = c.layout
+    st = magi_attn_plan_stats(lay.q_offsets, lay.kv_offsets, lay.seq_chunks, c.n_q_heads, c.n_kv_heads, c.head_dim,
+                              c.dtype)
+    whole = -(-lay.t_q // st["tile_q"]) * c.n_kv_heads * (c.n_q_heads // c.n_kv_heads // st["heads_per_item"])
+    assert whole == 384
+    assert st["n_items"] == 2 * whole
+    for name in ("video256x2", "video480x832"):
+        c = get_config(name)
+        lay = c.layout
+        st = magi_attn_plan_stats(lay.q_offsets, lay.kv_offsets, lay.seq_chunks, c.n_q_heads, c.n_kv_heads,
+                                  c.head_dim, c.dtype)
+        n_qt = -(-lay.t_q // st["tile_q"])
+        assert st["n_items"] == n_qt * c.n_kv_heads * (c.n_q_heads // c.n_kv_heads // st["heads_per_item"]), name
+    # 2 query tiles x 2 KV heads, each with 384 key tiles: 6 pieces of 64 tiles
+    kv = [512 * i for i in range(17)] + [8192 + 2048, 8192 + 4096]
+    q = [0] * 17 + [96, 192]
+    st = magi_attn_plan_stats(q, kv, [0, 18], 6, 2, 128, "bf16")
+    assert st["n_items"] >= 4 * 6
