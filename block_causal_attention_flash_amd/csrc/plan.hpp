@@ -63,7 +63,9 @@ constexpr double kPieceOverheadTiles = 16.0;
 // fewer (key block, KV head) items than CUs (a short text stream): each
 // token-tile list is cut into up to kBwdMaxPieces pieces of at least
 // kBwdMinPieceEntries entries, about total / kBwdSplitTargetItems each.
-// (With 384 items, video 256x2, the split was 9% slower than none.)
+// (With 384 items, video 256x2, the split was 9% slower than none, and
+// still 3.5% slower at 2 pieces per item, 768 pieces in three full rounds:
+// the fp32 partials and the merge cost more than the tail saves.)
 constexpr int kBwdSplitBelowItems = kNumCu;
 constexpr int kBwdSplitTargetItems = 4 * kNumCu;
 constexpr int kBwdMaxPieces = 64;
