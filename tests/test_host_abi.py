@@ -352,3 +352,23 @@ def test_split_piece_count_fills_whole_rounds(built_lib):
     q = [0] * 17 + [96, 192]
     st = magi_attn_plan_stats(q, kv, [0, 18], 6, 2, 128, "bf16")
     assert st["n_items"] >= 4 * 6
+
+
+def test_plain_c_client_of_the_host_calls(built_lib, tmp_path):
+    """The header compiles as strict C99 and a C program linked against the
+    library gets the documented answers from the host-only calls (planning
+    statistics, the tile classifier, the error path)."""
+    import shutil
+    import subprocess
+    gcc = shutil.which("gcc")
+    if gcc is None:
+        pytest.skip("gcc not found")
+    exe = tmp_path / "abi_host"
+    libdir = os.path.dirname(built_lib)
+    cmd = [gcc, "-std=c99", "-Wall", "-Wextra", "-pedantic", "-Werror", "-I", os.path.join(ROOT, "include"),
+           os.path.join(ROOT, "tests", "c", "abi_host.c"), "-L", libdir, "-lmagi_attn", f"-Wl,-rpath,{libdir}",
+           "-o", str(exe)]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
+    r = subprocess.run([str(exe)], capture_output=True, text=True, timeout=60)
+    assert r.returncode == 0 and r.stdout.strip() == "ok", r.stdout + r.stderr
