@@ -6,8 +6,10 @@ Each layout mixes what the fixed cases test one at a time: packed videos of
 one to three chunks, ragged chunk lengths off the tile grids, leading cached
 chunks without queries (a KV cache), a KV-range window, a last global block,
 and several GQA ratios. Tolerances are those of the fixed cases: forward bf16
-max-abs 2e-2, relative L2 5e-3 and LSE 1e-2 (the cross LSE: the per-row bound
-of its own tests); backward relative L2 1e-2 per gradient.
+max-abs 2e-2 and relative L2 5e-3; backward relative L2 1e-2 per gradient. The
+LSE of every row is held to max(1e-2, B) with B = 2^-7 sqrt(d) |q'| (lse_tol):
+a row that sees a single key has that key's logit as its LSE, so the logit's
+bf16 rounding shows undamped.
 """
 import math
 import sys
@@ -85,6 +87,18 @@ def rows_and_keys(lay, text=None):
     return ~m.any(axis=1), ~m.any(axis=0)
 
 
+def lse_tol(q, q_gain, k_gain, scale):
+    """[H, T] LSE tolerance: max(1e-2, B), B the first-order bound of the bf16
+    path's LSE error. The kernel rounds q' = rms(q) g_q g_k scale and k_hat to
+    bf16 (unit roundoff 2^-8 each) and accumulates in fp32, and the LSE moves
+    by at most the largest logit error: |d lse| <= max_j |d s_j|
+    <= 2^-7 sum_d |q'_d k_hat_jd| <= 2^-7 |q'| |k_hat_j|, |k_hat_j| <= sqrt(d)."""
+    qf = q.double().numpy()
+    qn = qf / np.sqrt(np.mean(qf ** 2, axis=-1, keepdims=True) + 1e-6) * q_gain.double().numpy()
+    qprime = np.linalg.norm(qn * k_gain.double().numpy(), axis=-1) * scale      # [T_q, H_q]
+    return np.maximum(1e-2, 2.0 ** -7 * math.sqrt(q.shape[-1]) * qprime.T)
+
+
 def rel_l2(got, ref):
     n = np.linalg.norm(ref)
     return float(np.linalg.norm(got - ref) / n) if n > 0 else float(np.linalg.norm(got))
@@ -119,7 +133,7 @@ def test_random_layout_self_attention(seed):
     d = got_out - ref_out
     assert np.all(np.isfinite(got_out)) and np.all(np.isfinite(got_lse))
     assert np.max(np.abs(d)) <= 2e-2 and rel_l2(got_out, ref_out) <= 5e-3
-    assert np.max(np.abs(got_lse - ref_lse)) <= 1e-2
+    assert np.all(np.abs(got_lse - ref_lse) <= lse_tol(inp["q"], inp["q_gain"], inp["k_gain"], sc))
     ref = oracle.attention_backward(inp["q"], inp["k"], inp["v"], inp["q_gain"], inp["k_gain"], 1e-6, sc, lay,
                                     dout)
     errs = [rel_l2(a, b) for a, b in zip(got, ref)]
@@ -161,11 +175,7 @@ def check_cross(seed, lay, text, hq, hk):
     assert np.max(np.abs(got_out - ref_out)) <= 2e-2 and rel_l2(got_out, ref_out) <= 5e-3
     live = np.isfinite(ref_lse)
     assert np.array_equal(np.isfinite(got_lse), live) and np.all(got_out[~live.T.any(axis=1)] == 0)
-    # the cross LSE bound of its own tests: 2^-7 sqrt(d) |q'| per row, at least 1e-2
-    qf = q.double().numpy()
-    qn = qf / np.sqrt(np.mean(qf ** 2, axis=-1, keepdims=True) + 1e-6) * tx["q_gain_x"].double().numpy()
-    qprime = np.linalg.norm(qn * tx["k_gain_x"].double().numpy(), axis=-1) * sc      # [T_q, H_q]
-    bound = np.maximum(1e-2, 2.0 ** -7 * math.sqrt(128) * qprime.T)
+    bound = lse_tol(q, tx["q_gain_x"], tx["k_gain_x"], sc)
     assert np.all(np.abs(got_lse[live] - ref_lse[live]) <= bound[live])
     ref = oracle.cross_attention_backward(q, tx["k_x"], tx["v_x"], tx["q_gain_x"], tx["k_gain_x"], 1e-6, sc,
                                           lay.q_offsets, text, dout)
@@ -244,7 +254,7 @@ def test_random_layout_wide_groups(seed, hq, hk):
     plan.close()
     ref_out, ref_lse = oracle.attention(inp["q"], inp["k"], inp["v"], inp["q_gain"], inp["k_gain"], 1e-6, sc, lay)
     assert np.max(np.abs(got_out - ref_out)) <= 2e-2 and rel_l2(got_out, ref_out) <= 5e-3
-    assert np.max(np.abs(got_lse - ref_lse)) <= 1e-2
+    assert np.all(np.abs(got_lse - ref_lse) <= lse_tol(inp["q"], inp["q_gain"], inp["k_gain"], sc))
     ref = oracle.attention_backward(inp["q"], inp["k"], inp["v"], inp["q_gain"], inp["k_gain"], 1e-6, sc, lay,
                                     dout)
     errs = [rel_l2(a, b) for a, b in zip(got, ref)]
