@@ -269,3 +269,47 @@ def test_random_layout_wide_groups_cross(seed, hq, hk):
     log(f"random cross wide groups {seed} {hq}/{hk}: {describe(lay, text, hq, hk)}")
     check_cross(seed, lay, text, hq, hk)
 
+
+
+def split_cache_case(seed):
+    """A KV-cache layout the plan splits: 4 to 39 cached chunks of 64 to 1,023
+    keys, then 1 to 3 query chunks of up to 299 tokens, so that few work items
+    hold long key lists (2 to 8 pieces each, merged afterwards)."""
+    rng = np.random.default_rng(91000 + seed)
+    n_cached, n_q = int(rng.integers(4, 40)), int(rng.integers(1, 4))
+    kv, q = [0], [0]
+    for c in range(n_cached + n_q):
+        kv.append(kv[-1] + int(rng.integers(64, 1024)))
+        q.append(q[-1] + (0 if c < n_cached else int(rng.integers(1, 300))))
+    lay = Layout(tuple(q), tuple(kv), (0, n_cached + n_q), kv_range=int(rng.choice([0, 0, 6, 12])), last_global=0)
+    hq, hk = [(2, 1), (4, 2), (6, 2), (8, 1), (12, 4), (16, 2), (24, 8)][int(rng.integers(0, 7))]
+    return lay, hq, hk
+
+
+@pytest.mark.parametrize("seed", list(range(6)))
+def test_random_split_kv_cache(seed):
+    from block_causal_attention_flash_amd import TrainPlan, magi_attn_plan_stats
+    lay, hq, hk = split_cache_case(seed)
+    st = magi_attn_plan_stats(lay.q_offsets, lay.kv_offsets, lay.seq_chunks, hq, hk, 128, "bf16")
+    whole = -(-lay.t_q // st["tile_q"]) * hk * (hq // hk // st["heads_per_item"])
+    log(f"random split {seed}: t_q {lay.t_q} t_k {lay.t_k} heads {hq}/{hk} items {st['n_items']} of {whole}")
+    assert st["n_items"] >= 2 * whole                      # every list was cut
+    sc = 1 / math.sqrt(128)
+    inp = make_inputs(lay, hq, hk, 128, "bf16", "uniform", seed)
+    dout = torch.from_numpy(np.random.default_rng(seed + 7).standard_normal((lay.t_q, hq, 128))
+                            .astype(np.float32)).to(torch.bfloat16)
+    g = {n: t.to(DEV) for n, t in inp.items()}
+    plan = TrainPlan.from_layout(lay, hq, hk, 128, "bf16")
+    out, lse = plan(g["q"], g["k"], g["v"], g["q_gain"], g["k_gain"], 1e-6, sc)
+    grads = plan.backward(g["q"], g["k"], g["v"], out, lse, dout.to(DEV), g["q_gain"], g["k_gain"], 1e-6, sc)
+    torch.cuda.synchronize()
+    got_out, got_lse = out.double().cpu().numpy(), lse.double().cpu().numpy()
+    got = [t.double().cpu().numpy() for t in grads]
+    plan.close()
+    ref_out, ref_lse = oracle.attention(inp["q"], inp["k"], inp["v"], inp["q_gain"], inp["k_gain"], 1e-6, sc, lay)
+    assert np.all(np.isfinite(got_out)) and np.all(np.isfinite(got_lse))
+    assert np.max(np.abs(got_out - ref_out)) <= 2e-2 and rel_l2(got_out, ref_out) <= 5e-3
+    assert np.all(np.abs(got_lse - ref_lse) <= lse_tol(inp["q"], inp["q_gain"], inp["k_gain"], sc))
+    ref = oracle.attention_backward(inp["q"], inp["k"], inp["v"], inp["q_gain"], inp["k_gain"], 1e-6, sc, lay, dout)
+    errs = [rel_l2(a, b) for a, b in zip(got, ref)]
+    assert max(errs) <= 1e-2, dict(zip(("dq", "dk", "dv", "dq_gain", "dk_gain"), errs))
