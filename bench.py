@@ -228,6 +228,7 @@ def bench_backward(args) -> None:
     if cross:       # the text's keys, values and gains take the places of the video's
         tx = make_text_inputs(text, cfg.n_kv_heads, cfg.head_dim, cfg.dtype, cfg.gain_kind, cfg.seed + 100)
         inp.update(k=tx["k_x"], v=tx["v_x"], q_gain=tx["q_gain_x"], k_gain=tx["k_gain_x"])
+    inp["q_gain"] = inp["q_gain"] * args.gain_scale
     g = {n: t.to(dev) for n, t in inp.items()}
     tdt = g["q"].dtype
     dout = torch.from_numpy(np.random.default_rng(cfg.seed + 7).standard_normal(
@@ -267,7 +268,8 @@ def bench_backward(args) -> None:
     roof = {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
             "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
             "traffic": stored_backward_traffic(cfg.name)
-            if cfg.dtype == "bf16" and not (cross or lay.kv_range or lay.last_global) else None}
+            if cfg.dtype == "bf16" and not (cross or lay.kv_range or lay.last_global or args.gain_scale != 1.0)
+            else None}
     rec = {
         "metric": METRIC_CROSS_BACKWARD if cross else METRIC_BACKWARD, "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak",
@@ -276,7 +278,8 @@ def bench_backward(args) -> None:
                    "t_k": text.t_text if cross else lay.t_k,
                    "n_chunks": lay.n_chunks, "n_q_heads": cfg.n_q_heads, "n_kv_heads": cfg.n_kv_heads,
                    "head_dim": cfg.head_dim, "kv_range": lay.kv_range, "last_global": lay.last_global,
-                   "useful_flops": flops, "unmasked_pairs_per_head": pairs},
+                   "useful_flops": flops, "unmasked_pairs_per_head": pairs,
+                   **({"gain_scale": args.gain_scale} if args.gain_scale != 1.0 else {})},
         "frac_of_peak": round(tflops / PEAK_BF16_TFLOPS, 4), "plan_create_ms": round(plan_ms, 2),
         "roofline": roof, "cpu_baseline": None,
     }
@@ -322,6 +325,9 @@ def main():
     ap.add_argument("--backward", action="store_true",
                     help="time the backward (magi_attn_bwd) of the self- or (--attention cross) the "
                          "cross-attention instead of the forward")
+    ap.add_argument("--gain-scale", type=float, default=1.0,
+                    help="multiply the query gains by this factor; large enough a factor takes the bf16 forward off "
+                         "the static-softmax kernel instance onto the online one (logit bound above 40)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=20.0)
     ap.add_argument("--copy-probe-mib", type=int, default=0,
@@ -357,6 +363,10 @@ def main():
     inp = make_inputs(lay, cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim, cfg.dtype, cfg.gain_kind, cfg.seed)
     tx = (make_text_inputs(text, cfg.n_kv_heads, cfg.head_dim, cfg.dtype, cfg.gain_kind, cfg.seed + 100)
           if text is not None else None)
+    if args.gain_scale != 1.0:
+        inp["q_gain"] = inp["q_gain"] * args.gain_scale
+        if tx is not None:
+            tx["q_gain_x"] = tx["q_gain_x"] * args.gain_scale
     gen_s = time.perf_counter() - t0
     g = lambda t: t.to(dev)  # noqa: E731
     q = g(inp["q"])
@@ -412,7 +422,9 @@ def main():
     pairs_x = useful_text_pairs(lay, text) if mode != "self" else 0
     flops = 4.0 * cfg.head_dim * cfg.n_q_heads * (pairs + pairs_x)
     tflops = flops / (ms * 1e-3) / 1e12
-    traffic = stored_traffic(cfg.name, mode) if not (lay.kv_range or lay.last_global) else None
+    # the stored counters belong to the static-softmax instance on the workload's own gains
+    traffic = (stored_traffic(cfg.name, mode)
+               if not (lay.kv_range or lay.last_global or args.gain_scale != 1.0) else None)
     roof = {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
             "frac": round(tflops / PEAK_BF16_TFLOPS, 4), "traffic": traffic}
 
@@ -425,6 +437,8 @@ def main():
               "n_videos": lay.n_seqs, "n_q_heads": cfg.n_q_heads, "n_kv_heads": cfg.n_kv_heads,
               "head_dim": cfg.head_dim, "kv_range": lay.kv_range, "last_global": lay.last_global,
               "useful_flops": flops, "unmasked_pairs_per_head": pairs}
+    if args.gain_scale != 1.0:
+        config["gain_scale"] = args.gain_scale
     if text is not None:
         config.update({"t_text": text.t_text, "text_pairs_per_head": pairs_x})
     rec = {
