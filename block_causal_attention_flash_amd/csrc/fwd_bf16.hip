@@ -32,10 +32,12 @@
 //
 // Softmax. QK-normalisation bounds every logit: |s_ij| <= |q'_i| |k_hat_j|
 // <= d max_c |g_q,c g_k,c| scale log2 e (the normalised rows have at most
-// norm sqrt(d)). When that bound of the item's gains is at most 40 (log2
+// norm sqrt(d)). When that bound of the item's gains is at most 64 (log2
 // units), the item uses exp2(s) directly, with no running maximum and no
-// rescaling: softmax is invariant to the shift and 2^+-40 lies far inside the
-// fp32/bf16 range. Otherwise it keeps a running row maximum and rescales its
+// rescaling: softmax is invariant to the shift, P = 2^s stays a normal number
+// in fp32 and bf16, and with at most 2^21 keys the row sum stays below 2^85,
+// so O = sum P v cannot overflow fp32 for |v| < 2^40. Otherwise it keeps a
+// running row maximum and rescales its
 // accumulator only when the maximum has grown by more than 2^8. The two cases
 // are two instances of the kernel, both launched: each workgroup takes the
 // gains of its phase, and the instance that does not match exits at once.
@@ -89,7 +91,7 @@ constexpr int WAIT_YOUNGER = 7;
 constexpr unsigned kNoTile = 0x80000000u;             // scalar offset past any tile image buffer (< 2 GiB): zeros
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
-constexpr float kStaticBound = 40.0f;
+constexpr float kStaticBound = 64.0f;
 constexpr float kRescaleSlack = 8.0f;
 constexpr float kNegInf = -__builtin_inff();
 
