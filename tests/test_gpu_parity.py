@@ -133,6 +133,26 @@ def test_bf16_split_key_ranges_merge():
         log(f"split window {hq}/{hk}: rel_l2={rl2:.3e} max_abs={mabs:.3e} lse_err={lerr:.3e}")
 
 
+@pytest.mark.parametrize("name", ["three_chunks_ragged", "kv_cache_mixed", "multi_tile_chunk_aligned"])
+def test_bf16_static_path_past_its_first_limit(name):
+    """Unit gains with one query channel at 3.1: the gains bound
+    d * 3.1 * scale * log2 e * 1.02 = 52 log2 units lies past the static
+    instance's first limit of 40 and inside its range (at most 64), so the
+    static instance runs where the online one used to. One channel keeps the
+    actual logits moderate, so the fixed tolerances apply. (With every
+    channel's gain product near 3, both instances miss them alike: the
+    logits' bf16 rounding grows with their size.)"""
+    lay = dict(SMALL)[name]
+    for hq, hk in ((6, 2), (8, 1)):
+        inp = make_inputs(lay, hq, hk, 128, "bf16", "ones", 17)
+        inp["q_gain"][0] = 3.1
+        sc = 1.0 / math.sqrt(128)
+        got_out, got_lse = run_gpu(lay, inp, hq, hk, 128, "bf16", 1e-6, sc)
+        ref_out, ref_lse = oracle.attention(inp["q"], inp["k"], inp["v"], inp["q_gain"], inp["k_gain"], 1e-6, sc, lay)
+        rl2, mabs, lerr = compare(got_out, got_lse, ref_out, ref_lse, "bf16")
+        log(f"static past 40 {name} {hq}/{hk}: rel_l2={rl2:.3e} max_abs={mabs:.3e} lse_err={lerr:.3e}")
+
+
 def test_bf16_split_online_path():
     """Pieces on the online-softmax path carry their own reference maxima."""
     lay = split_window_layout()
