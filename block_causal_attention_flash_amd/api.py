@@ -168,20 +168,21 @@ def magi_attn_bwd(handle: int, q, k, v, out, lse, dout, q_gain=None, k_gain=None
             raise ValueError(f"{name} must be a contiguous GPU tensor")
     d = q.shape[-1]
     dev = q.device
-    dq = torch.empty_like(q) if dq is None else dq
-    dk = torch.empty_like(k) if dk is None else dk
-    dv = torch.empty_like(v) if dv is None else dv
-    dq_gain = torch.empty(d, dtype=torch.float32, device=dev) if dq_gain is None else dq_gain
-    dk_gain = torch.empty(d, dtype=torch.float32, device=dev) if dk_gain is None else dk_gain
-    qg = _gain(q_gain, d, dev)
-    kg = _gain(k_gain, d, dev)
     sc = (1.0 / d ** 0.5) if scale is None else float(scale)
-    if workspace is None:                              # (the library checks a given workspace's size)
-        workspace = torch.empty(max(magi_attn_bwd_workspace_size(handle), 16), dtype=torch.uint8, device=dev)
-    ws_bytes = workspace.numel() * workspace.element_size()
-    io = _abi.BwdIO(*(t.data_ptr() for t in (q, k, v, qg, kg, out, lse, dout, dq, dk, dv, dq_gain, dk_gain)))
-    _check(lib, lib.magi_attn_bwd(handle, ctypes.byref(io), float(rms_eps), sc, workspace.data_ptr(), ws_bytes,
-                                  _stream_ptr(stream, dev)))
+    with _alloc_on(stream):
+        dq = torch.empty_like(q) if dq is None else dq
+        dk = torch.empty_like(k) if dk is None else dk
+        dv = torch.empty_like(v) if dv is None else dv
+        dq_gain = torch.empty(d, dtype=torch.float32, device=dev) if dq_gain is None else dq_gain
+        dk_gain = torch.empty(d, dtype=torch.float32, device=dev) if dk_gain is None else dk_gain
+        qg = _gain(q_gain, d, dev)
+        kg = _gain(k_gain, d, dev)
+        if workspace is None:                          # (the library checks a given workspace's size)
+            workspace = torch.empty(max(magi_attn_bwd_workspace_size(handle), 16), dtype=torch.uint8, device=dev)
+        ws_bytes = workspace.numel() * workspace.element_size()
+        io = _abi.BwdIO(*(t.data_ptr() for t in (q, k, v, qg, kg, out, lse, dout, dq, dk, dv, dq_gain, dk_gain)))
+        _check(lib, lib.magi_attn_bwd(handle, ctypes.byref(io), float(rms_eps), sc, workspace.data_ptr(), ws_bytes,
+                                      _stream_ptr(stream, dev)))
     return dq, dk, dv, dq_gain, dk_gain
 
 
@@ -217,6 +218,16 @@ def magi_attn_workspace_size(handle: int) -> int:
     return n.value
 
 
+def _alloc_on(stream):
+    """Context in which the wrappers allocate their temporaries and default
+    outputs: the caller's `stream`, so that torch's caching allocator ties
+    that memory to the stream the kernels read and write it on (it is reused
+    only after the stream's work, never under it). None: the current stream."""
+    import contextlib
+    import torch
+    return contextlib.nullcontext() if stream is None else torch.cuda.stream(stream)
+
+
 def _stream_ptr(stream, device):
     import torch
     s = torch.cuda.current_stream(device) if stream is None else stream
@@ -245,19 +256,20 @@ def magi_attn_fwd(handle: int, q, k, v, q_gain=None, k_gain=None, rms_eps: float
         if not t.is_cuda or not t.is_contiguous():
             raise ValueError(f"{name} must be a contiguous GPU tensor")
     d = q.shape[-1]
-    if out is None:
-        out = torch.empty_like(q)
-    if lse is None:
-        lse = torch.empty((q.shape[1], q.shape[0]), dtype=torch.float32, device=q.device)
-    qg = _gain(q_gain, d, q.device)
-    kg = _gain(k_gain, d, q.device)
     sc = (1.0 / d ** 0.5) if scale is None else float(scale)
-    if workspace is None:                              # (the library checks a given workspace's size)
-        workspace = torch.empty(max(magi_attn_workspace_size(handle), 16), dtype=torch.uint8, device=q.device)
-    ws_bytes = workspace.numel() * workspace.element_size()
-    _check(lib, lib.magi_attn_fwd(handle, q.data_ptr(), k.data_ptr(), v.data_ptr(), qg.data_ptr(), kg.data_ptr(),
-                                  float(rms_eps), sc, out.data_ptr(), lse.data_ptr(), workspace.data_ptr(), ws_bytes,
-                                  _stream_ptr(stream, q.device)))
+    with _alloc_on(stream):
+        if out is None:
+            out = torch.empty_like(q)
+        if lse is None:
+            lse = torch.empty((q.shape[1], q.shape[0]), dtype=torch.float32, device=q.device)
+        qg = _gain(q_gain, d, q.device)
+        kg = _gain(k_gain, d, q.device)
+        if workspace is None:                          # (the library checks a given workspace's size)
+            workspace = torch.empty(max(magi_attn_workspace_size(handle), 16), dtype=torch.uint8, device=q.device)
+        ws_bytes = workspace.numel() * workspace.element_size()
+        _check(lib, lib.magi_attn_fwd(handle, q.data_ptr(), k.data_ptr(), v.data_ptr(), qg.data_ptr(), kg.data_ptr(),
+                                      float(rms_eps), sc, out.data_ptr(), lse.data_ptr(), workspace.data_ptr(),
+                                      ws_bytes, _stream_ptr(stream, q.device)))
     return out, lse
 
 
@@ -276,21 +288,22 @@ def magi_attn_fwd_parallel(handle: int, q, k, v, q_x, k_x, v_x, q_gain=None, k_g
     d = q.shape[-1]
     dev = q.device
     lse_shape = (q.shape[1], q.shape[0])
-    out = torch.empty_like(q) if out is None else out
-    lse = torch.empty(lse_shape, dtype=torch.float32, device=dev) if lse is None else lse
-    out_x = torch.empty_like(q_x) if out_x is None else out_x
-    lse_x = torch.empty(lse_shape, dtype=torch.float32, device=dev) if lse_x is None else lse_x
-    gains = [_gain(g, d, dev) for g in (q_gain, k_gain, q_gain_x, k_gain_x)]
     sc = (1.0 / d ** 0.5) if scale is None else float(scale)
     scx = (1.0 / d ** 0.5) if scale_x is None else float(scale_x)
-    if workspace is None:                              # (the library checks a given workspace's size)
-        workspace = torch.empty(max(magi_attn_workspace_size(handle), 16), dtype=torch.uint8, device=dev)
-    ws_bytes = workspace.numel() * workspace.element_size()
-    io = _abi.ParallelIO(q.data_ptr(), k.data_ptr(), v.data_ptr(), gains[0].data_ptr(), gains[1].data_ptr(), sc,
-                         out.data_ptr(), lse.data_ptr(), q_x.data_ptr(), k_x.data_ptr(), v_x.data_ptr(),
-                         gains[2].data_ptr(), gains[3].data_ptr(), scx, out_x.data_ptr(), lse_x.data_ptr())
-    _check(lib, lib.magi_attn_fwd_parallel(handle, ctypes.byref(io), float(rms_eps), workspace.data_ptr(), ws_bytes,
-                                           _stream_ptr(stream, dev)))
+    with _alloc_on(stream):
+        out = torch.empty_like(q) if out is None else out
+        lse = torch.empty(lse_shape, dtype=torch.float32, device=dev) if lse is None else lse
+        out_x = torch.empty_like(q_x) if out_x is None else out_x
+        lse_x = torch.empty(lse_shape, dtype=torch.float32, device=dev) if lse_x is None else lse_x
+        gains = [_gain(g, d, dev) for g in (q_gain, k_gain, q_gain_x, k_gain_x)]
+        if workspace is None:                          # (the library checks a given workspace's size)
+            workspace = torch.empty(max(magi_attn_workspace_size(handle), 16), dtype=torch.uint8, device=dev)
+        ws_bytes = workspace.numel() * workspace.element_size()
+        io = _abi.ParallelIO(q.data_ptr(), k.data_ptr(), v.data_ptr(), gains[0].data_ptr(), gains[1].data_ptr(), sc,
+                             out.data_ptr(), lse.data_ptr(), q_x.data_ptr(), k_x.data_ptr(), v_x.data_ptr(),
+                             gains[2].data_ptr(), gains[3].data_ptr(), scx, out_x.data_ptr(), lse_x.data_ptr())
+        _check(lib, lib.magi_attn_fwd_parallel(handle, ctypes.byref(io), float(rms_eps), workspace.data_ptr(),
+                                               ws_bytes, _stream_ptr(stream, dev)))
     return out, lse, out_x, lse_x
 
 
@@ -302,17 +315,18 @@ def magi_attn_fwd_simple(q, k, v, chunk_offsets: Sequence[int], q_gain=None, k_g
     offs = _arr(chunk_offsets)
     d = q.shape[-1]
     dt = {torch.bfloat16: _abi.MAGI_DTYPE_BF16, torch.float32: _abi.MAGI_DTYPE_FP32}[q.dtype]
-    if out is None:
-        out = torch.empty_like(q)
-    if lse is None:
-        lse = torch.empty((q.shape[1], q.shape[0]), dtype=torch.float32, device=q.device)
-    qg = _gain(q_gain, d, q.device)
-    kg = _gain(k_gain, d, q.device)
     sc = (1.0 / d ** 0.5) if scale is None else float(scale)
-    _check(lib, lib.magi_attn_fwd_simple(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
-                                         offs.ctypes.data_as(_abi._i32p), len(offs) - 1, q.shape[1], k.shape[1], d, dt,
-                                         qg.data_ptr(), kg.data_ptr(), float(rms_eps), sc,
-                                         _stream_ptr(stream, q.device)))
+    with _alloc_on(stream):
+        if out is None:
+            out = torch.empty_like(q)
+        if lse is None:
+            lse = torch.empty((q.shape[1], q.shape[0]), dtype=torch.float32, device=q.device)
+        qg = _gain(q_gain, d, q.device)
+        kg = _gain(k_gain, d, q.device)
+        _check(lib, lib.magi_attn_fwd_simple(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                                             lse.data_ptr(), offs.ctypes.data_as(_abi._i32p), len(offs) - 1,
+                                             q.shape[1], k.shape[1], d, dt, qg.data_ptr(), kg.data_ptr(),
+                                             float(rms_eps), sc, _stream_ptr(stream, q.device)))
     return out, lse
 
 

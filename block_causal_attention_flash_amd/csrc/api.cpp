@@ -343,7 +343,8 @@ magi_status_t magi_attn_plan_destroy(magi_attn_plan_t* plan) {
 magi_status_t magi_attn_workspace_size(const magi_attn_plan_t* plan, size_t* bytes) {
   if (!plan || !bytes) return fail(MAGI_ERR_INVALID_ARG, "plan or bytes is NULL");
   const auto& H = plan->host;
-  *bytes = H.dtype == MAGI_DTYPE_BF16 ? magi::workspace_bytes_bf16(H.n_kt_img, H.hk, H.n_slots) : 0;
+  *bytes = H.dtype == MAGI_DTYPE_BF16 ? magi::workspace_bytes_bf16(H.n_kt_img, H.hk, H.n_slots, int(H.items.size()))
+                                      : 0;
   return MAGI_OK;
 }
 

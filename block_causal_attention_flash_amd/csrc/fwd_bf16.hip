@@ -30,19 +30,23 @@
 // Queries are normalised in the prologue (RMS over head_dim, times
 // g_q * g_k * scale * log2 e) and held in registers as bf16 MFMA operands.
 //
-// Softmax. QK-normalisation bounds every logit: |s_ij| <= |q'_i| |k_hat_j|
-// <= d max_c |g_q,c g_k,c| scale log2 e (the normalised rows have at most
-// norm sqrt(d)). When that bound of the item's gains is at most 64 (log2
-// units), the item uses exp2(s) directly, with no running maximum and no
-// rescaling: softmax is invariant to the shift, P = 2^s stays a normal number
-// in fp32 and bf16, and with at most 2^21 keys the row sum stays below 2^85,
-// so O = sum P v cannot overflow fp32 for |v| < 2^40. Otherwise it keeps a
-// running row maximum and rescales its
-// accumulator only when the maximum has grown by more than 2^8. The two cases
-// are two instances of the kernel, both launched: each workgroup takes the
-// gains of its phase, and the instance that does not match exits at once.
-// (One kernel holding both loops paid for the online loop's registers with
-// spills in the static one, 2.5% of its time.)
+// Softmax. QK-normalisation bounds every logit: s_ij = <q'_i, k_hat_j> <=
+// |q'_i| |k_hat_j| <= |q'_i| sqrt(d) (a normalised key has norm at most
+// sqrt(d)). Each wave takes B = the largest such bound of its 48 rows (log2
+// units, with 1% for the bf16 rounding of k_hat and fp32 sums) and computes
+// P = exp2(s - b) with the fixed shift b = max(0, B - 64), which the S products
+// start from (their accumulators begin at -b): no running maximum, no
+// rescaling and no VALU work for it. Softmax is invariant to the shift; P <=
+// 2^64, and with fewer than 2^23 keys (the 2 GiB limit on K) the row sum
+// stays below 2^87, so O = sum P v cannot overflow fp32 for |v| < 2^40. When
+// B is far above the actual logits (gains much larger than the data's
+// alignment uses, or keys pointing away from the query) a row's sum can fall
+// out of [2^-100, 2^100); its wave then flags the work item, and a second
+// instance of the kernel, launched after the first, redoes flagged items with
+// a running row maximum, rescaling its accumulator only when the maximum has
+// grown by more than 2^8. Unflagged items leave that instance at once. (One
+// kernel holding both loops paid for the online loop's registers with spills
+// in the static one.)
 //
 // The same kernel runs the block's text cross-attention (paperlayer §2.2.2,
 // §2.2.3; paper-notes §3.2.2, §3.2.6): only the key stream and the per-row key
@@ -91,7 +95,10 @@ constexpr int WAIT_YOUNGER = 7;
 constexpr unsigned kNoTile = 0x80000000u;             // scalar offset past any tile image buffer (< 2 GiB): zeros
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
-constexpr float kStaticBound = 64.0f;
+constexpr float kStaticBound = 64.0f;                // largest exponent of P on the static path
+constexpr float kBoundSlack = 1.01f;                  // bf16 rounding of k_hat (2^-8), fp32 sums
+constexpr float kMinRowSum = 0x1p-100f;               // static-path row sums outside [2^-100, 2^100):
+constexpr float kMaxRowSum = 0x1p100f;                //   the item goes to the running-maximum instance
 constexpr float kRescaleSlack = 8.0f;
 constexpr float kNegInf = -__builtin_inff();
 
@@ -205,6 +212,7 @@ struct WaveState {
   f32x4 o[NRB][8];       // O^T accumulators: row (l & 15), dims 16 db + 4 (l >> 4) + i
   bf16x8 p[NRB];         // P of the previous tile (B operands of P V)
   bf16x8 kpre[NPRE];     // first K fragments of the current tile, read before the barrier
+  f32x4 s0;              // initial S accumulator: -b, the wave's softmax shift (0 on the online path)
   float lsum[NRB];       // partial row sums over this lane's keys
   float m[NRB];          // online path: reference maximum (log2 units)
   int lo[NRB], hi[NRB];  // key bounds of the lane's rows
@@ -220,7 +228,7 @@ __device__ __forceinline__ bf16x8 k_frag(const LaneOffsets& lo, int kstage, int 
 __device__ __forceinline__ void qk_tile(int kstage, const LaneOffsets& lo, const WaveState& st,
                                         f32x4 (&s)[NRB][2]) {
 #pragma unroll
-  for (int rb = 0; rb < NRB; ++rb) s[rb][0] = s[rb][1] = f32x4{};
+  for (int rb = 0; rb < NRB; ++rb) s[rb][0] = s[rb][1] = st.s0;
 #pragma unroll
   for (int f = 0; f < 8; ++f) {
     const int ks = f >> 1, kb = f & 1;
@@ -288,7 +296,8 @@ __device__ __forceinline__ void softmax_tile(f32x4 (&s)[NRB][2], int kt, WaveSta
 #pragma unroll
         for (int i = 0; i < 4; ++i) s[rb][kb][i] -= m_use;
     }
-    const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+    // Row sums in fp32 of the unrounded exponentials (v_dot2 of the bf16 P
+    // shares the matrix cores' issue and cost more alongside the products).
     float ls = 0.0f;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
@@ -299,7 +308,7 @@ __device__ __forceinline__ void softmax_tile(f32x4 (&s)[NRB][2], int kt, WaveSta
         const bf16x2 pp = {(__bf16)e0, (__bf16)e1};
         p[rb][kb * 4 + i] = pp[0];
         p[rb][kb * 4 + i + 1] = pp[1];
-        ls = __builtin_amdgcn_fdot2_f32_bf16(pp, ones, ls, false);
+        ls += e0 + e1;
       }
     st.lsum[rb] = st.lsum[rb] * alpha[rb] + ls;
   }
@@ -410,6 +419,17 @@ __device__ __forceinline__ void unrolled_steps(const LoopCtx& c, const LaneOffse
   if constexpr (U + 1 < NSTAGE) unrolled_steps<STATIC, U + 1>(c, lo, st, i0, so, lane);
 }
 
+// Whether keys [lo, hi) meet any tile of the item's list (used only for rows
+// whose static-path sum is out of range in items without full tiles: a full
+// tile is seen by every row of the query tile).
+__device__ __forceinline__ bool row_sees_a_tile(const LoopCtx& c, int lo, int hi) {
+  for (int i = 0; i < c.n_tiles; ++i) {
+    const int k0 = (c.tiles[i] >> 1) * BN;
+    if (k0 < hi && k0 + BN > lo) return true;
+  }
+  return false;
+}
+
 // Full tiles first, then boundary tiles. Full tiles run NSTAGE at a time
 // (NSTAGE is even, so groups start on even steps) with compile-time stages and
 // their copy offsets loaded once per group; the rest one by one. Copy offsets
@@ -460,19 +480,12 @@ fwd_bf16_d128_kernel(FwdParams prm, const int4* __restrict__ items, const int* _
   const int lane = tid & 63;
   const int g = lane >> 4;
 
-  // ---- static or online softmax, from the gains of the item's phase (every
-  // wave reduces all D of them; the result is uniform over the grid's phase)
-  {
-    const float* gq = px ? prm.q_gain_x : prm.q_gain;
-    const float* gk = px ? prm.k_gain_x : prm.k_gain;
-    float gm = 0.0f;
-#pragma unroll
-    for (int c = lane; c < D; c += 64) gm = fmaxf(gm, __builtin_fabsf(gq[c] * gk[c]));
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) gm = fmaxf(gm, __shfl_xor(gm, o, 64));
-    const float bound = float(D) * gm * __builtin_fabsf((px ? prm.scale_x : prm.scale) * kLog2e) * 1.02f;
-    const bool stat = bound <= kStaticBound;          // false for NaN gains
-    if (stat != STATIC) return;
+  // ---- the running-maximum instance takes only the items that the static
+  // instance (launched first, on the same stream) flagged
+  if (!STATIC) {
+    const int4* fl = reinterpret_cast<const int4*>(prm.item_flag + size_t(blockIdx.x) * NWAVE);
+    const int4 f0 = fl[0], f1 = fl[1];
+    if ((f0.x | f0.y | f0.z | f0.w | f1.x | f1.y | f1.z | f1.w) == 0) return;
   }
   const int kvh = item.y >> 16, h0 = item.y & 0xffff;
   const int tb = item.z, n_tiles = item.w - item.z;
@@ -550,6 +563,25 @@ fwd_bf16_d128_kernel(FwdParams prm, const int4* __restrict__ items, const int* _
     st.lsum[rb] = 0.0f;
     st.m[rb] = kNegInf;
   }
+  // ---- the wave's softmax shift b = max(0, B - 64), B = max over its rows of
+  // |q'| sqrt(d) (1 + slack), from the rounded operands the products use
+  float shift = 0.0f;
+  if (STATIC) {
+    float qq = 0.0f;
+#pragma unroll
+    for (int rb = 0; rb < NRB; ++rb) {
+      float ss = 0.0f;
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) ss = sumsq8(st.qf[rb][ks], ss);
+      qq = fmaxf(qq, sum_groups(ss));
+    }
+#pragma unroll
+    for (int o = 1; o < 16; o <<= 1) qq = fmaxf(qq, __shfl_xor(qq, o, 64));
+    const float bound = __builtin_sqrtf(qq * float(D)) * kBoundSlack;
+    shift = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(
+                                          __builtin_bit_cast(int, fmaxf(0.0f, bound - kStaticBound))));
+  }
+  st.s0 = f32x4{-shift, -shift, -shift, -shift};
   run_tiles<STATIC>(ctx, lo, n_full, st, lane);
 
   // ---- epilogue: lane l holds dims 16 db + 4 g + i of row (l & 15) per block
@@ -561,16 +593,30 @@ fwd_bf16_d128_kernel(FwdParams prm, const int4* __restrict__ items, const int* _
     tok[rb] = item.x + r % prm.tile_q;
     valid[rb] = tok[rb] < prm.tq;
   }
+  float lsr[NRB];
+#pragma unroll
+  for (int rb = 0; rb < NRB; ++rb) lsr[rb] = sum_groups(st.lsum[rb]);
+  if (STATIC) {
+    // a row with keys whose sum left [2^-100, 2^100) flags the item for the
+    // running-maximum instance (every wave writes its flag on every call)
+    bool bad = false;
+#pragma unroll
+    for (int rb = 0; rb < NRB; ++rb)
+      if (valid[rb] && !(lsr[rb] >= kMinRowSum && lsr[rb] < kMaxRowSum))
+        bad |= n_full > 0 || row_sees_a_tile(ctx, st.lo[rb], st.hi[rb]);
+    const bool any_bad = __builtin_amdgcn_ballot_w64(bad) != 0;
+    if (lane == 0) prm.item_flag[size_t(blockIdx.x) * NWAVE + wave] = any_bad ? 1 : 0;
+  }
   if (slot >= 0) {
-    // piece of a split item: unnormalised O, reference maximum (0 on the
-    // static path: exp2(s) itself) and row sum, for the merge kernel
+    // piece of a split item: unnormalised O, reference maximum (the shift on
+    // the static path: P = exp2(s - b)) and row sum, for the merge kernel
 #pragma unroll
     for (int rb = 0; rb < NRB; ++rb) {
-      const float lsum = sum_groups(st.lsum[rb]);
+      const float lsum = lsr[rb];
       const size_t r = size_t(slot) * ROWS + size_t((wave * NRB + rb) * 16 + (lane & 15));
 #pragma unroll
       for (int db = 0; db < 8; ++db) *reinterpret_cast<f32x4*>(prm.part_o + r * D + db * 16 + g * 4) = st.o[rb][db];
-      if (g == 0) *reinterpret_cast<float2*>(prm.part_ml + r * 2) = float2{STATIC ? 0.0f : st.m[rb], lsum};
+      if (g == 0) *reinterpret_cast<float2*>(prm.part_ml + r * 2) = float2{STATIC ? shift : st.m[rb], lsum};
     }
     return;
   }
@@ -578,7 +624,7 @@ fwd_bf16_d128_kernel(FwdParams prm, const int4* __restrict__ items, const int* _
   float* const lbase = px ? prm.lsex : prm.lse;
 #pragma unroll
   for (int rb = 0; rb < NRB; ++rb) {
-    const float lsum = sum_groups(st.lsum[rb]);
+    const float lsum = lsr[rb];
     if (valid[rb]) {
       const bool any = lsum > 0.0f;                     // false only for a row that sees no key
       const float inv = any ? 1.0f / lsum : 0.0f;
@@ -592,7 +638,7 @@ fwd_bf16_d128_kernel(FwdParams prm, const int4* __restrict__ items, const int* _
       }
       if (g == 0) {
         const float l2 = __builtin_amdgcn_logf(lsum);   // log2
-        const float lse = !any ? kNegInf : STATIC ? l2 * kLn2 : (st.m[rb] + l2) * kLn2;
+        const float lse = !any ? kNegInf : ((STATIC ? shift : st.m[rb]) + l2) * kLn2;
         lbase[size_t(head[rb]) * prm.tq + tok[rb]] = lse;
       }
     }
@@ -710,9 +756,10 @@ size_t image_bytes_bf16(long long n_kt_img, int hk) { return size_t(n_kt_img) * 
 
 }  // namespace
 
-size_t workspace_bytes_bf16(long long n_kt_img, int hk, int n_slots) {
-  // K-hat images, V^T images, partial O, partial (m, l)
-  return 2 * image_bytes_bf16(n_kt_img, hk) + size_t(n_slots) * ROWS * (D + 2) * sizeof(float);
+size_t workspace_bytes_bf16(long long n_kt_img, int hk, int n_slots, int n_items) {
+  // K-hat images, V^T images, partial O, partial (m, l), per-wave item flags
+  return 2 * image_bytes_bf16(n_kt_img, hk) + size_t(n_slots) * ROWS * (D + 2) * sizeof(float) +
+         size_t(n_items) * NWAVE * sizeof(int);
 }
 
 hipError_t launch_fwd_bf16_d128(const FwdParams& prm, int n_items, int n_merges, int n_slots, hipStream_t stream) {
@@ -720,6 +767,7 @@ hipError_t launch_fwd_bf16_d128(const FwdParams& prm, int n_items, int n_merges,
   const size_t img = image_bytes_bf16(p.n_kt_img, p.hk);
   p.part_o = reinterpret_cast<float*>(static_cast<unsigned char*>(p.ws) + 2 * img);
   p.part_ml = p.part_o + size_t(n_slots) * ROWS * D;
+  p.item_flag = reinterpret_cast<int*>(p.part_ml + size_t(n_slots) * ROWS * 2);
   if (n_items > 0) {
     if (p.n_kt_img > 0) {
       unsigned char* kimg = static_cast<unsigned char*>(p.ws);
@@ -731,7 +779,8 @@ hipError_t launch_fwd_bf16_d128(const FwdParams& prm, int n_items, int n_merges,
       const hipError_t e = hipGetLastError();
       if (e != hipSuccess) return e;
     }
-    // Both instances: each workgroup runs in the one that matches its gains.
+    // The static instance runs every item and flags the ones whose row sums
+    // it lost; the running-maximum instance redoes only those.
     hipLaunchKernelGGL(fwd_bf16_d128_kernel<true>, dim3(n_items), dim3(NTHR), 0, stream, p, p.items, p.tiles,
                        p.soffs, p.rows);
     hipLaunchKernelGGL(fwd_bf16_d128_kernel<false>, dim3(n_items), dim3(NTHR), 0, stream, p, p.items, p.tiles,

@@ -28,6 +28,8 @@ struct FwdParams {
   const int4* merges;    // MergeItem[n_merges], two int4 each: split items and key-less rows
   float* part_o;         // bf16 path, set by the launcher: partial O of each slot, [slot][384 rows][d] (workspace)
   float* part_ml;        // bf16 path, set by the launcher: partial (m, l) of each slot, [slot][384 rows][2]
+  int* item_flag;        // bf16 path, set by the launcher: per (work item, wave) 1 when the static softmax lost a
+                         // row's sum and the running-maximum instance must redo the item (workspace)
   float eps;
   float scale;           // softmax temperature on <q_hat, k_hat>
   int tq, tk, hq, hk;
@@ -103,7 +105,7 @@ size_t bwd_workspace_bytes_fp32(long long tq, long long tk, int hq, int hk, int 
                                 int n_kv_items);
 
 hipError_t launch_fwd_bf16_d128(const FwdParams& p, int n_items, int n_merges, int n_slots, hipStream_t stream);
-size_t workspace_bytes_bf16(long long n_kt_img, int hk, int n_slots);
+size_t workspace_bytes_bf16(long long n_kt_img, int hk, int n_slots, int n_items);
 hipError_t launch_fwd_fp32(const FwdParams& p, int head_dim, int n_items, int n_merges, hipStream_t stream);
 
 }  // namespace magi
