@@ -38,6 +38,7 @@
 #include "kernels.hpp"
 
 #include <algorithm>
+#include <climits>
 #include <cmath>
 #include <cstring>
 #include <numeric>
@@ -96,6 +97,9 @@ magi_status_t validate_layout(const magi_attn_layout_t* L, std::string& err) {
   const int64_t q_elems = int64_t(L->q_offsets[L->n_chunks]) * L->n_q_heads;
   if (kv_bytes >= (int64_t(1) << 31)) { err = "K/V tensors must be smaller than 2 GiB each"; return MAGI_ERR_UNSUPPORTED; }
   if (q_elems >= (int64_t(1) << 31)) { err = "T_q * n_q_heads must be below 2^31"; return MAGI_ERR_UNSUPPORTED; }
+  // token indices plus a tile length stay far from int32 overflow, and the
+  // per-row host tables stay below 512 MiB
+  if (L->q_offsets[L->n_chunks] >= (int32_t(1) << 26)) { err = "T_q must be below 2^26 tokens"; return MAGI_ERR_UNSUPPORTED; }
   return MAGI_OK;
 }
 
@@ -287,7 +291,6 @@ int64_t split_piece_tiles(int64_t n_whole, int64_t total_cost) {
 
 magi_status_t build_host_plan(int32_t kind, const magi_attn_layout_t* L, const magi_attn_text_t* T,
                               const Tiling& tiling, HostPlan& P, std::string& err, bool allow_split) {
-  (void)err;
   const int32_t* kv = L->kv_offsets ? L->kv_offsets : L->q_offsets;
   P.kind = kind;
   P.n_phases = kind == kPlanParallel ? 2 : 1;
@@ -326,6 +329,26 @@ magi_status_t build_host_plan(int32_t kind, const magi_attn_layout_t* L, const m
   for (const RowBounds& b : P.rows) S.unmasked_pairs += int64_t(b.hi - b.lo);
 
   const int64_t n_lists = P.n_phases * n_qt;
+  // The kernels index the tile lists with int32: bound every list by the key
+  // tiles its rows' [lo, hi) span (plus the padding), in int64, and refuse the
+  // layout before building anything that could pass INT32_MAX entries.
+  {
+    int64_t bound = 0;
+    for (int ph = 0; ph < P.n_phases; ++ph)
+      for (int64_t qt = 0; qt < n_qt; ++qt) {
+        const int64_t r0 = qt * bm, r1 = std::min<int64_t>(P.tq, r0 + bm);
+        int64_t lo = INT64_MAX, hi = 0;
+        for (int64_t r = r0; r < r1; ++r) {
+          const RowBounds& b = P.rows[size_t(ph * P.tq + r)];
+          if (b.hi > b.lo) { lo = std::min<int64_t>(lo, b.lo); hi = std::max<int64_t>(hi, b.hi); }
+        }
+        bound += kTilePad + (hi > lo ? (hi + bn - 1) / bn - lo / bn : 0);
+      }
+    if (bound > INT32_MAX) {
+      err = "the layout's tile lists would pass 2^31 entries (" + std::to_string(bound) + ")";
+      return MAGI_ERR_UNSUPPORTED;
+    }
+  }
   P.tile_codes.clear();
   P.qt_tiles.assign(n_lists + 1, 0);
   P.qt_ntiles.assign(n_lists, 0);
@@ -508,6 +531,26 @@ magi_status_t build_bwd_plan(const magi_attn_layout_t* L, const magi_attn_text_t
 
   // Per key block: the token tiles that see any of its keys, full first.
   const int64_t n_kb = (tk + kb_size - 1) / kb_size;
+  const int64_t n_tt_all = (tq + tt_size - 1) / tt_size;
+  {
+    // int32 list indices on the device: bound the lists as the forward's are
+    int64_t bound = 0;
+    for (int64_t kb = 0; kb < n_kb; ++kb) {
+      int64_t lo = INT64_MAX, hi = 0, glo = INT64_MAX, ghi = 0;
+      for (int64_t j = kb * kb_size; j < std::min<int64_t>(tk, (kb + 1) * kb_size); ++j) {
+        const KeyBounds& b = B.key_rows[size_t(j)];
+        if (b.hi > b.lo) { lo = std::min<int64_t>(lo, b.lo); hi = std::max<int64_t>(hi, b.hi); }
+        if (b.ghi > b.glo) { glo = std::min<int64_t>(glo, b.glo); ghi = std::max<int64_t>(ghi, b.ghi); }
+      }
+      const int64_t a = hi > lo ? (hi + tt_size - 1) / tt_size - lo / tt_size : 0;
+      const int64_t c = ghi > glo ? (ghi + tt_size - 1) / tt_size - glo / tt_size : 0;
+      bound += kTilePad + std::min<int64_t>(n_tt_all, a + c);
+    }
+    if (bound > INT32_MAX) {
+      err = "the layout's backward tile lists would pass 2^31 entries (" + std::to_string(bound) + ")";
+      return MAGI_ERR_UNSUPPORTED;
+    }
+  }
   std::vector<int32_t> kb_begin(n_kb), kb_n(n_kb), kb_full(n_kb);
   std::vector<int32_t> masked_codes;
   std::vector<KeyBounds> iv;
@@ -525,8 +568,10 @@ magi_status_t build_bwd_plan(const magi_attn_layout_t* L, const magi_attn_text_t
     // candidate token tiles: those touching any key's ranges
     cand.assign(n_tt, 0);
     for (const KeyBounds& b : iv) {
-      if (b.hi > b.lo) for (int64_t tt = b.lo / tt_size; tt < (b.hi + tt_size - 1) / tt_size; ++tt) cand[tt] = 1;
-      if (b.ghi > b.glo) for (int64_t tt = b.glo / tt_size; tt < (b.ghi + tt_size - 1) / tt_size; ++tt) cand[tt] = 1;
+      if (b.hi > b.lo)
+        for (int64_t tt = b.lo / tt_size; tt < (int64_t(b.hi) + tt_size - 1) / tt_size; ++tt) cand[tt] = 1;
+      if (b.ghi > b.glo)
+        for (int64_t tt = b.glo / tt_size; tt < (int64_t(b.ghi) + tt_size - 1) / tt_size; ++tt) cand[tt] = 1;
     }
     kb_begin[kb] = int32_t(B.kv_tiles.size());
     masked_codes.clear();

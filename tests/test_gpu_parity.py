@@ -14,6 +14,7 @@ import pytest
 import torch
 
 import oracle
+from bf16_error_model import check as check_derived, predicted_errors
 from workloads import CONFIGS, Layout, get_config, layout_from_chunks, make_inputs, streaming_layout
 
 pytestmark = pytest.mark.gpu
@@ -135,13 +136,10 @@ def test_bf16_split_key_ranges_merge():
 
 @pytest.mark.parametrize("name", ["three_chunks_ragged", "kv_cache_mixed", "multi_tile_chunk_aligned"])
 def test_bf16_static_path_past_its_first_limit(name):
-    """Unit gains with one query channel at 3.1: the gains bound
-    d * 3.1 * scale * log2 e * 1.02 = 52 log2 units lies past the static
-    instance's first limit of 40 and inside its range (at most 64), so the
-    static instance runs where the online one used to. One channel keeps the
-    actual logits moderate, so the fixed tolerances apply. (With every
-    channel's gain product near 3, both instances miss them alike: the
-    logits' bf16 rounding grows with their size.)"""
+    """Unit gains with one query channel at 3.1: a large worst-case gain on
+    one channel keeps the actual logits moderate, so the fixed tolerances
+    apply (with every channel's gain product near 3 they do not: the logits'
+    bf16 rounding grows with their size, see the derived-tolerance test)."""
     lay = dict(SMALL)[name]
     for hq, hk in ((6, 2), (8, 1)):
         inp = make_inputs(lay, hq, hk, 128, "bf16", "ones", 17)
@@ -183,10 +181,10 @@ def test_bf16_online_softmax_path():
 
 
 def test_bf16_large_logits_stay_finite():
-    """Gains x2.5 make the logits ~6.8x larger than with N(0,1) inputs and unit
-    gains. Rounding the normalised query to bf16 (relative 2^-9) then moves a
-    logit s by about |s| 2^-9, so the log-sum-exp is held to a relative 2^-7
-    and the output to relative L2 2e-2 here."""
+    """U(0.5, 1.5) gains x2.5 (products up to 14) make the logits up to ~14x
+    those of unit gains. The outputs stay finite and meet the derived
+    tolerances of the bf16 error model: the operands' bf16 rounding is
+    relative, so the logits' errors grow with the logits."""
     log("bf16 large logits")
     lay = layout_from_chunks([[130, 70], [190]])
     inp = make_inputs(lay, 6, 2, 128, "bf16", "uniform", 11)
@@ -194,10 +192,49 @@ def test_bf16_large_logits_stay_finite():
     inp["k_gain"] = inp["k_gain"] * 2.5
     sc = 1 / math.sqrt(128)
     go, gl = run_gpu(lay, inp, 6, 2, 128, "bf16", 1e-6, sc)
-    ro, rl = oracle.attention(inp["q"], inp["k"], inp["v"], inp["q_gain"], inp["k_gain"], 1e-6, sc, lay)
-    assert np.all(np.isfinite(go)) and np.all(np.isfinite(gl))
-    assert np.max(np.abs(gl - rl) / np.maximum(np.abs(rl), 1.0)) <= 2.0 ** -7
-    assert np.linalg.norm(go - ro) / np.linalg.norm(ro) <= 2e-2
+    ro, rl, e, sig = predicted_errors(inp["q"], inp["k"], inp["v"], inp["q_gain"], inp["k_gain"], 1e-6, sc, lay)
+    rl2, mabs, lerr, ratios = check_derived(go, gl, ro, rl, e, sig)
+    log(f"large logits: rel_l2={rl2:.3e} max_abs={mabs:.3e} lse_err={lerr:.3e} error/tolerance={ratios}")
+
+
+# ------------------------------------------------------------------ uniform gain products: fixed and derived tolerances
+
+GAIN_LAYOUTS = ["three_chunks_ragged", "kv_cache_mixed", "multi_tile_chunk_aligned"]
+
+
+@pytest.mark.parametrize("name", GAIN_LAYOUTS)
+def test_bf16_fixed_tolerances_hold_to_gain_product_1_5(name):
+    """Every channel's gain product at 1.5 (g_q = g_k = sqrt(1.5)): the
+    fixed tolerances (max-abs 2e-2, rel-L2 5e-3, LSE 1e-2) still hold. This is
+    the documented range of the fixed tolerances; beyond it the bf16
+    rounding of the normalised operands, relative to the logits' size, takes
+    the error past them (next test)."""
+    lay = dict(SMALL)[name]
+    for hq, hk in ((6, 2), (8, 1)):
+        rl2, mabs, lerr = full_parity(lay, hq, hk, 128, "bf16", gains="ones", seed=17, gain_scale=math.sqrt(1.5))
+        log(f"gain product 1.5 {name} {hq}/{hk}: rel_l2={rl2:.3e} max_abs={mabs:.3e} lse_err={lerr:.3e}")
+
+
+@pytest.mark.parametrize("product", [3.0625, 4.0, 9.0])
+@pytest.mark.parametrize("name", GAIN_LAYOUTS)
+def test_bf16_uniform_gain_products_derived_tolerance(name, product):
+    """Every channel's gain product at 3.06 (g = 1.75 each), 4 and 9: the
+    logits are that many times those of unit gains, and so are their errors
+    from the bf16 rounding of the normalised operands. Out and LSE meet the
+    larger of the fixed tolerances and the first-order bounds of the bf16
+    error model. Product 9 puts the gain bound at 148 log2 units, so the
+    static softmax runs with a shift of 84."""
+    lay = dict(SMALL)[name]
+    sc = 1 / math.sqrt(128)
+    for hq, hk in ((6, 2), (8, 1)):
+        inp = make_inputs(lay, hq, hk, 128, "bf16", "ones", 17)
+        inp["q_gain"] = inp["q_gain"] * math.sqrt(product)
+        inp["k_gain"] = inp["k_gain"] * math.sqrt(product)
+        go, gl = run_gpu(lay, inp, hq, hk, 128, "bf16", 1e-6, sc)
+        ro, rl, e, sig = predicted_errors(inp["q"], inp["k"], inp["v"], inp["q_gain"], inp["k_gain"], 1e-6, sc, lay)
+        rl2, mabs, lerr, ratios = check_derived(go, gl, ro, rl, e, sig)
+        log(f"gain product {product} {name} {hq}/{hk}: rel_l2={rl2:.3e} max_abs={mabs:.3e} lse_err={lerr:.3e} "
+            f"error/tolerance={tuple(round(r, 2) for r in ratios)}")
 
 
 def test_bf16_scale_and_eps_are_honoured():
@@ -225,8 +262,31 @@ def sample_rows(layout, tile_q, n_random, seed):
     return np.array(sorted(rows))
 
 
+def structured_rows(layout, tile_q, per_chunk, seed):
+    """The measurement sample of a full-size layout: for every chunk with
+    queries, its first two and last two rows, the two rows on each side of
+    its last query-tile edge (multiples of tile_q) and of the last 32-key
+    tile edge before its end (a 9,360-token chunk ends 16 keys into a tile),
+    and `per_chunk` uniform rows (seeded)."""
+    rng = np.random.default_rng(seed)
+    rows = set()
+    for c in range(layout.n_chunks):
+        a, b = layout.q_offsets[c], layout.q_offsets[c + 1]
+        if b <= a:
+            continue
+        cand = [a, a + 1, b - 2, b - 1]
+        for edge in ((b - 1) // tile_q * tile_q, (b - 1) // 32 * 32):
+            cand += [edge - 2, edge - 1, edge, edge + 1]
+        rows.update(r for r in cand if a <= r < b)
+        rows.update(int(x) for x in rng.integers(a, b, per_chunk))
+    return np.array(sorted(rows))
+
+
 @pytest.mark.parametrize("name", [c.name for c in CONFIGS])
 def test_config_full_size_sampled_rows(name):
+    """Every workload at full size in the benchmark's launch configuration.
+    The small ones are compared whole (tiny) or on sampled rows; 480x832 on
+    the structured sample of every chunk (about 680 rows x 48 heads)."""
     from block_causal_attention_flash_amd import magi_attn_plan_stats
     c = get_config(name)
     log(f"config {name}: generating inputs")
@@ -235,19 +295,39 @@ def test_config_full_size_sampled_rows(name):
                               c.n_kv_heads, c.head_dim, c.dtype)
     log(f"config {name}: GPU run ({st['n_items']} workgroups)")
     got_out, got_lse = run_gpu(c.layout, inp, c.n_q_heads, c.n_kv_heads, c.head_dim, c.dtype, c.eps, c.scale)
-    budget = {"tiny": 10 ** 9, "video256x2": 40, "streaming": 40, "video480x832": 12, "packed8": 24}[name]
     if c.layout.t_q <= 512:
         rows = np.arange(c.layout.t_q)
+    elif name == "video480x832":
+        rows = structured_rows(c.layout, st["tile_q"], 32, seed=c.seed)
     else:
+        budget = {"video256x2": 40, "streaming": 40, "packed8": 24}[name]
         rows = sample_rows(c.layout, st["tile_q"], budget, seed=c.seed)
-        if name == "video480x832":
-            rows = rows[np.random.default_rng(1).permutation(len(rows))[:40]]
-            rows.sort()
     log(f"config {name}: oracle on {len(rows)} rows")
     ref_out, ref_lse = oracle.attention(inp["q"], inp["k"], inp["v"], inp["q_gain"], inp["k_gain"], c.eps,
                                         c.scale, c.layout, rows=rows)
     rl2, mabs, lerr = compare(got_out[rows], got_lse[:, rows], ref_out, ref_lse, c.dtype)
     log(f"config {name}: rows={len(rows)} rel_l2={rl2:.3e} max_abs={mabs:.3e} lse_err={lerr:.3e}")
+
+
+def test_480x832_gains_x4_shifted_static_softmax():
+    """480x832 with the query gains x4 (every logit bound ~66 log2 units, past
+    the unshifted static range of 64): the static softmax runs with a shift of
+    about 2. Structured rows (8 uniform per chunk) against the oracle at the
+    larger of the fixed tolerances and the bf16 error model's bounds."""
+    from block_causal_attention_flash_amd import magi_attn_plan_stats
+    c = get_config("video480x832")
+    inp = make_inputs(c.layout, c.n_q_heads, c.n_kv_heads, c.head_dim, c.dtype, c.gain_kind, c.seed)
+    inp["q_gain"] = inp["q_gain"] * 4.0
+    st = magi_attn_plan_stats(c.layout.q_offsets, c.layout.kv_offsets, c.layout.seq_chunks, c.n_q_heads,
+                              c.n_kv_heads, c.head_dim, c.dtype)
+    got_out, got_lse = run_gpu(c.layout, inp, c.n_q_heads, c.n_kv_heads, c.head_dim, c.dtype, c.eps, c.scale)
+    rows = structured_rows(c.layout, st["tile_q"], 8, seed=41)
+    log(f"480x832 gains x4: oracle on {len(rows)} rows")
+    ro, rl, e, sig = predicted_errors(inp["q"], inp["k"], inp["v"], inp["q_gain"], inp["k_gain"], c.eps, c.scale,
+                                      c.layout, rows=rows)
+    rl2, mabs, lerr, ratios = check_derived(got_out[rows], got_lse[:, rows], ro, rl, e, sig)
+    log(f"480x832 gains x4: rows={len(rows)} rel_l2={rl2:.3e} max_abs={mabs:.3e} lse_err={lerr:.3e} "
+        f"error/tolerance={tuple(round(r, 2) for r in ratios)}")
 
 
 # ------------------------------------------------------------------ KV-range window
@@ -279,9 +359,7 @@ def test_kv_range_480x832_sampled_rows():
     st = magi_attn_plan_stats(lay.q_offsets, lay.kv_offsets, lay.seq_chunks, c.n_q_heads, c.n_kv_heads,
                               c.head_dim, c.dtype, kv_range=5)
     got_out, got_lse = run_gpu(lay, inp, c.n_q_heads, c.n_kv_heads, c.head_dim, c.dtype, c.eps, c.scale)
-    rows = sample_rows(lay, st["tile_q"], 12, seed=5)
-    rows = rows[np.random.default_rng(2).permutation(len(rows))[:40]]
-    rows.sort()
+    rows = structured_rows(lay, st["tile_q"], 32, seed=5)
     ref_out, ref_lse = oracle.attention(inp["q"], inp["k"], inp["v"], inp["q_gain"], inp["k_gain"], c.eps,
                                         c.scale, lay, rows=rows)
     rl2, mabs, lerr = compare(got_out[rows], got_lse[:, rows], ref_out, ref_lse, c.dtype)

@@ -372,3 +372,22 @@ def test_plain_c_client_of_the_host_calls(built_lib, tmp_path):
     assert r.returncode == 0, r.stderr
     r = subprocess.run([str(exe)], capture_output=True, text=True, timeout=60)
     assert r.returncode == 0 and r.stdout.strip() == "ok", r.stdout + r.stderr
+
+
+def test_tile_lists_past_int32_are_refused(built_lib):
+    """One chunk of 8,388,000 tokens with one head passes the tensor limits
+    (K is just under 2 GiB) but its tile lists would hold 5.7e9 entries,
+    past the kernels' int32 indices: refused before any list is built."""
+    from block_causal_attention_flash_amd import MagiAttnError, magi_attn_plan_stats
+    with pytest.raises(MagiAttnError) as e:
+        magi_attn_plan_stats([0, 8388000], None, None, 1, 1, 128, "bf16")
+    assert e.value.status == 2 and "2^31" in e.value.message
+
+
+def test_query_stream_length_limit(built_lib):
+    """Query streams of 2^26 tokens or more are refused: int32 token indices
+    keep their headroom and the per-row host tables stay below 512 MiB."""
+    from block_causal_attention_flash_amd import MagiAttnError, magi_attn_plan_stats
+    with pytest.raises(MagiAttnError) as e:
+        magi_attn_plan_stats([0, 1 << 26], [0, 64], None, 1, 1, 128, "fp32")
+    assert e.value.status == 2
