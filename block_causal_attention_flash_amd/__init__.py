@@ -9,12 +9,12 @@ from .api import (CrossPlan, CrossTrainPlan, MagiAttnError, ParallelPlan, Plan, 
                   magi_attn_bwd_workspace_size, magi_attn_classify_host, magi_attn_key_classify_host,
                   magi_attn_cross_train_plan_create, magi_attn_train_plan_create,
                   magi_attn_cross_classify_host, magi_attn_cross_plan_create, magi_attn_cross_plan_stats,
-                  magi_attn_fwd, magi_attn_fwd_parallel, magi_attn_fwd_simple, magi_attn_parallel_plan_create,
+                  magi_attn_fwd, magi_attn_fwd_noalloc, magi_attn_fwd_parallel, magi_attn_fwd_simple, magi_attn_parallel_plan_create,
                   magi_attn_plan_create, magi_attn_plan_destroy, magi_attn_plan_stats, magi_attn_workspace_size)
 
 __all__ = ["CrossPlan", "CrossTrainPlan", "MagiAttnError", "ParallelPlan", "Plan", "TrainPlan", "magi_attn_abi_version", "magi_attn_bwd",
            "magi_attn_bwd_workspace_size", "magi_attn_classify_host", "magi_attn_key_classify_host",
            "magi_attn_cross_train_plan_create", "magi_attn_train_plan_create",
            "magi_attn_cross_classify_host", "magi_attn_cross_plan_create", "magi_attn_cross_plan_stats",
-           "magi_attn_fwd", "magi_attn_fwd_parallel", "magi_attn_fwd_simple", "magi_attn_parallel_plan_create",
+           "magi_attn_fwd", "magi_attn_fwd_noalloc", "magi_attn_fwd_parallel", "magi_attn_fwd_simple", "magi_attn_parallel_plan_create",
            "magi_attn_plan_create", "magi_attn_plan_destroy", "magi_attn_plan_stats", "magi_attn_workspace_size"]

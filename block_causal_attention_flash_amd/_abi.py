@@ -19,6 +19,8 @@ MAGI_ERR_HIP = 4
 MAGI_DTYPE_BF16 = 0
 MAGI_DTYPE_FP32 = 1
 
+MAGI_ATTN_NOALLOC_SCRATCH_BYTES = 256 << 20    # include/magi_attn.h
+
 _i32p = ctypes.POINTER(ctypes.c_int32)
 
 
@@ -105,6 +107,9 @@ SIGNATURES = {
                                      ctypes.c_void_p, ctypes.c_void_p, ctypes.c_float, ctypes.c_float,
                                      ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t,
                                      ctypes.c_void_p]),
+    "magi_attn_fwd_noalloc": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                             ctypes.c_void_p, ctypes.c_void_p, ctypes.c_float, ctypes.c_float,
+                                             ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]),
     "magi_attn_fwd_parallel": (ctypes.c_int, [ctypes.c_void_p, ctypes.POINTER(ParallelIO), ctypes.c_float,
                                               ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]),
     "magi_attn_fwd_simple": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,

@@ -273,6 +273,26 @@ def magi_attn_fwd(handle: int, q, k, v, q_gain=None, k_gain=None, rms_eps: float
     return out, lse
 
 
+def magi_attn_fwd_noalloc(handle: int, q, k, v, q_gain, k_gain, rms_eps: float, scale: float, out, lse,
+                          stream=None):
+    """magi_attn_fwd with the library's static device scratch as the
+    workspace: nothing is allocated here or in the library, so every tensor,
+    the gains included (fp32, on the device), must be given. Plans whose
+    workspace exceeds MAGI_ATTN_NOALLOC_SCRATCH_BYTES are refused. Calls that
+    overlap on one GPU share the scratch and must not run concurrently."""
+    lib = _abi.load()
+    for name, t in (("q", q), ("k", k), ("v", v), ("out", out), ("lse", lse)):
+        if t is None or not t.is_cuda or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous GPU tensor")
+    for name, g in (("q_gain", q_gain), ("k_gain", k_gain)):
+        if g is None or not g.is_cuda or not g.is_contiguous() or str(g.dtype) != "torch.float32":
+            raise ValueError(f"{name} must be a contiguous fp32 GPU tensor")
+    _check(lib, lib.magi_attn_fwd_noalloc(handle, q.data_ptr(), k.data_ptr(), v.data_ptr(), q_gain.data_ptr(),
+                                          k_gain.data_ptr(), float(rms_eps), float(scale), out.data_ptr(),
+                                          lse.data_ptr(), _stream_ptr(stream, q.device)))
+    return out, lse
+
+
 def magi_attn_fwd_parallel(handle: int, q, k, v, q_x, k_x, v_x, q_gain=None, k_gain=None, q_gain_x=None,
                            k_gain_x=None, rms_eps: float = 1e-6, scale: Optional[float] = None,
                            scale_x: Optional[float] = None, out=None, lse=None, out_x=None, lse_x=None,

@@ -234,6 +234,10 @@ magi_status_t launch(const magi_attn_plan_t* plan, const magi::FwdParams& prm, v
 
 }  // namespace
 
+namespace magi {
+magi_status_t set_last_error(magi_status_t s, const std::string& msg) { return fail(s, msg); }
+}  // namespace magi
+
 extern "C" {
 
 int magi_attn_abi_version(void) { return MAGI_ATTN_ABI_VERSION; }

@@ -3,8 +3,15 @@
 
 #include <hip/hip_runtime.h>
 #include <cstdint>
+#include <string>
+
+#include "magi_attn.h"
 
 namespace magi {
+
+// Records `msg` as the calling thread's last error (magi_attn_last_error)
+// and returns `s`; for entry points defined outside api.cpp.
+magi_status_t set_last_error(magi_status_t s, const std::string& msg);
 
 // (token, head) rows of one bf16 work item: tile_q * heads_per_item.
 constexpr int kBf16RowsPerItem = 384;

@@ -57,7 +57,7 @@
 extern "C" {
 #endif
 
-#define MAGI_ATTN_ABI_VERSION 6
+#define MAGI_ATTN_ABI_VERSION 7
 
 typedef enum magi_status {
   MAGI_OK = 0,
@@ -211,7 +211,8 @@ MAGI_API magi_status_t magi_attn_plan_destroy(magi_attn_plan_t* plan);
  * plus, when the
  * plan splits work items along the key axis (layouts with too few items to
  * fill the GPU), the pieces' partial results, pieces * 384 * (head_dim + 2)
- * * 4 bytes. fp32: 0.
+ * * 4 bytes, plus 32 bytes per work item (the flags by which the static
+ * softmax hands items to the running-maximum instance). fp32: 0.
  */
 MAGI_API magi_status_t magi_attn_workspace_size(const magi_attn_plan_t* plan, size_t* bytes);
 
@@ -236,6 +237,30 @@ MAGI_API magi_status_t magi_attn_fwd(const magi_attn_plan_t* plan,
                             float rms_eps, float scale,
                             void* out, float* lse,
                             void* workspace, size_t workspace_bytes, void* stream);
+
+/* Bytes of the static device scratch array behind magi_attn_fwd_noalloc. */
+#define MAGI_ATTN_NOALLOC_SCRATCH_BYTES 268435456u
+
+/*
+ * magi_attn_fwd without any allocation, for callers that cannot allocate
+ * device memory or pass a workspace: code being captured into a HIP graph,
+ * tight serving loops, harnesses that forbid allocation. Same arguments,
+ * results and errors as magi_attn_fwd, minus the workspace: the library uses
+ * a static device array of MAGI_ATTN_NOALLOC_SCRATCH_BYTES (256 MiB) bytes
+ * that every GPU it runs on holds until the process ends. Plans whose
+ * magi_attn_workspace_size() exceeds that are refused with
+ * MAGI_ERR_UNSUPPORTED (for example the 480x832 video: 613 MB of tile images;
+ * the 256x256 two-video batch fits). Allocates nothing and never
+ * synchronises. All calls on one GPU share its array, which keeps the last
+ * call's contents: calls that overlap in time on one GPU (two streams, two
+ * host threads) race and must be serialised by the caller. The device current
+ * at the call must be the device of the plan and of `stream`.
+ */
+MAGI_API magi_status_t magi_attn_fwd_noalloc(const magi_attn_plan_t* plan,
+                                             const void* q, const void* k, const void* v,
+                                             const float* q_gain, const float* k_gain,
+                                             float rms_eps, float scale,
+                                             void* out, float* lse, void* stream);
 
 /*
  * Tensors of one call of the parallel attention block. The self-attention

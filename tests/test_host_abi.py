@@ -34,7 +34,7 @@ def test_abi_version(built_lib):
     from block_causal_attention_flash_amd import magi_attn_abi_version
     hdr = open(os.path.join(ROOT, "include", "magi_attn.h")).read()
     declared = int(re.search(r"#define MAGI_ATTN_ABI_VERSION (\d+)", hdr).group(1))
-    assert magi_attn_abi_version() == declared == 6
+    assert magi_attn_abi_version() == declared == 7
 
 
 def brute_classes(layout, bm, bn, mask=None):
