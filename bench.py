@@ -109,6 +109,44 @@ def first_visible(lay, c):
     return max(lay.seq_chunks[s], c - R + 1) if R > 0 else lay.seq_chunks[s]
 
 
+def timing_record(times, span, steps):
+    import statistics
+    return {"mean_ms": round(span / steps, 4), "median_ms": round(statistics.median(times), 4),
+            "min_ms": round(min(times), 4), "max_ms": round(max(times), 4)}
+
+
+def cpu_model() -> str:
+    """The host CPU's model name (/proc/cpuinfo), for the baseline's record."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def step_times(step, stream, steps: int, flush=None):
+    """Runs `steps` steps on `stream`, each between two HIP events recorded
+    on that stream (the one the kernels are launched on); with `flush` (a
+    device buffer), overwrites it before every step, outside the timed pair,
+    so that each step starts with the caches holding other data. Returns the
+    per-step times (ms) and the events' total span (ms, warm runs only)."""
+    import torch
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(2 * steps)]
+    for i in range(steps):
+        if flush is not None:
+            flush.fill_(i & 0xff)
+        evs[2 * i].record(stream)
+        step()
+        evs[2 * i + 1].record(stream)
+    torch.cuda.synchronize()
+    times = [evs[2 * i].elapsed_time(evs[2 * i + 1]) for i in range(steps)]
+    span = evs[0].elapsed_time(evs[-1]) if flush is None else sum(times)
+    return times, span
+
+
 def cpu_baseline(cfg, inp, budget_s: float = 20.0, attention: str = "self", text=None, tx=None):
     """Times the fp64 oracle(s) of the benchmarked attention on a bounded
     sample of query rows (all heads) and converts it to useful TFLOP/s on
@@ -150,7 +188,8 @@ def cpu_baseline(cfg, inp, budget_s: float = 20.0, attention: str = "self", text
         if time.perf_counter() - t_start > 3 * budget_s:
             break
     what = {"self": "", "cross": " (cross-attention)", "parallel": " (self- and cross-attention)"}[attention]
-    return {"value": flops / spent / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+    return {"value": flops / spent / 1e12, "unit": "TFLOP/s", "cores": int(threads), "cpu_model": cpu_model(),
+            "kind": "oracle",
             "sample": f"{rows_done} query rows x {hq} heads of {cfg.name}{what} (blocks of 32 rows), "
                       f"{spent:.1f} s fp64 numpy on the host"}
 
@@ -201,7 +240,8 @@ def cpu_baseline_backward(cfg, inp, dout, budget_s: float = 20.0, text=None):
             break
         n *= 2
     what = "its text" if text is not None else "itself"
-    return {"value": flops / spent / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+    return {"value": flops / spent / 1e12, "unit": "TFLOP/s", "cores": int(threads), "cpu_model": cpu_model(),
+            "kind": "oracle",
             "sample": f"backward of the first {n} tokens of chunk {c} of {cfg.name} attending to {what}, "
                       f"{hq} heads, {spent:.1f} s fp64 numpy on the host"}
 
@@ -253,13 +293,8 @@ def bench_backward(args) -> None:
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    ev0.record(stream)
-    for _ in range(args.steps):
-        step()
-    ev1.record(stream)
-    torch.cuda.synchronize()
-    ms = ev0.elapsed_time(ev1) / args.steps
+    times, span = step_times(step, stream, args.steps)
+    ms = span / args.steps
     pairs = useful_text_pairs(lay, text) if cross else useful_pairs(lay)
     flops = 2.5 * 4.0 * cfg.head_dim * cfg.n_q_heads * pairs
     tflops = flops / (ms * 1e-3) / 1e12
@@ -281,6 +316,7 @@ def bench_backward(args) -> None:
                    "useful_flops": flops, "unmasked_pairs_per_head": pairs,
                    **({"gain_scale": args.gain_scale} if args.gain_scale != 1.0 else {})},
         "frac_of_peak": round(tflops / PEAK_BF16_TFLOPS, 4), "plan_create_ms": round(plan_ms, 2),
+        "timing": timing_record(times, span, args.steps),
         "roofline": roof, "cpu_baseline": None,
     }
     plan.close()
@@ -326,8 +362,11 @@ def main():
                     help="time the backward (magi_attn_bwd) of the self- or (--attention cross) the "
                          "cross-attention instead of the forward")
     ap.add_argument("--gain-scale", type=float, default=1.0,
-                    help="multiply the query gains by this factor; large enough a factor takes the bf16 forward off "
-                         "the static-softmax kernel instance onto the online one (logit bound above 40)")
+                    help="multiply the query gains by this factor (larger logits: the static softmax runs with a "
+                         "larger shift; work items whose row sums it loses go to the running-maximum instance)")
+    ap.add_argument("--cold", action="store_true",
+                    help="overwrite a 1 GiB buffer before every timed step (forward), so each step starts with the "
+                         "L2s and the Infinity Cache holding other data")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=20.0)
     ap.add_argument("--copy-probe-mib", type=int, default=0,
@@ -405,17 +444,15 @@ def main():
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    ev0 = torch.cuda.Event(enable_timing=True)
-    ev1 = torch.cuda.Event(enable_timing=True)
+    # --cold: a buffer larger than the L2s and the 256 MB Infinity Cache is
+    # overwritten before every step (outside the timed events)
+    flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev) if args.cold else None
     wall0 = time.perf_counter()
-    ev0.record(stream)
-    for _ in range(args.steps):
-        step()
-    ev1.record(stream)
-    torch.cuda.synchronize()
+    times, span = step_times(step, stream, args.steps, flush)
     wall_ms = (time.perf_counter() - wall0) * 1e3 / args.steps
-    ms = ev0.elapsed_time(ev1) / args.steps
-    print(f"[bench] {args.steps} steps: {ms:.3f} ms/step (events), {wall_ms:.3f} ms/step (host wall)",
+    ms = span / args.steps
+    print(f"[bench] {args.steps} steps{' (cold caches)' if args.cold else ''}: {ms:.3f} ms/step mean, "
+          f"median {sorted(times)[len(times) // 2]:.3f}, min {min(times):.3f} (events); {wall_ms:.3f} ms/step host wall",
           file=sys.stderr, flush=True)
 
     pairs = useful_pairs(lay) if mode != "cross" else 0
@@ -424,9 +461,11 @@ def main():
     tflops = flops / (ms * 1e-3) / 1e12
     # the stored counters belong to the static-softmax instance on the workload's own gains
     traffic = (stored_traffic(cfg.name, mode)
-               if not (lay.kv_range or lay.last_global or args.gain_scale != 1.0) else None)
+               if not (lay.kv_range or lay.last_global or args.gain_scale != 1.0 or args.cold) else None)
     roof = {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
             "frac": round(tflops / PEAK_BF16_TFLOPS, 4), "traffic": traffic}
+    if traffic:
+        roof["hbm_gbps"] = round(traffic / (ms * 1e-3) / 1e9, 1)
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -441,6 +480,8 @@ def main():
         config["gain_scale"] = args.gain_scale
     if text is not None:
         config.update({"t_text": text.t_text, "text_pairs_per_head": pairs_x})
+    if args.cold:
+        config["caches"] = "cold (1 GiB written between steps)"
     rec = {
         "metric": METRIC if mode == "self" else METRIC_CROSS if mode == "cross" else METRIC_PARALLEL,
         "value": round(tflops, 2),
@@ -458,6 +499,7 @@ def main():
         "config": config,
         "frac_of_peak": round(tflops / PEAK_BF16_TFLOPS, 4),
         "plan_create_ms": round(plan_ms, 2),
+        "timing": timing_record(times, span, args.steps),
         "roofline": roof,
         "cpu_baseline": cpu,
     }
