@@ -20,7 +20,7 @@ Propagated to first order:
     by all keys of the row, and Jensen's inequality bounds its part by the same
     p-weighted mean).
 
-The tolerances take the benchmark spec's fixed values or these first-order estimates,
+The tolerances take the fixed values (out max-abs 2e-2, rel-L2 5e-3; lse 1e-2) or these first-order estimates,
 whichever is larger:
   max-abs of out <= max(2e-2, Z_OUT e_id) per element;
   rel-L2 of out  <= max(5e-3, ||e|| / ||out||);
