@@ -31,6 +31,7 @@ struct magi_attn_plan {
   const int2* d_dq_zero = nullptr;
   const int2* d_kv_zero = nullptr;
   const int4* d_kv_merges = nullptr;
+  const int4* d_dq_merges = nullptr;
 };
 
 namespace {
@@ -144,6 +145,7 @@ magi_status_t create_plan(int32_t kind, bool train, const magi_attn_layout_t* la
   const size_t o_dq_zero = up.add(B.dq_zero.data(), bytes(B.dq_zero));
   const size_t o_kv_zero = up.add(B.kv_zero.data(), bytes(B.kv_zero));
   const size_t o_kv_merges = up.add(B.kv_merges.data(), bytes(B.kv_merges));
+  const size_t o_dq_merges = up.add(B.dq_merges.data(), bytes(B.dq_merges));
   hipError_t e = hipGetDevice(&p->device);
   if (e != hipSuccess) { delete p; return hip_fail(e, "hipGetDevice"); }
   e = hipMalloc(&p->dmem, std::max<size_t>(up.total, 256));
@@ -173,6 +175,7 @@ magi_status_t create_plan(int32_t kind, bool train, const magi_attn_layout_t* la
   p->d_dq_zero = reinterpret_cast<const int2*>(base + o_dq_zero);
   p->d_kv_zero = reinterpret_cast<const int2*>(base + o_kv_zero);
   p->d_kv_merges = reinterpret_cast<const int4*>(base + o_kv_merges);
+  p->d_dq_merges = reinterpret_cast<const int4*>(base + o_dq_merges);
   *out_plan = p;
   return MAGI_OK;
 }
@@ -422,7 +425,8 @@ magi_status_t magi_attn_bwd_workspace_size(const magi_attn_plan_t* plan, size_t*
   const int nq = int(plan->bwd.dq.items.size()), nk = int(plan->bwd.items.size());
   const auto& B = plan->bwd;
   *bytes = H.dtype == MAGI_DTYPE_BF16
-               ? magi::bwd_workspace_layout(H.tq, H.tk, H.hq, H.hk, nq, nk + int(B.kv_merges.size()), B.n_kv_slots).total
+               ? magi::bwd_workspace_layout(H.tq, H.tk, H.hq, H.hk, nq + int(B.dq_merges.size()),
+                                            nk + int(B.kv_merges.size()), B.n_kv_slots, B.dq.n_slots).total
                                       : magi::bwd_workspace_bytes_fp32(H.tq, H.tk, H.hq, H.hk, H.d, nq, nk);
   return MAGI_OK;
 }
@@ -492,6 +496,9 @@ magi_status_t magi_attn_bwd(const magi_attn_plan_t* plan, const magi_attn_bwd_io
   b.kv_merges = plan->d_kv_merges;
   b.n_kv_merges = int(plan->bwd.kv_merges.size());
   b.n_kv_slots = plan->bwd.n_kv_slots;
+  b.dq_merges = plan->d_dq_merges;
+  b.n_dq_merges = int(plan->bwd.dq_merges.size());
+  b.n_dq_slots = plan->bwd.dq.n_slots;
   b.n_dq_items = int(plan->bwd.dq.items.size());
   b.n_kv_items = int(plan->bwd.items.size());
   hipStream_t st = static_cast<hipStream_t>(stream);

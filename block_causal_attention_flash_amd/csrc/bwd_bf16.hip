@@ -26,7 +26,8 @@
 //           (32-token tile, query head) S and dP, then dV^T += dO^T P and
 //           dK^T += q_hat^T dS; when a plan has fewer key blocks x KV heads
 //           than CUs, each list is cut into pieces that write fp32 sums;
-//   merge   adds a split list's pieces in order and finishes like dkdv;
+//   merge   adds a split list's pieces in order and finishes like dkdv (and,
+//           for the split dq items of small layouts, like dq);
 //   zero    dq of rows no item covers (they see no key) and dk, dv of key
 //           blocks no row sees;
 //   reduce  the gain gradients from the per-workgroup partials.
@@ -449,6 +450,21 @@ bwd_dq_kernel(BwdParams p, BwdLayout L, const int4* __restrict__ items, const in
   }
   wait_vmcnt<0>();                                    // the padding copies of the last two steps
 
+  // A piece of a split item writes its fp32 dq-hat^T sums (times log2 e) to
+  // its slot, [256 item rows][128 dims], and an empty gain partial; the dq
+  // merge adds the pieces and finishes the rows.
+  const int slot = __builtin_amdgcn_readfirstlane(items[2 * blockIdx.x + 1].y);
+  if (slot >= 0) {
+    float* pd = reinterpret_cast<float*>(ws + L.pdq) + size_t(slot) * kBwdRowsPerItem * D;
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+      for (int db = 0; db < 8; ++db)
+        *reinterpret_cast<f32x4*>(pd + size_t(r0 + 16 * rb + r16) * D + 16 * db + 4 * g) = acc[rb][db];
+    if (tid < D) part[tid] = 0.0f;
+    return;
+  }
+
   // Epilogue: lane holds dims 16 db + 4 g + i of row r16 of block rb.
   float gp[8][4];
 #pragma unroll
@@ -800,6 +816,87 @@ __global__ void __launch_bounds__(MERGE_THREADS) bwd_kv_merge_kernel(BwdParams p
   }
 }
 
+// Finishes a split dq item: sums its pieces' slots in piece order
+// (dq-hat = sum / log2 e), applies the RMSNorm backward, writes dq and the
+// workgroup's gain partial (row n_dq_items + merge index). Item row r is token
+// t0 + r % tile_q of head h0 + r / tile_q. Thread t handles dims
+// [32 (t % 4), +32) of rows t / 4 + 64 i, i = 0..3.
+__global__ void __launch_bounds__(MERGE_THREADS) bwd_dq_merge_kernel(BwdParams p, BwdLayout L,
+                                                                     const int4* __restrict__ merges) {
+  __shared__ float gq[D];
+  __shared__ float red[64][D + 1];
+  unsigned char* ws = static_cast<unsigned char*>(p.ws);
+  const int4 m = merges[2 * blockIdx.x];              // t0, (kvh << 16) | h0, first slot, pieces
+  const int h0 = m.y & 0xffff;
+  const int t = threadIdx.x, quarter = t & 3, rq = t >> 2;
+  if (t < D) gq[t] = p.q_gain[t];
+  __syncthreads();
+  float gp[32];
+#pragma unroll
+  for (int i = 0; i < 32; ++i) gp[i] = 0.0f;
+  const float* slots = reinterpret_cast<const float*>(ws + L.pdq);
+  for (int pass = 0; pass < kBwdRowsPerItem / 64; ++pass) {
+    const int r = 64 * pass + rq;
+    const int tok = m.x + r % p.tile_q, head = h0 + r / p.tile_q;
+    const bool valid = tok < p.tq;
+    float sq[32];
+#pragma unroll
+    for (int i = 0; i < 32; ++i) sq[i] = 0.0f;
+    for (int k = 0; k < m.w; ++k) {
+      const float* s = slots + (size_t(m.z + k) * kBwdRowsPerItem + r) * D + 32 * quarter;
+#pragma unroll
+      for (int c = 0; c < 8; ++c) {
+        const f32x4 a = *reinterpret_cast<const f32x4*>(s + 4 * c);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) sq[4 * c + e] += a[e];
+      }
+    }
+    const size_t off = (size_t(valid ? tok : 0) * p.hq + head) * D + 32 * quarter;
+    float x[32];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const bf16x8 xv = valid ? *reinterpret_cast<const bf16x8*>(static_cast<const __bf16*>(p.q) + off + 8 * c)
+                              : bf16x8{};
+#pragma unroll
+      for (int e = 0; e < 8; ++e) x[8 * c + e] = float(xv[e]);
+    }
+    float ss = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 32; ++i) ss += x[i] * x[i];
+    ss += __shfl_xor(ss, 1, 64);
+    ss += __shfl_xor(ss, 2, 64);
+    const float rr = __builtin_amdgcn_rsqf(ss * (1.0f / D) + p.eps);
+    float mm = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 32; ++i) mm += x[i] * rr * gq[32 * quarter + i] * (sq[i] * (1.0f / kLog2e));
+    mm += __shfl_xor(mm, 1, 64);
+    mm += __shfl_xor(mm, 2, 64);
+    mm *= 1.0f / D;
+    if (valid) {
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        bf16x8 w;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int i = 8 * c + e;
+          const float dxh = sq[i] * (1.0f / kLog2e), u = x[i] * rr;
+          w[e] = (__bf16)((gq[32 * quarter + i] * dxh - u * mm) * rr);
+          gp[i] += u * dxh;
+        }
+        *reinterpret_cast<bf16x8*>(static_cast<__bf16*>(p.dq) + off + 8 * c) = w;
+      }
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < 32; ++i) red[rq][32 * quarter + i] = gp[i];
+  __syncthreads();
+  if (t < D) {
+    float s = 0.0f;
+    for (int k = 0; k < 64; ++k) s += red[k][t];
+    reinterpret_cast<float*>(ws + L.pgq)[size_t(p.n_dq_items + blockIdx.x) * D + t] = s;
+  }
+}
+
 // dq = 0 over the blocks whose rows see no key (no dq item covers them): one
 // workgroup per block of `rows` tokens x `heads` heads, 16-byte stores.
 __global__ void __launch_bounds__(256) bwd_zero_rows_kernel(unsigned char* dq, const int2* __restrict__ blocks,
@@ -829,8 +926,8 @@ hipError_t launch_bwd_zero_rows(const BwdParams& p, int row_bytes, hipStream_t s
   return hipGetLastError();
 }
 
-BwdLayout bwd_workspace_layout(long long tq, long long tk, int hq, int hk, int n_dq_items, int n_kv_rows,
-                               int n_kv_slots) {
+BwdLayout bwd_workspace_layout(long long tq, long long tk, int hq, int hk, int n_dq_rows, int n_kv_rows,
+                               int n_kv_slots, int n_dq_slots) {
   auto up = [](size_t x) { return (x + 255) / 256 * 256; };
   const size_t qimg = size_t((tq + TT - 1) / TT) * size_t(hq) * IMG;
   const size_t kimg = size_t((tk + TT - 1) / TT) * size_t(hk) * IMG;
@@ -841,16 +938,17 @@ BwdLayout bwd_workspace_layout(long long tq, long long tk, int hq, int hk, int n
   L.kh = L.rs + up(qimg / IMG * 256);
   L.vr = L.kh + up(kimg);
   L.pgq = L.vr + up(kimg);
-  L.pgk = L.pgq + up(size_t(n_dq_items) * D * sizeof(float));
+  L.pgk = L.pgq + up(size_t(n_dq_rows) * D * sizeof(float));
   L.pkv = L.pgk + up(size_t(n_kv_rows) * D * sizeof(float));
-  L.level = L.pkv + up(size_t(n_kv_slots) * 2 * kBwdKeysPerItem * D * sizeof(float));
+  L.pdq = L.pkv + up(size_t(n_kv_slots) * 2 * kBwdKeysPerItem * D * sizeof(float));
+  L.level = L.pdq + up(size_t(n_dq_slots) * kBwdRowsPerItem * D * sizeof(float));
   L.total = L.level + up(size_t(2 * REDUCE_SLICES) * D * sizeof(float));
   return L;
 }
 
 hipError_t launch_bwd_bf16_d128(const BwdParams& p, hipStream_t stream) {
-  const BwdLayout L =
-      bwd_workspace_layout(p.tq, p.tk, p.hq, p.hk, p.n_dq_items, p.n_kv_items + p.n_kv_merges, p.n_kv_slots);
+  const BwdLayout L = bwd_workspace_layout(p.tq, p.tk, p.hq, p.hk, p.n_dq_items + p.n_dq_merges,
+                                           p.n_kv_items + p.n_kv_merges, p.n_kv_slots, p.n_dq_slots);
   const unsigned n_tt = unsigned((p.tq + TT - 1) / TT), n_kt = unsigned((p.tk + TT - 1) / TT);
   hipLaunchKernelGGL(bwd_prep_q_kernel, dim3(n_tt * unsigned(p.hq)), dim3(PREP_THREADS), 0, stream, p, L);
   if (n_kt > 0)
@@ -864,10 +962,12 @@ hipError_t launch_bwd_bf16_d128(const BwdParams& p, hipStream_t stream) {
     hipLaunchKernelGGL(bwd_dkdv_kernel, dim3(p.n_kv_items), dim3(NTHR), 0, stream, p, L, p.kv_items, p.kv_tiles);
   if (p.n_kv_merges > 0)
     hipLaunchKernelGGL(bwd_kv_merge_kernel, dim3(p.n_kv_merges), dim3(MERGE_THREADS), 0, stream, p, L, p.kv_merges);
+  if (p.n_dq_merges > 0)
+    hipLaunchKernelGGL(bwd_dq_merge_kernel, dim3(p.n_dq_merges), dim3(MERGE_THREADS), 0, stream, p, L, p.dq_merges);
   unsigned char* ws = static_cast<unsigned char*>(p.ws);
   float* level = reinterpret_cast<float*>(ws + L.level);
   hipLaunchKernelGGL(bwd_gain_slices_kernel, dim3(2 * REDUCE_SLICES), dim3(256), 0, stream,
-                     reinterpret_cast<const float*>(ws + L.pgq), p.n_dq_items,
+                     reinterpret_cast<const float*>(ws + L.pgq), p.n_dq_items + p.n_dq_merges,
                      reinterpret_cast<const float*>(ws + L.pgk), p.n_kv_items + p.n_kv_merges, level);
   hipLaunchKernelGGL(bwd_gain_final_kernel, dim3(1), dim3(256), 0, stream, level, p.dq_gain, p.dk_gain);
   return hipGetLastError();

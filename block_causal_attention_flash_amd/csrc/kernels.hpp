@@ -91,18 +91,22 @@ struct BwdParams {
   const int2* dq_zero;    // (t0, first head) of the dq blocks (tile_q tokens x heads_per_item heads) with no key
   const int2* kv_zero;    // (first key, 0) of the key blocks (key_block keys x all KV heads) no query sees
   const int4* kv_merges;  // (key block, KV head, first slot, pieces) of the split dk/dv items
+  const int4* dq_merges;  // MergeItem[n_dq_merges], two int4 each: rows and slots of the split dq items
   int key_block;
   int n_dq_items, n_kv_items, n_dq_zero, n_kv_zero, n_kv_merges, n_kv_slots;
+  int n_dq_merges, n_dq_slots;
 };
 
 // Byte offsets of the backward workspace's parts.
 struct BwdLayout {
-  size_t qs, dos, rs, kh, vr, pgq, pgk, pkv, level, total;
+  size_t qs, dos, rs, kh, vr, pgq, pgk, pkv, pdq, level, total;
 };
-// n_kv_rows: dk/dv items plus merges (one gain partial each); n_kv_slots:
-// partial slots of split dk/dv items (fp32 dV and dK-hat sums, 256 KiB each).
-BwdLayout bwd_workspace_layout(long long tq, long long tk, int hq, int hk, int n_dq_items, int n_kv_rows,
-                               int n_kv_slots);
+// n_dq_rows / n_kv_rows: dq / dk-dv items plus merges (one gain partial
+// each); n_kv_slots: partial slots of split dk/dv items (fp32 dV and dK-hat
+// sums, 256 KiB each); n_dq_slots: those of split dq items (fp32 dq-hat sums,
+// 128 KiB each).
+BwdLayout bwd_workspace_layout(long long tq, long long tk, int hq, int hk, int n_dq_rows, int n_kv_rows,
+                               int n_kv_slots, int n_dq_slots);
 hipError_t launch_bwd_bf16_d128(const BwdParams& p, hipStream_t stream);
 hipError_t launch_bwd_fp32(const BwdParams& p, int head_dim, hipStream_t stream);
 // Writes zeros where no item writes: dq over the p.dq_zero blocks, dk and dv

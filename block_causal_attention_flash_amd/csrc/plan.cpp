@@ -290,7 +290,7 @@ int64_t split_piece_tiles(int64_t n_whole, int64_t total_cost) {
 }
 
 magi_status_t build_host_plan(int32_t kind, const magi_attn_layout_t* L, const magi_attn_text_t* T,
-                              const Tiling& tiling, HostPlan& P, std::string& err, bool allow_split) {
+                              const Tiling& tiling, HostPlan& P, std::string& err, bool allow_split, int split_below) {
   const int32_t* kv = L->kv_offsets ? L->kv_offsets : L->q_offsets;
   P.kind = kind;
   P.n_phases = kind == kPlanParallel ? 2 : 1;
@@ -414,7 +414,7 @@ magi_status_t build_host_plan(int32_t kind, const magi_attn_layout_t* L, const m
         n_whole += int64_t(P.hk) * groups_per_kvh;
         total_cost += int64_t(P.qt_ntiles[ph * n_qt + qt]) * P.hk * groups_per_kvh;
       }
-    const bool split = allow_split && P.dtype == MAGI_DTYPE_BF16 && n_whole > 0 && n_whole < kSplitBelowItems;
+    const bool split = allow_split && P.dtype == MAGI_DTYPE_BF16 && n_whole > 0 && n_whole < split_below;
     const int64_t piece = split ? split_piece_tiles(n_whole, total_cost) : int64_t(1) << 40;
     for (int kvh = 0; kvh < P.hk; ++kvh)
       for (int64_t qt = 0; qt < n_qt; ++qt) {
@@ -507,15 +507,19 @@ magi_status_t build_bwd_plan(const magi_attn_layout_t* L, const magi_attn_text_t
     err = "internal: backward query tile not a multiple of 32 tokens";
     return MAGI_ERR_UNSUPPORTED;
   }
-  magi_status_t s = build_host_plan(T ? kPlanCross : kPlanSelf, L, T, tiling, B.dq, err, /*allow_split=*/false);
+  magi_status_t s = build_host_plan(T ? kPlanCross : kPlanSelf, L, T, tiling, B.dq, err, /*allow_split=*/true,
+                                    kBwdDqSplitBelowItems);
   if (s != MAGI_OK) return s;
   // Query blocks without any key have no dq item (their merge entries hold no
-  // pieces): their dq is zero.
+  // pieces): their dq is zero. Entries with pieces are split dq items.
   B.dq_zero.clear();
+  B.dq_merges.clear();
   for (const MergeItem& m : B.dq.merges)
     if (m.n_pieces == 0) {
       B.dq_zero.push_back(m.t0);
       B.dq_zero.push_back(m.heads & 0xffff);
+    } else {
+      B.dq_merges.push_back(m);
     }
   const int32_t* kv = L->kv_offsets ? L->kv_offsets : L->q_offsets;
   const int64_t tq = L->q_offsets[L->n_chunks], tk = T ? T->t_text : kv[L->n_chunks];

@@ -70,6 +70,11 @@ constexpr int kBwdSplitBelowItems = kNumCu;
 constexpr int kBwdSplitTargetItems = 4 * kNumCu;
 constexpr int kBwdMaxPieces = 64;
 constexpr int kBwdMinPieceEntries = 8;
+// The backward's dq items (bf16) take the forward's split rule when there are
+// fewer than kBwdDqSplitBelowItems of them: the streaming window's 576 items
+// ran in three rounds, the last a quarter full. A piece writes its fp32 dq-hat
+// sums to a slot; a merge adds them in piece order and finishes the rows.
+constexpr int kBwdDqSplitBelowItems = 4 * kNumCu;
 
 constexpr int kTilePad = 16;
 constexpr uint32_t kNoTileOffset = 0x80000000u;   // past any tile image buffer (< 2 GiB): reads give zeros
@@ -148,6 +153,7 @@ struct BwdHostPlan {
   std::vector<int32_t> kv_tiles;     // per key block: token tile codes, full first, then boundary; padded
   std::vector<KeyItem> items;        // launch order (XCD-interleaved, padded)
   std::vector<int32_t> dq_zero;      // (t0, first head) of the dq blocks whose rows see no key: dq = 0 there
+  std::vector<MergeItem> dq_merges;  // split dq items (from dq.merges, those with pieces), merged after the dq kernel
   std::vector<int32_t> kv_zero;      // (first key, 0) of the key blocks no query sees: dk = dv = 0 there
   std::vector<KeyMerge> kv_merges;   // split (key block, KV head) items, summed after the dk/dv kernel
   int32_t n_kv_slots = 0;            // partial slots of their pieces
@@ -179,9 +185,10 @@ Tiling choose_bwd_tiling(int dtype, int head_dim, int group);
 
 // Builds the full host plan of a kind (layout and text must already be
 // valid; text is unused for kPlanSelf). allow_split = false keeps every work
-// item whole (the backward's dq lists).
+// item whole; split_below is the item count under which a phase is split.
 magi_status_t build_host_plan(int32_t kind, const magi_attn_layout_t* layout, const magi_attn_text_t* text,
-                              const Tiling& tiling, HostPlan& plan, std::string& err, bool allow_split = true);
+                              const Tiling& tiling, HostPlan& plan, std::string& err, bool allow_split = true,
+                              int split_below = kSplitBelowItems);
 
 // Builds the backward's work lists of a self-attention layout (valid).
 // Backward lists of a self plan (text == NULL) or of a cross plan (the text

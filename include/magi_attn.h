@@ -307,7 +307,10 @@ MAGI_API magi_status_t magi_attn_fwd_parallel(const magi_attn_plan_t* plan, cons
  * re-laid-out normalised queries, upstream gradients, keys and values, about
  * 2 * |q| + 2 * |k| bytes, plus 256 KiB of fp32 partial sums per piece when
  * the plan splits its dk/dv work because it has fewer key blocks times KV
- * heads than the GPU has CUs (a short text stream: about 1024 pieces);
+ * heads than the GPU has CUs (a short text stream: about 1024 pieces), and
+ * 128 KiB per piece when it splits its dq work because it has fewer than
+ * 1024 dq items (a streaming window with a long cached prefix: up to 8
+ * pieces per item);
  * fp32: the normalised queries, 2 * |q|; plus per-workgroup gain partials). */
 MAGI_API magi_status_t magi_attn_bwd_workspace_size(const magi_attn_plan_t* plan, size_t* bytes);
 

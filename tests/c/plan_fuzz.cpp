@@ -146,6 +146,41 @@ void check_bwd(const BwdHostPlan& B, int64_t tq, int64_t tk, const char* what) {
   }
   for (const KeyMerge& m : B.kv_merges) CHECK(m.slot0 + m.n_pieces <= B.n_kv_slots, "%s: key merge", what);
   check_plan(B.dq, what);
+  // Split dq items: every merge entry is either a query block without keys
+  // (dq_zero) or a split item (dq_merges, at least 2 pieces); its pieces are
+  // the items whose slots are slot0 .. slot0 + n - 1, of the same rows and
+  // heads, cutting the block's list into consecutive non-empty ranges in slot
+  // order; no other item has a slot.
+  const HostPlan& P = B.dq;
+  CHECK(B.dq_zero.size() % 2 == 0 && B.dq_zero.size() / 2 + B.dq_merges.size() == P.merges.size(),
+        "%s: dq merges %zu + zero blocks %zu != %zu", what, B.dq_merges.size(), B.dq_zero.size() / 2,
+        P.merges.size());
+  std::vector<const WorkItem*> by_slot(size_t(P.n_slots), nullptr);
+  for (const WorkItem& w : P.items) {
+    if (w.slot < 0) continue;
+    CHECK(w.slot < P.n_slots && !by_slot[size_t(w.slot)], "%s: dq slot %d", what, w.slot);
+    if (w.slot < P.n_slots) by_slot[size_t(w.slot)] = &w;
+  }
+  int32_t slots_seen = 0;
+  const int bm = P.tiling.tile_q;
+  for (const MergeItem& m : B.dq_merges) {
+    CHECK(m.n_pieces >= 2 && m.slot0 == slots_seen, "%s: dq merge pieces %d slot0 %d", what, m.n_pieces, m.slot0);
+    slots_seen = m.slot0 + m.n_pieces;
+    if (m.n_pieces < 2 || m.slot0 + m.n_pieces > P.n_slots) continue;
+    const int64_t li = m.phase * ((P.tq + bm - 1) / bm) + m.t0 / bm;
+    int32_t next = P.qt_tiles[li];
+    for (int k = 0; k < m.n_pieces; ++k) {
+      const WorkItem* w = by_slot[size_t(m.slot0 + k)];
+      CHECK(w != nullptr, "%s: dq slot %d has no piece", what, m.slot0 + k);
+      if (!w) break;
+      CHECK(w->t0 == m.t0 && w->heads == m.heads && w->phase == m.phase && w->tile_begin == next &&
+                w->tile_end > w->tile_begin,
+            "%s: dq piece %d of block %d", what, k, m.t0);
+      next = w->tile_end;
+    }
+    CHECK(next == P.qt_tiles[li] + P.qt_ntiles[li], "%s: dq pieces of block %d end at %d", what, m.t0, next);
+  }
+  CHECK(slots_seen == P.n_slots, "%s: dq slots %d of %d in merges", what, slots_seen, P.n_slots);
 }
 
 // Plans a case the way the C ABI does; returns the validation status.
@@ -282,6 +317,38 @@ void limit_cases() {
   }
 }
 
+// Streaming layouts (a cached prefix of n_cached chunks without queries, then
+// n_active chunks with queries) have few dq items with long lists: the
+// backward cuts them into pieces. The counts here are the ones the GPU parity
+// cases of split dq items rely on (16 x 1100 with 8/1 heads: 35 items of 585
+// tiles; 8 pieces would take two rounds of 256 workgroups, 7 take one).
+void split_cases() {
+  struct S { int n_cached, n_active, chunk, hq, hk, pieces; };
+  const S cases[] = {{8, 2, 600, 6, 2, 2}, {8, 2, 600, 8, 1, 2}, {16, 1, 1100, 6, 2, 8}, {16, 1, 1100, 8, 1, 7}};
+  for (const S& x : cases) {
+    Case c;
+    c.q = {0};
+    c.kv = {0};
+    for (int k = 0; k < x.n_cached + x.n_active; ++k) {
+      c.kv.push_back(c.kv.back() + x.chunk);
+      c.q.push_back(c.q.back() + (k < x.n_cached ? 0 : x.chunk));
+    }
+    c.seq = {0, x.n_cached + x.n_active};
+    c.hq = x.hq;
+    c.hk = x.hk;
+    char tag[96];
+    std::snprintf(tag, sizeof tag, "split %dx%d+%d %d/%d", x.n_cached, x.chunk, x.n_active, x.hq, x.hk);
+    run_case(c, true, tag);
+    Owned o = own(c);
+    std::string err;
+    BwdHostPlan B;
+    CHECK(build_bwd_plan(&o.L, nullptr, B, err) == MAGI_OK, "%s: %s", tag, err.c_str());
+    CHECK(!B.dq_merges.empty(), "%s: no split dq items", tag);
+    for (const MergeItem& m : B.dq_merges)
+      CHECK(m.n_pieces == x.pieces, "%s: block %d has %d pieces, want %d", tag, m.t0, m.n_pieces, x.pieces);
+  }
+}
+
 }  // namespace
 
 int main(int argc, char** argv) {
@@ -300,6 +367,7 @@ int main(int argc, char** argv) {
     }
   }
   limit_cases();
+  split_cases();
   std::printf("plan_fuzz: %d seeds, %d valid layouts planned, %d of %d broken layouts refused, %d failed checks\n", n,
               valid, refused, 8 * n, g_failures);
   return g_failures == 0 ? 0 : 1;

@@ -94,6 +94,27 @@ def test_bf16_backward_small(name, lay, hq, hk):
     log("  rel_l2 dq {:.2e} dk {:.2e} dv {:.2e} dgq {:.2e} dgk {:.2e}".format(*errs))
 
 
+# Layouts with too few dq items to fill the GPU and long tile lists: the
+# backward cuts each dq item into pieces of its key-tile list (fp32 partial
+# sums, then a merge that finishes the rows). A cached prefix of 8 x 600 keys
+# gives lists of 169-188 tiles (2 pieces); 16 x 1100 gives 585 tiles (8
+# pieces with 6/2 heads, 7 with 8/1; the planner's fuzz test pins the counts).
+# Both end in a ragged query tile; with 8/1 heads an item packs 8 heads of 32
+# tokens, with 6/2 one head of 256 tokens.
+SPLIT_DQ = [
+    ("prefix_8x600", streaming_layout(8, 2, 600)),
+    ("prefix_16x1100", streaming_layout(16, 1, 1100)),
+]
+
+
+@pytest.mark.parametrize("name,lay", SPLIT_DQ, ids=[s[0] for s in SPLIT_DQ])
+@pytest.mark.parametrize("hq,hk", [(6, 2), (8, 1)])
+def test_bf16_backward_split_dq_items(name, lay, hq, hk):
+    log(f"bf16 backward, split dq items: {name} {hq}/{hk}")
+    errs = check(lay, hq, hk, 128, "bf16", seed=hq * 11 + hk)
+    log("  rel_l2 dq {:.2e} dk {:.2e} dv {:.2e} dgq {:.2e} dgk {:.2e}".format(*errs))
+
+
 FP32_SMALL = SMALL[:4] + SMALL[-2:]
 
 
@@ -117,10 +138,12 @@ def test_bf16_backward_scale_and_eps():
     check(lay, 4, 2, 128, "bf16", seed=3, eps=0.25, scale=0.05)
 
 
-def test_backward_is_deterministic():
-    """Two backward calls give bit-identical gradients (no atomics)."""
+@pytest.mark.parametrize("lay", [layout_from_chunks([[100, 157, 91]]), streaming_layout(8, 2, 600)],
+                         ids=["ragged", "split_dq_items"])
+def test_backward_is_deterministic(lay):
+    """Two backward calls give bit-identical gradients (no atomics; split
+    items' pieces are added in a fixed order)."""
     from block_causal_attention_flash_amd import TrainPlan
-    lay = layout_from_chunks([[100, 157, 91]])
     inp = make_inputs(lay, 6, 2, 128, "bf16", "uniform", 5)
     g = {n: t.to(DEV) for n, t in inp.items()}
     dout = torch.randn(lay.t_q, 6, 128, generator=torch.Generator().manual_seed(1)).to(torch.bfloat16).to(DEV)
