@@ -229,7 +229,7 @@ magi_status_t launch(const magi_attn_plan_t* plan, const magi::FwdParams& prm, v
   hipStream_t st = static_cast<hipStream_t>(stream);
   const int n = int(H.items.size()), nm = int(H.merges.size());
   hipError_t e;
-  if (H.dtype == MAGI_DTYPE_BF16) e = magi::launch_fwd_bf16_d128(prm, n, nm, H.n_slots, st);
+  if (H.dtype == MAGI_DTYPE_BF16) e = magi::launch_fwd_bf16(prm, H.d, n, nm, H.n_slots, st);
   else e = magi::launch_fwd_fp32(prm, H.d, n, nm, st);
   if (e != hipSuccess) return hip_fail(e, "kernel launch");
   return MAGI_OK;
@@ -350,7 +350,7 @@ magi_status_t magi_attn_plan_destroy(magi_attn_plan_t* plan) {
 magi_status_t magi_attn_workspace_size(const magi_attn_plan_t* plan, size_t* bytes) {
   if (!plan || !bytes) return fail(MAGI_ERR_INVALID_ARG, "plan or bytes is NULL");
   const auto& H = plan->host;
-  *bytes = H.dtype == MAGI_DTYPE_BF16 ? magi::workspace_bytes_bf16(H.n_kt_img, H.hk, H.n_slots, int(H.items.size()))
+  *bytes = H.dtype == MAGI_DTYPE_BF16 ? magi::workspace_bytes_bf16(H.n_kt_img, H.hk, H.d, H.n_slots, int(H.items.size()))
                                       : 0;
   return MAGI_OK;
 }

@@ -1,4 +1,4 @@
-// Block-causal QK-RMSNorm GQA attention forward, bf16, head_dim 128, gfx950.
+// Block-causal QK-RMSNorm GQA attention forward, bf16, head_dim 64 or 128, gfx950.
 //
 // What is computed follows the MAGI-1 pages (paperlayer §2 / Figure 1 and
 // §2.2.2; paper-notes §3.2.2 block pseudocode and Figure 15): per query row,
@@ -55,6 +55,12 @@
 // follow the video keys' in the workspace. A row that sees no key (a chunk
 // without text) gets out = 0 and lse = -inf.
 //
+// head_dim D is a template parameter (64 or 128): a tile image holds 32 x D
+// bf16 values, so at D = 128 every thread copies 16 bytes of the K image and
+// 16 of the V image per tile, and at D = 64 waves 0-3 copy the K image and
+// waves 4-7 the V image. The S product takes D / 32 K fragments of two 16-key
+// halves, the P V product D / 16 dim blocks.
+//
 // MFMA lane layouts (v_mfma_f32_16x16x32_bf16, lane l, g = l / 16):
 //   A: A[l % 16][8g + j], B: B[8g + j][l % 16] (j = 0..7), D: D[4g + i][l % 16]
 //   (i = 0..3).
@@ -72,26 +78,43 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 #define LDS_PTR(T, p) ((__attribute__((address_space(3))) T*)(p))
 typedef __attribute__((address_space(3))) const bf16x8 lds_bf16x8;
 
-constexpr int D = 128;
 constexpr int BN = 32;                                // keys per tile
 constexpr int NWAVE = 8;                              // two waves per SIMD
 constexpr int NRB = 3;                                // 16-row MFMA blocks per wave
 constexpr int ROWS = NWAVE * NRB * 16;                // 384 rows per workgroup
 constexpr int NTHR = NWAVE * 64;
 constexpr int NSTAGE = 8;                             // LDS ring depth (K and V each)
-constexpr int ROW_BYTES = D * 2;                      // 256
-constexpr int TILE_BYTES = BN * ROW_BYTES;            // 8 KiB
 constexpr int NPRE = 2;                               // K fragments of the next tile read before the barrier
-static_assert(TILE_BYTES == NTHR * 16, "one 16-byte copy per thread per tensor and tile");
 static_assert(ROWS == kBf16RowsPerItem, "rows per work item");
-// The workgroup barrier runs on even steps only. After the barrier of even
-// step i, copies start for K(i+6), V(i+5), K(i+7), V(i+6), in that order, into
-// stages that every wave left before this barrier. Before the barrier of step
-// i, K(i), K(i+1), K(i+2), V(i-1), V(i) must have landed (steps i and i+1 read
-// them; step i+1 reads K(i+2) ahead): everything issued at step i-6 or
-// earlier, plus K(i+2), the first copy issued at step i-4. Up to 7 copies
-// younger than it may still fly.
-constexpr int WAIT_YOUNGER = 7;
+
+// Sizes that depend on head_dim D.
+template <int D>
+struct Geo {
+  static_assert(D == 64 || D == 128, "head_dim");
+  static constexpr int ROW_BYTES = D * 2;
+  static constexpr int TILE_BYTES = BN * ROW_BYTES;   // 8 KiB (D = 128) or 4 KiB (D = 64)
+  static constexpr int NKS = D / 32;                  // 32-dim steps of the S product
+  static constexpr int NKF = 2 * NKS;                 // K fragments per tile (two 16-key halves per step)
+  static constexpr int NDB = D / 16;                  // 16-dim blocks of O
+  static constexpr int COPY_THREADS = TILE_BYTES / 16;  // threads copying one image (16 bytes each)
+  static constexpr bool SPLIT_COPY = COPY_THREADS < NTHR;  // waves 0-3 copy K, waves 4-7 copy V
+  static_assert(COPY_THREADS == NTHR || 2 * COPY_THREADS == NTHR, "copy units");
+  // The workgroup barrier runs on even steps only. After the barrier of even
+  // step i, copies start for K(i+6), V(i+5), K(i+7), V(i+6), in that order,
+  // into stages that every wave left before this barrier. Before the barrier
+  // of step i, K(i), K(i+1), K(i+2), V(i-1), V(i) must have landed (steps i and
+  // i+1 read them; step i+1 reads K(i+2) ahead): everything issued at step
+  // i-6 or earlier, plus K(i+2), the first copy issued at step i-4. A wave
+  // waits for its own copies, the barrier publishes everyone's. When every
+  // wave copies both images (D = 128), up to 7 copies younger than K(i+2) may
+  // still fly. When a wave copies only K (D = 64), 3 may (K(i+3), K(i+4),
+  // K(i+5)); a V wave needs V(i), issued at step i-6, with 4 younger, and
+  // waits for 3 (one copy more than it needs).
+  static constexpr int WAIT_YOUNGER = SPLIT_COPY ? 3 : 7;
+  // Copies of the prologue (even steps -6, -4, -2) per wave, and how many of
+  // them may fly once the wave's first copy (K(0) for a K wave) has landed.
+  static constexpr int PROLOGUE_YOUNGER = SPLIT_COPY ? 5 : 11;
+};
 constexpr unsigned kNoTile = 0x80000000u;             // scalar offset past any tile image buffer (< 2 GiB): zeros
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
@@ -102,9 +125,10 @@ constexpr float kMaxRowSum = 0x1p100f;                //   the item goes to the 
 constexpr float kRescaleSlack = 8.0f;
 constexpr float kNegInf = -__builtin_inff();
 
+template <int D>
 struct Smem {
-  unsigned char k[NSTAGE][TILE_BYTES];
-  unsigned char v[NSTAGE][TILE_BYTES];
+  unsigned char k[NSTAGE][Geo<D>::TILE_BYTES];
+  unsigned char v[NSTAGE][Geo<D>::TILE_BYTES];
   float gqk[D];
 };
 
@@ -177,17 +201,17 @@ __device__ __forceinline__ void wait_vmcnt() {
 __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" : : : "memory"); }
 
 // Tile images. The pre-pass writes every (32-key tile, KV head) of K-hat and
-// of V as an 8 KiB block that is copied byte for byte into an LDS ring stage.
-// Both are chunk-major, so that a 16-lane phase of a ds_read_b128 reads 256
-// contiguous bytes (no bank conflicts) and every fragment address is a
-// per-lane base plus an instruction immediate:
-//   K-hat: [16 chunks][32 keys][16 bytes]: chunk c of key j (dims 8c..8c+7)
-//          at byte 512 c + 16 j;
-//   V^T:   [4 chunks][128 dims][16 bytes]: chunk c of dim row r holds keys
+// of V as a block of 64 D bytes that is copied byte for byte into an LDS ring
+// stage. Both are chunk-major, so that a 16-lane phase of a ds_read_b128
+// reads 256 contiguous bytes (no bank conflicts) and every fragment address is
+// a per-lane base plus an instruction immediate:
+//   K-hat: [D / 8 chunks][32 keys][16 bytes]: chunk c of key j (dims
+//          8c..8c+7) at byte 512 c + 16 j;
+//   V^T:   [4 chunks][D dims][16 bytes]: chunk c of dim row r holds keys
 //          4c + {0..3} and 16 + 4c + {0..3} (the key order of a lane's P
-//          fragment, see softmax_tile) at byte 2048 c + 16 r.
-// Images are stored [tile][KV head], so thread t copies bytes [16t, 16t + 16)
-// of one image.
+//          fragment, see softmax_tile) at byte 16 D c + 16 r.
+// Images are stored [tile][KV head], so copy thread t copies bytes
+// [16t, 16t + 16) of one image.
 struct LaneOffsets {
   unsigned dma;      // buffer offset of this thread's copy unit (the tile part goes in the scalar offset)
   unsigned kq;       // K ring, stage 0: fragment (ks, kb) at kq + 2048 ks + 256 kb
@@ -196,20 +220,22 @@ struct LaneOffsets {
   // stay instruction immediates wherever the rings lie in LDS.
 };
 
+template <int D>
 __device__ __forceinline__ LaneOffsets lane_offsets(int tid, int kvh, unsigned k_ring, unsigned v_ring) {
   LaneOffsets o;
   const int lane = tid & 63;
-  o.dma = unsigned(kvh) * TILE_BYTES + unsigned(tid) * 16;
+  o.dma = unsigned(kvh) * Geo<D>::TILE_BYTES + unsigned(tid % Geo<D>::COPY_THREADS) * 16;
   o.kq = k_ring + unsigned((lane >> 4) * 512 + (lane & 15) * 16);
-  o.vq = v_ring + unsigned((lane >> 4) * 2048 + (lane & 15) * 16);
+  o.vq = v_ring + unsigned((lane >> 4) * 16 * D + (lane & 15) * 16);
   asm("" : "+v"(o.kq));
   asm("" : "+v"(o.vq));
   return o;
 }
 
+template <int D>
 struct WaveState {
-  bf16x8 qf[NRB][4];     // B operands of S^T: row (l & 15) of block rb, dims 32 ks + 8 (l >> 4) ..
-  f32x4 o[NRB][8];       // O^T accumulators: row (l & 15), dims 16 db + 4 (l >> 4) + i
+  bf16x8 qf[NRB][Geo<D>::NKS];  // B operands of S^T: row (l & 15) of block rb, dims 32 ks + 8 (l >> 4) ..
+  f32x4 o[NRB][Geo<D>::NDB];    // O^T accumulators: row (l & 15), dims 16 db + 4 (l >> 4) + i
   bf16x8 p[NRB];         // P of the previous tile (B operands of P V)
   bf16x8 kpre[NPRE];     // first K fragments of the current tile, read before the barrier
   f32x4 s0;              // initial S accumulator: -b, the wave's softmax shift (0 on the online path)
@@ -220,19 +246,21 @@ struct WaveState {
 
 // K fragment f = 2 ks + kb of the tile in K stage kstage: keys 16 kb + (l & 15),
 // dims 32 ks + 8 (l >> 4) ..
+template <int D>
 __device__ __forceinline__ bf16x8 k_frag(const LaneOffsets& lo, int kstage, int f) {
-  return *(lds_bf16x8*)(size_t)(lo.kq + unsigned(kstage * TILE_BYTES + (f >> 1) * 2048 + (f & 1) * 256));
+  return *(lds_bf16x8*)(size_t)(lo.kq + unsigned(kstage * Geo<D>::TILE_BYTES + (f >> 1) * 2048 + (f & 1) * 256));
 }
 
 // Phase 1: S^T(tile in K stage kstage); its first NPRE K fragments are in st.kpre.
-__device__ __forceinline__ void qk_tile(int kstage, const LaneOffsets& lo, const WaveState& st,
+template <int D>
+__device__ __forceinline__ void qk_tile(int kstage, const LaneOffsets& lo, const WaveState<D>& st,
                                         f32x4 (&s)[NRB][2]) {
 #pragma unroll
   for (int rb = 0; rb < NRB; ++rb) s[rb][0] = s[rb][1] = st.s0;
 #pragma unroll
-  for (int f = 0; f < 8; ++f) {
+  for (int f = 0; f < Geo<D>::NKF; ++f) {
     const int ks = f >> 1, kb = f & 1;
-    const bf16x8 a = f < NPRE ? st.kpre[f < NPRE ? f : 0] : k_frag(lo, kstage, f);
+    const bf16x8 a = f < NPRE ? st.kpre[f < NPRE ? f : 0] : k_frag<D>(lo, kstage, f);
 #pragma unroll
     for (int rb = 0; rb < NRB; ++rb)
       s[rb][kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, st.qf[rb][ks], s[rb][kb], 0, 0, 0);
@@ -242,15 +270,17 @@ __device__ __forceinline__ void qk_tile(int kstage, const LaneOffsets& lo, const
 // Phase 2 (MFMA part): O^T += V^T P^T for one tile. The A operand of dim
 // block db is one 16-byte chunk of the V^T image: dims 16 db + (l & 15), the
 // 8 keys of chunk (l >> 4), in the order of the lane's P fragment.
+template <int D>
 __device__ __forceinline__ bf16x8 v_frag(const LaneOffsets& lo, int vstage, int db) {
-  return *(lds_bf16x8*)(size_t)(lo.vq + unsigned(vstage * TILE_BYTES + db * 256));
+  return *(lds_bf16x8*)(size_t)(lo.vq + unsigned(vstage * Geo<D>::TILE_BYTES + db * 256));
 }
 
-__device__ __forceinline__ void pv_tile(int vstage, const LaneOffsets& lo, const bf16x8 (&p)[NRB], WaveState& st,
+template <int D>
+__device__ __forceinline__ void pv_tile(int vstage, const LaneOffsets& lo, const bf16x8 (&p)[NRB], WaveState<D>& st,
                                         const bf16x8* vpre = nullptr) {
 #pragma unroll
-  for (int db = 0; db < 8; ++db) {
-    const bf16x8 a = (vpre && db < 2) ? vpre[db < 2 ? db : 0] : v_frag(lo, vstage, db);
+  for (int db = 0; db < Geo<D>::NDB; ++db) {
+    const bf16x8 a = (vpre && db < 2) ? vpre[db < 2 ? db : 0] : v_frag<D>(lo, vstage, db);
 #pragma unroll
     for (int rb = 0; rb < NRB; ++rb)
       st.o[rb][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, p[rb], st.o[rb][db], 0, 0, 0);
@@ -260,8 +290,8 @@ __device__ __forceinline__ void pv_tile(int vstage, const LaneOffsets& lo, const
 // Vector part: S -> P for one tile. Lane l holds, for row (l & 15) of each
 // row block, keys 16 kb + 4 g + i (g = l >> 4; kb = 0, 1; i = 0..3); P element
 // j of the B operand is key 16 (j / 4) + 4 g + (j % 4).
-template <bool MASKED, bool STATIC>
-__device__ __forceinline__ void softmax_tile(f32x4 (&s)[NRB][2], int kt, WaveState& st, bf16x8 (&p)[NRB],
+template <bool MASKED, bool STATIC, int D>
+__device__ __forceinline__ void softmax_tile(f32x4 (&s)[NRB][2], int kt, WaveState<D>& st, bf16x8 (&p)[NRB],
                                              float (&alpha)[NRB], int lane) {
   const int g = lane >> 4;
 #pragma unroll
@@ -321,22 +351,36 @@ struct LoopCtx {
   const int* tiles;           // this item's key tile codes (for the boundary mask)
   const unsigned* soffs;      // this item's tile copy offsets; kNoTile in the padding after the list
   int n_tiles;
+  // split copies (D = 64): whether this wave copies the K image (else the V
+  // image), and that image's buffer resource and LDS ring base
+  bool kwave;
+  i32x4 rs_own;
+  unsigned own_base;
 };
 
 // Starts the copies of the K tile image at scalar offset sk into stage js and
-// of the V image at sv into stage jvs (kNoTile: zeros).
+// of the V image at sv into stage jvs (kNoTile: zeros). With split copies a
+// wave issues only its own image's copy.
+template <int D>
 __device__ __forceinline__ void issue_copies(const LoopCtx& c, const LaneOffsets& lo, unsigned sk, int js, unsigned sv,
                                              int jvs) {
-  dma16(c.rsk, lo.dma, sk, c.k_base + js * TILE_BYTES);
-  dma16(c.rsv, lo.dma, sv, c.v_base + jvs * TILE_BYTES);
+  constexpr int TB = Geo<D>::TILE_BYTES;
+  if constexpr (Geo<D>::SPLIT_COPY) {
+    // wave-uniform selects, no branch: the unrolled steps stay one block
+    dma16(c.rs_own, lo.dma, c.kwave ? sk : sv, c.own_base + unsigned(c.kwave ? js : jvs) * TB);
+  } else {
+    dma16(c.rsk, lo.dma, sk, c.k_base + js * TB);
+    dma16(c.rsv, lo.dma, sv, c.v_base + jvs * TB);
+  }
 }
 
 // Reads the first NPRE K fragments of the tile in K stage kstage into
 // st.kpre; their latency is spent before the next barrier, where the wave
 // waits anyway.
-__device__ __forceinline__ void prefetch_k(int kstage, const LaneOffsets& lo, WaveState& st) {
+template <int D>
+__device__ __forceinline__ void prefetch_k(int kstage, const LaneOffsets& lo, WaveState<D>& st) {
 #pragma unroll
-  for (int f = 0; f < NPRE; ++f) st.kpre[f] = k_frag(lo, kstage, f);
+  for (int f = 0; f < NPRE; ++f) st.kpre[f] = k_frag<D>(lo, kstage, f);
 }
 
 // One step i. The stage of tile j is j % NSTAGE; callers that know i % NSTAGE
@@ -347,35 +391,36 @@ __device__ __forceinline__ void prefetch_k(int kstage, const LaneOffsets& lo, Wa
 // the softmax of S(i) between its MFMAs, and the first K fragments of tile
 // i+1 (published at this or the previous barrier).
 // so4: copy offsets of K(i+6), K(i+7), V(i+5), V(i+6); used on even steps.
-template <bool MASKED, bool STATIC>
-__device__ __forceinline__ void tile_step(const LoopCtx& c, const LaneOffsets& lo, WaveState& st, int i, int si,
+template <bool MASKED, bool STATIC, int D>
+__device__ __forceinline__ void tile_step(const LoopCtx& c, const LaneOffsets& lo, WaveState<D>& st, int i, int si,
                                           bool sync, const unsigned (&so4)[4], int lane) {
+  constexpr int NKF = Geo<D>::NKF, NDB = Geo<D>::NDB;
   if (sync) {
-    wait_vmcnt<WAIT_YOUNGER>();
+    wait_vmcnt<Geo<D>::WAIT_YOUNGER>();
     lds_barrier();
-    issue_copies(c, lo, so4[0], (si + 6) % NSTAGE, so4[2], (si + 5) % NSTAGE);
-    issue_copies(c, lo, so4[1], (si + 7) % NSTAGE, so4[3], (si + 6) % NSTAGE);
+    issue_copies<D>(c, lo, so4[0], (si + 6) % NSTAGE, so4[2], (si + 5) % NSTAGE);
+    issue_copies<D>(c, lo, so4[1], (si + 7) % NSTAGE, so4[3], (si + 6) % NSTAGE);
   }
   const int vst = (si + NSTAGE - 1) % NSTAGE;
   f32x4 s[NRB][2];
-  qk_tile(si, lo, st, s);
+  qk_tile<D>(si, lo, st, s);
   bf16x8 vpre[2];
-  vpre[0] = v_frag(lo, vst, 0);
-  vpre[1] = v_frag(lo, vst, 1);
+  vpre[0] = v_frag<D>(lo, vst, 0);
+  vpre[1] = v_frag<D>(lo, vst, 1);
   if (STATIC && !MASKED) {
     // region 1: K reads two ahead of the S MFMAs, then the first V reads
     __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
 #pragma unroll
-    for (int f = 0; f < 8; ++f) {
+    for (int f = 0; f < NKF; ++f) {
       __builtin_amdgcn_sched_group_barrier(0x008, NRB, 0);
-      if (f < 8 - NPRE) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      if (f < NKF - NPRE) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
     }
     __builtin_amdgcn_sched_barrier(0);
   }
-  pv_tile(vst, lo, st.p, st, vpre);
+  pv_tile<D>(vst, lo, st.p, st, vpre);
   bf16x8 p[NRB];
   float alpha[NRB];
-  softmax_tile<MASKED, STATIC>(s, MASKED ? (c.tiles[i] >> 1) : 0, st, p, alpha, lane);
+  softmax_tile<MASKED, STATIC, D>(s, MASKED ? (c.tiles[i] >> 1) : 0, st, p, alpha, lane);
   if (!STATIC) {
     bool any = false;
 #pragma unroll
@@ -384,19 +429,20 @@ __device__ __forceinline__ void tile_step(const LoopCtx& c, const LaneOffsets& l
 #pragma unroll
       for (int rb = 0; rb < NRB; ++rb)
 #pragma unroll
-        for (int db = 0; db < 8; ++db) st.o[rb][db] *= alpha[rb];
+        for (int db = 0; db < NDB; ++db) st.o[rb][db] *= alpha[rb];
     }
   }
 #pragma unroll
   for (int rb = 0; rb < NRB; ++rb) st.p[rb] = p[rb];
-  prefetch_k((si + 1) % NSTAGE, lo, st);
+  prefetch_k<D>((si + 1) % NSTAGE, lo, st);
   if (STATIC && !MASKED) {
-    // region 2: P V MFMAs with the next V read and the softmax of S(i) between them
+    // region 2: P V MFMAs with the next V read and the softmax of S(i) between
+    // them (the softmax's vector work per tile does not depend on D)
 #pragma unroll
-    for (int db = 0; db < 8; ++db) {
+    for (int db = 0; db < NDB; ++db) {
       __builtin_amdgcn_sched_group_barrier(0x008, NRB, 0);
-      if (db < 6) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x402, 2 * NRB, 0);
+      if (db < NDB - 2) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x402, 2 * NRB * (8 / NDB), 0);
     }
     __builtin_amdgcn_sched_group_barrier(0x100, NPRE, 0);
   }
@@ -411,12 +457,12 @@ __device__ __forceinline__ void step_offsets(const unsigned* soffs, int i, unsig
 }
 
 // so[u] is the copy offset of tile i0 + 5 + u.
-template <bool STATIC, int U>
-__device__ __forceinline__ void unrolled_steps(const LoopCtx& c, const LaneOffsets& lo, WaveState& st, int i0,
+template <bool STATIC, int U, int D>
+__device__ __forceinline__ void unrolled_steps(const LoopCtx& c, const LaneOffsets& lo, WaveState<D>& st, int i0,
                                                const unsigned (&so)[NSTAGE + 1], int lane) {
   const unsigned so4[4] = {so[U + 1], so[U + 2], so[U], so[U + 1]};
-  tile_step<false, STATIC>(c, lo, st, i0 + U, U, (U & 1) == 0, so4, lane);
-  if constexpr (U + 1 < NSTAGE) unrolled_steps<STATIC, U + 1>(c, lo, st, i0, so, lane);
+  tile_step<false, STATIC, D>(c, lo, st, i0 + U, U, (U & 1) == 0, so4, lane);
+  if constexpr (U + 1 < NSTAGE) unrolled_steps<STATIC, U + 1, D>(c, lo, st, i0, so, lane);
 }
 
 // Whether keys [lo, hi) meet any tile of the item's list (used only for rows
@@ -436,8 +482,8 @@ __device__ __forceinline__ bool row_sees_a_tile(const LoopCtx& c, int lo, int hi
 // are read up to 7 entries past the list, which the list's padding covers.
 // The last tile's P V runs after the loop, behind one more barrier when the
 // last step had none (V(n-1) was then not yet published).
-template <bool STATIC>
-__device__ __forceinline__ void run_tiles(const LoopCtx& c, const LaneOffsets& lo, int n_full, WaveState& st,
+template <bool STATIC, int D>
+__device__ __forceinline__ void run_tiles(const LoopCtx& c, const LaneOffsets& lo, int n_full, WaveState<D>& st,
                                           int lane) {
   const int n = c.n_tiles;
   int i = 0;
@@ -445,30 +491,31 @@ __device__ __forceinline__ void run_tiles(const LoopCtx& c, const LaneOffsets& l
     unsigned so[NSTAGE + 1];
 #pragma unroll
     for (int u = 0; u <= NSTAGE; ++u) so[u] = c.soffs[i + 5 + u];
-    unrolled_steps<STATIC, 0>(c, lo, st, i, so, lane);
+    unrolled_steps<STATIC, 0, D>(c, lo, st, i, so, lane);
   }
   for (; i < n_full; ++i) {
     unsigned so4[4];
     step_offsets(c.soffs, i, so4);
-    tile_step<false, STATIC>(c, lo, st, i, i % NSTAGE, (i & 1) == 0, so4, lane);
+    tile_step<false, STATIC, D>(c, lo, st, i, i % NSTAGE, (i & 1) == 0, so4, lane);
   }
   for (; i < n; ++i) {
     unsigned so4[4];
     step_offsets(c.soffs, i, so4);
-    tile_step<true, STATIC>(c, lo, st, i, i % NSTAGE, (i & 1) == 0, so4, lane);
+    tile_step<true, STATIC, D>(c, lo, st, i, i % NSTAGE, (i & 1) == 0, so4, lane);
   }
   if ((n & 1) == 0) {
     wait_vmcnt<0>();
     lds_barrier();
   }
-  pv_tile((n + NSTAGE - 1) % NSTAGE, lo, st.p, st);
+  pv_tile<D>((n + NSTAGE - 1) % NSTAGE, lo, st.p, st);
 }
 
-template <bool STATIC>
+template <bool STATIC, int D>
 __global__ void __launch_bounds__(NTHR) __attribute__((amdgpu_waves_per_eu(2, 2)))
-fwd_bf16_d128_kernel(FwdParams prm, const int4* __restrict__ items, const int* __restrict__ tiles,
-                     const unsigned* __restrict__ soffs, const int2* __restrict__ rows) {
-  __shared__ __attribute__((aligned(1024))) Smem sm;
+fwd_bf16_kernel(FwdParams prm, const int4* __restrict__ items, const int* __restrict__ tiles,
+                const unsigned* __restrict__ soffs, const int2* __restrict__ rows) {
+  using G = Geo<D>;
+  __shared__ __attribute__((aligned(1024))) Smem<D> sm;
   const int4 item = items[2 * blockIdx.x];
   if (item.z == item.w) return;                       // padding item
   const int4 item2 = items[2 * blockIdx.x + 1];
@@ -491,7 +538,7 @@ fwd_bf16_d128_kernel(FwdParams prm, const int4* __restrict__ items, const int* _
   const int tb = item.z, n_tiles = item.w - item.z;
 
   // Row r of the item (0..383) is token t0 + r % tile_q of head h0 + r / tile_q.
-  WaveState st;
+  WaveState<D> st;
   int tok[NRB], head[NRB];
   bool valid[NRB];
 #pragma unroll
@@ -502,52 +549,58 @@ fwd_bf16_d128_kernel(FwdParams prm, const int4* __restrict__ items, const int* _
     valid[rb] = tok[rb] < prm.tq;
   }
   // ---- query loads first (older than every K/V copy)
-  bf16x8 qr[NRB][4];
+  bf16x8 qr[NRB][G::NKS];
 #pragma unroll
   for (int rb = 0; rb < NRB; ++rb) {
     const __bf16* qrow =
         reinterpret_cast<const __bf16*>(px ? prm.qx : prm.q) + (size_t(tok[rb]) * prm.hq + head[rb]) * D;
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks)
+    for (int ks = 0; ks < G::NKS; ++ks)
       qr[rb][ks] = valid[rb] ? *reinterpret_cast<const bf16x8*>(qrow + ks * 32 + g * 8) : bf16x8{};
   }
 
   // ---- K/V copies ahead of the first step
-  const unsigned img_bytes = unsigned(prm.n_kt_img) * unsigned(prm.hk) * unsigned(TILE_BYTES);
-  const LaneOffsets lo = lane_offsets(tid, kvh, lds_addr(&sm.k[0][0]), lds_addr(&sm.v[0][0]));
+  const unsigned img_bytes = unsigned(prm.n_kt_img) * unsigned(prm.hk) * unsigned(G::TILE_BYTES);
+  const LaneOffsets lo = lane_offsets<D>(tid, kvh, lds_addr(&sm.k[0][0]), lds_addr(&sm.v[0][0]));
+  // copy wave w writes its 1 KiB block of every image (w % 4 with split copies)
+  const int cwave = G::SPLIT_COPY ? (wave & 3) : wave;
   LoopCtx ctx;
   ctx.rsk = make_rsrc(prm.ws, img_bytes);
   ctx.rsv = make_rsrc(static_cast<const unsigned char*>(prm.ws) + img_bytes, img_bytes);
-  ctx.k_base = __builtin_amdgcn_readfirstlane(lds_addr(&sm.k[0][0])) + wave * 1024;
-  ctx.v_base = __builtin_amdgcn_readfirstlane(lds_addr(&sm.v[0][0])) + wave * 1024;
+  ctx.k_base = __builtin_amdgcn_readfirstlane(lds_addr(&sm.k[0][0])) + cwave * 1024;
+  ctx.v_base = __builtin_amdgcn_readfirstlane(lds_addr(&sm.v[0][0])) + cwave * 1024;
   ctx.tiles = tiles + tb;
   ctx.soffs = soffs + tb;
   ctx.n_tiles = n_tiles;
+  ctx.kwave = __builtin_amdgcn_readfirstlane(wave < 4 ? 1 : 0) != 0;
+  ctx.rs_own = ctx.kwave ? ctx.rsk : ctx.rsv;
+  ctx.own_base = ctx.kwave ? ctx.k_base : ctx.v_base;
   // the copies of even steps -6, -4, -2 (V(-1) is a zero tile)
 #pragma unroll
   for (int j = -6; j < 0; j += 2) {
-    issue_copies(ctx, lo, ctx.soffs[j + 6], (j + 6 + NSTAGE) % NSTAGE, j + 5 >= 0 ? ctx.soffs[j + 5] : kNoTile,
-                 (j + 5 + NSTAGE) % NSTAGE);
-    issue_copies(ctx, lo, ctx.soffs[j + 7], (j + 7 + NSTAGE) % NSTAGE, ctx.soffs[j + 6], (j + 6 + NSTAGE) % NSTAGE);
+    issue_copies<D>(ctx, lo, ctx.soffs[j + 6], (j + 6 + NSTAGE) % NSTAGE, j + 5 >= 0 ? ctx.soffs[j + 5] : kNoTile,
+                    (j + 5 + NSTAGE) % NSTAGE);
+    issue_copies<D>(ctx, lo, ctx.soffs[j + 7], (j + 7 + NSTAGE) % NSTAGE, ctx.soffs[j + 6],
+                    (j + 6 + NSTAGE) % NSTAGE);
   }
 
   if (tid < D)
     sm.gqk[tid] = px ? prm.q_gain_x[tid] * prm.k_gain_x[tid] * (prm.scale_x * kLog2e)
                      : prm.q_gain[tid] * prm.k_gain[tid] * (prm.scale * kLog2e);
-  wait_vmcnt<11>();                                   // K(0), the oldest of the 12 copies, landed
+  wait_vmcnt<G::PROLOGUE_YOUNGER>();                  // the wave's oldest copy (K(0) on a K-copying wave) landed
   __syncthreads();                                     // gqk and K(0) visible
-  prefetch_k(0, lo, st);
+  prefetch_k<D>(0, lo, st);
 
   // ---- query prologue: RMS-normalise, fold gains/temperature, to bf16
 #pragma unroll
   for (int rb = 0; rb < NRB; ++rb) {
     float ss = 0.0f;
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) ss = sumsq8(qr[rb][ks], ss);
+    for (int ks = 0; ks < G::NKS; ++ks) ss = sumsq8(qr[rb][ks], ss);
     ss = sum_groups(ss);
     const float rq = valid[rb] ? __builtin_amdgcn_rsqf(ss * (1.0f / D) + prm.eps) : 0.0f;
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
+    for (int ks = 0; ks < G::NKS; ++ks) {
       const int d0 = ks * 32 + g * 8;
       const f32x4 g0 = *LDS_PTR(const f32x4, &sm.gqk[d0]);
       const f32x4 g1 = *LDS_PTR(const f32x4, &sm.gqk[d0 + 4]);
@@ -558,7 +611,7 @@ fwd_bf16_d128_kernel(FwdParams prm, const int4* __restrict__ items, const int* _
     st.lo[rb] = b.x;
     st.hi[rb] = b.y;
 #pragma unroll
-    for (int db = 0; db < 8; ++db) st.o[rb][db] = f32x4{};
+    for (int db = 0; db < G::NDB; ++db) st.o[rb][db] = f32x4{};
     st.p[rb] = bf16x8{};                                      // tile -1: P = 0
     st.lsum[rb] = 0.0f;
     st.m[rb] = kNegInf;
@@ -572,7 +625,7 @@ fwd_bf16_d128_kernel(FwdParams prm, const int4* __restrict__ items, const int* _
     for (int rb = 0; rb < NRB; ++rb) {
       float ss = 0.0f;
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks) ss = sumsq8(st.qf[rb][ks], ss);
+      for (int ks = 0; ks < G::NKS; ++ks) ss = sumsq8(st.qf[rb][ks], ss);
       qq = fmaxf(qq, sum_groups(ss));
     }
 #pragma unroll
@@ -582,7 +635,7 @@ fwd_bf16_d128_kernel(FwdParams prm, const int4* __restrict__ items, const int* _
                                           __builtin_bit_cast(int, fmaxf(0.0f, bound - kStaticBound))));
   }
   st.s0 = f32x4{-shift, -shift, -shift, -shift};
-  run_tiles<STATIC>(ctx, lo, n_full, st, lane);
+  run_tiles<STATIC, D>(ctx, lo, n_full, st, lane);
 
   // ---- epilogue: lane l holds dims 16 db + 4 g + i of row (l & 15) per block
   // (row coordinates recomputed rather than kept live through the loop)
@@ -615,7 +668,8 @@ fwd_bf16_d128_kernel(FwdParams prm, const int4* __restrict__ items, const int* _
       const float lsum = lsr[rb];
       const size_t r = size_t(slot) * ROWS + size_t((wave * NRB + rb) * 16 + (lane & 15));
 #pragma unroll
-      for (int db = 0; db < 8; ++db) *reinterpret_cast<f32x4*>(prm.part_o + r * D + db * 16 + g * 4) = st.o[rb][db];
+      for (int db = 0; db < G::NDB; ++db)
+        *reinterpret_cast<f32x4*>(prm.part_o + r * D + db * 16 + g * 4) = st.o[rb][db];
       if (g == 0) *reinterpret_cast<float2*>(prm.part_ml + r * 2) = float2{STATIC ? shift : st.m[rb], lsum};
     }
     return;
@@ -630,7 +684,7 @@ fwd_bf16_d128_kernel(FwdParams prm, const int4* __restrict__ items, const int* _
       const float inv = any ? 1.0f / lsum : 0.0f;
       __bf16* orow = obase + (size_t(tok[rb]) * prm.hq + head[rb]) * D;
 #pragma unroll
-      for (int db = 0; db < 8; ++db) {
+      for (int db = 0; db < G::NDB; ++db) {
         bf16x4 w;
 #pragma unroll
         for (int i = 0; i < 4; ++i) w[i] = (__bf16)(st.o[rb][db][i] * inv);
@@ -652,6 +706,7 @@ fwd_bf16_d128_kernel(FwdParams prm, const int4* __restrict__ items, const int* _
 // Workgroups [0, n0) cover the first key stream (k, v, tk); a parallel
 // plan's text keys (kx, vx, tkx) follow, so image block b is workgroup b.
 constexpr int PP_THREADS = 256;
+template <int D>
 __global__ void __launch_bounds__(PP_THREADS) kv_prepare_kernel(const __bf16* __restrict__ k0,
                                                                 const __bf16* __restrict__ v0,
                                                                 const __bf16* __restrict__ k1,
@@ -659,19 +714,21 @@ __global__ void __launch_bounds__(PP_THREADS) kv_prepare_kernel(const __bf16* __
                                                                 unsigned char* __restrict__ kimg,
                                                                 unsigned char* __restrict__ vimg, int tk0, int tk1,
                                                                 int n0, int hk, float eps) {
-  __shared__ __attribute__((aligned(16))) unsigned char vs[TILE_BYTES];
+  constexpr int ROW_BYTES = Geo<D>::ROW_BYTES, CHUNKS = D / 8;   // 16-byte chunks per key row
+  constexpr int ROUNDS = BN * CHUNKS / PP_THREADS;                // 2 (D = 128) or 1 (D = 64)
+  __shared__ __attribute__((aligned(16))) unsigned char vs[Geo<D>::TILE_BYTES];
   const bool second = int(blockIdx.x) >= n0;
   const int b = second ? int(blockIdx.x) - n0 : int(blockIdx.x);
   const __bf16* const k = second ? k1 : k0;
   const __bf16* const v = second ? v1 : v0;
   const int tk = second ? tk1 : tk0;
   const int kt = b / hk, kvh = b % hk;
-  const size_t img = size_t(blockIdx.x) * TILE_BYTES;
+  const size_t img = size_t(blockIdx.x) * Geo<D>::TILE_BYTES;
   const int tid = threadIdx.x;
 #pragma unroll
-  for (int r = 0; r < 2; ++r) {
-    const int u = tid + r * PP_THREADS;        // key u / 16, 16-byte chunk u % 16; 16 lanes per key
-    const int key = u >> 4, c = u & 15;
+  for (int r = 0; r < ROUNDS; ++r) {
+    const int u = tid + r * PP_THREADS;        // key u / CHUNKS, 16-byte chunk u % CHUNKS; CHUNKS lanes per key
+    const int key = u / CHUNKS, c = u % CHUNKS;
     const int tok = kt * BN + key;
     bf16x8 x = {}, y = {};
     if (tok < tk) {
@@ -683,7 +740,7 @@ __global__ void __launch_bounds__(PP_THREADS) kv_prepare_kernel(const __bf16* __
     ss += dpp<0xB1>(ss);                  // quad_perm [1,0,3,2]
     ss += dpp<0x4E>(ss);                  // quad_perm [2,3,0,1]
     ss += dpp<0x141>(ss);                 // row_half_mirror: the other quad of 8 lanes
-    ss += dpp<0x140>(ss);                 // row_mirror: the other half of the 16 lanes
+    if constexpr (CHUNKS == 16) ss += dpp<0x140>(ss);   // row_mirror: the other half of the 16 lanes
     const float rk = tok < tk ? __builtin_amdgcn_rsqf(ss * (1.0f / D) + eps) : 0.0f;
     bf16x8 xn;
 #pragma unroll
@@ -693,9 +750,9 @@ __global__ void __launch_bounds__(PP_THREADS) kv_prepare_kernel(const __bf16* __
   }
   __syncthreads();
 #pragma unroll
-  for (int r = 0; r < 2; ++r) {
-    const int u = tid + r * PP_THREADS;        // V^T unit: chunk u / 128, dim row u % 128
-    const int c = u >> 7, d = u & 127;
+  for (int r = 0; r < ROUNDS; ++r) {
+    const int u = tid + r * PP_THREADS;        // V^T unit: chunk u / D, dim row u % D
+    const int c = u / D, d = u % D;
     bf16x8 w;
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
@@ -713,14 +770,16 @@ __global__ void __launch_bounds__(PP_THREADS) kv_prepare_kernel(const __bf16* __
 // entry without pieces (rows that see no key) writes out = 0, lse = -inf, as
 // does a row whose pieces saw no key.
 constexpr int MG_THREADS = 256;
+template <int D>
 __global__ void __launch_bounds__(MG_THREADS) merge_kernel(FwdParams prm) {
+  constexpr int CPR = D / 16;                          // threads per row
   const int4 mi = prm.merges[2 * blockIdx.x];
   const bool px = prm.merges[2 * blockIdx.x + 1].x != 0;
   __bf16* const obase = reinterpret_cast<__bf16*>(px ? prm.outx : prm.out);
   float* const lbase = px ? prm.lsex : prm.lse;
   const int h0 = mi.y & 0xffff;
-  for (int u = threadIdx.x; u < ROWS * 8; u += MG_THREADS) {
-    const int r = u >> 3, c = u & 7;
+  for (int u = threadIdx.x; u < ROWS * CPR; u += MG_THREADS) {
+    const int r = u / CPR, c = u % CPR;
     const int head = h0 + r / prm.tile_q, tok = mi.x + r % prm.tile_q;
     if (tok >= prm.tq) continue;
     float mmax = kNegInf;
@@ -752,19 +811,12 @@ __global__ void __launch_bounds__(MG_THREADS) merge_kernel(FwdParams prm) {
   }
 }
 
-size_t image_bytes_bf16(long long n_kt_img, int hk) { return size_t(n_kt_img) * size_t(hk) * TILE_BYTES; }
+size_t image_bytes_bf16(long long n_kt_img, int hk, int d) { return size_t(n_kt_img) * size_t(hk) * BN * d * 2; }
 
-}  // namespace
-
-size_t workspace_bytes_bf16(long long n_kt_img, int hk, int n_slots, int n_items) {
-  // K-hat images, V^T images, partial O, partial (m, l), per-wave item flags
-  return 2 * image_bytes_bf16(n_kt_img, hk) + size_t(n_slots) * ROWS * (D + 2) * sizeof(float) +
-         size_t(n_items) * NWAVE * sizeof(int);
-}
-
-hipError_t launch_fwd_bf16_d128(const FwdParams& prm, int n_items, int n_merges, int n_slots, hipStream_t stream) {
+template <int D>
+hipError_t launch_fwd_bf16_d(const FwdParams& prm, int n_items, int n_merges, int n_slots, hipStream_t stream) {
   FwdParams p = prm;
-  const size_t img = image_bytes_bf16(p.n_kt_img, p.hk);
+  const size_t img = image_bytes_bf16(p.n_kt_img, p.hk, D);
   p.part_o = reinterpret_cast<float*>(static_cast<unsigned char*>(p.ws) + 2 * img);
   p.part_ml = p.part_o + size_t(n_slots) * ROWS * D;
   p.item_flag = reinterpret_cast<int*>(p.part_ml + size_t(n_slots) * ROWS * 2);
@@ -772,7 +824,7 @@ hipError_t launch_fwd_bf16_d128(const FwdParams& prm, int n_items, int n_merges,
     if (p.n_kt_img > 0) {
       unsigned char* kimg = static_cast<unsigned char*>(p.ws);
       const int n0 = (p.tk + BN - 1) / BN * p.hk;
-      hipLaunchKernelGGL(kv_prepare_kernel, dim3(unsigned(p.n_kt_img) * unsigned(p.hk)), dim3(PP_THREADS), 0, stream,
+      hipLaunchKernelGGL(kv_prepare_kernel<D>, dim3(unsigned(p.n_kt_img) * unsigned(p.hk)), dim3(PP_THREADS), 0, stream,
                          static_cast<const __bf16*>(p.k), static_cast<const __bf16*>(p.v),
                          static_cast<const __bf16*>(p.kx), static_cast<const __bf16*>(p.vx), kimg, kimg + img, p.tk,
                          p.tkx, n0, p.hk, p.eps);
@@ -781,16 +833,31 @@ hipError_t launch_fwd_bf16_d128(const FwdParams& prm, int n_items, int n_merges,
     }
     // The static instance runs every item and flags the ones whose row sums
     // it lost; the running-maximum instance redoes only those.
-    hipLaunchKernelGGL(fwd_bf16_d128_kernel<true>, dim3(n_items), dim3(NTHR), 0, stream, p, p.items, p.tiles,
+    hipLaunchKernelGGL((fwd_bf16_kernel<true, D>), dim3(n_items), dim3(NTHR), 0, stream, p, p.items, p.tiles,
                        p.soffs, p.rows);
-    hipLaunchKernelGGL(fwd_bf16_d128_kernel<false>, dim3(n_items), dim3(NTHR), 0, stream, p, p.items, p.tiles,
+    hipLaunchKernelGGL((fwd_bf16_kernel<false, D>), dim3(n_items), dim3(NTHR), 0, stream, p, p.items, p.tiles,
                        p.soffs, p.rows);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   if (n_merges == 0) return hipSuccess;
-  hipLaunchKernelGGL(merge_kernel, dim3(n_merges), dim3(MG_THREADS), 0, stream, p);
+  hipLaunchKernelGGL(merge_kernel<D>, dim3(n_merges), dim3(MG_THREADS), 0, stream, p);
   return hipGetLastError();
+}
+
+}  // namespace
+
+size_t workspace_bytes_bf16(long long n_kt_img, int hk, int head_dim, int n_slots, int n_items) {
+  // K-hat images, V^T images, partial O, partial (m, l), per-wave item flags
+  return 2 * image_bytes_bf16(n_kt_img, hk, head_dim) + size_t(n_slots) * ROWS * (head_dim + 2) * sizeof(float) +
+         size_t(n_items) * NWAVE * sizeof(int);
+}
+
+hipError_t launch_fwd_bf16(const FwdParams& p, int head_dim, int n_items, int n_merges, int n_slots,
+                           hipStream_t stream) {
+  if (head_dim == 128) return launch_fwd_bf16_d<128>(p, n_items, n_merges, n_slots, stream);
+  if (head_dim == 64) return launch_fwd_bf16_d<64>(p, n_items, n_merges, n_slots, stream);
+  return hipErrorInvalidValue;
 }
 
 }  // namespace magi

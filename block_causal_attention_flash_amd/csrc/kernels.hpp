@@ -115,8 +115,9 @@ hipError_t launch_bwd_zero_rows(const BwdParams& p, int row_bytes, hipStream_t s
 size_t bwd_workspace_bytes_fp32(long long tq, long long tk, int hq, int hk, int head_dim, int n_dq_items,
                                 int n_kv_items);
 
-hipError_t launch_fwd_bf16_d128(const FwdParams& p, int n_items, int n_merges, int n_slots, hipStream_t stream);
-size_t workspace_bytes_bf16(long long n_kt_img, int hk, int n_slots, int n_items);
+hipError_t launch_fwd_bf16(const FwdParams& p, int head_dim, int n_items, int n_merges, int n_slots,
+                           hipStream_t stream);
+size_t workspace_bytes_bf16(long long n_kt_img, int hk, int head_dim, int n_slots, int n_items);
 hipError_t launch_fwd_fp32(const FwdParams& p, int head_dim, int n_items, int n_merges, hipStream_t stream);
 
 }  // namespace magi

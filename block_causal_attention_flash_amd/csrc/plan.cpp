@@ -48,7 +48,7 @@ namespace magi {
 namespace {
 
 bool supported(int dtype, int d) {
-  if (dtype == MAGI_DTYPE_BF16) return d == 128;
+  if (dtype == MAGI_DTYPE_BF16) return d == 64 || d == 128;
   if (dtype == MAGI_DTYPE_FP32) return d == 64 || d == 128;
   return false;
 }
@@ -87,7 +87,7 @@ magi_status_t validate_layout(const magi_attn_layout_t* L, std::string& err) {
   if (L->dtype != MAGI_DTYPE_BF16 && L->dtype != MAGI_DTYPE_FP32) { err = "unknown dtype"; return MAGI_ERR_INVALID_ARG; }
   if (L->head_dim < 1) { err = "head_dim must be positive"; return MAGI_ERR_INVALID_ARG; }
   if (!supported(L->dtype, L->head_dim)) {
-    err = "unsupported head_dim " + std::to_string(L->head_dim) + " for this dtype (bf16: 128; fp32: 64, 128)";
+    err = "unsupported head_dim " + std::to_string(L->head_dim) + " (64 or 128)";
     return MAGI_ERR_UNSUPPORTED;
   }
   const int64_t esize = L->dtype == MAGI_DTYPE_BF16 ? 2 : 4;
@@ -502,6 +502,10 @@ magi_status_t build_host_plan(int32_t kind, const magi_attn_layout_t* L, const m
 magi_status_t build_bwd_plan(const magi_attn_layout_t* L, const magi_attn_text_t* T, BwdHostPlan& B,
                              std::string& err) {
   const int group = L->n_q_heads / L->n_kv_heads;
+  if (L->dtype == MAGI_DTYPE_BF16 && L->head_dim != 128) {
+    err = "the bf16 backward supports head_dim 128";
+    return MAGI_ERR_UNSUPPORTED;
+  }
   const Tiling tiling = choose_bwd_tiling(L->dtype, L->head_dim, group);
   if (L->dtype == MAGI_DTYPE_BF16 && tiling.tile_q % 32 != 0) {
     err = "internal: backward query tile not a multiple of 32 tokens";

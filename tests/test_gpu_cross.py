@@ -145,11 +145,12 @@ CASES = _cases()
 
 @pytest.mark.parametrize("name", list(CASES))
 @pytest.mark.parametrize("hq,hk", [(6, 2), (3, 1), (8, 1)])
-def test_bf16_cross_small(name, hq, hk):
+@pytest.mark.parametrize("d", [64, 128])
+def test_bf16_cross_small(name, hq, hk, d):
     lay, text = CASES[name]
-    log(f"bf16 cross {name} {hq}/{hk}")
-    inp, tx = inputs(lay, text, hq, hk, 128, "bf16", seed=hq * 10 + hk, distinct_qx=True)
-    got = run_cross(lay, text, tx, tx["q_x"], hq, hk, 128, "bf16", 0.09)
+    log(f"bf16 cross {name} {hq}/{hk} d={d}")
+    inp, tx = inputs(lay, text, hq, hk, d, "bf16", seed=hq * 10 + hk, distinct_qx=True)
+    got = run_cross(lay, text, tx, tx["q_x"], hq, hk, d, "bf16", 0.09)
     rl2, mabs, lerr = compare(*got, *ref_cross(lay, text, tx, 0.09), "bf16", tol_cross(tx, 0.09))
     log(f"  rel_l2={rl2:.3e} max_abs={mabs:.3e} lse_err={lerr:.3e}")
 
@@ -165,13 +166,13 @@ def test_fp32_cross_small(name, d):
 
 
 @pytest.mark.parametrize("name", list(CASES))
-@pytest.mark.parametrize("dtype,d", [("bf16", 128), ("fp32", 64)])
+@pytest.mark.parametrize("dtype,d", [("bf16", 128), ("bf16", 64), ("fp32", 64)])
 def test_parallel_small(name, dtype, d):
     """Both attentions of one parallel launch against their oracles, with a
     cross-attention query distinct from the self-attention query and its own
     gains and temperature."""
     lay, text = CASES[name]
-    log(f"parallel {name} {dtype}")
+    log(f"parallel {name} {dtype} d={d}")
     inp, tx = inputs(lay, text, 6, 2, d, dtype, seed=7, distinct_qx=True)
     sc, scx = 1 / math.sqrt(d), 0.8 / math.sqrt(d)
     out, lse, out_x, lse_x = run_parallel(lay, text, inp, tx, 6, 2, d, dtype, sc, scx)
@@ -206,7 +207,8 @@ def test_parallel_equals_separate_plans_bitwise():
     assert np.array_equal(out_x, xo) and np.array_equal(lse_x, xl)
 
 
-def test_parallel_with_split_self_attention():
+@pytest.mark.parametrize("d", [64, 128])
+def test_parallel_with_split_self_attention(d):
     """A layout with too few self-attention items for the GPU: the self phase
     is split along the keys and merged, while the cross phase has chunks
     without text (merge entries without pieces) -- both in one launch."""
@@ -216,10 +218,10 @@ def test_parallel_with_split_self_attention():
     lay = Layout(tuple(q), tuple(kv), (0, 18))
     text = chunk_prompts([None] * 17 + [0, None], [70])
     st = magi_attn_cross_plan_stats(lay.q_offsets, text.begin, text.end, text.t_text, lay.kv_offsets,
-                                    lay.seq_chunks, 6, 2, 128, "bf16", with_self=True)
-    log(f"parallel split: {st['n_items']} workgroups")
-    inp, tx = inputs(lay, text, 6, 2, 128, "bf16", seed=11, distinct_qx=True)
-    out, lse, out_x, lse_x = run_parallel(lay, text, inp, tx, 6, 2, 128, "bf16", 0.088, 0.088)
+                                    lay.seq_chunks, 6, 2, d, "bf16", with_self=True)
+    log(f"parallel split d={d}: {st['n_items']} workgroups")
+    inp, tx = inputs(lay, text, 6, 2, d, "bf16", seed=11, distinct_qx=True)
+    out, lse, out_x, lse_x = run_parallel(lay, text, inp, tx, 6, 2, d, "bf16", 0.088, 0.088)
     compare(out, lse, *oracle.attention(inp["q"], inp["k"], inp["v"], inp["q_gain"], inp["k_gain"], 1e-6, 0.088,
                                         lay), "bf16")
     compare(out_x, lse_x, *ref_cross(lay, text, tx, 0.088), "bf16", tol_cross(tx, 0.088))
@@ -247,7 +249,7 @@ def test_parallel_with_one_phase_on_the_online_softmax(online):
     compare(out_x, lse_x, *ref_cross(lay, text, tx, 0.07), "bf16", tol_cross(tx, 0.07))
 
 
-@pytest.mark.parametrize("dtype,d", [("bf16", 128), ("fp32", 128)])
+@pytest.mark.parametrize("dtype,d", [("bf16", 128), ("bf16", 64), ("fp32", 128)])
 def test_cross_without_any_text(dtype, d):
     """No chunk has text: nothing but zero rows, out = 0 and lse = -inf
     everywhere (outputs start as NaN so every row must be written)."""

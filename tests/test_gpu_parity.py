@@ -88,9 +88,20 @@ SMALL = [
 
 @pytest.mark.parametrize("name,layout", SMALL, ids=[s[0] for s in SMALL])
 @pytest.mark.parametrize("hq,hk", [(6, 2), (3, 1), (8, 2), (2, 2), (8, 1)])
-def test_bf16_small_layouts(name, layout, hq, hk):
-    log(f"bf16 {name} hq={hq} hk={hk}")
-    full_parity(layout, hq, hk, 128, "bf16", seed=zlib.crc32(f"{name}{hq}{hk}".encode()) % 1000)
+@pytest.mark.parametrize("d", [64, 128])
+def test_bf16_small_layouts(name, layout, hq, hk, d):
+    log(f"bf16 {name} hq={hq} hk={hk} d={d}")
+    full_parity(layout, hq, hk, d, "bf16", seed=zlib.crc32(f"{name}{hq}{hk}{d}".encode()) % 1000)
+
+
+@pytest.mark.parametrize("hq,hk", [(6, 2), (8, 1)])
+def test_bf16_d64_long_tile_lists(hq, hk):
+    """head_dim 64 over lists of 169-188 key tiles (a cached prefix of 8 x 600
+    keys, two query chunks of 600): the full tiles run in groups of eight
+    ring stages, then the boundary tiles of the chunk edge."""
+    lay = streaming_layout(8, 2, 600)
+    rl2, mabs, lerr = full_parity(lay, hq, hk, 64, "bf16", seed=hq + hk)
+    log(f"d64 long lists {hq}/{hk}: rel_l2={rl2:.3e} max_abs={mabs:.3e} lse_err={lerr:.3e}")
 
 
 @pytest.mark.parametrize("name,layout", SMALL[:5], ids=[s[0] for s in SMALL[:5]])
@@ -129,9 +140,10 @@ def test_bf16_split_key_ranges_merge():
     lay = split_window_layout()
     st = magi_attn_plan_stats(lay.q_offsets, lay.kv_offsets, lay.seq_chunks, 6, 2, 128, "bf16")
     assert st["n_items"] > 2 * 2, st                     # split into pieces
-    for hq, hk in ((6, 2), (8, 1)):
-        rl2, mabs, lerr = full_parity(lay, hq, hk, 128, "bf16", seed=11)
-        log(f"split window {hq}/{hk}: rel_l2={rl2:.3e} max_abs={mabs:.3e} lse_err={lerr:.3e}")
+    for d in (64, 128):
+        for hq, hk in ((6, 2), (8, 1)):
+            rl2, mabs, lerr = full_parity(lay, hq, hk, d, "bf16", seed=11)
+            log(f"split window d={d} {hq}/{hk}: rel_l2={rl2:.3e} max_abs={mabs:.3e} lse_err={lerr:.3e}")
 
 
 @pytest.mark.parametrize("name", ["three_chunks_ragged", "kv_cache_mixed", "multi_tile_chunk_aligned"])
@@ -151,31 +163,33 @@ def test_bf16_static_path_past_its_first_limit(name):
         log(f"static past 40 {name} {hq}/{hk}: rel_l2={rl2:.3e} max_abs={mabs:.3e} lse_err={lerr:.3e}")
 
 
-def test_bf16_split_online_path():
+@pytest.mark.parametrize("d", [64, 128])
+def test_bf16_split_online_path(d):
     """Pieces on the online-softmax path carry their own reference maxima."""
     lay = split_window_layout()
-    inp = make_inputs(lay, 6, 2, 128, "bf16", "uniform", 12)
+    inp = make_inputs(lay, 6, 2, d, "bf16", "uniform", 12)
     inp["q_gain"][0] = 40.0
     inp["k_gain"][0] = 40.0
     inp["k"][:, :, 0] = 0.0
-    sc = 1.0 / math.sqrt(128)
-    got_out, got_lse = run_gpu(lay, inp, 6, 2, 128, "bf16", 1e-6, sc)
+    sc = 1.0 / math.sqrt(d)
+    got_out, got_lse = run_gpu(lay, inp, 6, 2, d, "bf16", 1e-6, sc)
     ref_out, ref_lse = oracle.attention(inp["q"], inp["k"], inp["v"], inp["q_gain"], inp["k_gain"], 1e-6, sc, lay)
     compare(got_out, got_lse, ref_out, ref_lse, "bf16")
 
 
-def test_bf16_online_softmax_path():
+@pytest.mark.parametrize("d", [64, 128])
+def test_bf16_online_softmax_path(d):
     """A gain of 40 on channel 0 of both q and k, with k zero in that channel,
     makes the Cauchy-Schwarz logit bound huge (so every wave runs the
     running-maximum softmax) while leaving the logits themselves unchanged."""
-    log("bf16 online path")
+    log(f"bf16 online path d={d}")
     lay = layout_from_chunks([[130, 70], [190]])
-    inp = make_inputs(lay, 6, 2, 128, "bf16", "uniform", 11)
+    inp = make_inputs(lay, 6, 2, d, "bf16", "uniform", 11)
     inp["q_gain"][0] = 40.0
     inp["k_gain"][0] = 40.0
     inp["k"][:, :, 0] = 0.0
-    sc = 1 / math.sqrt(128)
-    got = run_gpu(lay, inp, 6, 2, 128, "bf16", 1e-6, sc)
+    sc = 1 / math.sqrt(d)
+    got = run_gpu(lay, inp, 6, 2, d, "bf16", 1e-6, sc)
     ref = oracle.attention(inp["q"], inp["k"], inp["v"], inp["q_gain"], inp["k_gain"], 1e-6, sc, lay)
     compare(*got, *ref, "bf16")
 

@@ -147,7 +147,7 @@ BAD = [
     (dict(q_offsets=[0, 4, 8], seq_chunks=[0, 1, 1, 2]), 1),         # empty video
     (dict(q_offsets=[0, 4], kv_offsets=[0, 0]), 1),                  # queries without keys
     (dict(q_offsets=[0, 4], n_q_heads=3, n_kv_heads=2), 1),          # heads not a multiple
-    (dict(q_offsets=[0, 4], head_dim=64, dtype="bf16"), 2),          # unsupported head_dim for bf16
+    (dict(q_offsets=[0, 4], head_dim=96, dtype="bf16"), 2),          # unsupported head_dim
     (dict(q_offsets=[0, 4], head_dim=96, dtype="fp32"), 2),
     (dict(q_offsets=[0, 4], dtype=7), 1),                            # unknown dtype
 ]
