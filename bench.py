@@ -260,6 +260,9 @@ def bench_backward(args) -> None:
     if args.kv_range or args.last_global:
         cfg = dataclasses.replace(cfg, layout=dataclasses.replace(cfg.layout, kv_range=args.kv_range,
                                                                   last_global=int(args.last_global)))
+    own_dim = args.head_dim in (0, cfg.head_dim)
+    if not own_dim:
+        cfg = dataclasses.replace(cfg, head_dim=args.head_dim)
     lay = cfg.layout
     cross = args.attention == "cross"
     dev = torch.device("cuda", 0)
@@ -303,8 +306,8 @@ def bench_backward(args) -> None:
     roof = {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
             "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
             "traffic": stored_backward_traffic(cfg.name)
-            if cfg.dtype == "bf16" and not (cross or lay.kv_range or lay.last_global or args.gain_scale != 1.0)
-            else None}
+            if cfg.dtype == "bf16" and own_dim
+            and not (cross or lay.kv_range or lay.last_global or args.gain_scale != 1.0) else None}
     rec = {
         "metric": METRIC_CROSS_BACKWARD if cross else METRIC_BACKWARD, "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak",
@@ -367,6 +370,9 @@ def main():
     ap.add_argument("--cold", action="store_true",
                     help="overwrite a 1 GiB buffer before every timed step (forward), so each step starts with the "
                          "L2s and the Infinity Cache holding other data")
+    ap.add_argument("--head-dim", type=int, default=0, choices=(0, 64, 128),
+                    help="run the workload at this head_dim instead of its own (64 or 128; the scale follows "
+                         "as 1/sqrt(head_dim))")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=20.0)
     ap.add_argument("--copy-probe-mib", type=int, default=0,
@@ -394,6 +400,9 @@ def main():
     if args.kv_range or args.last_global:
         cfg = dataclasses.replace(cfg, layout=dataclasses.replace(cfg.layout, kv_range=args.kv_range,
                                                                   last_global=int(args.last_global)))
+    own_dim = args.head_dim in (0, cfg.head_dim)
+    if not own_dim:
+        cfg = dataclasses.replace(cfg, head_dim=args.head_dim)
     lay = cfg.layout
     mode = args.attention
     text = text_layout(cfg) if mode != "self" else None
@@ -461,7 +470,7 @@ def main():
     tflops = flops / (ms * 1e-3) / 1e12
     # the stored counters belong to the static-softmax instance on the workload's own gains
     traffic = (stored_traffic(cfg.name, mode)
-               if not (lay.kv_range or lay.last_global or args.gain_scale != 1.0 or args.cold) else None)
+               if own_dim and not (lay.kv_range or lay.last_global or args.gain_scale != 1.0 or args.cold) else None)
     roof = {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
             "frac": round(tflops / PEAK_BF16_TFLOPS, 4), "traffic": traffic}
     if traffic:

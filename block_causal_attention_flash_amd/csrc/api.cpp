@@ -425,7 +425,7 @@ magi_status_t magi_attn_bwd_workspace_size(const magi_attn_plan_t* plan, size_t*
   const int nq = int(plan->bwd.dq.items.size()), nk = int(plan->bwd.items.size());
   const auto& B = plan->bwd;
   *bytes = H.dtype == MAGI_DTYPE_BF16
-               ? magi::bwd_workspace_layout(H.tq, H.tk, H.hq, H.hk, nq + int(B.dq_merges.size()),
+               ? magi::bwd_workspace_layout(H.tq, H.tk, H.hq, H.hk, H.d, nq + int(B.dq_merges.size()),
                                             nk + int(B.kv_merges.size()), B.n_kv_slots, B.dq.n_slots).total
                                       : magi::bwd_workspace_bytes_fp32(H.tq, H.tk, H.hq, H.hk, H.d, nq, nk);
   return MAGI_OK;
@@ -502,7 +502,7 @@ magi_status_t magi_attn_bwd(const magi_attn_plan_t* plan, const magi_attn_bwd_io
   b.n_dq_items = int(plan->bwd.dq.items.size());
   b.n_kv_items = int(plan->bwd.items.size());
   hipStream_t st = static_cast<hipStream_t>(stream);
-  const hipError_t e = H.dtype == MAGI_DTYPE_BF16 ? magi::launch_bwd_bf16_d128(b, st) : magi::launch_bwd_fp32(b, H.d, st);
+  const hipError_t e = H.dtype == MAGI_DTYPE_BF16 ? magi::launch_bwd_bf16(b, H.d, st) : magi::launch_bwd_fp32(b, H.d, st);
   if (e != hipSuccess) return hip_fail(e, "kernel launch");
   return MAGI_OK;
 }

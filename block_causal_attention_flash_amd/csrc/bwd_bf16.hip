@@ -1,4 +1,4 @@
-// Backward of the block-causal QK-RMSNorm GQA attention, bf16, head_dim 128, gfx950.
+// Backward of the block-causal QK-RMSNorm GQA attention, bf16, head_dim 64 or 128, gfx950.
 //
 // Training needs the gradients of the attention of the MAGI-1 pages
 // (paperlayer §2 / Figure 1, §2.2.2; paper-notes §3.2.2 and Figure 15), and
@@ -36,8 +36,9 @@
 // exponentials. A cross-attention plan runs the same kernels: its keys are
 // the text's, a row's range is its chunk's text, a text key's rows are the
 // chunks whose prompt holds it.
-// Every image is [16 chunks][32 row slots][16 B]: chunk c of row r (dims
-// 8c..8c+7) sits at byte 512 c + 16 (r XOR 12 (c mod 2)). The XOR keeps each
+// Every image is [D / 8 chunks][32 row slots][16 B] (head_dim D = 64 or 128,
+// a template parameter): chunk c of row r (dims 8c..8c+7) sits at byte
+// 512 c + 16 (r XOR 12 (c mod 2)). The XOR keeps each
 // 16-row block of a chunk in its own 256 bytes, so row reads stay contiguous,
 // and puts the odd chunk's rows of a transposed read (rows 4 g .. 4 g + 3 of
 // chunks 2 b and 2 b + 1 for the 16 lanes of group g) on the other banks: a
@@ -50,7 +51,10 @@
 // the row order of a lane's fragment of a 16x16 result pair. Copies into LDS
 // rings use LDS-direct buffer loads four steps ahead; on even steps a wave
 // waits for its copies of the step pair and the workgroup barrier publishes
-// both stages (and frees the two stages the next pair of copies fills).
+// both stages (and frees the two stages the next pair of copies fills). An
+// image is 64 D bytes: at D = 128 every thread copies 16 bytes of each of a
+// step's two images, at D = 64 waves 0-3 copy the first and waves 4-7 the
+// second.
 #include "kernels.hpp"
 
 namespace magi {
@@ -67,15 +71,24 @@ typedef __attribute__((address_space(3))) const f32x4 lds_f32x4;
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
-constexpr int D = 128;
 constexpr int TT = 32;                       // tokens per image (and per dk/dv step), keys per dq tile
-constexpr int IMG = TT * D * 2;              // 8 KiB
 constexpr int NTHR = 512;
 constexpr int RING = 8;                      // LDS ring stages: copies four steps ahead, a barrier every second step
 constexpr unsigned kNoTile = 0x80000000u;    // past every image array (< 2 GiB): zeros
 constexpr float kLog2e = 1.4426950408889634f;
-static_assert(IMG == NTHR * 16, "one 16-byte copy per thread per image");
 static_assert(kBwdRowsPerItem == 8 * 32 && kBwdKeysPerItem == 8 * 32, "8 waves per workgroup");
+
+// Sizes that depend on head_dim D.
+template <int D>
+struct BGeo {
+  static_assert(D == 64 || D == 128, "head_dim");
+  static constexpr int IMG = TT * D * 2;     // 8 KiB (D = 128) or 4 KiB (D = 64)
+  static constexpr int NKS = D / 32;         // 32-dim steps of a product over d
+  static constexpr int NDB = D / 16;         // 16-dim blocks of a result over d
+  static constexpr int COPY_THREADS = IMG / 16;
+  static constexpr bool SPLIT_COPY = COPY_THREADS < NTHR;  // one image per half workgroup
+  static_assert(COPY_THREADS == NTHR || 2 * COPY_THREADS == NTHR, "copy units");
+};
 
 __device__ __forceinline__ unsigned lds_addr(const void* p) {
   return unsigned(reinterpret_cast<uintptr_t>(LDS_PTR(const char, p)));
@@ -166,19 +179,22 @@ __device__ __forceinline__ bf16x8 tr_frag(unsigned addr, int db) {
 // ------------------------------------------------------------------ pre-passes
 
 // One workgroup per (32-token tile tt, query head h), image b = tt * hq + h;
-// thread t: token row j = t / 8, dims [16 (t % 8), +16).
+// thread t: token row j = t / 8, dims [D / 8 (t % 8), +D / 8) (PC = D / 64
+// chunks of 8 dims).
 constexpr int PREP_THREADS = 256;
+template <int D>
 __global__ void __launch_bounds__(PREP_THREADS) bwd_prep_q_kernel(BwdParams p, BwdLayout L) {
+  constexpr int PC = D / 64, IMG = BGeo<D>::IMG;
   unsigned char* ws = static_cast<unsigned char*>(p.ws);
   const int b = blockIdx.x, tt = b / p.hq, h = b % p.hq;
   const int t = threadIdx.x, j = t >> 3, part = t & 7;
   const int tok = tt * TT + j;
   const bool valid = tok < p.tq;
-  const size_t row = (size_t(tok) * p.hq + h) * D + part * 16;
-  bf16x8 q[2] = {}, dd[2] = {}, oo[2] = {};
+  const size_t row = (size_t(tok) * p.hq + h) * D + part * 8 * PC;
+  bf16x8 q[PC] = {}, dd[PC] = {}, oo[PC] = {};
   if (valid) {
 #pragma unroll
-    for (int c = 0; c < 2; ++c) {
+    for (int c = 0; c < PC; ++c) {
       q[c] = *reinterpret_cast<const bf16x8*>(static_cast<const __bf16*>(p.q) + row + 8 * c);
       dd[c] = *reinterpret_cast<const bf16x8*>(static_cast<const __bf16*>(p.dout) + row + 8 * c);
       oo[c] = *reinterpret_cast<const bf16x8*>(static_cast<const __bf16*>(p.out) + row + 8 * c);
@@ -186,7 +202,7 @@ __global__ void __launch_bounds__(PREP_THREADS) bwd_prep_q_kernel(BwdParams p, B
   }
   float ss = 0.0f, dsum = 0.0f;
 #pragma unroll
-  for (int c = 0; c < 2; ++c)
+  for (int c = 0; c < PC; ++c)
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       ss += float(q[c][e]) * float(q[c][e]);
@@ -196,11 +212,11 @@ __global__ void __launch_bounds__(PREP_THREADS) bwd_prep_q_kernel(BwdParams p, B
   dsum = sum8(dsum);
   const float rq = valid ? __builtin_amdgcn_rsqf(ss * (1.0f / D) + p.eps) : 0.0f;
 #pragma unroll
-  for (int c = 0; c < 2; ++c) {
+  for (int c = 0; c < PC; ++c) {
     bf16x8 qh;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) qh[e] = (__bf16)(float(q[c][e]) * rq * p.q_gain[part * 16 + 8 * c + e]);
-    const size_t at = size_t(b) * IMG + img_off(2 * part + c, j);
+    for (int e = 0; e < 8; ++e) qh[e] = (__bf16)(float(q[c][e]) * rq * p.q_gain[part * 8 * PC + 8 * c + e]);
+    const size_t at = size_t(b) * IMG + img_off(PC * part + c, j);
     *reinterpret_cast<bf16x8*>(ws + L.qs + at) = qh;
     *reinterpret_cast<bf16x8*>(ws + L.dos + at) = dd[c];
   }
@@ -212,47 +228,50 @@ __global__ void __launch_bounds__(PREP_THREADS) bwd_prep_q_kernel(BwdParams p, B
 }
 
 // One workgroup per (32-key tile kt, KV head), image b = kt * hk + kvh.
+template <int D>
 __global__ void __launch_bounds__(PREP_THREADS) bwd_prep_k_kernel(BwdParams p, BwdLayout L) {
+  constexpr int PC = D / 64, IMG = BGeo<D>::IMG;
   unsigned char* ws = static_cast<unsigned char*>(p.ws);
   const int b = blockIdx.x, kt = b / p.hk, kvh = b % p.hk;
   const int t = threadIdx.x, j = t >> 3, part = t & 7;
   const int key = kt * TT + j;
   const bool valid = key < p.tk;
-  const size_t row = (size_t(key) * p.hk + kvh) * D + part * 16;
-  bf16x8 k[2] = {}, v[2] = {};
+  const size_t row = (size_t(key) * p.hk + kvh) * D + part * 8 * PC;
+  bf16x8 k[PC] = {}, v[PC] = {};
   if (valid) {
 #pragma unroll
-    for (int c = 0; c < 2; ++c) {
+    for (int c = 0; c < PC; ++c) {
       k[c] = *reinterpret_cast<const bf16x8*>(static_cast<const __bf16*>(p.k) + row + 8 * c);
       v[c] = *reinterpret_cast<const bf16x8*>(static_cast<const __bf16*>(p.v) + row + 8 * c);
     }
   }
   float ss = 0.0f;
 #pragma unroll
-  for (int c = 0; c < 2; ++c)
+  for (int c = 0; c < PC; ++c)
 #pragma unroll
     for (int e = 0; e < 8; ++e) ss += float(k[c][e]) * float(k[c][e]);
   ss = sum8(ss);
   const float rk = valid ? __builtin_amdgcn_rsqf(ss * (1.0f / D) + p.eps) : 0.0f;
   const float fold = p.scale * kLog2e;
 #pragma unroll
-  for (int c = 0; c < 2; ++c) {
+  for (int c = 0; c < PC; ++c) {
     bf16x8 kf;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) kf[e] = (__bf16)(float(k[c][e]) * rk * p.k_gain[part * 16 + 8 * c + e] * fold);
-    const size_t at = size_t(b) * IMG + img_off(2 * part + c, j);
+    for (int e = 0; e < 8; ++e) kf[e] = (__bf16)(float(k[c][e]) * rk * p.k_gain[part * 8 * PC + 8 * c + e] * fold);
+    const size_t at = size_t(b) * IMG + img_off(PC * part + c, j);
     *reinterpret_cast<bf16x8*>(ws + L.kh + at) = kf;
     *reinterpret_cast<bf16x8*>(ws + L.vr + at) = v[c];
   }
 }
 
-// Writes the wave-summed gain partial of every lane's 32 dims (16 db + 4 g + i)
-// through LDS and the workgroup's sum to part[0 .. 127].
-__device__ __forceinline__ void store_gain_partial(float (&gp)[8][4], float (*red)[D], float* part, int wave,
+// Writes the wave-summed gain partial of every lane's D / 4 dims
+// (16 db + 4 g + i) through LDS and the workgroup's sum to part[0 .. D - 1].
+template <int D>
+__device__ __forceinline__ void store_gain_partial(float (&gp)[D / 16][4], float (*red)[D], float* part, int wave,
                                                    int lane, int tid) {
   const int g = lane >> 4;
 #pragma unroll
-  for (int db = 0; db < 8; ++db)
+  for (int db = 0; db < D / 16; ++db)
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const float x = sum16(gp[db][i]);
@@ -267,31 +286,33 @@ __device__ __forceinline__ void store_gain_partial(float (&gp)[8][4], float (*re
   }
 }
 
-// RMSNorm backward of one row held as 32 dims per lane (dims 16 db + 4 g + i,
-// four lanes per row): x the input row, dxh the gradient of x_hat = rms(x) g.
-// Writes dx (bf16) when `store`, and adds u * dxh to gp.
-__device__ __forceinline__ void rms_backward_row(const __bf16* xrow, __bf16* dxrow, const float (&dxh)[8][4],
-                                                 const float* gain, float eps, bool store, float (&gp)[8][4],
+// RMSNorm backward of one row held as D / 4 dims per lane (dims
+// 16 db + 4 g + i, four lanes per row): x the input row, dxh the gradient of
+// x_hat = rms(x) g. Writes dx (bf16) when `store`, and adds u * dxh to gp.
+template <int D>
+__device__ __forceinline__ void rms_backward_row(const __bf16* xrow, __bf16* dxrow, const float (&dxh)[D / 16][4],
+                                                 const float* gain, float eps, bool store, float (&gp)[D / 16][4],
                                                  int g) {
-  bf16x4 xv[8];
+  constexpr int NDB = D / 16;
+  bf16x4 xv[NDB];
 #pragma unroll
-  for (int db = 0; db < 8; ++db)
+  for (int db = 0; db < NDB; ++db)
     xv[db] = store ? *reinterpret_cast<const bf16x4*>(xrow + 16 * db + 4 * g) : bf16x4{};
   float ss = 0.0f;
 #pragma unroll
-  for (int db = 0; db < 8; ++db)
+  for (int db = 0; db < NDB; ++db)
 #pragma unroll
     for (int i = 0; i < 4; ++i) ss += float(xv[db][i]) * float(xv[db][i]);
   ss = sum_groups(ss);
   const float r = __builtin_amdgcn_rsqf(ss * (1.0f / D) + eps);
   float m = 0.0f;
 #pragma unroll
-  for (int db = 0; db < 8; ++db)
+  for (int db = 0; db < NDB; ++db)
 #pragma unroll
     for (int i = 0; i < 4; ++i) m += float(xv[db][i]) * r * gain[16 * db + 4 * g + i] * dxh[db][i];
   m = sum_groups(m) * (1.0f / D);
 #pragma unroll
-  for (int db = 0; db < 8; ++db) {
+  for (int db = 0; db < NDB; ++db) {
     bf16x4 w;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -305,17 +326,21 @@ __device__ __forceinline__ void rms_backward_row(const __bf16* xrow, __bf16* dxr
 
 // ------------------------------------------------------------------ dq
 
+template <int D>
 struct DqLds {
-  unsigned char kh[RING][IMG];
-  unsigned char vr[RING][IMG];
+  unsigned char kh[RING][BGeo<D>::IMG];
+  unsigned char vr[RING][BGeo<D>::IMG];
   float gq[D];
   float red[8][D];
 };
 
+template <int D>
 __global__ void __launch_bounds__(NTHR) __attribute__((amdgpu_waves_per_eu(2, 2)))
 bwd_dq_kernel(BwdParams p, BwdLayout L, const int4* __restrict__ items, const int* __restrict__ tiles,
               const unsigned* __restrict__ soffs_all) {
-  __shared__ __attribute__((aligned(1024))) DqLds sm;
+  using G = BGeo<D>;
+  constexpr int IMG = G::IMG, NKS = G::NKS, NDB = G::NDB;
+  __shared__ __attribute__((aligned(1024))) DqLds<D> sm;
   unsigned char* ws = static_cast<unsigned char*>(p.ws);
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -338,13 +363,13 @@ bwd_dq_kernel(BwdParams p, BwdLayout L, const int4* __restrict__ items, const in
   // it computes with zeros (P = 1, dP = 0, dS = 0) and stores nothing.
   const bool live = tok0 < p.tq;
 
-  bf16x8 qs[2][4], dov[2][4];
+  bf16x8 qs[2][NKS], dov[2][NKS];
   {
     const size_t base = size_t(live ? img : 0) * IMG + img_off(g, r16);
 #pragma unroll
     for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
+      for (int ks = 0; ks < NKS; ++ks) {
         qs[rb][ks] = live ? *reinterpret_cast<const bf16x8*>(ws + L.qs + base + 2048 * ks + 256 * rb) : bf16x8{};
         dov[rb][ks] = live ? *reinterpret_cast<const bf16x8*>(ws + L.dos + base + 2048 * ks + 256 * rb) : bf16x8{};
       }
@@ -368,28 +393,39 @@ bwd_dq_kernel(BwdParams p, BwdLayout L, const int4* __restrict__ items, const in
   const unsigned n_kt = unsigned(p.tk + TT - 1) / TT;
   const unsigned kbytes = n_kt * unsigned(p.hk) * IMG;
   const i32x4 rkh = make_rsrc(ws + L.kh, kbytes), rvr = make_rsrc(ws + L.vr, kbytes);
-  const unsigned voff = unsigned(kvh) * IMG + unsigned(tid) * 16;
+  const unsigned voff = unsigned(kvh) * IMG + unsigned(tid % G::COPY_THREADS) * 16;
   const unsigned kh0 = lds_addr(sm.kh[0]), vr0 = lds_addr(sm.vr[0]);
-  const unsigned wpart = unsigned(wave) * 1024;  // this wave's part of every image copy
+  // this wave's part of every image copy (split copies: waves 0-3 copy k', 4-7 V)
+  const unsigned wpart = unsigned(G::SPLIT_COPY ? (wave & 3) : wave) * 1024;
+  const bool kwave = wave < 4;
+  const i32x4 rown = kwave ? rkh : rvr;
+  const unsigned own0 = kwave ? kh0 : vr0;
   const int* codes = tiles + item.z;
   const unsigned* soffs = soffs_all + item.z;    // padded past the list with kNoTile
   auto issue = [&](int i) {
     const unsigned so = __builtin_amdgcn_readfirstlane(soffs[i]);
     const unsigned st = unsigned(i % RING) * IMG + wpart;
-    dma16(rkh, voff, so, kh0 + st);
-    dma16(rvr, voff, so, vr0 + st);
+    if constexpr (G::SPLIT_COPY) {
+      dma16(rown, voff, so, own0 + st);
+    } else {
+      dma16(rkh, voff, so, kh0 + st);
+      dma16(rvr, voff, so, vr0 + st);
+    }
   };
   for (int i = 0; i < 4; ++i) issue(i);
 
-  f32x4 acc[2][8];
+  f32x4 acc[2][NDB];
 #pragma unroll
   for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
-    for (int db = 0; db < 8; ++db) acc[rb][db] = f32x4{};
+    for (int db = 0; db < NDB; ++db) acc[rb][db] = f32x4{};
   const unsigned rowq = img_off(g, r16), trq = tr_lane_offset(lane);  // chunk g + 4 ks has g's parity
+  // copies per tile and wave: 2, or 1 when split; tiles i, i + 1 must have
+  // landed, the copies of i + 2, i + 3 may still fly
+  constexpr int kYounger = G::SPLIT_COPY ? 2 : 4;
   for (int i = 0; i < n; ++i) {
     if ((i & 1) == 0) {
-      wait_vmcnt<4>();                                // tiles i, i + 1 landed; i + 2, i + 3 may still fly
+      wait_vmcnt<kYounger>();
       lds_barrier();                                  // and every wave left the stages of tiles i - 4, i - 3
       issue(i + 4);
       issue(i + 5);
@@ -405,14 +441,14 @@ bwd_dq_kernel(BwdParams p, BwdLayout L, const int4* __restrict__ items, const in
       dp[rb][0] = dp[rb][1] = f32x4{nd[rb], nd[rb], nd[rb], nd[rb]};
     }
 #pragma unroll
-    for (int f = 0; f < 8; ++f) {
+    for (int f = 0; f < 2 * NKS; ++f) {
       const int ks = f >> 1, kb = f & 1;
       const bf16x8 a = *(lds_bf16x8*)(size_t)(kh0 + st + rowq + 2048 * ks + 256 * kb);
 #pragma unroll
       for (int rb = 0; rb < 2; ++rb) s[rb][kb] = mfma(a, qs[rb][ks], s[rb][kb]);
     }
 #pragma unroll
-    for (int f = 0; f < 8; ++f) {
+    for (int f = 0; f < 2 * NKS; ++f) {
       const int ks = f >> 1, kb = f & 1;
       const bf16x8 a = *(lds_bf16x8*)(size_t)(vr0 + st + rowq + 2048 * ks + 256 * kb);
 #pragma unroll
@@ -442,7 +478,7 @@ bwd_dq_kernel(BwdParams p, BwdLayout L, const int4* __restrict__ items, const in
         for (int e = 0; e < 4; ++e)
           ds[rb][4 * kb + e] = (__bf16)(__builtin_amdgcn_exp2f(s[rb][kb][e]) * dp[rb][kb][e]);
 #pragma unroll
-    for (int db = 0; db < 8; ++db) {
+    for (int db = 0; db < NDB; ++db) {
       const bf16x8 a = tr_frag(kh0 + st + trq, db);
 #pragma unroll
       for (int rb = 0; rb < 2; ++rb) acc[rb][db] = mfma(a, ds[rb], acc[rb][db]);
@@ -451,7 +487,7 @@ bwd_dq_kernel(BwdParams p, BwdLayout L, const int4* __restrict__ items, const in
   wait_vmcnt<0>();                                    // the padding copies of the last two steps
 
   // A piece of a split item writes its fp32 dq-hat^T sums (times log2 e) to
-  // its slot, [256 item rows][128 dims], and an empty gain partial; the dq
+  // its slot, [256 item rows][D dims], and an empty gain partial; the dq
   // merge adds the pieces and finishes the rows.
   const int slot = __builtin_amdgcn_readfirstlane(items[2 * blockIdx.x + 1].y);
   if (slot >= 0) {
@@ -459,16 +495,16 @@ bwd_dq_kernel(BwdParams p, BwdLayout L, const int4* __restrict__ items, const in
 #pragma unroll
     for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
-      for (int db = 0; db < 8; ++db)
+      for (int db = 0; db < NDB; ++db)
         *reinterpret_cast<f32x4*>(pd + size_t(r0 + 16 * rb + r16) * D + 16 * db + 4 * g) = acc[rb][db];
     if (tid < D) part[tid] = 0.0f;
     return;
   }
 
   // Epilogue: lane holds dims 16 db + 4 g + i of row r16 of block rb.
-  float gp[8][4];
+  float gp[NDB][4];
 #pragma unroll
-  for (int db = 0; db < 8; ++db)
+  for (int db = 0; db < NDB; ++db)
 #pragma unroll
     for (int e = 0; e < 4; ++e) gp[db][e] = 0.0f;
   __syncthreads();                                    // gains in LDS (and the loop's last reads) done
@@ -476,23 +512,24 @@ bwd_dq_kernel(BwdParams p, BwdLayout L, const int4* __restrict__ items, const in
   for (int rb = 0; rb < 2; ++rb) {
     const int tok = tok0 + 16 * rb + r16;
     const bool valid = tok < p.tq;
-    float dxh[8][4];
+    float dxh[NDB][4];
 #pragma unroll
-    for (int db = 0; db < 8; ++db)
+    for (int db = 0; db < NDB; ++db)
 #pragma unroll
       for (int e = 0; e < 4; ++e) dxh[db][e] = acc[rb][db][e] * (1.0f / kLog2e);
     const size_t off = (size_t(valid ? tok : 0) * p.hq + head) * D;
-    rms_backward_row(static_cast<const __bf16*>(p.q) + off, static_cast<__bf16*>(p.dq) + off, dxh, sm.gq, p.eps,
-                     valid, gp, g);
+    rms_backward_row<D>(static_cast<const __bf16*>(p.q) + off, static_cast<__bf16*>(p.dq) + off, dxh, sm.gq, p.eps,
+                        valid, gp, g);
   }
-  store_gain_partial(gp, sm.red, part, wave, lane, tid);
+  store_gain_partial<D>(gp, sm.red, part, wave, lane, tid);
 }
 
 // ------------------------------------------------------------------ dk / dv
 
+template <int D>
 struct KvLds {
-  unsigned char qs[RING][IMG];
-  unsigned char dos[RING][IMG];
+  unsigned char qs[RING][BGeo<D>::IMG];
+  unsigned char dos[RING][BGeo<D>::IMG];
   float rs[RING][8][64];  // per stage and wave: -lse log2 e [32], -D [32] of the step's rows
   float gk[D];
   float red[8][D];
@@ -501,9 +538,12 @@ struct KvLds {
 // 8 waves x 32 keys: wave w holds keys 32 w + 16 j + (0..15), j = 0, 1, of
 // the item's 256, which are rows 16 j + (0..15) of one 32-key image. Every
 // LDS fragment of a step feeds the MFMAs of both 16-key halves.
+template <int D>
 __global__ void __launch_bounds__(NTHR) __attribute__((amdgpu_waves_per_eu(2, 2)))
 bwd_dkdv_kernel(BwdParams p, BwdLayout L, const int4* __restrict__ items, const int* __restrict__ tiles) {
-  __shared__ __attribute__((aligned(1024))) KvLds sm;
+  using G = BGeo<D>;
+  constexpr int IMG = G::IMG, NKS = G::NKS, NDB = G::NDB;
+  __shared__ __attribute__((aligned(1024))) KvLds<D> sm;
   unsigned char* ws = static_cast<unsigned char*>(p.ws);
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -516,21 +556,21 @@ bwd_dkdv_kernel(BwdParams p, BwdLayout L, const int4* __restrict__ items, const 
   }
   const int n_full = items[2 * blockIdx.x + 1].x;
   const int kb = item.x, kvh = item.y;
-  const int G = p.hq / p.hk;
+  const int grp = p.hq / p.hk;
   const int n_entries = item.w - item.z;
-  const int n_steps = n_entries * G;
+  const int n_steps = n_entries * grp;
   // The lane's keys (B operand columns, output rows), one per half.
   const int kt = kb * (kBwdKeysPerItem / TT) + wave;
   const int key0 = kt * TT + r16;
   const unsigned n_kt = unsigned(p.tk + TT - 1) / TT;
-  bf16x8 ku[2][4], vv[2][4];
+  bf16x8 ku[2][NKS], vv[2][NKS];
   {
     const bool have = unsigned(kt) < n_kt;
     const size_t base = (size_t(have ? kt : 0) * p.hk + kvh) * IMG;
 #pragma unroll
     for (int j = 0; j < 2; ++j)
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
+      for (int ks = 0; ks < NKS; ++ks) {
         const size_t at = base + img_off(g, 16 * j + r16) + 2048 * ks;
         ku[j][ks] = have ? *reinterpret_cast<const bf16x8*>(ws + L.kh + at) : bf16x8{};
         vv[j][ks] = have ? *reinterpret_cast<const bf16x8*>(ws + L.vr + at) : bf16x8{};
@@ -547,33 +587,47 @@ bwd_dkdv_kernel(BwdParams p, BwdLayout L, const int4* __restrict__ items, const 
               rrs = make_rsrc(ws + L.rs, n_tt * unsigned(p.hq) * 256u);
   const unsigned qs0 = lds_addr(sm.qs[0]), do0 = lds_addr(sm.dos[0]), rs0 = lds_addr(&sm.rs[0][wave][0]);
   const int* codes = tiles + item.z;
-  const int hbase = kvh * G;
-  // Step s = (entry s / G, head hbase + s % G); its image (token tile, head).
+  const int hbase = kvh * grp;
+  // Step s = (entry s / grp, head hbase + s % grp); its image (token tile, head).
   int ie = 0, ih = 0;                                 // entry and head of the next step to issue
-  const unsigned wpart = unsigned(wave) * 1024;  // this wave's part of every image copy
+  // this wave's part of every image copy (split copies: waves 0-3 copy q_hat, 4-7 dO)
+  const unsigned wpart = unsigned(G::SPLIT_COPY ? (wave & 3) : wave) * 1024;
+  const bool qwave = wave < 4;
+  const i32x4 rown = qwave ? rqs : rdo;
+  const unsigned own0 = qwave ? qs0 : do0;
+  const unsigned voff = unsigned(tid % G::COPY_THREADS) * 16;
   auto issue = [&]() {
     const bool live = ie < n_entries;
     const unsigned imgi = __builtin_amdgcn_readfirstlane(live ? unsigned((codes[ie] >> 1) * p.hq + hbase + ih) : 0u);
     const unsigned so = live ? imgi * IMG : kNoTile;
-    const unsigned st = unsigned(((ie * G + ih) % RING)) * IMG + wpart;
-    dma16(rqs, unsigned(tid) * 16, so, qs0 + st);
-    dma16(rdo, unsigned(tid) * 16, so, do0 + st);
+    const unsigned st = unsigned(((ie * grp + ih) % RING)) * IMG + wpart;
+    if constexpr (G::SPLIT_COPY) {
+      dma16(rown, voff, so, own0 + st);
+    } else {
+      dma16(rqs, voff, so, qs0 + st);
+      dma16(rdo, voff, so, do0 + st);
+    }
     if (lane < 16)
-      dma16(rrs, unsigned(lane) * 16, live ? imgi * 256u : kNoTile, rs0 + unsigned((ie * G + ih) % RING) * 8 * 256);
-    if (++ih == G) { ih = 0; ++ie; }
+      dma16(rrs, unsigned(lane) * 16, live ? imgi * 256u : kNoTile,
+            rs0 + unsigned((ie * grp + ih) % RING) * 8 * 256);
+    if (++ih == grp) { ih = 0; ++ie; }
   };
   for (int i = 0; i < 4; ++i) issue();
 
-  f32x4 accv[2][8], acck[2][8];
+  f32x4 accv[2][NDB], acck[2][NDB];
 #pragma unroll
   for (int j = 0; j < 2; ++j)
 #pragma unroll
-    for (int db = 0; db < 8; ++db) accv[j][db] = acck[j][db] = f32x4{};
+    for (int db = 0; db < NDB; ++db) accv[j][db] = acck[j][db] = f32x4{};
   const unsigned rowq = img_off(g, r16), trq = tr_lane_offset(lane);  // chunk g + 4 ks has g's parity
+  // copies per step and wave: q_hat, dO and the row statistics (3), or one
+  // image and the statistics (2) when split; steps s, s + 1 must have landed,
+  // the copies of s + 2, s + 3 may still fly
+  constexpr int kYounger = G::SPLIT_COPY ? 4 : 6;
   int ce = 0, ch = 0;                                 // entry and head of the current step
   for (int s = 0; s < n_steps; ++s) {
     if ((s & 1) == 0) {
-      wait_vmcnt<6>();                                // steps s, s + 1 landed; s + 2, s + 3 may still fly
+      wait_vmcnt<kYounger>();
       lds_barrier();
       issue();
       issue();
@@ -588,7 +642,7 @@ bwd_dkdv_kernel(BwdParams p, BwdLayout L, const int4* __restrict__ items, const 
 #pragma unroll
     for (int rb = 0; rb < 2; ++rb) sc[0][rb] = sc[1][rb] = *(lds_f32x4*)(size_t)(rsa + 4 * (16 * rb + 4 * g));
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks)
+    for (int ks = 0; ks < NKS; ++ks)
 #pragma unroll
       for (int rb = 0; rb < 2; ++rb) {
         const bf16x8 a = *(lds_bf16x8*)(size_t)(qs0 + st + rowq + 2048 * ks + 256 * rb);
@@ -622,7 +676,7 @@ bwd_dkdv_kernel(BwdParams p, BwdLayout L, const int4* __restrict__ items, const 
           pb[j][4 * rb + e] = (__bf16)pv;
         }
 #pragma unroll
-    for (int db = 0; db < 8; ++db) {
+    for (int db = 0; db < NDB; ++db) {
       const bf16x8 a = tr_frag(do0 + st + trq, db);
       accv[0][db] = mfma(a, pb[0], accv[0][db]);
       accv[1][db] = mfma(a, pb[1], accv[1][db]);
@@ -631,7 +685,7 @@ bwd_dkdv_kernel(BwdParams p, BwdLayout L, const int4* __restrict__ items, const 
 #pragma unroll
     for (int rb = 0; rb < 2; ++rb) dp[0][rb] = dp[1][rb] = *(lds_f32x4*)(size_t)(rsa + 128 + 4 * (16 * rb + 4 * g));
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks)
+    for (int ks = 0; ks < NKS; ++ks)
 #pragma unroll
       for (int rb = 0; rb < 2; ++rb) {
         const bf16x8 a = *(lds_bf16x8*)(size_t)(do0 + st + rowq + 2048 * ks + 256 * rb);
@@ -646,24 +700,24 @@ bwd_dkdv_kernel(BwdParams p, BwdLayout L, const int4* __restrict__ items, const 
 #pragma unroll
         for (int e = 0; e < 4; ++e) dsb[j][4 * rb + e] = (__bf16)(pf[j][rb][e] * dp[j][rb][e]);
 #pragma unroll
-    for (int db = 0; db < 8; ++db) {
+    for (int db = 0; db < NDB; ++db) {
       const bf16x8 a = tr_frag(qs0 + st + trq, db);
       acck[0][db] = mfma(a, dsb[0], acck[0][db]);
       acck[1][db] = mfma(a, dsb[1], acck[1][db]);
     }
-    if (++ch == G) { ch = 0; ++ce; }
+    if (++ch == grp) { ch = 0; ++ce; }
   }
   wait_vmcnt<0>();
 
   // Epilogue: lane holds dims 16 db + 4 g + e of key key0 + 16 j. A piece of
   // a split list (slot >= 0) writes its fp32 sums of dV and of dK-hat / scale
-  // to the slot ([2][256 keys][128 dims]) and a zero gain partial; the merge
+  // to the slot ([2][256 keys][D dims]) and a zero gain partial; the merge
   // adds the pieces and finishes.
   const int slot = __builtin_amdgcn_readfirstlane(items[2 * blockIdx.x + 1].y);
   float* pk = reinterpret_cast<float*>(ws + L.pkv) + size_t(slot < 0 ? 0 : slot) * 2 * kBwdKeysPerItem * D;
-  float gp[8][4];
+  float gp[NDB][4];
 #pragma unroll
-  for (int db = 0; db < 8; ++db)
+  for (int db = 0; db < NDB; ++db)
 #pragma unroll
     for (int e = 0; e < 4; ++e) gp[db][e] = 0.0f;
   __syncthreads();
@@ -672,7 +726,7 @@ bwd_dkdv_kernel(BwdParams p, BwdLayout L, const int4* __restrict__ items, const 
     if (slot >= 0) {
       const int kl = 32 * wave + 16 * j + r16;
 #pragma unroll
-      for (int db = 0; db < 8; ++db) {
+      for (int db = 0; db < NDB; ++db) {
         *reinterpret_cast<f32x4*>(pk + size_t(kl) * D + 16 * db + 4 * g) = accv[j][db];
         *reinterpret_cast<f32x4*>(pk + size_t(kBwdKeysPerItem + kl) * D + 16 * db + 4 * g) = acck[j][db];
       }
@@ -683,47 +737,56 @@ bwd_dkdv_kernel(BwdParams p, BwdLayout L, const int4* __restrict__ items, const 
     const size_t off = (size_t(valid ? key : 0) * p.hk + kvh) * D;
     if (valid) {
 #pragma unroll
-      for (int db = 0; db < 8; ++db) {
+      for (int db = 0; db < NDB; ++db) {
         bf16x4 w;
 #pragma unroll
         for (int e = 0; e < 4; ++e) w[e] = (__bf16)accv[j][db][e];
         *reinterpret_cast<bf16x4*>(static_cast<__bf16*>(p.dv) + off + 16 * db + 4 * g) = w;
       }
     }
-    float dxh[8][4];
+    float dxh[NDB][4];
 #pragma unroll
-    for (int db = 0; db < 8; ++db)
+    for (int db = 0; db < NDB; ++db)
 #pragma unroll
       for (int e = 0; e < 4; ++e) dxh[db][e] = p.scale * acck[j][db][e];
-    rms_backward_row(static_cast<const __bf16*>(p.k) + off, static_cast<__bf16*>(p.dk) + off, dxh, sm.gk, p.eps,
-                     valid, gp, g);
+    rms_backward_row<D>(static_cast<const __bf16*>(p.k) + off, static_cast<__bf16*>(p.dk) + off, dxh, sm.gk, p.eps,
+                        valid, gp, g);
   }
-  store_gain_partial(gp, sm.red, part, wave, lane, tid);
+  store_gain_partial<D>(gp, sm.red, part, wave, lane, tid);
 }
 
 // Sums the per-workgroup gain partials in a fixed order, in two levels:
 // workgroup b of REDUCE_SLICES (for dq, then as many for dk) sums the
 // partial rows [n b / S, n (b + 1) / S) into level[b]; the final pass sums
-// the S level rows. Threads: 2 halves x 128 dims.
+// the S level rows. Threads: 256 / D lanes of each of the D dims, whose
+// strided sums add up in lane order.
 constexpr int REDUCE_SLICES = 256;
+template <int D>
 __global__ void __launch_bounds__(256) bwd_gain_slices_kernel(const float* pgq, int nq, const float* pgk, int nk,
                                                              float* level) {
+  constexpr int H = 256 / D;
   const bool kside = blockIdx.x >= REDUCE_SLICES;
   const int b = kside ? blockIdx.x - REDUCE_SLICES : blockIdx.x;
   const float* src = kside ? pgk : pgq;
   const int n = kside ? nk : nq;
   const int i0 = int(int64_t(n) * b / REDUCE_SLICES), i1 = int(int64_t(n) * (b + 1) / REDUCE_SLICES);
-  __shared__ float half[D];
-  const int t = threadIdx.x, d = t & 127, h = t >> 7;
+  __shared__ float lanes[H][D];
+  const int t = threadIdx.x, d = t % D, h = t / D;
   float x = 0.0f;
-  for (int i = i0 + h; i < i1; i += 2) x += src[size_t(i) * D + d];
-  if (h == 1) half[d] = x;
+  for (int i = i0 + h; i < i1; i += H) x += src[size_t(i) * D + d];
+  if (h > 0) lanes[h][d] = x;
   __syncthreads();
-  if (h == 0) level[size_t(blockIdx.x) * D + d] = x + half[d];
+  if (h == 0) {
+#pragma unroll
+    for (int k = 1; k < H; ++k) x += lanes[k][d];
+    level[size_t(blockIdx.x) * D + d] = x;
+  }
 }
 
+template <int D>
 __global__ void __launch_bounds__(256) bwd_gain_final_kernel(const float* level, float* dq_gain, float* dk_gain) {
-  const int t = threadIdx.x, d = t & 127, side = t >> 7;
+  const int t = threadIdx.x, d = t % D, side = t / D;
+  if (side > 1) return;
   float x = 0.0f;
   for (int b = 0; b < REDUCE_SLICES; ++b) x += level[size_t(side * REDUCE_SLICES + b) * D + d];
   (side ? dk_gain : dq_gain)[d] = x;
@@ -732,10 +795,12 @@ __global__ void __launch_bounds__(256) bwd_gain_final_kernel(const float* level,
 // Finishes a split dk/dv item: sums its pieces' slots in piece order, writes
 // dV, applies the RMSNorm backward to dK-hat = scale * sum and writes dK and
 // the workgroup's gain partial (row n_kv_items + merge index). Thread t
-// handles dims [32 (t % 4), +32) of keys t / 4 + 64 i, i = 0..3.
+// handles dims [D / 4 (t % 4), +D / 4) of keys t / 4 + 64 i, i = 0..3.
 constexpr int MERGE_THREADS = 256;
+template <int D>
 __global__ void __launch_bounds__(MERGE_THREADS) bwd_kv_merge_kernel(BwdParams p, BwdLayout L,
                                                                      const int4* __restrict__ merges) {
+  constexpr int DPT = D / 4;                          // dims per thread
   __shared__ float gk[D];
   __shared__ float red[64][D + 1];
   unsigned char* ws = static_cast<unsigned char*>(p.ws);
@@ -743,21 +808,21 @@ __global__ void __launch_bounds__(MERGE_THREADS) bwd_kv_merge_kernel(BwdParams p
   const int t = threadIdx.x, quarter = t & 3, kq = t >> 2;
   if (t < D) gk[t] = p.k_gain[t];
   __syncthreads();
-  float gp[32];
+  float gp[DPT];
 #pragma unroll
-  for (int i = 0; i < 32; ++i) gp[i] = 0.0f;
+  for (int i = 0; i < DPT; ++i) gp[i] = 0.0f;
   const float* slots = reinterpret_cast<const float*>(ws + L.pkv);
   for (int pass = 0; pass < kBwdKeysPerItem / 64; ++pass) {
     const int kl = 64 * pass + kq;
     const int key = m.x * kBwdKeysPerItem + kl;
     const bool valid = key < p.tk;
-    float sv[32], sk[32];
+    float sv[DPT], sk[DPT];
 #pragma unroll
-    for (int i = 0; i < 32; ++i) sv[i] = sk[i] = 0.0f;
+    for (int i = 0; i < DPT; ++i) sv[i] = sk[i] = 0.0f;
     for (int k = 0; k < m.w; ++k) {
-      const float* s = slots + size_t(m.z + k) * 2 * kBwdKeysPerItem * D + size_t(kl) * D + 32 * quarter;
+      const float* s = slots + size_t(m.z + k) * 2 * kBwdKeysPerItem * D + size_t(kl) * D + DPT * quarter;
 #pragma unroll
-      for (int c = 0; c < 8; ++c) {
+      for (int c = 0; c < DPT / 4; ++c) {
         const f32x4 a = *reinterpret_cast<const f32x4*>(s + 4 * c);
         const f32x4 b = *reinterpret_cast<const f32x4*>(s + size_t(kBwdKeysPerItem) * D + 4 * c);
 #pragma unroll
@@ -767,10 +832,10 @@ __global__ void __launch_bounds__(MERGE_THREADS) bwd_kv_merge_kernel(BwdParams p
         }
       }
     }
-    const size_t off = (size_t(valid ? key : 0) * p.hk + m.y) * D + 32 * quarter;
-    float x[32];
+    const size_t off = (size_t(valid ? key : 0) * p.hk + m.y) * D + DPT * quarter;
+    float x[DPT];
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
+    for (int c = 0; c < DPT / 8; ++c) {
       const bf16x8 xv = valid ? *reinterpret_cast<const bf16x8*>(static_cast<const __bf16*>(p.k) + off + 8 * c)
                               : bf16x8{};
 #pragma unroll
@@ -778,26 +843,26 @@ __global__ void __launch_bounds__(MERGE_THREADS) bwd_kv_merge_kernel(BwdParams p
     }
     float ss = 0.0f;
 #pragma unroll
-    for (int i = 0; i < 32; ++i) ss += x[i] * x[i];
+    for (int i = 0; i < DPT; ++i) ss += x[i] * x[i];
     ss += __shfl_xor(ss, 1, 64);
     ss += __shfl_xor(ss, 2, 64);
     const float r = __builtin_amdgcn_rsqf(ss * (1.0f / D) + p.eps);
     float mm = 0.0f;
 #pragma unroll
-    for (int i = 0; i < 32; ++i) mm += x[i] * r * gk[32 * quarter + i] * (p.scale * sk[i]);
+    for (int i = 0; i < DPT; ++i) mm += x[i] * r * gk[DPT * quarter + i] * (p.scale * sk[i]);
     mm += __shfl_xor(mm, 1, 64);
     mm += __shfl_xor(mm, 2, 64);
     mm *= 1.0f / D;
     if (valid) {
 #pragma unroll
-      for (int c = 0; c < 4; ++c) {
+      for (int c = 0; c < DPT / 8; ++c) {
         bf16x8 wv, wk;
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           const int i = 8 * c + e;
           const float dxh = p.scale * sk[i], u = x[i] * r;
           wv[e] = (__bf16)sv[i];
-          wk[e] = (__bf16)((gk[32 * quarter + i] * dxh - u * mm) * r);
+          wk[e] = (__bf16)((gk[DPT * quarter + i] * dxh - u * mm) * r);
           gp[i] += u * dxh;
         }
         *reinterpret_cast<bf16x8*>(static_cast<__bf16*>(p.dv) + off + 8 * c) = wv;
@@ -807,7 +872,7 @@ __global__ void __launch_bounds__(MERGE_THREADS) bwd_kv_merge_kernel(BwdParams p
   }
   // gain partial: sum over the 64 keys of each quarter
 #pragma unroll
-  for (int i = 0; i < 32; ++i) red[kq][32 * quarter + i] = gp[i];
+  for (int i = 0; i < DPT; ++i) red[kq][DPT * quarter + i] = gp[i];
   __syncthreads();
   if (t < D) {
     float s = 0.0f;
@@ -820,9 +885,11 @@ __global__ void __launch_bounds__(MERGE_THREADS) bwd_kv_merge_kernel(BwdParams p
 // (dq-hat = sum / log2 e), applies the RMSNorm backward, writes dq and the
 // workgroup's gain partial (row n_dq_items + merge index). Item row r is token
 // t0 + r % tile_q of head h0 + r / tile_q. Thread t handles dims
-// [32 (t % 4), +32) of rows t / 4 + 64 i, i = 0..3.
+// [D / 4 (t % 4), +D / 4) of rows t / 4 + 64 i, i = 0..3.
+template <int D>
 __global__ void __launch_bounds__(MERGE_THREADS) bwd_dq_merge_kernel(BwdParams p, BwdLayout L,
                                                                      const int4* __restrict__ merges) {
+  constexpr int DPT = D / 4;                          // dims per thread
   __shared__ float gq[D];
   __shared__ float red[64][D + 1];
   unsigned char* ws = static_cast<unsigned char*>(p.ws);
@@ -831,30 +898,30 @@ __global__ void __launch_bounds__(MERGE_THREADS) bwd_dq_merge_kernel(BwdParams p
   const int t = threadIdx.x, quarter = t & 3, rq = t >> 2;
   if (t < D) gq[t] = p.q_gain[t];
   __syncthreads();
-  float gp[32];
+  float gp[DPT];
 #pragma unroll
-  for (int i = 0; i < 32; ++i) gp[i] = 0.0f;
+  for (int i = 0; i < DPT; ++i) gp[i] = 0.0f;
   const float* slots = reinterpret_cast<const float*>(ws + L.pdq);
   for (int pass = 0; pass < kBwdRowsPerItem / 64; ++pass) {
     const int r = 64 * pass + rq;
     const int tok = m.x + r % p.tile_q, head = h0 + r / p.tile_q;
     const bool valid = tok < p.tq;
-    float sq[32];
+    float sq[DPT];
 #pragma unroll
-    for (int i = 0; i < 32; ++i) sq[i] = 0.0f;
+    for (int i = 0; i < DPT; ++i) sq[i] = 0.0f;
     for (int k = 0; k < m.w; ++k) {
-      const float* s = slots + (size_t(m.z + k) * kBwdRowsPerItem + r) * D + 32 * quarter;
+      const float* s = slots + (size_t(m.z + k) * kBwdRowsPerItem + r) * D + DPT * quarter;
 #pragma unroll
-      for (int c = 0; c < 8; ++c) {
+      for (int c = 0; c < DPT / 4; ++c) {
         const f32x4 a = *reinterpret_cast<const f32x4*>(s + 4 * c);
 #pragma unroll
         for (int e = 0; e < 4; ++e) sq[4 * c + e] += a[e];
       }
     }
-    const size_t off = (size_t(valid ? tok : 0) * p.hq + head) * D + 32 * quarter;
-    float x[32];
+    const size_t off = (size_t(valid ? tok : 0) * p.hq + head) * D + DPT * quarter;
+    float x[DPT];
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
+    for (int c = 0; c < DPT / 8; ++c) {
       const bf16x8 xv = valid ? *reinterpret_cast<const bf16x8*>(static_cast<const __bf16*>(p.q) + off + 8 * c)
                               : bf16x8{};
 #pragma unroll
@@ -862,25 +929,25 @@ __global__ void __launch_bounds__(MERGE_THREADS) bwd_dq_merge_kernel(BwdParams p
     }
     float ss = 0.0f;
 #pragma unroll
-    for (int i = 0; i < 32; ++i) ss += x[i] * x[i];
+    for (int i = 0; i < DPT; ++i) ss += x[i] * x[i];
     ss += __shfl_xor(ss, 1, 64);
     ss += __shfl_xor(ss, 2, 64);
     const float rr = __builtin_amdgcn_rsqf(ss * (1.0f / D) + p.eps);
     float mm = 0.0f;
 #pragma unroll
-    for (int i = 0; i < 32; ++i) mm += x[i] * rr * gq[32 * quarter + i] * (sq[i] * (1.0f / kLog2e));
+    for (int i = 0; i < DPT; ++i) mm += x[i] * rr * gq[DPT * quarter + i] * (sq[i] * (1.0f / kLog2e));
     mm += __shfl_xor(mm, 1, 64);
     mm += __shfl_xor(mm, 2, 64);
     mm *= 1.0f / D;
     if (valid) {
 #pragma unroll
-      for (int c = 0; c < 4; ++c) {
+      for (int c = 0; c < DPT / 8; ++c) {
         bf16x8 w;
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           const int i = 8 * c + e;
           const float dxh = sq[i] * (1.0f / kLog2e), u = x[i] * rr;
-          w[e] = (__bf16)((gq[32 * quarter + i] * dxh - u * mm) * rr);
+          w[e] = (__bf16)((gq[DPT * quarter + i] * dxh - u * mm) * rr);
           gp[i] += u * dxh;
         }
         *reinterpret_cast<bf16x8*>(static_cast<__bf16*>(p.dq) + off + 8 * c) = w;
@@ -888,7 +955,7 @@ __global__ void __launch_bounds__(MERGE_THREADS) bwd_dq_merge_kernel(BwdParams p
     }
   }
 #pragma unroll
-  for (int i = 0; i < 32; ++i) red[rq][32 * quarter + i] = gp[i];
+  for (int i = 0; i < DPT; ++i) red[rq][DPT * quarter + i] = gp[i];
   __syncthreads();
   if (t < D) {
     float s = 0.0f;
@@ -926,9 +993,10 @@ hipError_t launch_bwd_zero_rows(const BwdParams& p, int row_bytes, hipStream_t s
   return hipGetLastError();
 }
 
-BwdLayout bwd_workspace_layout(long long tq, long long tk, int hq, int hk, int n_dq_rows, int n_kv_rows,
+BwdLayout bwd_workspace_layout(long long tq, long long tk, int hq, int hk, int D, int n_dq_rows, int n_kv_rows,
                                int n_kv_slots, int n_dq_slots) {
   auto up = [](size_t x) { return (x + 255) / 256 * 256; };
+  const size_t IMG = size_t(TT) * D * 2;
   const size_t qimg = size_t((tq + TT - 1) / TT) * size_t(hq) * IMG;
   const size_t kimg = size_t((tk + TT - 1) / TT) * size_t(hk) * IMG;
   BwdLayout L{};
@@ -946,31 +1014,44 @@ BwdLayout bwd_workspace_layout(long long tq, long long tk, int hq, int hk, int n
   return L;
 }
 
-hipError_t launch_bwd_bf16_d128(const BwdParams& p, hipStream_t stream) {
-  const BwdLayout L = bwd_workspace_layout(p.tq, p.tk, p.hq, p.hk, p.n_dq_items + p.n_dq_merges,
+namespace {
+
+template <int D>
+hipError_t launch_bwd_bf16_d(const BwdParams& p, hipStream_t stream) {
+  const BwdLayout L = bwd_workspace_layout(p.tq, p.tk, p.hq, p.hk, D, p.n_dq_items + p.n_dq_merges,
                                            p.n_kv_items + p.n_kv_merges, p.n_kv_slots, p.n_dq_slots);
   const unsigned n_tt = unsigned((p.tq + TT - 1) / TT), n_kt = unsigned((p.tk + TT - 1) / TT);
-  hipLaunchKernelGGL(bwd_prep_q_kernel, dim3(n_tt * unsigned(p.hq)), dim3(PREP_THREADS), 0, stream, p, L);
+  hipLaunchKernelGGL(bwd_prep_q_kernel<D>, dim3(n_tt * unsigned(p.hq)), dim3(PREP_THREADS), 0, stream, p, L);
   if (n_kt > 0)
-    hipLaunchKernelGGL(bwd_prep_k_kernel, dim3(n_kt * unsigned(p.hk)), dim3(PREP_THREADS), 0, stream, p, L);
+    hipLaunchKernelGGL(bwd_prep_k_kernel<D>, dim3(n_kt * unsigned(p.hk)), dim3(PREP_THREADS), 0, stream, p, L);
   const hipError_t ez = launch_bwd_zero_rows(p, D * 2, stream);
   if (ez != hipSuccess) return ez;
   if (p.n_dq_items > 0)
-    hipLaunchKernelGGL(bwd_dq_kernel, dim3(p.n_dq_items), dim3(NTHR), 0, stream, p, L, p.dq_items, p.dq_tiles,
+    hipLaunchKernelGGL(bwd_dq_kernel<D>, dim3(p.n_dq_items), dim3(NTHR), 0, stream, p, L, p.dq_items, p.dq_tiles,
                        p.dq_soffs);
   if (p.n_kv_items > 0)
-    hipLaunchKernelGGL(bwd_dkdv_kernel, dim3(p.n_kv_items), dim3(NTHR), 0, stream, p, L, p.kv_items, p.kv_tiles);
+    hipLaunchKernelGGL(bwd_dkdv_kernel<D>, dim3(p.n_kv_items), dim3(NTHR), 0, stream, p, L, p.kv_items, p.kv_tiles);
   if (p.n_kv_merges > 0)
-    hipLaunchKernelGGL(bwd_kv_merge_kernel, dim3(p.n_kv_merges), dim3(MERGE_THREADS), 0, stream, p, L, p.kv_merges);
+    hipLaunchKernelGGL(bwd_kv_merge_kernel<D>, dim3(p.n_kv_merges), dim3(MERGE_THREADS), 0, stream, p, L,
+                       p.kv_merges);
   if (p.n_dq_merges > 0)
-    hipLaunchKernelGGL(bwd_dq_merge_kernel, dim3(p.n_dq_merges), dim3(MERGE_THREADS), 0, stream, p, L, p.dq_merges);
+    hipLaunchKernelGGL(bwd_dq_merge_kernel<D>, dim3(p.n_dq_merges), dim3(MERGE_THREADS), 0, stream, p, L,
+                       p.dq_merges);
   unsigned char* ws = static_cast<unsigned char*>(p.ws);
   float* level = reinterpret_cast<float*>(ws + L.level);
-  hipLaunchKernelGGL(bwd_gain_slices_kernel, dim3(2 * REDUCE_SLICES), dim3(256), 0, stream,
+  hipLaunchKernelGGL(bwd_gain_slices_kernel<D>, dim3(2 * REDUCE_SLICES), dim3(256), 0, stream,
                      reinterpret_cast<const float*>(ws + L.pgq), p.n_dq_items + p.n_dq_merges,
                      reinterpret_cast<const float*>(ws + L.pgk), p.n_kv_items + p.n_kv_merges, level);
-  hipLaunchKernelGGL(bwd_gain_final_kernel, dim3(1), dim3(256), 0, stream, level, p.dq_gain, p.dk_gain);
+  hipLaunchKernelGGL(bwd_gain_final_kernel<D>, dim3(1), dim3(256), 0, stream, level, p.dq_gain, p.dk_gain);
   return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_bwd_bf16(const BwdParams& p, int head_dim, hipStream_t stream) {
+  if (head_dim == 128) return launch_bwd_bf16_d<128>(p, stream);
+  if (head_dim == 64) return launch_bwd_bf16_d<64>(p, stream);
+  return hipErrorInvalidValue;
 }
 
 }  // namespace magi

@@ -105,9 +105,9 @@ struct BwdLayout {
 // each); n_kv_slots: partial slots of split dk/dv items (fp32 dV and dK-hat
 // sums, 256 KiB each); n_dq_slots: those of split dq items (fp32 dq-hat sums,
 // 128 KiB each).
-BwdLayout bwd_workspace_layout(long long tq, long long tk, int hq, int hk, int n_dq_rows, int n_kv_rows,
-                               int n_kv_slots, int n_dq_slots);
-hipError_t launch_bwd_bf16_d128(const BwdParams& p, hipStream_t stream);
+BwdLayout bwd_workspace_layout(long long tq, long long tk, int hq, int hk, int head_dim, int n_dq_rows,
+                               int n_kv_rows, int n_kv_slots, int n_dq_slots);
+hipError_t launch_bwd_bf16(const BwdParams& p, int head_dim, hipStream_t stream);
 hipError_t launch_bwd_fp32(const BwdParams& p, int head_dim, hipStream_t stream);
 // Writes zeros where no item writes: dq over the p.dq_zero blocks, dk and dv
 // over the p.kv_zero blocks (rows of row_bytes = head_dim * element size).

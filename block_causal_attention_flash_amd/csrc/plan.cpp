@@ -502,10 +502,6 @@ magi_status_t build_host_plan(int32_t kind, const magi_attn_layout_t* L, const m
 magi_status_t build_bwd_plan(const magi_attn_layout_t* L, const magi_attn_text_t* T, BwdHostPlan& B,
                              std::string& err) {
   const int group = L->n_q_heads / L->n_kv_heads;
-  if (L->dtype == MAGI_DTYPE_BF16 && L->head_dim != 128) {
-    err = "the bf16 backward supports head_dim 128";
-    return MAGI_ERR_UNSUPPORTED;
-  }
   const Tiling tiling = choose_bwd_tiling(L->dtype, L->head_dim, group);
   if (L->dtype == MAGI_DTYPE_BF16 && tiling.tile_q % 32 != 0) {
     err = "internal: backward query tile not a multiple of 32 tokens";

@@ -94,7 +94,7 @@ typedef enum magi_dtype {
  *                        its queries see every key of the stream, [0, T_k);
  *                        no other video sees its keys. 0: off.
  * A chunk that owns queries must see at least one key.
- * head_dim: 64 or 128 (the bf16 backward: 128). n_q_heads % n_kv_heads == 0.
+ * head_dim: 64 or 128. n_q_heads % n_kv_heads == 0.
  */
 typedef struct magi_attn_layout {
   int32_t n_seqs;

@@ -88,9 +88,10 @@ SMALL = [
 
 @pytest.mark.parametrize("name,lay", SMALL, ids=[s[0] for s in SMALL])
 @pytest.mark.parametrize("hq,hk", [(6, 2), (8, 1), (3, 3)])
-def test_bf16_backward_small(name, lay, hq, hk):
-    log(f"bf16 backward {name} {hq}/{hk}")
-    errs = check(lay, hq, hk, 128, "bf16", seed=hq * 7 + hk)
+@pytest.mark.parametrize("d", [64, 128])
+def test_bf16_backward_small(name, lay, hq, hk, d):
+    log(f"bf16 backward {name} {hq}/{hk} d={d}")
+    errs = check(lay, hq, hk, d, "bf16", seed=hq * 7 + hk + d)
     log("  rel_l2 dq {:.2e} dk {:.2e} dv {:.2e} dgq {:.2e} dgk {:.2e}".format(*errs))
 
 
@@ -109,9 +110,10 @@ SPLIT_DQ = [
 
 @pytest.mark.parametrize("name,lay", SPLIT_DQ, ids=[s[0] for s in SPLIT_DQ])
 @pytest.mark.parametrize("hq,hk", [(6, 2), (8, 1)])
-def test_bf16_backward_split_dq_items(name, lay, hq, hk):
-    log(f"bf16 backward, split dq items: {name} {hq}/{hk}")
-    errs = check(lay, hq, hk, 128, "bf16", seed=hq * 11 + hk)
+@pytest.mark.parametrize("d", [64, 128])
+def test_bf16_backward_split_dq_items(name, lay, hq, hk, d):
+    log(f"bf16 backward, split dq items: {name} {hq}/{hk} d={d}")
+    errs = check(lay, hq, hk, d, "bf16", seed=hq * 11 + hk + d)
     log("  rel_l2 dq {:.2e} dk {:.2e} dv {:.2e} dgq {:.2e} dgk {:.2e}".format(*errs))
 
 
@@ -133,9 +135,10 @@ def test_keys_no_row_sees_get_zero_gradients():
     assert np.all(got[1][:300] == 0) and np.all(got[2][:300] == 0)
 
 
-def test_bf16_backward_scale_and_eps():
+@pytest.mark.parametrize("d", [64, 128])
+def test_bf16_backward_scale_and_eps(d):
     lay = layout_from_chunks([[90, 60]])
-    check(lay, 4, 2, 128, "bf16", seed=3, eps=0.25, scale=0.05)
+    check(lay, 4, 2, d, "bf16", seed=3, eps=0.25, scale=0.05)
 
 
 @pytest.mark.parametrize("lay", [layout_from_chunks([[100, 157, 91]]), streaming_layout(8, 2, 600)],

@@ -100,9 +100,10 @@ SMALL = [
 
 @pytest.mark.parametrize("name,lay,text", SMALL, ids=[s[0] for s in SMALL])
 @pytest.mark.parametrize("hq,hk", [(6, 2), (8, 1), (3, 3)])
-def test_bf16_cross_backward_small(name, lay, text, hq, hk):
-    log(f"bf16 cross backward {name} {hq}/{hk}")
-    errs = check(lay, text, hq, hk, 128, "bf16", seed=hq * 7 + hk)
+@pytest.mark.parametrize("d", [64, 128])
+def test_bf16_cross_backward_small(name, lay, text, hq, hk, d):
+    log(f"bf16 cross backward {name} {hq}/{hk} d={d}")
+    errs = check(lay, text, hq, hk, d, "bf16", seed=hq * 7 + hk + d)
     log("  rel_l2 dq {:.2e} dk {:.2e} dv {:.2e} dgq {:.2e} dgk {:.2e}".format(*errs))
 
 
