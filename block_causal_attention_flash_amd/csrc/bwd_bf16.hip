@@ -637,10 +637,15 @@ bwd_dkdv_kernel(BwdParams p, BwdLayout L, const int4* __restrict__ items, const 
     const bool masked = ce >= n_full;
     const int tt = codes[ce] >> 1;
     // S (lane: key r16 of half j, rows 16 rb + 4 g + e of the step's token
-    // tile), started from the rows' -lse log2 e so that it ends as S - lse log2 e
-    f32x4 sc[2][2];
+    // tile), started from the rows' -lse log2 e so that it ends as S - lse log2 e,
+    // and dP, started from -D so that it ends as dP - D: both products read the
+    // step's row images and do not depend on the mask.
+    f32x4 sc[2][2], dp[2][2];
 #pragma unroll
-    for (int rb = 0; rb < 2; ++rb) sc[0][rb] = sc[1][rb] = *(lds_f32x4*)(size_t)(rsa + 4 * (16 * rb + 4 * g));
+    for (int rb = 0; rb < 2; ++rb) {
+      sc[0][rb] = sc[1][rb] = *(lds_f32x4*)(size_t)(rsa + 4 * (16 * rb + 4 * g));
+      dp[0][rb] = dp[1][rb] = *(lds_f32x4*)(size_t)(rsa + 128 + 4 * (16 * rb + 4 * g));
+    }
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks)
 #pragma unroll
@@ -649,6 +654,22 @@ bwd_dkdv_kernel(BwdParams p, BwdLayout L, const int4* __restrict__ items, const 
         sc[0][rb] = mfma(a, ku[0][ks], sc[0][rb]);
         sc[1][rb] = mfma(a, ku[1][ks], sc[1][rb]);
       }
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks)
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb) {
+        const bf16x8 a = *(lds_bf16x8*)(size_t)(do0 + st + rowq + 2048 * ks + 256 * rb);
+        dp[0][rb] = mfma(a, vv[0][ks], dp[0][rb]);
+        dp[1][rb] = mfma(a, vv[1][ks], dp[1][rb]);
+      }
+    // both products with their row fragments read two ahead of the MFMAs
+    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+#pragma unroll
+    for (int f = 0; f < 4 * NKS; ++f) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+      if (f < 4 * NKS - 2) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
     if (masked) {                                     // rows that do not see the key: S = -inf, P = 0
       asm volatile("" ::: "memory");                  // a branch, not selects on every step
 #pragma unroll
@@ -663,8 +684,9 @@ bwd_dkdv_kernel(BwdParams p, BwdLayout L, const int4* __restrict__ items, const 
               sc[j][rb][e] = -__builtin_inff();
           }
     }
-    f32x4 pf[2][2];
-    bf16x8 pb[2];
+    // P and dS = P (dP - D) in bf16, then dV^T += dO^T P and dK^T += q_hat^T dS,
+    // one transposed fragment of each image per dim block
+    bf16x8 pb[2], dsb[2];
 #pragma unroll
     for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
@@ -672,38 +694,24 @@ bwd_dkdv_kernel(BwdParams p, BwdLayout L, const int4* __restrict__ items, const 
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const float pv = __builtin_amdgcn_exp2f(sc[j][rb][e]);
-          pf[j][rb][e] = pv;
           pb[j][4 * rb + e] = (__bf16)pv;
+          dsb[j][4 * rb + e] = (__bf16)(pv * dp[j][rb][e]);
         }
 #pragma unroll
     for (int db = 0; db < NDB; ++db) {
       const bf16x8 a = tr_frag(do0 + st + trq, db);
+      const bf16x8 b = tr_frag(qs0 + st + trq, db);
       accv[0][db] = mfma(a, pb[0], accv[0][db]);
       accv[1][db] = mfma(a, pb[1], accv[1][db]);
+      acck[0][db] = mfma(b, dsb[0], acck[0][db]);
+      acck[1][db] = mfma(b, dsb[1], acck[1][db]);
     }
-    f32x4 dp[2][2];                                   // started from -D: ends as dP - D
-#pragma unroll
-    for (int rb = 0; rb < 2; ++rb) dp[0][rb] = dp[1][rb] = *(lds_f32x4*)(size_t)(rsa + 128 + 4 * (16 * rb + 4 * g));
-#pragma unroll
-    for (int ks = 0; ks < NKS; ++ks)
-#pragma unroll
-      for (int rb = 0; rb < 2; ++rb) {
-        const bf16x8 a = *(lds_bf16x8*)(size_t)(do0 + st + rowq + 2048 * ks + 256 * rb);
-        dp[0][rb] = mfma(a, vv[0][ks], dp[0][rb]);
-        dp[1][rb] = mfma(a, vv[1][ks], dp[1][rb]);
-      }
-    bf16x8 dsb[2];
-#pragma unroll
-    for (int rb = 0; rb < 2; ++rb)
-#pragma unroll
-      for (int j = 0; j < 2; ++j)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) dsb[j][4 * rb + e] = (__bf16)(pf[j][rb][e] * dp[j][rb][e]);
+    // transposed reads (two per fragment) one dim block ahead of the MFMAs
+    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
 #pragma unroll
     for (int db = 0; db < NDB; ++db) {
-      const bf16x8 a = tr_frag(qs0 + st + trq, db);
-      acck[0][db] = mfma(a, dsb[0], acck[0][db]);
-      acck[1][db] = mfma(a, dsb[1], acck[1][db]);
+      __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+      if (db < NDB - 1) __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
     }
     if (++ch == grp) { ch = 0; ++ce; }
   }
