@@ -263,6 +263,10 @@ def bench_backward(args) -> None:
     own_dim = args.head_dim in (0, cfg.head_dim)
     if not own_dim:
         cfg = dataclasses.replace(cfg, head_dim=args.head_dim)
+    if args.heads:
+        hq, hk = (int(x) for x in args.heads.split("/"))
+        own_dim = own_dim and (hq, hk) == (cfg.n_q_heads, cfg.n_kv_heads)
+        cfg = dataclasses.replace(cfg, n_q_heads=hq, n_kv_heads=hk)
     lay = cfg.layout
     cross = args.attention == "cross"
     dev = torch.device("cuda", 0)
@@ -373,6 +377,9 @@ def main():
     ap.add_argument("--head-dim", type=int, default=0, choices=(0, 64, 128),
                     help="run the workload at this head_dim instead of its own (64 or 128; the scale follows "
                          "as 1/sqrt(head_dim))")
+    ap.add_argument("--heads", default="",
+                    help="HQ/HK: run the workload with these head counts instead of its own, e.g. 6/1 for one GPU's "
+                         "share of the 48/8 heads sharded by KV head over 8 GPUs")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=20.0)
     ap.add_argument("--copy-probe-mib", type=int, default=0,
@@ -403,6 +410,10 @@ def main():
     own_dim = args.head_dim in (0, cfg.head_dim)
     if not own_dim:
         cfg = dataclasses.replace(cfg, head_dim=args.head_dim)
+    if args.heads:
+        hq, hk = (int(x) for x in args.heads.split("/"))
+        own_dim = own_dim and (hq, hk) == (cfg.n_q_heads, cfg.n_kv_heads)
+        cfg = dataclasses.replace(cfg, n_q_heads=hq, n_kv_heads=hk)
     lay = cfg.layout
     mode = args.attention
     text = text_layout(cfg) if mode != "self" else None

@@ -2,8 +2,8 @@
 scratch as its workspace, for callers that cannot allocate) against
 magi_attn_fwd with a caller workspace, through the C ABI.
 
-Two calls in a row on different plans, the second smaller than the first, so
-that the second reads a scratch array still holding the first call's images,
+Calls in a row on different plans (head_dim 128 and 64), the last smaller than
+the others, so that each reads a scratch array still holding the previous call's images,
 partial results and flags: each output must equal magi_attn_fwd's bit for bit
 (same kernels, same inputs), and both are checked against the fp64 oracle at
 the bf16 tolerances. Outputs start as NaN, so an element the call does not
@@ -47,29 +47,31 @@ def split_layout():
 
 
 CASES = [
-    ("two videos, 6/2", layout_from_chunks([[300, 157, 91], [200, 64]]), 6, 2, 31),
-    ("split KV cache, 8/2", split_layout(), 8, 2, 32),
-    ("one small chunk, 3/1", layout_from_chunks([[130, 70]]), 3, 1, 33),
+    ("two videos, 6/2", layout_from_chunks([[300, 157, 91], [200, 64]]), 6, 2, 128, 31),
+    ("split KV cache, 8/2", split_layout(), 8, 2, 128, 32),
+    ("split KV cache, 8/2, head_dim 64", split_layout(), 8, 2, 64, 34),
+    ("one small chunk, 3/1", layout_from_chunks([[130, 70]]), 3, 1, 128, 33),
 ]
 
 
-def _run_pair(lay, hq, hk, seed):
+def _run_pair(lay, hq, hk, d, seed):
     from block_causal_attention_flash_amd import Plan, magi_attn_fwd, magi_attn_fwd_noalloc, magi_attn_plan_stats
-    inp = make_inputs(lay, hq, hk, 128, "bf16", "uniform", seed)
+    sc = 1.0 / math.sqrt(d)
+    inp = make_inputs(lay, hq, hk, d, "bf16", "uniform", seed)
     g = {n: t.to(DEV) for n, t in inp.items()}
-    plan = Plan.from_layout(lay, hq, hk, 128, "bf16")
-    st = magi_attn_plan_stats(lay.q_offsets, lay.kv_offsets, lay.seq_chunks, hq, hk, 128, "bf16")
+    plan = Plan.from_layout(lay, hq, hk, d, "bf16")
+    st = magi_attn_plan_stats(lay.q_offsets, lay.kv_offsets, lay.seq_chunks, hq, hk, d, "bf16")
     out_a = torch.full_like(g["q"], float("nan"))
     lse_a = torch.full((hq, lay.t_q), float("nan"), dtype=torch.float32, device=DEV)
     ws = torch.empty(max(plan.workspace_size(), 16), dtype=torch.uint8, device=DEV)
-    magi_attn_fwd(plan.handle, g["q"], g["k"], g["v"], g["q_gain"], g["k_gain"], 1e-6, SC, out=out_a, lse=lse_a,
+    magi_attn_fwd(plan.handle, g["q"], g["k"], g["v"], g["q_gain"], g["k_gain"], 1e-6, sc, out=out_a, lse=lse_a,
                   workspace=ws)
     out_b = torch.full_like(g["q"], float("nan"))
     lse_b = torch.full((hq, lay.t_q), float("nan"), dtype=torch.float32, device=DEV)
-    magi_attn_fwd_noalloc(plan.handle, g["q"], g["k"], g["v"], g["q_gain"], g["k_gain"], 1e-6, SC, out_b, lse_b)
+    magi_attn_fwd_noalloc(plan.handle, g["q"], g["k"], g["v"], g["q_gain"], g["k_gain"], 1e-6, sc, out_b, lse_b)
     torch.cuda.synchronize()
     assert torch.equal(out_a, out_b) and torch.equal(lse_a, lse_b)
-    ro, rl = oracle.attention(inp["q"], inp["k"], inp["v"], inp["q_gain"], inp["k_gain"], 1e-6, SC, lay)
+    ro, rl = oracle.attention(inp["q"], inp["k"], inp["v"], inp["q_gain"], inp["k_gain"], 1e-6, sc, lay)
     got = out_b.double().cpu().numpy()
     gl = lse_b.double().cpu().numpy()
     rl2 = float(np.linalg.norm(got - ro) / np.linalg.norm(ro))
@@ -83,12 +85,12 @@ def _run_pair(lay, hq, hk, seed):
 
 def test_noalloc_equals_fwd_on_consecutive_calls():
     sizes = []
-    for name, lay, hq, hk, seed in CASES:
+    for name, lay, hq, hk, d, seed in CASES:
         log(f"noalloc: {name}")
-        ws_bytes, n_items, rl2 = _run_pair(lay, hq, hk, seed)
+        ws_bytes, n_items, rl2 = _run_pair(lay, hq, hk, d, seed)
         log(f"noalloc: {name}: workspace {ws_bytes} bytes, {n_items} items, rel_l2 {rl2:.3e}")
         sizes.append(ws_bytes)
-    assert sizes[2] < sizes[1] and sizes[2] < sizes[0]    # the last call is the smallest
+    assert all(sizes[-1] < x for x in sizes[:-1])         # the last call is the smallest
 
 
 def test_noalloc_refuses_a_workspace_beyond_the_scratch():
