@@ -63,11 +63,17 @@ def useful_text_pairs(layout, text) -> int:
                for c in range(layout.n_chunks))
 
 
+KERNEL_HEADERS = [os.path.join(ROOT, "block_causal_attention_flash_amd", "csrc", h) for h in ("cdna4.hpp", "kernels.hpp")]
+
+
 def kernel_hash(path: str = KERNEL_SRC) -> str:
-    """sha256 (16 hex digits) of a kernel source with comments and blank
-    space removed, so that the stored counters go stale on code changes only."""
-    with open(path) as f:
-        src = f.read()
+    """sha256 (16 hex digits) of a kernel source followed by the shared
+    headers it compiles with, comments and blank space removed, so that the
+    stored counters go stale on code changes only."""
+    src = ""
+    for name in [path] + KERNEL_HEADERS:
+        with open(name) as f:
+            src += f.read() + "\n"
     src = re.sub(r"/\*.*?\*/", " ", src, flags=re.S)
     src = re.sub(r"//[^\n]*", " ", src)
     src = " ".join(src.split())

@@ -55,27 +55,15 @@
 // image is 64 D bytes: at D = 128 every thread copies 16 bytes of each of a
 // step's two images, at D = 64 waves 0-3 copy the first and waves 4-7 the
 // second.
+#include "cdna4.hpp"
 #include "kernels.hpp"
 
 namespace magi {
 namespace {
 
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-typedef int i32x4 __attribute__((ext_vector_type(4)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-
-#define LDS_PTR(T, p) ((__attribute__((address_space(3))) T*)(p))
-typedef __attribute__((address_space(3))) const bf16x8 lds_bf16x8;
-typedef __attribute__((address_space(3))) const f32x4 lds_f32x4;
-typedef short i16x4 __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
-
 constexpr int TT = 32;                       // tokens per image (and per dk/dv step), keys per dq tile
 constexpr int NTHR = 512;
 constexpr int RING = 8;                      // LDS ring stages: copies four steps ahead, a barrier every second step
-constexpr unsigned kNoTile = 0x80000000u;    // past every image array (< 2 GiB): zeros
-constexpr float kLog2e = 1.4426950408889634f;
 static_assert(kBwdRowsPerItem == 8 * 32 && kBwdKeysPerItem == 8 * 32, "8 waves per workgroup");
 
 // Sizes that depend on head_dim D.
@@ -90,51 +78,7 @@ struct BGeo {
   static_assert(COPY_THREADS == NTHR || 2 * COPY_THREADS == NTHR, "copy units");
 };
 
-__device__ __forceinline__ unsigned lds_addr(const void* p) {
-  return unsigned(reinterpret_cast<uintptr_t>(LDS_PTR(const char, p)));
-}
-
-__device__ __forceinline__ i32x4 make_rsrc(const void* base, unsigned bytes) {
-  const unsigned long long a = reinterpret_cast<unsigned long long>(base);
-  i32x4 r;
-  r[0] = int(unsigned(a));
-  r[1] = int(unsigned(a >> 32) & 0xffffu);
-  r[2] = int(bytes);
-  r[3] = 0x00020000;
-  return r;
-}
-
-// Global -> LDS copy of 16 bytes per active lane: lane i (of the wave) reads
-// buffer offset voff + soff (zeros past the buffer) and writes LDS byte
-// lds + 16 i, so a workgroup that copies one 8 KiB image passes each wave's
-// own 1 KiB part of the stage as `lds`. m0 is saved and restored inside the
-// asm; completion is awaited with vmcnt.
-__device__ __forceinline__ void dma16(i32x4 rsrc, unsigned voff, unsigned soff, unsigned lds) {
-  unsigned saved;
-  asm volatile(
-      "s_mov_b32 %0, m0\n\t"
-      "s_mov_b32 m0, %1\n\t"
-      "s_nop 0\n\t"
-      "buffer_load_dwordx4 %2, %3, %4 offen lds\n\t"
-      "s_mov_b32 m0, %0"
-      : "=&s"(saved)
-      : "s"(lds), "v"(voff), "s"(rsrc), "s"(soff)
-      : "memory");
-}
-
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  asm volatile("s_waitcnt vmcnt(%0)" : : "n"(N) : "memory");
-}
-
-__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" : : : "memory"); }
-
-// Sums over the four 16-lane groups / over the 16 lanes of a group.
-__device__ __forceinline__ float sum_groups(float x) {
-  x += __shfl_xor(x, 16, 64);
-  x += __shfl_xor(x, 32, 64);
-  return x;
-}
+// Sums over the 16 lanes of a group / over 8 lanes.
 __device__ __forceinline__ float sum16(float x) {
   x += __shfl_xor(x, 1, 64);
   x += __shfl_xor(x, 2, 64);

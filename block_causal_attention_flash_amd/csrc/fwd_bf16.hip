@@ -64,19 +64,11 @@
 // MFMA lane layouts (v_mfma_f32_16x16x32_bf16, lane l, g = l / 16):
 //   A: A[l % 16][8g + j], B: B[8g + j][l % 16] (j = 0..7), D: D[4g + i][l % 16]
 //   (i = 0..3).
+#include "cdna4.hpp"
 #include "kernels.hpp"
 
 namespace magi {
 namespace {
-
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-typedef int i32x4 __attribute__((ext_vector_type(4)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-
-#define LDS_PTR(T, p) ((__attribute__((address_space(3))) T*)(p))
-typedef __attribute__((address_space(3))) const bf16x8 lds_bf16x8;
 
 constexpr int BN = 32;                                // keys per tile
 constexpr int NWAVE = 8;                              // two waves per SIMD
@@ -115,9 +107,6 @@ struct Geo {
   // them may fly once the wave's first copy (K(0) for a K wave) has landed.
   static constexpr int PROLOGUE_YOUNGER = SPLIT_COPY ? 5 : 11;
 };
-constexpr unsigned kNoTile = 0x80000000u;             // scalar offset past any tile image buffer (< 2 GiB): zeros
-constexpr float kLog2e = 1.4426950408889634f;
-constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kStaticBound = 64.0f;                // largest exponent of P on the static path
 constexpr float kBoundSlack = 1.01f;                  // bf16 rounding of k_hat (2^-8), fp32 sums
 constexpr float kMinRowSum = 0x1p-100f;               // static-path row sums outside [2^-100, 2^100):
@@ -137,12 +126,7 @@ __device__ __forceinline__ float dpp(float x) {
   return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xF, 0xF, false));
 }
 
-// Sum / maximum over the four 16-lane groups (lanes l, l^16, l^32, l^48).
-__device__ __forceinline__ float sum_groups(float x) {
-  x += __shfl_xor(x, 16, 64);
-  x += __shfl_xor(x, 32, 64);
-  return x;
-}
+// Maximum over the four 16-lane groups (lanes l, l^16, l^32, l^48).
 __device__ __forceinline__ float max_groups(float x) {
   x = fmaxf(x, __shfl_xor(x, 16, 64));
   x = fmaxf(x, __shfl_xor(x, 32, 64));
@@ -157,48 +141,6 @@ __device__ __forceinline__ float sumsq8(bf16x8 a, float acc) {
   }
   return acc;
 }
-
-__device__ __forceinline__ unsigned lds_addr(const void* p) {
-  return unsigned(reinterpret_cast<uintptr_t>(LDS_PTR(const char, p)));
-}
-
-// Raw buffer resource: base, stride 0, num_records = bytes (reads at or past
-// `bytes` return zero), dword3 = 32-bit data format as used for raw buffers.
-__device__ __forceinline__ i32x4 make_rsrc(const void* base, unsigned bytes) {
-  const unsigned long long a = reinterpret_cast<unsigned long long>(base);
-  i32x4 r;
-  r[0] = int(unsigned(a));
-  r[1] = int(unsigned(a >> 32) & 0xffffu);
-  r[2] = int(bytes);
-  r[3] = 0x00020000;
-  return r;
-}
-
-// Global -> LDS copy of 16 bytes per lane: lane i reads buffer offset
-// voff + soff (zeros past num_records) and writes LDS byte lds + 16 i. Issued
-// through asm so that the compiler does not order later LDS reads of other
-// ring stages behind it; completion is awaited explicitly (vmcnt) before the
-// barrier that publishes the stage. m0 is saved and restored inside the asm.
-__device__ __forceinline__ void dma16(i32x4 rsrc, unsigned voff, unsigned soff, unsigned lds) {
-  unsigned saved;
-  asm volatile(
-      "s_mov_b32 %0, m0\n\t"
-      "s_mov_b32 m0, %1\n\t"
-      "s_nop 0\n\t"
-      "buffer_load_dwordx4 %2, %3, %4 offen lds\n\t"
-      "s_mov_b32 m0, %0"
-      : "=&s"(saved)
-      : "s"(lds), "v"(voff), "s"(rsrc), "s"(soff)
-      : "memory");
-}
-
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  asm volatile("s_waitcnt vmcnt(%0)" : : "n"(N) : "memory");
-}
-
-// All LDS traffic of this wave finished, then the workgroup barrier.
-__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" : : : "memory"); }
 
 // Tile images. The pre-pass writes every (32-key tile, KV head) of K-hat and
 // of V as a block of 64 D bytes that is copied byte for byte into an LDS ring
