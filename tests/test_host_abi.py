@@ -140,6 +140,17 @@ def test_stats_480p_tile_counts(built_lib):
     assert st["executed_pairs"] / st["unmasked_pairs"] < 1.01
 
 
+def test_bf16_head_dim_64_plans_like_128(built_lib):
+    """head_dim 64 is accepted for bf16 and plans the same work items and tile
+    lists as 128 (the tiling depends on the heads, not on head_dim)."""
+    from block_causal_attention_flash_amd import magi_attn_plan_stats
+    lay = get_config("streaming").layout
+    for hq, hk in ((24, 8), (6, 2), (8, 1)):
+        a = magi_attn_plan_stats(lay.q_offsets, lay.kv_offsets, lay.seq_chunks, hq, hk, 64, "bf16")
+        b = magi_attn_plan_stats(lay.q_offsets, lay.kv_offsets, lay.seq_chunks, hq, hk, 128, "bf16")
+        assert a == b
+
+
 BAD = [
     (dict(q_offsets=[0, 4, 3]), 1),                                  # decreasing offsets
     (dict(q_offsets=[1, 4]), 1),                                     # not starting at 0
