@@ -44,8 +44,8 @@ HQ, HK, D = 6, 2, 128
 SC = 1.0 / math.sqrt(D)
 
 
-def _inputs(seed, gains="uniform"):
-    return {n: t.to(DEV) for n, t in make_inputs(LAY, HQ, HK, D, "bf16", gains, seed).items()}
+def _inputs(seed, gains="uniform", d=D):
+    return {n: t.to(DEV) for n, t in make_inputs(LAY, HQ, HK, d, "bf16", gains, seed).items()}
 
 
 def _replay_checks(graph, static, fresh, eager_fn, outs, n=3):
@@ -66,33 +66,35 @@ def _replay_checks(graph, static, fresh, eager_fn, outs, n=3):
         del junk
 
 
-def test_graph_capture_forward():
+@pytest.mark.parametrize("d", [128, 64])
+def test_graph_capture_forward(d):
     from block_causal_attention_flash_amd import Plan
-    plan = Plan.from_layout(LAY, HQ, HK, D, "bf16")
-    sets = [_inputs(s) for s in (1, 2, 3)]
+    sc = 1.0 / math.sqrt(d)
+    plan = Plan.from_layout(LAY, HQ, HK, d, "bf16")
+    sets = [_inputs(s, d=d) for s in (1, 2, 3)]
     static = {n: t.clone() for n, t in sets[0].items()}
     ws = torch.empty(max(plan.workspace_size(), 16), dtype=torch.uint8, device=DEV)
     out = torch.empty_like(static["q"])
     lse = torch.empty((HQ, LAY.t_q), dtype=torch.float32, device=DEV)
 
     def eager(src):
-        o, l_ = plan(src["q"], src["k"], src["v"], src["q_gain"], src["k_gain"], 1e-6, SC)
+        o, l_ = plan(src["q"], src["k"], src["v"], src["q_gain"], src["k_gain"], 1e-6, sc)
         torch.cuda.synchronize()
         return o, l_
 
     s = torch.cuda.Stream()
     s.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(s):                          # warm-up on the capture stream
-        plan(static["q"], static["k"], static["v"], static["q_gain"], static["k_gain"], 1e-6, SC, out=out, lse=lse,
+        plan(static["q"], static["k"], static["v"], static["q_gain"], static["k_gain"], 1e-6, sc, out=out, lse=lse,
              workspace=ws, stream=s)
     torch.cuda.current_stream().wait_stream(s)
     torch.cuda.synchronize()
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g, stream=s):
-        plan(static["q"], static["k"], static["v"], static["q_gain"], static["k_gain"], 1e-6, SC, out=out, lse=lse,
+        plan(static["q"], static["k"], static["v"], static["q_gain"], static["k_gain"], 1e-6, sc, out=out, lse=lse,
              workspace=ws, stream=s)
     _replay_checks(g, static, sets, eager, (out, lse))
-    log("graph forward: 3 replays equal the eager calls")
+    log(f"graph forward d={d}: 3 replays equal the eager calls")
     plan.close()
 
 
@@ -172,27 +174,29 @@ def test_graph_capture_parallel_forward():
     plan.close()
 
 
-def test_graph_capture_backward():
+@pytest.mark.parametrize("d", [128, 64])
+def test_graph_capture_backward(d):
     from block_causal_attention_flash_amd import TrainPlan
-    plan = TrainPlan.from_layout(LAY, HQ, HK, D, "bf16")
+    sc = 1.0 / math.sqrt(d)
+    plan = TrainPlan.from_layout(LAY, HQ, HK, d, "bf16")
     sets = []
     for sd in (8, 9):
-        x = _inputs(sd)
-        o, l_ = plan(x["q"], x["k"], x["v"], x["q_gain"], x["k_gain"], 1e-6, SC)
+        x = _inputs(sd, d=d)
+        o, l_ = plan(x["q"], x["k"], x["v"], x["q_gain"], x["k_gain"], 1e-6, sc)
         x["out"], x["lse"] = o, l_
-        x["dout"] = torch.from_numpy(np.random.default_rng(sd).standard_normal((LAY.t_q, HQ, D)).astype(
+        x["dout"] = torch.from_numpy(np.random.default_rng(sd).standard_normal((LAY.t_q, HQ, d)).astype(
             np.float32)).to(torch.bfloat16).to(DEV)
         sets.append(x)
     torch.cuda.synchronize()
     static = {n: t.clone() for n, t in sets[0].items()}
     ws = torch.empty(max(plan.bwd_workspace_size(), 16), dtype=torch.uint8, device=DEV)
     grads = [torch.empty_like(static["q"]), torch.empty_like(static["k"]), torch.empty_like(static["v"]),
-             torch.empty(D, dtype=torch.float32, device=DEV), torch.empty(D, dtype=torch.float32, device=DEV)]
+             torch.empty(d, dtype=torch.float32, device=DEV), torch.empty(d, dtype=torch.float32, device=DEV)]
 
     def call(src, stream=None, outs=None, workspace=None):
         kw = {} if outs is None else dict(dq=outs[0], dk=outs[1], dv=outs[2], dq_gain=outs[3], dk_gain=outs[4])
         return plan.backward(src["q"], src["k"], src["v"], src["out"], src["lse"], src["dout"], src["q_gain"],
-                             src["k_gain"], 1e-6, SC, workspace=workspace, stream=stream, **kw)
+                             src["k_gain"], 1e-6, sc, workspace=workspace, stream=stream, **kw)
 
     def eager(src):
         r = call(src)
@@ -207,7 +211,7 @@ def test_graph_capture_backward():
     with torch.cuda.graph(g, stream=s):
         call(static, stream=s, outs=grads, workspace=ws)
     _replay_checks(g, static, sets, eager, grads)
-    log("graph backward: replays equal the eager calls")
+    log(f"graph backward d={d}: replays equal the eager calls")
     plan.close()
 
 
