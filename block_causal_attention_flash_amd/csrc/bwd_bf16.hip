@@ -391,13 +391,6 @@ bwd_dq_kernel(BwdParams p, BwdLayout L, const int4* __restrict__ items, const in
 #pragma unroll
       for (int rb = 0; rb < 2; ++rb) s[rb][kb] = mfma(a, qs[rb][ks], s[rb][kb]);
     }
-#pragma unroll
-    for (int f = 0; f < 2 * NKS; ++f) {
-      const int ks = f >> 1, kb = f & 1;
-      const bf16x8 a = *(lds_bf16x8*)(size_t)(vr0 + st + rowq + 2048 * ks + 256 * kb);
-#pragma unroll
-      for (int rb = 0; rb < 2; ++rb) dp[rb][kb] = mfma(a, dov[rb][ks], dp[rb][kb]);
-    }
     // lane: row r16 of block rb, keys 16 kb + 4 g + i of the tile
     const bool masked = i >= n_full;
     const int kt = masked ? (codes[i] >> 1) : 0;
@@ -413,14 +406,36 @@ bwd_dq_kernel(BwdParams p, BwdLayout L, const int4* __restrict__ items, const in
             s[rb][kb][e] = base + unsigned(16 * kb + e) < len ? s[rb][kb][e] : -__builtin_inff();
       }
     }
+    // dP on the matrix cores with P = 2^S (in place of S) on the vector ALUs
+    // between its MFMAs: the exponentials do not wait for dP
+#pragma unroll
+    for (int f = 0; f < 2 * NKS; ++f) {
+      const int ks = f >> 1, kb = f & 1;
+      const bf16x8 a = *(lds_bf16x8*)(size_t)(vr0 + st + rowq + 2048 * ks + 256 * kb);
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb) dp[rb][kb] = mfma(a, dov[rb][ks], dp[rb][kb]);
+    }
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) s[rb][kb][e] = __builtin_amdgcn_exp2f(s[rb][kb][e]);
+    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+#pragma unroll
+    for (int f = 0; f < 2 * NKS; ++f) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+      if (f < 2 * NKS - 2) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x400, 2, 0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
     bf16x8 ds[2];
 #pragma unroll
     for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int e = 0; e < 4; ++e)
-          ds[rb][4 * kb + e] = (__bf16)(__builtin_amdgcn_exp2f(s[rb][kb][e]) * dp[rb][kb][e]);
+        for (int e = 0; e < 4; ++e) ds[rb][4 * kb + e] = (__bf16)(s[rb][kb][e] * dp[rb][kb][e]);
 #pragma unroll
     for (int db = 0; db < NDB; ++db) {
       const bf16x8 a = tr_frag(kh0 + st + trq, db);
@@ -581,9 +596,7 @@ bwd_dkdv_kernel(BwdParams p, BwdLayout L, const int4* __restrict__ items, const 
     const bool masked = ce >= n_full;
     const int tt = codes[ce] >> 1;
     // S (lane: key r16 of half j, rows 16 rb + 4 g + e of the step's token
-    // tile), started from the rows' -lse log2 e so that it ends as S - lse log2 e,
-    // and dP, started from -D so that it ends as dP - D: both products read the
-    // step's row images and do not depend on the mask.
+    // tile), started from the rows' -lse log2 e so that it ends as S - lse log2 e
     f32x4 sc[2][2], dp[2][2];
 #pragma unroll
     for (int rb = 0; rb < 2; ++rb) {
@@ -598,22 +611,6 @@ bwd_dkdv_kernel(BwdParams p, BwdLayout L, const int4* __restrict__ items, const 
         sc[0][rb] = mfma(a, ku[0][ks], sc[0][rb]);
         sc[1][rb] = mfma(a, ku[1][ks], sc[1][rb]);
       }
-#pragma unroll
-    for (int ks = 0; ks < NKS; ++ks)
-#pragma unroll
-      for (int rb = 0; rb < 2; ++rb) {
-        const bf16x8 a = *(lds_bf16x8*)(size_t)(do0 + st + rowq + 2048 * ks + 256 * rb);
-        dp[0][rb] = mfma(a, vv[0][ks], dp[0][rb]);
-        dp[1][rb] = mfma(a, vv[1][ks], dp[1][rb]);
-      }
-    // both products with their row fragments read two ahead of the MFMAs
-    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-#pragma unroll
-    for (int f = 0; f < 4 * NKS; ++f) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
-      if (f < 4 * NKS - 2) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-    }
-    __builtin_amdgcn_sched_barrier(0);
     if (masked) {                                     // rows that do not see the key: S = -inf, P = 0
       asm volatile("" ::: "memory");                  // a branch, not selects on every step
 #pragma unroll
@@ -628,6 +625,30 @@ bwd_dkdv_kernel(BwdParams p, BwdLayout L, const int4* __restrict__ items, const 
               sc[j][rb][e] = -__builtin_inff();
           }
     }
+    // dP, started from -D so that it ends as dP - D, on the matrix cores with
+    // P = 2^S (in place of S) on the vector ALUs between its MFMAs
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks)
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb) {
+        const bf16x8 a = *(lds_bf16x8*)(size_t)(do0 + st + rowq + 2048 * ks + 256 * rb);
+        dp[0][rb] = mfma(a, vv[0][ks], dp[0][rb]);
+        dp[1][rb] = mfma(a, vv[1][ks], dp[1][rb]);
+      }
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) sc[j][rb][e] = __builtin_amdgcn_exp2f(sc[j][rb][e]);
+    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+#pragma unroll
+    for (int f = 0; f < 2 * NKS; ++f) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+      if (f < 2 * NKS - 2) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x400, 2, 0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
     // P and dS = P (dP - D) in bf16, then dV^T += dO^T P and dK^T += q_hat^T dS,
     // one transposed fragment of each image per dim block
     bf16x8 pb[2], dsb[2];
@@ -637,7 +658,7 @@ bwd_dkdv_kernel(BwdParams p, BwdLayout L, const int4* __restrict__ items, const 
       for (int j = 0; j < 2; ++j)
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const float pv = __builtin_amdgcn_exp2f(sc[j][rb][e]);
+          const float pv = sc[j][rb][e];
           pb[j][4 * rb + e] = (__bf16)pv;
           dsb[j][4 * rb + e] = (__bf16)(pv * dp[j][rb][e]);
         }
