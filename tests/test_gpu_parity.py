@@ -323,6 +323,27 @@ def test_config_full_size_sampled_rows(name):
     log(f"config {name}: rows={len(rows)} rel_l2={rl2:.3e} max_abs={mabs:.3e} lse_err={lerr:.3e}")
 
 
+def test_480x832_head_dim_64_sampled_rows():
+    """480x832 at head_dim 64 (48/8 heads, scale 1/8), the launch that
+    `bench.py --head-dim 64` times: the structured sample of every chunk with
+    8 uniform rows per chunk, all 48 heads, at the fixed bf16 tolerances."""
+    import dataclasses
+    from block_causal_attention_flash_amd import magi_attn_plan_stats
+    c = dataclasses.replace(get_config("video480x832"), head_dim=64)
+    log("480x832 d64: generating inputs")
+    inp = make_inputs(c.layout, c.n_q_heads, c.n_kv_heads, c.head_dim, c.dtype, c.gain_kind, c.seed)
+    st = magi_attn_plan_stats(c.layout.q_offsets, c.layout.kv_offsets, c.layout.seq_chunks, c.n_q_heads,
+                              c.n_kv_heads, c.head_dim, c.dtype)
+    log(f"480x832 d64: GPU run ({st['n_items']} workgroups)")
+    got_out, got_lse = run_gpu(c.layout, inp, c.n_q_heads, c.n_kv_heads, c.head_dim, c.dtype, c.eps, c.scale)
+    rows = structured_rows(c.layout, st["tile_q"], 8, seed=c.seed + 64)
+    log(f"480x832 d64: oracle on {len(rows)} rows")
+    ref_out, ref_lse = oracle.attention(inp["q"], inp["k"], inp["v"], inp["q_gain"], inp["k_gain"], c.eps,
+                                        c.scale, c.layout, rows=rows)
+    rl2, mabs, lerr = compare(got_out[rows], got_lse[:, rows], ref_out, ref_lse, c.dtype)
+    log(f"480x832 d64: rows={len(rows)} rel_l2={rl2:.3e} max_abs={mabs:.3e} lse_err={lerr:.3e}")
+
+
 def test_480x832_gains_x4_shifted_static_softmax():
     """480x832 with the query gains x4 (every logit bound ~66 log2 units, past
     the unshifted static range of 64): the static softmax runs with a shift of
