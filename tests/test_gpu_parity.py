@@ -194,6 +194,31 @@ def test_bf16_online_softmax_path(d):
     compare(*got, *ref, "bf16")
 
 
+@pytest.mark.parametrize("d", [64, 128])
+def test_bf16_online_path_mixed_flags_many_items(d):
+    """Many items, some flagged: 128 query heads on 128 KV heads over three
+    384-token chunks give 384 one-head items. The gain-40 channel with k zero
+    there flags every item whose head has q nonzero in that channel; heads
+    h % 3 == 0 have q zero there and stay on the static path. The running-
+    maximum instance must redo exactly the flagged items and leave the others'
+    outputs as the static instance wrote them."""
+    from block_causal_attention_flash_amd import magi_attn_plan_stats
+    lay = layout_from_chunks([[384, 384, 384]])
+    hq = hk = 128
+    st = magi_attn_plan_stats(lay.q_offsets, lay.kv_offsets, lay.seq_chunks, hq, hk, d, "bf16")
+    assert st["n_items"] == 384
+    log(f"bf16 online path, {st['n_items']} items d={d}")
+    inp = make_inputs(lay, hq, hk, d, "bf16", "uniform", 23)
+    inp["q_gain"][0] = 40.0
+    inp["k_gain"][0] = 40.0
+    inp["k"][:, :, 0] = 0.0
+    inp["q"][:, ::3, 0] = 0.0
+    sc = 1 / math.sqrt(d)
+    got = run_gpu(lay, inp, hq, hk, d, "bf16", 1e-6, sc)
+    ref = oracle.attention(inp["q"], inp["k"], inp["v"], inp["q_gain"], inp["k_gain"], 1e-6, sc, lay)
+    compare(*got, *ref, "bf16")
+
+
 def test_bf16_large_logits_stay_finite():
     """U(0.5, 1.5) gains x2.5 (products up to 14) make the logits up to ~14x
     those of unit gains. The outputs stay finite and meet the derived
