@@ -270,7 +270,10 @@ __device__ __forceinline__ void softmax_tile(f32x4 (&s)[NRB][2], int kt, WaveSta
     }
     // Row sums in fp32 of the unrounded exponentials (v_dot2 of the bf16 P
     // shares the matrix cores' issue and cost more alongside the products).
-    float ls = 0.0f;
+    // (the sum starts at the first pair rather than at 0: the same value, since
+    // a sum of exponentials is never -0, without the add of 0 that strict fp
+    // semantics would keep)
+    float ls;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -280,7 +283,7 @@ __device__ __forceinline__ void softmax_tile(f32x4 (&s)[NRB][2], int kt, WaveSta
         const bf16x2 pp = {(__bf16)e0, (__bf16)e1};
         p[rb][kb * 4 + i] = pp[0];
         p[rb][kb * 4 + i + 1] = pp[1];
-        ls += e0 + e1;
+        ls = (kb == 0 && i == 0) ? e0 + e1 : ls + (e0 + e1);
       }
     st.lsum[rb] = st.lsum[rb] * alpha[rb] + ls;
   }
