@@ -346,8 +346,7 @@ bwd_dq_kernel(BwdParams p, BwdLayout L, const int4* __restrict__ items, const in
   const unsigned own0 = kwave ? kh0 : vr0;
   const int* codes = tiles + item.z;
   const unsigned* soffs = soffs_all + item.z;    // padded past the list with kNoTile
-  auto issue = [&](int i) {
-    const unsigned so = __builtin_amdgcn_readfirstlane(soffs[i]);
+  auto issue_at = [&](int i, unsigned so) {
     const unsigned st = unsigned(i % RING) * IMG + wpart;
     if constexpr (G::SPLIT_COPY) {
       dma16(rown, voff, so, own0 + st);
@@ -356,7 +355,7 @@ bwd_dq_kernel(BwdParams p, BwdLayout L, const int4* __restrict__ items, const in
       dma16(rvr, voff, so, vr0 + st);
     }
   };
-  for (int i = 0; i < 4; ++i) issue(i);
+  for (int i = 0; i < 4; ++i) issue_at(i, __builtin_amdgcn_readfirstlane(soffs[i]));
 
   f32x4 acc[2][NDB];
 #pragma unroll
@@ -371,8 +370,11 @@ bwd_dq_kernel(BwdParams p, BwdLayout L, const int4* __restrict__ items, const in
     if ((i & 1) == 0) {
       wait_vmcnt<kYounger>();
       lds_barrier();                                  // and every wave left the stages of tiles i - 4, i - 3
-      issue(i + 4);
-      issue(i + 5);
+      // both offsets read before either copy, so that they come in one scalar load
+      const unsigned so4 = __builtin_amdgcn_readfirstlane(soffs[i + 4]);
+      const unsigned so5 = __builtin_amdgcn_readfirstlane(soffs[i + 5]);
+      issue_at(i + 4, so4);
+      issue_at(i + 5, so5);
     }
     const unsigned st = unsigned(i % RING) * IMG;
     // The S^T and dP^T chains start from -lse log2 e and -D (the lane's row
@@ -555,9 +557,10 @@ bwd_dkdv_kernel(BwdParams p, BwdLayout L, const int4* __restrict__ items, const 
   const i32x4 rown = qwave ? rqs : rdo;
   const unsigned own0 = qwave ? qs0 : do0;
   const unsigned voff = unsigned(tid % G::COPY_THREADS) * 16;
+  int icode = __builtin_amdgcn_readfirstlane(codes[0]);   // code of entry ie, read once per entry
   auto issue = [&]() {
     const bool live = ie < n_entries;
-    const unsigned imgi = __builtin_amdgcn_readfirstlane(live ? unsigned((codes[ie] >> 1) * p.hq + hbase + ih) : 0u);
+    const unsigned imgi = __builtin_amdgcn_readfirstlane(live ? unsigned((icode >> 1) * p.hq + hbase + ih) : 0u);
     const unsigned so = live ? imgi * IMG : kNoTile;
     const unsigned st = unsigned(((ie * grp + ih) % RING)) * IMG + wpart;
     if constexpr (G::SPLIT_COPY) {
@@ -569,7 +572,11 @@ bwd_dkdv_kernel(BwdParams p, BwdLayout L, const int4* __restrict__ items, const 
     if (lane < 16)
       dma16(rrs, unsigned(lane) * 16, live ? imgi * 256u : kNoTile,
             rs0 + unsigned((ie * grp + ih) % RING) * 8 * 256);
-    if (++ih == grp) { ih = 0; ++ie; }
+    if (++ih == grp) {
+      ih = 0;
+      ++ie;
+      icode = __builtin_amdgcn_readfirstlane(codes[ie]);   // the list is padded past its end
+    }
   };
   for (int i = 0; i < 4; ++i) issue();
 
@@ -594,7 +601,6 @@ bwd_dkdv_kernel(BwdParams p, BwdLayout L, const int4* __restrict__ items, const 
     const unsigned st = unsigned(s % RING) * IMG;
     const unsigned rsa = rs0 + unsigned(s % RING) * 8 * 256;
     const bool masked = ce >= n_full;
-    const int tt = codes[ce] >> 1;
     // S (lane: key r16 of half j, rows 16 rb + 4 g + e of the step's token
     // tile), started from the rows' -lse log2 e so that it ends as S - lse log2 e
     f32x4 sc[2][2], dp[2][2];
@@ -613,6 +619,7 @@ bwd_dkdv_kernel(BwdParams p, BwdLayout L, const int4* __restrict__ items, const 
       }
     if (masked) {                                     // rows that do not see the key: S = -inf, P = 0
       asm volatile("" ::: "memory");                  // a branch, not selects on every step
+      const int tt = codes[ce] >> 1;
 #pragma unroll
       for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
