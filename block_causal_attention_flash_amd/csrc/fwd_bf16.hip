@@ -621,26 +621,47 @@ fwd_bf16_kernel(FwdParams prm, const int4* __restrict__ items, const int* __rest
   }
   __bf16* const obase = reinterpret_cast<__bf16*>(px ? prm.outx : prm.out);
   float* const lbase = px ? prm.lsex : prm.lse;
+  // The output leaves through LDS so that every store writes whole rows (a
+  // lane's accumulators hold 4 dims of each of 16 rows: stored directly, each
+  // store instruction would write 32 bytes in 16 rows). The wave's 48 rows go
+  // to its own block of the rings, free once every wave has read its last V
+  // tile, in row order with 16-byte chunks XOR-swizzled by the row (no bank
+  // conflicts), and come back 16 bytes per lane, D / 8 lanes per row.
+  constexpr int CPR = D / 8;                          // 16-byte chunks per row
+  constexpr int WROWS = NRB * 16;                     // rows per wave
+  constexpr int RPI = 64 / CPR;                       // rows per store instruction
+  const auto swz = [](int row, int c) { return D == 128 ? (c ^ (row & 15)) : (c ^ ((row >> 1) & 7)); };
+  __syncthreads();
+  const unsigned ob = lds_addr(&sm.k[0][0]) + unsigned(wave * WROWS * G::ROW_BYTES);
 #pragma unroll
   for (int rb = 0; rb < NRB; ++rb) {
     const float lsum = lsr[rb];
-    if (valid[rb]) {
-      const bool any = lsum > 0.0f;                     // false only for a row that sees no key
-      const float inv = any ? 1.0f / lsum : 0.0f;
-      __bf16* orow = obase + (size_t(tok[rb]) * prm.hq + head[rb]) * D;
+    const bool any = lsum > 0.0f;                       // false only for a row that sees no key
+    const float inv = any ? 1.0f / lsum : 0.0f;
+    const int row = rb * 16 + (lane & 15);
 #pragma unroll
-      for (int db = 0; db < G::NDB; ++db) {
-        bf16x4 w;
+    for (int db = 0; db < G::NDB; ++db) {
+      bf16x4 w;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) w[i] = (__bf16)(st.o[rb][db][i] * inv);
-        *reinterpret_cast<bf16x4*>(orow + db * 16 + g * 4) = w;
-      }
-      if (g == 0) {
-        const float l2 = __builtin_amdgcn_logf(lsum);   // log2
-        const float lse = !any ? kNegInf : ((STATIC ? shift : st.m[rb]) + l2) * kLn2;
-        lbase[size_t(head[rb]) * prm.tq + tok[rb]] = lse;
-      }
+      for (int i = 0; i < 4; ++i) w[i] = (__bf16)(st.o[rb][db][i] * inv);
+      const int c = 2 * db + (g >> 1);
+      *LDS_PTR(bf16x4, size_t(ob + unsigned(row * G::ROW_BYTES + swz(row, c) * 16 + (g & 1) * 8))) = w;
     }
+    if (valid[rb] && g == 0) {
+      const float l2 = __builtin_amdgcn_logf(lsum);     // log2
+      const float lse = !any ? kNegInf : ((STATIC ? shift : st.m[rb]) + l2) * kLn2;
+      lbase[size_t(head[rb]) * prm.tq + tok[rb]] = lse;
+    }
+  }
+  const int c = lane % CPR;
+#pragma unroll
+  for (int k = 0; k < WROWS / RPI; ++k) {
+    const int row = k * RPI + lane / CPR;
+    const bf16x8 x = *(lds_bf16x8*)(size_t)(ob + unsigned(row * G::ROW_BYTES + swz(row, c) * 16));
+    const int r = wave * WROWS + row;                   // row of the item
+    const int t = item.x + r % prm.tile_q;
+    if (t < prm.tq)
+      *reinterpret_cast<bf16x8*>(obase + (size_t(t) * prm.hq + h0 + r / prm.tile_q) * D + c * 8) = x;
   }
 }
 
