@@ -493,15 +493,24 @@ fwd_bf16_kernel(FwdParams prm, const int4* __restrict__ items, const int* __rest
     tok[rb] = item.x + r % prm.tile_q;
     valid[rb] = tok[rb] < prm.tq;
   }
-  // ---- query loads first (older than every K/V copy)
+  // ---- every load of the prologue first, older than every K/V copy, so that
+  // they share one round trip: the gains, the query rows (unconditionally: a
+  // row past the stream's end reads the last row, and its norm factor is 0)
+  // and the rows' key bounds
+  float gq = 0.0f, gk = 0.0f;
+  if (tid < D) {
+    gq = px ? prm.q_gain_x[tid] : prm.q_gain[tid];
+    gk = px ? prm.k_gain_x[tid] : prm.k_gain[tid];
+  }
   bf16x8 qr[NRB][G::NKS];
+  int2 bnd[NRB];
 #pragma unroll
   for (int rb = 0; rb < NRB; ++rb) {
-    const __bf16* qrow =
-        reinterpret_cast<const __bf16*>(px ? prm.qx : prm.q) + (size_t(tok[rb]) * prm.hq + head[rb]) * D;
+    const int t = min(tok[rb], prm.tq - 1);
+    const __bf16* qrow = reinterpret_cast<const __bf16*>(px ? prm.qx : prm.q) + (size_t(t) * prm.hq + head[rb]) * D;
 #pragma unroll
-    for (int ks = 0; ks < G::NKS; ++ks)
-      qr[rb][ks] = valid[rb] ? *reinterpret_cast<const bf16x8*>(qrow + ks * 32 + g * 8) : bf16x8{};
+    for (int ks = 0; ks < G::NKS; ++ks) qr[rb][ks] = *reinterpret_cast<const bf16x8*>(qrow + ks * 32 + g * 8);
+    bnd[rb] = rows[(px ? prm.tq : 0) + t];
   }
 
   // ---- K/V copies ahead of the first step
@@ -529,9 +538,7 @@ fwd_bf16_kernel(FwdParams prm, const int4* __restrict__ items, const int* __rest
                     (j + 6 + NSTAGE) % NSTAGE);
   }
 
-  if (tid < D)
-    sm.gqk[tid] = px ? prm.q_gain_x[tid] * prm.k_gain_x[tid] * (prm.scale_x * kLog2e)
-                     : prm.q_gain[tid] * prm.k_gain[tid] * (prm.scale * kLog2e);
+  if (tid < D) sm.gqk[tid] = gq * gk * ((px ? prm.scale_x : prm.scale) * kLog2e);
   wait_vmcnt<G::PROLOGUE_YOUNGER>();                  // the wave's oldest copy (K(0) on a K-copying wave) landed
   __syncthreads();                                     // gqk and K(0) visible
   prefetch_k<D>(0, lo, st);
@@ -552,7 +559,7 @@ fwd_bf16_kernel(FwdParams prm, const int4* __restrict__ items, const int* __rest
 #pragma unroll
       for (int j = 0; j < 8; ++j) st.qf[rb][ks][j] = (__bf16)(float(qr[rb][ks][j]) * rq * (j < 4 ? g0[j] : g1[j - 4]));
     }
-    const int2 b = valid[rb] ? rows[(px ? prm.tq : 0) + tok[rb]] : int2{0, 0};
+    const int2 b = valid[rb] ? bnd[rb] : int2{0, 0};
     st.lo[rb] = b.x;
     st.hi[rb] = b.y;
 #pragma unroll
